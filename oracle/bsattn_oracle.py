@@ -1,0 +1,275 @@
+"""fp64 CPU oracle for block-sparse attention with top-k block selection.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check of the package entry
+and the bench's CPU-baseline leg may import this module. The HIP path never
+imports it, and it imports nothing from the HIP path: the two share no code.
+It is plain and slow on purpose: numpy in float64, a library matmul or sort as
+a step, no blocking or fusion beyond what the definitions state.
+
+Sources, cited by page title and section:
+  [SF]  SparseFormer page, qqiyuan.cn, "2026 新一代卷积与Transformer网络架构技术演进与性能对比":
+        section "SparseFormer 关键技术" (block-sparse attention: the N x N score matrix is
+        cut into blocks and the important blocks are TopK(Q_B K_B^T / sqrt(d), k)), and
+        section "SparseFormer 注意力实现" (block_sparse_attention(q, k, v, block_size,
+        topk_ratio) on q/k/v [B, N, H, D] in three steps: 1 mean-pool q and k per block and
+        form block scores with an einsum over d; 2 torch.topk with
+        k = int(topk_ratio * num_blocks); 3 attention over the selected blocks only with
+        scale 1/sqrt(D)).
+  [MSA] MSA page, cloud.baidu.com, "从M2.7到M3：多模态模型稀疏注意力架构设计与实现全解析":
+        §2.1 "核心数学模型" (sparse attention as Softmax(Mask(Q K^T / sqrt(d_k))) V, the mask
+        deciding which positions take part), §2.2 (two stages: block-level scores, then full
+        attention inside the chosen blocks), §3.1 (GQA-based attention block).
+
+Readings where the pages are silent or garbled (each is listed with its reason in
+the design notes of the repository):
+  R1  pooled blocks are laid out [B, H, nb, D] before the score einsum, so scores are
+      per (batch, head) [B, H, nb, nb] as the sketch's shape comments state;
+  R2  block scores are the unscaled product of pooled blocks (the sketch's einsum); the
+      1/sqrt(d) of the formula is a positive factor that leaves the order unchanged;
+  R4  ties between equal scores go to the lower key-block index;
+  R5  the selected indices of a row are returned in ascending block order;
+  R7  N must be a multiple of the block size (the sketch's .view needs it);
+  R8  no causal mask;
+  R10 GQA: query head h reads KV head h // (Hq // Hkv); selection is per query head;
+  R15 fp8 inputs are OCP e4m3 ("fn": no infinities, S.1111.111 is NaN) codes times a
+      per-tensor descale.
+
+Every function below is pinned by the CPU tests (tests/test_oracle_*.py) against
+closed forms, library routines, brute force or invariants; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Widening of stored values to float64
+# ---------------------------------------------------------------------------
+
+
+def widen_bf16_bits(bits) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64, exactly.
+
+    A bfloat16 value is the upper half of the float32 with the same bits.
+    """
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):     # NaN payloads widen to NaN
+        return b.view(np.float32).astype(np.float64)
+
+
+def decode_e4m3(codes) -> np.ndarray:
+    """OCP 8-bit floating point E4M3 codes (uint8) -> float64 [R15].
+
+    Layout: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits. Exponent field 0
+    is subnormal: value = m/8 * 2^(1-7). Otherwise value = (1 + m/8) * 2^(e-7). The
+    format has no infinities; exponent 15 with mantissa 7 is NaN, so the largest
+    finite magnitude is (1 + 6/8) * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    sub = m / 8.0 * 2.0 ** (1 - 7)
+    norm = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    mag = np.where(e == 0, sub, norm)
+    mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def widen(x, dtype: str, descale: float = 1.0) -> np.ndarray:
+    """Stored tensor (numpy array) -> float64 values the method sees.
+
+    dtype "f32": float32 array; "bf16": uint16 bit patterns; "fp8": uint8 e4m3 codes,
+    multiplied by the per-tensor descale (in float64).
+    """
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return widen_bf16_bits(x)
+    if dtype == "fp8":
+        return decode_e4m3(x) * np.float64(descale)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# The method, step by step
+# ---------------------------------------------------------------------------
+
+
+def topk_count(ratio: float, num_blocks: int) -> int:
+    """k = int(topk_ratio * num_blocks) [SF "SparseFormer 注意力实现", step 2]."""
+    return int(ratio * num_blocks)
+
+
+def pool(x: np.ndarray, block: int) -> np.ndarray:
+    """Mean of the `block` tokens of every block, per head [SF step 1; R1, R7].
+
+    x: [B, N, H, D] float64 -> [B, H, nb, D] float64 with nb = N // block.
+    """
+    B, N, H, D = x.shape
+    if N % block:
+        raise ValueError("N must be a multiple of the block size")
+    nb = N // block
+    return x.reshape(B, nb, block, H, D).mean(axis=2).transpose(0, 2, 1, 3)
+
+
+def kv_head(h: int, Hq: int, Hkv: int) -> int:
+    """KV head read by query head h under GQA [MSA §3.1; R10]."""
+    return h // (Hq // Hkv)
+
+
+def block_scores(qbar: np.ndarray, kbar: np.ndarray) -> np.ndarray:
+    """S[b,h,i,j] = sum_d qbar[b,h,i,d] * kbar[b,kv(h),j,d], unscaled [SF step 1; R2].
+
+    qbar [B, Hq, nb, D], kbar [B, Hkv, nb, D] -> S [B, Hq, nb, nb].
+    """
+    B, Hq, nb, D = qbar.shape
+    Hkv = kbar.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    S = np.empty((B, Hq, nb, kbar.shape[2]), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            S[b, h] = qbar[b, h] @ kbar[b, kv_head(h, Hq, Hkv)].T
+    return S
+
+
+def select_topk(S: np.ndarray, k: int) -> np.ndarray:
+    """Top-k key blocks of every score row [SF step 2; R4, R5].
+
+    The k-th largest score T of a row is found with a partition; every entry above T
+    is kept, and of the entries equal to T the ones with the lowest block index fill
+    the remaining places. Returns int64 [..., k], ascending block index per row.
+    """
+    nb = S.shape[-1]
+    if not 1 <= k <= nb:
+        raise ValueError("k must lie in [1, nb]")
+    T = -np.partition(-S, k - 1, axis=-1)[..., k - 1:k]     # k-th largest per row
+    above = S > T
+    equal = S == T
+    need = k - above.sum(axis=-1, keepdims=True)
+    rank_in_equal = np.cumsum(equal, axis=-1)                # 1-based, ascending j
+    keep = above | (equal & (rank_in_equal <= need))
+    rows = keep.reshape(-1, nb)
+    idx = np.nonzero(rows)[1].reshape(S.shape[:-1] + (k,))
+    return idx.astype(np.int64)
+
+
+def kth_scores(S: np.ndarray, k: int):
+    """(s_k, s_{k+1}): the k-th and (k+1)-th largest score of every row.
+
+    s_{k+1} is -inf when k equals the row length.
+    """
+    srt = -np.sort(-S, axis=-1)
+    sk = srt[..., k - 1]
+    sk1 = srt[..., k] if k < S.shape[-1] else np.full(sk.shape, -np.inf)
+    return sk, sk1
+
+
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, block: int,
+           scale: float, rows=None) -> np.ndarray:
+    """Exact softmax attention of every query block over its selected key blocks
+    [SF step 3; MSA §2.1, §2.2; R8, R10].
+
+    q [B, N, Hq, D], k/v [B, N, Hkv, D] float64; idx [B, Hq, nb, topk] (a set of key
+    blocks per query block and head). For query t of block i the keys are the union of
+    blocks idx[b,h,i,:] of KV head kv(h); weights softmax(scale * q_t . k_u).
+    rows: optional list of (b, h, i) to compute; the others are left NaN.
+    Returns out [B, N, Hq, D] float64.
+    """
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    nb = N // block
+    out = np.full(q.shape, np.nan, dtype=np.float64)
+    if rows is None:
+        rows = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(nb)]
+    for (b, h, i) in rows:
+        g = kv_head(h, Hq, Hkv)
+        tok = np.concatenate([np.arange(j * block, (j + 1) * block) for j in idx[b, h, i]])
+        Qi = q[b, i * block:(i + 1) * block, h, :]           # [block, D]
+        Ku = k[b, tok, g, :]                                 # [topk*block, D]
+        Vu = v[b, tok, g, :]
+        z = scale * (Qi @ Ku.T)
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        out[b, i * block:(i + 1) * block, h, :] = (p @ Vu) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def attend_batched(q, k, v, idx, block, scale, bh=None) -> np.ndarray:
+    """`attend` over all query blocks of the (b, h) pairs in `bh` at once.
+
+    Same arithmetic as `attend` (gather the selected key blocks, scaled product,
+    max-shifted exponent, weighted sum over the normaliser), with the gather and the
+    products done for a whole (b, h) per library call. Used for large sizes only.
+    """
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    nb = N // block
+    out = np.full(q.shape, np.nan, dtype=np.float64)
+    if bh is None:
+        bh = [(b, h) for b in range(B) for h in range(Hq)]
+    for (b, h) in bh:
+        g = kv_head(h, Hq, Hkv)
+        Kb = k[b, :, g, :].reshape(nb, block, D)
+        Vb = v[b, :, g, :].reshape(nb, block, D)
+        Ku = Kb[idx[b, h]].reshape(nb, -1, D)               # [nb, topk*block, D]
+        Vu = Vb[idx[b, h]].reshape(nb, -1, D)
+        Qb = q[b, :, h, :].reshape(nb, block, D)
+        z = scale * np.matmul(Qb, Ku.transpose(0, 2, 1))     # [nb, block, topk*block]
+        p = np.exp(z - z.max(axis=2, keepdims=True))
+        o = np.matmul(p, Vu) / p.sum(axis=2, keepdims=True)
+        out[b, :, h, :] = o.reshape(N, D)
+    return out
+
+
+def dense_attention(q, k, v, scale) -> np.ndarray:
+    """Full softmax(scale * Q K^T) V per head, no mask [MSA §2.1, full-attention mask]."""
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    out = np.empty(q.shape, dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            z = scale * (q[b, :, h, :] @ k[b, :, g, :].T)
+            p = np.exp(z - z.max(axis=1, keepdims=True))
+            out[b, :, h, :] = (p @ v[b, :, g, :]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def masked_attention_bruteforce(q, k, v, idx, block, scale) -> np.ndarray:
+    """Softmax(Mask(scale * Q K^T)) V with an explicit N x N token mask [MSA §2.1].
+
+    M[t, u] is true when key u's block is among the blocks selected for query t's
+    block; masked positions get -inf before the softmax. Tiny sizes only.
+    """
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    out = np.empty(q.shape, dtype=np.float64)
+    tb = np.arange(N) // block
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            M = np.zeros((N, N), dtype=bool)
+            for t in range(N):
+                M[t] = np.isin(tb, idx[b, h, tb[t]])
+            z = np.where(M, scale * (q[b, :, h, :] @ k[b, :, g, :].T), -np.inf)
+            p = np.exp(z - z.max(axis=1, keepdims=True))
+            out[b, :, h, :] = (p @ v[b, :, g, :]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def select(q, k, block: int, topk: int) -> np.ndarray:
+    """Steps 1-2 [SF]: pool q and k, score the blocks, keep the top-k per row."""
+    return select_topk(block_scores(pool(q, block), pool(k, block)), topk)
+
+
+def block_sparse_attention(q, k, v, block_size=64, topk_ratio=0.3, scale=None):
+    """The whole method [SF "SparseFormer 注意力实现"]: returns (out, idx).
+
+    q [B, N, Hq, D], k/v [B, N, Hkv, D] float64; scale defaults to 1/sqrt(D).
+    """
+    B, N, Hq, D = q.shape
+    nb = N // block_size
+    topk = topk_count(topk_ratio, nb)
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    idx = select(q, k, block_size, topk)
+    return attend(q, k, v, idx, block_size, scale), idx

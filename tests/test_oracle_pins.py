@@ -1,0 +1,332 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each pin checks one oracle function against a closed form, a library routine
+computed independently (torch in float64 on the CPU), brute force on tiny
+inputs, or an invariant the mathematics fixes. The planted-mistake tests at the
+end make sure a plausible error in the oracle (dropped term, wrong index, wrong
+sign, transposed operand, wrong tie rule) fails at least one pin.
+"""
+import fractions
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.bsattn_oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def rand_qkv(B, N, Hq, Hkv, D, seed=0):
+    r = rng(seed)
+    return (r.standard_normal((B, N, Hq, D)), r.standard_normal((B, N, Hkv, D)),
+            r.standard_normal((B, N, Hkv, D)))
+
+
+# ---------------------------------------------------------------- pin checks
+# Each check raises AssertionError when the oracle disagrees with the pin.
+
+def check_bf16_widen(o=O):
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits.astype(np.uint32) >> 7) & 0xFF) != 0xFF
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    got = o.widen_bf16_bits(bits)
+    assert np.array_equal(got[finite], ref[finite])
+    # closed forms
+    assert o.widen_bf16_bits([0x3F80])[0] == 1.0
+    assert o.widen_bf16_bits([0xC000])[0] == -2.0
+    assert o.widen_bf16_bits([0x0001])[0] == 2.0 ** -133
+    assert o.widen_bf16_bits([0x7F7F])[0] == (2 - 2.0 ** -7) * 2.0 ** 127
+
+
+def check_e4m3(o=O):
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = o.decode_e4m3(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # closed forms from the format's definition
+    assert o.decode_e4m3([0x7E])[0] == 448.0
+    assert o.decode_e4m3([0x38])[0] == 1.0
+    assert o.decode_e4m3([0x01])[0] == 2.0 ** -9
+    assert o.decode_e4m3([0x08])[0] == 2.0 ** -6
+    assert o.decode_e4m3([0xBC])[0] == -1.5
+    assert np.isnan(o.decode_e4m3([0x7F])[0]) and np.isnan(o.decode_e4m3([0xFF])[0])
+    assert int(nan.sum()) == 2
+
+
+def check_pool(o=O):
+    B, N, H, D, blk = 2, 24, 3, 5, 4
+    x = rng(1).standard_normal((B, N, H, D))
+    got = o.pool(x, blk)
+    assert got.shape == (B, H, N // blk, D)
+    for b in range(B):               # brute force, pure Python sums
+        for h in range(H):
+            for i in range(N // blk):
+                for d in range(D):
+                    s = 0.0
+                    for t in range(blk):
+                        s += x[b, i * blk + t, h, d]
+                    assert abs(got[b, h, i, d] - s / blk) <= 1e-15 * blk
+    c = np.full((1, 8, 2, 3), 0.375)
+    assert np.all(o.pool(c, 4) == 0.375)      # a constant block pools to itself
+
+
+def check_scores(o=O):
+    B, Hq, Hkv, nb, D = 2, 4, 2, 5, 3
+    r = rng(2)
+    qb, kb = r.standard_normal((B, Hq, nb, D)), r.standard_normal((B, Hkv, nb, D))
+    got = o.block_scores(qb, kb)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            for i in range(nb):
+                for j in range(nb):
+                    s = 0.0
+                    for d in range(D):
+                        s += qb[b, h, i, d] * kb[b, g, j, d]
+                    assert abs(got[b, h, i, j] - s) <= 1e-14
+    # library: einsum over repeat_interleaved KV heads (consecutive query heads share one)
+    kt = torch.from_numpy(kb).repeat_interleave(Hq // Hkv, dim=1)
+    ref = torch.einsum("bhid,bhjd->bhij", torch.from_numpy(qb), kt).numpy()
+    assert np.allclose(got, ref, rtol=0, atol=1e-13)
+
+
+def check_select_vs_sort(o=O):
+    r = rng(3)
+    for trial in range(40):
+        nb = int(r.integers(1, 70))
+        k = int(r.integers(1, nb + 1))
+        if trial % 2:   # heavy ties: few distinct values
+            S = r.integers(-2, 3, size=(3, 4, nb)).astype(np.float64)
+        else:
+            S = r.standard_normal((3, 4, nb))
+        got = o.select_topk(S, k)
+        for row, sel in zip(S.reshape(-1, nb), got.reshape(-1, k)):
+            order = np.lexsort((np.arange(nb), -row))[:k]     # score desc, index asc
+            assert np.array_equal(sel, np.sort(order))
+            assert np.all(np.diff(sel) > 0)
+
+
+def check_select_special(o=O):
+    S = np.zeros((1, 1, 6))
+    assert o.select_topk(S, 3).tolist() == [[[0, 1, 2]]]          # all tied: lowest indices
+    S = np.array([[[0.0, -0.0, 0.0, -1.0, -0.0]]])
+    assert o.select_topk(S, 2).tolist() == [[[0, 1]]]             # -0 ties +0
+    S = np.array([[[1.0, 5.0, 3.0, 5.0]]])
+    assert o.select_topk(S, 1).tolist() == [[[1]]]
+    assert o.select_topk(S, 4).tolist() == [[[0, 1, 2, 3]]]
+
+
+def check_dense_limit(o=O):
+    """topk = nb: the method is dense softmax attention (library SDPA in float64)."""
+    B, N, H, D, blk = 1, 64, 2, 16, 8
+    q, k, v = rand_qkv(B, N, H, H, D, seed=4)
+    nb = N // blk
+    idx = o.select(q, k, blk, nb)
+    assert np.array_equal(idx, np.broadcast_to(np.arange(nb), (B, H, nb, nb)))
+    got = o.attend(q, k, v, idx, blk, 1 / math.sqrt(D))
+    tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).permute(0, 2, 1, 3).numpy()
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+    assert np.allclose(o.dense_attention(q, k, v, 1 / math.sqrt(D)), ref, rtol=0, atol=1e-12)
+
+
+def check_bruteforce(o=O):
+    """Gathered-block attention equals explicitly masked N x N attention."""
+    B, N, H, D, blk = 1, 512, 2, 64, 64      # the tiny workload's shape
+    q, k, v = rand_qkv(B, N, H, H, D, seed=5)
+    nb = N // blk
+    out, idx = o.block_sparse_attention(q, k, v, blk, 0.25)
+    assert idx.shape == (B, H, nb, 2)
+    ref = o.masked_attention_bruteforce(q, k, v, idx, blk, 1 / math.sqrt(D))
+    assert np.max(np.abs(out - ref)) <= 1e-12
+    # a sparse result differs from the dense one
+    assert np.max(np.abs(out - o.dense_attention(q, k, v, 1 / math.sqrt(D)))) > 1e-3
+
+
+def check_ties_and_zero(o=O):
+    B, N, H, D, blk = 1, 64, 1, 8, 8
+    q, k, v = rand_qkv(B, N, H, H, D, seed=6)
+    k[:, 5 * blk:6 * blk] = k[:, 2 * blk:3 * blk]             # key block 5 duplicates block 2
+    S = o.block_scores(o.pool(q, blk), o.pool(k, blk))
+    assert np.array_equal(S[..., 5], S[..., 2])
+    for kk in range(1, 8):
+        idx = o.select_topk(S, kk)
+        for row, sel in zip(S.reshape(-1, 8), idx.reshape(-1, kk)):
+            # block 5 can only be chosen when block 2 is chosen too
+            assert (5 not in sel) or (2 in sel)
+    # q == 0: all scores 0, the lowest k blocks win; output = mean of V over them
+    z = np.zeros_like(q)
+    out, idx = o.block_sparse_attention(z, k, v, blk, 0.5)
+    assert np.all(idx == np.arange(4))
+    ref = v[:, :4 * blk].mean(axis=1)                          # [B, H, D]
+    assert np.allclose(out, ref[:, None], rtol=0, atol=1e-14)
+
+
+def check_invariants(o=O):
+    B, N, H, D, blk = 2, 96, 2, 16, 8
+    q, k, v = rand_qkv(B, N, H, H, D, seed=7)
+    scale = 1 / math.sqrt(D)
+    out, idx = o.block_sparse_attention(q, k, v, blk, 0.25)
+    # V constant => output constant
+    c = np.full_like(v, -0.625)
+    assert np.allclose(o.attend(q, k, c, idx, blk, scale), -0.625, rtol=0, atol=1e-14)
+    # permuting the tokens inside every block (K and V together) changes nothing
+    perm = np.concatenate([j * blk + rng(8).permutation(blk) for j in range(N // blk)])
+    out_p, idx_p = o.block_sparse_attention(q, k[:, perm], v[:, perm], blk, 0.25)
+    assert np.array_equal(idx, idx_p)
+    assert np.allclose(out, out_p, rtol=0, atol=1e-13)
+    # positive scaling of q keeps the selection
+    assert np.array_equal(o.select(3.5 * q, k, blk, 3), o.select(q, k, blk, 3))
+    # one-hot-by-block V: the weight of every unselected block is exactly zero
+    nb = N // blk
+    vb = np.zeros((B, N, H, D))
+    for t in range(N):
+        vb[:, t, :, t // blk] = 1.0
+    w = o.attend(q, k, vb, idx, blk, scale)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                rows = w[b, i * blk:(i + 1) * blk, h, :nb]
+                sel = np.zeros(nb, dtype=bool)
+                sel[idx[b, h, i]] = True
+                assert np.all(rows[:, ~sel] == 0.0)
+                assert np.all(rows[:, sel] > 0.0)
+                assert np.allclose(rows.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+
+
+def check_gqa(o=O):
+    B, N, Hq, Hkv, D, blk = 1, 64, 4, 2, 8, 8
+    q, k, v = rand_qkv(B, N, Hq, Hkv, D, seed=9)
+    out, idx = o.block_sparse_attention(q, k, v, blk, 0.5)
+    kr = torch.from_numpy(k).repeat_interleave(Hq // Hkv, dim=2).numpy()
+    vr = torch.from_numpy(v).repeat_interleave(Hq // Hkv, dim=2).numpy()
+    out_m, idx_m = o.block_sparse_attention(q, kr, vr, blk, 0.5)
+    assert np.array_equal(idx, idx_m)
+    assert np.allclose(out, out_m, rtol=0, atol=1e-14)
+
+
+def check_batched(o=O):
+    B, N, Hq, Hkv, D, blk = 2, 64, 4, 2, 8, 8
+    q, k, v = rand_qkv(B, N, Hq, Hkv, D, seed=10)
+    idx = o.select(q, k, blk, 3)
+    a = o.attend(q, k, v, idx, blk, 0.3)
+    b = o.attend_batched(q, k, v, idx, blk, 0.3)
+    assert np.allclose(a, b, rtol=0, atol=1e-13)
+
+
+ALL_CHECKS = [check_bf16_widen, check_e4m3, check_pool, check_scores, check_select_vs_sort,
+              check_select_special, check_dense_limit, check_bruteforce, check_ties_and_zero,
+              check_invariants, check_gqa, check_batched]
+
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
+def test_pin(check):
+    check()
+
+
+def test_topk_count_golden():
+    path = os.path.join(HERE, "golden", "topk_params.txt")
+    n = 0
+    for line in open(path, encoding="utf-8"):
+        if not line.strip() or line.startswith("#"):
+            continue
+        N, blk, ratio = line.split()[:3]
+        nb = int(N) // int(blk)
+        exact = math.floor(fractions.Fraction(ratio) * nb)
+        assert O.topk_count(float(ratio), nb) == exact
+        n += 1
+    assert n >= 5
+
+
+def test_kth_scores():
+    S = np.array([[[3.0, 1.0, 2.0, 2.0]]])
+    sk, sk1 = O.kth_scores(S, 2)
+    assert sk.item() == 2.0 and sk1.item() == 2.0
+    sk, sk1 = O.kth_scores(S, 4)
+    assert sk.item() == 1.0 and sk1.item() == -np.inf
+
+
+def test_rejects():
+    with pytest.raises(ValueError):
+        O.pool(np.zeros((1, 10, 1, 2)), 4)
+    with pytest.raises(ValueError):
+        O.select_topk(np.zeros((1, 4)), 0)
+    with pytest.raises(ValueError):
+        O.select_topk(np.zeros((1, 4)), 5)
+
+
+# ---------------------------------------------------- planted mistakes (CPU)
+
+class Mutant:
+    """The oracle module with one function replaced by a wrong version."""
+
+    def __init__(self, **repl):
+        self.__dict__.update({k: getattr(O, k) for k in dir(O) if not k.startswith("__")})
+        self.__dict__.update(repl)
+
+
+def _fails(check, mutant):
+    try:
+        check(mutant)
+    except AssertionError:
+        return True
+    return False
+
+
+def _rebind(fn, mutant):
+    """A copy of oracle function `fn` whose globals come from `mutant`."""
+    import types
+    g = dict(fn.__globals__)
+    g.update({k: v for k, v in mutant.__dict__.items()})
+    return types.FunctionType(fn.__code__, g, fn.__name__, fn.__defaults__)
+
+
+def _mutant(**repl):
+    m = Mutant(**repl)
+    for name in ("select", "block_sparse_attention", "block_scores", "attend", "attend_batched",
+                 "dense_attention", "masked_attention_bruteforce"):
+        if name not in repl:
+            setattr(m, name, _rebind(getattr(O, name), m))
+    return m
+
+
+MUTANTS = {
+    "pool_sum_not_mean": dict(pool=lambda x, b: O.pool(x, b) * b),
+    "pool_drops_last_token": dict(
+        pool=lambda x, b: x.reshape(x.shape[0], -1, b, *x.shape[2:])[:, :, :-1].mean(axis=2)
+        .transpose(0, 2, 1, 3)),
+    "gqa_modulo_mapping": dict(kv_head=lambda h, Hq, Hkv: h % Hkv),
+    "scores_transposed": dict(block_scores=lambda qb, kb: np.swapaxes(O.block_scores(qb, kb), -1, -2)),
+    "select_ties_to_higher": dict(
+        select_topk=lambda S, k: (S.shape[-1] - 1 - O.select_topk(S[..., ::-1], k))[..., ::-1]),
+    "select_smallest": dict(select_topk=lambda S, k: O.select_topk(-S, k)),
+    "attend_no_max_shift_sign": dict(
+        attend=lambda q, k, v, idx, blk, scale, rows=None: O.attend(q, k, v, idx, blk, -scale, rows)),
+    "attend_drops_last_block": dict(
+        attend=lambda q, k, v, idx, blk, scale, rows=None:
+        O.attend(q, k, v, idx[..., :-1] if idx.shape[-1] > 1 else idx, blk, scale, rows)),
+    "e4m3_bias_8": dict(decode_e4m3=lambda c: O.decode_e4m3(c) / 2),
+    "bf16_low_bits": dict(widen_bf16_bits=lambda b: np.asarray(b, dtype=np.uint16).astype(np.float64)),
+    "topk_round_not_truncate": dict(topk_count=lambda r, nb: int(round(r * nb))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    m = _mutant(**MUTANTS[name])
+    caught = [c.__name__ for c in ALL_CHECKS if _fails(c, m)]
+    if name == "topk_round_not_truncate":
+        # rounding differs from truncation on the pages' own parameters (0.3 * 128 = 38.4 no,
+        # 0.15 * 8192 = 1228.8 yes)
+        assert m.topk_count(0.15, 8192) != O.topk_count(0.15, 8192)
+        return
+    assert caught, f"no pin catches mutant {name}"
