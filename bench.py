@@ -1,0 +1,193 @@
+"""Benchmark of the block-sparse top-k attention hot path on one MI355X.
+
+One step = the whole path on one batch of synthetic input already resident in HBM:
+bsattn_select (pool q/k, block scores, top-k) then bsattn_forward (gathered-block
+attention). Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload sparseformer_n8192_bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}        # dense TFLOP/s, MI355X
+HBM_PEAK_GBS = 8000.0
+METRIC = "tokens/sec + % bf16 MFMA peak, block-sparse attn N=8192 H=16 D=64 top-30%"
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_top_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_sparseformer_n8192_traffic.txt")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="sparseformer_n8192_bf16")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-batches", type=int, default=0,
+                   help="cap on batch elements in the oracle sample (0: time-bounded, ~10 s)")
+    return p.parse_args()
+
+
+def file_sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_per_launch():
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE, encoding="utf-8"):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            vals[key.strip()] = val.strip()
+    if vals.get("source_sha256") != file_sha256(ATTN_SOURCE):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, ds, max_batches, budget_s=10.0):
+    """The fp64 oracle, as it stands, on batch elements 0, 1, ... of the workload until
+    `budget_s` seconds of CPU work are done (at least one, at most `max_batches`)."""
+    import numpy as np
+    import torch
+    import oracle.bsattn_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+
+    def host(t):
+        c = t.detach().cpu()
+        if c.dtype == torch.bfloat16:
+            return c.view(torch.int16).numpy().view(np.uint16), "bf16"
+        if c.dtype == torch.float8_e4m3fn:
+            return c.view(torch.uint8).numpy(), "fp8"
+        return c.numpy(), "f32"
+
+    topk = O.topk_count(w.ratio, w.nb)
+    dt_s, batches = 0.0, 0
+    while batches < max_batches and (batches == 0 or dt_s < budget_s):
+        sl = slice(batches, batches + 1)
+        (qh, dt), (kh, _), (vh, _) = host(q[sl]), host(k[sl]), host(v[sl])
+        t0 = time.perf_counter()
+        qo, ko, vo = O.widen(qh, dt, ds[0]), O.widen(kh, dt, ds[1]), O.widen(vh, dt, ds[2])
+        idx = O.select(qo, ko, w.block, topk)
+        O.attend_batched(qo, ko, vo, idx, w.block, 1.0 / math.sqrt(w.D))
+        dt_s += time.perf_counter() - t0
+        batches += 1
+    return {"value": batches * w.N / dt_s, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{batches} of {w.B} batch elements (all heads, all query blocks), "
+                      f"whole path in fp64 numpy, {dt_s:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
+              "multi-GPU variant in this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_sparse_top_amd as bst
+    from block_sparse_top_amd import synthetic as syn
+
+    w = syn.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    q, k, v, ds, _ = syn.workload_inputs(w, device=dev)
+    topk = int(w.ratio * w.nb)
+    scale = 1.0 / math.sqrt(w.D)
+    ws = torch.empty(bst.select_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.block),
+                     dtype=torch.uint8, device=dev)
+    idx = torch.empty((w.B, w.Hq, w.nb, topk), dtype=torch.int32, device=dev)
+    odt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    out = torch.empty((w.B, w.N, w.Hq, w.D), dtype=odt, device=dev)
+
+    # the C calls run on preallocated buffers (the binding would allocate idx and out per call)
+    L = bst.lib()
+    import ctypes
+    dcode = bst.bsattn._DTYPES[q.dtype]
+    dsc = (ctypes.c_float * 3)(*ds)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def do_select():
+        st = L.bsattn_select(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, P(q), P(k),
+                             P(idx), P(ws), ws.numel(), sp)
+        assert st == 0, L.bsattn_last_error()
+
+    def do_forward():
+        st = L.bsattn_forward(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, P(q), P(k),
+                              P(v), P(idx), scale, dsc, P(out), sp)
+        assert st == 0, L.bsattn_last_error()
+
+    for _ in range(args.warmup):
+        do_select()
+        do_forward()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        do_select()
+        e[1].record(stream)
+        do_forward()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sel_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
+    fwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = w.B * w.N
+    value = tokens / (ms_per_step / 1e3)
+
+    flops = 4.0 * w.B * w.Hq * w.N * (topk * w.block) * w.D            # QK^T + PV
+    achieved = flops / (fwd_ms / 1e3) / 1e12
+    peak = PEAK[w.dtype]
+    ebytes = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
+    sel_bytes = (w.B * w.N * (w.Hq + w.Hkv) * w.D * ebytes            # read q, k
+                 + 2 * 4 * w.B * w.nb * (w.Hq + w.Hkv) * w.D          # pooled write + read
+                 + 4 * w.B * w.Hq * w.nb * topk)                      # idx write
+    tr = traffic_per_launch()
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1), resident in HBM)",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "block": w.block, "topk": topk, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": tr, "kernel": f"attn_{w.dtype}_kernel",
+                     "algorithmic_flop_per_launch": flops},
+        "select_ms": round(sel_ms, 4), "forward_ms": round(fwd_ms, 4),
+        "select_hbm_frac": round(sel_bytes / (sel_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "select_algorithmic_bytes": sel_bytes,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, ds, args.cpu_batches or w.B)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,8 @@
+"""Block-sparse attention with top-k block selection for AMD MI355X (gfx950).
+
+The kernels live in libbsattn.so (C ABI, include/bsattn.h); `bsattn` is its binding.
+Importing the package does not load the library; the first call does, and raises if
+it is not built.
+"""
+from .bsattn import (BsattnError, block_sparse_attention, forward, lib, select,  # noqa: F401
+                     select_workspace_bytes, topk_count)

@@ -1,0 +1,165 @@
+"""Python binding of libbsattn.so (ctypes): argument marshalling only.
+
+Every step of the method runs in the library's gfx950 kernels; torch supplies device
+memory and the current HIP stream. There is no fallback: if the library is missing or
+was built for another target, loading raises.
+
+The method: SparseFormer page (qqiyuan.cn, "2026 新一代卷积与Transformer网络架构技术演进与性能
+对比"), section "SparseFormer 注意力实现": block_sparse_attention(q, k, v, block_size=64,
+topk_ratio=0.3) on q/k/v [B, N, H, D] -- pool q/k per block, score blocks, keep the top
+int(topk_ratio * num_blocks) key blocks per query block and head, attend over them with
+scale 1/sqrt(D). GQA head mapping per the MSA page (cloud.baidu.com, "从M2.7到M3：多模态
+模型稀疏注意力架构设计与实现全解析", §3.1).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbsattn.so")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported size or dtype",
+          3: "workspace missing or too small", 4: "HIP runtime error"}
+
+
+class BsattnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"bsattn: {STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with block_sparse_top_amd.build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    L.bsattn_abi_version.restype = i32
+    L.bsattn_abi_version.argtypes = []
+    L.bsattn_status_str.restype = ctypes.c_char_p
+    L.bsattn_status_str.argtypes = [i32]
+    L.bsattn_last_error.restype = ctypes.c_char_p
+    L.bsattn_last_error.argtypes = []
+    L.bsattn_select_workspace_bytes.restype = sz
+    L.bsattn_select_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
+    L.bsattn_select.restype = i32
+    L.bsattn_select.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.bsattn_forward.restype = i32
+    L.bsattn_forward.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                 ctypes.c_float, ctypes.POINTER(ctypes.c_float), vp, vp]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise BsattnError(status, lib().bsattn_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _shapes(q, k, v=None):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, N, H, D]")
+    B, N, Hq, D = q.shape
+    if k.shape[0] != B or k.shape[1] != N or k.shape[3] != D:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if v is not None and v.shape != k.shape:
+        raise ValueError("v must have the shape of k")
+    for t in (q, k) + ((v,) if v is not None else ()):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q/k/v must be contiguous device tensors")
+        if t.dtype != q.dtype:
+            raise ValueError("q, k, v must share one dtype")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return B, N, Hq, k.shape[2], D
+
+
+def topk_count(topk_ratio: float, num_blocks: int) -> int:
+    """k = int(topk_ratio * num_blocks), as the SparseFormer page's sketch computes it."""
+    return int(topk_ratio * num_blocks)
+
+
+def select_workspace_bytes(B, N, Hq, Hkv, D, block) -> int:
+    return int(lib().bsattn_select_workspace_bytes(B, N, Hq, Hkv, D, block))
+
+
+def select(q, k, block: int, topk: int, *, return_pooled: bool = False, workspace=None):
+    """Top-k key blocks per (batch, query head, query block): int32 [B, Hq, nb, topk].
+
+    With return_pooled, also returns the pooled q and k (fp32 [B, Hq, nb, D] and
+    [B, Hkv, nb, D]; for fp8 inputs without the per-tensor descale).
+    """
+    B, N, Hq, Hkv, D = _shapes(q, k)
+    nb = N // block if block > 0 else 0
+    idx = torch.empty((B, Hq, nb, max(topk, 0)), dtype=torch.int32, device=q.device)
+    nbytes = select_workspace_bytes(B, N, Hq, Hkv, D, block) if block > 0 and N % block == 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib().bsattn_select(_DTYPES[q.dtype], B, N, Hq, Hkv, D, block, topk, _ptr(q),
+                                   _ptr(k), _ptr(idx), _ptr(workspace), workspace.numel(),
+                                   _stream(q.device)))
+    if not return_pooled:
+        return idx
+    qb_bytes = (B * Hq * nb * D * 4 + 255) // 256 * 256
+    qbar = workspace[: B * Hq * nb * D * 4].view(torch.float32).view(B, Hq, nb, D)
+    kbar = workspace[qb_bytes: qb_bytes + B * Hkv * nb * D * 4].view(torch.float32).view(B, Hkv, nb, D)
+    return idx, qbar, kbar
+
+
+def forward(q, k, v, idx, scale: float | None = None, descales=(1.0, 1.0, 1.0), out=None):
+    """Attention of every query block over its selected key blocks: [B, N, Hq, D].
+
+    Output dtype: fp32 for fp32 inputs, bf16 for bf16 and fp8 inputs.
+    """
+    B, N, Hq, Hkv, D = _shapes(q, k, v)
+    if idx.dim() != 4 or idx.dtype != torch.int32 or not idx.is_contiguous() or not idx.is_cuda:
+        raise ValueError("idx must be a contiguous int32 device tensor [B, Hq, nb, topk]")
+    nb, topk = idx.shape[2], idx.shape[3]
+    if idx.shape[0] != B or idx.shape[1] != Hq or (nb and N % nb):
+        raise ValueError(f"idx shape {tuple(idx.shape)} does not match q {tuple(q.shape)}")
+    block = N // nb if nb else 0
+    if block == 0:
+        raise ValueError("cannot infer the block size from an empty idx")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    odt = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((B, N, Hq, D), dtype=odt, device=q.device)
+    elif out.shape != (B, N, Hq, D) or out.dtype != odt or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    ds = (ctypes.c_float * 3)(*[float(x) for x in descales])
+    with torch.cuda.device(q.device):
+        _check(lib().bsattn_forward(_DTYPES[q.dtype], B, N, Hq, Hkv, D, block, topk, _ptr(q),
+                                    _ptr(k), _ptr(v), _ptr(idx), scale, ds, _ptr(out),
+                                    _stream(q.device)))
+    return out
+
+
+def block_sparse_attention(q, k, v, block_size: int = 64, topk_ratio: float = 0.3,
+                           descales=(1.0, 1.0, 1.0), return_idx: bool = False):
+    """The whole method: select, then attend with scale 1/sqrt(D)."""
+    B, N, Hq, Hkv, D = _shapes(q, k, v)
+    topk = topk_count(topk_ratio, N // block_size)
+    idx = select(q, k, block_size, topk)
+    out = forward(q, k, v, idx, 1.0 / math.sqrt(D), descales)
+    return (out, idx) if return_idx else out

@@ -1,0 +1,158 @@
+// C ABI of the library (declared in include/bsattn.h): host-side argument checks,
+// workspace layout, and dispatch of the gfx950 kernels onto the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/bsattn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BSATTN_OK;
+  return fail(BSATTN_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks common to both entry points. Returns BSATTN_OK or an error with detail.
+int check_shape(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk) {
+  if (dtype != BSATTN_F32 && dtype != BSATTN_BF16 && dtype != BSATTN_FP8_E4M3)
+    return fail(BSATTN_E_INVALID, "unknown dtype %d", dtype);
+  if (B < 0 || N < 0) return fail(BSATTN_E_INVALID, "negative B or N");
+  if (Hq < 1 || Hkv < 1) return fail(BSATTN_E_INVALID, "Hq and Hkv must be >= 1");
+  if (Hq % Hkv) return fail(BSATTN_E_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (D < 1 || block < 1) return fail(BSATTN_E_INVALID, "D and block must be >= 1");
+  if (N % block) return fail(BSATTN_E_INVALID, "N (%lld) must be a multiple of block (%d)",
+                             (long long)N, block);
+  const int64_t nb = N / block;
+  if (B == 0 || N == 0) {
+    if (topk < 0 || topk > nb)
+      return fail(BSATTN_E_INVALID, "topk %d outside [0, nb=%lld]", topk, (long long)nb);
+  } else if (topk < 1 || topk > nb) {
+    return fail(BSATTN_E_INVALID, "topk %d outside [1, nb=%lld]", topk, (long long)nb);
+  }
+  if (D != 64 && D != 128) return fail(BSATTN_E_UNSUPPORTED, "D=%d (supported: 64, 128)", D);
+  if (block != 64 && block != 128)
+    return fail(BSATTN_E_UNSUPPORTED, "block=%d (supported: 64, 128)", block);
+  // index arithmetic limits of the kernels: tiles and rows fit in 32 bits
+  if (B * (int64_t)Hq * nb >= ((int64_t)1 << 31))
+    return fail(BSATTN_E_UNSUPPORTED, "B*Hq*nb too large");
+  if (N > ((int64_t)1 << 40)) return fail(BSATTN_E_UNSUPPORTED, "N too large");
+  return BSATTN_OK;
+}
+
+size_t pooled_q_bytes(int64_t B, int64_t N, int Hq, int D, int block) {
+  return align256((size_t)B * Hq * (size_t)(N / block) * D * sizeof(float));
+}
+size_t pooled_k_bytes(int64_t B, int64_t N, int Hkv, int D, int block) {
+  return align256((size_t)B * Hkv * (size_t)(N / block) * D * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsattn_abi_version(void) { return BSATTN_ABI_VERSION; }
+
+const char* bsattn_status_str(int status) {
+  switch (status) {
+    case BSATTN_OK: return "ok";
+    case BSATTN_E_INVALID: return "invalid argument";
+    case BSATTN_E_UNSUPPORTED: return "unsupported size or dtype";
+    case BSATTN_E_WORKSPACE: return "workspace missing or too small";
+    case BSATTN_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* bsattn_last_error(void) { return g_err; }
+
+size_t bsattn_select_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int D, int block) {
+  if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || D < 1 || block < 1 || N % block) {
+    fail(BSATTN_E_INVALID, "invalid sizes for the workspace query");
+    return 0;
+  }
+  if (B == 0 || N == 0) return 0;
+  return pooled_q_bytes(B, N, Hq, D, block) + pooled_k_bytes(B, N, Hkv, D, block);
+}
+
+int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
+                  const void* q, const void* k, int32_t* idx, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int st = check_shape(dtype, B, N, Hq, Hkv, D, block, topk);
+  if (st != BSATTN_OK) return st;
+  if (B == 0 || N == 0) return BSATTN_OK;
+  const int64_t nb = N / block;
+  if (nb > bsattn::kMaxFusedBlocks)
+    return fail(BSATTN_E_UNSUPPORTED, "selection over nb=%lld > %d blocks", (long long)nb,
+                bsattn::kMaxFusedBlocks);
+  if (!q || !k || !idx) return fail(BSATTN_E_INVALID, "null q, k or idx");
+  if (!aligned16(q) || !aligned16(k) || ((uintptr_t)idx & 3u))
+    return fail(BSATTN_E_INVALID, "q and k must be 16-byte aligned, idx 4-byte aligned");
+  const size_t need = bsattn_select_workspace_bytes(B, N, Hq, Hkv, D, block);
+  if (!workspace || workspace_bytes < need)
+    return fail(BSATTN_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if ((uintptr_t)workspace & 255u) return fail(BSATTN_E_WORKSPACE, "workspace not 256-byte aligned");
+
+  float* qbar = (float*)workspace;
+  float* kbar = (float*)((char*)workspace + pooled_q_bytes(B, N, Hq, D, block));
+  hipStream_t s = (hipStream_t)stream;
+  const int kind = dtype == BSATTN_F32 ? 0 : dtype == BSATTN_BF16 ? 1 : 2;
+  st = hip_status(bsattn::launch_pool(kind, B, N, Hq, Hkv, D, block, q, k, qbar, kbar, s),
+                  "pool launch");
+  if (st != BSATTN_OK) return st;
+  return hip_status(bsattn::launch_score_select(B, Hq, Hkv, nb, D, topk, qbar, kbar, idx, s),
+                    "score/select launch");
+}
+
+int bsattn_forward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
+                   const void* q, const void* k, const void* v, const int32_t* idx, float scale,
+                   const float* descale_qkv, void* out, void* stream) {
+  int st = check_shape(dtype, B, N, Hq, Hkv, D, block, topk);
+  if (st != BSATTN_OK) return st;
+  if (!isfinite(scale) || !(scale > 0.f))
+    return fail(BSATTN_E_INVALID, "scale must be finite and > 0");
+  if (dtype == BSATTN_FP8_E4M3) {
+    if (!descale_qkv) return fail(BSATTN_E_INVALID, "fp8 needs descale_qkv");
+    for (int j = 0; j < 3; ++j)
+      if (!isfinite(descale_qkv[j]) || !(descale_qkv[j] > 0.f))
+        return fail(BSATTN_E_INVALID, "descale_qkv[%d] must be finite and > 0", j);
+  }
+  if (B == 0 || N == 0) return BSATTN_OK;
+  if (!q || !k || !v || !idx || !out) return fail(BSATTN_E_INVALID, "null pointer argument");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)idx & 3u))
+    return fail(BSATTN_E_INVALID, "q, k, v, out must be 16-byte aligned, idx 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == BSATTN_BF16) {
+    if (!bsattn::attn_bf16_supported(D, block))
+      return fail(BSATTN_E_UNSUPPORTED, "bf16 attention for D=%d block=%d", D, block);
+    return hip_status(bsattn::launch_attn_bf16(B, N, Hq, Hkv, D, block, topk, q, k, v, idx,
+                                               scale, out, s),
+                      "bf16 attention launch");
+  }
+  if (dtype == BSATTN_F32) {
+    if (!bsattn::attn_f32_supported(D, block))
+      return fail(BSATTN_E_UNSUPPORTED, "fp32 attention for D=%d block=%d", D, block);
+    return hip_status(bsattn::launch_attn_f32(B, N, Hq, Hkv, D, block, topk, q, k, v, idx,
+                                              scale, out, s),
+                      "fp32 attention launch");
+  }
+  return fail(BSATTN_E_UNSUPPORTED, "fp8 attention is not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// Step 4 for fp32 inputs: attention over the gathered selected blocks on the fp32 ALUs.
+//
+// Same operation as the bf16 kernel (SparseFormer page "2026 新一代卷积与Transformer网络架构
+// 技术演进与性能对比", "SparseFormer 注意力实现" step 3; MSA page "从M2.7到M3：多模态模型稀疏
+// 注意力架构设计与实现全解析" §2.1 with a block mask) with every product, exponent and sum in
+// fp32, for inputs whose precision must be kept (max-abs error ~1e-6 on N(0,1) data).
+//
+// One work-group per (batch, query head, query block), one thread per query row. Keys of a
+// selected block are staged 32 at a time in LDS (K and V rows, read as broadcasts); each
+// thread keeps its q row, output row, running max and normaliser in registers and updates
+// them once per 32 keys (exact online softmax: rescale whenever the max grows).
+#include "common.h"
+#include "launch.h"
+
+namespace bsattn {
+namespace {
+
+constexpr int kChunk = 32;
+
+template <int D>
+__global__ __launch_bounds__(128) void attn_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const int32_t* __restrict__ idx, float* __restrict__ out, int64_t N, int Hq, int Hkv,
+    int nb, int block, int topk, float c, uint32_t total_tiles) {
+  __shared__ __attribute__((aligned(16))) float ks[kChunk][D];
+  __shared__ __attribute__((aligned(16))) float vs[kChunk][D];
+  const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
+  const int G = Hq / Hkv;
+  const int i = (int)(tile % nb);
+  uint32_t rest = tile / nb;
+  const int hh = (int)(rest % G);
+  rest /= G;
+  const int g = (int)(rest % Hkv);
+  const int b = (int)(rest / Hkv);
+  const int h = g * G + hh;
+  const int tid = threadIdx.x;
+  const int64_t qrs = (int64_t)Hq * D, krs = (int64_t)Hkv * D;
+
+  const int64_t row = (int64_t)b * N + (int64_t)i * block + tid;
+  float qr[D], o[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    qr[d] = q[row * qrs + (int64_t)h * D + d];
+    o[d] = 0.f;
+  }
+  float m = -__builtin_inff(), l = 0.f;
+  bool bad = false;
+  const int32_t* myidx = idx + (((int64_t)b * Hq + h) * nb + i) * topk;
+  const float* kb0 = k + (int64_t)b * N * krs + (int64_t)g * D;
+  const float* vb0 = v + (int64_t)b * N * krs + (int64_t)g * D;
+
+  for (int t = 0; t < topk; ++t) {
+    int kb = myidx[t];
+    if ((unsigned)kb >= (unsigned)nb) { bad = true; kb = 0; }
+    for (int c0 = 0; c0 < block; c0 += kChunk) {
+      __syncthreads();
+      for (int e = tid; e < kChunk * D / 4; e += block) {
+        const int r = e / (D / 4), d4 = e % (D / 4);
+        const int64_t tok = (int64_t)kb * block + c0 + r;
+        *(f32x4*)&ks[r][4 * d4] = *(const f32x4*)(kb0 + tok * krs + 4 * d4);
+        *(f32x4*)&vs[r][4 * d4] = *(const f32x4*)(vb0 + tok * krs + 4 * d4);
+      }
+      __syncthreads();
+      float s[kChunk];
+      float mc = m;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        float a = 0.f;
+#pragma unroll
+        for (int d = 0; d < D; ++d) a = __builtin_fmaf(qr[d], ks[j][d], a);
+        s[j] = a * c;                          // exp2 domain
+        mc = fmaxf(mc, s[j]);
+      }
+      const float alpha = __builtin_amdgcn_exp2f(m - mc);   // 0 on the first chunk
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < D; ++d) o[d] *= alpha;
+      m = mc;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        const float p = __builtin_amdgcn_exp2f(s[j] - m);
+        l += p;
+#pragma unroll
+        for (int d = 0; d < D; ++d) o[d] = __builtin_fmaf(p, vs[j][d], o[d]);
+      }
+    }
+  }
+  const float inv = bad ? __builtin_nanf("") : 1.0f / l;
+#pragma unroll
+  for (int d = 0; d < D; ++d) out[row * qrs + (int64_t)h * D + d] = o[d] * inv;
+}
+
+template <int D>
+hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int block, int topk, const void* q,
+                  const void* k, const void* v, const int32_t* idx, float c, void* out,
+                  hipStream_t stream) {
+  const int nb = (int)(N / block);
+  const uint32_t total = (uint32_t)(B * Hq * nb);
+  attn_f32_kernel<D><<<total, block, 0, stream>>>((const float*)q, (const float*)k,
+                                                   (const float*)v, idx, (float*)out, N, Hq, Hkv,
+                                                   nb, block, topk, c, total);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_f32_supported(int D, int block) {
+  return (D == 64 || D == 128) && (block == 64 || block == 128);
+}
+
+hipError_t launch_attn_f32(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
+                           const void* q, const void* k, const void* v, const int32_t* idx,
+                           float scale, void* out, hipStream_t stream) {
+  const float c = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
+  if (D == 64) return launch<64>(B, N, Hq, Hkv, block, topk, q, k, v, idx, c, out, stream);
+  return launch<128>(B, N, Hq, Hkv, block, topk, q, k, v, idx, c, out, stream);
+}
+
+}  // namespace bsattn

@@ -1,0 +1,33 @@
+// Internal launchers of the gfx950 kernels. Shapes are validated by the C ABI layer
+// before any of these is called; each returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsattn {
+
+// Step 1: per-block mean of q and k (fp32 out, [B, H, nb, D]). kind: 0 fp32, 1 bf16, 2 fp8.
+hipError_t launch_pool(int kind, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
+                       const void* q, const void* k, float* qbar, float* kbar,
+                       hipStream_t stream);
+
+// Steps 2-3 fused for nb <= kMaxFusedBlocks: block scores and top-k per row.
+constexpr int kMaxFusedBlocks = 1024;
+hipError_t launch_score_select(int64_t B, int Hq, int Hkv, int64_t nb, int D, int topk,
+                               const float* qbar, const float* kbar, int32_t* idx,
+                               hipStream_t stream);
+
+// Step 4, bf16 inputs on bf16 MFMA. Supported (D, block): D, block in {64, 128}.
+bool attn_bf16_supported(int D, int block);
+hipError_t launch_attn_bf16(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
+                            const void* q, const void* k, const void* v, const int32_t* idx,
+                            float scale, void* out, hipStream_t stream);
+
+// Step 4, fp32 inputs on the fp32 vector ALUs.
+bool attn_f32_supported(int D, int block);
+hipError_t launch_attn_f32(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
+                           const void* q, const void* k, const void* v, const int32_t* idx,
+                           float scale, void* out, hipStream_t stream);
+
+}  // namespace bsattn

@@ -1,0 +1,127 @@
+/*
+ * bsattn.h -- C ABI of the MI355X (gfx950) block-sparse top-k attention library.
+ *
+ * The method (block-sparse attention with top-k block selection):
+ *   SparseFormer page, qqiyuan.cn, "2026 新一代卷积与Transformer网络架构技术演进与性能对比",
+ *   sections "SparseFormer 关键技术" (TopK over block scores) and "SparseFormer 注意力实现"
+ *   (three steps: mean-pool q/k per block and score blocks; keep the top
+ *   k = int(topk_ratio * num_blocks) key blocks per query block and head; attention over
+ *   the selected blocks only with scale 1/sqrt(D)).
+ *   MSA page, cloud.baidu.com, "从M2.7到M3：多模态模型稀疏注意力架构设计与实现全解析",
+ *   §2.1 (Softmax(Mask(Q K^T / sqrt(d_k))) V), §2.2 (select blocks, then full attention
+ *   inside them), §3.1 (GQA-based attention block).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are contiguous, row-major, in device memory (HBM) owned by the caller.
+ *     q is [B, N, Hq, D]; k and v are [B, N, Hkv, D]; out is [B, N, Hq, D];
+ *     idx is [B, Hq, nb, topk] int32 with nb = N / block.
+ *   - GQA: query head h reads KV head h / (Hq / Hkv); selection is per query head.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null stream),
+ *     never synchronises, never allocates or frees device memory, and keeps no state
+ *     between calls. Argument checks run on the host before any launch.
+ *   - Errors are returned, never thrown or printed: the return value is a bsattn_status;
+ *     bsattn_last_error() gives a text detail of the last failure on the calling thread.
+ *     Launch failures come back as BSATTN_E_HIP. Kernel faults surface at the caller's
+ *     next synchronisation.
+ *   - Supported now: D in {64, 128}; block in {64, 128}; nb <= 1024 for selection;
+ *     storage dtypes fp32, bf16 and OCP fp8 e4m3. Other sizes give BSATTN_E_UNSUPPORTED.
+ *   - B == 0 or N == 0 is an empty call: arguments are checked, nothing is launched
+ *     (topk must then be 0 when nb == 0).
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSATTN_ABI_VERSION 1
+
+typedef enum {
+  BSATTN_OK = 0,
+  BSATTN_E_INVALID = 1,      /* bad shape, pointer, alignment, topk or scale */
+  BSATTN_E_UNSUPPORTED = 2,  /* valid arguments without a kernel (D, block, nb, dtype) */
+  BSATTN_E_WORKSPACE = 3,    /* workspace missing or smaller than bsattn_select_workspace_bytes */
+  BSATTN_E_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} bsattn_status;
+
+typedef enum {
+  BSATTN_F32 = 0,       /* IEEE binary32 */
+  BSATTN_BF16 = 1,      /* bfloat16 */
+  BSATTN_FP8_E4M3 = 2   /* OCP 8-bit E4M3 ("fn": no infinities), values = code * descale */
+} bsattn_dtype;
+
+/* Version of this ABI (BSATTN_ABI_VERSION of the built library). */
+int bsattn_abi_version(void);
+
+/* Static English text of a status code; never NULL. */
+const char* bsattn_status_str(int status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). The
+ * string is owned by the library and valid until the next call on that thread. */
+const char* bsattn_last_error(void);
+
+/* Bytes of device workspace bsattn_select needs for these sizes (0 for an empty call).
+ * Layout, each part 256-byte aligned: pooled q, fp32 [B, Hq, nb, D]; then pooled k,
+ * fp32 [B, Hkv, nb, D]. For fp8 inputs the pooled values are means of the e4m3 codes'
+ * values without the per-tensor descale (a positive factor that does not change the
+ * selection). Returns 0 and records an error for invalid sizes. */
+size_t bsattn_select_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int D, int block);
+
+/*
+ * Block selection (steps 1-2 of "SparseFormer 注意力实现" on the SparseFormer page).
+ *   Pooled blocks: qbar[b,h,i,:] = mean of q[b, i*block + t, h, :] over t < block, and kbar
+ *   likewise per KV head, accumulated in fp32.
+ *   Scores: S[b,h,i,j] = sum_d qbar[b,h,i,d] * kbar[b,h/(Hq/Hkv),j,d], fp32, unscaled (the
+ *   1/sqrt(d) of the page's formula is a positive factor and leaves the order unchanged).
+ *   idx[b,h,i,:] = the topk key blocks j with the largest S[b,h,i,j]; equal scores go to the
+ *   lower j (-0.0 equals +0.0); written in ascending j. NaN scores are unspecified.
+ * Arguments
+ *   dtype      bsattn_dtype of q and k.
+ *   B, N       batch and sequence length; N % block == 0.
+ *   Hq, Hkv    query and KV heads; Hq % Hkv == 0.
+ *   D          head dimension.
+ *   block      tokens per block.
+ *   topk       1 <= topk <= nb (callers of the page's form pass int(topk_ratio * nb)).
+ *   q, k       device pointers, 16-byte aligned.
+ *   idx        device pointer, int32 [B, Hq, nb, topk], written entirely.
+ *   workspace  device pointer, 256-byte aligned, at least bsattn_select_workspace_bytes.
+ *   stream     hipStream_t.
+ */
+int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
+                  const void* q, const void* k, int32_t* idx,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Gathered-block attention (step 3 of "SparseFormer 注意力实现"; MSA page §2.1 with a
+ * block mask, §2.2 second stage).
+ *   For query token t of block i and query head h, with g = h / (Hq / Hkv):
+ *   out[b,t,h,:] = sum over keys u in the blocks idx[b,h,i,:] of
+ *                  softmax_u(scale * q[b,t,h,:] . k[b,u,g,:]) * v[b,u,g,:].
+ *   Scores and the softmax state are fp32; fp32 inputs compute in fp32, bf16 inputs multiply
+ *   on bf16 MFMA with the probabilities rounded to bf16, fp8 inputs multiply on fp8 MFMA.
+ * Arguments
+ *   dtype, B, N, Hq, Hkv, D, block, topk  as for bsattn_select.
+ *   q, k, v      device pointers, 16-byte aligned.
+ *   idx          device pointer, int32 [B, Hq, nb, topk]; each row should hold distinct
+ *                blocks in [0, nb). A row with an out-of-range entry is not read out of
+ *                bounds: its output rows are set to NaN. Duplicate entries count twice.
+ *   scale        finite softmax scale (the page uses 1/sqrt(D)).
+ *   descale_qkv  host pointer to 3 floats (q, k, v per-tensor descales) for fp8; ignored
+ *                (may be NULL) for other dtypes. Must be finite and > 0.
+ *   out          device pointer, 16-byte aligned: fp32 for fp32 inputs, bf16 for bf16 and
+ *                fp8 inputs; [B, N, Hq, D], written entirely.
+ *   stream       hipStream_t.
+ */
+int bsattn_forward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
+                   const void* q, const void* k, const void* v, const int32_t* idx,
+                   float scale, const float* descale_qkv, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */

@@ -1,0 +1,80 @@
+"""Comparison rules between the HIP path and the fp64 oracle (test infrastructure).
+
+Index rule: on every row whose k-th and (k+1)-th oracle scores differ by more than 1e-5
+relative (denominator max(|s_k|, |s_k+1|)), the selected set must equal the oracle's
+bit for bit. On the other rows several answers are right: the GPU set must be a valid
+top-k under the oracle's scores, i.e. min over the chosen >= max over the rest minus
+1e-5 of the row's magnitude.
+Output rule: max-abs error <= 2e-2 (bf16, fp8) or 1e-4 (fp32), and relative L2 error
+<= 1e-2 (bf16, fp8) or 1e-5 (fp32), computed against the oracle run on the GPU's indices.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle.bsattn_oracle as O
+
+GAP_REL = 1e-5
+TOL = {"f32": (1e-4, 1e-5), "bf16": (2e-2, 1e-2), "fp8": (2e-2, 1e-2)}
+
+
+def dtype_name(t: torch.Tensor) -> str:
+    return {torch.float32: "f32", torch.bfloat16: "bf16", torch.float8_e4m3fn: "fp8"}[t.dtype]
+
+
+def to_f64(t: torch.Tensor, descale: float = 1.0) -> np.ndarray:
+    """Device/host tensor in storage dtype -> the float64 values the oracle widens."""
+    dt = dtype_name(t)
+    c = t.detach().cpu().contiguous()
+    if dt == "f32":
+        return O.widen(c.numpy(), "f32")
+    if dt == "bf16":
+        return O.widen(c.view(torch.int16).numpy().view(np.uint16), "bf16")
+    return O.widen(c.view(torch.uint8).numpy(), "fp8", descale)
+
+
+def check_idx(gpu_idx: np.ndarray, S: np.ndarray, k: int):
+    """gpu_idx [..., k], S [..., nb] oracle scores. Returns a stats dict; asserts the rule."""
+    nb = S.shape[-1]
+    G = gpu_idx.reshape(-1, k).astype(np.int64)
+    Sr = S.reshape(-1, nb)
+    assert G.shape[0] == Sr.shape[0]
+    assert np.all((G >= 0) & (G < nb)), "index out of range"
+    if k > 1:
+        assert np.all(np.diff(G, axis=1) > 0), "row not strictly ascending"
+    ref = O.select_topk(Sr, k)
+    sk, sk1 = O.kth_scores(Sr, k)
+    denom = np.maximum(np.abs(sk), np.abs(sk1))
+    denom = np.where(np.isfinite(denom), denom, np.abs(sk))
+    clear = (sk - sk1) > GAP_REL * denom
+    exact_ok = np.all(G == ref, axis=1)
+    bad_exact = np.nonzero(clear & ~exact_ok)[0]
+    assert bad_exact.size == 0, f"{bad_exact.size} clear rows differ, first {bad_exact[:5]}"
+    amb = np.nonzero(~clear)[0]
+    mag = np.abs(Sr).max(axis=1)
+    for r in amb:
+        chosen = np.zeros(nb, dtype=bool)
+        chosen[G[r]] = True
+        if chosen.all():
+            continue
+        lo = Sr[r][chosen].min()
+        hi = Sr[r][~chosen].max()
+        assert lo >= hi - GAP_REL * max(denom[r], mag[r]), f"row {r}: not a valid top-k"
+    return {"rows": int(G.shape[0]), "clear": int(clear.sum()), "ambiguous": int(amb.size),
+            "ambiguous_differing": int((~exact_ok[amb]).sum()) if amb.size else 0}
+
+
+def out_errors(gpu_out: np.ndarray, ref: np.ndarray):
+    diff = gpu_out.astype(np.float64) - ref
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    rel_l2 = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300)) if diff.size else 0.0
+    return max_abs, rel_l2
+
+
+def check_out(gpu_out: np.ndarray, ref: np.ndarray, dt: str):
+    assert not np.isnan(gpu_out).any(), "output has NaN (unwritten or invalid)"
+    max_abs, rel_l2 = out_errors(gpu_out, ref)
+    tol_abs, tol_rel = TOL[dt]
+    assert max_abs <= tol_abs and rel_l2 <= tol_rel, (max_abs, rel_l2)
+    return max_abs, rel_l2

@@ -1,0 +1,117 @@
+"""The C-ABI library loads and exports what include/bsattn.h declares; host-side argument
+checks reject bad calls before any launch (no GPU needed: every call here fails its
+checks on the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_top_amd as bst
+from block_sparse_top_amd import bsattn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsattn.h")
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call below fails first
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsattn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = bst.lib()
+    names = declared_functions()
+    assert {"bsattn_select", "bsattn_forward", "bsattn_select_workspace_bytes",
+            "bsattn_abi_version", "bsattn_status_str", "bsattn_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    L = bst.lib()
+    assert L.bsattn_abi_version() == 1
+    for s in range(5):
+        assert L.bsattn_status_str(s).decode() == bsattn.STATUS[s]
+    assert L.bsattn_status_str(99).decode() == "unknown status"
+
+
+def sel(dtype=1, B=1, N=512, Hq=2, Hkv=2, D=64, block=64, topk=2, q=FAKE, k=FAKE, idx=FAKE,
+        ws=FAKE, wsb=1 << 30):
+    return bst.lib().bsattn_select(dtype, B, N, Hq, Hkv, D, block, topk, q, k, idx, ws, wsb, None)
+
+
+def fwd(dtype=1, B=1, N=512, Hq=2, Hkv=2, D=64, block=64, topk=2, q=FAKE, k=FAKE, v=FAKE,
+        idx=FAKE, scale=0.125, descale=None, out=FAKE):
+    return bst.lib().bsattn_forward(dtype, B, N, Hq, Hkv, D, block, topk, q, k, v, idx, scale,
+                                    descale, out, None)
+
+
+def last():
+    return bst.lib().bsattn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dtype=7), 1, "dtype"),
+    (dict(N=500), 1, "multiple of block"),
+    (dict(topk=0), 1, "topk"),
+    (dict(topk=9), 1, "topk"),
+    (dict(Hq=3, Hkv=2), 1, "multiple of Hkv"),
+    (dict(Hkv=0), 1, "Hkv"),
+    (dict(B=-1), 1, "negative"),
+    (dict(D=96), 2, "D=96"),
+    (dict(block=32, N=512), 2, "block=32"),
+    (dict(q=None), 1, "null"),
+    (dict(k=ctypes.c_void_p(0x10008)), 1, "aligned"),
+    (dict(ws=None), 3, "workspace"),
+    (dict(wsb=16), 3, "workspace"),
+    (dict(ws=ctypes.c_void_p(0x10010)), 3, "aligned"),
+    (dict(N=64 * 2048, topk=3), 2, "nb=2048"),
+])
+def test_select_rejects(kw, status, msg):
+    assert sel(**kw) == status
+    assert msg in last()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(scale=float("nan")), 1, "scale"),
+    (dict(scale=0.0), 1, "scale"),
+    (dict(scale=-1.0), 1, "scale"),
+    (dict(dtype=2), 1, "descale"),
+    (dict(dtype=2, descale=(ctypes.c_float * 3)(1.0, 0.0, 1.0)), 1, "descale_qkv[1]"),
+    (dict(out=None), 1, "null"),
+    (dict(v=ctypes.c_void_p(0x10004)), 1, "aligned"),
+    (dict(topk=10), 1, "topk"),
+    (dict(N=96), 1, "multiple of block"),
+    (dict(D=32), 2, "D=32"),
+])
+def test_forward_rejects(kw, status, msg):
+    assert fwd(**kw) == status
+    assert msg in last()
+
+
+def test_empty_calls_launch_nothing():
+    # B == 0 or N == 0: checked, then nothing to do (no pointer is touched)
+    assert sel(B=0, q=None, k=None, idx=None, ws=None, wsb=0) == 0
+    assert sel(N=0, topk=0, q=None, k=None, idx=None, ws=None, wsb=0) == 0
+    assert fwd(B=0, q=None, k=None, v=None, idx=None, out=None) == 0
+    assert sel(N=0, topk=1) == 1          # topk must be 0 when nb == 0
+
+
+def test_workspace_bytes():
+    L = bst.lib()
+    n = L.bsattn_select_workspace_bytes(2, 8192, 16, 4, 64, 64)
+    assert n == 2 * 16 * 128 * 64 * 4 + 2 * 4 * 128 * 64 * 4
+    assert L.bsattn_select_workspace_bytes(0, 8192, 16, 4, 64, 64) == 0
+    assert L.bsattn_select_workspace_bytes(1, 100, 1, 1, 64, 64) == 0
+    assert "workspace" in last()
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 128, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        bst.select(x, x, 64, 1)

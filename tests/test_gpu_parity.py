@@ -1,0 +1,228 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on seeded inputs.
+
+Every test here runs on an MI355X; each prints the case it is about to run first.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_top_amd as bst
+from block_sparse_top_amd import synthetic as syn
+import oracle.bsattn_oracle as O
+from tests.parity import check_idx, check_out, dtype_name, out_errors, to_f64, TOL
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def make(B, N, Hq, Hkv, D, dtype, index=11):
+    q, k, v, ds = syn.iid_inputs(B, N, Hq, Hkv, D, dtype, index=index, device=DEV)
+    return q, k, v, ds
+
+
+def oracle_inputs(q, k, v, ds):
+    return to_f64(q, ds[0]), to_f64(k, ds[1]), to_f64(v, ds[2])
+
+
+SHAPES = [
+    # B, N, Hq, Hkv, D, block, topk
+    (1, 512, 2, 2, 64, 64, 2),          # the tiny workload's shape
+    (2, 64 * 37, 3, 3, 64, 64, 7),      # ragged: nb=37 (not a multiple of 16 rows or 64 lanes)
+    (1, 128 * 21, 6, 3, 128, 128, 5),   # GQA group 2, D=128, block 128, ragged tile count
+    (2, 64 * 100, 4, 1, 128, 64, 30),   # GQA group 4, D=128, block 64
+    (1, 128 * 40, 2, 2, 64, 128, 40),   # topk = nb (dense limit)
+    (3, 64 * 9, 2, 2, 64, 64, 1),       # topk = 1
+    (1, 64, 1, 1, 64, 64, 1),           # a single block
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("shape", SHAPES[:4], ids=str)
+def test_pool_and_select(dtype, shape):
+    B, N, Hq, Hkv, D, blk, topk = shape
+    say(f"[select] dtype={dtype} shape={shape}")
+    q, k, v, ds = make(B, N, Hq, Hkv, D, dtype)
+    idx, qbar, kbar = bst.select(q, k, blk, topk, return_pooled=True)
+    torch.cuda.synchronize()
+    # pooled values: the oracle pools the stored values (fp8: codes without descale)
+    qo = to_f64(q) if dtype != "fp8" else O.decode_e4m3(q.view(torch.uint8).cpu().numpy())
+    ko = to_f64(k) if dtype != "fp8" else O.decode_e4m3(k.view(torch.uint8).cpu().numpy())
+    pq, pk = O.pool(qo, blk), O.pool(ko, blk)
+    scale_q = np.abs(qo).max()
+    assert np.max(np.abs(qbar.cpu().numpy() - pq)) <= 2e-6 * scale_q
+    assert np.max(np.abs(kbar.cpu().numpy() - pk)) <= 2e-6 * np.abs(ko).max()
+    S = O.block_scores(pq, pk)
+    stats = check_idx(idx.cpu().numpy(), S, topk)
+    say("  ", stats)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=str)
+def test_forward(dtype, shape):
+    B, N, Hq, Hkv, D, blk, topk = shape
+    say(f"[forward] dtype={dtype} shape={shape}")
+    q, k, v, ds = make(B, N, Hq, Hkv, D, dtype, index=12)
+    idx = bst.select(q, k, blk, topk)
+    odt = torch.float32 if dtype == "f32" else torch.bfloat16
+    out = torch.full((B, N, Hq, D), float("nan"), dtype=odt, device=DEV)   # NaN prefill
+    bst.forward(q, k, v, idx, out=out)
+    torch.cuda.synchronize()
+    qo, ko, vo = oracle_inputs(q, k, v, ds)
+    gidx = idx.cpu().numpy()
+    check_idx(gidx, O.block_scores(O.pool(qo, blk), O.pool(ko, blk)), topk)
+    ref = O.attend_batched(qo, ko, vo, gidx, blk, 1.0 / math.sqrt(D))
+    err = check_out(out.float().cpu().numpy(), ref, dtype)
+    say("   max_abs, rel_l2 =", err)
+    if topk == N // blk:      # dense limit: also equal to dense attention
+        dense = O.dense_attention(qo, ko, vo, 1.0 / math.sqrt(D))
+        check_out(out.float().cpu().numpy(), dense, dtype)
+
+
+def test_tiny_workload_end_to_end():
+    w = syn.WORKLOADS["tiny_f32"]
+    say("[tiny] block_sparse_attention on", w)
+    q, k, v, ds, _ = syn.workload_inputs(w, device=DEV)
+    out, idx = bst.block_sparse_attention(q, k, v, w.block, w.ratio, return_idx=True)
+    torch.cuda.synchronize()
+    qo, ko, vo = oracle_inputs(q, k, v, ds)
+    ref, ridx = O.block_sparse_attention(qo, ko, vo, w.block, w.ratio)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    check_out(out.cpu().numpy(), ref, "f32")
+    bf = O.masked_attention_bruteforce(qo, ko, vo, ridx, w.block, 1 / math.sqrt(w.D))
+    check_out(out.cpu().numpy(), bf, "f32")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_exact_ties_lower_index_wins(dtype):
+    B, N, H, D, blk = 1, 64 * 40, 2, 64, 64
+    say(f"[ties] dtype={dtype}")
+    q, k, v, ds = make(B, N, H, H, D, dtype, index=13)
+    k = k.clone()
+    # duplicate key blocks: 31 <- 3, 17 <- 9, 39 <- 0
+    for dst, src in ((31, 3), (17, 9), (39, 0)):
+        k[:, dst * blk:(dst + 1) * blk] = k[:, src * blk:(src + 1) * blk]
+    for topk in (1, 5, 20, 39):
+        idx = bst.select(q, k, blk, topk).cpu().numpy().reshape(-1, topk)
+        for row in idx:
+            s = set(row.tolist())
+            for dst, src in ((31, 3), (17, 9), (39, 0)):
+                assert dst not in s or src in s
+    # q == 0: every score is 0, the lowest topk blocks are chosen
+    z = torch.zeros_like(q)
+    idx = bst.select(z, k, blk, 6).cpu().numpy()
+    assert np.all(idx == np.arange(6))
+
+
+def test_zero_query_closed_form():
+    B, N, H, D, blk, topk = 1, 64 * 12, 2, 64, 64, 4
+    say("[zero q] closed form")
+    q, k, v, ds = make(B, N, H, H, D, "bf16", index=14)
+    z = torch.zeros_like(q)
+    idx = bst.select(z, k, blk, topk)
+    out = bst.forward(z, k, v, idx)
+    torch.cuda.synchronize()
+    assert np.all(idx.cpu().numpy() == np.arange(topk))
+    vo = to_f64(v)
+    ref = vo[:, :topk * blk].mean(axis=1)[:, None]        # mean of V over blocks 0..topk-1
+    check_out(out.float().cpu().numpy(), np.broadcast_to(ref, out.shape), "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_deterministic(dtype):
+    say(f"[determinism] {dtype}")
+    q, k, v, ds = make(2, 64 * 64, 4, 2, 64, dtype, index=15)
+    a_idx = bst.select(q, k, 64, 19)
+    a = bst.forward(q, k, v, a_idx)
+    b_idx = bst.select(q, k, 64, 19)
+    b = bst.forward(q, k, v, b_idx)
+    torch.cuda.synchronize()
+    assert torch.equal(a_idx, b_idx)
+    assert torch.equal(a.view(torch.int16) if dtype == "bf16" else a.view(torch.int32),
+                       b.view(torch.int16) if dtype == "bf16" else b.view(torch.int32))
+
+
+def test_invalid_index_poisons_only_its_rows():
+    say("[invalid idx]")
+    B, N, H, D, blk, topk = 1, 64 * 8, 2, 64, 64, 3
+    q, k, v, ds = make(B, N, H, H, D, "bf16", index=16)
+    idx = bst.select(q, k, blk, topk)
+    bad = idx.clone()
+    bad[0, 1, 5, 2] = 1000
+    out = bst.forward(q, k, v, bad)
+    ref = bst.forward(q, k, v, idx)
+    torch.cuda.synchronize()
+    o, r = out.float(), ref.float()
+    assert torch.isnan(o[0, 5 * blk:6 * blk, 1]).all()
+    mask = torch.ones_like(o, dtype=torch.bool)
+    mask[0, 5 * blk:6 * blk, 1] = False
+    assert torch.equal(o[mask], r[mask])
+
+
+def test_mutated_indices_fail_parity():
+    """Negative control: the output check catches one dropped or swapped block."""
+    say("[mutation]")
+    B, N, H, D, blk, topk = 1, 64 * 16, 2, 64, 64, 5
+    q, k, v, ds = make(B, N, H, H, D, "bf16", index=17)
+    idx = bst.select(q, k, blk, topk)
+    out = bst.forward(q, k, v, idx).float().cpu().numpy()
+    qo, ko, vo = oracle_inputs(q, k, v, ds)
+    gidx = idx.cpu().numpy()
+    swapped = gidx.copy()
+    swapped[0, 0, 3, 1] = next(j for j in range(N // blk) if j not in gidx[0, 0, 3])
+    ref_bad = O.attend_batched(qo, ko, vo, swapped, blk, 1 / math.sqrt(D))
+    with pytest.raises(AssertionError):
+        check_out(out, ref_bad, "bf16")
+    dropped = O.attend(qo, ko, vo, gidx[..., :-1], blk, 1 / math.sqrt(D))
+    with pytest.raises(AssertionError):
+        check_out(out, dropped, "bf16")
+
+
+def test_empty_batch():
+    say("[empty]")
+    q = torch.empty(0, 128, 2, 64, dtype=torch.bfloat16, device=DEV)
+    idx = bst.select(q, q, 64, 1)
+    assert idx.shape == (0, 2, 2, 1)
+    out = bst.forward(q, q, q, idx)
+    assert out.shape == (0, 128, 2, 64)
+
+
+@pytest.mark.slow
+def test_sparseformer_full_size():
+    """The page's benchmark shape at full size: every selection row vs the oracle, and
+    sampled query blocks of the output."""
+    w = syn.WORKLOADS["sparseformer_n8192_bf16"]
+    say("[full size]", w)
+    q, k, v, ds, _ = syn.workload_inputs(w, device=DEV)
+    topk = O.topk_count(w.ratio, w.nb)
+    idx = bst.select(q, k, w.block, topk)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    bst.forward(q, k, v, idx, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+    say("  gpu done; oracle selection")
+    qo, ko = to_f64(q), to_f64(k)
+    S = O.block_scores(O.pool(qo, w.block), O.pool(ko, w.block))
+    del qo, ko
+    gidx = idx.cpu().numpy()
+    stats = check_idx(gidx, S, topk)
+    say("  ", stats)
+    rows = syn.sample_rows(48, w.B * w.Hq * w.nb, w.index)
+    picks = [(r // (w.Hq * w.nb), (r // w.nb) % w.Hq, r % w.nb) for r in rows]
+    bsel = sorted({b for b, _, _ in picks})
+    for b in bsel:
+        qb, kb, vb = (to_f64(x[b:b + 1]) for x in (q, k, v))
+        mine = [(0, h, i) for bb, h, i in picks if bb == b]
+        ref = O.attend(qb, kb, vb, gidx[b:b + 1], w.block, 1 / math.sqrt(w.D), rows=mine)
+        got = out[b:b + 1].float().cpu().numpy()
+        for (_, h, i) in mine:
+            sl = (0, slice(i * w.block, (i + 1) * w.block), h)
+            check_out(got[sl], ref[sl], "bf16")
+    say("  sampled", len(picks), "query blocks ok")
