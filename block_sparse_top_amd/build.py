@@ -26,6 +26,8 @@ CFLAGS = [
     "-Wno-unused-function",
     # no packed-fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results and accumulators in ordinary VGPRs: no AGPR <-> VGPR copies in the loops
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

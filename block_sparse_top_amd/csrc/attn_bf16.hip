@@ -5,46 +5,58 @@
 // scale 1/sqrt(D); MSA page ("从M2.7到M3：多模态模型稀疏注意力架构设计与实现全解析") §2.1:
 // Softmax(Mask(Q K^T / sqrt(d_k))) V with a block mask, §2.2: full attention inside the chosen
 // blocks, §3.1: GQA. The softmax is exact: it is evaluated online over the k selected key
-// blocks with a running maximum and normaliser in fp32.
+// blocks with a reference maximum and a normaliser in fp32.
 //
 // One work-group owns one query block (BLK rows) of one (batch, query head); each of its
-// BLK/32 waves owns 32 query rows. Per selected key block the work-group stages K [BLK][D]
-// row-major and V transposed [D][BLK] in LDS (two buffers: the next block's global loads are
-// issued before the current block's math), then each wave computes
+// BLK/32 waves owns 32 query rows. Per selected key block the work-group stages K and V
+// [BLK][D] row-major in LDS (two buffers: the next block's global loads are issued before the
+// current block's math), then each wave computes
 //   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = its Q^T in registers)
-//   P^T = exp2(c*S^T - c*m)   (c = scale*log2(e), m = running row max)
-//   O^T += V^T P^T (A = V^T rows from LDS, B = P^T straight from the S^T accumulators)
-// Working on the transposed products keeps every query's 64 key scores in two lanes (l and
-// l^32): the row max needs one cross-lane exchange, the rescale factor is one value per lane,
-// and the score accumulators are already in the B-operand layout of the next product (the
-// 16 k-slots of a step are matched to keys {4h..4h+3, 8+4h..8+4h+3} on both operands).
-// The running max is only moved when a block's max exceeds it by more than 2^8 in the
-// exp2 domain, so the O rescale is skipped for almost every block; the final O/l is exact
-// either way because O and l always use the same reference maximum.
+//   P^T = exp2(c*S^T - c*m)   (c = scale*log2(e), m = reference max of the query row)
+//   O^T += V^T P^T (A = V^T via ds_read_b64_tr_b16 transpose reads of the row-major V tile,
+//                   B = P^T built straight from the S^T accumulators)
+// Working on the transposed products keeps each query's key scores in two lanes (l, l^32),
+// and the score accumulators are already in the B-operand layout of the next product: the 16
+// k-slots of a step are matched to keys {4h..4h+3, 8+4h..8+4h+3} on both operands.
+//
+// Reference maximum: it is the query row's max over the first selected block and is moved
+// only when a later block would make some weight exp2(c*s - c*m) exceed 2^32 (checked on the
+// per-lane block sum). Then the row max is recomputed, O and l are rescaled and the block's
+// weights are recomputed. Because O and l always use the same reference, O/l is exact; the
+// common case needs no max, no rescale and no cross-lane traffic. The normaliser is summed
+// from the bf16-rounded weights (v_dot2c_f32_bf16), i.e. from exactly the weights the PV
+// product uses.
 #include "common.h"
 #include "launch.h"
 
 namespace bsattn {
 namespace {
 
-constexpr float kLazyRescaleLog2 = 8.0f;
+constexpr float kRescaleSum = 4294967296.0f;    // 2^32
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <int D, int BLK>
 struct Cfg {
   static constexpr int NW = BLK / 32;          // waves (32 query rows each)
   static constexpr int NT = NW * kWave;        // threads
-  static constexpr int KS = D + 8;             // K row stride in LDS (bf16 elements)
-  static constexpr int VS = BLK + 4;           // V^T row stride in LDS (bf16 elements)
+  static constexpr int KS = D + 8;             // K row stride in LDS (bf16): b128 reads
+  static constexpr int VS = D + 16;            // V row stride in LDS (bf16): transpose reads
   static constexpr int K_ELEMS = BLK * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int LDS_BYTES = 2 * (K_ELEMS + V_ELEMS) * 2;
-  static constexpr int KCH = D / 16;           // 16-byte K chunks per thread per block
-  static constexpr int VU = D / 32;            // V units (2 rows x 16 bytes) per thread
+  static constexpr int V_ELEMS = BLK * VS;
+  static constexpr int CH = BLK * D / 8 / NT;  // 16-byte chunks per thread per tile (= D/16)
   static constexpr int NKT = BLK / 32;         // 32-key sub-tiles per block
   static constexpr int NS = D / 16;            // k-steps of Q K^T
   static constexpr int NDT = D / 32;           // 32-row d tiles of O^T
   static constexpr int NPS = BLK / 16;         // k-steps of V^T P^T
 };
+
+__device__ __forceinline__ s16x4 ds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) void*)(p));
+}
 
 template <int D, int BLK>
 __global__ __launch_bounds__(BLK * 2) void attn_bf16_kernel(
@@ -54,7 +66,7 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16_kernel(
   using C = Cfg<D, BLK>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (C::K_ELEMS + C::V_ELEMS)];
   uint16_t* Ks = lds;                          // [2][BLK][KS]
-  uint16_t* Vt = lds + 2 * C::K_ELEMS;         // [2][D][VS]
+  uint16_t* Vs = lds + 2 * C::K_ELEMS;         // [2][BLK][VS]
 
   // tile order: (b, kv head, head within group, query block); blocks reading the same K/V
   // are consecutive and land on one XCD
@@ -84,60 +96,48 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16_kernel(
   const uint16_t* kbase0 = k + (int64_t)b * N * krs + (int64_t)g * D;
   const uint16_t* vbase0 = v + (int64_t)b * N * krs + (int64_t)g * D;
 
-  u32x4 kreg[C::KCH];
-  u32x4 vreg[C::VU][2];
+  // staging: thread owns 16-byte chunks ch = tid + NT*x of the tile, row ch/(D/8); the
+  // per-lane element offsets inside a tile are fixed, only the (uniform) tile base moves
+  u32x4 kreg[C::CH], vreg[C::CH];
+  uint32_t goff[C::CH];                        // byte offsets (tile < 2^32 bytes)
+#pragma unroll
+  for (int x = 0; x < C::CH; ++x) {
+    const int ch = tid + C::NT * x;
+    goff[x] = (uint32_t)(((ch / (D / 8)) * krs + (ch % (D / 8)) * 8) * 2);
+  }
   bool bad = false;
-
   auto load_tile = [&](int kb) {
     if ((unsigned)kb >= (unsigned)nb) { bad = true; kb = 0; }
-    const uint16_t* kb_ptr = kbase0 + (int64_t)kb * BLK * krs;
-    const uint16_t* vb_ptr = vbase0 + (int64_t)kb * BLK * krs;
+    const char* kt = (const char*)(kbase0 + (int64_t)kb * BLK * krs);
+    const char* vt = (const char*)(vbase0 + (int64_t)kb * BLK * krs);
 #pragma unroll
-    for (int x = 0; x < C::KCH; ++x) {
-      const int ch = tid + C::NT * x;
-      const int r = ch / (D / 8), dc = ch % (D / 8);
-      kreg[x] = *(const u32x4*)(kb_ptr + r * krs + dc * 8);
-    }
-#pragma unroll
-    for (int x = 0; x < C::VU; ++x) {
-      const int u = tid + C::NT * x;
-      const int m = u % (BLK / 2), dc = u / (BLK / 2);
-      vreg[x][0] = *(const u32x4*)(vb_ptr + (2 * m) * krs + dc * 8);
-      vreg[x][1] = *(const u32x4*)(vb_ptr + (2 * m + 1) * krs + dc * 8);
+    for (int x = 0; x < C::CH; ++x) {
+      kreg[x] = *(const u32x4*)(kt + goff[x]);
+      vreg[x] = *(const u32x4*)(vt + goff[x]);
     }
   };
   auto store_tile = [&](int buf) {
-    uint16_t* ks = Ks + buf * C::K_ELEMS;
-    uint32_t* vt = (uint32_t*)(Vt + buf * C::V_ELEMS);
 #pragma unroll
-    for (int x = 0; x < C::KCH; ++x) {
+    for (int x = 0; x < C::CH; ++x) {
       const int ch = tid + C::NT * x;
       const int r = ch / (D / 8), dc = ch % (D / 8);
-      *(u32x4*)(ks + r * C::KS + dc * 8) = kreg[x];
-    }
-#pragma unroll
-    for (int x = 0; x < C::VU; ++x) {
-      const int u = tid + C::NT * x;
-      const int m = u % (BLK / 2), dc = u / (BLK / 2);
-      const u32x4 a = vreg[x][0], bb = vreg[x][1];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // (v[2m][d], v[2m+1][d]) for d = 8dc + 2w and 8dc + 2w + 1
-        const uint32_t lo = __builtin_amdgcn_perm(bb[w], a[w], 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(bb[w], a[w], 0x07060302u);
-        vt[(dc * 8 + 2 * w) * (C::VS / 2) + m] = lo;
-        vt[(dc * 8 + 2 * w + 1) * (C::VS / 2) + m] = hi;
-      }
+      *(u32x4*)(Ks + buf * C::K_ELEMS + r * C::KS + dc * 8) = kreg[x];
+      *(u32x4*)(Vs + buf * C::V_ELEMS + r * C::VS + dc * 8) = vreg[x];
     }
   };
+
+  // transpose-read address of this lane inside a V tile: in each 16-lane group the lane
+  // 4e+t names row (key) 4*half + e and columns d0 + 4t, d0 = 16*((lane/16)&1)
+  const int tr_off = (4 * half + ((lane & 15) >> 2)) * C::VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   f32x16 oacc[C::NDT];
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-  float m_used = -__builtin_inff();            // reference max of this lane's query row
+  float mc = 0.f;                              // c * reference max of this lane's query row
   float lsum = 0.f;                            // this lane's share of the normaliser
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   load_tile(myidx[0]);
   store_tile(0);
@@ -162,50 +162,59 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16_kernel(
       }
     }
 
-    // online softmax (lane pair l, l^32 shares one query row)
-    float mt = sacc[0][0];
+    auto row_max_c = [&]() {                   // c * max over this block of the lane's row
+      float mt = sacc[0][0];
 #pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt)
+      for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kt][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool grow = (mt - m_used) * c > kLazyRescaleLog2;
-    if (__ballot(grow)) {
-      const float m_new = fmaxf(m_used, mt);
-      const float alpha = __builtin_amdgcn_exp2f((m_used - m_new) * c);
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kt][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      return mt * c;
+    };
+    if (t == 0) mc = row_max_c();
+
+    // weights as packed bf16 pairs, grouped per PV k-step; per-lane block sum
+    uint32_t pw[C::NPS][4];
+    float bsum = 0.f;
+    auto weights = [&]() {
+      bsum = 0.f;
+#pragma unroll
+      for (int s = 0; s < C::NPS; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + 2 * e], c, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + 2 * e + 1], c, -mc));
+          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+          pw[s][e] = __builtin_bit_cast(uint32_t, pp);
+          bsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, bsum, false);
+        }
+    };
+    weights();
+    if (__ballot(bsum > kRescaleSum)) {        // rare: move the reference max up
+      const float m_new = fmaxf(mc, row_max_c());
+      const float alpha = __builtin_amdgcn_exp2f(mc - m_new);
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      m_used = m_new;
+      mc = m_new;
+      weights();
     }
-    const float mc = m_used * c;
-#pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], c, -mc));
-        lsum += p;
-        sacc[kt][r] = p;
-      }
+    lsum += bsum;
 
     // O^T += V^T P^T
-    const uint16_t* vt = Vt + buf * C::V_ELEMS;
+    const uint16_t* vs = Vs + buf * C::V_ELEMS + tr_off;
 #pragma unroll
     for (int s = 0; s < C::NPS; ++s) {
-      const f32x16& pa = sacc[s >> 1];
-      const int o8 = 8 * (s & 1);
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pa[o8 + e];
+      const u32x4 pv = {pw[s][0], pw[s][1], pw[s][2], pw[s][3]};
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt) {
-        const uint16_t* row = vt + (32 * dt + l32) * C::VS + 16 * s + 4 * half;
-        const u32x2 lo = *(const u32x2*)(row);
-        const u32x2 hi = *(const u32x2*)(row + 8);
-        const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb,
+        const s16x4 lo = ds_read_tr16(vs + (16 * s) * C::VS + 32 * dt);
+        const s16x4 hi = ds_read_tr16(vs + (16 * s + 8) * C::VS + 32 * dt);
+        const s16x4 a8[2] = {lo, hi};
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb,
                                                            oacc[dt], 0, 0, 0);
       }
     }
