@@ -7,17 +7,26 @@
 // blocks, §3.1: GQA. The softmax is exact: it is evaluated online over the k selected key
 // blocks with a reference maximum and a normaliser in fp32.
 //
-// One work-group owns one query block (BLK rows) of one (batch, query head); each of its
-// BLK/32 waves owns 32 query rows. Per selected key block the work-group stages K and V
-// [BLK][D] row-major in LDS (two buffers: the next block's global loads are issued before the
-// current block's math), then each wave computes
-//   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = its Q^T in registers)
+// Work split: one work-group owns one query block (BLK rows) of one (batch, query head); each
+// of its waves owns QW query rows (QW = 64 for D = 64, 32 for D = 128), i.e. QW/32 column
+// tiles of the 32x32 MFMA. Per selected key block each wave computes
+//   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q^T in registers)
 //   P^T = exp2(c*S^T - c*m)   (c = scale*log2(e), m = reference max of the query row)
 //   O^T += V^T P^T (A = V^T via ds_read_b64_tr_b16 transpose reads of the row-major V tile,
 //                   B = P^T built straight from the S^T accumulators)
+// Each A operand read from LDS feeds all QW/32 column tiles of the wave.
 // Working on the transposed products keeps each query's key scores in two lanes (l, l^32),
 // and the score accumulators are already in the B-operand layout of the next product: the 16
 // k-slots of a step are matched to keys {4h..4h+3, 8+4h..8+4h+3} on both operands.
+//
+// Data movement: K and V tiles go from HBM/L2 straight into LDS with global_load_lds_dwordx4
+// (lane l of one instruction fills bytes [16l, 16l+16) of a 1 KiB LDS span; the lane fetches
+// whichever 16-byte chunk belongs there). One LDS buffer per tensor: the wave reads all K
+// operands of block t into registers, then starts the K transfer of block t+1 and computes
+// S^T and the softmax while it flies; V likewise before the PV product. The 16-byte chunk c
+// of tile row r sits at chunk position c ^ f(r), f(r) = 2(r&3) + ((r>>2)&1), which makes both
+// the row reads of K (8 rows, one chunk) and the transpose reads of V (4 rows, 2 chunks) hit
+// all 32 banks once.
 //
 // Reference maximum: it is the query row's max over the first selected block and is moved
 // only when a later block would make some weight exp2(c*s - c*m) exceed 2^32 (checked on the
@@ -36,37 +45,54 @@ constexpr float kRescaleSum = 4294967296.0f;    // 2^32
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_cvoid;
 
 template <int D, int BLK>
 struct Cfg {
-  static constexpr int NW = BLK / 32;          // waves (32 query rows each)
+  static constexpr int QW = D == 64 ? 64 : 32;  // query rows per wave
+  static constexpr int QC = QW / 32;           // 32-query column tiles per wave
+  static constexpr int NW = BLK / QW;          // waves
   static constexpr int NT = NW * kWave;        // threads
-  static constexpr int KS = D + 8;             // K row stride in LDS (bf16): b128 reads
-  static constexpr int VS = D + 16;            // V row stride in LDS (bf16): transpose reads
-  static constexpr int K_ELEMS = BLK * KS;
-  static constexpr int V_ELEMS = BLK * VS;
-  static constexpr int CH = BLK * D / 8 / NT;  // 16-byte chunks per thread per tile (= D/16)
+  static constexpr int TILE = BLK * D * 2;     // bytes of one K or V tile
+  static constexpr int DMA = TILE / 1024 / NW; // 1 KiB transfers per tile per wave
   static constexpr int NKT = BLK / 32;         // 32-key sub-tiles per block
   static constexpr int NS = D / 16;            // k-steps of Q K^T
   static constexpr int NDT = D / 32;           // 32-row d tiles of O^T
   static constexpr int NPS = BLK / 16;         // k-steps of V^T P^T
+  static_assert(DMA * NW * 1024 == TILE, "tile must split into whole 1 KiB transfers");
 };
 
-__device__ __forceinline__ s16x4 ds_read_tr16(const uint16_t* p) {
+// vmcnt-only waits (expcnt and lgkmcnt left free), gfx9 s_waitcnt encoding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
+// chunk position of logical 16-byte chunk c in tile row r
+__device__ __forceinline__ int swz(int r, int c) {
+  const int f = 2 * (r & 3) + ((r >> 2) & 1);
+  return (c & ~7) | ((c & 7) ^ f);
+}
+
+__device__ __forceinline__ s16x4 ds_read_tr16(const char* lds_bytes) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(__attribute__((address_space(3))) void*)(p));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_void*)(lds_bytes));
 }
 
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) void attn_bf16_kernel(
+__global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
     int64_t N, int Hq, int Hkv, int nb, int topk, float c, uint32_t total_tiles) {
   using C = Cfg<D, BLK>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (C::K_ELEMS + C::V_ELEMS)];
-  uint16_t* Ks = lds;                          // [2][BLK][KS]
-  uint16_t* Vs = lds + 2 * C::K_ELEMS;         // [2][BLK][VS]
+  __shared__ __attribute__((aligned(1024))) char lds[2 * C::TILE];
+  char* Kl = lds;                              // [BLK][D] bf16, swizzled chunks
+  char* Vl = lds + C::TILE;
 
   // tile order: (b, kv head, head within group, query block); blocks reading the same K/V
   // are consecutive and land on one XCD
@@ -85,158 +111,203 @@ __global__ __launch_bounds__(BLK * 2) void attn_bf16_kernel(
   const int64_t qrs = (int64_t)Hq * D;         // token stride of q/out
   const int64_t krs = (int64_t)Hkv * D;        // token stride of k/v
 
-  // Q^T as B operand: lane holds q[row = 32*wave + l32][d = 16s + 8*half .. +7]
-  const int64_t qrow = (int64_t)b * N + (int64_t)i * BLK + 32 * wave + l32;
-  bf16x8 qf[C::NS];
+  // Q^T as B operands: lane holds q[row = QW*wave + 32*qc + l32][d = 16s + 8*half .. +7]
+  const int64_t qrow0 = (int64_t)b * N + (int64_t)i * BLK + C::QW * wave + l32;
+  bf16x8 qf[C::QC][C::NS];
 #pragma unroll
-  for (int s = 0; s < C::NS; ++s)
-    qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q + qrow * qrs + (int64_t)h * D + 16 * s + 8 * half));
+  for (int qc = 0; qc < C::QC; ++qc)
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s)
+      qf[qc][s] = __builtin_bit_cast(
+          bf16x8, *(const u32x4*)(q + (qrow0 + 32 * qc) * qrs + (int64_t)h * D + 16 * s + 8 * half));
 
   const int32_t* myidx = idx + (((int64_t)b * Hq + h) * nb + i) * topk;
-  const uint16_t* kbase0 = k + (int64_t)b * N * krs + (int64_t)g * D;
-  const uint16_t* vbase0 = v + (int64_t)b * N * krs + (int64_t)g * D;
+  const char* kbase0 = (const char*)(k + (int64_t)b * N * krs + (int64_t)g * D);
+  const char* vbase0 = (const char*)(v + (int64_t)b * N * krs + (int64_t)g * D);
 
-  // staging: thread owns 16-byte chunks ch = tid + NT*x of the tile, row ch/(D/8); the
-  // per-lane element offsets inside a tile are fixed, only the (uniform) tile base moves
-  u32x4 kreg[C::CH], vreg[C::CH];
-  uint32_t goff[C::CH];                        // byte offsets (tile < 2^32 bytes)
+  // DMA source byte offsets of this lane inside a tile (fixed), destination spans uniform
+  uint32_t goff[C::DMA];
 #pragma unroll
-  for (int x = 0; x < C::CH; ++x) {
-    const int ch = tid + C::NT * x;
-    goff[x] = (uint32_t)(((ch / (D / 8)) * krs + (ch % (D / 8)) * 8) * 2);
+  for (int x = 0; x < C::DMA; ++x) {
+    const int pos = (wave * C::DMA + x) * 64 + lane;         // chunk position in the tile
+    const int r = pos / (D / 8), p = pos % (D / 8);
+    goff[x] = (uint32_t)((r * krs + swz(r, p) * 8) * 2);
   }
   bool bad = false;
-  auto load_tile = [&](int kb) {
+  auto tile_base = [&](int kb) -> int64_t {
     if ((unsigned)kb >= (unsigned)nb) { bad = true; kb = 0; }
-    const char* kt = (const char*)(kbase0 + (int64_t)kb * BLK * krs);
-    const char* vt = (const char*)(vbase0 + (int64_t)kb * BLK * krs);
-#pragma unroll
-    for (int x = 0; x < C::CH; ++x) {
-      kreg[x] = *(const u32x4*)(kt + goff[x]);
-      vreg[x] = *(const u32x4*)(vt + goff[x]);
-    }
+    return (int64_t)kb * BLK * krs * 2;
   };
-  auto store_tile = [&](int buf) {
+  auto dma = [&](const char* src_base, char* dst) {
 #pragma unroll
-    for (int x = 0; x < C::CH; ++x) {
-      const int ch = tid + C::NT * x;
-      const int r = ch / (D / 8), dc = ch % (D / 8);
-      *(u32x4*)(Ks + buf * C::K_ELEMS + r * C::KS + dc * 8) = kreg[x];
-      *(u32x4*)(Vs + buf * C::V_ELEMS + r * C::VS + dc * 8) = vreg[x];
-    }
+    for (int x = 0; x < C::DMA; ++x)
+      __builtin_amdgcn_global_load_lds((global_cvoid*)(src_base + goff[x]),
+                                       (lds_void*)(dst + (wave * C::DMA + x) * 1024), 16, 0, 0);
   };
 
-  // transpose-read address of this lane inside a V tile: in each 16-lane group the lane
-  // 4e+t names row (key) 4*half + e and columns d0 + 4t, d0 = 16*((lane/16)&1)
-  const int tr_off = (4 * half + ((lane & 15) >> 2)) * C::VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // LDS read offsets of this lane
+  int koff[C::NS];                             // K row l32, chunk 2s+half (+ 32*kt rows)
+#pragma unroll
+  for (int s = 0; s < C::NS; ++s) koff[s] = l32 * D * 2 + 16 * swz(l32, 2 * s + half);
+  // V transpose reads: in each 16-lane group lane 4e+t names row 4*half+e (+16s, +8) and
+  // columns 32dt + 16*((lane>>4)&1) + 4t, i.e. chunk 4dt + 2*((lane>>4)&1) + t/2, half t&1
+  int voff[C::NDT];
+  {
+    const int e = (lane & 15) >> 2, r = 4 * half + e;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+      const int ch = 4 * dt + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+      voff[dt] = r * D * 2 + 16 * swz(r, ch) + 8 * (lane & 1);
+    }
+  }
 
-  f32x16 oacc[C::NDT];
+  f32x16 oacc[C::NDT][C::QC];
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-  float mc = 0.f;                              // c * reference max of this lane's query row
-  float lsum = 0.f;                            // this lane's share of the normaliser
+    for (int qc = 0; qc < C::QC; ++qc)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][qc][r] = 0.f;
+  float mc[C::QC], lsum[C::QC];               // c * reference max; this lane's normaliser share
+#pragma unroll
+  for (int qc = 0; qc < C::QC; ++qc) { mc[qc] = 0.f; lsum[qc] = 0.f; }
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  load_tile(myidx[0]);
-  store_tile(0);
-  __syncthreads();
+  {
+    const int64_t tb = tile_base(myidx[0]);
+    dma(kbase0 + tb, Kl);
+    dma(vbase0 + tb, Vl);
+  }
 
   for (int t = 0; t < topk; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < topk) load_tile(myidx[t + 1]);
+    const bool more = t + 1 < topk;
+    const int64_t tb_next = more ? tile_base(myidx[t + 1]) : 0;
 
-    // S^T = K Q^T for this wave's 32 queries
-    const uint16_t* ks = Ks + buf * C::K_ELEMS;
-    f32x16 sacc[C::NKT];
+    // ---- K(t): wait for this wave's share (V(t) may still fly), then the whole work-group
+    wait_vmcnt<C::DMA>();
+    if (C::NW > 1) __syncthreads();
+    bf16x8 ka[C::NKT][C::NS];
 #pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt) {
+    for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+      for (int s = 0; s < C::NS; ++s)
+        ka[kt][s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kl + kt * 32 * D * 2 + koff[s]));
+    wait_lgkmcnt0();
+    if (C::NW > 1) __syncthreads();
+    if (more) dma(kbase0 + tb_next, Kl);
+
+    // ---- S^T = K Q^T
+    f32x16 sacc[C::NKT][C::QC];
 #pragma unroll
-      for (int s = 0; s < C::NS; ++s) {
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, *(const u32x4*)(ks + (32 * kt + l32) * C::KS + 16 * s + 8 * half));
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
+    for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+      for (int qc = 0; qc < C::QC; ++qc) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kt][qc][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s)
+          sacc[kt][qc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kt][s], qf[qc][s], sacc[kt][qc], 0, 0, 0);
       }
-    }
 
-    auto row_max_c = [&]() {                   // c * max over this block of the lane's row
-      float mt = sacc[0][0];
+    // ---- softmax weights (lane pair l, l^32 shares one query row)
+    auto row_max_c = [&](int qc) {
+      float mt = sacc[0][qc][0];
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kt][r]);
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kt][qc][r]);
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       return mt * c;
     };
-    if (t == 0) mc = row_max_c();
-
-    // weights as packed bf16 pairs, grouped per PV k-step; per-lane block sum
-    uint32_t pw[C::NPS][4];
-    float bsum = 0.f;
-    auto weights = [&]() {
-      bsum = 0.f;
+    if (t == 0) {
+#pragma unroll
+      for (int qc = 0; qc < C::QC; ++qc) mc[qc] = row_max_c(qc);
+    }
+    uint32_t pw[C::QC][C::NPS][4];
+    float bsum[C::QC];
+    auto weights = [&](int qc) {
+      bsum[qc] = 0.f;
 #pragma unroll
       for (int s = 0; s < C::NPS; ++s)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + 2 * e], c, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[s >> 1][8 * (s & 1) + 2 * e + 1], c, -mc));
+          const float s0 = sacc[s >> 1][qc][8 * (s & 1) + 2 * e];
+          const float s1 = sacc[s >> 1][qc][8 * (s & 1) + 2 * e + 1];
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -mc[qc]));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -mc[qc]));
           const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-          pw[s][e] = __builtin_bit_cast(uint32_t, pp);
-          bsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, bsum, false);
+          pw[qc][s][e] = __builtin_bit_cast(uint32_t, pp);
+          bsum[qc] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, bsum[qc], false);
         }
     };
-    weights();
-    if (__ballot(bsum > kRescaleSum)) {        // rare: move the reference max up
-      const float m_new = fmaxf(mc, row_max_c());
-      const float alpha = __builtin_amdgcn_exp2f(mc - m_new);
-      lsum *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt)
+    for (int qc = 0; qc < C::QC; ++qc) weights(qc);
+    bool grow = false;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      mc = m_new;
-      weights();
-    }
-    lsum += bsum;
-
-    // O^T += V^T P^T
-    const uint16_t* vs = Vs + buf * C::V_ELEMS + tr_off;
+    for (int qc = 0; qc < C::QC; ++qc) grow |= bsum[qc] > kRescaleSum;
+    if (__ballot(grow)) {                      // rare: move the reference max up
 #pragma unroll
-    for (int s = 0; s < C::NPS; ++s) {
-      const u32x4 pv = {pw[s][0], pw[s][1], pw[s][2], pw[s][3]};
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
+      for (int qc = 0; qc < C::QC; ++qc) {
+        const float m_new = fmaxf(mc[qc], row_max_c(qc));
+        const float alpha = __builtin_amdgcn_exp2f(mc[qc] - m_new);
+        lsum[qc] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) {
-        const s16x4 lo = ds_read_tr16(vs + (16 * s) * C::VS + 32 * dt);
-        const s16x4 hi = ds_read_tr16(vs + (16 * s + 8) * C::VS + 32 * dt);
-        const s16x4 a8[2] = {lo, hi};
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb,
-                                                           oacc[dt], 0, 0, 0);
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][qc][r] *= alpha;
+        mc[qc] = m_new;
+        weights(qc);
       }
     }
+#pragma unroll
+    for (int qc = 0; qc < C::QC; ++qc) lsum[qc] += bsum[qc];
 
-    if (t + 1 < topk) store_tile(buf ^ 1);
-    __syncthreads();
+    // ---- V(t): wait (K(t+1) may still fly), read all V^T operands, then start V(t+1)
+    if (more) wait_vmcnt<C::DMA>(); else wait_vmcnt<0>();
+    if (C::NW > 1) __syncthreads();
+    bf16x8 va[C::NPS][C::NDT];
+#pragma unroll
+    for (int s = 0; s < C::NPS; ++s)
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt) {
+        const char* p = Vl + (16 * s) * D * 2 + voff[dt];
+        const s16x4 a8[2] = {ds_read_tr16(p), ds_read_tr16(p + 8 * D * 2)};
+        va[s][dt] = __builtin_bit_cast(bf16x8, a8);
+      }
+    wait_lgkmcnt0();
+    if (C::NW > 1) __syncthreads();
+    if (more) dma(vbase0 + tb_next, Vl);
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int s = 0; s < C::NPS; ++s)
+#pragma unroll
+      for (int qc = 0; qc < C::QC; ++qc) {
+        const u32x4 pv = {pw[qc][s][0], pw[qc][s][1], pw[qc][s][2], pw[qc][s][3]};
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+          oacc[dt][qc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s][dt], pb, oacc[dt][qc], 0, 0, 0);
+      }
   }
 
   // epilogue: O = O^T / l, bf16, 4 consecutive d per store
-  const float l_all = lsum + __shfl_xor(lsum, 32);
-  const float inv = bad ? __builtin_nanf("") : 1.0f / l_all;
-  uint16_t* orow = out + qrow * qrs + (int64_t)h * D;
 #pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt)
+  for (int qc = 0; qc < C::QC; ++qc) {
+    const float l_all = lsum[qc] + __shfl_xor(lsum[qc], 32);
+    const float inv = bad ? __builtin_nanf("") : 1.0f / l_all;
+    uint16_t* orow = out + (qrow0 + 32 * qc) * qrs + (int64_t)h * D;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d0 = 32 * dt + 8 * j + 4 * half;
-      u32x2 w;
-      w[0] = pack_bf16x2(oacc[dt][4 * j + 0] * inv, oacc[dt][4 * j + 1] * inv);
-      w[1] = pack_bf16x2(oacc[dt][4 * j + 2] * inv, oacc[dt][4 * j + 3] * inv);
-      *(u32x2*)(orow + d0) = w;
-    }
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * dt + 8 * j + 4 * half;
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[dt][qc][4 * j + 0] * inv, oacc[dt][qc][4 * j + 1] * inv);
+        w[1] = pack_bf16x2(oacc[dt][qc][4 * j + 2] * inv, oacc[dt][qc][4 * j + 3] * inv);
+        *(u32x2*)(orow + d0) = w;
+      }
+  }
 }
 
 template <int D, int BLK>
