@@ -90,9 +90,8 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
     int64_t N, int Hq, int Hkv, int nb, int topk, float c, uint32_t total_tiles) {
   using C = Cfg<D, BLK>;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * C::TILE];
-  char* Kl = lds;                              // [BLK][D] bf16, swizzled chunks
-  char* Vl = lds + C::TILE;
+  __shared__ __attribute__((aligned(1024))) char Kl[C::TILE];   // [BLK][D] bf16, swizzled
+  __shared__ __attribute__((aligned(1024))) char Vl[C::TILE];
 
   // tile order: (b, kv head, head within group, query block); blocks reading the same K/V
   // are consecutive and land on one XCD
@@ -138,11 +137,26 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
     if ((unsigned)kb >= (unsigned)nb) { bad = true; kb = 0; }
     return (int64_t)kb * BLK * krs * 2;
   };
+  // The transfers are issued from inline asm so that the compiler's wait-count pass, which
+  // cannot tell the K and V buffers apart, does not add full vmcnt(0) waits before every LDS
+  // read; the waits below are placed by hand (each wave issues exactly DMA transfers per tile
+  // and no other vector-memory instruction inside the loop).
+  static_assert(C::DMA == 8, "the transfer sequence below issues 8 spans of 1 KiB");
   auto dma = [&](const char* src_base, char* dst) {
-#pragma unroll
-    for (int x = 0; x < C::DMA; ++x)
-      __builtin_amdgcn_global_load_lds((global_cvoid*)(src_base + goff[x]),
-                                       (lds_void*)(dst + (wave * C::DMA + x) * 1024), 16, 0, 0);
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_void*)dst + wave * C::DMA * 1024);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %9\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %9\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %9\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %9\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %9\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %9\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, %9\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %8, %9"
+        :: "s"(lds0), "v"(goff[0]), "v"(goff[1]), "v"(goff[2]), "v"(goff[3]), "v"(goff[4]),
+           "v"(goff[5]), "v"(goff[6]), "v"(goff[7]), "s"(src_base)
+        : "memory", "m0", "scc");
   };
 
   // LDS read offsets of this lane
@@ -173,6 +187,12 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
   for (int qc = 0; qc < C::QC; ++qc) { mc[qc] = 0.f; lsum[qc] = 0.f; }
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
+  // Q must have landed before the first transfer: the hand-placed vmcnt waits in the loop
+  // count transfers only (the empty asm consumes the loaded registers here)
+#pragma unroll
+  for (int qc = 0; qc < C::QC; ++qc)
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) asm volatile("" ::"v"(qf[qc][s]));
   {
     const int64_t tb = tile_base(myidx[0]);
     dma(kbase0 + tb, Kl);
