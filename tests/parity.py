@@ -72,9 +72,13 @@ def out_errors(gpu_out: np.ndarray, ref: np.ndarray):
     return max_abs, rel_l2
 
 
-def check_out(gpu_out: np.ndarray, ref: np.ndarray, dt: str):
+def check_out(gpu_out: np.ndarray, ref: np.ndarray, dt: str, abs_scale: float = 1.0,
+              rel_scale: float = 1.0):
+    """abs_scale and rel_scale multiply the bounds. The bounds above are for N(0,1)-like
+    inputs (|out| ~ 0.03, |scores| ~ 10); tests with outputs of O(|v|) or scores of O(1e3),
+    whose fp32 dot products alone carry ~1e-4 relative error, pass larger factors."""
     assert not np.isnan(gpu_out).any(), "output has NaN (unwritten or invalid)"
     max_abs, rel_l2 = out_errors(gpu_out, ref)
     tol_abs, tol_rel = TOL[dt]
-    assert max_abs <= tol_abs and rel_l2 <= tol_rel, (max_abs, rel_l2)
+    assert max_abs <= tol_abs * abs_scale and rel_l2 <= tol_rel * rel_scale, (max_abs, rel_l2)
     return max_abs, rel_l2

@@ -86,6 +86,40 @@ def test_forward(dtype, shape):
         check_out(out.float().cpu().numpy(), dense, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", ["huge_first", "tiny_all", "huge_later"])
+def test_extreme_score_ranges(dtype, case):
+    """Scores far outside exp2's range: the softmax must still be the exact average
+    (covers the kernels' reference-maximum paths)."""
+    say(f"[extreme] {case} {dtype}")
+    B, N, H, D, blk, topk = 1, 64 * 16, 2, 64, 64, 6
+    g = torch.Generator().manual_seed(31)
+    q = torch.randn(B, N, H, D, generator=g)
+    k = torch.randn(B, N, H, D, generator=g)
+    v = torch.randn(B, N, H, D, generator=g)
+    if case == "huge_first":
+        q *= 60.0                                  # |scale*q.k| in the thousands
+    elif case == "tiny_all":
+        k += 10.0                                  # every key shares a large component ...
+        q = -3.0 + 0.1 * q                         # ... and every query points against it
+    else:
+        k[:, 9 * blk:10 * blk] *= 40.0             # one key block with huge scores
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q, k, v = (x.to(tdt).to(DEV) for x in (q, k, v))
+    idx = bst.select(q, k, blk, topk)
+    if case == "huge_later":                       # make block 9 a late member of every row
+        idx = torch.tensor([[0, 1, 2, 3, 4, 9]] * (H * (N // blk)), dtype=torch.int32,
+                           device=DEV).view(B, H, N // blk, topk)
+    out = bst.forward(q, k, v, idx)
+    torch.cuda.synchronize()
+    qo, ko, vo = to_f64(q), to_f64(k), to_f64(v)
+    ref = O.attend(qo, ko, vo, idx.cpu().numpy(), blk, 1 / math.sqrt(D))
+    # near one-hot softmax: outputs are O(|v|), so the max-abs bound scales with them
+    err = check_out(out.float().cpu().numpy(), ref, dtype, abs_scale=max(1.0, float(np.abs(ref).max())),
+                    rel_scale=10.0 if dtype == "f32" else 1.0)
+    say("   max_abs, rel_l2 =", err)
+
+
 def test_tiny_workload_end_to_end():
     w = syn.WORKLOADS["tiny_f32"]
     say("[tiny] block_sparse_attention on", w)
