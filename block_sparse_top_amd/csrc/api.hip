@@ -113,11 +113,12 @@ int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int b
   float* kbar = (float*)((char*)workspace + pooled_q_bytes(B, N, Hq, D, block));
   hipStream_t s = (hipStream_t)stream;
   const int kind = dtype == BSATTN_F32 ? 0 : dtype == BSATTN_BF16 ? 1 : 2;
-  st = hip_status(bsattn::launch_pool(kind, B, N, Hq, Hkv, D, block, q, k, qbar, kbar, s),
-                  "pool launch");
+  st = hip_status(bsattn::launch_pool(kind, 2, B, N, Hq, Hkv, D, block, q, k, qbar, kbar, s),
+                  "key pool launch");
   if (st != BSATTN_OK) return st;
-  return hip_status(bsattn::launch_score_select(B, Hq, Hkv, nb, D, topk, qbar, kbar, idx, s),
-                    "score/select launch");
+  return hip_status(bsattn::launch_pool_score_select(kind, B, N, Hq, Hkv, D, block, topk, q,
+                                                     qbar, kbar, idx, s),
+                    "query pool/score/select launch");
 }
 
 int bsattn_forward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,

@@ -51,4 +51,35 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t w, uint32_t total) {
   return (w % kXcd) * per + (w / kXcd);
 }
 
+// Storage kinds: 0 fp32, 1 bf16, 2 OCP fp8 e4m3. Vec<KIND>: elements per 16-byte vector and
+// their fp32 values added into an accumulator array.
+template <int KIND> struct Vec;
+template <> struct Vec<0> {            // fp32
+  static constexpr int E = 4;
+  __device__ static void add(const u32x4& w, float* a) {
+    a[0] += __uint_as_float(w.x); a[1] += __uint_as_float(w.y);
+    a[2] += __uint_as_float(w.z); a[3] += __uint_as_float(w.w);
+  }
+};
+template <> struct Vec<1> {            // bf16
+  static constexpr int E = 8;
+  __device__ static void add(const u32x4& w, float* a) {
+    a[0] += bf16lo(w.x); a[1] += bf16hi(w.x); a[2] += bf16lo(w.y); a[3] += bf16hi(w.y);
+    a[4] += bf16lo(w.z); a[5] += bf16hi(w.z); a[6] += bf16lo(w.w); a[7] += bf16hi(w.w);
+  }
+};
+template <> struct Vec<2> {            // OCP fp8 e4m3 (gfx950 converts the OCP format)
+  static constexpr int E = 16;
+  __device__ static void add(const u32x4& w, float* a) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[i], false);
+      auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[i], true);
+      a[4 * i + 0] += lo[0]; a[4 * i + 1] += lo[1];
+      a[4 * i + 2] += hi[0]; a[4 * i + 3] += hi[1];
+    }
+  }
+};
+
 }  // namespace bsattn

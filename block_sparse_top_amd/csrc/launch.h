@@ -7,16 +7,18 @@
 
 namespace bsattn {
 
-// Step 1: per-block mean of q and k (fp32 out, [B, H, nb, D]). kind: 0 fp32, 1 bf16, 2 fp8.
-hipError_t launch_pool(int kind, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
-                       const void* q, const void* k, float* qbar, float* kbar,
+// Step 1: per-block mean (fp32 out, [B, H, nb, D]) of the tensors in `which` (bit 0: q,
+// bit 1: k). kind: 0 fp32, 1 bf16, 2 fp8.
+hipError_t launch_pool(int kind, int which, int64_t B, int64_t N, int Hq, int Hkv, int D,
+                       int block, const void* q, const void* k, float* qbar, float* kbar,
                        hipStream_t stream);
 
-// Steps 2-3 fused for nb <= kMaxFusedBlocks: block scores and top-k per row.
+// Steps 1 (query side), 2 and 3 fused for nb <= kMaxFusedBlocks: query pooling (also stored
+// to qbar), block scores against the pooled keys kbar, top-k per row.
 constexpr int kMaxFusedBlocks = 1024;
-hipError_t launch_score_select(int64_t B, int Hq, int Hkv, int64_t nb, int D, int topk,
-                               const float* qbar, const float* kbar, int32_t* idx,
-                               hipStream_t stream);
+hipError_t launch_pool_score_select(int kind, int64_t B, int64_t N, int Hq, int Hkv, int D,
+                                    int block, int topk, const void* q, float* qbar,
+                                    const float* kbar, int32_t* idx, hipStream_t stream);
 
 // Step 4, bf16 inputs on bf16 MFMA. Supported (D, block): D, block in {64, 128}.
 bool attn_bf16_supported(int D, int block);

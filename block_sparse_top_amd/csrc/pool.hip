@@ -17,36 +17,12 @@ namespace bsattn {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kUnroll = 16;                 // 16-byte loads in flight per thread
 
-// Elements per 16-byte vector and their fp32 values, per storage kind.
-template <int KIND> struct Vec;
-template <> struct Vec<0> {            // fp32
-  static constexpr int E = 4;
-  __device__ static void add(const u32x4& w, float* a) {
-    a[0] += __uint_as_float(w.x); a[1] += __uint_as_float(w.y);
-    a[2] += __uint_as_float(w.z); a[3] += __uint_as_float(w.w);
-  }
-};
-template <> struct Vec<1> {            // bf16
-  static constexpr int E = 8;
-  __device__ static void add(const u32x4& w, float* a) {
-    a[0] += bf16lo(w.x); a[1] += bf16hi(w.x); a[2] += bf16lo(w.y); a[3] += bf16hi(w.y);
-    a[4] += bf16lo(w.z); a[5] += bf16hi(w.z); a[6] += bf16lo(w.w); a[7] += bf16hi(w.w);
-  }
-};
-template <> struct Vec<2> {            // OCP fp8 e4m3 (gfx950 converts the OCP format)
-  static constexpr int E = 16;
-  __device__ static void add(const u32x4& w, float* a) {
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[i], false);
-      auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[i], true);
-      a[4 * i + 0] += lo[0]; a[4 * i + 1] += lo[1];
-      a[4 * i + 2] += hi[0]; a[4 * i + 3] += hi[1];
-    }
-  }
-};
+// Every input byte is read exactly once: stream it past the caches (nontemporal load).
+__device__ __forceinline__ u32x4 load16(const uint8_t* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
 
 struct PoolArgs {
   const uint8_t* x;   // [B, N, H, D] storage
@@ -76,15 +52,14 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
     if (grp < T) {
       const uint8_t* p = base + (int64_t)c * 16;
       int t = grp;
-      for (; t + 7 * T < block; t += 8 * T) {          // 8 loads in flight
-        u32x4 w[8];
+      for (; t + (kUnroll - 1) * T < block; t += kUnroll * T) {   // kUnroll loads in flight
+        u32x4 w[kUnroll];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          w[u] = *(const u32x4*)(p + (int64_t)(t + u * T) * row_bytes);
+        for (int u = 0; u < kUnroll; ++u) w[u] = load16(p + (int64_t)(t + u * T) * row_bytes);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) Vec<KIND>::add(w[u], acc);
+        for (int u = 0; u < kUnroll; ++u) Vec<KIND>::add(w[u], acc);
       }
-      for (; t < block; t += T) Vec<KIND>::add(*(const u32x4*)(p + (int64_t)t * row_bytes), acc);
+      for (; t < block; t += T) Vec<KIND>::add(load16(p + (int64_t)t * row_bytes), acc);
 #pragma unroll
       for (int e = 0; e < E; ++e) red[grp * V * E + c * E + e] = acc[e];
     }
@@ -102,14 +77,14 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
       for (int e = 0; e < E; ++e) acc[e] = 0.f;
       const uint8_t* p = base + (int64_t)c * 16;
       int t = 0;
-      for (; t + 7 < block; t += 8) {
-        u32x4 w[8];
+      for (; t + kUnroll - 1 < block; t += kUnroll) {
+        u32x4 w[kUnroll];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) w[u] = *(const u32x4*)(p + (int64_t)(t + u) * row_bytes);
+        for (int u = 0; u < kUnroll; ++u) w[u] = load16(p + (int64_t)(t + u) * row_bytes);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) Vec<KIND>::add(w[u], acc);
+        for (int u = 0; u < kUnroll; ++u) Vec<KIND>::add(w[u], acc);
       }
-      for (; t < block; ++t) Vec<KIND>::add(*(const u32x4*)(p + (int64_t)t * row_bytes), acc);
+      for (; t < block; ++t) Vec<KIND>::add(load16(p + (int64_t)t * row_bytes), acc);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int o = c * E + e;
@@ -122,15 +97,15 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
 
 }  // namespace
 
-hipError_t launch_pool(int kind, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
-                       const void* q, const void* k, float* qbar, float* kbar,
+hipError_t launch_pool(int kind, int which, int64_t B, int64_t N, int Hq, int Hkv, int D,
+                       int block, const void* q, const void* k, float* qbar, float* kbar,
                        hipStream_t stream) {
   const int64_t nb = N / block;
   const int ebytes = kind == 0 ? 4 : kind == 1 ? 2 : 1;
   const int E = 16 / ebytes;
   // LDS for the partial sums: T * V * E floats with T = 256 / V, i.e. at most 256 * E.
   size_t lds = 0;
-  for (int H : {Hq, Hkv}) {
+  for (int H : {which & 1 ? Hq : Hkv, which & 2 ? Hkv : Hq}) {
     int V = H * D / E;
     if (V <= kThreads) {
       size_t s = (size_t)(kThreads / V) * V * E * sizeof(float);
@@ -139,7 +114,8 @@ hipError_t launch_pool(int kind, int64_t B, int64_t N, int Hq, int Hkv, int D, i
   }
   PoolArgs qa{(const uint8_t*)q, qbar, Hq};
   PoolArgs ka{(const uint8_t*)k, kbar, Hkv};
-  dim3 grid((unsigned)(B * nb), 2);
+  if (which == 2) qa = ka;                             // k only: grid.y == 1 reads qa
+  dim3 grid((unsigned)(B * nb), which == 3 ? 2 : 1);
   const float inv = 1.0f / (float)block;               // exact for power-of-two blocks
   switch (kind) {
     case 0: pool_kernel<0><<<grid, kThreads, lds, stream>>>(qa, ka, nb, D, block, inv); break;

@@ -1,22 +1,31 @@
-// Steps 2-3 of block selection, fused: block scores and per-row top-k.
+// Steps 1 (query side), 2 and 3 of block selection, fused: query-block pooling, block scores
+// and per-row top-k. The key side is pooled beforehand (pool.hip), since every row needs all
+// pooled key blocks.
 //
 // SparseFormer page ("2026 新一代卷积与Transformer网络架构技术演进与性能对比"), section
 // "SparseFormer 注意力实现": step 1 forms block_scores[b,h,i,j] = sum_d qbar[b,h,i,d] *
 // kbar[b,h,j,d] (an einsum, no scale); step 2 keeps torch.topk(block_scores,
 // k = int(topk_ratio * num_blocks)) per row. The MSA page ("从M2.7到M3：多模态模型稀疏注意力架构
 // 设计与实现全解析", §3.3 计算优化) suggests computing the block scores as a matrix product and
-// fusing kernels; here the score tile never leaves the chip.
+// fusing kernels; here the score rows never leave the chip.
 //
-// Layout: one work-group = 4 waves = 16 consecutive query-block rows of one (batch, query
-// head). Key-block columns are staged through LDS 64 at a time, transposed to [D][64], so
-// lane l owns columns j = l + 64*c. Scores are fp32, summed over d in order with fused
-// multiply-adds, identically for every column (equal pooled key blocks give equal scores).
+// Layout: one work-group = 4 waves = 4*RW consecutive query-block rows of one (batch, query
+// head). It first averages its rows' query tokens (16-byte loads, streamed past the caches:
+// this phase is HBM-bound and overlaps the arithmetic of the other work-groups on the CU),
+// keeps the pooled rows in LDS and also stores them to the workspace. Then each wave holds
+// RW rows x CPL columns of scores in registers, lane l owning columns
+// j = l + 64*c. Key-block columns are staged through LDS 64 at a time with coalesced row
+// loads, kept row-major with a one-float pad (lane j reads row j: banks j + d, no conflict).
+// Scores are fp32, summed over d in order with fused multiply-adds, identically for every
+// column (equal pooled key blocks give equal scores).
 //
 // Selection of one row is done by its wave with no sorting: scores map to order-preserving
-// 32-bit keys, the k-th largest key T is built bit by bit from the top (a candidate bit stays
-// when at least k keys are >= the candidate, counted with ballots), then every key > T is
-// kept and the keys == T fill the remaining places in ascending j (the lower index wins a
-// tie). Kept columns are compacted with ballot/mbcnt in ascending j order.
+// 32-bit keys, and a threshold T is built bit by bit from the top (a candidate bit stays when
+// at least k keys are >= the candidate, counted with ballots). The search stops as soon as
+// exactly k keys are >= T (then T separates the top k); otherwise it runs to the last bit
+// and T is the k-th largest key. Every key > T is kept and the keys == T fill the remaining
+// places in ascending j (the lower index wins a tie). Kept columns are compacted with
+// ballot/mbcnt in ascending j order.
 #include "common.h"
 #include "launch.h"
 
@@ -24,59 +33,117 @@ namespace bsattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerWave = 4;
-constexpr int kRowsPerGroup = kRowsPerWave * (kThreads / kWave);  // 16
+constexpr int kWaves = kThreads / kWave;
 
-template <int CPL>  // score columns per lane: nb <= 64 * CPL
-__global__ __launch_bounds__(kThreads) void score_select_kernel(
-    const float* __restrict__ qbar, const float* __restrict__ kbar, int32_t* __restrict__ idx,
-    int Hq, int Hkv, int nb, int D, int topk, int row_tiles) {
+// Small work-groups (8 rows) give ~5 rounds of work-groups per CU, so that the pooling loads
+// of some overlap the score/select arithmetic of others.
+template <int CPL>
+struct SelCfg {
+  static constexpr int RW = 2;                                  // rows per wave
+  static constexpr int RG = kWaves * RW;                       // rows per work-group
+};
+
+template <int KIND, int CPL>  // storage kind; score columns per lane: nb <= 64 * CPL
+__global__ __launch_bounds__(kThreads) void select_kernel(
+    const uint8_t* __restrict__ q, float* __restrict__ qbar, const float* __restrict__ kbar,
+    int32_t* __restrict__ idx, int64_t N, int Hq, int Hkv, int nb, int D, int block, int topk,
+    int row_tiles, float inv_block) {
+  constexpr int RW = SelCfg<CPL>::RW, RG = SelCfg<CPL>::RG;
+  constexpr int E = Vec<KIND>::E;
+  constexpr int EB = 16 / E;                // bytes per stored element
   extern __shared__ float smem[];
-  float* kT = smem;                         // [D][64] current column chunk, transposed
-  float* qs = smem + D * 64;                // [16][D] query rows of this work-group
+  const int KS = D + 1;                     // padded row stride of the key chunk
+  float* ks = smem;                         // [64][D+1] current key-block chunk
+  float* qs = smem + 64 * KS;               // [RG][D] pooled query rows of this work-group
 
   const int tile = blockIdx.x;
   const int rt = tile % row_tiles;
   const int bh = tile / row_tiles;          // b * Hq + h
   const int h = bh % Hq, b = bh / Hq;
   const int g = h / (Hq / Hkv);
-  const float* Q = qbar + (int64_t)bh * nb * D;
   const float* K = kbar + ((int64_t)b * Hkv + g) * nb * D;
-  const int row0 = rt * kRowsPerGroup;
+  const int row0 = rt * RG;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int D4 = D / 4;
 
-  for (int e = tid; e < kRowsPerGroup * D; e += kThreads) {
-    const int r = e / D;
-    qs[e] = (row0 + r < nb) ? Q[(int64_t)(row0 + r) * D + (e - r * D)] : 0.f;
+  // ---- pool the RG query rows: pair (row r, 16-byte column c); TG token groups per pair
+  {
+    const int C16 = D / E;                  // 16-byte columns per token of one head
+    const int pairs = RG * C16;
+    const int per_pass = pairs < kThreads ? pairs : kThreads;
+    const int TG = kThreads / per_pass;     // token groups (>= 1)
+    const int64_t tok_bytes = (int64_t)Hq * D * EB;
+    float* red = ks;                        // [TG][per_pass][E] partial sums (fits: D >= 64)
+    for (int p0 = 0; p0 < pairs; p0 += per_pass) {
+      const int pr = p0 + tid % per_pass, tg = tid / per_pass;
+      const int r = pr / C16, c = pr % C16;
+      const int row = row0 + r;
+      float acc[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = 0.f;
+      if (tg < TG && row < nb) {
+        const uint8_t* src = q + (((int64_t)b * N + (int64_t)row * block) * Hq + h) * D * EB + c * 16;
+        int t = tg;
+        for (; t + 7 * TG < block; t += 8 * TG) {
+          u32x4 w[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            w[u] = __builtin_nontemporal_load((const u32x4*)(src + (int64_t)(t + u * TG) * tok_bytes));
+#pragma unroll
+          for (int u = 0; u < 8; ++u) Vec<KIND>::add(w[u], acc);
+        }
+        for (; t < block; t += TG)
+          Vec<KIND>::add(__builtin_nontemporal_load((const u32x4*)(src + (int64_t)t * tok_bytes)), acc);
+      }
+      if (TG > 1) {
+        __syncthreads();                    // previous pass done with red
+        if (tg < TG)
+#pragma unroll
+          for (int e = 0; e < E; ++e) red[(tg * per_pass + tid % per_pass) * E + e] = acc[e];
+        __syncthreads();
+        for (int o = tid; o < per_pass * E; o += kThreads) {
+          float sum = 0.f;
+          for (int t2 = 0; t2 < TG; ++t2) sum += red[t2 * per_pass * E + o];
+          const int pr2 = p0 + o / E, r2 = pr2 / C16, d = (pr2 % C16) * E + o % E;
+          const float m = sum * inv_block;
+          qs[r2 * D + d] = m;
+          if (row0 + r2 < nb) qbar[((int64_t)bh * nb + row0 + r2) * D + d] = m;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float m = acc[e] * inv_block;
+          qs[r * D + c * E + e] = m;
+          if (row < nb) qbar[((int64_t)bh * nb + row) * D + c * E + e] = m;
+        }
+      }
+    }
   }
 
-  float acc[kRowsPerWave][CPL];
+  float acc[RW][CPL];
 #pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r)
+  for (int r = 0; r < RW; ++r)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[r][c] = 0.f;
 
-  const int D4 = D / 4;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    __syncthreads();                        // previous chunk consumed
+    __syncthreads();                        // previous chunk consumed (and qs written)
     for (int e = tid; e < 64 * D4; e += kThreads) {
-      const int col = e % 64, d4 = e / 64;
+      const int col = e / D4, d4 = e - col * D4;
       const int j = c * 64 + col;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
       if (j < nb) v = *(const f32x4*)(K + (int64_t)j * D + 4 * d4);
-      kT[(4 * d4 + 0) * 64 + col] = v[0];
-      kT[(4 * d4 + 1) * 64 + col] = v[1];
-      kT[(4 * d4 + 2) * 64 + col] = v[2];
-      kT[(4 * d4 + 3) * 64 + col] = v[3];
+      float* dst = ks + col * KS + 4 * d4;
+      dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
     }
     __syncthreads();
-    const float* qw = qs + wave * kRowsPerWave * D;
+    const float* qw = qs + wave * RW * D;
+    const float* kr = ks + lane * KS;
     for (int d = 0; d < D; d += 4) {
-      const float k0 = kT[(d + 0) * 64 + lane], k1 = kT[(d + 1) * 64 + lane];
-      const float k2 = kT[(d + 2) * 64 + lane], k3 = kT[(d + 3) * 64 + lane];
+      const float k0 = kr[d], k1 = kr[d + 1], k2 = kr[d + 2], k3 = kr[d + 3];
 #pragma unroll
-      for (int r = 0; r < kRowsPerWave; ++r) {
+      for (int r = 0; r < RW; ++r) {
         const f32x4 qv = *(const f32x4*)(qw + r * D + d);
         float s = acc[r][c];
         s = __builtin_fmaf(qv[0], k0, s);
@@ -90,63 +157,77 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(
 
   // ---- per-row top-k, one wave per row
 #pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) {
-    const int row = row0 + wave * kRowsPerWave + r;
+  for (int r = 0; r < RW; ++r) {
+    const int row = row0 + wave * RW + r;
     if (row >= nb) break;                   // wave-uniform
+    // columns past nb hold key 0, which no candidate (always >= 1) and no T reached by the
+    // search (>= 1 once any bit is set) can count
     uint32_t key[CPL];
-    bool valid[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      valid[c] = (c * 64 + lane) < nb;
-      key[c] = valid[c] ? order_key(acc[r][c]) : 0u;
-    }
+    for (int c = 0; c < CPL; ++c) key[c] = (c * 64 + lane) < nb ? order_key(acc[r][c]) : 0u;
     uint32_t T = 0;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);
       int cnt = 0;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) cnt += __popcll(__ballot(valid[c] && key[c] >= cand));
+      for (int c = 0; c < CPL; ++c) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[c] >= cand));
       if (cnt >= topk) T = cand;
+      if (cnt == topk) break;               // exactly k keys >= T: T separates the top k
     }
     int gt = 0;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) gt += __popcll(__ballot(valid[c] && key[c] > T));
+    for (int c = 0; c < CPL; ++c) gt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[c] > T));
     const int need = topk - gt;             // >= 1 places for keys equal to T
     int32_t* out = idx + ((int64_t)bh * nb + row) * topk;
     int eq_before = 0, sel_before = 0;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const bool is_eq = valid[c] && key[c] == T;
-      const uint64_t meq = __ballot(is_eq);
-      const bool sel = valid[c] && (key[c] > T || (is_eq && eq_before + lanes_below(meq) < need));
-      const uint64_t msel = __ballot(sel);
+      const bool valid = (c * 64 + lane) < nb;
+      const bool is_eq = valid && key[c] == T;
+      const uint64_t meq = __builtin_amdgcn_ballot_w64(is_eq);
+      const bool sel = valid && (key[c] > T || (is_eq && eq_before + lanes_below(meq) < need));
+      const uint64_t msel = __builtin_amdgcn_ballot_w64(sel);
       if (sel) out[sel_before + lanes_below(msel)] = c * 64 + lane;
-      eq_before += __popcll(meq);
-      sel_before += __popcll(msel);
+      eq_before += __builtin_popcountll(meq);
+      sel_before += __builtin_popcountll(msel);
     }
   }
 }
 
+template <int KIND, int CPL>
+hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int nb, int D, int block, int topk,
+                  const void* q, float* qbar, const float* kbar, int32_t* idx,
+                  hipStream_t stream) {
+  constexpr int RG = SelCfg<CPL>::RG;
+  const int row_tiles = (nb + RG - 1) / RG;
+  const dim3 grid((unsigned)(B * Hq * row_tiles));
+  const size_t lds = (size_t)(64 * (D + 1) + RG * D) * sizeof(float);
+  select_kernel<KIND, CPL><<<grid, kThreads, lds, stream>>>(
+      (const uint8_t*)q, qbar, kbar, idx, N, Hq, Hkv, nb, D, block, topk, row_tiles,
+      1.0f / (float)block);
+  return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_kind(int64_t B, int64_t N, int Hq, int Hkv, int nb, int D, int block, int topk,
+                       const void* q, float* qbar, const float* kbar, int32_t* idx,
+                       hipStream_t stream) {
+  if (nb <= 64) return launch<KIND, 1>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
+  if (nb <= 128) return launch<KIND, 2>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
+  if (nb <= 256) return launch<KIND, 4>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
+  if (nb <= 512) return launch<KIND, 8>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
+  return launch<KIND, 16>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
+}
+
 }  // namespace
 
-hipError_t launch_score_select(int64_t B, int Hq, int Hkv, int64_t nb, int D, int topk,
-                               const float* qbar, const float* kbar, int32_t* idx,
-                               hipStream_t stream) {
-  const int row_tiles = (int)((nb + kRowsPerGroup - 1) / kRowsPerGroup);
-  const dim3 grid((unsigned)(B * Hq * row_tiles));
-  const size_t lds = (size_t)(D * 64 + kRowsPerGroup * D) * sizeof(float);
-  const int n = (int)nb;
-  if (nb <= 64)
-    score_select_kernel<1><<<grid, kThreads, lds, stream>>>(qbar, kbar, idx, Hq, Hkv, n, D, topk, row_tiles);
-  else if (nb <= 128)
-    score_select_kernel<2><<<grid, kThreads, lds, stream>>>(qbar, kbar, idx, Hq, Hkv, n, D, topk, row_tiles);
-  else if (nb <= 256)
-    score_select_kernel<4><<<grid, kThreads, lds, stream>>>(qbar, kbar, idx, Hq, Hkv, n, D, topk, row_tiles);
-  else if (nb <= 512)
-    score_select_kernel<8><<<grid, kThreads, lds, stream>>>(qbar, kbar, idx, Hq, Hkv, n, D, topk, row_tiles);
-  else
-    score_select_kernel<16><<<grid, kThreads, lds, stream>>>(qbar, kbar, idx, Hq, Hkv, n, D, topk, row_tiles);
-  return hipGetLastError();
+hipError_t launch_pool_score_select(int kind, int64_t B, int64_t N, int Hq, int Hkv, int D,
+                                    int block, int topk, const void* q, float* qbar,
+                                    const float* kbar, int32_t* idx, hipStream_t stream) {
+  const int nb = (int)(N / block);
+  if (kind == 0) return launch_kind<0>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
+  if (kind == 1) return launch_kind<1>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
+  return launch_kind<2>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
 }
 
 }  // namespace bsattn
