@@ -62,6 +62,12 @@ size_t pooled_q_bytes(int64_t B, int64_t N, int Hq, int D, int block) {
 size_t pooled_k_bytes(int64_t B, int64_t N, int Hkv, int D, int block) {
   return align256((size_t)B * Hkv * (size_t)(N / block) * D * sizeof(float));
 }
+// score matrix, only for the many-block path
+size_t scores_bytes(int64_t B, int64_t N, int Hq, int block) {
+  const size_t nb = (size_t)(N / block);
+  if (nb <= (size_t)bsattn::kMaxFusedBlocks) return 0;
+  return align256((size_t)B * Hq * nb * nb * sizeof(float));
+}
 
 }  // namespace
 
@@ -88,7 +94,8 @@ size_t bsattn_select_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int 
     return 0;
   }
   if (B == 0 || N == 0) return 0;
-  return pooled_q_bytes(B, N, Hq, D, block) + pooled_k_bytes(B, N, Hkv, D, block);
+  return pooled_q_bytes(B, N, Hq, D, block) + pooled_k_bytes(B, N, Hkv, D, block) +
+         scores_bytes(B, N, Hq, block);
 }
 
 int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
@@ -98,9 +105,11 @@ int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int b
   if (st != BSATTN_OK) return st;
   if (B == 0 || N == 0) return BSATTN_OK;
   const int64_t nb = N / block;
-  if (nb > bsattn::kMaxFusedBlocks)
-    return fail(BSATTN_E_UNSUPPORTED, "selection over nb=%lld > %d blocks", (long long)nb,
-                bsattn::kMaxFusedBlocks);
+  const bool large = nb > bsattn::kMaxFusedBlocks;
+  if (large && (nb > bsattn::kMaxLargeBlocks || nb % 64))
+    return fail(BSATTN_E_UNSUPPORTED,
+                "selection over nb=%lld blocks (supported: nb <= %d, or a multiple of 64 up to %d)",
+                (long long)nb, bsattn::kMaxFusedBlocks, bsattn::kMaxLargeBlocks);
   if (!q || !k || !idx) return fail(BSATTN_E_INVALID, "null q, k or idx");
   if (!aligned16(q) || !aligned16(k) || ((uintptr_t)idx & 3u))
     return fail(BSATTN_E_INVALID, "q and k must be 16-byte aligned, idx 4-byte aligned");
@@ -113,6 +122,17 @@ int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int b
   float* kbar = (float*)((char*)workspace + pooled_q_bytes(B, N, Hq, D, block));
   hipStream_t s = (hipStream_t)stream;
   const int kind = dtype == BSATTN_F32 ? 0 : dtype == BSATTN_BF16 ? 1 : 2;
+  if (large) {
+    float* S = (float*)((char*)kbar + pooled_k_bytes(B, N, Hkv, D, block));
+    st = hip_status(bsattn::launch_pool(kind, 3, B, N, Hq, Hkv, D, block, q, k, qbar, kbar, s),
+                    "pool launch");
+    if (st != BSATTN_OK) return st;
+    st = hip_status(bsattn::launch_scores_large(B, Hq, Hkv, (int)nb, D, qbar, kbar, S, s),
+                    "score launch");
+    if (st != BSATTN_OK) return st;
+    return hip_status(bsattn::launch_topk_rows(B * Hq * nb, (int)nb, topk, S, idx, s),
+                      "top-k launch");
+  }
   st = hip_status(bsattn::launch_pool(kind, 2, B, N, Hq, Hkv, D, block, q, k, qbar, kbar, s),
                   "key pool launch");
   if (st != BSATTN_OK) return st;

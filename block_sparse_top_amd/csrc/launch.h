@@ -20,6 +20,14 @@ hipError_t launch_pool_score_select(int kind, int64_t B, int64_t N, int Hq, int 
                                     int block, int topk, const void* q, float* qbar,
                                     const float* kbar, int32_t* idx, hipStream_t stream);
 
+// Steps 2-3 for nb > kMaxFusedBlocks (nb % 64 == 0, nb <= kMaxLargeBlocks): S = scores
+// [B, Hq, nb, nb] fp32 in the workspace, then the top-k of each of its rows.
+constexpr int kMaxLargeBlocks = 8192;
+hipError_t launch_scores_large(int64_t B, int Hq, int Hkv, int nb, int D, const float* qbar,
+                               const float* kbar, float* S, hipStream_t stream);
+hipError_t launch_topk_rows(int64_t rows, int nb, int topk, const float* S, int32_t* idx,
+                            hipStream_t stream);
+
 // Step 4, bf16 inputs on bf16 MFMA. Supported (D, block): D, block in {64, 128}.
 bool attn_bf16_supported(int D, int block);
 hipError_t launch_attn_bf16(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,

@@ -1,0 +1,199 @@
+// Steps 2-3 of block selection for many key blocks (nb > 1024): the score matrix is built in
+// the workspace by an fp32 MFMA product, then each row's top-k is found by one work-group.
+//
+// SparseFormer page ("2026 新一代卷积与Transformer网络架构技术演进与性能对比"), section
+// "SparseFormer 注意力实现": block_scores = einsum over d of the pooled query and key blocks
+// (no scale), then torch.topk with k = int(topk_ratio * num_blocks) per row. MSA page
+// ("从M2.7到M3：多模态模型稀疏注意力架构设计与实现全解析") §3.2: 1M-token context at block 128, i.e.
+// 8192 key blocks per row; §3.3: block scores as a matrix product.
+//
+// score_gemm_kernel: S[b,h] = qbar[b,h] (nb x D) * kbar[b,g]^T, fp32, unscaled. One wave
+// computes a 64x64 tile with v_mfma_f32_32x32x2_f32 (four 32x32 sub-tiles); the lane half h of
+// k-step s carries d = s + (D/2)*h on both operands, so every lane reads contiguous halves of
+// its query and key rows. Every score goes through the same instruction sequence, so equal
+// pooled key blocks give bit-equal scores.
+//
+// topk_rows_kernel: one work-group (256 threads) per row; thread t holds the 32-column chunk
+// j = 32t .. 32t+31 (nb = 8192) as order-preserving keys. A threshold T is built bit by bit
+// (block-wide counts of keys >= candidate; early exit once exactly k keys are >= T), keys > T
+// are kept and keys == T fill the remaining places in ascending j (the lower index wins).
+// Output positions come from block-wide exclusive scans, so the row is written in ascending j.
+#include "common.h"
+#include "launch.h"
+
+namespace bsattn {
+namespace {
+
+typedef float f32x16v __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------- score GEMM
+__global__ __launch_bounds__(64) void score_gemm_kernel(const float* __restrict__ qbar,
+                                                        const float* __restrict__ kbar,
+                                                        float* __restrict__ S, int Hq, int Hkv,
+                                                        int nb, int D, int tiles) {
+  // tile index: (b*Hq + h) * tiles^2 + ti * tiles + tj, 64x64 each
+  const int64_t t = blockIdx.x;
+  const int tj = (int)(t % tiles), ti = (int)((t / tiles) % tiles);
+  const int64_t bh = t / ((int64_t)tiles * tiles);
+  const int h = (int)(bh % Hq), b = (int)(bh / Hq);
+  const int g = h / (Hq / Hkv);
+  const float* Q = qbar + bh * nb * D;
+  const float* K = kbar + ((int64_t)b * Hkv + g) * nb * D;
+  const int lane = threadIdx.x, l32 = lane & 31, half = lane >> 5;
+  const int half_d = D / 2;
+
+  f32x16v acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
+
+  const float* qrow[2];
+  const float* krow[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    qrow[a] = Q + (int64_t)(ti * 64 + 32 * a + l32) * D + half * half_d;
+    krow[a] = K + (int64_t)(tj * 64 + 32 * a + l32) * D + half * half_d;
+  }
+  for (int s0 = 0; s0 < half_d; s0 += 4) {
+    f32x4 qa[2], kb[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      qa[a] = *(const f32x4*)(qrow[a] + s0);
+      kb[a] = *(const f32x4*)(krow[a] + s0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[a][e], kb[c][e], acc[a][c], 0, 0, 0);
+  }
+  // acc[a][c][r]: row ti*64 + 32a + 8(r/4) + 4*half + r%4, column tj*64 + 32c + l32
+  float* Sbh = S + bh * nb * nb;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = ti * 64 + 32 * a + 8 * (r >> 2) + 4 * half + (r & 3);
+        Sbh[(int64_t)row * nb + tj * 64 + 32 * c + l32] = acc[a][c][r];
+      }
+}
+
+// ---------------------------------------------------------------- per-row top-k
+constexpr int kTopkThreads = 256;
+constexpr int kPerThread = 32;             // columns per thread: nb <= 8192
+
+__device__ __forceinline__ int block_sum(int v, int* red) {
+  // wave sum by butterfly, then the 4 wave sums through LDS (caller syncs around reuse)
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  const int total = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return total;
+}
+
+// exclusive prefix of v over threads in thread order, and the block total
+__device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) red[w] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < w) before += red[i];
+    tot += red[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return before + incl - v;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __restrict__ S,
+                                                                 int32_t* __restrict__ idx,
+                                                                 int nb, int topk) {
+  __shared__ int red[4];
+  const int64_t row = blockIdx.x;
+  const float* srow = S + row * nb;
+  const int t = threadIdx.x;
+  const int j0 = t * kPerThread;
+  uint32_t key[kPerThread];
+#pragma unroll
+  for (int e = 0; e < kPerThread; e += 4) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (j0 + e < nb) v = *(const f32x4*)(srow + j0 + e);   // nb is a multiple of 4
+#pragma unroll
+    for (int q = 0; q < 4; ++q) key[e + q] = (j0 + e + q) < nb ? order_key(v[q]) : 0u;
+  }
+  // keys of columns past nb are 0: no candidate (>= 1) and no reached T (>= 1) counts them
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) c += key[e] >= cand;
+    const int cnt = block_sum(c, red);
+    if (cnt >= topk) T = cand;
+    if (cnt == topk) break;
+  }
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    gt += key[e] > T;
+    eq += (j0 + e < nb) && key[e] == T;
+  }
+  const int tot_gt = block_sum(gt, red);
+  int tot_eq;
+  const int eq_before = block_exclusive_scan(eq, red, &tot_eq);
+  const int need = topk - tot_gt;          // places for keys equal to T
+  int sel = 0;
+  int eq_seen = eq_before;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const bool is_eq = (j0 + e < nb) && key[e] == T;
+    sel += key[e] > T || (is_eq && eq_seen < need);
+    eq_seen += is_eq;
+  }
+  int tot_sel;
+  int pos = block_exclusive_scan(sel, red, &tot_sel);
+  int32_t* out = idx + row * topk;
+  eq_seen = eq_before;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const bool is_eq = (j0 + e < nb) && key[e] == T;
+    if (key[e] > T || (is_eq && eq_seen < need)) out[pos++] = j0 + e;
+    eq_seen += is_eq;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_scores_large(int64_t B, int Hq, int Hkv, int nb, int D, const float* qbar,
+                               const float* kbar, float* S, hipStream_t stream) {
+  const int tiles = nb / 64;
+  const int64_t n = B * Hq * (int64_t)tiles * tiles;
+  score_gemm_kernel<<<dim3((unsigned)n), 64, 0, stream>>>(qbar, kbar, S, Hq, Hkv, nb, D, tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_rows(int64_t rows, int nb, int topk, const float* S, int32_t* idx,
+                            hipStream_t stream) {
+  topk_rows_kernel<<<dim3((unsigned)rows), kTopkThreads, 0, stream>>>(S, idx, nb, topk);
+  return hipGetLastError();
+}
+
+}  // namespace bsattn

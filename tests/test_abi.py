@@ -69,7 +69,8 @@ def last():
     (dict(ws=None), 3, "workspace"),
     (dict(wsb=16), 3, "workspace"),
     (dict(ws=ctypes.c_void_p(0x10010)), 3, "aligned"),
-    (dict(N=64 * 2048, topk=3), 2, "nb=2048"),
+    (dict(N=64 * 2048 + 64, topk=3), 2, "nb=2049"),
+    (dict(N=64 * 16384, topk=3), 2, "nb=16384"),
 ])
 def test_select_rejects(kw, status, msg):
     assert sel(**kw) == status

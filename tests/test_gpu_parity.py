@@ -260,3 +260,89 @@ def test_sparseformer_full_size():
             sl = (0, slice(i * w.block, (i + 1) * w.block), h)
             check_out(got[sl], ref[sl], "bf16")
     say("  sampled", len(picks), "query blocks ok")
+
+
+@pytest.mark.parametrize("shape", [
+    # B, N, Hq, Hkv, D, block, topk: more than 1024 key blocks (score matrix in the workspace)
+    (1, 64 * 2048, 4, 2, 64, 64, 300),
+    (1, 128 * 1088, 2, 1, 128, 128, 163),
+])
+def test_select_many_blocks(shape):
+    B, N, Hq, Hkv, D, blk, topk = shape
+    say(f"[select many blocks] shape={shape}")
+    q, k, v, ds = make(B, N, Hq, Hkv, D, "bf16", index=18)
+    del v
+    idx, qbar, kbar = bst.select(q, k, blk, topk, return_pooled=True)
+    torch.cuda.synchronize()
+    qo, ko = to_f64(q), to_f64(k)
+    pq, pk = O.pool(qo, blk), O.pool(ko, blk)
+    assert np.max(np.abs(qbar.cpu().numpy() - pq)) <= 2e-6 * np.abs(qo).max()
+    assert np.max(np.abs(kbar.cpu().numpy() - pk)) <= 2e-6 * np.abs(ko).max()
+    stats = check_idx(idx.cpu().numpy(), O.block_scores(pq, pk), topk)
+    say("  ", stats)
+
+
+def test_planted_workload_sampled():
+    """The planted-structure workload at full size: every selection row vs the oracle
+    (the planted blocks are recovered statistically, not asserted), sampled outputs."""
+    w = syn.WORKLOADS["planted_n32768_bf16"]
+    say("[planted]", w)
+    q, k, v, ds, extra = syn.workload_inputs(w, device=DEV)
+    topk = O.topk_count(w.ratio, w.nb)
+    idx = bst.select(q, k, w.block, topk)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    bst.forward(q, k, v, idx, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+    qo, ko = to_f64(q), to_f64(k)
+    gidx = idx.cpu().numpy()
+    stats = check_idx(gidx, O.block_scores(O.pool(qo, w.block), O.pool(ko, w.block)), topk)
+    planted = extra["planted"].cpu().numpy()
+    hit = np.mean([len(set(a) & set(b)) / topk for a, b in
+                   zip(gidx.reshape(-1, topk), planted.reshape(-1, topk))])
+    say("  ", stats, "planted recovery", round(float(hit), 3))
+    rows = syn.sample_rows(24, w.B * w.Hq * w.nb, w.index)
+    picks = [(r // (w.Hq * w.nb), (r // w.nb) % w.Hq, r % w.nb) for r in rows]
+    vo = to_f64(v)
+    ref = O.attend(qo, ko, vo, gidx, w.block, 1 / math.sqrt(w.D), rows=picks)
+    got = out.float().cpu().numpy()
+    for (b, h, i) in picks:
+        sl = (b, slice(i * w.block, (i + 1) * w.block), h)
+        check_out(got[sl], ref[sl], "bf16")
+
+
+@pytest.mark.slow
+def test_long_context_gqa_sampled():
+    """1M tokens, 32 query / 8 KV heads, 8192 key blocks: sampled rows of the selection and
+    of the output against the oracle (which pools all keys of the sampled heads)."""
+    w = syn.WORKLOADS["longctx_gqa_n1m_bf16"]
+    say("[long context]", w)
+    q, k, v, ds, _ = syn.workload_inputs(w, device=DEV)
+    topk = O.topk_count(w.ratio, w.nb)
+    ws = torch.empty(bst.select_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.block),
+                     dtype=torch.uint8, device=DEV)
+    idx = bst.select(q, k, w.block, topk, workspace=ws)
+    del ws
+    out = bst.forward(q, k, v, idx)
+    torch.cuda.synchronize()
+    say("  gpu done")
+    G = w.Hq // w.Hkv
+    rows = syn.sample_rows(16, w.Hq * w.nb, w.index)
+    picks = [(0, r // w.nb, r % w.nb) for r in rows]
+    gidx = idx.cpu().numpy()
+    qfull = np.zeros((1, w.N, 1, w.D))
+    for g in sorted({h // G for _, h, _ in picks}):
+        kg = to_f64(k[:, :, g:g + 1])                                  # [1, N, 1, D]
+        vg = to_f64(v[:, :, g:g + 1])
+        kbar = O.pool(kg, w.block)[0, 0]                               # [nb, D]
+        for (_, h, i) in [p for p in picks if p[1] // G == g]:
+            blk = slice(i * w.block, (i + 1) * w.block)
+            qb = to_f64(q[:, blk, h:h + 1])                            # [1, block, 1, D]
+            s = O.pool(qb, w.block)[0, 0, 0] @ kbar.T                  # [nb]
+            check_idx(gidx[0, h, i][None], s[None], topk)
+            qfull[:, blk] = qb
+            ref = O.attend(qfull, kg, vg, gidx[:, h:h + 1], w.block, 1 / math.sqrt(w.D),
+                           rows=[(0, 0, i)])
+            qfull[:, blk] = 0.0
+            check_out(out[0, blk, h].float().cpu().numpy(), ref[0, blk, 0], "bf16")
+        say(f"  kv head {g} ok")
