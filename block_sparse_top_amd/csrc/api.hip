@@ -173,7 +173,12 @@ int bsattn_forward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int 
                                               scale, out, s),
                       "fp32 attention launch");
   }
-  return fail(BSATTN_E_UNSUPPORTED, "fp8 attention is not built yet");
+  if (!bsattn::attn_fp8_supported(D, block))
+    return fail(BSATTN_E_UNSUPPORTED, "fp8 attention for D=%d block=%d (supported: D=128)", D,
+                block);
+  return hip_status(bsattn::launch_attn_fp8(B, N, Hq, Hkv, D, block, topk, q, k, v, idx, scale,
+                                            descale_qkv, out, s),
+                    "fp8 attention launch");
 }
 
 }  // extern "C"

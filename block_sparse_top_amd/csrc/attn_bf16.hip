@@ -141,23 +141,28 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
   // The transfers are issued from inline asm so that the compiler's wait-count pass, which
   // cannot tell the K and V buffers apart, does not add full vmcnt(0) waits before every LDS
   // read; the waits below are placed by hand (each wave issues exactly DMA transfers per tile
-  // and no other vector-memory instruction inside the loop).
+  // and no other vector-memory instruction inside the loop). M0 (the LDS destination) is
+  // saved and restored around them.
   static_assert(C::DMA == 8, "the transfer sequence below issues 8 spans of 1 KiB");
   auto dma = [&](const char* src_base, char* dst) {
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(lds_void*)dst + wave * C::DMA * 1024);
+    uint32_t m0_saved;
     asm volatile(
-        "s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %9\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %9\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %9\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %9\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %9\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %9\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, %9\n\t"
-        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %8, %9"
-        :: "s"(lds0), "v"(goff[0]), "v"(goff[1]), "v"(goff[2]), "v"(goff[3]), "v"(goff[4]),
-           "v"(goff[5]), "v"(goff[6]), "v"(goff[7]), "s"(src_base)
-        : "memory", "m0", "scc");
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %10\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %10\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %10\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %10\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %10\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, %10\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %8, %10\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %9, %10\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0_saved)
+        : "s"(lds0), "v"(goff[0]), "v"(goff[1]), "v"(goff[2]), "v"(goff[3]), "v"(goff[4]),
+          "v"(goff[5]), "v"(goff[6]), "v"(goff[7]), "s"(src_base)
+        : "memory", "scc");
   };
 
   // LDS read offsets of this lane

@@ -40,4 +40,12 @@ hipError_t launch_attn_f32(int64_t B, int64_t N, int Hq, int Hkv, int D, int blo
                            const void* q, const void* k, const void* v, const int32_t* idx,
                            float scale, void* out, hipStream_t stream);
 
+// Step 4, OCP fp8 e4m3 inputs on the fp8 MFMA, bf16 output. Supported: D = 128,
+// block in {64, 128}. descale_qkv: host array of the three per-tensor descales.
+bool attn_fp8_supported(int D, int block);
+hipError_t launch_attn_fp8(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
+                           const void* q, const void* k, const void* v, const int32_t* idx,
+                           float scale, const float* descale_qkv, void* out,
+                           hipStream_t stream);
+
 }  // namespace bsattn

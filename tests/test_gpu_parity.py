@@ -346,3 +346,70 @@ def test_long_context_gqa_sampled():
             qfull[:, blk] = 0.0
             check_out(out[0, blk, h].float().cpu().numpy(), ref[0, blk, 0], "bf16")
         say(f"  kv head {g} ok")
+
+
+FP8_SHAPES = [
+    # B, N, Hq, Hkv, D, block, topk (the fp8 kernel is built for D = 128)
+    (1, 64 * 8, 2, 2, 128, 64, 8),          # topk = nb: dense limit
+    (2, 64 * 37, 4, 2, 128, 64, 11),        # ragged nb, GQA 2
+    (1, 128 * 21, 6, 3, 128, 128, 5),       # block 128
+    (1, 64 * 40, 2, 2, 128, 64, 1),         # topk = 1
+]
+
+
+@pytest.mark.parametrize("shape", FP8_SHAPES, ids=str)
+def test_forward_fp8(shape):
+    B, N, Hq, Hkv, D, blk, topk = shape
+    say(f"[forward fp8] shape={shape}")
+    q, k, v, ds = make(B, N, Hq, Hkv, D, "fp8", index=19)
+    idx = bst.select(q, k, blk, topk)
+    out = torch.full((B, N, Hq, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    bst.forward(q, k, v, idx, descales=ds, out=out)
+    torch.cuda.synchronize()
+    qo, ko, vo = oracle_inputs(q, k, v, ds)
+    gidx = idx.cpu().numpy()
+    check_idx(gidx, O.block_scores(O.pool(qo, blk), O.pool(ko, blk)), topk)
+    ref = O.attend_batched(qo, ko, vo, gidx, blk, 1.0 / math.sqrt(D))
+    vmax = float(np.abs(vo).max())
+    err = check_out(out.float().cpu().numpy(), ref, "fp8", fp8_v=(vmax, topk * blk))
+    say("   max_abs, rel_l2 =", err)
+    if topk == 1 or topk == N // blk:
+        return
+    # negative control at this bound: one dropped block of a few is caught
+    few = idx[..., :3].contiguous() if topk > 3 else idx
+    out3 = bst.forward(q, k, v, few, descales=ds).float().cpu().numpy()
+    g3 = few.cpu().numpy()
+    dropped = O.attend_batched(qo, ko, vo, g3[..., :-1], blk, 1.0 / math.sqrt(D))
+    with pytest.raises(AssertionError):
+        check_out(out3, dropped, "fp8", fp8_v=(vmax, 2 * blk))
+
+
+def test_fp8_workload_sampled():
+    """The fp8 workload at full size: every selection row vs the oracle (pooled per batch
+    element), sampled query blocks of the output."""
+    w = syn.WORKLOADS["fp8_n65536"]
+    say("[fp8 workload]", w)
+    q, k, v, ds, _ = syn.workload_inputs(w, device=DEV)
+    topk = O.topk_count(w.ratio, w.nb)
+    idx = bst.select(q, k, w.block, topk)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    bst.forward(q, k, v, idx, descales=ds, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+    gidx = idx.cpu().numpy()
+    for b in range(w.B):
+        qb, kb = to_f64(q[b:b + 1], ds[0]), to_f64(k[b:b + 1], ds[1])
+        check_idx(gidx[b:b + 1], O.block_scores(O.pool(qb, w.block), O.pool(kb, w.block)), topk)
+    say("  selection ok")
+    rows = syn.sample_rows(16, w.B * w.Hq * w.nb, w.index)
+    picks = [(r // (w.Hq * w.nb), (r // w.nb) % w.Hq, r % w.nb) for r in rows]
+    for b in sorted({p[0] for p in picks}):
+        qb, kb, vb = (to_f64(x[b:b + 1], d) for x, d in zip((q, k, v), ds))
+        mine = [(0, h, i) for bb, h, i in picks if bb == b]
+        ref = O.attend(qb, kb, vb, gidx[b:b + 1], w.block, 1 / math.sqrt(w.D), rows=mine)
+        got = out[b:b + 1].float().cpu().numpy()
+        vmax = float(np.abs(vb).max())
+        for (_, h, i) in mine:
+            sl = (0, slice(i * w.block, (i + 1) * w.block), h)
+            check_out(got[sl], ref[sl], "fp8", fp8_v=(vmax, topk * w.block))
+    say("  sampled outputs ok")

@@ -74,3 +74,46 @@ def test_ambiguous_rows_accept_any_valid_choice():
     assert stats["ambiguous"] == 1
     with pytest.raises(AssertionError):
         check_idx(np.array([[[0, 1]]]), S, 2)
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Nearest e4m3 value of x >= 0 (the grid decoded by the oracle from all 256 codes)."""
+    grid = O.decode_e4m3(np.arange(128, dtype=np.uint8))        # +0 .. 448, ascending
+    grid = np.sort(grid[np.isfinite(grid)])
+    j = np.clip(np.searchsorted(grid, x), 1, grid.size - 1)
+    lo, hi = grid[j - 1], grid[j]
+    return np.where(x - lo <= hi - x, lo, hi)
+
+
+def fp8_weight_output(q, kk, v, idx, blk, scale):
+    """Attention with every softmax weight exp2(z - max + 7) rounded to e4m3 and the exact
+    normaliser: the arithmetic the fp8 rule bounds."""
+    B, N, H, D = q.shape
+    out = np.zeros_like(q)
+    for b in range(B):
+        for h in range(H):
+            for i in range(N // blk):
+                keys = np.concatenate([np.arange(j * blk, (j + 1) * blk) for j in idx[b, h, i]])
+                z = q[b, i * blk:(i + 1) * blk, h] @ kk[b, keys, h].T * scale * math.log2(math.e)
+                p = np.exp2(z - z.max(axis=1, keepdims=True) + 7)
+                out[b, i * blk:(i + 1) * blk, h] = (e4m3_round(p) @ v[b, keys, h]) / p.sum(1)[:, None]
+    return out
+
+
+def test_fp8_rule_accepts_e4m3_weights_and_rejects_one_bad_row():
+    q, kk, v, S, idx, out, blk, k, D = setup(3)
+    fp8 = fp8_weight_output(q, kk, v, idx, blk, 1 / math.sqrt(D))
+    vmax = float(np.abs(v).max())
+    max_abs, rel = check_out(fp8, out, "fp8", fp8_v=(vmax, k * blk))
+    assert 1e-3 < rel < 5e-2 and max_abs > 0          # the rounding is visible, and within
+    # one query row attending to one wrong block: the tensor-wide figures dilute it, the
+    # per-row figure does not
+    sw = idx.copy()
+    sw[0, 1, 3, 0] = next(j for j in range(12) if j not in sw[0, 1, 3])
+    bad = O.attend(q, kk, v, sw, blk, 1 / math.sqrt(D), rows=[(0, 1, 3)])
+    one_row = fp8.copy()
+    one_row[0, 3 * blk + 5, 1] = bad[0, 3 * blk + 5, 1]
+    with pytest.raises(AssertionError):
+        check_out(one_row, out, "fp8", fp8_v=(vmax, k * blk))
+    with pytest.raises(AssertionError):
+        check_out(fp8, out, "fp8")                    # fp8 needs its bound's inputs
