@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/bsattn.h"
@@ -28,6 +29,12 @@ int hip_status(hipError_t e, const char* what) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// BSATTN_VALIDATE=1 in the environment: bsattn_forward checks idx on the GPU first
+bool validate_enabled() {
+  const char* v = getenv("BSATTN_VALIDATE");
+  return v && v[0] == '1' && v[1] == 0;
+}
 
 // Shape checks common to both entry points. Returns BSATTN_OK or an error with detail.
 int check_shape(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk) {
@@ -159,6 +166,16 @@ int bsattn_forward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)idx & 3u))
     return fail(BSATTN_E_INVALID, "q, k, v, out must be 16-byte aligned, idx 4-byte aligned");
   hipStream_t s = (hipStream_t)stream;
+  if (validate_enabled()) {
+    unsigned int bad = 0;
+    const int64_t nb = N / block;
+    st = hip_status(bsattn::validate_idx(B * Hq * nb, topk, (int)nb, idx, s, &bad),
+                    "idx validation");
+    if (st != BSATTN_OK) return st;
+    if (bad)
+      return fail(BSATTN_E_INVALID, "idx: %u rows are not strictly ascending in [0, nb=%lld)",
+                  bad, (long long)nb);
+  }
   if (dtype == BSATTN_BF16) {
     if (!bsattn::attn_bf16_supported(D, block))
       return fail(BSATTN_E_UNSUPPORTED, "bf16 attention for D=%d block=%d", D, block);

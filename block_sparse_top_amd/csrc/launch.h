@@ -48,4 +48,10 @@ hipError_t launch_attn_fp8(int64_t B, int64_t N, int Hq, int Hkv, int D, int blo
                            float scale, const float* descale_qkv, void* out,
                            hipStream_t stream);
 
+// Checks every idx row (topk values, strictly ascending, in [0, nb)); waits for the stream and
+// returns the number of failing rows in *bad_rows. Uses one device-global counter per device:
+// concurrent validations on one device race.
+hipError_t validate_idx(int64_t rows, int topk, int nb, const int32_t* idx, hipStream_t stream,
+                        unsigned int* bad_rows);
+
 }  // namespace bsattn

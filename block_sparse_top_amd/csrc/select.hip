@@ -56,7 +56,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   float* ks = smem;                         // [64][D+1] current key-block chunk
   float* qs = smem + 64 * KS;               // [RG][D] pooled query rows of this work-group
 
-  const int tile = blockIdx.x;
+  // work-groups of one (batch, head) read the same pooled keys: keep them on one XCD's L2
+  const int tile = (int)xcd_remap(blockIdx.x, gridDim.x);
   const int rt = tile % row_tiles;
   const int bh = tile / row_tiles;          // b * Hq + h
   const int h = bh % Hq, b = bh / Hq;

@@ -32,7 +32,8 @@ __global__ __launch_bounds__(64) void score_gemm_kernel(const float* __restrict_
                                                         float* __restrict__ S, int Hq, int Hkv,
                                                         int nb, int D, int tiles) {
   // tile index: (b*Hq + h) * tiles^2 + ti * tiles + tj, 64x64 each
-  const int64_t t = blockIdx.x;
+  // tiles of one (batch, head) share their pooled rows: keep them on one XCD's L2
+  const int64_t t = xcd_remap(blockIdx.x, gridDim.x);
   const int tj = (int)(t % tiles), ti = (int)((t / tiles) % tiles);
   const int64_t bh = t / ((int64_t)tiles * tiles);
   const int h = (int)(bh % Hq), b = (int)(bh / Hq);

@@ -1,0 +1,50 @@
+// Optional check of the selected-block indices handed to bsattn_forward (enabled by the
+// environment variable BSATTN_VALIDATE=1): every row must hold topk values in [0, nb), strictly
+// ascending. The attention kernels themselves only guard against out-of-range values (such a
+// row's output becomes NaN); duplicates or a wrong order would silently change the result.
+#include "common.h"
+#include "launch.h"
+
+namespace bsattn {
+namespace {
+
+// rows that failed the check since the last reset (one counter per device)
+__device__ unsigned int g_bad_rows;
+
+__global__ void reset_kernel() { g_bad_rows = 0u; }
+
+// one thread per row
+__global__ __launch_bounds__(256) void validate_kernel(const int32_t* __restrict__ idx,
+                                                       int64_t rows, int topk, int nb) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  const int32_t* row = idx + r * topk;
+  bool ok = true;
+  int prev = -1;
+  for (int j = 0; j < topk; ++j) {
+    const int x = row[j];
+    ok &= x > prev && x < nb;
+    prev = x;
+  }
+  if (!ok) atomicAdd(&g_bad_rows, 1u);
+}
+
+}  // namespace
+
+hipError_t validate_idx(int64_t rows, int topk, int nb, const int32_t* idx, hipStream_t stream,
+                        unsigned int* bad_rows) {
+  *bad_rows = 0;
+  if (rows == 0) return hipSuccess;
+  reset_kernel<<<1, 1, 0, stream>>>();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  validate_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(idx, rows, topk, nb);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipMemcpyFromSymbolAsync(bad_rows, HIP_SYMBOL(g_bad_rows), sizeof(unsigned int), 0,
+                               hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return e;
+  return hipStreamSynchronize(stream);
+}
+
+}  // namespace bsattn

@@ -17,14 +17,17 @@
  *     idx is [B, Hq, nb, topk] int32 with nb = N / block.
  *   - GQA: query head h reads KV head h / (Hq / Hkv); selection is per query head.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null stream),
- *     never synchronises, never allocates or frees device memory, and keeps no state
- *     between calls. Argument checks run on the host before any launch.
+ *     never synchronises (except the optional idx validation of bsattn_forward), never
+ *     allocates or frees device memory, and keeps no state between calls. Argument checks
+ *     run on the host before any launch.
  *   - Errors are returned, never thrown or printed: the return value is a bsattn_status;
  *     bsattn_last_error() gives a text detail of the last failure on the calling thread.
  *     Launch failures come back as BSATTN_E_HIP. Kernel faults surface at the caller's
  *     next synchronisation.
- *   - Supported now: D in {64, 128}; block in {64, 128}; nb <= 1024 for selection;
- *     storage dtypes fp32, bf16 and OCP fp8 e4m3. Other sizes give BSATTN_E_UNSUPPORTED.
+ *   - Supported now: D in {64, 128}; block in {64, 128}; storage dtypes fp32, bf16 and OCP
+ *     fp8 e4m3 (fp8 attention: D = 128). Selection: nb <= 1024, or nb a multiple of 64 up
+ *     to 8192 (the score matrix then goes through the workspace). Other sizes give
+ *     BSATTN_E_UNSUPPORTED.
  *   - B == 0 or N == 0 is an empty call: arguments are checked, nothing is launched
  *     (topk must then be 0 when nb == 0).
  */
@@ -66,7 +69,8 @@ const char* bsattn_last_error(void);
 
 /* Bytes of device workspace bsattn_select needs for these sizes (0 for an empty call).
  * Layout, each part 256-byte aligned: pooled q, fp32 [B, Hq, nb, D]; then pooled k,
- * fp32 [B, Hkv, nb, D]. For fp8 inputs the pooled values are means of the e4m3 codes'
+ * fp32 [B, Hkv, nb, D]; when nb > 1024 also the score matrix, fp32 [B, Hq, nb, nb]
+ * (MSA page §3.2: 1M tokens at block 128 give 8192 key blocks per row). For fp8 inputs the pooled values are means of the e4m3 codes'
  * values without the per-tensor descale (a positive factor that does not change the
  * selection). Returns 0 and records an error for invalid sizes. */
 size_t bsattn_select_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int D, int block);
@@ -102,13 +106,18 @@ int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int b
  *   out[b,t,h,:] = sum over keys u in the blocks idx[b,h,i,:] of
  *                  softmax_u(scale * q[b,t,h,:] . k[b,u,g,:]) * v[b,u,g,:].
  *   Scores and the softmax state are fp32; fp32 inputs compute in fp32, bf16 inputs multiply
- *   on bf16 MFMA with the probabilities rounded to bf16, fp8 inputs multiply on fp8 MFMA.
+ *   on bf16 MFMA with the probabilities rounded to bf16, fp8 inputs multiply on the fp8 MFMA
+ *   with the probabilities rounded to e4m3 (values = codes * descale_qkv).
  * Arguments
  *   dtype, B, N, Hq, Hkv, D, block, topk  as for bsattn_select.
  *   q, k, v      device pointers, 16-byte aligned.
  *   idx          device pointer, int32 [B, Hq, nb, topk]; each row should hold distinct
  *                blocks in [0, nb). A row with an out-of-range entry is not read out of
  *                bounds: its output rows are set to NaN. Duplicate entries count twice.
+ *                With BSATTN_VALIDATE=1 in the environment every row is first checked on
+ *                the GPU (strictly ascending, in [0, nb)); a failing row makes the call
+ *                return BSATTN_E_INVALID before the attention launch. This mode waits for
+ *                the stream, and concurrent validating calls on one device race.
  *   scale        finite softmax scale (the page uses 1/sqrt(D)).
  *   descale_qkv  host pointer to 3 floats (q, k, v per-tensor descales) for fp8; ignored
  *                (may be NULL) for other dtypes. Must be finite and > 0.

@@ -200,6 +200,34 @@ def test_invalid_index_poisons_only_its_rows():
     assert torch.equal(o[mask], r[mask])
 
 
+def test_validate_mode_rejects_bad_rows(monkeypatch):
+    """BSATTN_VALIDATE=1: forward checks idx on the GPU (ascending, in range) and returns
+    BSATTN_E_INVALID for a bad row; valid rows give the same output as without the check."""
+    say("[validate mode]")
+    B, N, H, D, blk, topk = 2, 64 * 8, 2, 64, 64, 3
+    q, k, v, ds = make(B, N, H, H, D, "bf16", index=16)
+    idx = bst.select(q, k, blk, topk)
+    ref = bst.forward(q, k, v, idx)
+    monkeypatch.setenv("BSATTN_VALIDATE", "1")
+    out = bst.forward(q, k, v, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    for name, edit in [("out of range", lambda t: t.__setitem__((1, 1, 5, 2), 8)),
+                       ("negative", lambda t: t.__setitem__((0, 0, 0, 0), -1)),
+                       ("descending", lambda t: t.__setitem__((0, 1, 3), t[0, 1, 3].flip(0))),
+                       ("duplicate", lambda t: t.__setitem__((1, 0, 7, 1), t[1, 0, 7, 0]))]:
+        bad = idx.clone()
+        edit(bad)
+        with pytest.raises(bst.BsattnError) as e:
+            bst.forward(q, k, v, bad)
+        assert e.value.status == 1 and "1 rows" in str(e.value), (name, str(e.value))
+    monkeypatch.delenv("BSATTN_VALIDATE")
+    bad = idx.clone()
+    bad[0, 1, 3] = bad[0, 1, 3].flip(0)
+    bst.forward(q, k, v, bad)                         # unchecked: accepted
+    torch.cuda.synchronize()
+
+
 def test_mutated_indices_fail_parity():
     """Negative control: the output check catches one dropped or swapped block."""
     say("[mutation]")
