@@ -29,10 +29,20 @@ the design notes of the repository):
   R4  ties between equal scores go to the lower key-block index;
   R5  the selected indices of a row are returned in ascending block order;
   R7  N must be a multiple of the block size (the sketch's .view needs it);
-  R8  no causal mask;
+  R8  no causal mask in the pages' method; the causal variant (R20) is an option;
   R10 GQA: query head h reads KV head h // (Hq // Hkv); selection is per query head;
   R15 fp8 inputs are OCP e4m3 ("fn": no infinities, S.1111.111 is NaN) codes times a
       per-tensor descale.
+  R20 causal variant: query block i may select key blocks j <= i only; its own block i is
+      always selected and the other min(k, i+1) - 1 places go to the best-scoring j < i
+      (ties to the lower j); unused places of a row hold -1; inside the own block query t
+      sees keys u <= t. (The MSA page names MoBA among the block-based methods and checks
+      that weights concentrate near the diagonal; the pages give no causal rule.)
+  R21 in-block max pooling: the "in-block extremum" scoring of the MSA page's §2.2 table
+      read as the elementwise maximum over the block's tokens, for q and k alike.
+  R22 group-shared selection (GQA, MSA §3.1): one selection per KV head from the sum of
+      the block scores of its query heads (equivalently, from the summed pooled queries);
+      every query head of the group uses it.
 
 Every function below is pinned by the CPU tests (tests/test_oracle_*.py) against
 closed forms, library routines, brute force or invariants; none is "parity unpinned".
@@ -112,6 +122,18 @@ def pool(x: np.ndarray, block: int) -> np.ndarray:
     return x.reshape(B, nb, block, H, D).mean(axis=2).transpose(0, 2, 1, 3)
 
 
+def pool_max(x: np.ndarray, block: int) -> np.ndarray:
+    """Elementwise maximum over the `block` tokens of every block, per head [R21].
+
+    x: [B, N, H, D] float64 -> [B, H, nb, D] float64.
+    """
+    B, N, H, D = x.shape
+    if N % block:
+        raise ValueError("N must be a multiple of the block size")
+    nb = N // block
+    return x.reshape(B, nb, block, H, D).max(axis=2).transpose(0, 2, 1, 3)
+
+
 def kv_head(h: int, Hq: int, Hkv: int) -> int:
     """KV head read by query head h under GQA [MSA §3.1; R10]."""
     return h // (Hq // Hkv)
@@ -154,6 +176,36 @@ def select_topk(S: np.ndarray, k: int) -> np.ndarray:
     return idx.astype(np.int64)
 
 
+def select_topk_causal(S: np.ndarray, k: int) -> np.ndarray:
+    """Causal selection [R20]: row i (the query block, second-to-last axis) keeps its own
+    block i and the min(k, i+1) - 1 best blocks among j < i (ties to the lower j, as in
+    `select_topk`); ascending order; places past min(k, i+1) hold -1.
+    Returns int64 [..., nb, k].
+    """
+    nb = S.shape[-1]
+    if S.shape[-2] != nb or not 1 <= k <= nb:
+        raise ValueError("square score rows and k in [1, nb] required")
+    out = np.full(S.shape[:-1] + (k,), -1, dtype=np.int64)
+    for i in range(nb):
+        ki = min(k, i + 1)
+        row = out[..., i, :]
+        if ki > 1:
+            row[..., :ki - 1] = select_topk(S[..., i, :i], ki - 1)   # over j < i
+        row[..., ki - 1] = i                                      # own block, largest index
+    return out
+
+
+def group_scores(S: np.ndarray, Hkv: int) -> np.ndarray:
+    """Block scores of a KV head group: the sum over its query heads [R22].
+
+    S [B, Hq, nb, nb] -> [B, Hkv, nb, nb]; query heads g*G .. g*G+G-1 form group g.
+    """
+    B, Hq, nb, nbk = S.shape
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return S.reshape(B, Hkv, Hq // Hkv, nb, nbk).sum(axis=2)
+
+
 def kth_scores(S: np.ndarray, k: int):
     """(s_k, s_{k+1}): the k-th and (k+1)-th largest score of every row.
 
@@ -166,13 +218,14 @@ def kth_scores(S: np.ndarray, k: int):
 
 
 def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, block: int,
-           scale: float, rows=None) -> np.ndarray:
+           scale: float, rows=None, causal: bool = False) -> np.ndarray:
     """Exact softmax attention of every query block over its selected key blocks
-    [SF step 3; MSA §2.1, §2.2; R8, R10].
+    [SF step 3; MSA §2.1, §2.2; R8, R10; R20 when causal].
 
     q [B, N, Hq, D], k/v [B, N, Hkv, D] float64; idx [B, Hq, nb, topk] (a set of key
-    blocks per query block and head). For query t of block i the keys are the union of
-    blocks idx[b,h,i,:] of KV head kv(h); weights softmax(scale * q_t . k_u).
+    blocks per query block and head; entries -1 are unused places). For query t of block i
+    the keys are the union of blocks idx[b,h,i,:] of KV head kv(h); weights
+    softmax(scale * q_t . k_u); causal: only keys u <= t.
     rows: optional list of (b, h, i) to compute; the others are left NaN.
     Returns out [B, N, Hq, D] float64.
     """
@@ -184,22 +237,27 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, block: 
         rows = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(nb)]
     for (b, h, i) in rows:
         g = kv_head(h, Hq, Hkv)
-        tok = np.concatenate([np.arange(j * block, (j + 1) * block) for j in idx[b, h, i]])
+        tok = np.concatenate([np.arange(j * block, (j + 1) * block)
+                              for j in idx[b, h, i] if j >= 0])
         Qi = q[b, i * block:(i + 1) * block, h, :]           # [block, D]
-        Ku = k[b, tok, g, :]                                 # [topk*block, D]
+        Ku = k[b, tok, g, :]                                 # [keys, D]
         Vu = v[b, tok, g, :]
         z = scale * (Qi @ Ku.T)
+        if causal:
+            t = np.arange(i * block, (i + 1) * block)
+            z = np.where(tok[None, :] <= t[:, None], z, -np.inf)
         p = np.exp(z - z.max(axis=1, keepdims=True))
         out[b, i * block:(i + 1) * block, h, :] = (p @ Vu) / p.sum(axis=1, keepdims=True)
     return out
 
 
-def attend_batched(q, k, v, idx, block, scale, bh=None) -> np.ndarray:
+def attend_batched(q, k, v, idx, block, scale, bh=None, causal: bool = False) -> np.ndarray:
     """`attend` over all query blocks of the (b, h) pairs in `bh` at once.
 
     Same arithmetic as `attend` (gather the selected key blocks, scaled product,
     max-shifted exponent, weighted sum over the normaliser), with the gather and the
-    products done for a whole (b, h) per library call. Used for large sizes only.
+    products done for a whole (b, h) per library call. Unused places (-1) and, causal,
+    keys after the query are masked with -inf. Used for large sizes only.
     """
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -211,35 +269,49 @@ def attend_batched(q, k, v, idx, block, scale, bh=None) -> np.ndarray:
         g = kv_head(h, Hq, Hkv)
         Kb = k[b, :, g, :].reshape(nb, block, D)
         Vb = v[b, :, g, :].reshape(nb, block, D)
-        Ku = Kb[idx[b, h]].reshape(nb, -1, D)               # [nb, topk*block, D]
-        Vu = Vb[idx[b, h]].reshape(nb, -1, D)
+        sel = idx[b, h]                                      # [nb, topk]
+        used = sel >= 0
+        safe = np.where(used, sel, 0)
+        Ku = Kb[safe].reshape(nb, -1, D)                     # [nb, topk*block, D]
+        Vu = Vb[safe].reshape(nb, -1, D)
         Qb = q[b, :, h, :].reshape(nb, block, D)
         z = scale * np.matmul(Qb, Ku.transpose(0, 2, 1))     # [nb, block, topk*block]
+        keep = np.repeat(used, block, axis=1)[:, None, :]    # [nb, 1, topk*block]
+        if causal:
+            u = (safe[:, :, None] * block + np.arange(block)).reshape(nb, 1, -1)
+            t = np.arange(N).reshape(nb, block, 1)
+            keep = keep & (u <= t)
+        z = np.where(keep, z, -np.inf)
         p = np.exp(z - z.max(axis=2, keepdims=True))
         o = np.matmul(p, Vu) / p.sum(axis=2, keepdims=True)
         out[b, :, h, :] = o.reshape(N, D)
     return out
 
 
-def dense_attention(q, k, v, scale) -> np.ndarray:
-    """Full softmax(scale * Q K^T) V per head, no mask [MSA §2.1, full-attention mask]."""
+def dense_attention(q, k, v, scale, causal: bool = False) -> np.ndarray:
+    """Full softmax(scale * Q K^T) V per head [MSA §2.1, full-attention mask]; causal:
+    query t sees keys u <= t only."""
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
     out = np.empty(q.shape, dtype=np.float64)
+    lower = np.tril(np.ones((N, N), dtype=bool))
     for b in range(B):
         for h in range(Hq):
             g = kv_head(h, Hq, Hkv)
             z = scale * (q[b, :, h, :] @ k[b, :, g, :].T)
+            if causal:
+                z = np.where(lower, z, -np.inf)
             p = np.exp(z - z.max(axis=1, keepdims=True))
             out[b, :, h, :] = (p @ v[b, :, g, :]) / p.sum(axis=1, keepdims=True)
     return out
 
 
-def masked_attention_bruteforce(q, k, v, idx, block, scale) -> np.ndarray:
+def masked_attention_bruteforce(q, k, v, idx, block, scale, causal: bool = False) -> np.ndarray:
     """Softmax(Mask(scale * Q K^T)) V with an explicit N x N token mask [MSA §2.1].
 
     M[t, u] is true when key u's block is among the blocks selected for query t's
-    block; masked positions get -inf before the softmax. Tiny sizes only.
+    block (and, causal, u <= t); masked positions get -inf before the softmax. Tiny sizes
+    only.
     """
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -251,15 +323,30 @@ def masked_attention_bruteforce(q, k, v, idx, block, scale) -> np.ndarray:
             M = np.zeros((N, N), dtype=bool)
             for t in range(N):
                 M[t] = np.isin(tb, idx[b, h, tb[t]])
+                if causal:
+                    M[t, t + 1:] = False
             z = np.where(M, scale * (q[b, :, h, :] @ k[b, :, g, :].T), -np.inf)
             p = np.exp(z - z.max(axis=1, keepdims=True))
             out[b, :, h, :] = (p @ v[b, :, g, :]) / p.sum(axis=1, keepdims=True)
     return out
 
 
-def select(q, k, block: int, topk: int) -> np.ndarray:
-    """Steps 1-2 [SF]: pool q and k, score the blocks, keep the top-k per row."""
-    return select_topk(block_scores(pool(q, block), pool(k, block)), topk)
+def select(q, k, block: int, topk: int, causal: bool = False, pooling: str = "mean",
+           group: bool = False) -> np.ndarray:
+    """Steps 1-2 [SF]: pool q and k, score the blocks, keep the top-k per row.
+
+    causal [R20], pooling "mean" [SF] or "max" [R21], group: one selection per KV head
+    group, repeated for each of its query heads [R22]. Returns [B, Hq, nb, topk].
+    """
+    pf = pool if pooling == "mean" else pool_max
+    S = block_scores(pf(q, block), pf(k, block))
+    Hq, Hkv = q.shape[2], k.shape[2]
+    if group:
+        S = group_scores(S, Hkv)
+    idx = select_topk_causal(S, topk) if causal else select_topk(S, topk)
+    if group:
+        idx = np.repeat(idx, Hq // Hkv, axis=1)
+    return idx
 
 
 def block_sparse_attention(q, k, v, block_size=64, topk_ratio=0.3, scale=None):

@@ -223,9 +223,98 @@ def check_batched(o=O):
     assert np.allclose(a, b, rtol=0, atol=1e-13)
 
 
+def check_causal_select(o=O):
+    """Causal selection [R20] against a full sort of each row's admissible blocks."""
+    r = rng(11)
+    for k in (1, 3, 7):
+        S = np.round(r.standard_normal((2, 3, 9, 9)), 1)       # coarse values: many ties
+        idx = o.select_topk_causal(S, k)
+        for b in range(2):
+            for h in range(3):
+                for i in range(9):
+                    ki = min(k, i + 1)
+                    # stable sort of j < i by descending score, then the own block
+                    past = np.lexsort((np.arange(i), -S[b, h, i, :i]))[:ki - 1]
+                    want = sorted(past.tolist() + [i]) + [-1] * (k - ki)
+                    assert idx[b, h, i].tolist() == want
+    assert o.select_topk_causal(np.zeros((1, 4, 4)), 2).tolist() == [[[0, -1], [0, 1], [0, 2],
+                                                                       [0, 3]]]
+
+
+def check_causal_dense_limit(o=O):
+    """Causal with topk = nb: every earlier block is kept, the result is causal dense
+    attention (library SDPA with is_causal, float64)."""
+    B, N, H, D, blk = 1, 64, 2, 16, 8
+    q, k, v = rand_qkv(B, N, H, H, D, seed=12)
+    nb = N // blk
+    idx = o.select(q, k, blk, nb, causal=True)
+    got = o.attend(q, k, v, idx, blk, 1 / math.sqrt(D), causal=True)
+    tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    ref = ref.permute(0, 2, 1, 3).numpy()
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+    assert np.allclose(o.dense_attention(q, k, v, 1 / math.sqrt(D), causal=True), ref,
+                       rtol=0, atol=1e-12)
+
+
+def check_causal_bruteforce(o=O):
+    """Causal gathered-block attention equals the explicit N x N mask with u <= t."""
+    B, N, Hq, Hkv, D, blk = 1, 512, 4, 2, 32, 64
+    q, k, v = rand_qkv(B, N, Hq, Hkv, D, seed=13)
+    idx = o.select(q, k, blk, 3, causal=True)
+    got = o.attend(q, k, v, idx, blk, 0.2, causal=True)
+    ref = o.masked_attention_bruteforce(q, k, v, idx, blk, 0.2, causal=True)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+    assert np.allclose(o.attend_batched(q, k, v, idx, blk, 0.2, causal=True), got,
+                       rtol=0, atol=1e-13)
+    # the first token of every sequence sees only itself
+    kr = np.repeat(k, Hq // Hkv, axis=2)
+    vr = np.repeat(v, Hq // Hkv, axis=2)
+    assert np.allclose(got[:, 0], vr[:, 0], rtol=0, atol=1e-14)
+    assert kr.shape == q.shape
+
+
+def check_pool_max(o=O):
+    """In-block max pooling [R21] against torch.amax, and its invariances."""
+    B, N, H, D, blk = 2, 96, 3, 8, 16
+    q, _, _ = rand_qkv(B, N, H, H, D, seed=14)
+    got = o.pool_max(q, blk)
+    ref = torch.from_numpy(q).reshape(B, N // blk, blk, H, D).amax(dim=2).permute(0, 2, 1, 3)
+    assert np.array_equal(got, ref.numpy())
+    perm = np.concatenate([j * blk + rng(15).permutation(blk) for j in range(N // blk)])
+    assert np.array_equal(o.pool_max(q[:, perm], blk), got)
+    assert np.all(got >= o.pool(q, blk))
+    a = o.select(q, q[:, :, :1], blk, 2, pooling="max")
+    S = o.block_scores(got, o.pool_max(q[:, :, :1], blk))
+    assert np.array_equal(a, o.select_topk(S, 2))
+
+
+def check_group_select(o=O):
+    """Group-shared selection [R22]: scores of the summed pooled queries of the group,
+    one index set per group; G = 1 is per-head selection."""
+    B, N, Hq, Hkv, D, blk = 2, 128, 6, 2, 8, 16
+    q, k, _ = rand_qkv(B, N, Hq, Hkv, D, seed=16)
+    G = Hq // Hkv
+    idx = o.select(q, k, blk, 3, group=True)
+    qb, kb = o.pool(q, blk), o.pool(k, blk)
+    for b in range(B):
+        for g in range(Hkv):
+            qsum = sum(qb[b, g * G + j] for j in range(G))          # [nb, D]
+            S = qsum @ kb[b, g].T
+            want = o.select_topk(S[None], 3)[0]
+            for j in range(G):
+                assert np.array_equal(idx[b, g * G + j], want)
+    q1 = q[:, :, :Hkv]
+    assert np.array_equal(o.select(q1, k, blk, 3, group=True), o.select(q1, k, blk, 3))
+    ci = o.select(q, k, blk, 3, group=True, causal=True)
+    assert np.array_equal(ci[:, 0], ci[:, 1]) and np.all(ci[:, :, 0, 1:] == -1)
+
+
 ALL_CHECKS = [check_bf16_widen, check_e4m3, check_pool, check_scores, check_select_vs_sort,
               check_select_special, check_dense_limit, check_bruteforce, check_ties_and_zero,
-              check_invariants, check_gqa, check_batched]
+              check_invariants, check_gqa, check_batched, check_causal_select,
+              check_causal_dense_limit, check_causal_bruteforce, check_pool_max,
+              check_group_select]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -266,6 +355,29 @@ def test_rejects():
 
 # ---------------------------------------------------- planted mistakes (CPU)
 
+def _strict_causal(q, k, v, idx, blk, scale, rows=None, causal=False):
+    """attend with the causal mask u < t (a key never sees itself): a planted mistake."""
+    if not causal:
+        return O.attend(q, k, v, idx, blk, scale, rows)
+    out = O.attend(q, k, v, idx, blk, scale, rows, causal=True)
+    B, N, Hq, D = q.shape
+    # recompute rows t > 0 of every block without the diagonal term
+    Hkv = k.shape[2]
+    for b in range(B):
+        for h in range(Hq):
+            g = O.kv_head(h, Hq, Hkv)
+            for i in range(N // blk):
+                tok = np.concatenate([np.arange(j * blk, (j + 1) * blk) for j in idx[b, h, i] if j >= 0])
+                for t in range(i * blk, (i + 1) * blk):
+                    keys = tok[tok < t]
+                    if keys.size == 0:
+                        continue
+                    z = scale * (k[b, keys, g] @ q[b, t, h])
+                    p = np.exp(z - z.max())
+                    out[b, t, h] = p @ v[b, keys, g] / p.sum()
+    return out
+
+
 class Mutant:
     """The oracle module with one function replaced by a wrong version."""
 
@@ -293,7 +405,7 @@ def _rebind(fn, mutant):
 def _mutant(**repl):
     m = Mutant(**repl)
     for name in ("select", "block_sparse_attention", "block_scores", "attend", "attend_batched",
-                 "dense_attention", "masked_attention_bruteforce"):
+                 "dense_attention", "masked_attention_bruteforce", "select_topk_causal"):
         if name not in repl:
             setattr(m, name, _rebind(getattr(O, name), m))
     return m
@@ -310,10 +422,22 @@ MUTANTS = {
         select_topk=lambda S, k: (S.shape[-1] - 1 - O.select_topk(S[..., ::-1], k))[..., ::-1]),
     "select_smallest": dict(select_topk=lambda S, k: O.select_topk(-S, k)),
     "attend_no_max_shift_sign": dict(
-        attend=lambda q, k, v, idx, blk, scale, rows=None: O.attend(q, k, v, idx, blk, -scale, rows)),
+        attend=lambda q, k, v, idx, blk, scale, rows=None, causal=False:
+        O.attend(q, k, v, idx, blk, -scale, rows, causal)),
     "attend_drops_last_block": dict(
-        attend=lambda q, k, v, idx, blk, scale, rows=None:
-        O.attend(q, k, v, idx[..., :-1] if idx.shape[-1] > 1 else idx, blk, scale, rows)),
+        attend=lambda q, k, v, idx, blk, scale, rows=None, causal=False:
+        O.attend(q, k, v, idx[..., :-1] if idx.shape[-1] > 1 else idx, blk, scale, rows, causal)),
+    "causal_diagonal_not_forced": dict(
+        select_topk_causal=lambda S, k: np.stack(
+            [np.concatenate([O.select_topk(S[..., i, :i + 1], min(k, i + 1)),
+                             np.full(S.shape[:-2] + (k - min(k, i + 1),), -1)], axis=-1)
+             for i in range(S.shape[-1])], axis=-2)),
+    "causal_mask_excludes_self": dict(
+        attend=lambda q, k, v, idx, blk, scale, rows=None, causal=False:
+        _strict_causal(q, k, v, idx, blk, scale, rows, causal)),
+    "pool_max_is_min": dict(pool_max=lambda x, b: -O.pool_max(-x, b)),
+    "group_first_head_only": dict(
+        group_scores=lambda S, Hkv: S.reshape(S.shape[0], Hkv, -1, *S.shape[2:])[:, :, 0]),
     "e4m3_bias_8": dict(decode_e4m3=lambda c: O.decode_e4m3(c) / 2),
     "bf16_low_bits": dict(widen_bf16_bits=lambda b: np.asarray(b, dtype=np.uint16).astype(np.float64)),
     "topk_round_not_truncate": dict(topk_count=lambda r, nb: int(round(r * nb))),
