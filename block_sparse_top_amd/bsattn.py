@@ -59,6 +59,13 @@ def lib() -> ctypes.CDLL:
     L.bsattn_forward.restype = i32
     L.bsattn_forward.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp,
                                  ctypes.c_float, ctypes.POINTER(ctypes.c_float), vp, vp]
+    u32 = ctypes.c_uint
+    L.bsattn_select_ex.restype = i32
+    L.bsattn_select_ex.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, u32, vp, vp, vp, vp,
+                                   sz, vp]
+    L.bsattn_forward_ex.restype = i32
+    L.bsattn_forward_ex.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, u32, vp, vp, vp, vp,
+                                    ctypes.c_float, ctypes.POINTER(ctypes.c_float), vp, vp]
     _lib = L
     return L
 
@@ -94,6 +101,17 @@ def _shapes(q, k, v=None):
     return B, N, Hq, k.shape[2], D
 
 
+# option bits of the extended entry points (include/bsattn.h)
+CAUSAL, POOL_MAX, GROUP_SELECT = 1, 2, 4
+
+
+def _flags(causal=False, pooling="mean", group=False) -> int:
+    if pooling not in ("mean", "max"):
+        raise ValueError("pooling must be 'mean' or 'max'")
+    return (CAUSAL if causal else 0) | (POOL_MAX if pooling == "max" else 0) | \
+        (GROUP_SELECT if group else 0)
+
+
 def topk_count(topk_ratio: float, num_blocks: int) -> int:
     """k = int(topk_ratio * num_blocks), as the SparseFormer page's sketch computes it."""
     return int(topk_ratio * num_blocks)
@@ -103,12 +121,16 @@ def select_workspace_bytes(B, N, Hq, Hkv, D, block) -> int:
     return int(lib().bsattn_select_workspace_bytes(B, N, Hq, Hkv, D, block))
 
 
-def select(q, k, block: int, topk: int, *, return_pooled: bool = False, workspace=None):
+def select(q, k, block: int, topk: int, *, causal: bool = False, pooling: str = "mean",
+           group: bool = False, return_pooled: bool = False, workspace=None):
     """Top-k key blocks per (batch, query head, query block): int32 [B, Hq, nb, topk].
 
+    causal: own block forced, earlier blocks only, unused places -1; pooling "max": in-block
+    maximum instead of the mean; group: one selection per KV head for all its query heads.
     With return_pooled, also returns the pooled q and k (fp32 [B, Hq, nb, D] and
     [B, Hkv, nb, D]; for fp8 inputs without the per-tensor descale).
     """
+    flags = _flags(causal, pooling, group)
     B, N, Hq, Hkv, D = _shapes(q, k)
     nb = N // block if block > 0 else 0
     idx = torch.empty((B, Hq, nb, max(topk, 0)), dtype=torch.int32, device=q.device)
@@ -116,9 +138,9 @@ def select(q, k, block: int, topk: int, *, return_pooled: bool = False, workspac
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     with torch.cuda.device(q.device):
-        _check(lib().bsattn_select(_DTYPES[q.dtype], B, N, Hq, Hkv, D, block, topk, _ptr(q),
-                                   _ptr(k), _ptr(idx), _ptr(workspace), workspace.numel(),
-                                   _stream(q.device)))
+        _check(lib().bsattn_select_ex(_DTYPES[q.dtype], B, N, Hq, Hkv, D, block, topk, flags,
+                                      _ptr(q), _ptr(k), _ptr(idx), _ptr(workspace),
+                                      workspace.numel(), _stream(q.device)))
     if not return_pooled:
         return idx
     qb_bytes = (B * Hq * nb * D * 4 + 255) // 256 * 256
@@ -127,10 +149,12 @@ def select(q, k, block: int, topk: int, *, return_pooled: bool = False, workspac
     return idx, qbar, kbar
 
 
-def forward(q, k, v, idx, scale: float | None = None, descales=(1.0, 1.0, 1.0), out=None):
+def forward(q, k, v, idx, scale: float | None = None, descales=(1.0, 1.0, 1.0), out=None, *,
+            causal: bool = False):
     """Attention of every query block over its selected key blocks: [B, N, Hq, D].
 
-    Output dtype: fp32 for fp32 inputs, bf16 for bf16 and fp8 inputs.
+    Output dtype: fp32 for fp32 inputs, bf16 for bf16 and fp8 inputs. causal: rows in the
+    form `select(..., causal=True)` writes; keys after the query are masked.
     """
     B, N, Hq, Hkv, D = _shapes(q, k, v)
     if idx.dim() != 4 or idx.dtype != torch.int32 or not idx.is_contiguous() or not idx.is_cuda:
@@ -149,17 +173,18 @@ def forward(q, k, v, idx, scale: float | None = None, descales=(1.0, 1.0, 1.0), 
         raise ValueError("out has the wrong shape, dtype or layout")
     ds = (ctypes.c_float * 3)(*[float(x) for x in descales])
     with torch.cuda.device(q.device):
-        _check(lib().bsattn_forward(_DTYPES[q.dtype], B, N, Hq, Hkv, D, block, topk, _ptr(q),
-                                    _ptr(k), _ptr(v), _ptr(idx), scale, ds, _ptr(out),
-                                    _stream(q.device)))
+        _check(lib().bsattn_forward_ex(_DTYPES[q.dtype], B, N, Hq, Hkv, D, block, topk,
+                                       CAUSAL if causal else 0, _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(idx), scale, ds, _ptr(out), _stream(q.device)))
     return out
 
 
 def block_sparse_attention(q, k, v, block_size: int = 64, topk_ratio: float = 0.3,
-                           descales=(1.0, 1.0, 1.0), return_idx: bool = False):
+                           descales=(1.0, 1.0, 1.0), return_idx: bool = False, *,
+                           causal: bool = False, pooling: str = "mean", group: bool = False):
     """The whole method: select, then attend with scale 1/sqrt(D)."""
     B, N, Hq, Hkv, D = _shapes(q, k, v)
     topk = topk_count(topk_ratio, N // block_size)
-    idx = select(q, k, block_size, topk)
-    out = forward(q, k, v, idx, 1.0 / math.sqrt(D), descales)
+    idx = select(q, k, block_size, topk, causal=causal, pooling=pooling, group=group)
+    out = forward(q, k, v, idx, 1.0 / math.sqrt(D), descales, causal=causal)
     return (out, idx) if return_idx else out

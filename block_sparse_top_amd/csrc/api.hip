@@ -108,8 +108,17 @@ size_t bsattn_select_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int 
 int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                   const void* q, const void* k, int32_t* idx, void* workspace,
                   size_t workspace_bytes, void* stream) {
+  return bsattn_select_ex(dtype, B, N, Hq, Hkv, D, block, topk, 0u, q, k, idx, workspace,
+                          workspace_bytes, stream);
+}
+
+int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
+                     int topk, unsigned flags, const void* q, const void* k, int32_t* idx,
+                     void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_shape(dtype, B, N, Hq, Hkv, D, block, topk);
   if (st != BSATTN_OK) return st;
+  if (flags & ~(unsigned)(BSATTN_CAUSAL | BSATTN_POOL_MAX | BSATTN_GROUP_SELECT))
+    return fail(BSATTN_E_INVALID, "unknown flags 0x%x", flags);
   if (B == 0 || N == 0) return BSATTN_OK;
   const int64_t nb = N / block;
   const bool large = nb > bsattn::kMaxFusedBlocks;
@@ -117,6 +126,9 @@ int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int b
     return fail(BSATTN_E_UNSUPPORTED,
                 "selection over nb=%lld blocks (supported: nb <= %d, or a multiple of 64 up to %d)",
                 (long long)nb, bsattn::kMaxFusedBlocks, bsattn::kMaxLargeBlocks);
+  if (large && (flags & BSATTN_GROUP_SELECT))
+    return fail(BSATTN_E_UNSUPPORTED, "group selection over nb=%lld > %d blocks",
+                (long long)nb, bsattn::kMaxFusedBlocks);
   if (!q || !k || !idx) return fail(BSATTN_E_INVALID, "null q, k or idx");
   if (!aligned16(q) || !aligned16(k) || ((uintptr_t)idx & 3u))
     return fail(BSATTN_E_INVALID, "q and k must be 16-byte aligned, idx 4-byte aligned");
@@ -129,30 +141,44 @@ int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int b
   float* kbar = (float*)((char*)workspace + pooled_q_bytes(B, N, Hq, D, block));
   hipStream_t s = (hipStream_t)stream;
   const int kind = dtype == BSATTN_F32 ? 0 : dtype == BSATTN_BF16 ? 1 : 2;
+  const bool pmax = flags & BSATTN_POOL_MAX, causal = flags & BSATTN_CAUSAL;
   if (large) {
     float* S = (float*)((char*)kbar + pooled_k_bytes(B, N, Hkv, D, block));
-    st = hip_status(bsattn::launch_pool(kind, 3, B, N, Hq, Hkv, D, block, q, k, qbar, kbar, s),
-                    "pool launch");
+    st = hip_status(
+        bsattn::launch_pool(kind, 3, B, N, Hq, Hkv, D, block, q, k, qbar, kbar, pmax, s),
+        "pool launch");
     if (st != BSATTN_OK) return st;
     st = hip_status(bsattn::launch_scores_large(B, Hq, Hkv, (int)nb, D, qbar, kbar, S, s),
                     "score launch");
     if (st != BSATTN_OK) return st;
-    return hip_status(bsattn::launch_topk_rows(B * Hq * nb, (int)nb, topk, S, idx, s),
+    return hip_status(bsattn::launch_topk_rows(B * Hq * nb, (int)nb, topk, S, idx, causal, s),
                       "top-k launch");
   }
-  st = hip_status(bsattn::launch_pool(kind, 2, B, N, Hq, Hkv, D, block, q, k, qbar, kbar, s),
-                  "key pool launch");
+  st = hip_status(
+      bsattn::launch_pool(kind, 2, B, N, Hq, Hkv, D, block, q, k, qbar, kbar, pmax, s),
+      "key pool launch");
   if (st != BSATTN_OK) return st;
   return hip_status(bsattn::launch_pool_score_select(kind, B, N, Hq, Hkv, D, block, topk, q,
-                                                     qbar, kbar, idx, s),
+                                                     qbar, kbar, idx, flags, s),
                     "query pool/score/select launch");
 }
 
 int bsattn_forward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                    const void* q, const void* k, const void* v, const int32_t* idx, float scale,
                    const float* descale_qkv, void* out, void* stream) {
+  return bsattn_forward_ex(dtype, B, N, Hq, Hkv, D, block, topk, 0u, q, k, v, idx, scale,
+                           descale_qkv, out, stream);
+}
+
+int bsattn_forward_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
+                      int topk, unsigned flags, const void* q, const void* k, const void* v,
+                      const int32_t* idx, float scale, const float* descale_qkv, void* out,
+                      void* stream) {
   int st = check_shape(dtype, B, N, Hq, Hkv, D, block, topk);
   if (st != BSATTN_OK) return st;
+  if (flags & ~(unsigned)(BSATTN_CAUSAL | BSATTN_POOL_MAX | BSATTN_GROUP_SELECT))
+    return fail(BSATTN_E_INVALID, "unknown flags 0x%x", flags);
+  const bool causal = flags & BSATTN_CAUSAL;
   if (!isfinite(scale) || !(scale > 0.f))
     return fail(BSATTN_E_INVALID, "scale must be finite and > 0");
   if (dtype == BSATTN_FP8_E4M3) {
@@ -169,32 +195,35 @@ int bsattn_forward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int 
   if (validate_enabled()) {
     unsigned int bad = 0;
     const int64_t nb = N / block;
-    st = hip_status(bsattn::validate_idx(B * Hq * nb, topk, (int)nb, idx, s, &bad),
+    st = hip_status(bsattn::validate_idx(B * Hq * nb, topk, (int)nb, idx, causal, s, &bad),
                     "idx validation");
     if (st != BSATTN_OK) return st;
     if (bad)
-      return fail(BSATTN_E_INVALID, "idx: %u rows are not strictly ascending in [0, nb=%lld)",
+      return fail(BSATTN_E_INVALID,
+                  causal ? "idx: %u rows are not causal rows (strictly ascending in [0, i], "
+                           "then -1; nb=%lld)"
+                         : "idx: %u rows are not strictly ascending in [0, nb=%lld)",
                   bad, (long long)nb);
   }
   if (dtype == BSATTN_BF16) {
     if (!bsattn::attn_bf16_supported(D, block))
       return fail(BSATTN_E_UNSUPPORTED, "bf16 attention for D=%d block=%d", D, block);
     return hip_status(bsattn::launch_attn_bf16(B, N, Hq, Hkv, D, block, topk, q, k, v, idx,
-                                               scale, out, s),
+                                               scale, out, causal, s),
                       "bf16 attention launch");
   }
   if (dtype == BSATTN_F32) {
     if (!bsattn::attn_f32_supported(D, block))
       return fail(BSATTN_E_UNSUPPORTED, "fp32 attention for D=%d block=%d", D, block);
     return hip_status(bsattn::launch_attn_f32(B, N, Hq, Hkv, D, block, topk, q, k, v, idx,
-                                              scale, out, s),
+                                              scale, out, causal, s),
                       "fp32 attention launch");
   }
   if (!bsattn::attn_fp8_supported(D, block))
     return fail(BSATTN_E_UNSUPPORTED, "fp8 attention for D=%d block=%d (supported: D=128)", D,
                 block);
   return hip_status(bsattn::launch_attn_fp8(B, N, Hq, Hkv, D, block, topk, q, k, v, idx, scale,
-                                            descale_qkv, out, s),
+                                            descale_qkv, out, causal, s),
                     "fp8 attention launch");
 }
 

@@ -35,6 +35,10 @@
 // reference to its running max, rescaling O and l by exp2(m_old - m_new). O and l always
 // share one reference, so O/l is the exact softmax average. The normaliser is summed from the
 // bf16-rounded weights (v_dot2c_f32_bf16), i.e. from exactly the weights the PV product uses.
+//
+// Causal variant (template flag): query block i reads the first min(topk, i+1) entries of its
+// row, each of which must lie in [0, i]; in its own block i the scores of keys after the
+// query are set to -inf before the weights (weight 0).
 #include "common.h"
 #include "launch.h"
 
@@ -85,7 +89,7 @@ __device__ __forceinline__ s16x4 ds_read_tr16(const char* lds_bytes) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_void*)(lds_bytes));
 }
 
-template <int D, int BLK>
+template <int D, int BLK, bool CAUSAL>
 __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
@@ -124,6 +128,8 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
   const int32_t* myidx = idx + (((int64_t)b * Hq + h) * nb + i) * topk;
   const char* kbase0 = (const char*)(k + (int64_t)b * N * krs + (int64_t)g * D);
   const char* vbase0 = (const char*)(v + (int64_t)b * N * krs + (int64_t)g * D);
+  const int kcount = CAUSAL && i + 1 < topk ? i + 1 : topk;   // entries of the row used
+  const unsigned klim = CAUSAL ? (unsigned)(i + 1) : (unsigned)nb;   // admissible blocks
 
   // DMA source byte offsets of this lane inside a tile (fixed), destination spans uniform
   uint32_t goff[C::DMA];
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
   }
   bool bad = false;
   auto tile_base = [&](int kb) -> int64_t {
-    if ((unsigned)kb >= (unsigned)nb) { bad = true; kb = 0; }
+    if ((unsigned)kb >= klim) { bad = true; kb = 0; }
     return (int64_t)kb * BLK * krs * 2;
   };
   // The transfers are issued from inline asm so that the compiler's wait-count pass, which
@@ -199,15 +205,17 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
   for (int qc = 0; qc < C::QC; ++qc)
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) asm volatile("" ::"v"(qf[qc][s]));
+  int kb_cur = myidx[0];
   {
-    const int64_t tb = tile_base(myidx[0]);
+    const int64_t tb = tile_base(kb_cur);
     dma(kbase0 + tb, Kl);
     dma(vbase0 + tb, Vl);
   }
 
-  for (int t = 0; t < topk; ++t) {
-    const bool more = t + 1 < topk;
-    const int64_t tb_next = more ? tile_base(myidx[t + 1]) : 0;
+  for (int t = 0; t < kcount; ++t) {
+    const bool more = t + 1 < kcount;
+    const int kb_next = more ? myidx[t + 1] : 0;
+    const int64_t tb_next = more ? tile_base(kb_next) : 0;
 
     // ---- K(t): wait for this wave's share (V(t) may still fly), then the whole work-group
     wait_vmcnt<C::DMA>();
@@ -234,6 +242,18 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
         for (int s = 0; s < C::NS; ++s)
           sacc[kt][qc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kt][s], qf[qc][s], sacc[kt][qc], 0, 0, 0);
       }
+    if (CAUSAL && kb_cur == i) {               // own block: keys after the query get -inf
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+        for (int qc = 0; qc < C::QC; ++qc)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+            const int qry = C::QW * wave + 32 * qc + l32;
+            if (key > qry) sacc[kt][qc][r] = -__builtin_inff();
+          }
+    }
 
     // ---- softmax weights (lane pair l, l^32 shares one query row): p = exp2(c*s - m), m the
     // row reference in the exp2 domain (0 until a block sum leaves [2^-64, 2^64])
@@ -317,6 +337,7 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
         for (int dt = 0; dt < C::NDT; ++dt)
           oacc[dt][qc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s][dt], pb, oacc[dt][qc], 0, 0, 0);
       }
+    kb_cur = kb_next;
   }
 
   // epilogue: O = O^T / l, bf16, 4 consecutive d per store
@@ -340,12 +361,18 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
 
 template <int D, int BLK>
 hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int topk, const void* q, const void* k,
-                  const void* v, const int32_t* idx, float c, void* out, hipStream_t stream) {
+                  const void* v, const int32_t* idx, float c, void* out, bool causal,
+                  hipStream_t stream) {
   const int nb = (int)(N / BLK);
   const uint32_t total = (uint32_t)(B * Hq * nb);
-  attn_bf16_kernel<D, BLK><<<total, Cfg<D, BLK>::NT, 0, stream>>>(
-      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, N, Hq,
-      Hkv, nb, topk, c, total);
+  if (causal)
+    attn_bf16_kernel<D, BLK, true><<<total, Cfg<D, BLK>::NT, 0, stream>>>(
+        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, N, Hq,
+        Hkv, nb, topk, c, total);
+  else
+    attn_bf16_kernel<D, BLK, false><<<total, Cfg<D, BLK>::NT, 0, stream>>>(
+        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, N, Hq,
+        Hkv, nb, topk, c, total);
   return hipGetLastError();
 }
 
@@ -357,12 +384,12 @@ bool attn_bf16_supported(int D, int block) {
 
 hipError_t launch_attn_bf16(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                             const void* q, const void* k, const void* v, const int32_t* idx,
-                            float scale, void* out, hipStream_t stream) {
+                            float scale, void* out, bool causal, hipStream_t stream) {
   const float c = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
-  if (D == 64 && block == 64) return launch<64, 64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, stream);
-  if (D == 64 && block == 128) return launch<64, 128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, stream);
-  if (D == 128 && block == 64) return launch<128, 64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, stream);
-  return launch<128, 128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, stream);
+  if (D == 64 && block == 64) return launch<64, 64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, causal, stream);
+  if (D == 64 && block == 128) return launch<64, 128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, causal, stream);
+  if (D == 128 && block == 64) return launch<128, 64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, causal, stream);
+  return launch<128, 128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, causal, stream);
 }
 
 }  // namespace bsattn

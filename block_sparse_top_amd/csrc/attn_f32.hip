@@ -9,6 +9,10 @@
 // selected block are staged 32 at a time in LDS (K and V rows, read as broadcasts); each
 // thread keeps its q row, output row, running max and normaliser in registers and updates
 // them once per 32 keys (exact online softmax: rescale whenever the max grows).
+//
+// Causal variant (template flag): query block i reads the first min(topk, i+1) entries of its
+// row, each in [0, i]; in its own block keys after the query score -inf (weight 0). The first
+// chunk of the own block always holds key 0 <= query, so no chunk starts from an all -inf max.
 #include "common.h"
 #include "launch.h"
 
@@ -17,7 +21,7 @@ namespace {
 
 constexpr int kChunk = 32;
 
-template <int D>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(128) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ idx, float* __restrict__ out, int64_t N, int Hq, int Hkv,
@@ -49,9 +53,12 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
   const float* kb0 = k + (int64_t)b * N * krs + (int64_t)g * D;
   const float* vb0 = v + (int64_t)b * N * krs + (int64_t)g * D;
 
-  for (int t = 0; t < topk; ++t) {
+  const int kcount = CAUSAL && i + 1 < topk ? i + 1 : topk;
+  const unsigned klim = CAUSAL ? (unsigned)(i + 1) : (unsigned)nb;
+  for (int t = 0; t < kcount; ++t) {
     int kb = myidx[t];
-    if ((unsigned)kb >= (unsigned)nb) { bad = true; kb = 0; }
+    if ((unsigned)kb >= klim) { bad = true; kb = 0; }
+    const bool own = CAUSAL && kb == i;
     for (int c0 = 0; c0 < block; c0 += kChunk) {
       __syncthreads();
       for (int e = tid; e < kChunk * D / 4; e += block) {
@@ -69,6 +76,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
 #pragma unroll
         for (int d = 0; d < D; ++d) a = __builtin_fmaf(qr[d], ks[j][d], a);
         s[j] = a * c;                          // exp2 domain
+        if (own && c0 + j > tid) s[j] = -__builtin_inff();
         mc = fmaxf(mc, s[j]);
       }
       const float alpha = __builtin_amdgcn_exp2f(m - mc);   // 0 on the first chunk
@@ -93,12 +101,17 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
 template <int D>
 hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int block, int topk, const void* q,
                   const void* k, const void* v, const int32_t* idx, float c, void* out,
-                  hipStream_t stream) {
+                  bool causal, hipStream_t stream) {
   const int nb = (int)(N / block);
   const uint32_t total = (uint32_t)(B * Hq * nb);
-  attn_f32_kernel<D><<<total, block, 0, stream>>>((const float*)q, (const float*)k,
-                                                   (const float*)v, idx, (float*)out, N, Hq, Hkv,
-                                                   nb, block, topk, c, total);
+  if (causal)
+    attn_f32_kernel<D, true><<<total, block, 0, stream>>>((const float*)q, (const float*)k,
+                                                          (const float*)v, idx, (float*)out, N,
+                                                          Hq, Hkv, nb, block, topk, c, total);
+  else
+    attn_f32_kernel<D, false><<<total, block, 0, stream>>>((const float*)q, (const float*)k,
+                                                           (const float*)v, idx, (float*)out, N,
+                                                           Hq, Hkv, nb, block, topk, c, total);
   return hipGetLastError();
 }
 
@@ -110,10 +123,10 @@ bool attn_f32_supported(int D, int block) {
 
 hipError_t launch_attn_f32(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                            const void* q, const void* k, const void* v, const int32_t* idx,
-                           float scale, void* out, hipStream_t stream) {
+                           float scale, void* out, bool causal, hipStream_t stream) {
   const float c = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
-  if (D == 64) return launch<64>(B, N, Hq, Hkv, block, topk, q, k, v, idx, c, out, stream);
-  return launch<128>(B, N, Hq, Hkv, block, topk, q, k, v, idx, c, out, stream);
+  if (D == 64) return launch<64>(B, N, Hq, Hkv, block, topk, q, k, v, idx, c, out, causal, stream);
+  return launch<128>(B, N, Hq, Hkv, block, topk, q, k, v, idx, c, out, causal, stream);
 }
 
 }  // namespace bsattn

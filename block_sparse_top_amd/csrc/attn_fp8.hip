@@ -24,6 +24,10 @@
 // tile row r sits at chunk c ^ f(r), f(r) = (r&3) | (((r>>2) ^ (r>>3)) & 1) << 2, which keeps
 // both the K row reads (8 rows) and the V transpose reads (8 rows x 2 half-chunks) on 32
 // distinct banks.
+//
+// Causal variant (template flag): query block i reads the first min(topk, i+1) entries of its
+// row, each in [0, i]; in its own block the scores of keys after the query are -inf before
+// the row maximum and the weights.
 #include "common.h"
 #include "launch.h"
 
@@ -74,7 +78,7 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f3
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-template <int BLK>
+template <int BLK, bool CAUSAL>
 __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ out, int64_t N, int Hq, int Hkv,
@@ -124,8 +128,10 @@ __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
     goff[x] = (uint32_t)(r * krs + (p ^ swz8(r)) * 16);
   }
   bool bad = false;
+  const int kcount = CAUSAL && i + 1 < topk ? i + 1 : topk;   // entries of the row used
+  const unsigned klim = CAUSAL ? (unsigned)(i + 1) : (unsigned)nb;
   auto tile_base = [&](int kb) -> int64_t {
-    if ((unsigned)kb >= (unsigned)nb) { bad = true; kb = 0; }
+    if ((unsigned)kb >= klim) { bad = true; kb = 0; }
     return (int64_t)kb * BLK * krs;
   };
   // transfers from inline asm: the compiler's wait-count pass adds no vmcnt(0) before the
@@ -175,15 +181,17 @@ __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
   float m = -__builtin_inff();                // reference (exp2 domain) of this lane's row
   float lsum = 0.f;
 
+  int kb_cur = myidx[0];
   {
-    const int64_t tb = tile_base(myidx[0]);
+    const int64_t tb = tile_base(kb_cur);
     dma(kbase0 + tb, Kl);
     dma(vbase0 + tb, Vl);
   }
 
-  for (int t = 0; t < topk; ++t) {
-    const bool more = t + 1 < topk;
-    const int64_t tb_next = more ? tile_base(myidx[t + 1]) : 0;
+  for (int t = 0; t < kcount; ++t) {
+    const bool more = t + 1 < kcount;
+    const int kb_next = more ? myidx[t + 1] : 0;
+    const int64_t tb_next = more ? tile_base(kb_next) : 0;
 
     wait_vmcnt<C::DMA>();
     if (C::NW > 1) __syncthreads();
@@ -208,6 +216,15 @@ __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
       for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
 #pragma unroll
       for (int s = 0; s < C::NS; ++s) sacc[kt] = mfma8(ka[kt][s], qf[s], sacc[kt]);
+    }
+    if (CAUSAL && kb_cur == i) {               // own block: keys after the query get -inf
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key > 32 * wave + l32) sacc[kt][r] = -__builtin_inff();
+        }
     }
 
     // reference: follow the row max (lane pair l, l^32 shares one row)
@@ -267,6 +284,7 @@ __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
     for (int ks = 0; ks < C::NKS; ++ks)
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] = mfma8(va[ks][dt], pb[ks], oacc[dt]);
+    kb_cur = kb_next;
   }
 
   const float l_all = lsum + __shfl_xor(lsum, 32);
@@ -286,13 +304,18 @@ __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
 
 template <int BLK>
 hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int topk, const void* q, const void* k,
-                  const void* v, const int32_t* idx, float c, float dv, void* out,
+                  const void* v, const int32_t* idx, float c, float dv, void* out, bool causal,
                   hipStream_t stream) {
   const int nb = (int)(N / BLK);
   const uint32_t total = (uint32_t)(B * Hq * nb);
-  attn_fp8_kernel<BLK><<<total, Cfg8<BLK>::NT, 0, stream>>>(
-      (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, (uint16_t*)out, N, Hq, Hkv,
-      nb, topk, c, dv, total);
+  if (causal)
+    attn_fp8_kernel<BLK, true><<<total, Cfg8<BLK>::NT, 0, stream>>>(
+        (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, (uint16_t*)out, N, Hq,
+        Hkv, nb, topk, c, dv, total);
+  else
+    attn_fp8_kernel<BLK, false><<<total, Cfg8<BLK>::NT, 0, stream>>>(
+        (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, (uint16_t*)out, N, Hq,
+        Hkv, nb, topk, c, dv, total);
   return hipGetLastError();
 }
 
@@ -302,14 +325,14 @@ bool attn_fp8_supported(int D, int block) { return D == 128 && (block == 64 || b
 
 hipError_t launch_attn_fp8(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                            const void* q, const void* k, const void* v, const int32_t* idx,
-                           float scale, const float* descale_qkv, void* out,
+                           float scale, const float* descale_qkv, void* out, bool causal,
                            hipStream_t stream) {
   (void)D;
   const float c = (float)((double)scale * 1.4426950408889634 * (double)descale_qkv[0] *
                           (double)descale_qkv[1]);
   const float dv = descale_qkv[2];
-  if (block == 64) return launch<64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, dv, out, stream);
-  return launch<128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, dv, out, stream);
+  if (block == 64) return launch<64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, dv, out, causal, stream);
+  return launch<128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, dv, out, causal, stream);
 }
 
 }  // namespace bsattn

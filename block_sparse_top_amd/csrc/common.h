@@ -52,7 +52,7 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t w, uint32_t total) {
 }
 
 // Storage kinds: 0 fp32, 1 bf16, 2 OCP fp8 e4m3. Vec<KIND>: elements per 16-byte vector and
-// their fp32 values added into an accumulator array.
+// their fp32 values folded into an accumulator array (add: sums; vmax: elementwise maxima).
 template <int KIND> struct Vec;
 template <> struct Vec<0> {            // fp32
   static constexpr int E = 4;
@@ -60,12 +60,24 @@ template <> struct Vec<0> {            // fp32
     a[0] += __uint_as_float(w.x); a[1] += __uint_as_float(w.y);
     a[2] += __uint_as_float(w.z); a[3] += __uint_as_float(w.w);
   }
+  __device__ static void vmax(const u32x4& w, float* a) {
+    a[0] = fmaxf(a[0], __uint_as_float(w.x)); a[1] = fmaxf(a[1], __uint_as_float(w.y));
+    a[2] = fmaxf(a[2], __uint_as_float(w.z)); a[3] = fmaxf(a[3], __uint_as_float(w.w));
+  }
 };
 template <> struct Vec<1> {            // bf16
   static constexpr int E = 8;
   __device__ static void add(const u32x4& w, float* a) {
     a[0] += bf16lo(w.x); a[1] += bf16hi(w.x); a[2] += bf16lo(w.y); a[3] += bf16hi(w.y);
     a[4] += bf16lo(w.z); a[5] += bf16hi(w.z); a[6] += bf16lo(w.w); a[7] += bf16hi(w.w);
+  }
+  __device__ static void vmax(const u32x4& w, float* a) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[2 * i] = fmaxf(a[2 * i], bf16lo(ws[i]));
+      a[2 * i + 1] = fmaxf(a[2 * i + 1], bf16hi(ws[i]));
+    }
   }
 };
 template <> struct Vec<2> {            // OCP fp8 e4m3 (gfx950 converts the OCP format)
@@ -80,6 +92,21 @@ template <> struct Vec<2> {            // OCP fp8 e4m3 (gfx950 converts the OCP 
       a[4 * i + 2] += hi[0]; a[4 * i + 3] += hi[1];
     }
   }
+  __device__ static void vmax(const u32x4& w, float* a) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[i], false);
+      auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[i], true);
+      a[4 * i + 0] = fmaxf(a[4 * i + 0], lo[0]); a[4 * i + 1] = fmaxf(a[4 * i + 1], lo[1]);
+      a[4 * i + 2] = fmaxf(a[4 * i + 2], hi[0]); a[4 * i + 3] = fmaxf(a[4 * i + 3], hi[1]);
+    }
+  }
 };
+
+// Selection options (flags of the extended entry points)
+constexpr unsigned kCausal = 1u;     // key blocks j <= i only, own block forced
+constexpr unsigned kPoolMax = 2u;    // in-block elementwise maximum instead of the mean
+constexpr unsigned kGroup = 4u;      // one selection per KV head from the group's summed scores
 
 }  // namespace bsattn

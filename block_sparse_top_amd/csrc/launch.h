@@ -11,14 +11,15 @@ namespace bsattn {
 // bit 1: k). kind: 0 fp32, 1 bf16, 2 fp8.
 hipError_t launch_pool(int kind, int which, int64_t B, int64_t N, int Hq, int Hkv, int D,
                        int block, const void* q, const void* k, float* qbar, float* kbar,
-                       hipStream_t stream);
+                       bool pmax, hipStream_t stream);
 
 // Steps 1 (query side), 2 and 3 fused for nb <= kMaxFusedBlocks: query pooling (also stored
 // to qbar), block scores against the pooled keys kbar, top-k per row.
 constexpr int kMaxFusedBlocks = 1024;
 hipError_t launch_pool_score_select(int kind, int64_t B, int64_t N, int Hq, int Hkv, int D,
                                     int block, int topk, const void* q, float* qbar,
-                                    const float* kbar, int32_t* idx, hipStream_t stream);
+                                    const float* kbar, int32_t* idx, unsigned flags,
+                                    hipStream_t stream);
 
 // Steps 2-3 for nb > kMaxFusedBlocks (nb % 64 == 0, nb <= kMaxLargeBlocks): S = scores
 // [B, Hq, nb, nb] fp32 in the workspace, then the top-k of each of its rows.
@@ -26,32 +27,33 @@ constexpr int kMaxLargeBlocks = 8192;
 hipError_t launch_scores_large(int64_t B, int Hq, int Hkv, int nb, int D, const float* qbar,
                                const float* kbar, float* S, hipStream_t stream);
 hipError_t launch_topk_rows(int64_t rows, int nb, int topk, const float* S, int32_t* idx,
-                            hipStream_t stream);
+                            bool causal, hipStream_t stream);
 
 // Step 4, bf16 inputs on bf16 MFMA. Supported (D, block): D, block in {64, 128}.
 bool attn_bf16_supported(int D, int block);
 hipError_t launch_attn_bf16(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                             const void* q, const void* k, const void* v, const int32_t* idx,
-                            float scale, void* out, hipStream_t stream);
+                            float scale, void* out, bool causal, hipStream_t stream);
 
 // Step 4, fp32 inputs on the fp32 vector ALUs.
 bool attn_f32_supported(int D, int block);
 hipError_t launch_attn_f32(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                            const void* q, const void* k, const void* v, const int32_t* idx,
-                           float scale, void* out, hipStream_t stream);
+                           float scale, void* out, bool causal, hipStream_t stream);
 
 // Step 4, OCP fp8 e4m3 inputs on the fp8 MFMA, bf16 output. Supported: D = 128,
 // block in {64, 128}. descale_qkv: host array of the three per-tensor descales.
 bool attn_fp8_supported(int D, int block);
 hipError_t launch_attn_fp8(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                            const void* q, const void* k, const void* v, const int32_t* idx,
-                           float scale, const float* descale_qkv, void* out,
+                           float scale, const float* descale_qkv, void* out, bool causal,
                            hipStream_t stream);
 
-// Checks every idx row (topk values, strictly ascending, in [0, nb)); waits for the stream and
-// returns the number of failing rows in *bad_rows. Uses one device-global counter per device:
-// concurrent validations on one device race.
-hipError_t validate_idx(int64_t rows, int topk, int nb, const int32_t* idx, hipStream_t stream,
-                        unsigned int* bad_rows);
+// Checks every idx row (topk values, strictly ascending, in [0, nb); causal: the first
+// min(topk, i+1) values strictly ascending in [0, i] for query block i, the rest -1); waits
+// for the stream and returns the number of failing rows in *bad_rows. Uses one device-global
+// counter per device: concurrent validations on one device race.
+hipError_t validate_idx(int64_t rows, int topk, int nb, const int32_t* idx, bool causal,
+                        hipStream_t stream, unsigned int* bad_rows);
 
 }  // namespace bsattn

@@ -1,4 +1,6 @@
-// Step 1 of block selection: per-block mean of q and k.
+// Step 1 of block selection: per-block mean of q and k (or, as an option, the elementwise
+// maximum over the block's tokens: the "in-block extremum" scoring that the MSA page's §2.2
+// table lists for block-based methods).
 //
 // SparseFormer page ("2026 新一代卷积与Transformer网络架构技术演进与性能对比"), section
 // "SparseFormer 注意力实现", step 1: q and k [B, N, H, D] are viewed as
@@ -30,10 +32,18 @@ struct PoolArgs {
   int H;
 };
 
+// fold one 16-byte vector into the accumulators: sum, or elementwise max when pmax
+template <int KIND>
+__device__ __forceinline__ void fold(bool pmax, const u32x4& w, float* acc) {
+  if (pmax) Vec<KIND>::vmax(w, acc); else Vec<KIND>::add(w, acc);
+}
+
 template <int KIND>
 __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka, int64_t nb,
-                                                        int D, int block, float inv_block) {
+                                                        int D, int block, float inv_block,
+                                                        bool pmax) {
   constexpr int E = Vec<KIND>::E;
+  const float init = pmax ? -__builtin_inff() : 0.f;
   extern __shared__ float red[];                       // [T][V*E] partial sums
   const PoolArgs a = blockIdx.y == 0 ? qa : ka;
   const int64_t bi = blockIdx.x;                       // b * nb + i
@@ -48,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
     const int c = tid % V, grp = tid / V;
     float acc[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int e = 0; e < E; ++e) acc[e] = init;
     if (grp < T) {
       const uint8_t* p = base + (int64_t)c * 16;
       int t = grp;
@@ -56,17 +66,23 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
         u32x4 w[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) w[u] = load16(p + (int64_t)(t + u * T) * row_bytes);
+        if (pmax) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) Vec<KIND>::add(w[u], acc);
+          for (int u = 0; u < kUnroll; ++u) Vec<KIND>::vmax(w[u], acc);
+        } else {
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) Vec<KIND>::add(w[u], acc);
+        }
       }
-      for (; t < block; t += T) Vec<KIND>::add(load16(p + (int64_t)t * row_bytes), acc);
+      for (; t < block; t += T) fold<KIND>(pmax, load16(p + (int64_t)t * row_bytes), acc);
 #pragma unroll
       for (int e = 0; e < E; ++e) red[grp * V * E + c * E + e] = acc[e];
     }
     __syncthreads();
     for (int o = tid; o < V * E; o += kThreads) {
-      float s = 0.f;
-      for (int g2 = 0; g2 < T; ++g2) s += red[g2 * V * E + o];
+      float s = init;
+      for (int g2 = 0; g2 < T; ++g2)
+        s = pmax ? fmaxf(s, red[g2 * V * E + o]) : s + red[g2 * V * E + o];
       const int h = o / D, d = o - h * D;
       a.out[(((int64_t)b * a.H + h) * nb + i) * D + d] = s * inv_block;
     }
@@ -74,17 +90,22 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
     for (int c = tid; c < V; c += kThreads) {
       float acc[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = 0.f;
+      for (int e = 0; e < E; ++e) acc[e] = init;
       const uint8_t* p = base + (int64_t)c * 16;
       int t = 0;
       for (; t + kUnroll - 1 < block; t += kUnroll) {
         u32x4 w[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) w[u] = load16(p + (int64_t)(t + u) * row_bytes);
+        if (pmax) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) Vec<KIND>::add(w[u], acc);
+          for (int u = 0; u < kUnroll; ++u) Vec<KIND>::vmax(w[u], acc);
+        } else {
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) Vec<KIND>::add(w[u], acc);
+        }
       }
-      for (; t < block; ++t) Vec<KIND>::add(load16(p + (int64_t)t * row_bytes), acc);
+      for (; t < block; ++t) fold<KIND>(pmax, load16(p + (int64_t)t * row_bytes), acc);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int o = c * E + e;
@@ -99,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
 
 hipError_t launch_pool(int kind, int which, int64_t B, int64_t N, int Hq, int Hkv, int D,
                        int block, const void* q, const void* k, float* qbar, float* kbar,
-                       hipStream_t stream) {
+                       bool pmax, hipStream_t stream) {
   const int64_t nb = N / block;
   const int ebytes = kind == 0 ? 4 : kind == 1 ? 2 : 1;
   const int E = 16 / ebytes;
@@ -116,11 +137,11 @@ hipError_t launch_pool(int kind, int which, int64_t B, int64_t N, int Hq, int Hk
   PoolArgs ka{(const uint8_t*)k, kbar, Hkv};
   if (which == 2) qa = ka;                             // k only: grid.y == 1 reads qa
   dim3 grid((unsigned)(B * nb), which == 3 ? 2 : 1);
-  const float inv = 1.0f / (float)block;               // exact for power-of-two blocks
+  const float inv = pmax ? 1.0f : 1.0f / (float)block;  // exact for power-of-two blocks
   switch (kind) {
-    case 0: pool_kernel<0><<<grid, kThreads, lds, stream>>>(qa, ka, nb, D, block, inv); break;
-    case 1: pool_kernel<1><<<grid, kThreads, lds, stream>>>(qa, ka, nb, D, block, inv); break;
-    default: pool_kernel<2><<<grid, kThreads, lds, stream>>>(qa, ka, nb, D, block, inv); break;
+    case 0: pool_kernel<0><<<grid, kThreads, lds, stream>>>(qa, ka, nb, D, block, inv, pmax); break;
+    case 1: pool_kernel<1><<<grid, kThreads, lds, stream>>>(qa, ka, nb, D, block, inv, pmax); break;
+    default: pool_kernel<2><<<grid, kThreads, lds, stream>>>(qa, ka, nb, D, block, inv, pmax); break;
   }
   return hipGetLastError();
 }

@@ -26,6 +26,14 @@
 // and T is the k-th largest key. Every key > T is kept and the keys == T fill the remaining
 // places in ascending j (the lower index wins a tie). Kept columns are compacted with
 // ballot/mbcnt in ascending j order.
+//
+// Options (flags): kPoolMax pools with the elementwise maximum instead of the mean.
+// kCausal restricts row i to the key blocks j <= i and forces its own block: column j > i
+// gets key 0 (never counted), column i the largest key, and the row keeps min(topk, i+1)
+// blocks; its remaining places are set to -1. kGroup makes one selection per KV head: the
+// work-group pools the rows of all G query heads of the group and sums them (the scores of
+// the sum are the sum of the heads' scores), and the chosen blocks are written for each of
+// the G heads; the pooled-query workspace rows of the group's first head hold the sums.
 #include "common.h"
 #include "launch.h"
 
@@ -47,7 +55,7 @@ template <int KIND, int CPL>  // storage kind; score columns per lane: nb <= 64 
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const uint8_t* __restrict__ q, float* __restrict__ qbar, const float* __restrict__ kbar,
     int32_t* __restrict__ idx, int64_t N, int Hq, int Hkv, int nb, int D, int block, int topk,
-    int row_tiles, float inv_block) {
+    int row_tiles, float inv_block, unsigned flags) {
   constexpr int RW = SelCfg<CPL>::RW, RG = SelCfg<CPL>::RG;
   constexpr int E = Vec<KIND>::E;
   constexpr int EB = 16 / E;                // bytes per stored element
@@ -58,17 +66,27 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 
   // work-groups of one (batch, head) read the same pooled keys: keep them on one XCD's L2
   const int tile = (int)xcd_remap(blockIdx.x, gridDim.x);
+  const bool causal = flags & kCausal, pmax = flags & kPoolMax, group = flags & kGroup;
+  const int G = Hq / Hkv;
+  const int HS = group ? Hkv : Hq;          // selection heads
   const int rt = tile % row_tiles;
-  const int bh = tile / row_tiles;          // b * Hq + h
-  const int h = bh % Hq, b = bh / Hq;
-  const int g = h / (Hq / Hkv);
+  const int sh = tile / row_tiles;          // b * HS + selection head
+  const int b = sh / HS;
+  const int g = group ? sh % HS : (sh % HS) / G;
+  const int h0 = group ? g * G : sh % HS;   // first query head pooled here
+  const int nh = group ? G : 1;             // query heads pooled and summed
+  const int bh = b * Hq + h0;               // workspace row set of the pooled queries
   const float* K = kbar + ((int64_t)b * Hkv + g) * nb * D;
   const int row0 = rt * RG;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int D4 = D / 4;
 
   // ---- pool the RG query rows: pair (row r, 16-byte column c); TG token groups per pair
-  {
+  const float init = pmax ? -__builtin_inff() : 0.f;
+  const float scl = pmax ? 1.f : inv_block;
+  for (int j = 0; j < nh; ++j) {
+    const int h = h0 + j;
+    const bool last = j == nh - 1;
     const int C16 = D / E;                  // 16-byte columns per token of one head
     const int pairs = RG * C16;
     const int per_pass = pairs < kThreads ? pairs : kThreads;
@@ -81,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       const int row = row0 + r;
       float acc[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = 0.f;
+      for (int e = 0; e < E; ++e) acc[e] = init;
       if (tg < TG && row < nb) {
         const uint8_t* src = q + (((int64_t)b * N + (int64_t)row * block) * Hq + h) * D * EB + c * 16;
         int t = tg;
@@ -90,11 +108,18 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 #pragma unroll
           for (int u = 0; u < 8; ++u)
             w[u] = __builtin_nontemporal_load((const u32x4*)(src + (int64_t)(t + u * TG) * tok_bytes));
+          if (pmax) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u) Vec<KIND>::add(w[u], acc);
+            for (int u = 0; u < 8; ++u) Vec<KIND>::vmax(w[u], acc);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) Vec<KIND>::add(w[u], acc);
+          }
         }
-        for (; t < block; t += TG)
-          Vec<KIND>::add(__builtin_nontemporal_load((const u32x4*)(src + (int64_t)t * tok_bytes)), acc);
+        for (; t < block; t += TG) {
+          const u32x4 w = __builtin_nontemporal_load((const u32x4*)(src + (int64_t)t * tok_bytes));
+          if (pmax) Vec<KIND>::vmax(w, acc); else Vec<KIND>::add(w, acc);
+        }
       }
       if (TG > 1) {
         __syncthreads();                    // previous pass done with red
@@ -103,19 +128,22 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
           for (int e = 0; e < E; ++e) red[(tg * per_pass + tid % per_pass) * E + e] = acc[e];
         __syncthreads();
         for (int o = tid; o < per_pass * E; o += kThreads) {
-          float sum = 0.f;
-          for (int t2 = 0; t2 < TG; ++t2) sum += red[t2 * per_pass * E + o];
+          float sum = init;
+          for (int t2 = 0; t2 < TG; ++t2)
+            sum = pmax ? fmaxf(sum, red[t2 * per_pass * E + o]) : sum + red[t2 * per_pass * E + o];
           const int pr2 = p0 + o / E, r2 = pr2 / C16, d = (pr2 % C16) * E + o % E;
-          const float m = sum * inv_block;
+          float m = sum * scl;
+          if (j > 0) m += qs[r2 * D + d];   // the same thread wrote it for the previous head
           qs[r2 * D + d] = m;
-          if (row0 + r2 < nb) qbar[((int64_t)bh * nb + row0 + r2) * D + d] = m;
+          if (last && row0 + r2 < nb) qbar[((int64_t)bh * nb + row0 + r2) * D + d] = m;
         }
       } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float m = acc[e] * inv_block;
+          float m = acc[e] * scl;
+          if (j > 0) m += qs[r * D + c * E + e];
           qs[r * D + c * E + e] = m;
-          if (row < nb) qbar[((int64_t)bh * nb + row) * D + c * E + e] = m;
+          if (last && row < nb) qbar[((int64_t)bh * nb + row) * D + c * E + e] = m;
         }
       }
     }
@@ -161,74 +189,85 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   for (int r = 0; r < RW; ++r) {
     const int row = row0 + wave * RW + r;
     if (row >= nb) break;                   // wave-uniform
-    // columns past nb hold key 0, which no candidate (always >= 1) and no T reached by the
-    // search (>= 1 once any bit is set) can count
+    // columns past nb (and, causal, past the row) hold key 0, which no candidate (always
+    // >= 1) and no T reached by the search (>= 1 once any bit is set) can count; causal rows
+    // give their own block the largest key
+    const int lim = causal ? row + 1 : nb;  // admissible columns j < lim
+    const int kr = causal && row + 1 < topk ? row + 1 : topk;
     uint32_t key[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) key[c] = (c * 64 + lane) < nb ? order_key(acc[r][c]) : 0u;
+    for (int c = 0; c < CPL; ++c) {
+      const int j = c * 64 + lane;
+      key[c] = j < lim ? (causal && j == row ? 0xFFFFFFFFu : order_key(acc[r][c])) : 0u;
+    }
     uint32_t T = 0;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);
       int cnt = 0;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[c] >= cand));
-      if (cnt >= topk) T = cand;
-      if (cnt == topk) break;               // exactly k keys >= T: T separates the top k
+      if (cnt >= kr) T = cand;
+      if (cnt == kr) break;                 // exactly kr keys >= T: T separates the top kr
     }
     int gt = 0;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) gt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[c] > T));
-    const int need = topk - gt;             // >= 1 places for keys equal to T
-    int32_t* out = idx + ((int64_t)bh * nb + row) * topk;
-    int eq_before = 0, sel_before = 0;
+    const int need = kr - gt;               // places for keys equal to T
+    for (int j = 0; j < nh; ++j) {
+      int32_t* out = idx + ((int64_t)(bh + j) * nb + row) * topk;
+      int eq_before = 0, sel_before = 0;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const bool valid = (c * 64 + lane) < nb;
-      const bool is_eq = valid && key[c] == T;
-      const uint64_t meq = __builtin_amdgcn_ballot_w64(is_eq);
-      const bool sel = valid && (key[c] > T || (is_eq && eq_before + lanes_below(meq) < need));
-      const uint64_t msel = __builtin_amdgcn_ballot_w64(sel);
-      if (sel) out[sel_before + lanes_below(msel)] = c * 64 + lane;
-      eq_before += __builtin_popcountll(meq);
-      sel_before += __builtin_popcountll(msel);
+      for (int c = 0; c < CPL; ++c) {
+        const bool valid = (c * 64 + lane) < lim;
+        const bool is_eq = valid && key[c] == T;
+        const uint64_t meq = __builtin_amdgcn_ballot_w64(is_eq);
+        const bool sel = valid && (key[c] > T || (is_eq && eq_before + lanes_below(meq) < need));
+        const uint64_t msel = __builtin_amdgcn_ballot_w64(sel);
+        if (sel) out[sel_before + lanes_below(msel)] = c * 64 + lane;
+        eq_before += __builtin_popcountll(meq);
+        sel_before += __builtin_popcountll(msel);
+      }
+      for (int p = kr + lane; p < topk; p += kWave) out[p] = -1;   // unused causal places
     }
   }
 }
 
 template <int KIND, int CPL>
 hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int nb, int D, int block, int topk,
-                  const void* q, float* qbar, const float* kbar, int32_t* idx,
+                  const void* q, float* qbar, const float* kbar, int32_t* idx, unsigned flags,
                   hipStream_t stream) {
   constexpr int RG = SelCfg<CPL>::RG;
   const int row_tiles = (nb + RG - 1) / RG;
-  const dim3 grid((unsigned)(B * Hq * row_tiles));
+  const int HS = (flags & kGroup) ? Hkv : Hq;
+  const dim3 grid((unsigned)(B * HS * row_tiles));
   const size_t lds = (size_t)(64 * (D + 1) + RG * D) * sizeof(float);
   select_kernel<KIND, CPL><<<grid, kThreads, lds, stream>>>(
       (const uint8_t*)q, qbar, kbar, idx, N, Hq, Hkv, nb, D, block, topk, row_tiles,
-      1.0f / (float)block);
+      1.0f / (float)block, flags);
   return hipGetLastError();
 }
 
 template <int KIND>
 hipError_t launch_kind(int64_t B, int64_t N, int Hq, int Hkv, int nb, int D, int block, int topk,
                        const void* q, float* qbar, const float* kbar, int32_t* idx,
-                       hipStream_t stream) {
-  if (nb <= 64) return launch<KIND, 1>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
-  if (nb <= 128) return launch<KIND, 2>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
-  if (nb <= 256) return launch<KIND, 4>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
-  if (nb <= 512) return launch<KIND, 8>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
-  return launch<KIND, 16>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
+                       unsigned flags, hipStream_t stream) {
+  if (nb <= 64) return launch<KIND, 1>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
+  if (nb <= 128) return launch<KIND, 2>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
+  if (nb <= 256) return launch<KIND, 4>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
+  if (nb <= 512) return launch<KIND, 8>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
+  return launch<KIND, 16>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
 }
 
 }  // namespace
 
 hipError_t launch_pool_score_select(int kind, int64_t B, int64_t N, int Hq, int Hkv, int D,
                                     int block, int topk, const void* q, float* qbar,
-                                    const float* kbar, int32_t* idx, hipStream_t stream) {
+                                    const float* kbar, int32_t* idx, unsigned flags,
+                                    hipStream_t stream) {
   const int nb = (int)(N / block);
-  if (kind == 0) return launch_kind<0>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
-  if (kind == 1) return launch_kind<1>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
-  return launch_kind<2>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, stream);
+  if (kind == 0) return launch_kind<0>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
+  if (kind == 1) return launch_kind<1>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
+  return launch_kind<2>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
 }
 
 }  // namespace bsattn

@@ -18,6 +18,8 @@
 // (block-wide counts of keys >= candidate; early exit once exactly k keys are >= T), keys > T
 // are kept and keys == T fill the remaining places in ascending j (the lower index wins).
 // Output positions come from block-wide exclusive scans, so the row is written in ascending j.
+// Causal option: as in the fused kernel, columns j > i get key 0, column i the largest key,
+// the row keeps min(topk, i+1) blocks and its remaining places are set to -1.
 #include "common.h"
 #include "launch.h"
 
@@ -126,9 +128,12 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total)
 
 __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __restrict__ S,
                                                                  int32_t* __restrict__ idx,
-                                                                 int nb, int topk) {
+                                                                 int nb, int topk, bool causal) {
   __shared__ int red[4];
   const int64_t row = blockIdx.x;
+  const int i = (int)(row % nb);           // query block of this row
+  const int lim = causal ? i + 1 : nb;     // admissible columns j < lim
+  const int kr = causal && i + 1 < topk ? i + 1 : topk;
   const float* srow = S + row * nb;
   const int t = threadIdx.x;
   const int j0 = t * kPerThread;
@@ -138,9 +143,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     if (j0 + e < nb) v = *(const f32x4*)(srow + j0 + e);   // nb is a multiple of 4
 #pragma unroll
-    for (int q = 0; q < 4; ++q) key[e + q] = (j0 + e + q) < nb ? order_key(v[q]) : 0u;
+    for (int q = 0; q < 4; ++q) {
+      const int j = j0 + e + q;
+      key[e + q] = j < lim ? (causal && j == i ? 0xFFFFFFFFu : order_key(v[q])) : 0u;
+    }
   }
-  // keys of columns past nb are 0: no candidate (>= 1) and no reached T (>= 1) counts them
+  // keys of columns past lim are 0: no candidate (>= 1) and no reached T (>= 1) counts them
   uint32_t T = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
@@ -148,24 +156,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
 #pragma unroll
     for (int e = 0; e < kPerThread; ++e) c += key[e] >= cand;
     const int cnt = block_sum(c, red);
-    if (cnt >= topk) T = cand;
-    if (cnt == topk) break;
+    if (cnt >= kr) T = cand;
+    if (cnt == kr) break;
   }
   int gt = 0, eq = 0;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
     gt += key[e] > T;
-    eq += (j0 + e < nb) && key[e] == T;
+    eq += (j0 + e < lim) && key[e] == T;
   }
   const int tot_gt = block_sum(gt, red);
   int tot_eq;
   const int eq_before = block_exclusive_scan(eq, red, &tot_eq);
-  const int need = topk - tot_gt;          // places for keys equal to T
+  const int need = kr - tot_gt;            // places for keys equal to T
   int sel = 0;
   int eq_seen = eq_before;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
-    const bool is_eq = (j0 + e < nb) && key[e] == T;
+    const bool is_eq = (j0 + e < lim) && key[e] == T;
     sel += key[e] > T || (is_eq && eq_seen < need);
     eq_seen += is_eq;
   }
@@ -175,10 +183,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
   eq_seen = eq_before;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
-    const bool is_eq = (j0 + e < nb) && key[e] == T;
+    const bool is_eq = (j0 + e < lim) && key[e] == T;
     if (key[e] > T || (is_eq && eq_seen < need)) out[pos++] = j0 + e;
     eq_seen += is_eq;
   }
+  for (int p = kr + t; p < topk; p += kTopkThreads) out[p] = -1;   // unused causal places
 }
 
 }  // namespace
@@ -192,8 +201,8 @@ hipError_t launch_scores_large(int64_t B, int Hq, int Hkv, int nb, int D, const 
 }
 
 hipError_t launch_topk_rows(int64_t rows, int nb, int topk, const float* S, int32_t* idx,
-                            hipStream_t stream) {
-  topk_rows_kernel<<<dim3((unsigned)rows), kTopkThreads, 0, stream>>>(S, idx, nb, topk);
+                            bool causal, hipStream_t stream) {
+  topk_rows_kernel<<<dim3((unsigned)rows), kTopkThreads, 0, stream>>>(S, idx, nb, topk, causal);
   return hipGetLastError();
 }
 

@@ -13,32 +13,39 @@ __device__ unsigned int g_bad_rows;
 
 __global__ void reset_kernel() { g_bad_rows = 0u; }
 
-// one thread per row
+// one thread per row; causal rows (query block i = row index mod nb) use min(topk, i+1)
+// places with values in [0, i] and hold -1 in the others
 __global__ __launch_bounds__(256) void validate_kernel(const int32_t* __restrict__ idx,
-                                                       int64_t rows, int topk, int nb) {
+                                                       int64_t rows, int topk, int nb,
+                                                       bool causal) {
   const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= rows) return;
+  const int i = (int)(r % nb);
+  const int used = causal && i + 1 < topk ? i + 1 : topk;
+  const int lim = causal ? i + 1 : nb;
   const int32_t* row = idx + r * topk;
   bool ok = true;
   int prev = -1;
-  for (int j = 0; j < topk; ++j) {
+  for (int j = 0; j < used; ++j) {
     const int x = row[j];
-    ok &= x > prev && x < nb;
+    ok &= x > prev && x < lim;
     prev = x;
   }
+  for (int j = used; j < topk; ++j) ok &= row[j] == -1;
   if (!ok) atomicAdd(&g_bad_rows, 1u);
 }
 
 }  // namespace
 
-hipError_t validate_idx(int64_t rows, int topk, int nb, const int32_t* idx, hipStream_t stream,
-                        unsigned int* bad_rows) {
+hipError_t validate_idx(int64_t rows, int topk, int nb, const int32_t* idx, bool causal,
+                        hipStream_t stream, unsigned int* bad_rows) {
   *bad_rows = 0;
   if (rows == 0) return hipSuccess;
   reset_kernel<<<1, 1, 0, stream>>>();
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  validate_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(idx, rows, topk, nb);
+  validate_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(idx, rows, topk, nb,
+                                                                      causal);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = hipMemcpyFromSymbolAsync(bad_rows, HIP_SYMBOL(g_bad_rows), sizeof(unsigned int), 0,

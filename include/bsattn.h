@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define BSATTN_ABI_VERSION 1
+#define BSATTN_ABI_VERSION 2
 
 typedef enum {
   BSATTN_OK = 0,
@@ -57,7 +57,25 @@ typedef enum {
   BSATTN_FP8_E4M3 = 2   /* OCP 8-bit E4M3 ("fn": no infinities), values = code * descale */
 } bsattn_dtype;
 
-/* Version of this ABI (BSATTN_ABI_VERSION of the built library). */
+/* Options of the extended entry points (bit flags, combine with |). */
+/* Causal variant: query block i may select only key blocks j <= i; its own block i is always
+ * selected, the other min(topk, i+1) - 1 places go to the best-scoring j < i (ties to the
+ * lower j), the row stays ascending and its unused places hold -1; attention reads the
+ * first min(topk, i+1) entries of the row, which must lie in [0, i], and inside block i
+ * query t sees keys u <= t only. (The pages give no causal rule; the MSA page names MoBA
+ * among the block-based methods and checks that weights concentrate near the diagonal.) */
+#define BSATTN_CAUSAL 1u
+/* Selection only: pool with the elementwise maximum over the block's tokens instead of the
+ * mean (the "in-block extremum" scoring of the MSA page's §2.2 table). */
+#define BSATTN_POOL_MAX 2u
+/* Selection only (GQA, MSA page §3.1): one selection per KV head, from the sum over its
+ * Hq/Hkv query heads of their block scores; it is written to the idx rows of each of those
+ * heads. The workspace's pooled-query rows of the group's first head then hold the summed
+ * pooled queries. Supported for nb <= 1024. */
+#define BSATTN_GROUP_SELECT 4u
+
+/* Version of this ABI (BSATTN_ABI_VERSION of the built library). Version 2 added the
+ * BSATTN_* option flags and the two _ex entry points; version-1 calls are unchanged. */
 int bsattn_abi_version(void);
 
 /* Static English text of a status code; never NULL. */
@@ -99,6 +117,13 @@ int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int b
                   const void* q, const void* k, int32_t* idx,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* bsattn_select with options: flags is a combination of BSATTN_CAUSAL, BSATTN_POOL_MAX and
+ * BSATTN_GROUP_SELECT (0 gives bsattn_select). Other bits: BSATTN_E_INVALID. Same workspace
+ * size. Arguments, layouts and errors otherwise as bsattn_select. */
+int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
+                     int topk, unsigned flags, const void* q, const void* k, int32_t* idx,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Gathered-block attention (step 3 of "SparseFormer 注意力实现"; MSA page §2.1 with a
  * block mask, §2.2 second stage).
@@ -128,6 +153,17 @@ int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int b
 int bsattn_forward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                    const void* q, const void* k, const void* v, const int32_t* idx,
                    float scale, const float* descale_qkv, void* out, void* stream);
+
+/* bsattn_forward with options: BSATTN_CAUSAL gives the causal variant (row i reads its first
+ * min(topk, i+1) entries, each in [0, i]; an entry outside makes that query block's output
+ * NaN; keys after the query inside block i are masked). The selection-only bits
+ * BSATTN_POOL_MAX and BSATTN_GROUP_SELECT are accepted and have no effect here; other bits:
+ * BSATTN_E_INVALID. Under BSATTN_VALIDATE=1 causal rows are checked in that form (unused
+ * places must hold -1). Arguments, layouts and errors otherwise as bsattn_forward. */
+int bsattn_forward_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
+                      int topk, unsigned flags, const void* q, const void* k, const void* v,
+                      const int32_t* idx, float scale, const float* descale_qkv, void* out,
+                      void* stream);
 
 #ifdef __cplusplus
 }

@@ -74,6 +74,21 @@ def check_idx(gpu_idx: np.ndarray, S: np.ndarray, k: int):
             "ambiguous_differing": int((~exact_ok[amb]).sum()) if amb.size else 0}
 
 
+def check_idx_causal(gpu_idx: np.ndarray, S: np.ndarray, k: int):
+    """Causal rows [R20]: row i holds min(k, i+1) ascending blocks, the last being i itself,
+    then -1; its first min(k, i+1) - 1 entries must pass the index rule above against the
+    scores of the blocks j < i. gpu_idx [..., nb, k], S [..., nb, nb] oracle scores."""
+    nb = S.shape[-1]
+    assert gpu_idx.shape[-2:] == (nb, k)
+    for i in range(nb):
+        ki = min(k, i + 1)
+        rows = gpu_idx[..., i, :]
+        assert np.all(rows[..., ki:] == -1), f"row {i}: unused places not -1"
+        assert np.all(rows[..., ki - 1] == i), f"row {i}: own block not last"
+        if ki > 1:
+            check_idx(np.ascontiguousarray(rows[..., :ki - 1]), S[..., i, :i], ki - 1)
+
+
 def out_errors(gpu_out: np.ndarray, ref: np.ndarray):
     diff = gpu_out.astype(np.float64) - ref
     max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0

@@ -26,14 +26,15 @@ def test_library_exports_every_declared_function():
     L = bst.lib()
     names = declared_functions()
     assert {"bsattn_select", "bsattn_forward", "bsattn_select_workspace_bytes",
-            "bsattn_abi_version", "bsattn_status_str", "bsattn_last_error"} <= set(names)
+            "bsattn_abi_version", "bsattn_status_str", "bsattn_last_error",
+            "bsattn_select_ex", "bsattn_forward_ex"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings():
     L = bst.lib()
-    assert L.bsattn_abi_version() == 1
+    assert L.bsattn_abi_version() == 2
     for s in range(5):
         assert L.bsattn_status_str(s).decode() == bsattn.STATUS[s]
     assert L.bsattn_status_str(99).decode() == "unknown status"
@@ -92,6 +93,28 @@ def test_select_rejects(kw, status, msg):
 def test_forward_rejects(kw, status, msg):
     assert fwd(**kw) == status
     assert msg in last()
+
+
+def sel_ex(flags, **kw):
+    a = dict(dtype=1, B=1, N=512, Hq=2, Hkv=2, D=64, block=64, topk=2, q=FAKE, k=FAKE,
+             idx=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return bst.lib().bsattn_select_ex(a["dtype"], a["B"], a["N"], a["Hq"], a["Hkv"], a["D"],
+                                      a["block"], a["topk"], flags, a["q"], a["k"], a["idx"],
+                                      a["ws"], a["wsb"], None)
+
+
+def test_extended_entry_points_reject():
+    assert sel_ex(8) == 1 and "flags" in last()                   # unknown bit
+    assert sel_ex(4, N=64 * 2048, topk=3) == 2 and "group" in last()   # group: fused path only
+    assert sel_ex(1, q=None) == 1 and "null" in last()           # checks as bsattn_select
+    L = bst.lib()
+    st = L.bsattn_forward_ex(1, 1, 512, 2, 2, 64, 64, 2, 16, FAKE, FAKE, FAKE, FAKE, 0.125, None,
+                             FAKE, None)
+    assert st == 1 and "flags" in last()
+    st = L.bsattn_forward_ex(1, 1, 512, 2, 2, 64, 64, 2, 1, FAKE, FAKE, FAKE, FAKE,
+                             float("inf"), None, FAKE, None)
+    assert st == 1 and "scale" in last()
 
 
 def test_empty_calls_launch_nothing():

@@ -1,0 +1,143 @@
+"""Parity of the selection options and the causal variant (through the C ABI's extended
+entry points) with the fp64 oracle, on seeded inputs.
+
+Every test here runs on an MI355X; each prints the case it is about to run first.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_top_amd as bst
+from block_sparse_top_amd import synthetic as syn
+import oracle.bsattn_oracle as O
+from tests.parity import check_idx, check_idx_causal, check_out, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def stored_values(t):
+    """What the selection pools: the stored values (fp8: codes without the descale)."""
+    if t.dtype == torch.float8_e4m3fn:
+        return O.decode_e4m3(t.view(torch.uint8).cpu().numpy())
+    return to_f64(t)
+
+
+SHAPES = [
+    # B, N, Hq, Hkv, D, block, topk
+    (2, 64 * 37, 4, 2, 64, 64, 7),       # ragged nb, GQA 2
+    (1, 128 * 21, 6, 3, 128, 128, 5),    # block 128, D 128
+    (1, 64 * 300, 4, 1, 128, 64, 90),    # nb 300 (5 lanes of columns), GQA 4
+]
+OPTIONS = [
+    dict(causal=True), dict(pooling="max"), dict(group=True),
+    dict(causal=True, group=True), dict(causal=True, pooling="max"),
+]
+
+
+@pytest.mark.parametrize("opts", OPTIONS, ids=lambda o: "-".join(f"{k}={v}" for k, v in o.items()))
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("shape", SHAPES, ids=str)
+def test_select_options(shape, dtype, opts):
+    B, N, Hq, Hkv, D, blk, topk = shape
+    say(f"[select options] {opts} dtype={dtype} shape={shape}")
+    q, k, _, _ = syn.iid_inputs(B, N, Hq, Hkv, D, dtype, index=21, device=DEV)
+    idx = bst.select(q, k, blk, topk, **opts).cpu().numpy()
+    qo, ko = stored_values(q), stored_values(k)
+    pf = O.pool_max if opts.get("pooling") == "max" else O.pool
+    S = O.block_scores(pf(qo, blk), pf(ko, blk))
+    G = Hq // Hkv
+    if opts.get("group"):
+        for j in range(1, G):                      # every head of a group shares the rows
+            assert np.array_equal(idx[:, j::G], idx[:, ::G])
+        idx, S = idx[:, ::G], O.group_scores(S, Hkv)
+    if opts.get("causal"):
+        check_idx_causal(idx, S, topk)
+    else:
+        say("  ", check_idx(idx, S, topk))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("shape", [
+    (2, 64 * 37, 4, 2, 128, 64, 7),
+    (1, 128 * 21, 6, 3, 128, 128, 5),
+    (1, 64 * 12, 2, 2, 128, 64, 12),      # topk = nb: causal dense limit
+    (3, 64 * 9, 2, 1, 128, 64, 1),        # topk = 1: own block only
+], ids=str)
+def test_forward_causal(shape, dtype):
+    B, N, Hq, Hkv, D, blk, topk = shape
+    say(f"[forward causal] dtype={dtype} shape={shape}")
+    q, k, v, ds = syn.iid_inputs(B, N, Hq, Hkv, D, dtype, index=22, device=DEV)
+    idx = bst.select(q, k, blk, topk, causal=True)
+    out = bst.forward(q, k, v, idx, descales=ds, causal=True)
+    torch.cuda.synchronize()
+    qo, ko, vo = (to_f64(x, d) for x, d in zip((q, k, v), ds))
+    gidx = idx.cpu().numpy()
+    ref = O.attend_batched(qo, ko, vo, gidx, blk, 1 / math.sqrt(D), causal=True)
+    got = out.float().cpu().numpy()
+    fp8v = (float(np.abs(vo).max()), topk * blk) if dtype == "fp8" else None
+    say("   max_abs, rel_l2 =", check_out(got, ref, dtype, fp8_v=fp8v))
+    if topk == N // blk:
+        dense = O.dense_attention(qo, ko, vo, 1 / math.sqrt(D), causal=True)
+        check_out(got, dense, dtype, fp8_v=fp8v)
+    # negative control: the same rows without the causal mask differ
+    if dtype != "fp8":
+        nomask = O.attend_batched(qo, ko, vo, gidx, blk, 1 / math.sqrt(D), causal=False)
+        with pytest.raises(AssertionError):
+            check_out(got, nomask, dtype)
+
+
+def test_causal_out_of_range_entry_poisons_its_rows():
+    """A causal row naming a later block is not read: its query block's output is NaN."""
+    say("[causal later block]")
+    B, N, H, D, blk, topk = 1, 64 * 8, 2, 64, 64, 3
+    q, k, v, _ = syn.iid_inputs(B, N, H, H, D, "bf16", index=23, device=DEV)
+    idx = bst.select(q, k, blk, topk, causal=True)
+    ref = bst.forward(q, k, v, idx, causal=True)
+    bad = idx.clone()
+    bad[0, 1, 4, 1] = 6                          # block 6 > 4: after the query block
+    out = bst.forward(q, k, v, bad, causal=True)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[0, 4 * blk:5 * blk, 1].float()).all()
+    mask = torch.ones_like(out, dtype=torch.bool)
+    mask[0, 4 * blk:5 * blk, 1] = False
+    assert torch.equal(out[mask], ref[mask])
+
+
+def test_causal_validate_mode(monkeypatch):
+    say("[causal validate]")
+    B, N, H, D, blk, topk = 1, 64 * 8, 2, 64, 64, 3
+    q, k, v, _ = syn.iid_inputs(B, N, H, H, D, "bf16", index=23, device=DEV)
+    idx = bst.select(q, k, blk, topk, causal=True)
+    monkeypatch.setenv("BSATTN_VALIDATE", "1")
+    bst.forward(q, k, v, idx, causal=True)
+    for edit in (lambda t: t.__setitem__((0, 1, 4, 1), 6),      # later block
+                 lambda t: t.__setitem__((0, 0, 1, 2), 0)):     # unused place not -1
+        bad = idx.clone()
+        edit(bad)
+        with pytest.raises(bst.BsattnError) as e:
+            bst.forward(q, k, v, bad, causal=True)
+        assert e.value.status == 1 and "causal" in str(e.value)
+    with pytest.raises(bst.BsattnError):                      # causal rows are not full rows
+        bst.forward(q, k, v, idx)
+    torch.cuda.synchronize()
+
+
+def test_select_many_blocks_causal():
+    """More than 1024 key blocks (score matrix in the workspace), causal and max pooling."""
+    B, N, Hq, Hkv, D, blk, topk = 1, 64 * 1152, 2, 1, 64, 64, 200
+    say(f"[select many blocks causal] shape={(B, N, Hq, Hkv, D, blk, topk)}")
+    q, k, _, _ = syn.iid_inputs(B, N, Hq, Hkv, D, "bf16", index=24, device=DEV)
+    qo, ko = to_f64(q), to_f64(k)
+    idx = bst.select(q, k, blk, topk, causal=True).cpu().numpy()
+    check_idx_causal(idx, O.block_scores(O.pool(qo, blk), O.pool(ko, blk)), topk)
+    idx = bst.select(q, k, blk, topk, pooling="max").cpu().numpy()
+    say("  ", check_idx(idx, O.block_scores(O.pool_max(qo, blk), O.pool_max(ko, blk)), topk))
