@@ -35,6 +35,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-batches", type=int, default=0,
                    help="cap on batch elements in the oracle sample (0: time-bounded, ~10 s)")
+    p.add_argument("--causal", action="store_true",
+                   help="causal variant (own block forced, earlier blocks only, masked own block)")
+    p.add_argument("--pooling", choices=("mean", "max"), default="mean")
+    p.add_argument("--group", action="store_true", help="one selection per KV head group")
     return p.parse_args()
 
 
@@ -61,7 +65,8 @@ def traffic_per_launch():
         return None
 
 
-def cpu_baseline(w, q, k, v, ds, max_batches, budget_s=10.0):
+def cpu_baseline(w, q, k, v, ds, max_batches, budget_s=10.0, causal=False, pooling="mean",
+                 group=False):
     """The fp64 oracle, as it stands, on batch elements 0, 1, ... of the workload until
     `budget_s` seconds of CPU work are done (at least one, at most `max_batches`)."""
     import numpy as np
@@ -88,8 +93,8 @@ def cpu_baseline(w, q, k, v, ds, max_batches, budget_s=10.0):
         (qh, dt), (kh, _), (vh, _) = host(q[sl]), host(k[sl]), host(v[sl])
         t0 = time.perf_counter()
         qo, ko, vo = O.widen(qh, dt, ds[0]), O.widen(kh, dt, ds[1]), O.widen(vh, dt, ds[2])
-        idx = O.select(qo, ko, w.block, topk)
-        O.attend_batched(qo, ko, vo, idx, w.block, 1.0 / math.sqrt(w.D))
+        idx = O.select(qo, ko, w.block, topk, causal=causal, pooling=pooling, group=group)
+        O.attend_batched(qo, ko, vo, idx, w.block, 1.0 / math.sqrt(w.D), causal=causal)
         dt_s += time.perf_counter() - t0
         batches += 1
     return {"value": batches * w.N / dt_s, "unit": "tokens/s", "cores": int(threads),
@@ -129,14 +134,17 @@ def main():
     sp = ctypes.c_void_p(stream.cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
 
+    flags = (bst.CAUSAL if args.causal else 0) | (bst.POOL_MAX if args.pooling == "max" else 0) \
+        | (bst.GROUP_SELECT if args.group else 0)
+
     def do_select():
-        st = L.bsattn_select(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, P(q), P(k),
-                             P(idx), P(ws), ws.numel(), sp)
+        st = L.bsattn_select_ex(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, P(q),
+                                P(k), P(idx), P(ws), ws.numel(), sp)
         assert st == 0, L.bsattn_last_error()
 
     def do_forward():
-        st = L.bsattn_forward(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, P(q), P(k),
-                              P(v), P(idx), scale, dsc, P(out), sp)
+        st = L.bsattn_forward_ex(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, P(q),
+                                 P(k), P(v), P(idx), scale, dsc, P(out), sp)
         assert st == 0, L.bsattn_last_error()
 
     for _ in range(args.warmup):
@@ -161,21 +169,30 @@ def main():
     tokens = w.B * w.N
     value = tokens / (ms_per_step / 1e3)
 
-    flops = 4.0 * w.B * w.Hq * w.N * (topk * w.block) * w.D            # QK^T + PV
+    # QK^T + PV over every computed key block (causal: query block i computes min(topk, i+1)
+    # blocks, its own one in full although half of it is masked)
+    blocks = sum(min(topk, i + 1) for i in range(w.nb)) if args.causal else w.nb * topk
+    flops = 4.0 * w.B * w.Hq * w.block * (blocks * w.block) * w.D
     achieved = flops / (fwd_ms / 1e3) / 1e12
     peak = PEAK[w.dtype]
     ebytes = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
     sel_bytes = (w.B * w.N * (w.Hq + w.Hkv) * w.D * ebytes            # read q, k
                  + 2 * 4 * w.B * w.nb * (w.Hq + w.Hkv) * w.D          # pooled write + read
                  + 4 * w.B * w.Hq * w.nb * topk)                      # idx write
-    tr = traffic_per_launch()
+    if w.nb > 1024:                                                   # score matrix write + read
+        sel_bytes += 2 * 4 * w.B * w.Hq * w.nb * w.nb
+    plain = not (args.causal or args.group or args.pooling == "max")
+    tr = traffic_per_launch() if plain and w.name == "sparseformer_n8192_bf16" else None
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded N(0,1), resident in HBM)",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
-                   "block": w.block, "topk": topk, "parallelism": "single GPU"},
+                   "block": w.block, "topk": topk, "parallelism": "single GPU",
+                   **({"causal": True} if args.causal else {}),
+                   **({"pooling": "max"} if args.pooling == "max" else {}),
+                   **({"group_select": True} if args.group else {})},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": tr, "kernel": f"attn_{w.dtype}_kernel",
@@ -185,7 +202,9 @@ def main():
         "select_algorithmic_bytes": sel_bytes,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, ds, args.cpu_batches or w.B)
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, ds, args.cpu_batches or w.B,
+                                           causal=args.causal, pooling=args.pooling,
+                                           group=args.group)
     print(json.dumps(rec), flush=True)
 
 

@@ -4,5 +4,6 @@ The kernels live in libbsattn.so (C ABI, include/bsattn.h); `bsattn` is its bind
 Importing the package does not load the library; the first call does, and raises if
 it is not built.
 """
-from .bsattn import (BsattnError, block_sparse_attention, forward, lib, select,  # noqa: F401
-                     select_workspace_bytes, topk_count)
+from .bsattn import (CAUSAL, GROUP_SELECT, POOL_MAX, BsattnError,  # noqa: F401
+                     block_sparse_attention, forward, lib, select, select_workspace_bytes,
+                     topk_count)

@@ -72,7 +72,8 @@ size_t pooled_k_bytes(int64_t B, int64_t N, int Hkv, int D, int block) {
 // score matrix, only for the many-block path
 size_t scores_bytes(int64_t B, int64_t N, int Hq, int block) {
   const size_t nb = (size_t)(N / block);
-  if (nb <= (size_t)bsattn::kMaxFusedBlocks) return 0;
+  // the workspace query has no flags: size for the ungrouped selection (the larger one)
+  if (!bsattn::materialized_scores((int64_t)nb, false)) return 0;
   return align256((size_t)B * Hq * nb * nb * sizeof(float));
 }
 
@@ -121,7 +122,7 @@ int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, in
     return fail(BSATTN_E_INVALID, "unknown flags 0x%x", flags);
   if (B == 0 || N == 0) return BSATTN_OK;
   const int64_t nb = N / block;
-  const bool large = nb > bsattn::kMaxFusedBlocks;
+  const bool large = bsattn::materialized_scores(nb, flags & BSATTN_GROUP_SELECT);
   if (large && (nb > bsattn::kMaxLargeBlocks || nb % 64))
     return fail(BSATTN_E_UNSUPPORTED,
                 "selection over nb=%lld blocks (supported: nb <= %d, or a multiple of 64 up to %d)",

@@ -26,8 +26,8 @@
  *     next synchronisation.
  *   - Supported now: D in {64, 128}; block in {64, 128}; storage dtypes fp32, bf16 and OCP
  *     fp8 e4m3 (fp8 attention: D = 128). Selection: nb <= 1024, or nb a multiple of 64 up
- *     to 8192 (the score matrix then goes through the workspace). Other sizes give
- *     BSATTN_E_UNSUPPORTED.
+ *     to 8192 (the score matrix then goes through the workspace; group selection needs
+ *     nb <= 1024). Other sizes give BSATTN_E_UNSUPPORTED.
  *   - B == 0 or N == 0 is an empty call: arguments are checked, nothing is launched
  *     (topk must then be 0 when nb == 0).
  */

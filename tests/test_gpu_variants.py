@@ -141,3 +141,21 @@ def test_select_many_blocks_causal():
     check_idx_causal(idx, O.block_scores(O.pool(qo, blk), O.pool(ko, blk)), topk)
     idx = bst.select(q, k, blk, topk, pooling="max").cpu().numpy()
     say("  ", check_idx(idx, O.block_scores(O.pool_max(qo, blk), O.pool_max(ko, blk)), topk))
+
+
+@pytest.mark.parametrize("opts", [{}, dict(causal=True), dict(group=True)],
+                         ids=lambda o: "-".join(o) or "plain")
+def test_select_mid_range_blocks(opts):
+    """nb = 512: the fused kernel at 8 columns per lane, plain, causal and group."""
+    B, N, Hq, Hkv, D, blk, topk = 1, 64 * 512, 4, 2, 128, 64, 150
+    say(f"[select nb=512] {opts}")
+    q, k, _, _ = syn.iid_inputs(B, N, Hq, Hkv, D, "bf16", index=25, device=DEV)
+    idx = bst.select(q, k, blk, topk, **opts).cpu().numpy()
+    S = O.block_scores(O.pool(to_f64(q), blk), O.pool(to_f64(k), blk))
+    if opts.get("group"):
+        assert np.array_equal(idx[:, 1::2], idx[:, ::2])
+        idx, S = idx[:, ::2], O.group_scores(S, Hkv)
+    if opts.get("causal"):
+        check_idx_causal(idx, S, topk)
+    else:
+        say("  ", check_idx(idx, S, topk))
