@@ -43,6 +43,10 @@ the design notes of the repository):
   R22 group-shared selection (GQA, MSA §3.1): one selection per KV head from the sum of
       the block scores of its query heads (equivalently, from the summed pooled queries);
       every query head of the group uses it.
+  R25 backward (the MSA page's §4.1 checks that back-propagation is complete; the
+      SparseFormer page recommends the method for training large models, "千亿参数大模型训练"):
+      gradients of the gathered-block attention with the selection held fixed (top-k is
+      piecewise constant); the softmax Jacobian written out.
 
 Every function below is pinned by the CPU tests (tests/test_oracle_*.py) against
 closed forms, library routines, brute force or invariants; none is "parity unpinned".
@@ -329,6 +333,70 @@ def masked_attention_bruteforce(q, k, v, idx, block, scale, causal: bool = False
             p = np.exp(z - z.max(axis=1, keepdims=True))
             out[b, :, h, :] = (p @ v[b, :, g, :]) / p.sum(axis=1, keepdims=True)
     return out
+
+
+def attend_lse(q, k, idx, block, scale, causal: bool = False) -> np.ndarray:
+    """Natural log-sum-exp of every query row's scaled scores over its selected keys
+    [SF step 3; R20 when causal]: lse[b, h, t] = log sum_u exp(scale * q_t . k_u).
+    Returns [B, Hq, N] float64.
+    """
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    nb = N // block
+    lse = np.empty((B, Hq, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            for i in range(nb):
+                tok = np.concatenate([np.arange(j * block, (j + 1) * block)
+                                      for j in idx[b, h, i] if j >= 0])
+                z = scale * (q[b, i * block:(i + 1) * block, h, :] @ k[b, tok, g, :].T)
+                if causal:
+                    t = np.arange(i * block, (i + 1) * block)
+                    z = np.where(tok[None, :] <= t[:, None], z, -np.inf)
+                m = z.max(axis=1)
+                lse[b, h, i * block:(i + 1) * block] = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+    return lse
+
+
+def attend_backward(q, k, v, idx, block, scale, dout, causal: bool = False):
+    """Gradients of the gathered-block attention with the selection held fixed (NEXT N2):
+    for query block i with selected keys U, P = softmax(scale * Q_i K_U^T) (masked when
+    causal), O_i = P V_U, and for the upstream gradient dO_i:
+        dV_U += P^T dO_i,   dP = dO_i V_U^T,   dS = P * (dP - rowsum(dO_i * O_i)),
+        dQ_i = scale * dS K_U,   dK_U += scale * dS^T Q_i
+    (the softmax Jacobian written out). GQA: K/V gradients of KV head g collect the
+    contributions of all its query heads. Returns (dq, dk, dv) float64 with the shapes of
+    q, k, v.
+    """
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    nb = N // block
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            for i in range(nb):
+                rows = slice(i * block, (i + 1) * block)
+                tok = np.concatenate([np.arange(j * block, (j + 1) * block)
+                                      for j in idx[b, h, i] if j >= 0])
+                Qi, dOi = q[b, rows, h, :], dout[b, rows, h, :]
+                Ku, Vu = k[b, tok, g, :], v[b, tok, g, :]
+                z = scale * (Qi @ Ku.T)
+                if causal:
+                    t = np.arange(i * block, (i + 1) * block)
+                    z = np.where(tok[None, :] <= t[:, None], z, -np.inf)
+                p = np.exp(z - z.max(axis=1, keepdims=True))
+                P = p / p.sum(axis=1, keepdims=True)
+                Oi = P @ Vu
+                dP = dOi @ Vu.T
+                dS = P * (dP - (dOi * Oi).sum(axis=1, keepdims=True))
+                dq[b, rows, h, :] = scale * (dS @ Ku)
+                np.add.at(dk[b, :, g, :], tok, scale * (dS.T @ Qi))
+                np.add.at(dv[b, :, g, :], tok, P.T @ dOi)
+    return dq, dk, dv
 
 
 def select(q, k, block: int, topk: int, causal: bool = False, pooling: str = "mean",

@@ -310,11 +310,94 @@ def check_group_select(o=O):
     assert np.array_equal(ci[:, 0], ci[:, 1]) and np.all(ci[:, :, 0, 1:] == -1)
 
 
+def _dense_masked_torch(q, k, v, idx, blk, scale, causal):
+    """Masked dense attention in torch float64 (explicit N x N mask), for autograd."""
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    tb = np.arange(N) // blk
+    outs = []
+    for b in range(B):
+        per_h = []
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            M = np.zeros((N, N), dtype=bool)
+            for t in range(N):
+                M[t] = np.isin(tb, idx[b, h, tb[t]])
+                if causal:
+                    M[t, t + 1:] = False
+            z = scale * (q[b, :, h] @ k[b, :, g].T)
+            z = z.masked_fill(~torch.from_numpy(M), float("-inf"))
+            per_h.append(torch.softmax(z, dim=1) @ v[b, :, g])
+        outs.append(torch.stack(per_h, dim=1))
+    return torch.stack(outs, dim=0)
+
+
+def check_backward_autograd(o=O):
+    """Backward [N2] against torch autograd through the explicitly masked dense attention,
+    with GQA, plain and causal."""
+    B, N, Hq, Hkv, D, blk = 2, 192, 4, 2, 16, 32
+    q, k, v = rand_qkv(B, N, Hq, Hkv, D, seed=17)
+    dout = rng(18).standard_normal(q.shape)
+    for causal in (False, True):
+        idx = o.select(q, k, blk, 3, causal=causal)
+        dq, dk, dv = o.attend_backward(q, k, v, idx, blk, 0.3, dout, causal=causal)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        out = _dense_masked_torch(tq, tk, tv, idx, blk, 0.3, causal)
+        (out * torch.from_numpy(dout)).sum().backward()
+        for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+            assert np.max(np.abs(mine - ref.numpy())) <= 1e-12
+
+
+def check_backward_fd_and_invariants(o=O):
+    """Central finite differences of sum(out * dout) on a few entries, and the sums that
+    softmax rows fix: sum over keys of dV = sum over queries of dO (per KV head), sum over
+    keys of dK = 0."""
+    B, N, Hq, Hkv, D, blk = 1, 64, 2, 1, 8, 16
+    q, k, v = rand_qkv(B, N, Hq, Hkv, D, seed=19)
+    dout = rng(20).standard_normal(q.shape)
+    idx = o.select(q, k, blk, 2)
+    dq, dk, dv = o.attend_backward(q, k, v, idx, blk, 0.5, dout)
+    f = lambda qq, kk, vv: float(np.sum(o.attend(qq, kk, vv, idx, blk, 0.5) * dout))
+    eps = 1e-6
+    r = rng(21)
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(6):
+            pos = tuple(int(r.integers(0, n)) for n in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += eps
+            xm[pos] -= eps
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd = (f(*args_p) - f(*args_m)) / (2 * eps)
+            assert abs(fd - grad[pos]) <= 1e-7 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
+    assert np.allclose(dv.sum(axis=1)[:, 0], dout.sum(axis=(1, 2)), rtol=0, atol=1e-12)
+    assert np.allclose(dk.sum(axis=1), 0.0, rtol=0, atol=1e-12)
+
+
+def check_lse(o=O):
+    """Log-sum-exp of the masked scores against scipy's logsumexp of the dense masked rows."""
+    from scipy.special import logsumexp
+    B, N, H, D, blk = 1, 128, 2, 16, 32
+    q, k, _ = rand_qkv(B, N, H, H, D, seed=22)
+    for causal in (False, True):
+        idx = o.select(q, k, blk, 2, causal=causal)
+        got = o.attend_lse(q, k, idx, blk, 0.25, causal=causal)
+        tb = np.arange(N) // blk
+        for h in range(H):
+            z = 0.25 * (q[0, :, h] @ k[0, :, h].T)
+            for t in range(N):
+                keep = np.isin(tb, idx[0, h, tb[t]])
+                if causal:
+                    keep[t + 1:] = False
+                assert abs(got[0, h, t] - logsumexp(z[t][keep])) <= 1e-12
+
+
 ALL_CHECKS = [check_bf16_widen, check_e4m3, check_pool, check_scores, check_select_vs_sort,
               check_select_special, check_dense_limit, check_bruteforce, check_ties_and_zero,
               check_invariants, check_gqa, check_batched, check_causal_select,
               check_causal_dense_limit, check_causal_bruteforce, check_pool_max,
-              check_group_select]
+              check_group_select, check_backward_autograd, check_backward_fd_and_invariants,
+              check_lse]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -378,6 +461,27 @@ def _strict_causal(q, k, v, idx, blk, scale, rows=None, causal=False):
     return out
 
 
+def _backward_no_rowterm(q, k, v, idx, blk, scale, dout, causal=False):
+    """attend_backward with dS = P * dP (the rowsum(dO * O) term dropped): a planted mistake."""
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    dq, dk, dv = (np.zeros(x.shape) for x in (q, k, v))
+    for b in range(B):
+        for h in range(Hq):
+            g = O.kv_head(h, Hq, Hkv)
+            for i in range(N // blk):
+                rows = slice(i * blk, (i + 1) * blk)
+                tok = np.concatenate([np.arange(j * blk, (j + 1) * blk) for j in idx[b, h, i] if j >= 0])
+                z = scale * (q[b, rows, h] @ k[b, tok, g].T)
+                p = np.exp(z - z.max(axis=1, keepdims=True))
+                P = p / p.sum(axis=1, keepdims=True)
+                dS = P * (dout[b, rows, h] @ v[b, tok, g].T)
+                dq[b, rows, h] = scale * dS @ k[b, tok, g]
+                np.add.at(dk[b, :, g], tok, scale * dS.T @ q[b, rows, h])
+                np.add.at(dv[b, :, g], tok, P.T @ dout[b, rows, h])
+    return dq, dk, dv
+
+
 class Mutant:
     """The oracle module with one function replaced by a wrong version."""
 
@@ -436,6 +540,14 @@ MUTANTS = {
         attend=lambda q, k, v, idx, blk, scale, rows=None, causal=False:
         _strict_causal(q, k, v, idx, blk, scale, rows, causal)),
     "pool_max_is_min": dict(pool_max=lambda x, b: -O.pool_max(-x, b)),
+    "backward_without_row_term": dict(
+        attend_backward=lambda q, k, v, idx, blk, scale, dout, causal=False:
+        _backward_no_rowterm(q, k, v, idx, blk, scale, dout, causal)),
+    "backward_dk_unscaled": dict(
+        attend_backward=lambda q, k, v, idx, blk, scale, dout, causal=False:
+        (lambda g: (g[0], g[1] / scale, g[2]))(O.attend_backward(q, k, v, idx, blk, scale, dout, causal))),
+    "lse_log2": dict(attend_lse=lambda q, k, idx, blk, scale, causal=False:
+                     O.attend_lse(q, k, idx, blk, scale, causal) / np.log(2.0)),
     "group_first_head_only": dict(
         group_scores=lambda S, Hkv: S.reshape(S.shape[0], Hkv, -1, *S.shape[2:])[:, :, 0]),
     "e4m3_bias_8": dict(decode_e4m3=lambda c: O.decode_e4m3(c) / 2),
