@@ -144,7 +144,7 @@ def main():
 
     def do_forward():
         st = L.bsattn_forward_ex(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, P(q),
-                                 P(k), P(v), P(idx), scale, dsc, P(out), sp)
+                                 P(k), P(v), P(idx), scale, dsc, P(out), None, sp)
         assert st == 0, L.bsattn_last_error()
 
     for _ in range(args.warmup):

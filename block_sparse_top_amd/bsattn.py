@@ -65,7 +65,12 @@ def lib() -> ctypes.CDLL:
                                    sz, vp]
     L.bsattn_forward_ex.restype = i32
     L.bsattn_forward_ex.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, u32, vp, vp, vp, vp,
-                                    ctypes.c_float, ctypes.POINTER(ctypes.c_float), vp, vp]
+                                    ctypes.c_float, ctypes.POINTER(ctypes.c_float), vp, vp, vp]
+    L.bsattn_backward_workspace_bytes.restype = sz
+    L.bsattn_backward_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32, i32]
+    L.bsattn_backward.restype = i32
+    L.bsattn_backward.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, u32, vp, vp, vp, vp, vp,
+                                  vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     _lib = L
     return L
 
@@ -150,11 +155,12 @@ def select(q, k, block: int, topk: int, *, causal: bool = False, pooling: str = 
 
 
 def forward(q, k, v, idx, scale: float | None = None, descales=(1.0, 1.0, 1.0), out=None, *,
-            causal: bool = False):
+            causal: bool = False, return_lse: bool = False):
     """Attention of every query block over its selected key blocks: [B, N, Hq, D].
 
     Output dtype: fp32 for fp32 inputs, bf16 for bf16 and fp8 inputs. causal: rows in the
-    form `select(..., causal=True)` writes; keys after the query are masked.
+    form `select(..., causal=True)` writes; keys after the query are masked. return_lse: also
+    the rows' natural log-sum-exp, fp32 [B, Hq, N] (the input `backward` needs).
     """
     B, N, Hq, Hkv, D = _shapes(q, k, v)
     if idx.dim() != 4 or idx.dtype != torch.int32 or not idx.is_contiguous() or not idx.is_cuda:
@@ -172,11 +178,44 @@ def forward(q, k, v, idx, scale: float | None = None, descales=(1.0, 1.0, 1.0), 
     elif out.shape != (B, N, Hq, D) or out.dtype != odt or not out.is_contiguous():
         raise ValueError("out has the wrong shape, dtype or layout")
     ds = (ctypes.c_float * 3)(*[float(x) for x in descales])
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if return_lse else None
     with torch.cuda.device(q.device):
         _check(lib().bsattn_forward_ex(_DTYPES[q.dtype], B, N, Hq, Hkv, D, block, topk,
                                        CAUSAL if causal else 0, _ptr(q), _ptr(k), _ptr(v),
-                                       _ptr(idx), scale, ds, _ptr(out), _stream(q.device)))
-    return out
+                                       _ptr(idx), scale, ds, _ptr(out), _ptr(lse),
+                                       _stream(q.device)))
+    return (out, lse) if return_lse else out
+
+
+def backward(q, k, v, idx, out, dout, lse, scale: float | None = None, *, causal: bool = False,
+             workspace=None):
+    """Gradients (dq, dk, dv), fp32, of the attention with the selection `idx` held fixed.
+
+    out and lse come from `forward(..., return_lse=True)`; dout is bf16 like out.
+    """
+    B, N, Hq, Hkv, D = _shapes(q, k, v)
+    nb, topk = idx.shape[2], idx.shape[3]
+    block = N // nb if nb else 0
+    for t in (out, dout):
+        if t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("out and dout must be contiguous bf16 [B, N, Hq, D]")
+    if lse.shape != (B, Hq, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, Hq, N]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    L = lib()
+    nbytes = int(L.bsattn_backward_workspace_bytes(B, N, Hq, Hkv, D, block, topk)) if block else 0
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(L.bsattn_backward(_DTYPES[q.dtype], B, N, Hq, Hkv, D, block, topk,
+                                 CAUSAL if causal else 0, _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                                 _ptr(out), _ptr(dout), _ptr(lse), scale, _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(workspace), workspace.numel(),
+                                 _stream(q.device)))
+    return dq, dk, dv
 
 
 def block_sparse_attention(q, k, v, block_size: int = 64, topk_ratio: float = 0.3,

@@ -168,13 +168,13 @@ int bsattn_forward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int 
                    const void* q, const void* k, const void* v, const int32_t* idx, float scale,
                    const float* descale_qkv, void* out, void* stream) {
   return bsattn_forward_ex(dtype, B, N, Hq, Hkv, D, block, topk, 0u, q, k, v, idx, scale,
-                           descale_qkv, out, stream);
+                           descale_qkv, out, nullptr, stream);
 }
 
 int bsattn_forward_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
                       int topk, unsigned flags, const void* q, const void* k, const void* v,
                       const int32_t* idx, float scale, const float* descale_qkv, void* out,
-                      void* stream) {
+                      float* lse, void* stream) {
   int st = check_shape(dtype, B, N, Hq, Hkv, D, block, topk);
   if (st != BSATTN_OK) return st;
   if (flags & ~(unsigned)(BSATTN_CAUSAL | BSATTN_POOL_MAX | BSATTN_GROUP_SELECT))
@@ -190,8 +190,10 @@ int bsattn_forward_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, i
   }
   if (B == 0 || N == 0) return BSATTN_OK;
   if (!q || !k || !v || !idx || !out) return fail(BSATTN_E_INVALID, "null pointer argument");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)idx & 3u))
-    return fail(BSATTN_E_INVALID, "q, k, v, out must be 16-byte aligned, idx 4-byte aligned");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)idx & 3u) ||
+      ((uintptr_t)lse & 3u))
+    return fail(BSATTN_E_INVALID,
+                "q, k, v, out must be 16-byte aligned, idx and lse 4-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   if (validate_enabled()) {
     unsigned int bad = 0;
@@ -210,22 +212,68 @@ int bsattn_forward_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, i
     if (!bsattn::attn_bf16_supported(D, block))
       return fail(BSATTN_E_UNSUPPORTED, "bf16 attention for D=%d block=%d", D, block);
     return hip_status(bsattn::launch_attn_bf16(B, N, Hq, Hkv, D, block, topk, q, k, v, idx,
-                                               scale, out, causal, s),
+                                               scale, out, lse, causal, s),
                       "bf16 attention launch");
   }
   if (dtype == BSATTN_F32) {
     if (!bsattn::attn_f32_supported(D, block))
       return fail(BSATTN_E_UNSUPPORTED, "fp32 attention for D=%d block=%d", D, block);
     return hip_status(bsattn::launch_attn_f32(B, N, Hq, Hkv, D, block, topk, q, k, v, idx,
-                                              scale, out, causal, s),
+                                              scale, out, lse, causal, s),
                       "fp32 attention launch");
   }
   if (!bsattn::attn_fp8_supported(D, block))
     return fail(BSATTN_E_UNSUPPORTED, "fp8 attention for D=%d block=%d (supported: D=128)", D,
                 block);
   return hip_status(bsattn::launch_attn_fp8(B, N, Hq, Hkv, D, block, topk, q, k, v, idx, scale,
-                                            descale_qkv, out, causal, s),
+                                            descale_qkv, out, lse, causal, s),
                     "fp8 attention launch");
+}
+
+size_t bsattn_backward_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
+                                       int topk) {
+  (void)D;
+  if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || block < 1 || N % block || topk < 0) {
+    fail(BSATTN_E_INVALID, "invalid sizes for the workspace query");
+    return 0;
+  }
+  if (B == 0 || N == 0) return 0;
+  return bsattn::attn_bwd_workspace_bytes(B, N, Hq, Hkv, block, topk);
+}
+
+int bsattn_backward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
+                    unsigned flags, const void* q, const void* k, const void* v,
+                    const int32_t* idx, const void* out, const void* dout, const float* lse,
+                    float scale, float* dq, float* dk, float* dv, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = check_shape(dtype, B, N, Hq, Hkv, D, block, topk);
+  if (st != BSATTN_OK) return st;
+  if (flags & ~(unsigned)(BSATTN_CAUSAL | BSATTN_POOL_MAX | BSATTN_GROUP_SELECT))
+    return fail(BSATTN_E_INVALID, "unknown flags 0x%x", flags);
+  if (!isfinite(scale) || !(scale > 0.f))
+    return fail(BSATTN_E_INVALID, "scale must be finite and > 0");
+  const int kind = dtype == BSATTN_F32 ? 0 : dtype == BSATTN_BF16 ? 1 : 2;
+  if (!bsattn::attn_bwd_supported(kind, D, block))
+    return fail(BSATTN_E_UNSUPPORTED, "backward for dtype %d D=%d block=%d (supported: bf16, "
+                                      "D 64 or 128, block 64)", dtype, D, block);
+  if (N / block > bsattn::kMaxBwdBlocks)
+    return fail(BSATTN_E_UNSUPPORTED, "backward over nb=%lld > %d blocks",
+                (long long)(N / block), bsattn::kMaxBwdBlocks);
+  if (B == 0 || N == 0) return BSATTN_OK;
+  if (!q || !k || !v || !idx || !out || !dout || !lse || !dq || !dk || !dv)
+    return fail(BSATTN_E_INVALID, "null pointer argument");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)idx & 3u) ||
+      ((uintptr_t)lse & 3u))
+    return fail(BSATTN_E_INVALID, "tensors must be 16-byte aligned, idx and lse 4-byte aligned");
+  const size_t need = bsattn::attn_bwd_workspace_bytes(B, N, Hq, Hkv, block, topk);
+  if (!workspace || workspace_bytes < need)
+    return fail(BSATTN_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if ((uintptr_t)workspace & 255u) return fail(BSATTN_E_WORKSPACE, "workspace not 256-byte aligned");
+  return hip_status(bsattn::launch_attn_bwd(B, N, Hq, Hkv, D, topk, flags & BSATTN_CAUSAL, q, k, v,
+                                            idx, out, dout, lse, scale, dq, dk, dv, workspace,
+                                            (hipStream_t)stream),
+                    "backward launch");
 }
 
 }  // extern "C"

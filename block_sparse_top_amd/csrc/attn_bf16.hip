@@ -93,7 +93,8 @@ template <int D, int BLK, bool CAUSAL>
 __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
-    int64_t N, int Hq, int Hkv, int nb, int topk, float c, uint32_t total_tiles) {
+    float* __restrict__ lse, int64_t N, int Hq, int Hkv, int nb, int topk, float c,
+    uint32_t total_tiles) {
   using C = Cfg<D, BLK>;
   __shared__ __attribute__((aligned(1024))) char Kl[C::TILE];   // [BLK][D] bf16, swizzled
   __shared__ __attribute__((aligned(1024))) char Vl[C::TILE];
@@ -346,6 +347,9 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
     const float l_all = lsum[qc] + __shfl_xor(lsum[qc], 32);
     const float inv = bad ? __builtin_nanf("") : 1.0f / l_all;
     uint16_t* orow = out + (qrow0 + 32 * qc) * qrs + (int64_t)h * D;
+    if (lse && half == 0)                      // natural log-sum-exp of the row's scaled scores
+      lse[((int64_t)b * Hq + h) * N + (qrow0 - (int64_t)b * N) + 32 * qc] =
+          bad ? __builtin_nanf("") : (mc[qc] + log2f(l_all)) * 0.6931471805599453f;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -361,18 +365,18 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
 
 template <int D, int BLK>
 hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int topk, const void* q, const void* k,
-                  const void* v, const int32_t* idx, float c, void* out, bool causal,
-                  hipStream_t stream) {
+                  const void* v, const int32_t* idx, float c, void* out, float* lse,
+                  bool causal, hipStream_t stream) {
   const int nb = (int)(N / BLK);
   const uint32_t total = (uint32_t)(B * Hq * nb);
   if (causal)
     attn_bf16_kernel<D, BLK, true><<<total, Cfg<D, BLK>::NT, 0, stream>>>(
-        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, N, Hq,
-        Hkv, nb, topk, c, total);
+        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, lse, N,
+        Hq, Hkv, nb, topk, c, total);
   else
     attn_bf16_kernel<D, BLK, false><<<total, Cfg<D, BLK>::NT, 0, stream>>>(
-        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, N, Hq,
-        Hkv, nb, topk, c, total);
+        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, lse, N,
+        Hq, Hkv, nb, topk, c, total);
   return hipGetLastError();
 }
 
@@ -384,12 +388,13 @@ bool attn_bf16_supported(int D, int block) {
 
 hipError_t launch_attn_bf16(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                             const void* q, const void* k, const void* v, const int32_t* idx,
-                            float scale, void* out, bool causal, hipStream_t stream) {
+                            float scale, void* out, float* lse, bool causal,
+                            hipStream_t stream) {
   const float c = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
-  if (D == 64 && block == 64) return launch<64, 64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, causal, stream);
-  if (D == 64 && block == 128) return launch<64, 128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, causal, stream);
-  if (D == 128 && block == 64) return launch<128, 64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, causal, stream);
-  return launch<128, 128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, causal, stream);
+  if (D == 64 && block == 64) return launch<64, 64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal, stream);
+  if (D == 64 && block == 128) return launch<64, 128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal, stream);
+  if (D == 128 && block == 64) return launch<128, 64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal, stream);
+  return launch<128, 128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal, stream);
 }
 
 }  // namespace bsattn

@@ -1,0 +1,469 @@
+// Backward of the gathered-block attention (bf16 inputs, fp32 gradients, block 64, D 64 or
+// 128) with the selected blocks held fixed.
+//
+// SparseFormer page ("2026 新一代卷积与Transformer网络架构技术演进与性能对比"): the method is
+// recommended for training large models ("千亿参数大模型训练"); MSA page
+// ("从M2.7到M3：多模态模型稀疏注意力架构设计与实现全解析") §4.1 checks that back-propagation
+// through the sparse attention is complete. For query block i with selected keys U,
+// P = softmax(scale * Q_i K_U^T) (row log-sum-exp from the forward), and the upstream dO_i:
+//   dV_U += P^T dO_i,  dP = dO_i V_U^T,  dS = P * (dP - rowsum(dO_i * O_i)),
+//   dQ_i = scale * dS K_U,  dK_U += scale * dS^T Q_i.
+//
+// Kernels:
+//   rowdot_kernel   Dvec[b,h,t] = sum_d dO * O (fp32), one thread per row.
+//   index_kernel    per (batch, KV head): for every key block j the list of (query head of
+//                   the group, query block) pairs that selected it, in ascending pair order
+//                   (LDS counts, a scan, then the rows in order), so the key-side sums run in
+//                   a fixed order and the gradients are reproducible bit for bit.
+//   dq_kernel       query-major like the forward: per selected block S^T = K Q^T and
+//                   dP^T = V dO^T on bf16 MFMA (A = K or V rows from LDS, B = Q^T or dO^T in
+//                   registers), P^T and dS^T in fp32, dQ^T += K^T dS^T (A = K^T by LDS
+//                   transpose reads, B = dS^T rounded to bf16 straight from the accumulators).
+//   dkv_kernel      key-major: one work-group per (batch, KV head, key block) keeps K and V rows
+//                   of its keys in registers (B operands) and walks its pair list: S = Q K^T,
+//                   dP = dO V^T (A = Q or dO rows from LDS), P and dS in fp32, then
+//                   dV^T += dO^T P and dK^T += Q^T dS (A = dO^T, Q^T by transpose reads,
+//                   B = P, dS rounded to bf16 from the accumulators). No atomics.
+// Layout conventions follow the forward kernel: 32x32 MFMA accumulators (register r, lane l:
+// row 8(r/4) + 4(l/32) + r%4, column l%32), 16-key (or 16-query) k-steps whose 16 slots are
+// matched to {4h..4h+3, 8+4h..8+4h+3} on both operands, tiles [64][D] bf16 in LDS with the
+// 16-byte chunk c of row r at chunk c ^ f(r), f(r) = 2(r&3) + ((r>>2)&1).
+// Causal option: query block i reads its first min(topk, i+1) entries (each in [0, i]) and in
+// its own block keys after the query get weight 0; the dS of masked pairs is 0.
+#include "common.h"
+#include "launch.h"
+
+namespace bsattn {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kBlk = 64;                      // block size of this backward
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int swz(int r, int c) {
+  const int f = 2 * (r & 3) + ((r >> 2) & 1);
+  return (c & ~7) | ((c & 7) ^ f);
+}
+
+__device__ __forceinline__ s16x4 ds_read_tr16(const char* lds_bytes) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_void*)(lds_bytes));
+}
+
+// Copy rows [row0, row0 + 64) of a [*, H, D] bf16 tensor (head h) into an LDS tile [64][D],
+// swizzled; all threads of the work-group take part.
+template <int D, int NT>
+__device__ __forceinline__ void load_tile(char* tile, const uint16_t* base, int64_t row0,
+                                          int64_t rstride, int tid) {
+  constexpr int CH = D / 8;                   // 16-byte chunks per row
+#pragma unroll
+  for (int x = 0; x < kBlk * CH / NT; ++x) {
+    const int pos = x * NT + tid;
+    const int r = pos / CH, c = pos % CH;
+    const u32x4 w = *(const u32x4*)(base + (row0 + r) * rstride + 8 * c);
+    *(u32x4*)(tile + r * D * 2 + 16 * swz(r, c)) = w;
+  }
+}
+
+// A operand (32 rows x 16 d) of a row-major tile: rows 32*t + l32, d = 16s + 8*half .. +7
+template <int D>
+__device__ __forceinline__ bf16x8 rows_operand(const char* tile, int t, int s, int l32, int half) {
+  const int r = 32 * t + l32;
+  return __builtin_bit_cast(bf16x8, *(const u32x4*)(tile + r * D * 2 + 16 * swz(r, 2 * s + half)));
+}
+
+// A operand (32 d x 16 rows) of a row-major tile read transposed: d rows 32*dt + l32, rows
+// 16*ps + {4h..4h+3, 8+4h..8+4h+3} (the forward's V^T reads)
+template <int D>
+__device__ __forceinline__ bf16x8 trans_operand(const char* tile, int dt, int ps, int lane) {
+  const int half = lane >> 5;
+  const int e = (lane & 15) >> 2, r = 4 * half + e;
+  const int ch = 4 * dt + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const char* p = tile + (16 * ps + r) * D * 2 + 16 * swz(r, ch) + 8 * (lane & 1);
+  const s16x4 a8[2] = {ds_read_tr16(p), ds_read_tr16(p + 8 * D * 2)};
+  return __builtin_bit_cast(bf16x8, a8);
+}
+
+// 8 bf16 of a global row (B operand: the lane's row, d = 16s + 8*half .. +7)
+__device__ __forceinline__ bf16x8 row_chunk(const uint16_t* row, int s, int half) {
+  return __builtin_bit_cast(bf16x8, *(const u32x4*)(row + 16 * s + 8 * half));
+}
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// B operand of a 16-slot k-step from two 32-row accumulator tiles: k-step ps covers
+// accumulator tile ps >> 1, registers 8*(ps&1) .. +7 (slots {4h.., 8+4h..})
+__device__ __forceinline__ bf16x8 pack_step(const f32x16 (&acc)[2], int ps) {
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = pack_bf16x2(acc[ps >> 1][8 * (ps & 1) + 2 * e], acc[ps >> 1][8 * (ps & 1) + 2 * e + 1]);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// ---------------------------------------------------------------- Dvec
+template <int D>
+__global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict__ out,
+                                                     const uint16_t* __restrict__ dout,
+                                                     float* __restrict__ dvec, int64_t rows,
+                                                     int64_t N, int Hq) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, t, h) row
+  if (r >= rows) return;
+  const uint16_t* o = out + r * D;
+  const uint16_t* g = dout + r * D;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const u32x4 a = *(const u32x4*)(o + 8 * c), x = *(const u32x4*)(g + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc += bf16lo(a[e]) * bf16lo(x[e]) + bf16hi(a[e]) * bf16hi(x[e]);
+  }
+  const int h = (int)(r % Hq);
+  const int64_t bt = r / Hq, b = bt / N, t = bt % N;
+  dvec[(b * Hq + h) * N + t] = acc;
+}
+
+// ---------------------------------------------------------------- inverted index
+constexpr int kIdxThreads = 256;
+
+// one work-group per (b, g): counts[j] of pairs selecting key block j, offsets (exclusive
+// scan, written to `offsets` [nb + 1]) and pairs in ascending (query head of the group, query
+// block) order, pair = hh * nb + i, stored at seg + offsets[j] + rank
+__global__ __launch_bounds__(kIdxThreads) void index_kernel(const int32_t* __restrict__ idx,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ pairs,
+                                                            int Hq, int Hkv, int nb, int topk,
+                                                            bool causal) {
+  extern __shared__ int sm[];
+  int* cnt = sm;                              // [nb + 1]: counts, then offsets
+  int* cur = sm + nb + 1;                     // [nb]: next free place per key block
+  __shared__ int wsum[kIdxThreads / kWave];
+  const int bg = blockIdx.x;
+  const int b = bg / Hkv, g = bg % Hkv, G = Hq / Hkv;
+  const int tid = threadIdx.x;
+  const int rows = G * nb;                    // (hh, i) rows of this group, in pair order
+  const int32_t* gidx = idx + ((int64_t)b * Hq + (int64_t)g * G) * nb * topk;
+  for (int j = tid; j <= nb; j += kIdxThreads) cnt[j] = 0;
+  __syncthreads();
+  for (int64_t e = tid; e < (int64_t)rows * topk; e += kIdxThreads) {
+    const int i = (int)((e / topk) % nb), t = (int)(e % topk);
+    const int used = causal && i + 1 < topk ? i + 1 : topk;
+    const int j = gidx[e];
+    if (t < used && (unsigned)j < (unsigned)nb) atomicAdd(&cnt[j], 1);
+  }
+  __syncthreads();
+  // exclusive scan of cnt[0..nb) in place; cnt[nb] = total
+  {
+    const int per = (nb + kIdxThreads - 1) / kIdxThreads;
+    const int j0 = tid * per;
+    int local = 0;
+    for (int j = j0; j < j0 + per && j < nb; ++j) local += cnt[j];
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if ((tid & (kWave - 1)) >= o) incl += y;
+    }
+    if ((tid & (kWave - 1)) == kWave - 1) wsum[tid / kWave] = incl;
+    __syncthreads();
+    int before = incl - local;
+    for (int w = 0; w < tid / kWave; ++w) before += wsum[w];
+    __syncthreads();
+    for (int j = j0; j < j0 + per && j < nb; ++j) {
+      const int c = cnt[j];
+      cnt[j] = before;
+      cur[j] = before;
+      before += c;
+    }
+    if (tid == kIdxThreads - 1) cnt[nb] = before;
+  }
+  __syncthreads();
+  int32_t* off = offsets + (int64_t)bg * (nb + 1);
+  for (int j = tid; j <= nb; j += kIdxThreads) off[j] = cnt[j];
+  int32_t* seg = pairs + (int64_t)bg * rows * topk;
+  // rows in order; the entries of one row name distinct blocks, so one step has no conflict
+  for (int row = 0; row < rows; ++row) {
+    const int i = row % nb;
+    const int used = causal && i + 1 < topk ? i + 1 : topk;
+    for (int t = tid; t < used; t += kIdxThreads) {
+      const int j = gidx[(int64_t)row * topk + t];
+      if ((unsigned)j < (unsigned)nb) seg[atomicAdd(&cur[j], 1)] = row;   // atomic: a row
+    }                                                                      // may repeat j
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+// work-group per (b, h, query block i): 2 waves x 32 queries
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(128) void dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const int32_t* __restrict__ idx, const float* __restrict__ lse,
+    const float* __restrict__ dvec, float* __restrict__ dq, int64_t N, int Hq, int Hkv, int nb,
+    int topk, float c, float scale, uint32_t total_tiles) {
+  constexpr int NS = D / 16, NDT = D / 32;
+  __shared__ __attribute__((aligned(16))) char Kt[kBlk * D * 2];
+  __shared__ __attribute__((aligned(16))) char Vt[kBlk * D * 2];
+  const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
+  const int G = Hq / Hkv;
+  const int i = (int)(tile % nb);
+  uint32_t rest = tile / nb;
+  const int hh = (int)(rest % G);
+  rest /= G;
+  const int g = (int)(rest % Hkv);
+  const int b = (int)(rest / Hkv);
+  const int h = g * G + hh;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int64_t qrs = (int64_t)Hq * D, krs = (int64_t)Hkv * D;
+  const int qloc = 32 * wave + l32;           // query row of this lane's column, in the block
+  const int64_t qrow = (int64_t)b * N + (int64_t)i * kBlk + qloc;
+
+  bf16x8 qf[NS], gf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    qf[s] = row_chunk(q + qrow * qrs + (int64_t)h * D, s, half);
+    gf[s] = row_chunk(dout + qrow * qrs + (int64_t)h * D, s, half);
+  }
+  const int64_t rowid = ((int64_t)b * Hq + h) * N + (int64_t)i * kBlk + qloc;
+  const float l2 = lse[rowid] * kLog2e;       // log2-sum-exp of the row
+  const float dd = dvec[rowid];
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  const int32_t* myidx = idx + (((int64_t)b * Hq + h) * nb + i) * topk;
+  const int kcount = CAUSAL && i + 1 < topk ? i + 1 : topk;
+  const unsigned klim = CAUSAL ? (unsigned)(i + 1) : (unsigned)nb;
+  const uint16_t* kb0 = k + (int64_t)b * N * krs + (int64_t)g * D;
+  const uint16_t* vb0 = v + (int64_t)b * N * krs + (int64_t)g * D;
+
+  for (int t = 0; t < kcount; ++t) {
+    const int j = myidx[t];
+    if ((unsigned)j >= klim) continue;        // never read out of range (forward gave NaN)
+    __syncthreads();
+    load_tile<D, 128>(Kt, kb0, (int64_t)j * kBlk, krs, tid);
+    load_tile<D, 128>(Vt, vb0, (int64_t)j * kBlk, krs, tid);
+    __syncthreads();
+    f32x16 st[2], dpt[2];                     // S^T and dP^T: rows = 64 keys, cols = queries
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { st[kt][r] = 0.f; dpt[kt][r] = 0.f; }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        st[kt] = mfma(rows_operand<D>(Kt, kt, s, l32, half), qf[s], st[kt]);
+        dpt[kt] = mfma(rows_operand<D>(Vt, kt, s, l32, half), gf[s], dpt[kt]);
+      }
+    }
+    // dS^T = P^T (dP^T - Dvec), P^T = exp2(c s - lse2); masked keys give 0
+    const bool own = CAUSAL && j == i;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][r], c, -l2));
+        if (own && key > qloc) p = 0.f;
+        dpt[kt][r] = p * (dpt[kt][r] - dd);
+      }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int ps = 0; ps < 4; ++ps) {
+      const bf16x8 bds = pack_step(dpt, ps);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma(trans_operand<D>(Kt, dt, ps, lane), bds, acc[dt]);
+    }
+  }
+  // dQ = scale * (dQ^T)^T: lane holds d = 32dt + 8(r/4) + 4*half + r%4 of query qloc
+  float* drow = dq + qrow * qrs + (int64_t)h * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      f32x4 w;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = acc[dt][4 * jj + u] * scale;
+      *(f32x4*)(drow + 32 * dt + 8 * jj + 4 * half) = w;
+    }
+}
+
+// ---------------------------------------------------------------- dK, dV
+// work-group per (b, g, key block j): 2 waves x 32 keys
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(128) void dkv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ dvec,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
+    float* __restrict__ dk, float* __restrict__ dv, int64_t N, int Hq, int Hkv, int nb,
+    int topk, float c, float scale, uint32_t total_tiles) {
+  constexpr int NS = D / 16, NDT = D / 32;
+  __shared__ __attribute__((aligned(16))) char Qt[kBlk * D * 2];
+  __shared__ __attribute__((aligned(16))) char Gt[kBlk * D * 2];   // dO tile
+  __shared__ float l2s[kBlk], dds[kBlk];
+  const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
+  const int j = (int)(tile % nb);
+  const int bg = (int)(tile / nb);
+  const int b = bg / Hkv, g = bg % Hkv, G = Hq / Hkv;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int64_t qrs = (int64_t)Hq * D, krs = (int64_t)Hkv * D;
+  const int kloc = 32 * wave + l32;           // key of this lane's column, in the block
+  const int64_t krow = (int64_t)b * N + (int64_t)j * kBlk + kloc;
+
+  bf16x8 kf[NS], vf[NS];                      // B operands: K^T, V^T (lane = key)
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    kf[s] = row_chunk(k + krow * krs + (int64_t)g * D, s, half);
+    vf[s] = row_chunk(v + krow * krs + (int64_t)g * D, s, half);
+  }
+  f32x16 dka[NDT], dva[NDT];                  // dK^T, dV^T: rows = d, cols = keys
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dka[dt][r] = 0.f; dva[dt][r] = 0.f; }
+
+  const int32_t* off = offsets + (int64_t)bg * (nb + 1);
+  const int32_t* seg = pairs + (int64_t)bg * G * nb * topk;
+  const int p0 = off[j], p1 = off[j + 1];
+  for (int p = p0; p < p1; ++p) {
+    const int row = seg[p];                   // hh * nb + i
+    if ((unsigned)row >= (unsigned)(G * nb)) continue;   // uniform; never read out of range
+    const int hh = row / nb, i = row % nb;
+    const int h = g * G + hh;
+    __syncthreads();
+    load_tile<D, 128>(Qt, q + (int64_t)h * D, (int64_t)b * N + (int64_t)i * kBlk, qrs, tid);
+    load_tile<D, 128>(Gt, dout + (int64_t)h * D, (int64_t)b * N + (int64_t)i * kBlk, qrs, tid);
+    if (tid < kBlk) {
+      const int64_t rid = ((int64_t)b * Hq + h) * N + (int64_t)i * kBlk + tid;
+      l2s[tid] = lse[rid] * kLog2e;
+      dds[tid] = dvec[rid];
+    }
+    __syncthreads();
+    f32x16 sa[2], dpa[2];                     // S and dP: rows = 64 queries, cols = keys
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { sa[qt][r] = 0.f; dpa[qt][r] = 0.f; }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sa[qt] = mfma(rows_operand<D>(Qt, qt, s, l32, half), kf[s], sa[qt]);
+        dpa[qt] = mfma(rows_operand<D>(Gt, qt, s, l32, half), vf[s], dpa[qt]);
+      }
+    }
+    const bool own = CAUSAL && i == j;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qq = 32 * qt + 8 * (r >> 2) + 4 * half + (r & 3);
+        float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[qt][r], c, -l2s[qq]));
+        if (own && kloc > qq) pp = 0.f;
+        sa[qt][r] = pp;                                   // P
+        dpa[qt][r] = pp * (dpa[qt][r] - dds[qq]);         // dS
+      }
+    // dV^T += dO^T P, dK^T += Q^T dS (k-steps over the 64 queries)
+#pragma unroll
+    for (int ps = 0; ps < 4; ++ps) {
+      const bf16x8 bp = pack_step(sa, ps), bs = pack_step(dpa, ps);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        dva[dt] = mfma(trans_operand<D>(Gt, dt, ps, lane), bp, dva[dt]);
+        dka[dt] = mfma(trans_operand<D>(Qt, dt, ps, lane), bs, dka[dt]);
+      }
+    }
+  }
+  float* krow_dk = dk + krow * krs + (int64_t)g * D;
+  float* krow_dv = dv + krow * krs + (int64_t)g * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      f32x4 wk, wv;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wk[u] = dka[dt][4 * jj + u] * scale;
+        wv[u] = dva[dt][4 * jj + u];
+      }
+      *(f32x4*)(krow_dk + 32 * dt + 8 * jj + 4 * half) = wk;
+      *(f32x4*)(krow_dv + 32 * dt + 8 * jj + 4 * half) = wv;
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(int64_t B, int64_t N, int Hq, int Hkv, int topk, const void* q,
+                      const void* k, const void* v, const int32_t* idx, const void* out,
+                      const void* dout, const float* lse, float scale, float* dq, float* dk,
+                      float* dv, float* dvec, int32_t* offsets, int32_t* pairs,
+                      hipStream_t stream) {
+  const int nb = (int)(N / kBlk);
+  const float c = (float)((double)scale * 1.4426950408889634);
+  const int64_t rows = B * N * Hq;
+  rowdot_kernel<D><<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
+      (const uint16_t*)out, (const uint16_t*)dout, dvec, rows, N, Hq);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = (size_t)(2 * nb + 1) * sizeof(int);
+  index_kernel<<<(unsigned)(B * Hkv), kIdxThreads, lds, stream>>>(idx, offsets, pairs, Hq, Hkv,
+                                                                  nb, topk, CAUSAL);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t tq = (uint32_t)(B * Hq * nb);
+  dq_kernel<D, CAUSAL><<<tq, 128, 0, stream>>>(
+      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, idx,
+      lse, dvec, dq, N, Hq, Hkv, nb, topk, c, scale, tq);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t tk = (uint32_t)(B * Hkv * nb);
+  dkv_kernel<D, CAUSAL><<<tk, 128, 0, stream>>>(
+      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse,
+      dvec, offsets, pairs, dk, dv, N, Hq, Hkv, nb, topk, c, scale, tk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_bwd_supported(int dtype_kind, int D, int block) {
+  return dtype_kind == 1 && (D == 64 || D == 128) && block == kBlk;
+}
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int block, int topk) {
+  const int64_t nb = N / block;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return al((size_t)B * Hq * N * sizeof(float)) +                  // Dvec
+         al((size_t)B * Hkv * (nb + 1) * sizeof(int32_t)) +        // offsets
+         al((size_t)B * Hq * nb * topk * sizeof(int32_t));         // pairs
+}
+
+hipError_t launch_attn_bwd(int64_t B, int64_t N, int Hq, int Hkv, int D, int topk, bool causal,
+                           const void* q, const void* k, const void* v, const int32_t* idx,
+                           const void* out, const void* dout, const float* lse, float scale,
+                           float* dq, float* dk, float* dv, void* workspace,
+                           hipStream_t stream) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const int64_t nb = N / kBlk;
+  char* w = (char*)workspace;
+  float* dvec = (float*)w;
+  int32_t* offsets = (int32_t*)(w + al((size_t)B * Hq * N * sizeof(float)));
+  int32_t* pairs = (int32_t*)((char*)offsets + al((size_t)B * Hkv * (nb + 1) * sizeof(int32_t)));
+  if (D == 64)
+    return causal ? launch_bwd<64, true>(B, N, Hq, Hkv, topk, q, k, v, idx, out, dout, lse, scale,
+                                         dq, dk, dv, dvec, offsets, pairs, stream)
+                  : launch_bwd<64, false>(B, N, Hq, Hkv, topk, q, k, v, idx, out, dout, lse, scale,
+                                          dq, dk, dv, dvec, offsets, pairs, stream);
+  return causal ? launch_bwd<128, true>(B, N, Hq, Hkv, topk, q, k, v, idx, out, dout, lse, scale,
+                                        dq, dk, dv, dvec, offsets, pairs, stream)
+                : launch_bwd<128, false>(B, N, Hq, Hkv, topk, q, k, v, idx, out, dout, lse, scale,
+                                         dq, dk, dv, dvec, offsets, pairs, stream);
+}
+
+}  // namespace bsattn

@@ -24,8 +24,8 @@ constexpr int kChunk = 32;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(128) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const int32_t* __restrict__ idx, float* __restrict__ out, int64_t N, int Hq, int Hkv,
-    int nb, int block, int topk, float c, uint32_t total_tiles) {
+    const int32_t* __restrict__ idx, float* __restrict__ out, float* __restrict__ lse,
+    int64_t N, int Hq, int Hkv, int nb, int block, int topk, float c, uint32_t total_tiles) {
   __shared__ __attribute__((aligned(16))) float ks[kChunk][D];
   __shared__ __attribute__((aligned(16))) float vs[kChunk][D];
   const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
@@ -94,6 +94,9 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
     }
   }
   const float inv = bad ? __builtin_nanf("") : 1.0f / l;
+  if (lse)                                     // natural log-sum-exp of the row's scaled scores
+    lse[((int64_t)b * Hq + h) * N + (int64_t)i * block + tid] =
+        bad ? __builtin_nanf("") : (m + log2f(l)) * 0.6931471805599453f;
 #pragma unroll
   for (int d = 0; d < D; ++d) out[row * qrs + (int64_t)h * D + d] = o[d] * inv;
 }
@@ -101,16 +104,16 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
 template <int D>
 hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int block, int topk, const void* q,
                   const void* k, const void* v, const int32_t* idx, float c, void* out,
-                  bool causal, hipStream_t stream) {
+                  float* lse, bool causal, hipStream_t stream) {
   const int nb = (int)(N / block);
   const uint32_t total = (uint32_t)(B * Hq * nb);
   if (causal)
     attn_f32_kernel<D, true><<<total, block, 0, stream>>>((const float*)q, (const float*)k,
-                                                          (const float*)v, idx, (float*)out, N,
+                                                          (const float*)v, idx, (float*)out, lse, N,
                                                           Hq, Hkv, nb, block, topk, c, total);
   else
     attn_f32_kernel<D, false><<<total, block, 0, stream>>>((const float*)q, (const float*)k,
-                                                           (const float*)v, idx, (float*)out, N,
+                                                           (const float*)v, idx, (float*)out, lse, N,
                                                            Hq, Hkv, nb, block, topk, c, total);
   return hipGetLastError();
 }
@@ -123,10 +126,11 @@ bool attn_f32_supported(int D, int block) {
 
 hipError_t launch_attn_f32(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                            const void* q, const void* k, const void* v, const int32_t* idx,
-                           float scale, void* out, bool causal, hipStream_t stream) {
+                           float scale, void* out, float* lse, bool causal,
+                           hipStream_t stream) {
   const float c = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
-  if (D == 64) return launch<64>(B, N, Hq, Hkv, block, topk, q, k, v, idx, c, out, causal, stream);
-  return launch<128>(B, N, Hq, Hkv, block, topk, q, k, v, idx, c, out, causal, stream);
+  if (D == 64) return launch<64>(B, N, Hq, Hkv, block, topk, q, k, v, idx, c, out, lse, causal, stream);
+  return launch<128>(B, N, Hq, Hkv, block, topk, q, k, v, idx, c, out, lse, causal, stream);
 }
 
 }  // namespace bsattn

@@ -81,8 +81,8 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f3
 template <int BLK, bool CAUSAL>
 __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
-    const int32_t* __restrict__ idx, uint16_t* __restrict__ out, int64_t N, int Hq, int Hkv,
-    int nb, int topk, float c, float dv, uint32_t total_tiles) {
+    const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse,
+    int64_t N, int Hq, int Hkv, int nb, int topk, float c, float dv, uint32_t total_tiles) {
   using C = Cfg8<BLK>;
   __shared__ __attribute__((aligned(1024))) char Kl[C::TILE];
   __shared__ __attribute__((aligned(1024))) char Vl[C::TILE];
@@ -289,6 +289,9 @@ __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
 
   const float l_all = lsum + __shfl_xor(lsum, 32);
   const float inv = bad ? __builtin_nanf("") : dv / l_all;
+  if (lse && half == 0)                        // natural log-sum-exp (weights carry 2^kBias)
+    lse[((int64_t)b * Hq + h) * N + (qrow - (int64_t)b * N)] =
+        bad ? __builtin_nanf("") : (m - kBias + log2f(l_all)) * 0.6931471805599453f;
   uint16_t* orow = out + qrow * qrs + (int64_t)h * kD;
 #pragma unroll
   for (int dt = 0; dt < C::NDT; ++dt)
@@ -304,17 +307,17 @@ __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
 
 template <int BLK>
 hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int topk, const void* q, const void* k,
-                  const void* v, const int32_t* idx, float c, float dv, void* out, bool causal,
-                  hipStream_t stream) {
+                  const void* v, const int32_t* idx, float c, float dv, void* out, float* lse,
+                  bool causal, hipStream_t stream) {
   const int nb = (int)(N / BLK);
   const uint32_t total = (uint32_t)(B * Hq * nb);
   if (causal)
     attn_fp8_kernel<BLK, true><<<total, Cfg8<BLK>::NT, 0, stream>>>(
-        (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, (uint16_t*)out, N, Hq,
+        (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, (uint16_t*)out, lse, N, Hq,
         Hkv, nb, topk, c, dv, total);
   else
     attn_fp8_kernel<BLK, false><<<total, Cfg8<BLK>::NT, 0, stream>>>(
-        (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, (uint16_t*)out, N, Hq,
+        (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, (uint16_t*)out, lse, N, Hq,
         Hkv, nb, topk, c, dv, total);
   return hipGetLastError();
 }
@@ -325,14 +328,14 @@ bool attn_fp8_supported(int D, int block) { return D == 128 && (block == 64 || b
 
 hipError_t launch_attn_fp8(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                            const void* q, const void* k, const void* v, const int32_t* idx,
-                           float scale, const float* descale_qkv, void* out, bool causal,
-                           hipStream_t stream) {
+                           float scale, const float* descale_qkv, void* out, float* lse,
+                           bool causal, hipStream_t stream) {
   (void)D;
   const float c = (float)((double)scale * 1.4426950408889634 * (double)descale_qkv[0] *
                           (double)descale_qkv[1]);
   const float dv = descale_qkv[2];
-  if (block == 64) return launch<64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, dv, out, causal, stream);
-  return launch<128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, dv, out, causal, stream);
+  if (block == 64) return launch<64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, dv, out, lse, causal, stream);
+  return launch<128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, dv, out, lse, causal, stream);
 }
 
 }  // namespace bsattn

@@ -41,20 +41,34 @@ hipError_t launch_topk_rows(int64_t rows, int nb, int topk, const float* S, int3
 bool attn_bf16_supported(int D, int block);
 hipError_t launch_attn_bf16(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                             const void* q, const void* k, const void* v, const int32_t* idx,
-                            float scale, void* out, bool causal, hipStream_t stream);
+                            float scale, void* out, float* lse, bool causal,
+                            hipStream_t stream);
 
 // Step 4, fp32 inputs on the fp32 vector ALUs.
 bool attn_f32_supported(int D, int block);
 hipError_t launch_attn_f32(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                            const void* q, const void* k, const void* v, const int32_t* idx,
-                           float scale, void* out, bool causal, hipStream_t stream);
+                           float scale, void* out, float* lse, bool causal,
+                           hipStream_t stream);
 
 // Step 4, OCP fp8 e4m3 inputs on the fp8 MFMA, bf16 output. Supported: D = 128,
 // block in {64, 128}. descale_qkv: host array of the three per-tensor descales.
 bool attn_fp8_supported(int D, int block);
 hipError_t launch_attn_fp8(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                            const void* q, const void* k, const void* v, const int32_t* idx,
-                           float scale, const float* descale_qkv, void* out, bool causal,
+                           float scale, const float* descale_qkv, void* out, float* lse,
+                           bool causal, hipStream_t stream);
+
+// Backward (bf16 inputs, fp32 gradients): supported for block 64, D in {64, 128}.
+// dtype_kind: 0 fp32, 1 bf16, 2 fp8. Workspace: Dvec [B,Hq,N] fp32, key-block offsets
+// [B,Hkv,nb+1], pair lists [B,Hq,nb,topk] int32.
+constexpr int kMaxBwdBlocks = 4096;
+bool attn_bwd_supported(int dtype_kind, int D, int block);
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int block, int topk);
+hipError_t launch_attn_bwd(int64_t B, int64_t N, int Hq, int Hkv, int D, int topk, bool causal,
+                           const void* q, const void* k, const void* v, const int32_t* idx,
+                           const void* out, const void* dout, const float* lse, float scale,
+                           float* dq, float* dk, float* dv, void* workspace,
                            hipStream_t stream);
 
 // Checks every idx row (topk values, strictly ascending, in [0, nb); causal: the first

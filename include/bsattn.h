@@ -75,7 +75,8 @@ typedef enum {
 #define BSATTN_GROUP_SELECT 4u
 
 /* Version of this ABI (BSATTN_ABI_VERSION of the built library). Version 2 added the
- * BSATTN_* option flags and the two _ex entry points; version-1 calls are unchanged. */
+ * BSATTN_* option flags, the two _ex entry points (with the optional log-sum-exp output) and
+ * the backward; version-1 calls are unchanged. */
 int bsattn_abi_version(void);
 
 /* Static English text of a status code; never NULL. */
@@ -159,11 +160,56 @@ int bsattn_forward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int 
  * NaN; keys after the query inside block i are masked). The selection-only bits
  * BSATTN_POOL_MAX and BSATTN_GROUP_SELECT are accepted and have no effect here; other bits:
  * BSATTN_E_INVALID. Under BSATTN_VALIDATE=1 causal rows are checked in that form (unused
- * places must hold -1). Arguments, layouts and errors otherwise as bsattn_forward. */
+ * places must hold -1).
+ *   lse  optional device pointer (NULL: not written), fp32 [B, Hq, N], 4-byte aligned: the
+ *        natural log-sum-exp of every query row's scaled scores over its keys,
+ *        log sum_u exp(scale * q_t . k_u) (for fp8, of the descaled values); NaN for a row
+ *        whose idx entry was out of range. bsattn_backward takes it.
+ * Arguments, layouts and errors otherwise as bsattn_forward. */
 int bsattn_forward_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
                       int topk, unsigned flags, const void* q, const void* k, const void* v,
                       const int32_t* idx, float scale, const float* descale_qkv, void* out,
-                      void* stream);
+                      float* lse, void* stream);
+
+/* Bytes of device workspace bsattn_backward needs (0 for an empty call): Dvec fp32
+ * [B, Hq, N], key-block offsets int32 [B, Hkv, nb + 1], pair lists int32 [B, Hq, nb, topk],
+ * each part 256-byte aligned. Returns 0 and records an error for invalid sizes. */
+size_t bsattn_backward_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
+                                       int topk);
+
+/*
+ * Backward of bsattn_forward(_ex) with the selection held fixed (the top-k choice is piecewise
+ * constant in q and k). SparseFormer page: the method is recommended for training large
+ * models; MSA page §4.1 checks that back-propagation through the sparse attention is complete.
+ * For query block i with keys U (its selected blocks; causal: masked as in the forward),
+ * P = softmax(scale * Q_i K_U^T), O_i = P V_U and the upstream gradient dO_i:
+ *   dV_U += P^T dO_i, dP = dO_i V_U^T, dS = P * (dP - rowsum(dO_i * O_i)),
+ *   dQ_i = scale * dS K_U, dK_U += scale * dS^T Q_i
+ * (GQA: a KV head collects the contributions of all its query heads).
+ * Supported: dtype BSATTN_BF16, D in {64, 128}, block 64, nb <= 4096; other combinations give
+ * BSATTN_E_UNSUPPORTED. Products on bf16 MFMA with fp32 accumulation (P and dS rounded to bf16
+ * as MFMA operands); the key-side sums run in a fixed order, so results are reproducible.
+ * Arguments
+ *   dtype .. topk, flags  as for bsattn_forward_ex (BSATTN_CAUSAL selects the causal variant;
+ *                the other bits have no effect).
+ *   q, k, v, idx, out    the forward's inputs and output (out: bf16 [B, N, Hq, D]); idx rows
+ *                must name distinct blocks (as bsattn_select writes them); an out-of-range
+ *                entry is skipped (never read out of bounds).
+ *   dout         device pointer, bf16 [B, N, Hq, D]: gradient of the loss w.r.t. out.
+ *   lse          device pointer, fp32 [B, Hq, N]: as written by bsattn_forward_ex.
+ *   scale        the forward's scale (finite, > 0).
+ *   dq           device pointer, fp32 [B, N, Hq, D], written entirely.
+ *   dk, dv       device pointers, fp32 [B, N, Hkv, D], written entirely (0 for keys no query
+ *                block selected).
+ *   workspace    device pointer, 256-byte aligned, at least bsattn_backward_workspace_bytes.
+ *   stream       hipStream_t.
+ * Tensors 16-byte aligned; idx and lse 4-byte aligned.
+ */
+int bsattn_backward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
+                    unsigned flags, const void* q, const void* k, const void* v,
+                    const int32_t* idx, const void* out, const void* dout, const float* lse,
+                    float scale, float* dq, float* dk, float* dv, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -89,6 +89,24 @@ def check_idx_causal(gpu_idx: np.ndarray, S: np.ndarray, k: int):
             check_idx(np.ascontiguousarray(rows[..., :ki - 1]), S[..., i, :i], ki - 1)
 
 
+GRAD_REL_L2 = 1e-2
+GRAD_MAX_REL = 2e-2
+
+
+def check_grad(gpu: np.ndarray, ref: np.ndarray, name: str = ""):
+    """Gradient rule (bf16 backward): relative L2 <= 1e-2 and max-abs <= 2e-2 of max |ref|.
+    Derived from the arithmetic: the inputs are the same bf16 values on both sides; the GPU
+    rounds P and dS to bf16 (relative error <= 2^-9 each) as MFMA operands and sums in fp32,
+    and its rowsum(dO * O) uses the bf16-rounded forward output, so each gradient entry, a sum
+    of such products, carries a relative error of a few 2^-9 at most (rms well below 1e-2)."""
+    assert not np.isnan(gpu).any(), f"{name}: NaN"
+    diff = gpu.astype(np.float64) - ref
+    rel = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300))
+    mx = float(np.max(np.abs(diff))) / max(float(np.max(np.abs(ref))), 1e-300)
+    assert rel <= GRAD_REL_L2 and mx <= GRAD_MAX_REL, (name, rel, mx)
+    return rel, mx
+
+
 def out_errors(gpu_out: np.ndarray, ref: np.ndarray):
     diff = gpu_out.astype(np.float64) - ref
     max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0

@@ -110,11 +110,47 @@ def test_extended_entry_points_reject():
     assert sel_ex(1, q=None) == 1 and "null" in last()           # checks as bsattn_select
     L = bst.lib()
     st = L.bsattn_forward_ex(1, 1, 512, 2, 2, 64, 64, 2, 16, FAKE, FAKE, FAKE, FAKE, 0.125, None,
-                             FAKE, None)
+                             FAKE, None, None)
     assert st == 1 and "flags" in last()
     st = L.bsattn_forward_ex(1, 1, 512, 2, 2, 64, 64, 2, 1, FAKE, FAKE, FAKE, FAKE,
-                             float("inf"), None, FAKE, None)
+                             float("inf"), None, FAKE, None, None)
     assert st == 1 and "scale" in last()
+    st = L.bsattn_forward_ex(1, 1, 512, 2, 2, 64, 64, 2, 0, FAKE, FAKE, FAKE, FAKE, 0.125, None,
+                             FAKE, ctypes.c_void_p(0x10002), None)
+    assert st == 1 and "lse" in last()
+
+
+def bwd(**kw):
+    a = dict(dtype=1, B=1, N=512, Hq=2, Hkv=2, D=64, block=64, topk=2, flags=0, t=FAKE,
+             scale=0.125, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    t = a["t"]
+    return bst.lib().bsattn_backward(a["dtype"], a["B"], a["N"], a["Hq"], a["Hkv"], a["D"],
+                                     a["block"], a["topk"], a["flags"], t, t, t, t, t, t, t,
+                                     a["scale"], t, t, t, a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dtype=0), 2, "backward"),
+    (dict(dtype=2, D=128), 2, "backward"),
+    (dict(block=128, N=1024), 2, "block=128"),
+    (dict(N=64 * 5000, topk=3), 2, "nb=5000"),
+    (dict(flags=8), 1, "flags"),
+    (dict(scale=0.0), 1, "scale"),
+    (dict(t=None), 1, "null"),
+    (dict(ws=None), 3, "workspace"),
+    (dict(wsb=8), 3, "workspace"),
+])
+def test_backward_rejects(kw, status, msg):
+    assert bwd(**kw) == status
+    assert msg in last()
+
+
+def test_backward_workspace_bytes():
+    L = bst.lib()
+    n = L.bsattn_backward_workspace_bytes(2, 8192, 16, 4, 64, 64, 38)
+    al = lambda x: (x + 255) // 256 * 256
+    assert n == al(2 * 16 * 8192 * 4) + al(2 * 4 * 129 * 4) + al(2 * 16 * 128 * 38 * 4)
 
 
 def test_empty_calls_launch_nothing():
