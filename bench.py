@@ -39,6 +39,8 @@ def parse():
                    help="causal variant (own block forced, earlier blocks only, masked own block)")
     p.add_argument("--pooling", choices=("mean", "max"), default="mean")
     p.add_argument("--group", action="store_true", help="one selection per KV head group")
+    p.add_argument("--backward", action="store_true",
+                   help="also time bsattn_backward (bf16, block 64) on the same selection")
     return p.parse_args()
 
 
@@ -101,6 +103,46 @@ def cpu_baseline(w, q, k, v, ds, max_batches, budget_s=10.0, causal=False, pooli
             "kind": "oracle",
             "sample": f"{batches} of {w.B} batch elements (all heads, all query blocks), "
                       f"whole path in fp64 numpy, {dt_s:.1f} s"}
+
+
+def time_backward(args, w, q, k, v, idx, out, topk, scale, flags, L, P, sp, stream, fwd_flops):
+    """HIP-event time of one bsattn_backward call (after a forward that writes the row
+    log-sum-exp). Algorithmic flops: the five products S, dP, dV, dK, dQ = 2.5 x forward."""
+    import torch
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=q.device)
+    dcode = 1
+    st = L.bsattn_forward_ex(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, P(q), P(k),
+                             P(v), P(idx), scale, None, P(out), P(lse), sp)
+    assert st == 0, L.bsattn_last_error()
+    g = torch.Generator(device=q.device).manual_seed(7)
+    dout = torch.randn(out.shape, generator=g, device=q.device).to(torch.bfloat16)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    nbytes = L.bsattn_backward_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+
+    def call():
+        st = L.bsattn_backward(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, P(q),
+                               P(k), P(v), P(idx), P(out), P(dout), P(lse), scale, P(dq), P(dk),
+                               P(dv), P(ws), ws.numel(), sp)
+        assert st == 0, L.bsattn_last_error()
+
+    for _ in range(max(1, args.warmup // 2)):
+        call()
+    torch.cuda.synchronize()
+    n = max(1, args.steps // 2)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    bflops = 2.5 * fwd_flops
+    return {"ms": round(ms, 4), "algorithmic_flop": bflops,
+            "tflops": round(bflops / ms / 1e9, 2),
+            "frac_bf16_peak": round(bflops / ms / 1e9 / PEAK["bf16"], 4)}
 
 
 def main():
@@ -201,6 +243,9 @@ def main():
         "select_hbm_frac": round(sel_bytes / (sel_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "select_algorithmic_bytes": sel_bytes,
     }
+    if args.backward:
+        rec["backward"] = time_backward(args, w, q, k, v, idx, out, topk, scale, flags, L, P, sp,
+                                        stream, flops)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, ds, args.cpu_batches or w.B,
                                            causal=args.causal, pooling=args.pooling,

@@ -53,20 +53,33 @@ __device__ __forceinline__ s16x4 ds_read_tr16(const char* lds_bytes) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_void*)(lds_bytes));
 }
 
-// Copy rows [row0, row0 + 64) of a [*, H, D] bf16 tensor (head h) into an LDS tile [64][D],
-// swizzled; all threads of the work-group take part.
+// Rows [row0, row0 + 64) of a [*, H, D] bf16 tensor (head offset folded into `base`) as an
+// LDS tile [64][D], swizzled; all NT threads of the work-group take part. The copy is split
+// into a load into registers (issued one step ahead, in flight during the products) and a
+// store into LDS.
 template <int D, int NT>
-__device__ __forceinline__ void load_tile(char* tile, const uint16_t* base, int64_t row0,
-                                          int64_t rstride, int tid) {
-  constexpr int CH = D / 8;                   // 16-byte chunks per row
+struct TileRegs {
+  static constexpr int CH = D / 8;            // 16-byte chunks per row
+  static constexpr int X = kBlk * CH / NT;    // chunks per thread
+  u32x4 w[X];
+  __device__ __forceinline__ void load(const uint16_t* base, int64_t row0, int64_t rstride,
+                                       int tid) {
 #pragma unroll
-  for (int x = 0; x < kBlk * CH / NT; ++x) {
-    const int pos = x * NT + tid;
-    const int r = pos / CH, c = pos % CH;
-    const u32x4 w = *(const u32x4*)(base + (row0 + r) * rstride + 8 * c);
-    *(u32x4*)(tile + r * D * 2 + 16 * swz(r, c)) = w;
+    for (int x = 0; x < X; ++x) {
+      const int pos = x * NT + tid;
+      const int r = pos / CH, c = pos % CH;
+      w[x] = *(const u32x4*)(base + (row0 + r) * rstride + 8 * c);
+    }
   }
-}
+  __device__ __forceinline__ void store(char* tile, int tid) const {
+#pragma unroll
+    for (int x = 0; x < X; ++x) {
+      const int pos = x * NT + tid;
+      const int r = pos / CH, c = pos % CH;
+      *(u32x4*)(tile + r * D * 2 + 16 * swz(r, c)) = w[x];
+    }
+  }
+};
 
 // A operand (32 rows x 16 d) of a row-major tile: rows 32*t + l32, d = 16s + 8*half .. +7
 template <int D>
@@ -246,13 +259,28 @@ __global__ __launch_bounds__(128) void dq_kernel(
   const uint16_t* kb0 = k + (int64_t)b * N * krs + (int64_t)g * D;
   const uint16_t* vb0 = v + (int64_t)b * N * krs + (int64_t)g * D;
 
+  // an out-of-range entry is never read (the forward gave its rows NaN): block 0 stands in
+  // and the step is skipped
+  TileRegs<D, 128> kr, vr;
+  int jn = myidx[0];
+  {
+    const int64_t r0 = (unsigned)jn < klim ? (int64_t)jn * kBlk : 0;
+    kr.load(kb0, r0, krs, tid);
+    vr.load(vb0, r0, krs, tid);
+  }
   for (int t = 0; t < kcount; ++t) {
-    const int j = myidx[t];
-    if ((unsigned)j >= klim) continue;        // never read out of range (forward gave NaN)
+    const int j = jn;
+    __syncthreads();                          // the previous step is done with the tiles
+    kr.store(Kt, tid);
+    vr.store(Vt, tid);
     __syncthreads();
-    load_tile<D, 128>(Kt, kb0, (int64_t)j * kBlk, krs, tid);
-    load_tile<D, 128>(Vt, vb0, (int64_t)j * kBlk, krs, tid);
-    __syncthreads();
+    if (t + 1 < kcount) {                     // next tiles fly during this step's products
+      jn = myidx[t + 1];
+      const int64_t r0 = (unsigned)jn < klim ? (int64_t)jn * kBlk : 0;
+      kr.load(kb0, r0, krs, tid);
+      vr.load(vb0, r0, krs, tid);
+    }
+    if ((unsigned)j >= klim) continue;        // uniform
     f32x16 st[2], dpt[2];                     // S^T and dP^T: rows = 64 keys, cols = queries
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -335,20 +363,34 @@ __global__ __launch_bounds__(128) void dkv_kernel(
   const int32_t* off = offsets + (int64_t)bg * (nb + 1);
   const int32_t* seg = pairs + (int64_t)bg * G * nb * topk;
   const int p0 = off[j], p1 = off[j + 1];
-  for (int p = p0; p < p1; ++p) {
-    const int row = seg[p];                   // hh * nb + i
-    if ((unsigned)row >= (unsigned)(G * nb)) continue;   // uniform; never read out of range
-    const int hh = row / nb, i = row % nb;
-    const int h = g * G + hh;
-    __syncthreads();
-    load_tile<D, 128>(Qt, q + (int64_t)h * D, (int64_t)b * N + (int64_t)i * kBlk, qrs, tid);
-    load_tile<D, 128>(Gt, dout + (int64_t)h * D, (int64_t)b * N + (int64_t)i * kBlk, qrs, tid);
+  // tiles of pair p + 1 are loaded into registers while pair p is multiplied; a pair value out
+  // of range (only possible for idx rows with repeated blocks) is skipped, pair 0 standing in
+  TileRegs<D, 128> qr, gr;
+  float l2n = 0.f, ddn = 0.f;
+  auto fetch = [&](int p) {
+    int row = seg[p];
+    if ((unsigned)row >= (unsigned)(G * nb)) row = 0;
+    const int h = g * G + row / nb, i = row % nb;
+    const int64_t r0 = (int64_t)b * N + (int64_t)i * kBlk;
+    qr.load(q + (int64_t)h * D, r0, qrs, tid);
+    gr.load(dout + (int64_t)h * D, r0, qrs, tid);
     if (tid < kBlk) {
       const int64_t rid = ((int64_t)b * Hq + h) * N + (int64_t)i * kBlk + tid;
-      l2s[tid] = lse[rid] * kLog2e;
-      dds[tid] = dvec[rid];
+      l2n = lse[rid] * kLog2e;
+      ddn = dvec[rid];
     }
+  };
+  if (p0 < p1) fetch(p0);
+  for (int p = p0; p < p1; ++p) {
+    const int row = seg[p];                   // hh * nb + i
+    __syncthreads();                          // the previous pair is done with the tiles
+    qr.store(Qt, tid);
+    gr.store(Gt, tid);
+    if (tid < kBlk) { l2s[tid] = l2n; dds[tid] = ddn; }
     __syncthreads();
+    if (p + 1 < p1) fetch(p + 1);
+    if ((unsigned)row >= (unsigned)(G * nb)) continue;   // uniform
+    const int i = row % nb;
     f32x16 sa[2], dpa[2];                     // S and dP: rows = 64 queries, cols = keys
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
