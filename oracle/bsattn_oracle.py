@@ -43,6 +43,12 @@ the design notes of the repository):
   R22 group-shared selection (GQA, MSA §3.1): one selection per KV head from the sum of
       the block scores of its query heads (equivalently, from the summed pooled queries);
       every query head of the group uses it.
+  R26 decode (NEXT N4; the pages' KV cache and first-token latency remarks): one new query
+      token per sequence against a cache of L tokens, the query at position L-1. Its own block
+      (L-1) // b, complete or not, is always used; the other min(k, own+1) - 1 places go to
+      the complete blocks j < own with the largest q . kbar_j (kbar: mean of the block's keys,
+      kept up to date as blocks complete; ties to the lower j); attention over those blocks
+      and the own block's cached tokens (all at positions <= L-1).
   R25 backward (the MSA page's §4.1 checks that back-propagation is complete; the
       SparseFormer page recommends the method for training large models, "千亿参数大模型训练"):
       gradients of the gathered-block attention with the selection held fixed (top-k is
@@ -397,6 +403,43 @@ def attend_backward(q, k, v, idx, block, scale, dout, causal: bool = False):
                 np.add.at(dk[b, :, g, :], tok, scale * (dS.T @ Qi))
                 np.add.at(dv[b, :, g, :], tok, P.T @ dOi)
     return dq, dk, dv
+
+
+def decode_select(q_tok, kbar, lens, block: int, topk: int) -> np.ndarray:
+    """Blocks for one decode step [R26]. q_tok [B, Hq, D]; kbar [B, Hkv, nb, D] (rows of
+    complete blocks are read); lens [B] (1 <= lens[b]). Returns int64 [B, Hq, topk]:
+    ascending, own block last, -1 in unused places."""
+    B, Hq, D = q_tok.shape
+    Hkv = kbar.shape[1]
+    out = np.full((B, Hq, topk), -1, dtype=np.int64)
+    for b in range(B):
+        own = (int(lens[b]) - 1) // block
+        kb = min(topk, own + 1)
+        for h in range(Hq):
+            if kb > 1:
+                s = kbar[b, kv_head(h, Hq, Hkv), :own] @ q_tok[b, h]       # [own]
+                out[b, h, :kb - 1] = select_topk(s[None], kb - 1)[0]
+            out[b, h, kb - 1] = own
+    return out
+
+
+def decode_attend(q_tok, k_cache, v_cache, idx, lens, block: int, scale: float) -> np.ndarray:
+    """Attention of each sequence's newest token over its decode blocks [R26]: keys of the
+    selected blocks (-1 unused), the own block only up to position lens[b] - 1.
+    q_tok [B, Hq, D], caches [B, Lmax, Hkv, D] -> out [B, Hq, D]."""
+    B, Hq, D = q_tok.shape
+    Hkv = k_cache.shape[2]
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(lens[b])
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            tok = np.concatenate([np.arange(j * block, min((j + 1) * block, L))
+                                  for j in idx[b, h] if j >= 0])
+            z = scale * (k_cache[b, tok, g] @ q_tok[b, h])
+            p = np.exp(z - z.max())
+            out[b, h] = (p @ v_cache[b, tok, g]) / p.sum()
+    return out
 
 
 def select(q, k, block: int, topk: int, causal: bool = False, pooling: str = "mean",

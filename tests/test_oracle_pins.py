@@ -392,12 +392,56 @@ def check_lse(o=O):
                 assert abs(got[0, h, t] - logsumexp(z[t][keep])) <= 1e-12
 
 
+def check_decode(o=O):
+    """Decode step [R26]: selection against a full sort over the complete earlier blocks plus
+    the own block; with topk covering every block the step is causal dense attention of the
+    last token (library SDPA on the prefix); gathered keys equal an explicit mask over the
+    cache; a zero query with ties takes the lowest blocks."""
+    B, Lmax, Hq, Hkv, D, blk = 3, 256, 4, 2, 16, 32
+    r = rng(23)
+    qt = r.standard_normal((B, Hq, D))
+    kc, vc = r.standard_normal((2, B, Lmax, Hkv, D))
+    lens = np.array([256, 97, 33])
+    kbar = o.pool(kc, blk)                                       # complete-block means
+    for topk in (1, 3, 8):
+        idx = o.decode_select(qt, kbar, lens, blk, topk)
+        for b in range(B):
+            own = (lens[b] - 1) // blk
+            kb = min(topk, own + 1)
+            for h in range(Hq):
+                s = kbar[b, h // 2, :own] @ qt[b, h]
+                past = np.lexsort((np.arange(own), -s))[:kb - 1]
+                assert idx[b, h].tolist() == sorted(past.tolist() + [own]) + [-1] * (topk - kb)
+        got = o.decode_attend(qt, kc, vc, idx, lens, blk, 0.25)
+        for b in range(B):
+            L = lens[b]
+            tb = np.arange(L) // blk
+            for h in range(Hq):
+                keep = np.isin(tb, idx[b, h])
+                z = 0.25 * (kc[b, :L, h // 2] @ qt[b, h])
+                z = np.where(keep, z, -np.inf)
+                p = np.exp(z - z.max())
+                assert np.allclose(got[b, h], p @ vc[b, :L, h // 2] / p.sum(), rtol=0, atol=1e-13)
+    idx = o.decode_select(qt, kbar, lens, blk, 8)                # covers every block
+    got = o.decode_attend(qt, kc, vc, idx, lens, blk, 0.25)
+    for b in range(B):
+        L = lens[b]
+        for h in range(Hq):
+            tq = torch.from_numpy(qt[b, h])[None, None, None]    # [1, 1, 1, D]
+            tk = torch.from_numpy(kc[b, :L, h // 2])[None, None]
+            tv = torch.from_numpy(vc[b, :L, h // 2])[None, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=0.25)
+            assert np.allclose(got[b, h], ref[0, 0, 0].numpy(), rtol=0, atol=1e-12)
+    z = o.decode_select(np.zeros_like(qt), kbar, lens, blk, 3)
+    assert z[0, 0].tolist() == [0, 1, 7] and z[2, 0].tolist() == [0, 1, -1]
+
+
 ALL_CHECKS = [check_bf16_widen, check_e4m3, check_pool, check_scores, check_select_vs_sort,
               check_select_special, check_dense_limit, check_bruteforce, check_ties_and_zero,
               check_invariants, check_gqa, check_batched, check_causal_select,
               check_causal_dense_limit, check_causal_bruteforce, check_pool_max,
               check_group_select, check_backward_autograd, check_backward_fd_and_invariants,
-              check_lse]
+              check_lse, check_decode]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -482,6 +526,19 @@ def _backward_no_rowterm(q, k, v, idx, blk, scale, dout, causal=False):
     return dq, dk, dv
 
 
+def _decode_unforced(q_tok, kbar, lens, blk, topk):
+    """decode_select choosing among blocks j <= own by score only: a planted mistake."""
+    B, Hq, D = q_tok.shape
+    out = np.full((B, Hq, topk), -1, dtype=np.int64)
+    for b in range(B):
+        own = (int(lens[b]) - 1) // blk
+        kb = min(topk, own + 1)
+        for h in range(Hq):
+            s = kbar[b, h * kbar.shape[1] // Hq, :own + 1] @ q_tok[b, h]
+            out[b, h, :kb] = O.select_topk(s[None], kb)[0]
+    return out
+
+
 class Mutant:
     """The oracle module with one function replaced by a wrong version."""
 
@@ -509,7 +566,8 @@ def _rebind(fn, mutant):
 def _mutant(**repl):
     m = Mutant(**repl)
     for name in ("select", "block_sparse_attention", "block_scores", "attend", "attend_batched",
-                 "dense_attention", "masked_attention_bruteforce", "select_topk_causal"):
+                 "dense_attention", "masked_attention_bruteforce", "select_topk_causal",
+                 "decode_select", "decode_attend"):
         if name not in repl:
             setattr(m, name, _rebind(getattr(O, name), m))
     return m
@@ -546,6 +604,8 @@ MUTANTS = {
     "backward_dk_unscaled": dict(
         attend_backward=lambda q, k, v, idx, blk, scale, dout, causal=False:
         (lambda g: (g[0], g[1] / scale, g[2]))(O.attend_backward(q, k, v, idx, blk, scale, dout, causal))),
+    "decode_own_block_not_forced": dict(
+        decode_select=lambda q, kb, lens, blk, topk: _decode_unforced(q, kb, lens, blk, topk)),
     "lse_log2": dict(attend_lse=lambda q, k, idx, blk, scale, causal=False:
                      O.attend_lse(q, k, idx, blk, scale, causal) / np.log(2.0)),
     "group_first_head_only": dict(
