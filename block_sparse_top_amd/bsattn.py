@@ -71,6 +71,13 @@ def lib() -> ctypes.CDLL:
     L.bsattn_backward.restype = i32
     L.bsattn_backward.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, u32, vp, vp, vp, vp, vp,
                                   vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+    L.bsattn_decode_pool.restype = i32
+    L.bsattn_decode_pool.argtypes = [i32, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.bsattn_decode_workspace_bytes.restype = sz
+    L.bsattn_decode_workspace_bytes.argtypes = [i64, i32, i32, i32]
+    L.bsattn_decode.restype = i32
+    L.bsattn_decode.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                ctypes.c_float, vp, vp, vp, sz, vp]
     _lib = L
     return L
 
@@ -227,3 +234,36 @@ def block_sparse_attention(q, k, v, block_size: int = 64, topk_ratio: float = 0.
     idx = select(q, k, block_size, topk, causal=causal, pooling=pooling, group=group)
     out = forward(q, k, v, idx, 1.0 / math.sqrt(D), descales, causal=causal)
     return (out, idx) if return_idx else out
+
+
+def decode_pool(k_cache, lens_new, kbar, block: int, lens_old=None):
+    """Pools the key blocks completed between lens_old and lens_new (all complete blocks if
+    lens_old is None) into kbar, fp32 [B, Hkv, Lmax // block, D], in place."""
+    B, Lmax, Hkv, D = k_cache.shape
+    with torch.cuda.device(k_cache.device):
+        _check(lib().bsattn_decode_pool(_DTYPES[k_cache.dtype], B, Lmax, Hkv, D, block,
+                                        _ptr(k_cache), _ptr(lens_old), _ptr(lens_new),
+                                        _ptr(kbar), _stream(k_cache.device)))
+    return kbar
+
+
+def decode(q, k_cache, v_cache, kbar, lens, block: int, topk: int, scale: float | None = None,
+           workspace=None):
+    """One decode step: q bf16 [B, Hq, D] (the newest token of each sequence), caches bf16
+    [B, Lmax, Hkv, D], kbar from `decode_pool`, lens int32 [B] on the device.
+    Returns (out bf16 [B, Hq, D], idx int32 [B, Hq, topk])."""
+    B, Hq, D = q.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    idx = torch.empty((B, Hq, topk), dtype=torch.int32, device=q.device)
+    L = lib()
+    if workspace is None:
+        n = int(L.bsattn_decode_workspace_bytes(B, Hq, D, max(topk, 1))) if B else 0
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(L.bsattn_decode(_DTYPES[q.dtype], B, Lmax, Hq, Hkv, D, block, topk, _ptr(q),
+                               _ptr(k_cache), _ptr(v_cache), _ptr(kbar), _ptr(lens), scale,
+                               _ptr(out), _ptr(idx), _ptr(workspace), workspace.numel(),
+                               _stream(q.device)))
+    return out, idx

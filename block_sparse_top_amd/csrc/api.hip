@@ -276,4 +276,78 @@ int bsattn_backward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int
                     "backward launch");
 }
 
+namespace {
+
+// sizes shared by the decode entry points
+int check_decode(int dtype, int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int block) {
+  if (dtype != BSATTN_F32 && dtype != BSATTN_BF16 && dtype != BSATTN_FP8_E4M3)
+    return fail(BSATTN_E_INVALID, "unknown dtype %d", dtype);
+  if (B < 0 || Lmax < 0) return fail(BSATTN_E_INVALID, "negative B or Lmax");
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv)
+    return fail(BSATTN_E_INVALID, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  if (block < 1 || Lmax % block)
+    return fail(BSATTN_E_INVALID, "Lmax (%lld) must be a multiple of block (%d)",
+                (long long)Lmax, block);
+  if (dtype != BSATTN_BF16) return fail(BSATTN_E_UNSUPPORTED, "decode for dtype %d (bf16 only)", dtype);
+  if (!bsattn::decode_supported(D, block))
+    return fail(BSATTN_E_UNSUPPORTED, "decode for D=%d block=%d", D, block);
+  if (Lmax / block > bsattn::kMaxDecodeBlocks)
+    return fail(BSATTN_E_UNSUPPORTED, "decode over %lld > %d blocks", (long long)(Lmax / block),
+                bsattn::kMaxDecodeBlocks);
+  if (B > 65535) return fail(BSATTN_E_UNSUPPORTED, "decode batch B=%lld > 65535", (long long)B);
+  if (B * (int64_t)Hq * 64 >= ((int64_t)1 << 31)) return fail(BSATTN_E_UNSUPPORTED, "B*Hq too large");
+  return BSATTN_OK;
+}
+
+}  // namespace
+
+size_t bsattn_decode_workspace_bytes(int64_t B, int Hq, int D, int topk) {
+  if (B < 0 || Hq < 1 || D < 1 || topk < 1) {
+    fail(BSATTN_E_INVALID, "invalid sizes for the workspace query");
+    return 0;
+  }
+  if (B == 0) return 0;
+  return bsattn::decode_workspace_bytes(B, Hq, D, topk);
+}
+
+int bsattn_decode_pool(int dtype, int64_t B, int64_t Lmax, int Hkv, int D, int block,
+                       const void* k_cache, const int32_t* lens_old, const int32_t* lens_new,
+                       float* kbar, void* stream) {
+  int st = check_decode(dtype, B, Lmax, Hkv, Hkv, D, block);
+  if (st != BSATTN_OK) return st;
+  if (B == 0 || Lmax == 0) return BSATTN_OK;
+  if (!k_cache || !lens_new || !kbar) return fail(BSATTN_E_INVALID, "null pointer argument");
+  if (!aligned16(k_cache) || !aligned16(kbar) || ((uintptr_t)lens_new & 3u) ||
+      ((uintptr_t)lens_old & 3u))
+    return fail(BSATTN_E_INVALID, "k_cache and kbar must be 16-byte aligned, lens 4-byte aligned");
+  return hip_status(bsattn::launch_decode_pool(B, Lmax, Hkv, D, block, k_cache, lens_old,
+                                               lens_new, kbar, (hipStream_t)stream),
+                    "decode pool launch");
+}
+
+int bsattn_decode(int dtype, int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int block, int topk,
+                  const void* q, const void* k_cache, const void* v_cache, const float* kbar,
+                  const int32_t* lens, float scale, void* out, int32_t* idx, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int st = check_decode(dtype, B, Lmax, Hq, Hkv, D, block);
+  if (st != BSATTN_OK) return st;
+  if (topk < 1) return fail(BSATTN_E_INVALID, "topk %d must be >= 1", topk);
+  if (!isfinite(scale) || !(scale > 0.f))
+    return fail(BSATTN_E_INVALID, "scale must be finite and > 0");
+  if (B == 0 || Lmax == 0) return BSATTN_OK;
+  if (!q || !k_cache || !v_cache || !kbar || !lens || !out || !idx)
+    return fail(BSATTN_E_INVALID, "null pointer argument");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kbar) ||
+      !aligned16(out) || ((uintptr_t)lens & 3u) || ((uintptr_t)idx & 3u))
+    return fail(BSATTN_E_INVALID, "tensors must be 16-byte aligned, lens and idx 4-byte aligned");
+  const size_t need = bsattn::decode_workspace_bytes(B, Hq, D, topk);
+  if (!workspace || workspace_bytes < need)
+    return fail(BSATTN_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if ((uintptr_t)workspace & 255u) return fail(BSATTN_E_WORKSPACE, "workspace not 256-byte aligned");
+  return hip_status(bsattn::launch_decode(B, Lmax, Hq, Hkv, D, block, topk, q, k_cache, v_cache,
+                                          kbar, lens, scale, out, idx, workspace,
+                                          (hipStream_t)stream),
+                    "decode launch");
+}
+
 }  // extern "C"

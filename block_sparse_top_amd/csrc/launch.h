@@ -71,6 +71,19 @@ hipError_t launch_attn_bwd(int64_t B, int64_t N, int Hq, int Hkv, int D, int top
                            float* dq, float* dk, float* dv, void* workspace,
                            hipStream_t stream);
 
+// Decode step (bf16 caches; D in {64, 128}, block in {64, 128}, Lmax / block <= 8192).
+int decode_splits(int64_t B, int Hq, int topk);
+size_t decode_workspace_bytes(int64_t B, int Hq, int D, int topk);
+bool decode_supported(int D, int block);
+constexpr int kMaxDecodeBlocks = 8192;
+hipError_t launch_decode_pool(int64_t B, int64_t Lmax, int Hkv, int D, int block,
+                              const void* k_cache, const int32_t* lens_old,
+                              const int32_t* lens_new, float* kbar, hipStream_t stream);
+hipError_t launch_decode(int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int block, int topk,
+                         const void* q, const void* k_cache, const void* v_cache,
+                         const float* kbar, const int32_t* lens, float scale, void* out,
+                         int32_t* idx, void* workspace, hipStream_t stream);
+
 // Checks every idx row (topk values, strictly ascending, in [0, nb); causal: the first
 // min(topk, i+1) values strictly ascending in [0, i] for query block i, the rest -1); waits
 // for the stream and returns the number of failing rows in *bad_rows. Uses one device-global

@@ -211,6 +211,43 @@ int bsattn_backward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int
                     float scale, float* dq, float* dk, float* dv, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/*
+ * Decode (one new query token per sequence against a KV cache).
+ * Caches: k_cache, v_cache bf16 [B, Lmax, Hkv, D] (token t of sequence b at row t), pooled
+ * keys kbar fp32 [B, Hkv, Lmax / block, D] (row j = mean of the keys of block j once that
+ * block is complete), lens int32 [B] on the device: tokens cached per sequence
+ * (1 <= lens[b] <= Lmax; the query is token lens[b] - 1, its K and V already in the cache).
+ * SparseFormer page, "SparseFormer 注意力实现" (pooled key blocks, top-k blocks, attention over
+ * them with scale 1/sqrt(D)); MSA page §5.2 (first-token latency of the block scoring).
+ * Supported: dtype BSATTN_BF16, D in {64, 128}, block in {64, 128}, Lmax / block <= 8192,
+ * B <= 65535; else BSATTN_E_UNSUPPORTED. Asynchronous on `stream`, no allocation.
+ */
+
+/* Pools the blocks completed between two lengths: for every sequence b, the blocks
+ * j with lens_old[b] / block <= j < lens_new[b] / block get kbar rows (fp32 means of their
+ * keys, all KV heads). lens_old may be NULL (then every complete block is pooled). Sequences
+ * with an invalid length pair are skipped. k_cache, kbar 16-byte aligned. */
+int bsattn_decode_pool(int dtype, int64_t B, int64_t Lmax, int Hkv, int D, int block,
+                       const void* k_cache, const int32_t* lens_old, const int32_t* lens_new,
+                       float* kbar, void* stream);
+
+/* Bytes of device workspace bsattn_decode needs (per-split partial results, fp32). */
+size_t bsattn_decode_workspace_bytes(int64_t B, int Hq, int D, int topk);
+
+/* One decode step for every sequence and query head h (KV head h / (Hq / Hkv)):
+ *   own = (lens[b] - 1) / block is always used; the other min(topk, own + 1) - 1 places go to
+ *   the complete blocks j < own with the largest sum_d q[b,h,d] * kbar[b,g,j,d] (fp32;
+ *   ties to the lower j); idx[b,h,:] receives them ascending (own last), then -1.
+ *   out[b,h,:] = softmax over the keys of those blocks (own block: positions < lens[b]) of
+ *   scale * q . k, times v; bf16 [B, Hq, D]; fp32 scores and sums.
+ * q bf16 [B, Hq, D]; idx int32 [B, Hq, topk] written; workspace at least
+ * bsattn_decode_workspace_bytes, 256-byte aligned. A sequence with lens[b] outside
+ * [1, Lmax] gets idx -1 and NaN output. */
+int bsattn_decode(int dtype, int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int block, int topk,
+                  const void* q, const void* k_cache, const void* v_cache, const float* kbar,
+                  const int32_t* lens, float scale, void* out, int32_t* idx, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
