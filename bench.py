@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--group", action="store_true", help="one selection per KV head group")
     p.add_argument("--backward", action="store_true",
                    help="also time bsattn_backward (bf16, block 64) on the same selection")
+    p.add_argument("--decode", action="store_true",
+                   help="time the decode step instead (workload decode_gqa_l32768)")
     return p.parse_args()
 
 
@@ -145,12 +147,80 @@ def time_backward(args, w, q, k, v, idx, out, topk, scale, flags, L, P, sp, stre
             "frac_bf16_peak": round(bflops / ms / 1e9 / PEAK["bf16"], 4)}
 
 
+def bench_decode(args):
+    """One step = bsattn_decode for every sequence of the batch (one new token each) against
+    a full cache; the pooled-key cache is built once beforehand (untimed). Prints one line."""
+    import ctypes
+    import torch
+    import block_sparse_top_amd as bst
+    from block_sparse_top_amd import synthetic as syn
+    w = syn.DECODE_WORKLOADS["decode_gqa_l32768"]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    q, kc, vc = syn.decode_inputs(w, device=dev)
+    topk = int(w.ratio * w.nb)
+    lens = torch.full((w.B,), w.N, dtype=torch.int32, device=dev)
+    kbar = torch.empty((w.B, w.Hkv, w.D, w.nb), dtype=torch.float32, device=dev)
+    bst.decode_pool(kc, lens, kbar, w.block)
+    L = bst.lib()
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((w.B, w.Hq, topk), dtype=torch.int32, device=dev)
+    ws = torch.empty(L.bsattn_decode_workspace_bytes(w.B, w.Hq, w.D, topk), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    scale = 1.0 / math.sqrt(w.D)
+
+    def step():
+        st = L.bsattn_decode(1, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, P(q), P(kc), P(vc),
+                             P(kbar), P(lens), scale, P(out), P(idx), P(ws), ws.numel(), sp)
+        assert st == 0, L.bsattn_last_error()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    # bytes each query head's kernels read: keys and values of its chosen blocks, the pooled
+    # keys of its KV head, the query, the output and idx
+    kv_bytes = w.B * w.Hq * topk * w.block * w.D * 2 * 2
+    kbar_bytes = w.B * w.Hq * w.nb * w.D * 4
+    total = kv_bytes + kbar_bytes + w.B * w.Hq * (w.D * 4 + topk * 4)
+    rec = {
+        "metric": "decode tokens/s (one new token per sequence, block-sparse attention step)",
+        "value": round(w.B / (wall / args.steps), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) caches, resident in HBM)",
+        "config": {"workload": w.name, "B": w.B, "cache_len": w.N, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "D": w.D, "block": w.block, "topk": topk, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(total / (ms / 1e3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(total / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "bsattn_decode (select + split attention + combine)",
+                     "algorithmic_bytes_per_step": total},
+        "decode_ms": round(ms, 4),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
               "multi-GPU variant in this build.", file=sys.stderr)
         sys.exit(2)
+    if args.decode:
+        bench_decode(args)
+        return
     import torch
     import block_sparse_top_amd as bst
     from block_sparse_top_amd import synthetic as syn

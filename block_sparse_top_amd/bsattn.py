@@ -238,7 +238,7 @@ def block_sparse_attention(q, k, v, block_size: int = 64, topk_ratio: float = 0.
 
 def decode_pool(k_cache, lens_new, kbar, block: int, lens_old=None):
     """Pools the key blocks completed between lens_old and lens_new (all complete blocks if
-    lens_old is None) into kbar, fp32 [B, Hkv, Lmax // block, D], in place."""
+    lens_old is None) into kbar, fp32 [B, Hkv, D, Lmax // block] (transposed), in place."""
     B, Lmax, Hkv, D = k_cache.shape
     with torch.cuda.device(k_cache.device):
         _check(lib().bsattn_decode_pool(_DTYPES[k_cache.dtype], B, Lmax, Hkv, D, block,

@@ -9,18 +9,23 @@
 // token L-1): its own block (L-1)/b is always used; the other min(k, own+1) - 1 places go to
 // the complete blocks j < own with the largest q . kbar_j (ties to the lower j).
 //
-// Kernels (bf16 caches [B, Lmax, Hkv, D], fp32 pooled cache [B, Hkv, Lmax/b, D]):
+// Kernels (bf16 caches [B, Lmax, Hkv, D]; fp32 pooled cache stored transposed,
+// [B, Hkv, D, Lmax/b], so that lanes owning consecutive blocks read consecutive words):
 //   pool_new_kernel    one work-group per (sequence, block): pools the blocks completed
 //                      between the old and the new length (all complete blocks without old
 //                      lengths).
-//   dselect_kernel     one work-group per (sequence, query head): fp32 scores of the complete
-//                      earlier blocks (one thread per block, fixed summation order), the same
-//                      bitwise threshold search as the prefill selection, ascending output.
+//   dselect_kernel     one work-group of 4 waves per (sequence, query head) for up to 2048
+//                      blocks (one wave beyond): lane l owns blocks l + 64c; each wave sums a
+//                      quarter of d in order (coalesced loads of the transposed cache), the
+//                      quarters meet in LDS in a fixed order (fp32 scores), then one wave runs
+//                      the prefill selection's bitwise threshold search with ballots and
+//                      compacts the chosen blocks in ascending order.
 //   dattn_kernel       split-K over the chosen blocks (flash-decoding): one wave per
 //                      (sequence, query head, split); per block, lanes own keys for the scores
-//                      (16-byte row loads), the weights go through LDS, then lanes own pairs of
-//                      d for the weighted value sum (coalesced 4-byte loads per key row).
-//                      Writes the split's (max, sum, unnormalised output).
+//                      (16-byte row loads), the weights go through LDS, then groups of lanes
+//                      own 8 consecutive d of one key (16-byte loads, several keys in
+//                      flight) for the weighted value sum. Writes the split's (max, sum,
+//                      unnormalised output).
 //   dcombine_kernel    per (sequence, query head): merges the splits, writes bf16.
 // The work is HBM-bound (each key and value of a chosen block is read once per query head);
 // the single query row leaves nothing for the matrix cores.
@@ -49,120 +54,105 @@ __global__ __launch_bounds__(256) void pool_new_kernel(const uint16_t* __restric
     const uint16_t* p = kc + ((int64_t)b * Lmax + (int64_t)j * block) * rs + 8 * c;
     for (int t = 0; t < block; ++t) Vec<1>::add(*(const u32x4*)(p + t * rs), acc);
     const int g = (8 * c) / D, d0 = (8 * c) % D;
-    float* o = kbar + (((int64_t)b * Hkv + g) * nbmax + j) * D + d0;
+    float* o = kbar + (((int64_t)b * Hkv + g) * D + d0) * nbmax + j;   // [.., d, j]
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = acc[e] * inv;
+    for (int e = 0; e < 8; ++e) o[(int64_t)e * nbmax] = acc[e] * inv;
   }
 }
 
 // ---------------------------------------------------------------- selection
-constexpr int kSelThreads = 256;
-constexpr int kSelPer = 32;                   // columns per thread: nb <= 8192
+constexpr int kSelWaves = 4;                  // (sequence, head) pairs per work-group
+constexpr int kSelCols = kMaxDecodeBlocks / kWave;   // blocks per lane: nb <= 8192
 
-__device__ __forceinline__ int block_sum(int v, int* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x / kWave] = v;
-  __syncthreads();
-  const int total = red[0] + red[1] + red[2] + red[3];
-  __syncthreads();
-  return total;
-}
-
-__device__ __forceinline__ int block_exclusive_scan(int v, int* red) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x / kWave;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) red[w] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int i = 0; i < w; ++i) before += red[i];
-  __syncthreads();
-  return before + incl - v;
-}
-
-template <int D>
-__global__ __launch_bounds__(kSelThreads) void dselect_kernel(
+// SPLIT waves per (sequence, head) share the d range (SPLIT = 4, nb <= 2048) or one wave does
+// all of it (SPLIT = 1, kSelWaves heads per work-group)
+template <int D, int CPL, int SPLIT>
+__global__ __launch_bounds__(256) void dselect_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ kbar,
     const int32_t* __restrict__ lens, int32_t* __restrict__ idx, int64_t Lmax, int Hq, int Hkv,
-    int block, int nbmax, int topk) {
-  __shared__ float qs[D];
-  __shared__ int red[4];
-  const int bh = blockIdx.x;
+    int block, int nbmax, int topk, int heads) {
+  constexpr int HPW = SPLIT == 1 ? kSelWaves : 1;       // (sequence, head) pairs per group
+  __shared__ float qs[HPW][D];
+  __shared__ float partial[SPLIT == 1 ? 1 : SPLIT - 1][SPLIT == 1 ? 1 : 64 * CPL];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int slot = SPLIT == 1 ? wave : 0;               // this wave's pair in the group
+  const int part = SPLIT == 1 ? 0 : wave;               // this wave's quarter of d
+  const int bh = blockIdx.x * HPW + slot;
+  if (bh >= heads) return;                    // SPLIT == 1 only (grid covers heads exactly
+                                              // for SPLIT == 4): no barrier follows
   const int b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
-  const int tid = threadIdx.x;
   int32_t* out = idx + (int64_t)bh * topk;
   const int64_t L = lens[b];
-  if (L < 1 || L > Lmax) {                    // invalid length: no block
-    for (int p = tid; p < topk; p += kSelThreads) out[p] = -1;
+  const bool len_ok = L >= 1 && L <= Lmax;
+  const int own = len_ok ? (int)((L - 1) / block) : 0;
+  const int kb = own + 1 < topk ? own + 1 : topk;
+  const int need = len_ok ? kb - 1 : 0;       // places for complete earlier blocks
+  for (int d = lane; d < D; d += kWave)
+    qs[slot][d] = __uint_as_float((uint32_t)q[(int64_t)bh * D + d] << 16);
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  if (need > 0) {
+    // scores: lane owns blocks lane + 64c (c < CPL); this wave's d range in order
+    const float* K = kbar + ((int64_t)b * Hkv + g) * D * nbmax;
+    constexpr int DR = D / SPLIT;
+    for (int d = part * DR; d < (part + 1) * DR; ++d) {
+      const float qd = qs[slot][d];
+      const float* row = K + (int64_t)d * nbmax;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int j = lane + 64 * c;
+        if (j < own) acc[c] = __builtin_fmaf(qd, row[j], acc[c]);
+      }
+    }
+  }
+  if (SPLIT > 1) {                            // quarters 1.. to LDS, wave 0 adds them in order
+    if (part > 0)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) partial[part - 1][lane + 64 * c] = acc[c];
+    __syncthreads();
+    if (part > 0) return;
+#pragma unroll
+    for (int w = 0; w < SPLIT - 1; ++w)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] += partial[w][lane + 64 * c];
+  }
+  if (!len_ok) {                              // invalid length: no block
+    for (int p = lane; p < topk; p += kWave) out[p] = -1;
     return;
   }
-  const int own = (int)((L - 1) / block);
-  const int kb = own + 1 < topk ? own + 1 : topk;
-  const int need_k = kb - 1;                  // places for complete earlier blocks
-  for (int d = tid; d < D; d += kSelThreads) {
-    const uint16_t w = q[(int64_t)bh * D + d];
-    qs[d] = __uint_as_float((uint32_t)w << 16);
-  }
-  __syncthreads();
-  const float* K = kbar + ((int64_t)b * Hkv + g) * nbmax * D;
-  uint32_t key[kSelPer];
+  if (need > 0) {
+    uint32_t key[CPL];
 #pragma unroll
-  for (int e = 0; e < kSelPer; ++e) {
-    const int j = e * kSelThreads + tid;     // columns strided: a warp's loads share lines
-    key[e] = 0u;
-    if (j < own) {
-      const float* row = K + (int64_t)j * D;
-      float s = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < D; d += 4) {
-        const f32x4 kv = *(const f32x4*)(row + d);
-        s = __builtin_fmaf(qs[d], kv[0], s);
-        s = __builtin_fmaf(qs[d + 1], kv[1], s);
-        s = __builtin_fmaf(qs[d + 2], kv[2], s);
-        s = __builtin_fmaf(qs[d + 3], kv[3], s);
-      }
-      key[e] = order_key(s);
-    }
-  }
-  // threshold T: the need_k-th largest key (keys 0 = no column never count)
-  uint32_t T = 0;
-  if (need_k > 0) {
+    for (int c = 0; c < CPL; ++c) key[c] = (lane + 64 * c) < own ? order_key(acc[c]) : 0u;
+    uint32_t T = 0;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);
-      int c = 0;
+      int cnt = 0;
 #pragma unroll
-      for (int e = 0; e < kSelPer; ++e) c += key[e] >= cand;
-      const int cnt = block_sum(c, red);
-      if (cnt >= need_k) T = cand;
-      if (cnt == need_k) break;
+      for (int c = 0; c < CPL; ++c) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[c] >= cand));
+      if (cnt >= need) T = cand;
+      if (cnt == need) break;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) gt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[c] > T));
+    const int eq_need = need - gt;
+    int eq_before = 0, sel_before = 0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const bool valid = (lane + 64 * c) < own;
+      const bool is_eq = valid && key[c] == T;
+      const uint64_t meq = __builtin_amdgcn_ballot_w64(is_eq);
+      const bool sel = valid && (key[c] > T || (is_eq && eq_before + lanes_below(meq) < eq_need));
+      const uint64_t msel = __builtin_amdgcn_ballot_w64(sel);
+      if (sel) out[sel_before + lanes_below(msel)] = lane + 64 * c;
+      eq_before += __builtin_popcountll(meq);
+      sel_before += __builtin_popcountll(msel);
     }
   }
-  // selected: key > T, then keys == T by ascending column; columns are strided over threads,
-  // so ranks go column by column: e outer, threads inner
-  int gt = 0;
-#pragma unroll
-  for (int e = 0; e < kSelPer; ++e) gt += need_k > 0 && key[e] > T;
-  const int tot_gt = block_sum(gt, red);
-  int eq_seen = 0, pos_seen = 0;
-  for (int e = 0; e < kSelPer; ++e) {
-    if (e * kSelThreads >= own) break;       // uniform
-    const int j = e * kSelThreads + tid;
-    const bool valid = need_k > 0 && j < own;
-    const bool is_eq = valid && T != 0 && key[e] == T;
-    const int eq_before = eq_seen + block_exclusive_scan(is_eq ? 1 : 0, red);
-    const bool sel = valid && (key[e] > T || (is_eq && eq_before < need_k - tot_gt));
-    const int p_before = pos_seen + block_exclusive_scan(sel ? 1 : 0, red);
-    if (sel) out[p_before] = j;
-    eq_seen += block_sum(is_eq ? 1 : 0, red);
-    pos_seen += block_sum(sel ? 1 : 0, red);
-  }
-  if (tid == 0) out[kb - 1] = own;
-  for (int p = kb + tid; p < topk; p += kSelThreads) out[p] = -1;
+  if (lane == 0) out[kb - 1] = own;
+  for (int p = kb + lane; p < topk; p += kWave) out[p] = -1;
 }
 
 // ---------------------------------------------------------------- split-K attention
@@ -172,7 +162,6 @@ __global__ __launch_bounds__(64) void dattn_kernel(
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ lens, float* __restrict__ part, int64_t Lmax, int Hq, int Hkv,
     int block, int topk, int splits, float c) {
-  constexpr int DP = D / 2;                   // bf16 pairs per row
   __shared__ float qs[D];
   __shared__ float ps[128];                   // weights of one block (block <= 128)
   const int bh = blockIdx.x / splits, sp = blockIdx.x % splits;
@@ -190,11 +179,13 @@ __global__ __launch_bounds__(64) void dattn_kernel(
   const int per = (topk + splits - 1) / splits;
   const int e0 = sp * per, e1 = e0 + per < topk ? e0 + per : topk;
   float m = -__builtin_inff(), l = 0.f;
-  // value accumulators: D = 128: lane owns pair (lane); D = 64: lanes 0..31 own pairs of even
-  // keys, lanes 32..63 the same pairs of odd keys (summed at the end)
-  const int pair = D == 128 ? lane : (lane & 31);
-  const int kpar = D == 128 ? 0 : (lane >> 5);
-  float o0 = 0.f, o1 = 0.f;
+  // value accumulators: lane owns d = 8*dg .. 8*dg+7 of keys kq, kq + KG, ... (KG key groups
+  // of LG lanes; the groups are summed at the end)
+  constexpr int LG = D / 8, KG = 64 / LG;
+  const int dg = lane % LG, kq = lane / LG;
+  float o[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) o[x] = 0.f;
   const uint16_t* kb0 = kc + (int64_t)b * Lmax * rs + (int64_t)g * D;
   const uint16_t* vb0 = vc + (int64_t)b * Lmax * rs + (int64_t)g * D;
   const bool len_ok = L >= 1 && L <= Lmax;
@@ -242,24 +233,43 @@ __global__ __launch_bounds__(64) void dattn_kernel(
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) lp += __shfl_xor(lp, o);
     l = l * alpha + lp;
-    o0 *= alpha;
-    o1 *= alpha;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) o[x] *= alpha;
     __syncthreads();
-    const int step = D == 128 ? 1 : 2;
-    for (int t = kpar; t < nk; t += step) {
-      const uint32_t w = *(const uint32_t*)(vb0 + (t0 + t) * rs + 2 * pair);
+    const uint16_t* vrow = vb0 + (t0 + kq) * rs + 8 * dg;
+    int t = kq;
+    for (; t + 3 * KG < nk; t += 4 * KG) {    // four keys of this lane in flight
+      u32x4 w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = *(const u32x4*)(vrow + (int64_t)(t - kq + u * KG) * rs);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float p = ps[t + u * KG];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          o[2 * x] = __builtin_fmaf(p, bf16lo(w[u][x]), o[2 * x]);
+          o[2 * x + 1] = __builtin_fmaf(p, bf16hi(w[u][x]), o[2 * x + 1]);
+        }
+      }
+    }
+    for (; t < nk; t += KG) {
+      const u32x4 w = *(const u32x4*)(vrow + (int64_t)(t - kq) * rs);
       const float p = ps[t];
-      o0 = __builtin_fmaf(p, bf16lo(w), o0);
-      o1 = __builtin_fmaf(p, bf16hi(w), o1);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        o[2 * x] = __builtin_fmaf(p, bf16lo(w[x]), o[2 * x]);
+        o[2 * x + 1] = __builtin_fmaf(p, bf16hi(w[x]), o[2 * x + 1]);
+      }
     }
   }
-  if (D == 64) {                              // fold the odd-key half into lanes 0..31
-    o0 += __shfl_down(o0, 32);
-    o1 += __shfl_down(o1, 32);
-  }
-  if (lane < DP) {
-    my[2 + 2 * pair] = o0;
-    my[2 + 2 * pair + 1] = o1;
+  // sum the key groups (lanes dg, dg + LG, ...)
+#pragma unroll
+  for (int off = LG; off < 64; off <<= 1)
+#pragma unroll
+    for (int x = 0; x < 8; ++x) o[x] += __shfl_xor(o[x], off);
+  if (kq == 0) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) my[2 + 8 * dg + x] = o[x];
   }
   if (lane == 0) {
     my[0] = m;
@@ -295,11 +305,37 @@ __global__ __launch_bounds__(64) void dcombine_kernel(const float* __restrict__ 
   }
 }
 
+template <int D, int CPL>
+hipError_t launch_dsel(const void* q, const float* kbar, const int32_t* lens, int32_t* idx,
+                       int64_t Lmax, int Hq, int Hkv, int block, int nbmax, int topk,
+                       unsigned heads, hipStream_t stream) {
+  if (CPL <= 32)                              // nb <= 2048: 4 waves per (sequence, head)
+    dselect_kernel<D, CPL, 4><<<heads, 256, 0, stream>>>(
+        (const uint16_t*)q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, (int)heads);
+  else
+    dselect_kernel<D, CPL, 1><<<(heads + kSelWaves - 1) / kSelWaves, kSelWaves * 64, 0, stream>>>(
+        (const uint16_t*)q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, (int)heads);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dselect(const void* q, const float* kbar, const int32_t* lens, int32_t* idx,
+                          int64_t Lmax, int Hq, int Hkv, int block, int nbmax, int topk,
+                          unsigned heads, hipStream_t stream) {
+  if (nbmax <= 64) return launch_dsel<D, 1>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, stream);
+  if (nbmax <= 256) return launch_dsel<D, 4>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, stream);
+  if (nbmax <= 1024) return launch_dsel<D, 16>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, stream);
+  if (nbmax <= 2048) return launch_dsel<D, 32>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, stream);
+  if (nbmax <= 4096) return launch_dsel<D, 64>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, stream);
+  return launch_dsel<D, kSelCols>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, stream);
+}
+
 }  // namespace
 
 int decode_splits(int64_t B, int Hq, int topk) {
   const int64_t heads = B * Hq;
-  int64_t s = (2048 + heads - 1) / heads;     // aim at >= 2048 waves on 256 CUs
+  int64_t s = (8192 + heads - 1) / heads;     // aim at >= 8192 waves (8 per SIMD): each
+                                              // wave's blocks are a chain of dependent loads
   if (s > topk) s = topk;
   if (s < 1) s = 1;
   if (s > 64) s = 64;
@@ -332,13 +368,12 @@ hipError_t launch_decode(int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int bl
   const float c = (float)((double)scale * 1.4426950408889634);
   float* part = (float*)workspace;
   const unsigned heads = (unsigned)(B * Hq);
-  if (D == 64)
-    dselect_kernel<64><<<heads, kSelThreads, 0, stream>>>((const uint16_t*)q, kbar, lens, idx,
-                                                           Lmax, Hq, Hkv, block, nbmax, topk);
-  else
-    dselect_kernel<128><<<heads, kSelThreads, 0, stream>>>((const uint16_t*)q, kbar, lens, idx,
-                                                            Lmax, Hq, Hkv, block, nbmax, topk);
-  hipError_t e = hipGetLastError();
+  hipError_t e = D == 64 ? launch_dselect<64>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax,
+                                              topk, heads, stream)
+                         : launch_dselect<128>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax,
+                                               topk, heads, stream);
+  if (e != hipSuccess) return e;
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (D == 64)
     dattn_kernel<64><<<heads * splits, 64, 0, stream>>>(

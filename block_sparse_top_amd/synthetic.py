@@ -61,6 +61,13 @@ WORKLOADS = {
 }
 
 
+# Decode workload (one new token per sequence against a full KV cache of N tokens).
+DECODE_WORKLOADS = {
+    "decode_gqa_l32768": Workload("decode_gqa_l32768", B=32, N=32768, Hq=32, Hkv=8, D=128,
+                                  block=64, ratio=0.15, dtype="bf16", index=6),
+}
+
+
 def seeds(index: int) -> dict:
     """Seed family of a workload: q, k, v, sampling and planted-structure streams."""
     base = 1000 * index
@@ -116,6 +123,16 @@ def iid_inputs(B, N, Hq, Hkv, D, dtype="bf16", index=0, device="cpu"):
         out.append(x)
         ds.append(d)
     return out[0], out[1], out[2], tuple(ds)
+
+
+def decode_inputs(w: Workload, device="cpu"):
+    """Decode inputs: the newest query token q [B, Hq, D] and caches k, v [B, N, Hkv, D],
+    i.i.d. N(0,1) rounded to the workload's dtype (the q, k, v seeds of its family)."""
+    s = seeds(w.index)
+    q, _ = to_storage(randn((w.B, w.Hq, w.D), s["q"], device), w.dtype)
+    k, _ = to_storage(randn((w.B, w.N, w.Hkv, w.D), s["k"], device), w.dtype)
+    v, _ = to_storage(randn((w.B, w.N, w.Hkv, w.D), s["v"], device), w.dtype)
+    return q, k, v
 
 
 def planted_inputs(B, N, Hq, Hkv, D, block, planted_k, dtype="bf16", index=0, device="cpu",

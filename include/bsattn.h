@@ -214,8 +214,8 @@ int bsattn_backward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int
 /*
  * Decode (one new query token per sequence against a KV cache).
  * Caches: k_cache, v_cache bf16 [B, Lmax, Hkv, D] (token t of sequence b at row t), pooled
- * keys kbar fp32 [B, Hkv, Lmax / block, D] (row j = mean of the keys of block j once that
- * block is complete), lens int32 [B] on the device: tokens cached per sequence
+ * keys kbar fp32 [B, Hkv, D, Lmax / block] (transposed: kbar[b,g,:,j] = mean of the keys of
+ * block j once that block is complete), lens int32 [B] on the device: tokens cached per sequence
  * (1 <= lens[b] <= Lmax; the query is token lens[b] - 1, its K and V already in the cache).
  * SparseFormer page, "SparseFormer 注意力实现" (pooled key blocks, top-k blocks, attention over
  * them with scale 1/sqrt(D)); MSA page §5.2 (first-token latency of the block scoring).
@@ -236,7 +236,7 @@ size_t bsattn_decode_workspace_bytes(int64_t B, int Hq, int D, int topk);
 
 /* One decode step for every sequence and query head h (KV head h / (Hq / Hkv)):
  *   own = (lens[b] - 1) / block is always used; the other min(topk, own + 1) - 1 places go to
- *   the complete blocks j < own with the largest sum_d q[b,h,d] * kbar[b,g,j,d] (fp32;
+ *   the complete blocks j < own with the largest sum_d q[b,h,d] * kbar[b,g,d,j] (fp32;
  *   ties to the lower j); idx[b,h,:] receives them ascending (own last), then -1.
  *   out[b,h,:] = softmax over the keys of those blocks (own block: positions < lens[b]) of
  *   scale * q . k, times v; bf16 [B, Hq, D]; fp32 scores and sums.

@@ -58,13 +58,13 @@ def test_decode(case):
     say(f"[decode] {case}")
     q, kc, vc = caches(B, Lmax, Hq, Hkv, D, index=41)
     lens = torch.tensor(lens_l, dtype=torch.int32, device=DEV)
-    kbar = torch.full((B, Hkv, Lmax // blk, D), float("nan"), dtype=torch.float32, device=DEV)
+    kbar = torch.full((B, Hkv, D, Lmax // blk), float("nan"), dtype=torch.float32, device=DEV)
     bst.decode_pool(kc, lens, kbar, blk)
     out, idx = bst.decode(q, kc, vc, kbar, lens, blk, topk)
     torch.cuda.synchronize()
     qo, ko, vo = to_f64(q), to_f64(kc), to_f64(vc)
     kbar_o = O.pool(ko, blk)
-    kg = kbar.cpu().numpy()
+    kg = kbar.cpu().numpy().transpose(0, 1, 3, 2)           # -> [B, Hkv, nb, D]
     for b in range(B):                                       # complete blocks only
         nc = lens_l[b] // blk
         assert np.max(np.abs(kg[b, :, :nc] - kbar_o[b, :, :nc]), initial=0.0) <= 2e-6 * np.abs(ko).max()
@@ -84,7 +84,7 @@ def test_decode_incremental_pool_and_invalid_length():
     B, Lmax, Hq, Hkv, D, blk = 3, 64 * 10, 4, 2, 64, 64
     say("[decode incremental]")
     q, kc, vc = caches(B, Lmax, Hq, Hkv, D, index=42)
-    kbar = torch.zeros((B, Hkv, Lmax // blk, D), dtype=torch.float32, device=DEV)
+    kbar = torch.zeros((B, Hkv, D, Lmax // blk), dtype=torch.float32, device=DEV)
     lens_seq = [[1, 5, 64], [63, 64, 65], [128, 200, 640], [640, 400, 640]]
     prev = torch.zeros(B, dtype=torch.int32, device=DEV)
     for ls in lens_seq[:3]:
@@ -96,7 +96,7 @@ def test_decode_incremental_pool_and_invalid_length():
     torch.cuda.synchronize()
     for b in range(B):
         nc = int(prev[b]) // blk
-        assert torch.equal(kbar[b, :, :nc], full[b, :, :nc])
+        assert torch.equal(kbar[b, :, :, :nc], full[b, :, :, :nc])
     lens = torch.tensor([640, 0, 300], dtype=torch.int32, device=DEV)
     out, idx = bst.decode(q, kc, vc, full, lens, blk, 3)
     torch.cuda.synchronize()
