@@ -49,6 +49,12 @@ the design notes of the repository):
       the complete blocks j < own with the largest q . kbar_j (kbar: mean of the block's keys,
       kept up to date as blocks complete; ties to the lower j); attention over those blocks
       and the own block's cached tokens (all at positions <= L-1).
+  R27 random blocks (NEXT N3; the MSA page's §5.1 remedy "5% random blocks"): of a row's k
+      places, k - r keep the best scores and r go to blocks drawn uniformly without
+      replacement from the others: draw p (p < r) takes the (x mod m_p)-th remaining block in
+      ascending order, m_p = nb - (k - r) - p, x = element row * 2^16 + p of the SplitMix64
+      sequence (Steele, Lea, Flood, OOPSLA 2014) seeded with the caller's seed, row the
+      row's position (batch, head, query block) in C order.
   R25 backward (the MSA page's §4.1 checks that back-propagation is complete; the
       SparseFormer page recommends the method for training large models, "千亿参数大模型训练"):
       gradients of the gathered-block attention with the selection held fixed (top-k is
@@ -203,6 +209,40 @@ def select_topk_causal(S: np.ndarray, k: int) -> np.ndarray:
             row[..., :ki - 1] = select_topk(S[..., i, :i], ki - 1)   # over j < i
         row[..., ki - 1] = i                                      # own block, largest index
     return out
+
+
+_U64 = (1 << 64) - 1
+_GAMMA = 0x9E3779B97F4A7C15
+
+
+def splitmix64(seed: int, n: int) -> int:
+    """Element n (0-based) of the SplitMix64 sequence seeded with `seed`: the state after
+    n + 1 Weyl steps of GAMMA, through the published 64-bit finaliser [R27]."""
+    z = (seed + (n + 1) * _GAMMA) & _U64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _U64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _U64
+    return z ^ (z >> 31)
+
+
+def select_topk_random(S: np.ndarray, k: int, r: int, seed: int) -> np.ndarray:
+    """Top k - r blocks by score plus r random others per row [R27]; ascending.
+
+    S [..., nb]; the row number of S[..., :] is its position in C order over the leading axes.
+    """
+    nb = S.shape[-1]
+    if not (1 <= k <= nb and 0 <= r <= k):
+        raise ValueError("need 1 <= k <= nb and 0 <= r <= k")
+    rows = S.reshape(-1, nb)
+    out = np.empty((rows.shape[0], k), dtype=np.int64)
+    for row in range(rows.shape[0]):
+        top = select_topk(rows[row][None], k - r)[0].tolist() if k > r else []
+        rest = [j for j in range(nb) if j not in set(top)]
+        picked = []
+        for p in range(r):
+            x = splitmix64(seed, row * 65536 + p)
+            picked.append(rest.pop(x % len(rest)))
+        out[row] = sorted(top + picked)
+    return out.reshape(S.shape[:-1] + (k,))
 
 
 def group_scores(S: np.ndarray, Hkv: int) -> np.ndarray:
@@ -443,18 +483,24 @@ def decode_attend(q_tok, k_cache, v_cache, idx, lens, block: int, scale: float) 
 
 
 def select(q, k, block: int, topk: int, causal: bool = False, pooling: str = "mean",
-           group: bool = False) -> np.ndarray:
+           group: bool = False, nrand: int = 0, seed: int = 0) -> np.ndarray:
     """Steps 1-2 [SF]: pool q and k, score the blocks, keep the top-k per row.
 
     causal [R20], pooling "mean" [SF] or "max" [R21], group: one selection per KV head
-    group, repeated for each of its query heads [R22]. Returns [B, Hq, nb, topk].
+    group, repeated for each of its query heads [R22], nrand random places [R27] (not with
+    causal). Returns [B, Hq, nb, topk].
     """
     pf = pool if pooling == "mean" else pool_max
     S = block_scores(pf(q, block), pf(k, block))
     Hq, Hkv = q.shape[2], k.shape[2]
     if group:
         S = group_scores(S, Hkv)
-    idx = select_topk_causal(S, topk) if causal else select_topk(S, topk)
+    if nrand:
+        if causal:
+            raise ValueError("random places are defined for the non-causal selection")
+        idx = select_topk_random(S, topk, nrand, seed)
+    else:
+        idx = select_topk_causal(S, topk) if causal else select_topk(S, topk)
     if group:
         idx = np.repeat(idx, Hq // Hkv, axis=1)
     return idx

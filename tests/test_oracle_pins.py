@@ -436,12 +436,48 @@ def check_decode(o=O):
     assert z[0, 0].tolist() == [0, 1, 7] and z[2, 0].tolist() == [0, 1, -1]
 
 
+def check_random_fill(o=O):
+    """Random places [R27]: SplitMix64 against its published first outputs for seed 0; per
+    row the top k - r blocks, r further distinct blocks, ascending; r = 0 is select_topk;
+    the draws are uniform over the remaining blocks (chi-square over many rows)."""
+    assert [o.splitmix64(0, n) for n in range(3)] == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4,
+                                                      0x06C45D188009454F]
+    r_ = rng(24)
+    S = np.round(r_.standard_normal((2, 3, 10, 40)), 1)
+    for k, rr in ((6, 2), (8, 8), (5, 0), (40, 3)):
+        idx = o.select_topk_random(S, k, rr, seed=1234)
+        top = o.select_topk(S, k - rr) if k > rr else np.zeros(S.shape[:-1] + (0,), dtype=int)
+        nrows = int(np.prod(S.shape[:-1]))
+        for row_i, row_t in zip(idx.reshape(nrows, k), top.reshape(nrows, k - rr)):
+            assert np.all(np.diff(row_i) > 0) and row_i.min() >= 0 and row_i.max() < 40
+            assert set(row_t.tolist()) <= set(row_i.tolist())
+        if rr == 0:
+            assert np.array_equal(idx, o.select_topk(S, k))
+    assert not np.array_equal(o.select_topk_random(S, 6, 2, 1), o.select_topk_random(S, 6, 2, 2))
+    # uniformity: one random place among 19 others, many rows with equal scores for the rest
+    S2 = np.zeros((4000, 20))
+    S2[:, 0] = 1.0
+    picks = o.select_topk_random(S2, 2, 1, seed=99)[:, 1]
+    counts = np.bincount(picks, minlength=20)[1:]
+    chi2 = float(((counts - 4000 / 19) ** 2 / (4000 / 19)).sum())
+    assert chi2 < 45.0, chi2                     # 18 degrees of freedom: p ~ 5e-4
+    # without replacement every 2-subset of the 3 non-top blocks is equally likely
+    S3 = np.zeros((6000, 4))
+    S3[:, 0] = 1.0
+    pairs = o.select_topk_random(S3, 3, 2, seed=7)[:, 1:]
+    codes = pairs[:, 0] * 4 + pairs[:, 1]
+    counts = np.array([(codes == c).sum() for c in (1 * 4 + 2, 1 * 4 + 3, 2 * 4 + 3)])
+    assert counts.sum() == 6000
+    chi2 = float(((counts - 2000) ** 2 / 2000).sum())
+    assert chi2 < 16.0, (counts, chi2)          # 2 degrees of freedom: p ~ 3e-4
+
+
 ALL_CHECKS = [check_bf16_widen, check_e4m3, check_pool, check_scores, check_select_vs_sort,
               check_select_special, check_dense_limit, check_bruteforce, check_ties_and_zero,
               check_invariants, check_gqa, check_batched, check_causal_select,
               check_causal_dense_limit, check_causal_bruteforce, check_pool_max,
               check_group_select, check_backward_autograd, check_backward_fd_and_invariants,
-              check_lse, check_decode]
+              check_lse, check_decode, check_random_fill]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -539,6 +575,23 @@ def _decode_unforced(q_tok, kbar, lens, blk, topk):
     return out
 
 
+def _random_with_replacement(S, k, r, seed):
+    """select_topk_random drawing from all non-top blocks each time (a block can come twice,
+    then the row is padded with the next free block): a planted mistake."""
+    nb = S.shape[-1]
+    rows = S.reshape(-1, nb)
+    out = np.empty((rows.shape[0], k), dtype=np.int64)
+    for row in range(rows.shape[0]):
+        top = O.select_topk(rows[row][None], k - r)[0].tolist() if k > r else []
+        rest = [j for j in range(nb) if j not in set(top)]
+        picked = set()
+        for p in range(r):
+            picked.add(rest[O.splitmix64(seed, row * 65536 + p) % len(rest)])
+        extra = [j for j in rest if j not in picked][: r - len(picked)]
+        out[row] = sorted(top + sorted(picked) + extra)
+    return out.reshape(S.shape[:-1] + (k,))
+
+
 class Mutant:
     """The oracle module with one function replaced by a wrong version."""
 
@@ -567,7 +620,7 @@ def _mutant(**repl):
     m = Mutant(**repl)
     for name in ("select", "block_sparse_attention", "block_scores", "attend", "attend_batched",
                  "dense_attention", "masked_attention_bruteforce", "select_topk_causal",
-                 "decode_select", "decode_attend"):
+                 "decode_select", "decode_attend", "select_topk_random"):
         if name not in repl:
             setattr(m, name, _rebind(getattr(O, name), m))
     return m
@@ -606,6 +659,8 @@ MUTANTS = {
         (lambda g: (g[0], g[1] / scale, g[2]))(O.attend_backward(q, k, v, idx, blk, scale, dout, causal))),
     "decode_own_block_not_forced": dict(
         decode_select=lambda q, kb, lens, blk, topk: _decode_unforced(q, kb, lens, blk, topk)),
+    "random_fill_with_replacement": dict(
+        select_topk_random=lambda S, k, r, seed: _random_with_replacement(S, k, r, seed)),
     "lse_log2": dict(attend_lse=lambda q, k, idx, blk, scale, causal=False:
                      O.attend_lse(q, k, idx, blk, scale, causal) / np.log(2.0)),
     "group_first_head_only": dict(
