@@ -250,8 +250,8 @@ def main():
         | (bst.GROUP_SELECT if args.group else 0)
 
     def do_select():
-        st = L.bsattn_select_ex(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, P(q),
-                                P(k), P(idx), P(ws), ws.numel(), sp)
+        st = L.bsattn_select_ex(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, 0, 0,
+                                P(q), P(k), P(idx), P(ws), ws.numel(), sp)
         assert st == 0, L.bsattn_last_error()
 
     def do_forward():

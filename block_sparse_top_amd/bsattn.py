@@ -61,8 +61,8 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_float, ctypes.POINTER(ctypes.c_float), vp, vp]
     u32 = ctypes.c_uint
     L.bsattn_select_ex.restype = i32
-    L.bsattn_select_ex.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, u32, vp, vp, vp, vp,
-                                   sz, vp]
+    L.bsattn_select_ex.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, u32, i32,
+                                   ctypes.c_uint64, vp, vp, vp, vp, sz, vp]
     L.bsattn_forward_ex.restype = i32
     L.bsattn_forward_ex.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, u32, vp, vp, vp, vp,
                                     ctypes.c_float, ctypes.POINTER(ctypes.c_float), vp, vp, vp]
@@ -134,11 +134,13 @@ def select_workspace_bytes(B, N, Hq, Hkv, D, block) -> int:
 
 
 def select(q, k, block: int, topk: int, *, causal: bool = False, pooling: str = "mean",
-           group: bool = False, return_pooled: bool = False, workspace=None):
+           group: bool = False, nrand: int = 0, seed: int = 0, return_pooled: bool = False,
+           workspace=None):
     """Top-k key blocks per (batch, query head, query block): int32 [B, Hq, nb, topk].
 
     causal: own block forced, earlier blocks only, unused places -1; pooling "max": in-block
-    maximum instead of the mean; group: one selection per KV head for all its query heads.
+    maximum instead of the mean; group: one selection per KV head for all its query heads;
+    nrand, seed: nrand of the topk places drawn at random from the non-top blocks.
     With return_pooled, also returns the pooled q and k (fp32 [B, Hq, nb, D] and
     [B, Hkv, nb, D]; for fp8 inputs without the per-tensor descale).
     """
@@ -151,8 +153,9 @@ def select(q, k, block: int, topk: int, *, causal: bool = False, pooling: str = 
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     with torch.cuda.device(q.device):
         _check(lib().bsattn_select_ex(_DTYPES[q.dtype], B, N, Hq, Hkv, D, block, topk, flags,
-                                      _ptr(q), _ptr(k), _ptr(idx), _ptr(workspace),
-                                      workspace.numel(), _stream(q.device)))
+                                      int(nrand), int(seed) & ((1 << 64) - 1), _ptr(q), _ptr(k),
+                                      _ptr(idx), _ptr(workspace), workspace.numel(),
+                                      _stream(q.device)))
     if not return_pooled:
         return idx
     qb_bytes = (B * Hq * nb * D * 4 + 255) // 256 * 256

@@ -109,17 +109,22 @@ size_t bsattn_select_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int 
 int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                   const void* q, const void* k, int32_t* idx, void* workspace,
                   size_t workspace_bytes, void* stream) {
-  return bsattn_select_ex(dtype, B, N, Hq, Hkv, D, block, topk, 0u, q, k, idx, workspace,
-                          workspace_bytes, stream);
+  return bsattn_select_ex(dtype, B, N, Hq, Hkv, D, block, topk, 0u, 0, 0ull, q, k, idx,
+                          workspace, workspace_bytes, stream);
 }
 
 int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
-                     int topk, unsigned flags, const void* q, const void* k, int32_t* idx,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     int topk, unsigned flags, int nrand, uint64_t seed, const void* q,
+                     const void* k, int32_t* idx, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   int st = check_shape(dtype, B, N, Hq, Hkv, D, block, topk);
   if (st != BSATTN_OK) return st;
   if (flags & ~(unsigned)(BSATTN_CAUSAL | BSATTN_POOL_MAX | BSATTN_GROUP_SELECT))
     return fail(BSATTN_E_INVALID, "unknown flags 0x%x", flags);
+  if (nrand < 0 || nrand > topk)
+    return fail(BSATTN_E_INVALID, "nrand %d outside [0, topk=%d]", nrand, topk);
+  if (nrand > 0 && (flags & BSATTN_CAUSAL))
+    return fail(BSATTN_E_UNSUPPORTED, "random places with the causal selection");
   if (B == 0 || N == 0) return BSATTN_OK;
   const int64_t nb = N / block;
   const bool large = bsattn::materialized_scores(nb, flags & BSATTN_GROUP_SELECT);
@@ -130,6 +135,9 @@ int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, in
   if (large && (flags & BSATTN_GROUP_SELECT))
     return fail(BSATTN_E_UNSUPPORTED, "group selection over nb=%lld > %d blocks",
                 (long long)nb, bsattn::kMaxFusedBlocks);
+  if (large && nrand > 0)
+    return fail(BSATTN_E_UNSUPPORTED, "random places over nb=%lld > %d blocks", (long long)nb,
+                bsattn::kMaxFusedBlocks);
   if (!q || !k || !idx) return fail(BSATTN_E_INVALID, "null q, k or idx");
   if (!aligned16(q) || !aligned16(k) || ((uintptr_t)idx & 3u))
     return fail(BSATTN_E_INVALID, "q and k must be 16-byte aligned, idx 4-byte aligned");
@@ -160,7 +168,7 @@ int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, in
       "key pool launch");
   if (st != BSATTN_OK) return st;
   return hip_status(bsattn::launch_pool_score_select(kind, B, N, Hq, Hkv, D, block, topk, q,
-                                                     qbar, kbar, idx, flags, s),
+                                                     qbar, kbar, idx, flags, nrand, seed, s),
                     "query pool/score/select launch");
 }
 

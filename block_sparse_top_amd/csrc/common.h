@@ -104,6 +104,16 @@ template <> struct Vec<2> {            // OCP fp8 e4m3 (gfx950 converts the OCP 
   }
 };
 
+// Element n (0-based) of the SplitMix64 sequence seeded with `seed` (Steele, Lea, Flood,
+// "Fast splittable pseudorandom number generators", OOPSLA 2014): the state after n + 1 Weyl
+// steps of the golden-ratio increment, through the published 64-bit finaliser.
+__device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t n) {
+  uint64_t z = seed + (n + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
 // Selection options (flags of the extended entry points)
 constexpr unsigned kCausal = 1u;     // key blocks j <= i only, own block forced
 constexpr unsigned kPoolMax = 2u;    // in-block elementwise maximum instead of the mean

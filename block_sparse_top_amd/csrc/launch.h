@@ -19,7 +19,7 @@ constexpr int kMaxFusedBlocks = 1024;
 hipError_t launch_pool_score_select(int kind, int64_t B, int64_t N, int Hq, int Hkv, int D,
                                     int block, int topk, const void* q, float* qbar,
                                     const float* kbar, int32_t* idx, unsigned flags,
-                                    hipStream_t stream);
+                                    int nrand, uint64_t seed, hipStream_t stream);
 
 // Steps 2-3 for nb > kMaxFusedBlocks (nb % 64 == 0, nb <= kMaxLargeBlocks): S = scores
 // [B, Hq, nb, nb] fp32 in the workspace, then the top-k of each of its rows.

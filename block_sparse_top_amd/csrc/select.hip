@@ -34,6 +34,10 @@
 // work-group pools the rows of all G query heads of the group and sums them (the scores of
 // the sum are the sum of the heads' scores), and the chosen blocks are written for each of
 // the G heads; the pooled-query workspace rows of the group's first head hold the sums.
+// nrand > 0 (random places): the row keeps its top topk - nrand blocks, then draw p takes the
+// (x mod m_p)-th of the m_p = nb - (topk - nrand) - p blocks not yet chosen, in ascending
+// order, x = element row * 2^16 + p of the SplitMix64 sequence (Steele, Lea, Flood, 2014)
+// seeded with `seed`, row = (batch, selection head, query block) in C order.
 #include "common.h"
 #include "launch.h"
 
@@ -55,7 +59,7 @@ template <int KIND, int CPL>  // storage kind; score columns per lane: nb <= 64 
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const uint8_t* __restrict__ q, float* __restrict__ qbar, const float* __restrict__ kbar,
     int32_t* __restrict__ idx, int64_t N, int Hq, int Hkv, int nb, int D, int block, int topk,
-    int row_tiles, float inv_block, unsigned flags) {
+    int row_tiles, float inv_block, unsigned flags, int nrand, uint64_t seed) {
   constexpr int RW = SelCfg<CPL>::RW, RG = SelCfg<CPL>::RG;
   constexpr int E = Vec<KIND>::E;
   constexpr int EB = 16 / E;                // bytes per stored element
@@ -193,41 +197,70 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     // >= 1) and no T reached by the search (>= 1 once any bit is set) can count; causal rows
     // give their own block the largest key
     const int lim = causal ? row + 1 : nb;  // admissible columns j < lim
-    const int kr = causal && row + 1 < topk ? row + 1 : topk;
+    const int kt = causal && row + 1 < topk ? row + 1 : topk;   // places of the row
+    const int kr = kt - nrand;              // places taken by score (nrand = 0 if causal)
     uint32_t key[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int j = c * 64 + lane;
       key[c] = j < lim ? (causal && j == row ? 0xFFFFFFFFu : order_key(acc[r][c])) : 0u;
     }
-    uint32_t T = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      int cnt = 0;
+    // chosen columns of this lane: the top kr by key (ties to the lower column) ...
+    bool chosen[CPL];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[c] >= cand));
-      if (cnt >= kr) T = cand;
-      if (cnt == kr) break;                 // exactly kr keys >= T: T separates the top kr
-    }
-    int gt = 0;
+    for (int c = 0; c < CPL; ++c) chosen[c] = false;
+    if (kr > 0) {
+      uint32_t T = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        int cnt = 0;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) gt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[c] > T));
-    const int need = kr - gt;               // places for keys equal to T
-    for (int j = 0; j < nh; ++j) {
-      int32_t* out = idx + ((int64_t)(bh + j) * nb + row) * topk;
-      int eq_before = 0, sel_before = 0;
+        for (int c = 0; c < CPL; ++c) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[c] >= cand));
+        if (cnt >= kr) T = cand;
+        if (cnt == kr) break;               // exactly kr keys >= T: T separates the top kr
+      }
+      int gt = 0;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) gt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[c] > T));
+      const int need = kr - gt;             // places for keys equal to T
+      int eq_before = 0;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const bool valid = (c * 64 + lane) < lim;
         const bool is_eq = valid && key[c] == T;
         const uint64_t meq = __builtin_amdgcn_ballot_w64(is_eq);
-        const bool sel = valid && (key[c] > T || (is_eq && eq_before + lanes_below(meq) < need));
-        const uint64_t msel = __builtin_amdgcn_ballot_w64(sel);
-        if (sel) out[sel_before + lanes_below(msel)] = c * 64 + lane;
+        chosen[c] = valid && (key[c] > T || (is_eq && eq_before + lanes_below(meq) < need));
         eq_before += __builtin_popcountll(meq);
+      }
+    }
+    // ... then nrand random others, one draw at a time (uniform across the wave)
+    if (nrand > 0) {
+      const uint64_t srow = (uint64_t)((int64_t)sh * nb + row);
+      for (int p = 0; p < nrand; ++p) {
+        const uint32_t m = (uint32_t)(nb - kr - p);              // blocks not yet chosen
+        const uint32_t x = (uint32_t)(splitmix64(seed, srow * 65536u + (uint64_t)p) % m);
+        uint32_t before = 0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const uint64_t mrem = __builtin_amdgcn_ballot_w64((c * 64 + lane) < nb && !chosen[c]);
+          const uint32_t cnt = (uint32_t)__builtin_popcountll(mrem);
+          if (x >= before && x < before + cnt && ((mrem >> lane) & 1ull) &&
+              (uint32_t)lanes_below(mrem) == x - before)
+            chosen[c] = true;
+          before += cnt;
+        }
+      }
+    }
+    for (int j = 0; j < nh; ++j) {
+      int32_t* out = idx + ((int64_t)(bh + j) * nb + row) * topk;
+      int sel_before = 0;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const uint64_t msel = __builtin_amdgcn_ballot_w64(chosen[c]);
+        if (chosen[c]) out[sel_before + lanes_below(msel)] = c * 64 + lane;
         sel_before += __builtin_popcountll(msel);
       }
-      for (int p = kr + lane; p < topk; p += kWave) out[p] = -1;   // unused causal places
+      for (int p = kt + lane; p < topk; p += kWave) out[p] = -1;   // unused causal places
     }
   }
 }
@@ -235,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 template <int KIND, int CPL>
 hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int nb, int D, int block, int topk,
                   const void* q, float* qbar, const float* kbar, int32_t* idx, unsigned flags,
-                  hipStream_t stream) {
+                  int nrand, uint64_t seed, hipStream_t stream) {
   constexpr int RG = SelCfg<CPL>::RG;
   const int row_tiles = (nb + RG - 1) / RG;
   const int HS = (flags & kGroup) ? Hkv : Hq;
@@ -243,19 +276,19 @@ hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int nb, int D, int bloc
   const size_t lds = (size_t)(64 * (D + 1) + RG * D) * sizeof(float);
   select_kernel<KIND, CPL><<<grid, kThreads, lds, stream>>>(
       (const uint8_t*)q, qbar, kbar, idx, N, Hq, Hkv, nb, D, block, topk, row_tiles,
-      1.0f / (float)block, flags);
+      1.0f / (float)block, flags, nrand, seed);
   return hipGetLastError();
 }
 
 template <int KIND>
 hipError_t launch_kind(int64_t B, int64_t N, int Hq, int Hkv, int nb, int D, int block, int topk,
                        const void* q, float* qbar, const float* kbar, int32_t* idx,
-                       unsigned flags, hipStream_t stream) {
-  if (nb <= 64) return launch<KIND, 1>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
-  if (nb <= 128) return launch<KIND, 2>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
-  if (nb <= 256) return launch<KIND, 4>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
-  if (nb <= 512) return launch<KIND, 8>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
-  return launch<KIND, 16>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
+                       unsigned flags, int nrand, uint64_t seed, hipStream_t stream) {
+  if (nb <= 64) return launch<KIND, 1>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
+  if (nb <= 128) return launch<KIND, 2>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
+  if (nb <= 256) return launch<KIND, 4>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
+  if (nb <= 512) return launch<KIND, 8>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
+  return launch<KIND, 16>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
 }
 
 }  // namespace
@@ -263,11 +296,11 @@ hipError_t launch_kind(int64_t B, int64_t N, int Hq, int Hkv, int nb, int D, int
 hipError_t launch_pool_score_select(int kind, int64_t B, int64_t N, int Hq, int Hkv, int D,
                                     int block, int topk, const void* q, float* qbar,
                                     const float* kbar, int32_t* idx, unsigned flags,
-                                    hipStream_t stream) {
+                                    int nrand, uint64_t seed, hipStream_t stream) {
   const int nb = (int)(N / block);
-  if (kind == 0) return launch_kind<0>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
-  if (kind == 1) return launch_kind<1>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
-  return launch_kind<2>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, stream);
+  if (kind == 0) return launch_kind<0>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
+  if (kind == 1) return launch_kind<1>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
+  return launch_kind<2>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
 }
 
 }  // namespace bsattn

@@ -120,10 +120,21 @@ int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int b
 
 /* bsattn_select with options: flags is a combination of BSATTN_CAUSAL, BSATTN_POOL_MAX and
  * BSATTN_GROUP_SELECT (0 gives bsattn_select). Other bits: BSATTN_E_INVALID. Same workspace
- * size. Arguments, layouts and errors otherwise as bsattn_select. */
+ * size.
+ *   nrand  random places (the MSA page's §5.1 remedy "5% random blocks"; 0: none): each row
+ *          keeps its topk - nrand best blocks, then draw p = 0 .. nrand-1 takes the
+ *          (x mod m_p)-th of the m_p = nb - (topk - nrand) - p blocks not yet chosen, in
+ *          ascending order, with x = element row * 65536 + p of the SplitMix64 sequence
+ *          (Steele, Lea, Flood, OOPSLA 2014) seeded with `seed`; row = (b * S + s) * nb + i
+ *          for selection head s of S (S = Hq, or Hkv with BSATTN_GROUP_SELECT). The row stays
+ *          ascending. 0 <= nrand <= topk (else BSATTN_E_INVALID); not with BSATTN_CAUSAL and
+ *          only for nb <= 1024 (else BSATTN_E_UNSUPPORTED).
+ *   seed   the generator's seed.
+ * Arguments, layouts and errors otherwise as bsattn_select. */
 int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
-                     int topk, unsigned flags, const void* q, const void* k, int32_t* idx,
-                     void* workspace, size_t workspace_bytes, void* stream);
+                     int topk, unsigned flags, int nrand, uint64_t seed, const void* q,
+                     const void* k, int32_t* idx, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /*
  * Gathered-block attention (step 3 of "SparseFormer 注意力实现"; MSA page §2.1 with a

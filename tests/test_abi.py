@@ -100,14 +100,17 @@ def sel_ex(flags, **kw):
              idx=FAKE, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return bst.lib().bsattn_select_ex(a["dtype"], a["B"], a["N"], a["Hq"], a["Hkv"], a["D"],
-                                      a["block"], a["topk"], flags, a["q"], a["k"], a["idx"],
-                                      a["ws"], a["wsb"], None)
+                                      a["block"], a["topk"], flags, a.get("nrand", 0), 0,
+                                      a["q"], a["k"], a["idx"], a["ws"], a["wsb"], None)
 
 
 def test_extended_entry_points_reject():
     assert sel_ex(8) == 1 and "flags" in last()                   # unknown bit
     assert sel_ex(4, N=64 * 2048, topk=3) == 2 and "group" in last()   # group: fused path only
     assert sel_ex(1, q=None) == 1 and "null" in last()           # checks as bsattn_select
+    assert sel_ex(0, nrand=3) == 1 and "nrand" in last()         # nrand > topk
+    assert sel_ex(1, nrand=1) == 2 and "causal" in last()
+    assert sel_ex(0, nrand=1, N=64 * 2048, topk=3) == 2 and "random" in last()
     L = bst.lib()
     st = L.bsattn_forward_ex(1, 1, 512, 2, 2, 64, 64, 2, 16, FAKE, FAKE, FAKE, FAKE, 0.125, None,
                              FAKE, None, None)

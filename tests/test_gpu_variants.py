@@ -159,3 +159,37 @@ def test_select_mid_range_blocks(opts):
         check_idx_causal(idx, S, topk)
     else:
         say("  ", check_idx(idx, S, topk))
+
+
+@pytest.mark.parametrize("group", [False, True])
+@pytest.mark.parametrize("nrand", [1, 3, 7])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_select_random_places(dtype, nrand, group):
+    """Random places: rows whose top topk - nrand is clear under the oracle's scores equal the
+    oracle's rows exactly (the draws depend only on the seed, the row and the non-top set);
+    every row is ascending, distinct and in range."""
+    B, N, Hq, Hkv, D, blk, topk = 2, 64 * 37, 4, 2, 64, 64, 7
+    seed = 0x1234_5678_9ABC_DEF0
+    say(f"[select random] dtype={dtype} nrand={nrand} group={group}")
+    q, k, _, _ = syn.iid_inputs(B, N, Hq, Hkv, D, dtype, index=26, device=DEV)
+    idx = bst.select(q, k, blk, topk, group=group, nrand=nrand, seed=seed).cpu().numpy()
+    S = O.block_scores(O.pool(stored_values(q), blk), O.pool(stored_values(k), blk))
+    if group:
+        assert np.array_equal(idx[:, 1::2], idx[:, ::2])
+        idx, S = idx[:, ::2], O.group_scores(S, Hkv)
+    ref = O.select_topk_random(S, topk, nrand, seed)
+    rows_g, rows_r, rows_s = idx.reshape(-1, topk), ref.reshape(-1, topk), S.reshape(-1, S.shape[-1])
+    assert np.all(np.diff(rows_g, axis=1) > 0) and rows_g.min() >= 0 and rows_g.max() < N // blk
+    kt = topk - nrand
+    if kt > 0:
+        sk, sk1 = O.kth_scores(rows_s, kt)
+        clear = (sk - sk1) > 1e-5 * np.maximum(np.abs(sk), np.abs(sk1))
+    else:
+        clear = np.ones(rows_s.shape[0], dtype=bool)
+    assert clear.mean() > 0.9
+    bad = np.nonzero(clear & ~np.all(rows_g == rows_r, axis=1))[0]
+    assert bad.size == 0, f"{bad.size} clear rows differ, first {bad[:5]}"
+    # a different seed changes some rows
+    other = bst.select(q, k, blk, topk, group=group, nrand=nrand, seed=seed + 1).cpu().numpy()
+    assert not np.array_equal(other, bst.select(q, k, blk, topk, group=group, nrand=nrand,
+                                                seed=seed).cpu().numpy())
