@@ -7,9 +7,9 @@
 // blocks, §3.1: GQA. The softmax is exact: it is evaluated online over the k selected key
 // blocks with a reference maximum and a normaliser in fp32.
 //
-// Work split: one work-group owns one query block (BLK rows) of one (batch, query head); each
-// of its waves owns QW query rows (QW = 64 for D = 64, 32 for D = 128), i.e. QW/32 column
-// tiles of the 32x32 MFMA. Per selected key block each wave computes
+// Work split: one work-group owns 64 query rows of one (batch, query head) — a whole 64-token
+// query block, or half of a 128-token one; each of its waves owns QW query rows (QW = 64 for
+// D = 64, 32 for D = 128), i.e. QW/32 column tiles of the 32x32 MFMA. Per selected key block each wave computes
 //   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q^T in registers)
 //   P^T = exp2(c*S^T - m)   (c = scale*log2(e), m = row reference, usually 0)
 //   O^T += V^T P^T (A = V^T via ds_read_b64_tr_b16 transpose reads of the row-major V tile,
@@ -89,22 +89,34 @@ __device__ __forceinline__ s16x4 ds_read_tr16(const char* lds_bytes) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_void*)(lds_bytes));
 }
 
-template <int D, int BLK, bool CAUSAL>
-__global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel(
+// Rows per tile and per work-group (HALF): a 128-token selection block can run as 64-row
+// halves — a work-group takes half of a query block and each selected block as two 64-key
+// units. Whole 128-row tiles need every operand of a block in registers at once (one wave per
+// SIMD), halves fetch every gathered tile twice; the launch takes halves when one (batch, KV
+// head)'s K and V stay in the last-level cache.
+template <int SB, bool HALF>
+constexpr int tile_rows() { return HALF ? 64 : SB; }
+
+template <int D, int SB, bool CAUSAL, bool HALF>
+__global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
     float* __restrict__ lse, int64_t N, int Hq, int Hkv, int nb, int topk, float c,
     uint32_t total_tiles) {
+  constexpr int BLK = tile_rows<SB, HALF>();  // rows of one tile and of this work-group
+  constexpr int UN = SB / BLK;                // tiles per selected block = work-groups per
+                                              // query block
   using C = Cfg<D, BLK>;
   __shared__ __attribute__((aligned(1024))) char Kl[C::TILE];   // [BLK][D] bf16, swizzled
   __shared__ __attribute__((aligned(1024))) char Vl[C::TILE];
 
-  // tile order: (b, kv head, head within group, query block); blocks reading the same K/V
-  // are consecutive and land on one XCD
+  // tile order: (b, kv head, head within group, query block, half); blocks reading the same
+  // K/V are consecutive and land on one XCD
   const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
   const int G = Hq / Hkv;
-  const int i = (int)(tile % nb);
-  uint32_t rest = tile / nb;
+  const int i = (int)((tile / UN) % nb);
+  const int hq = (int)(tile % UN);            // which BLK rows of the query block
+  uint32_t rest = tile / UN / nb;
   const int hh = (int)(rest % G);
   rest /= G;
   const int g = (int)(rest % Hkv);
@@ -117,7 +129,7 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
   const int64_t krs = (int64_t)Hkv * D;        // token stride of k/v
 
   // Q^T as B operands: lane holds q[row = QW*wave + 32*qc + l32][d = 16s + 8*half .. +7]
-  const int64_t qrow0 = (int64_t)b * N + (int64_t)i * BLK + C::QW * wave + l32;
+  const int64_t qrow0 = (int64_t)b * N + (int64_t)i * SB + BLK * hq + C::QW * wave + l32;
   bf16x8 qf[C::QC][C::NS];
 #pragma unroll
   for (int qc = 0; qc < C::QC; ++qc)
@@ -141,9 +153,9 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
     goff[x] = (uint32_t)((r * krs + swz(r, p) * 8) * 2);
   }
   bool bad = false;
-  auto tile_base = [&](int kb) -> int64_t {
+  auto tile_base = [&](int kb, int u) -> int64_t {   // unit u (BLK rows) of selected block kb
     if ((unsigned)kb >= klim) { bad = true; kb = 0; }
-    return (int64_t)kb * BLK * krs * 2;
+    return ((int64_t)kb * SB + BLK * u) * krs * 2;
   };
   // The transfers are issued from inline asm so that the compiler's wait-count pass, which
   // cannot tell the K and V buffers apart, does not add full vmcnt(0) waits before every LDS
@@ -206,17 +218,18 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
   for (int qc = 0; qc < C::QC; ++qc)
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) asm volatile("" ::"v"(qf[qc][s]));
-  int kb_cur = myidx[0];
+  int kb_cur = myidx[0], u_cur = 0;
   {
-    const int64_t tb = tile_base(kb_cur);
+    const int64_t tb = tile_base(kb_cur, 0);
     dma(kbase0 + tb, Kl);
     dma(vbase0 + tb, Vl);
   }
 
-  for (int t = 0; t < kcount; ++t) {
-    const bool more = t + 1 < kcount;
-    const int kb_next = more ? myidx[t + 1] : 0;
-    const int64_t tb_next = more ? tile_base(kb_next) : 0;
+  for (int t = 0; t < kcount * UN; ++t) {     // units: UN per selected block
+    const bool more = t + 1 < kcount * UN;
+    const int kb_next = more ? myidx[(t + 1) / UN] : 0;
+    const int u_next = (t + 1) % UN;
+    const int64_t tb_next = more ? tile_base(kb_next, u_next) : 0;
 
     // ---- K(t): wait for this wave's share (V(t) may still fly), then the whole work-group
     wait_vmcnt<C::DMA>();
@@ -250,8 +263,8 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
         for (int qc = 0; qc < C::QC; ++qc)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-            const int qry = C::QW * wave + 32 * qc + l32;
+            const int key = BLK * u_cur + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+            const int qry = BLK * hq + C::QW * wave + 32 * qc + l32;
             if (key > qry) sacc[kt][qc][r] = -__builtin_inff();
           }
     }
@@ -339,6 +352,7 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
           oacc[dt][qc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s][dt], pb, oacc[dt][qc], 0, 0, 0);
       }
     kb_cur = kb_next;
+    u_cur = u_next;
   }
 
   // epilogue: O = O^T / l, bf16, 4 consecutive d per store
@@ -363,21 +377,37 @@ __global__ __launch_bounds__(BLK / (D == 64 ? 64 : 32) * 64) void attn_bf16_kern
   }
 }
 
+template <int D, int BLK, bool HALF>
+hipError_t launch_tiles(int64_t B, int64_t N, int Hq, int Hkv, int topk, const void* q,
+                        const void* k, const void* v, const int32_t* idx, float c, void* out,
+                        float* lse, bool causal, hipStream_t stream) {
+  const int nb = (int)(N / BLK);
+  constexpr int TR = tile_rows<BLK, HALF>();
+  const uint32_t total = (uint32_t)(B * Hq * nb * (BLK / TR));
+  if (causal)
+    attn_bf16_kernel<D, BLK, true, HALF><<<total, Cfg<D, TR>::NT, 0, stream>>>(
+        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, lse, N,
+        Hq, Hkv, nb, topk, c, total);
+  else
+    attn_bf16_kernel<D, BLK, false, HALF><<<total, Cfg<D, TR>::NT, 0, stream>>>(
+        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, lse, N,
+        Hq, Hkv, nb, topk, c, total);
+  return hipGetLastError();
+}
+
+// K and V of one (batch, KV head) up to this size: 128-token blocks run as 64-row halves (the
+// gathered tiles, fetched twice, come from the 256 MB last-level cache); beyond, whole tiles.
+constexpr int64_t kHalfTileMaxBytes = 64ll << 20;
+
 template <int D, int BLK>
 hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int topk, const void* q, const void* k,
                   const void* v, const int32_t* idx, float c, void* out, float* lse,
                   bool causal, hipStream_t stream) {
-  const int nb = (int)(N / BLK);
-  const uint32_t total = (uint32_t)(B * Hq * nb);
-  if (causal)
-    attn_bf16_kernel<D, BLK, true><<<total, Cfg<D, BLK>::NT, 0, stream>>>(
-        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, lse, N,
-        Hq, Hkv, nb, topk, c, total);
-  else
-    attn_bf16_kernel<D, BLK, false><<<total, Cfg<D, BLK>::NT, 0, stream>>>(
-        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, lse, N,
-        Hq, Hkv, nb, topk, c, total);
-  return hipGetLastError();
+  if (BLK == 128 && N * D * 2 * 2 <= kHalfTileMaxBytes)
+    return launch_tiles<D, BLK, true>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal,
+                                      stream);
+  return launch_tiles<D, BLK, false>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal,
+                                     stream);
 }
 
 }  // namespace

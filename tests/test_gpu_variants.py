@@ -95,6 +95,35 @@ def test_forward_causal(shape, dtype):
             check_out(got, nomask, dtype)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [
+    # K and V of one (batch, KV head) above 64 MiB: 128-token blocks run as whole 128-row
+    # tiles, not as 64-row halves (the launch picks by that footprint)
+    (1, 128 * 1152, 2, 1, 128, 128, 9),
+    (1, 128 * 2112, 1, 1, 64, 128, 6),
+], ids=str)
+def test_forward_block128_whole_tiles(shape, causal):
+    B, N, Hq, Hkv, D, blk, topk = shape
+    assert N * D * 2 * 2 > 64 << 20
+    say(f"[block 128 whole tiles] shape={shape} causal={causal}")
+    q, k, v, ds = syn.iid_inputs(B, N, Hq, Hkv, D, "bf16", index=23, device=DEV)
+    ws = torch.empty(bst.select_workspace_bytes(B, N, Hq, Hkv, D, blk), dtype=torch.uint8,
+                     device=DEV)
+    idx = bst.select(q, k, blk, topk, causal=causal, workspace=ws)
+    out = bst.forward(q, k, v, idx, causal=causal)
+    torch.cuda.synchronize()
+    nb = N // blk
+    rows = syn.sample_rows(12, B * Hq * nb, 23) + [B * Hq * nb - 1]
+    picks = sorted({(r // (Hq * nb), (r // nb) % Hq, r % nb) for r in rows})
+    qo, ko, vo = to_f64(q), to_f64(k), to_f64(v)
+    gidx = idx.cpu().numpy()
+    ref = O.attend(qo, ko, vo, gidx, blk, 1 / math.sqrt(D), rows=picks, causal=causal)
+    got = out.float().cpu().numpy()
+    for (b, h, i) in picks:
+        sl = (b, slice(i * blk, (i + 1) * blk), h)
+        check_out(got[sl], ref[sl], "bf16")
+
+
 def test_causal_out_of_range_entry_poisons_its_rows():
     """A causal row naming a later block is not read: its query block's output is NaN."""
     say("[causal later block]")
