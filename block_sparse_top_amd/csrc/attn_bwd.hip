@@ -337,7 +337,8 @@ __global__ __launch_bounds__(128) void dkv_kernel(
   constexpr int NS = D / 16, NDT = D / 32;
   __shared__ __attribute__((aligned(16))) char Qt[kBlk * D * 2];
   __shared__ __attribute__((aligned(16))) char Gt[kBlk * D * 2];   // dO tile
-  __shared__ float l2s[kBlk], dds[kBlk];
+  __shared__ __attribute__((aligned(16))) float l2s[kBlk];
+  __shared__ __attribute__((aligned(16))) float dds[kBlk];
   const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
   const int j = (int)(tile % nb);
   const int bg = (int)(tile / nb);
@@ -406,12 +407,18 @@ __global__ __launch_bounds__(128) void dkv_kernel(
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qq = 32 * qt + 8 * (r >> 2) + 4 * half + (r & 3);
-        float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[qt][r], c, -l2s[qq]));
-        if (own && kloc > qq) pp = 0.f;
-        sa[qt][r] = pp;                                   // P
-        dpa[qt][r] = pp * (dpa[qt][r] - dds[qq]);         // dS
+      for (int r4 = 0; r4 < 4; ++r4) {
+        // registers 4*r4 .. 4*r4+3 hold rows q0 .. q0+3: one 16-byte read of each statistic
+        const int q0 = 32 * qt + 8 * r4 + 4 * half;
+        const f32x4 l4 = *(const f32x4*)(l2s + q0), d4 = *(const f32x4*)(dds + q0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * r4 + u;
+          float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[qt][r], c, -l4[u]));
+          if (own && kloc > q0 + u) pp = 0.f;
+          sa[qt][r] = pp;                                 // P
+          dpa[qt][r] = pp * (dpa[qt][r] - d4[u]);         // dS
+        }
       }
     // dV^T += dO^T P, dK^T += Q^T dS (k-steps over the 64 queries)
 #pragma unroll
