@@ -55,6 +55,12 @@ the design notes of the repository):
       ascending order, m_p = nb - (k - r) - p, x = element row * 2^16 + p of the SplitMix64
       sequence (Steele, Lea, Flood, OOPSLA 2014) seeded with the caller's seed, row the
       row's position (batch, head, query block) in C order.
+  R28 overlapping key blocks (NEXT N3; the MSA page's §5.3 remedy for block-boundary effects,
+      overlap ratio 0.25): key block j holds the b tokens from j*s on, cut at N, with the
+      stride s = b - overlap*b (48 for b = 64, 96 for b = 128), and key blocks follow until one
+      reaches the last token; query blocks stay the b-token partition. Pooling, scores and
+      top-k run over the key blocks; a query block attends to the union of the tokens of its
+      selected key blocks, each token once. The causal rule (R20) is not defined for them.
   R25 backward (the MSA page's §4.1 checks that back-propagation is complete; the
       SparseFormer page recommends the method for training large models, "千亿参数大模型训练"):
       gradients of the gathered-block attention with the selection held fixed (top-k is
@@ -148,6 +154,44 @@ def pool_max(x: np.ndarray, block: int) -> np.ndarray:
         raise ValueError("N must be a multiple of the block size")
     nb = N // block
     return x.reshape(B, nb, block, H, D).max(axis=2).transpose(0, 2, 1, 3)
+
+
+def key_block_ranges(N: int, block: int, stride: int):
+    """Token ranges [start, end) of overlapping key blocks [R28].
+
+    Key block j starts at token j * stride and holds `block` tokens, cut at N; blocks follow
+    until one ends at N. stride == block gives the plain partition of `pool`. The stride
+    lies in [block/2, block], so only neighbouring key blocks share tokens.
+    """
+    if not (0 < stride <= block and 2 * stride >= block):
+        raise ValueError("the key stride must lie in [block/2, block]")
+    ranges = []
+    start = 0
+    while N > 0:
+        end = min(start + block, N)
+        ranges.append((start, end))
+        if end == N:
+            break
+        start += stride
+    return ranges
+
+
+def pool_key_blocks(x: np.ndarray, block: int, stride: int, pooling: str = "mean") -> np.ndarray:
+    """Pooled overlapping key blocks [R28; R21 for "max"]: the mean (or elementwise maximum)
+    of each key block's own tokens; a shorter last block is pooled over the tokens it has.
+
+    x: [B, N, H, D] float64 -> [B, H, nw, D] float64, nw = len(key_block_ranges(...)).
+    """
+    reduce = np.mean if pooling == "mean" else np.max
+    parts = [reduce(x[:, s:e], axis=1) for s, e in key_block_ranges(x.shape[1], block, stride)]
+    return np.stack(parts, axis=2)
+
+
+def union_tokens(sel, N: int, block: int, stride: int) -> np.ndarray:
+    """Ascending token positions covered by the key blocks `sel` (entries -1 skipped), each
+    position once [R28]."""
+    ranges = key_block_ranges(N, block, stride)
+    return np.unique(np.concatenate([np.arange(*ranges[j]) for j in sel if j >= 0]))
 
 
 def kv_head(h: int, Hq: int, Hkv: int) -> int:
@@ -268,27 +312,33 @@ def kth_scores(S: np.ndarray, k: int):
 
 
 def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, block: int,
-           scale: float, rows=None, causal: bool = False) -> np.ndarray:
+           scale: float, rows=None, causal: bool = False, stride=None) -> np.ndarray:
     """Exact softmax attention of every query block over its selected key blocks
-    [SF step 3; MSA §2.1, §2.2; R8, R10; R20 when causal].
+    [SF step 3; MSA §2.1, §2.2; R8, R10; R20 when causal; R28 with a key stride].
 
     q [B, N, Hq, D], k/v [B, N, Hkv, D] float64; idx [B, Hq, nb, topk] (a set of key
     blocks per query block and head; entries -1 are unused places). For query t of block i
     the keys are the union of blocks idx[b,h,i,:] of KV head kv(h); weights
-    softmax(scale * q_t . k_u); causal: only keys u <= t.
+    softmax(scale * q_t . k_u); causal: only keys u <= t. stride: the key blocks overlap
+    (`key_block_ranges`) and each token of the union counts once.
     rows: optional list of (b, h, i) to compute; the others are left NaN.
     Returns out [B, N, Hq, D] float64.
     """
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
     nb = N // block
+    if stride is not None and causal:
+        raise ValueError("overlapping key blocks have no causal rule")
     out = np.full(q.shape, np.nan, dtype=np.float64)
     if rows is None:
         rows = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(nb)]
     for (b, h, i) in rows:
         g = kv_head(h, Hq, Hkv)
-        tok = np.concatenate([np.arange(j * block, (j + 1) * block)
-                              for j in idx[b, h, i] if j >= 0])
+        if stride is None:
+            tok = np.concatenate([np.arange(j * block, (j + 1) * block)
+                                  for j in idx[b, h, i] if j >= 0])
+        else:
+            tok = union_tokens(idx[b, h, i], N, block, stride)
         Qi = q[b, i * block:(i + 1) * block, h, :]           # [block, D]
         Ku = k[b, tok, g, :]                                 # [keys, D]
         Vu = v[b, tok, g, :]
@@ -356,23 +406,30 @@ def dense_attention(q, k, v, scale, causal: bool = False) -> np.ndarray:
     return out
 
 
-def masked_attention_bruteforce(q, k, v, idx, block, scale, causal: bool = False) -> np.ndarray:
+def masked_attention_bruteforce(q, k, v, idx, block, scale, causal: bool = False,
+                                stride=None) -> np.ndarray:
     """Softmax(Mask(scale * Q K^T)) V with an explicit N x N token mask [MSA §2.1].
 
     M[t, u] is true when key u's block is among the blocks selected for query t's
-    block (and, causal, u <= t); masked positions get -inf before the softmax. Tiny sizes
-    only.
+    block (and, causal, u <= t); with a key stride [R28], when u lies in the token range of
+    a selected key block. Masked positions get -inf before the softmax. Tiny sizes only.
     """
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
     out = np.empty(q.shape, dtype=np.float64)
     tb = np.arange(N) // block
+    ranges = key_block_ranges(N, block, stride) if stride is not None else None
     for b in range(B):
         for h in range(Hq):
             g = kv_head(h, Hq, Hkv)
             M = np.zeros((N, N), dtype=bool)
             for t in range(N):
-                M[t] = np.isin(tb, idx[b, h, tb[t]])
+                if ranges is None:
+                    M[t] = np.isin(tb, idx[b, h, tb[t]])
+                else:
+                    for j in idx[b, h, tb[t]]:
+                        if j >= 0:
+                            M[t, ranges[j][0]:ranges[j][1]] = True
                 if causal:
                     M[t, t + 1:] = False
             z = np.where(M, scale * (q[b, :, h, :] @ k[b, :, g, :].T), -np.inf)
@@ -483,15 +540,22 @@ def decode_attend(q_tok, k_cache, v_cache, idx, lens, block: int, scale: float) 
 
 
 def select(q, k, block: int, topk: int, causal: bool = False, pooling: str = "mean",
-           group: bool = False, nrand: int = 0, seed: int = 0) -> np.ndarray:
+           group: bool = False, nrand: int = 0, seed: int = 0, stride=None) -> np.ndarray:
     """Steps 1-2 [SF]: pool q and k, score the blocks, keep the top-k per row.
 
     causal [R20], pooling "mean" [SF] or "max" [R21], group: one selection per KV head
     group, repeated for each of its query heads [R22], nrand random places [R27] (not with
-    causal). Returns [B, Hq, nb, topk].
+    causal), stride: overlapping key blocks [R28] (not with causal). Returns
+    [B, Hq, nb, topk] (entries index key blocks).
     """
     pf = pool if pooling == "mean" else pool_max
-    S = block_scores(pf(q, block), pf(k, block))
+    if stride is None:
+        kbar = pf(k, block)
+    else:
+        if causal:
+            raise ValueError("overlapping key blocks have no causal rule")
+        kbar = pool_key_blocks(k, block, stride, pooling)
+    S = block_scores(pf(q, block), kbar)
     Hq, Hkv = q.shape[2], k.shape[2]
     if group:
         S = group_scores(S, Hkv)

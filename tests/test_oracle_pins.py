@@ -472,12 +472,65 @@ def check_random_fill(o=O):
     assert chi2 < 16.0, (counts, chi2)          # 2 degrees of freedom: p ~ 3e-4
 
 
+def check_overlap(o=O):
+    """Overlapping key blocks [R28]: block ranges against the closed form
+    nw = ceil((N - b) / s) + 1 with starts j*s; hand-computed pooled values; stride == block
+    reduces to the plain partition; union attention against the explicit token mask, against
+    dense attention when every key block is chosen, and against dense attention over one
+    contiguous token range when two neighbouring blocks are chosen; the selection finds a
+    planted key block that only the overlapping geometry has."""
+    assert o.key_block_ranges(8, 4, 3) == [(0, 4), (3, 7), (6, 8)]
+    for N, b, s in ((64, 16, 12), (256, 64, 48), (8192, 64, 48), (8192, 128, 96), (128, 64, 32),
+                    (192, 64, 40), (64, 64, 64)):
+        rg = o.key_block_ranges(N, b, s)
+        assert len(rg) == -(-(N - b) // s) + 1
+        assert [a for a, _ in rg] == [j * s for j in range(len(rg))]
+        assert all(e == min(a + b, N) for a, e in rg) and rg[-1][1] == N
+    x = np.arange(8.0).reshape(1, 8, 1, 1)
+    assert o.pool_key_blocks(x, 4, 3).ravel().tolist() == [1.5, 4.5, 6.5]
+    assert o.pool_key_blocks(x, 4, 3, "max").ravel().tolist() == [3.0, 6.0, 7.0]
+    q, k, v = rand_qkv(2, 96, 4, 2, 8, seed=31)
+    blk = 16
+    assert np.allclose(o.pool_key_blocks(k, blk, blk), o.pool(k, blk), rtol=0, atol=1e-15)
+    assert np.array_equal(o.pool_key_blocks(k, blk, blk, "max"), o.pool_max(k, blk))
+    assert np.array_equal(o.select(q, k, blk, 3, stride=blk), o.select(q, k, blk, 3))
+    idx = o.select(q, k, blk, 3)
+    assert np.allclose(o.attend(q, k, v, idx, blk, 0.3, stride=blk),
+                       o.attend(q, k, v, idx, blk, 0.3), rtol=0, atol=1e-13)
+    stride = 12
+    nw = len(o.key_block_ranges(96, blk, stride))              # 8 key blocks for 6 query blocks
+    assert nw == 8
+    r_ = rng(32)
+    idx = np.sort(np.stack([np.stack([np.stack([r_.choice(nw, 3, replace=False) for _ in range(6)])
+                                      for _ in range(4)]) for _ in range(2)]), axis=-1)
+    got = o.attend(q, k, v, idx, blk, 0.3, stride=stride)
+    assert np.allclose(got, o.masked_attention_bruteforce(q, k, v, idx, blk, 0.3, stride=stride),
+                       rtol=0, atol=1e-13)
+    every = np.broadcast_to(np.arange(nw), (2, 4, 6, nw))
+    assert np.allclose(o.attend(q, k, v, every, blk, 0.3, stride=stride),
+                       o.dense_attention(q, k, v, 0.3), rtol=0, atol=1e-13)
+    pair = np.broadcast_to(np.array([2, 3]), (2, 4, 6, 2))     # tokens [24, 52): one range
+    rng_ = slice(2 * stride, 3 * stride + blk)
+    ref = o.dense_attention(q, k[:, rng_], v[:, rng_], 0.3)
+    assert np.allclose(o.attend(q, k, v, pair, blk, 0.3, stride=stride), ref, rtol=0, atol=1e-13)
+    # planted: only the tokens of key block 5 (60..75, across query blocks 3 and 4) point
+    # along d = 0, the queries too; block 5 must rank first everywhere
+    kp = r_.standard_normal((1, 96, 1, 8)) * 0.01
+    kp[0, 60:76, 0, 0] += 1.0
+    qp = np.zeros((1, 96, 2, 8))
+    qp[..., 0] = 1.0
+    top = o.select(qp, kp, blk, 1, stride=stride)
+    assert np.all(top == 5), top.ravel()
+    top2 = o.select(qp, kp, blk, 2, stride=stride, pooling="max")
+    assert np.all(top2 == [4, 5]) or np.all(top2 == [5, 6]), top2[0, 0, 0]
+
+
 ALL_CHECKS = [check_bf16_widen, check_e4m3, check_pool, check_scores, check_select_vs_sort,
               check_select_special, check_dense_limit, check_bruteforce, check_ties_and_zero,
               check_invariants, check_gqa, check_batched, check_causal_select,
               check_causal_dense_limit, check_causal_bruteforce, check_pool_max,
               check_group_select, check_backward_autograd, check_backward_fd_and_invariants,
-              check_lse, check_decode, check_random_fill]
+              check_lse, check_decode, check_random_fill, check_overlap]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -518,10 +571,10 @@ def test_rejects():
 
 # ---------------------------------------------------- planted mistakes (CPU)
 
-def _strict_causal(q, k, v, idx, blk, scale, rows=None, causal=False):
+def _strict_causal(q, k, v, idx, blk, scale, rows=None, causal=False, stride=None):
     """attend with the causal mask u < t (a key never sees itself): a planted mistake."""
     if not causal:
-        return O.attend(q, k, v, idx, blk, scale, rows)
+        return O.attend(q, k, v, idx, blk, scale, rows, stride=stride)
     out = O.attend(q, k, v, idx, blk, scale, rows, causal=True)
     B, N, Hq, D = q.shape
     # recompute rows t > 0 of every block without the diagonal term
@@ -620,7 +673,8 @@ def _mutant(**repl):
     m = Mutant(**repl)
     for name in ("select", "block_sparse_attention", "block_scores", "attend", "attend_batched",
                  "dense_attention", "masked_attention_bruteforce", "select_topk_causal",
-                 "decode_select", "decode_attend", "select_topk_random"):
+                 "decode_select", "decode_attend", "select_topk_random", "pool_key_blocks",
+                 "union_tokens"):
         if name not in repl:
             setattr(m, name, _rebind(getattr(O, name), m))
     return m
@@ -637,19 +691,20 @@ MUTANTS = {
         select_topk=lambda S, k: (S.shape[-1] - 1 - O.select_topk(S[..., ::-1], k))[..., ::-1]),
     "select_smallest": dict(select_topk=lambda S, k: O.select_topk(-S, k)),
     "attend_no_max_shift_sign": dict(
-        attend=lambda q, k, v, idx, blk, scale, rows=None, causal=False:
-        O.attend(q, k, v, idx, blk, -scale, rows, causal)),
+        attend=lambda q, k, v, idx, blk, scale, rows=None, causal=False, stride=None:
+        O.attend(q, k, v, idx, blk, -scale, rows, causal, stride)),
     "attend_drops_last_block": dict(
-        attend=lambda q, k, v, idx, blk, scale, rows=None, causal=False:
-        O.attend(q, k, v, idx[..., :-1] if idx.shape[-1] > 1 else idx, blk, scale, rows, causal)),
+        attend=lambda q, k, v, idx, blk, scale, rows=None, causal=False, stride=None:
+        O.attend(q, k, v, idx[..., :-1] if idx.shape[-1] > 1 else idx, blk, scale, rows, causal,
+                 stride)),
     "causal_diagonal_not_forced": dict(
         select_topk_causal=lambda S, k: np.stack(
             [np.concatenate([O.select_topk(S[..., i, :i + 1], min(k, i + 1)),
                              np.full(S.shape[:-2] + (k - min(k, i + 1),), -1)], axis=-1)
              for i in range(S.shape[-1])], axis=-2)),
     "causal_mask_excludes_self": dict(
-        attend=lambda q, k, v, idx, blk, scale, rows=None, causal=False:
-        _strict_causal(q, k, v, idx, blk, scale, rows, causal)),
+        attend=lambda q, k, v, idx, blk, scale, rows=None, causal=False, stride=None:
+        _strict_causal(q, k, v, idx, blk, scale, rows, causal, stride)),
     "pool_max_is_min": dict(pool_max=lambda x, b: -O.pool_max(-x, b)),
     "backward_without_row_term": dict(
         attend_backward=lambda q, k, v, idx, blk, scale, dout, causal=False:
@@ -668,6 +723,17 @@ MUTANTS = {
     "e4m3_bias_8": dict(decode_e4m3=lambda c: O.decode_e4m3(c) / 2),
     "bf16_low_bits": dict(widen_bf16_bits=lambda b: np.asarray(b, dtype=np.uint16).astype(np.float64)),
     "topk_round_not_truncate": dict(topk_count=lambda r, nb: int(round(r * nb))),
+    "overlap_short_block_dropped": dict(
+        key_block_ranges=lambda N, b, s: [r for r in O.key_block_ranges(N, b, s)
+                                          if r[1] - r[0] == b]),
+    "overlap_pool_divides_by_block": dict(
+        pool_key_blocks=lambda x, b, s, pooling="mean": (
+            O.pool_key_blocks(x, b, s, pooling) if pooling != "mean" else np.stack(
+                [x[:, a:e].sum(axis=1) / b for a, e in O.key_block_ranges(x.shape[1], b, s)],
+                axis=2))),
+    "overlap_shared_tokens_twice": dict(
+        union_tokens=lambda sel, N, b, s: np.concatenate(
+            [np.arange(*O.key_block_ranges(N, b, s)[j]) for j in sel if j >= 0])),
 }
 
 
