@@ -39,6 +39,9 @@ def parse():
                    help="causal variant (own block forced, earlier blocks only, masked own block)")
     p.add_argument("--pooling", choices=("mean", "max"), default="mean")
     p.add_argument("--group", action="store_true", help="one selection per KV head group")
+    p.add_argument("--key-stride", type=int, default=0,
+                   help="overlapping key blocks starting every KEY_STRIDE tokens (0: block; "
+                        "the overlap ratio 0.25 is 3/4 of the block)")
     p.add_argument("--backward", action="store_true",
                    help="also time bsattn_backward (bf16, block 64) on the same selection")
     p.add_argument("--decode", action="store_true",
@@ -70,7 +73,7 @@ def traffic_per_launch():
 
 
 def cpu_baseline(w, q, k, v, ds, max_batches, budget_s=10.0, causal=False, pooling="mean",
-                 group=False):
+                 group=False, key_stride=0):
     """The fp64 oracle, as it stands, on batch elements 0, 1, ... of the workload until
     `budget_s` seconds of CPU work are done (at least one, at most `max_batches`)."""
     import numpy as np
@@ -90,15 +93,21 @@ def cpu_baseline(w, q, k, v, ds, max_batches, budget_s=10.0, causal=False, pooli
             return c.view(torch.uint8).numpy(), "fp8"
         return c.numpy(), "f32"
 
-    topk = O.topk_count(w.ratio, w.nb)
+    nkb = len(O.key_block_ranges(w.N, w.block, key_stride)) if key_stride else w.nb
+    topk = O.topk_count(w.ratio, nkb)
     dt_s, batches = 0.0, 0
     while batches < max_batches and (batches == 0 or dt_s < budget_s):
         sl = slice(batches, batches + 1)
         (qh, dt), (kh, _), (vh, _) = host(q[sl]), host(k[sl]), host(v[sl])
         t0 = time.perf_counter()
         qo, ko, vo = O.widen(qh, dt, ds[0]), O.widen(kh, dt, ds[1]), O.widen(vh, dt, ds[2])
-        idx = O.select(qo, ko, w.block, topk, causal=causal, pooling=pooling, group=group)
-        O.attend_batched(qo, ko, vo, idx, w.block, 1.0 / math.sqrt(w.D), causal=causal)
+        stride = key_stride or None
+        idx = O.select(qo, ko, w.block, topk, causal=causal, pooling=pooling, group=group,
+                       stride=stride)
+        if stride:
+            O.attend(qo, ko, vo, idx, w.block, 1.0 / math.sqrt(w.D), stride=stride)
+        else:
+            O.attend_batched(qo, ko, vo, idx, w.block, 1.0 / math.sqrt(w.D), causal=causal)
         dt_s += time.perf_counter() - t0
         batches += 1
     return {"value": batches * w.N / dt_s, "unit": "tokens/s", "cores": int(threads),
@@ -113,8 +122,8 @@ def time_backward(args, w, q, k, v, idx, out, topk, scale, flags, L, P, sp, stre
     import torch
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=q.device)
     dcode = 1
-    st = L.bsattn_forward_ex(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, P(q), P(k),
-                             P(v), P(idx), scale, None, P(out), P(lse), sp)
+    st = L.bsattn_forward_ex(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, 0, P(q),
+                             P(k), P(v), P(idx), scale, None, P(out), P(lse), sp)
     assert st == 0, L.bsattn_last_error()
     g = torch.Generator(device=q.device).manual_seed(7)
     dout = torch.randn(out.shape, generator=g, device=q.device).to(torch.bfloat16)
@@ -229,9 +238,13 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     q, k, v, ds, _ = syn.workload_inputs(w, device=dev)
-    topk = int(w.ratio * w.nb)
+    ks = args.key_stride or w.block
+    if ks != w.block and (args.causal or args.backward):
+        sys.exit("bench.py: overlapping key blocks run the non-causal forward only")
+    nkb = bst.key_blocks(w.N, w.block, ks)
+    topk = int(w.ratio * nkb)                  # k = int(topk_ratio * number of key blocks)
     scale = 1.0 / math.sqrt(w.D)
-    ws = torch.empty(bst.select_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.block),
+    ws = torch.empty(bst.select_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.block, ks),
                      dtype=torch.uint8, device=dev)
     idx = torch.empty((w.B, w.Hq, w.nb, topk), dtype=torch.int32, device=dev)
     odt = torch.float32 if w.dtype == "f32" else torch.bfloat16
@@ -251,12 +264,12 @@ def main():
 
     def do_select():
         st = L.bsattn_select_ex(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, 0, 0,
-                                P(q), P(k), P(idx), P(ws), ws.numel(), sp)
+                                ks, P(q), P(k), P(idx), P(ws), ws.numel(), sp)
         assert st == 0, L.bsattn_last_error()
 
     def do_forward():
-        st = L.bsattn_forward_ex(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, P(q),
-                                 P(k), P(v), P(idx), scale, dsc, P(out), None, sp)
+        st = L.bsattn_forward_ex(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, ks,
+                                 P(q), P(k), P(v), P(idx), scale, dsc, P(out), None, sp)
         assert st == 0, L.bsattn_last_error()
 
     for _ in range(args.warmup):
@@ -285,15 +298,23 @@ def main():
     # blocks, its own one in full although half of it is masked)
     blocks = sum(min(topk, i + 1) for i in range(w.nb)) if args.causal else w.nb * topk
     flops = 4.0 * w.B * w.Hq * w.block * (blocks * w.block) * w.D
+    if ks != w.block:
+        # overlapping key blocks: the keys attended are the union of each row's blocks (the
+        # rows are ascending; a pair j-1, j shares block - ks tokens, the last block is short)
+        adj = (idx[..., 1:] == idx[..., :-1] + 1).sum().item()
+        last = (idx == nkb - 1).sum().item()
+        keys = (w.B * w.Hq * w.nb * topk * w.block - adj * (w.block - ks)
+                - last * (w.block - (w.N - (nkb - 1) * ks)))
+        flops = 4.0 * w.block * keys * w.D
     achieved = flops / (fwd_ms / 1e3) / 1e12
     peak = PEAK[w.dtype]
     ebytes = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
     sel_bytes = (w.B * w.N * (w.Hq + w.Hkv) * w.D * ebytes            # read q, k
-                 + 2 * 4 * w.B * w.nb * (w.Hq + w.Hkv) * w.D          # pooled write + read
+                 + 2 * 4 * w.B * (w.nb * w.Hq + nkb * w.Hkv) * w.D    # pooled write + read
                  + 4 * w.B * w.Hq * w.nb * topk)                      # idx write
     if w.nb > 1024:                                                   # score matrix write + read
         sel_bytes += 2 * 4 * w.B * w.Hq * w.nb * w.nb
-    plain = not (args.causal or args.group or args.pooling == "max")
+    plain = not (args.causal or args.group or args.pooling == "max" or ks != w.block)
     tr = traffic_per_launch() if plain and w.name == "sparseformer_n8192_bf16" else None
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -304,7 +325,8 @@ def main():
                    "block": w.block, "topk": topk, "parallelism": "single GPU",
                    **({"causal": True} if args.causal else {}),
                    **({"pooling": "max"} if args.pooling == "max" else {}),
-                   **({"group_select": True} if args.group else {})},
+                   **({"group_select": True} if args.group else {}),
+                   **({"key_stride": ks, "key_blocks": nkb} if ks != w.block else {})},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": tr, "kernel": f"attn_{w.dtype}_kernel",
@@ -319,7 +341,8 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, ds, args.cpu_batches or w.B,
                                            causal=args.causal, pooling=args.pooling,
-                                           group=args.group)
+                                           group=args.group,
+                                           key_stride=ks if ks != w.block else 0)
     print(json.dumps(rec), flush=True)
 
 

@@ -5,5 +5,6 @@ Importing the package does not load the library; the first call does, and raises
 it is not built.
 """
 from .bsattn import (CAUSAL, GROUP_SELECT, POOL_MAX, BsattnError,  # noqa: F401
-                     backward, block_sparse_attention, decode, decode_pool, forward, lib,
+                     backward, block_sparse_attention, decode, decode_pool, forward, key_blocks,
+                     lib,
                      select, select_workspace_bytes, topk_count)

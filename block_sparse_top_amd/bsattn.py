@@ -62,10 +62,14 @@ def lib() -> ctypes.CDLL:
     u32 = ctypes.c_uint
     L.bsattn_select_ex.restype = i32
     L.bsattn_select_ex.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, u32, i32,
-                                   ctypes.c_uint64, vp, vp, vp, vp, sz, vp]
+                                   ctypes.c_uint64, i32, vp, vp, vp, vp, sz, vp]
     L.bsattn_forward_ex.restype = i32
-    L.bsattn_forward_ex.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, u32, vp, vp, vp, vp,
-                                    ctypes.c_float, ctypes.POINTER(ctypes.c_float), vp, vp, vp]
+    L.bsattn_forward_ex.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, u32, i32, vp, vp, vp,
+                                    vp, ctypes.c_float, ctypes.POINTER(ctypes.c_float), vp, vp, vp]
+    L.bsattn_key_blocks.restype = i64
+    L.bsattn_key_blocks.argtypes = [i64, i32, i32]
+    L.bsattn_select_workspace_bytes_ex.restype = sz
+    L.bsattn_select_workspace_bytes_ex.argtypes = [i64, i64, i32, i32, i32, i32, i32]
     L.bsattn_backward_workspace_bytes.restype = sz
     L.bsattn_backward_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32, i32]
     L.bsattn_backward.restype = i32
@@ -129,48 +133,64 @@ def topk_count(topk_ratio: float, num_blocks: int) -> int:
     return int(topk_ratio * num_blocks)
 
 
-def select_workspace_bytes(B, N, Hq, Hkv, D, block) -> int:
-    return int(lib().bsattn_select_workspace_bytes(B, N, Hq, Hkv, D, block))
+def select_workspace_bytes(B, N, Hq, Hkv, D, block, key_stride: int = 0) -> int:
+    return int(lib().bsattn_select_workspace_bytes_ex(B, N, Hq, Hkv, D, block, key_stride))
+
+
+def key_blocks(N: int, block: int, key_stride: int = 0) -> int:
+    """Key blocks of N tokens at key_stride (0: block): the plain N // block, or the
+    overlapping blocks starting every key_stride tokens, the last one ending at token N."""
+    n = int(lib().bsattn_key_blocks(N, block, key_stride))
+    if n < 0:
+        raise BsattnError(1, lib().bsattn_last_error().decode())
+    return n
 
 
 def select(q, k, block: int, topk: int, *, causal: bool = False, pooling: str = "mean",
-           group: bool = False, nrand: int = 0, seed: int = 0, return_pooled: bool = False,
-           workspace=None):
+           group: bool = False, nrand: int = 0, seed: int = 0, key_stride: int = 0,
+           return_pooled: bool = False, workspace=None):
     """Top-k key blocks per (batch, query head, query block): int32 [B, Hq, nb, topk].
 
     causal: own block forced, earlier blocks only, unused places -1; pooling "max": in-block
     maximum instead of the mean; group: one selection per KV head for all its query heads;
-    nrand, seed: nrand of the topk places drawn at random from the non-top blocks.
+    nrand, seed: nrand of the topk places drawn at random from the non-top blocks;
+    key_stride: overlapping key blocks starting every key_stride tokens (0: block), the
+    entries then index those key blocks (`key_blocks`).
     With return_pooled, also returns the pooled q and k (fp32 [B, Hq, nb, D] and
-    [B, Hkv, nb, D]; for fp8 inputs without the per-tensor descale).
+    [B, Hkv, key blocks, D]; for fp8 inputs without the per-tensor descale).
     """
     flags = _flags(causal, pooling, group)
     B, N, Hq, Hkv, D = _shapes(q, k)
     nb = N // block if block > 0 else 0
     idx = torch.empty((B, Hq, nb, max(topk, 0)), dtype=torch.int32, device=q.device)
-    nbytes = select_workspace_bytes(B, N, Hq, Hkv, D, block) if block > 0 and N % block == 0 else 0
+    valid = block > 0 and N % block == 0 and (key_stride == 0 or block <= 2 * key_stride <= 2 * block)
+    nbytes = select_workspace_bytes(B, N, Hq, Hkv, D, block, key_stride) if valid else 0
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     with torch.cuda.device(q.device):
         _check(lib().bsattn_select_ex(_DTYPES[q.dtype], B, N, Hq, Hkv, D, block, topk, flags,
-                                      int(nrand), int(seed) & ((1 << 64) - 1), _ptr(q), _ptr(k),
-                                      _ptr(idx), _ptr(workspace), workspace.numel(),
-                                      _stream(q.device)))
+                                      int(nrand), int(seed) & ((1 << 64) - 1), int(key_stride),
+                                      _ptr(q), _ptr(k), _ptr(idx), _ptr(workspace),
+                                      workspace.numel(), _stream(q.device)))
     if not return_pooled:
         return idx
+    nkb = key_blocks(N, block, key_stride)
     qb_bytes = (B * Hq * nb * D * 4 + 255) // 256 * 256
     qbar = workspace[: B * Hq * nb * D * 4].view(torch.float32).view(B, Hq, nb, D)
-    kbar = workspace[qb_bytes: qb_bytes + B * Hkv * nb * D * 4].view(torch.float32).view(B, Hkv, nb, D)
+    kbar = workspace[qb_bytes: qb_bytes + B * Hkv * nkb * D * 4].view(torch.float32).view(
+        B, Hkv, nkb, D)
     return idx, qbar, kbar
 
 
 def forward(q, k, v, idx, scale: float | None = None, descales=(1.0, 1.0, 1.0), out=None, *,
-            causal: bool = False, return_lse: bool = False):
+            causal: bool = False, key_stride: int = 0, return_lse: bool = False):
     """Attention of every query block over its selected key blocks: [B, N, Hq, D].
 
     Output dtype: fp32 for fp32 inputs, bf16 for bf16 and fp8 inputs. causal: rows in the
-    form `select(..., causal=True)` writes; keys after the query are masked. return_lse: also
-    the rows' natural log-sum-exp, fp32 [B, Hq, N] (the input `backward` needs).
+    form `select(..., causal=True)` writes; keys after the query are masked. key_stride: idx
+    names overlapping key blocks (as `select(..., key_stride=...)` writes them) and each query
+    block attends to the union of their tokens. return_lse: also the rows' natural
+    log-sum-exp, fp32 [B, Hq, N] (the input `backward` needs).
     """
     B, N, Hq, Hkv, D = _shapes(q, k, v)
     if idx.dim() != 4 or idx.dtype != torch.int32 or not idx.is_contiguous() or not idx.is_cuda:
@@ -191,7 +211,8 @@ def forward(q, k, v, idx, scale: float | None = None, descales=(1.0, 1.0, 1.0), 
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if return_lse else None
     with torch.cuda.device(q.device):
         _check(lib().bsattn_forward_ex(_DTYPES[q.dtype], B, N, Hq, Hkv, D, block, topk,
-                                       CAUSAL if causal else 0, _ptr(q), _ptr(k), _ptr(v),
+                                       CAUSAL if causal else 0, int(key_stride), _ptr(q),
+                                       _ptr(k), _ptr(v),
                                        _ptr(idx), scale, ds, _ptr(out), _ptr(lse),
                                        _stream(q.device)))
     return (out, lse) if return_lse else out
@@ -230,12 +251,19 @@ def backward(q, k, v, idx, out, dout, lse, scale: float | None = None, *, causal
 
 def block_sparse_attention(q, k, v, block_size: int = 64, topk_ratio: float = 0.3,
                            descales=(1.0, 1.0, 1.0), return_idx: bool = False, *,
-                           causal: bool = False, pooling: str = "mean", group: bool = False):
-    """The whole method: select, then attend with scale 1/sqrt(D)."""
+                           causal: bool = False, pooling: str = "mean", group: bool = False,
+                           overlap_ratio: float = 0.0):
+    """The whole method: select, then attend with scale 1/sqrt(D).
+
+    overlap_ratio: neighbouring key blocks share round(overlap_ratio * block_size) tokens
+    (the MSA page's §5.3 suggests 0.25); top-k then counts int(topk_ratio * key blocks).
+    """
     B, N, Hq, Hkv, D = _shapes(q, k, v)
-    topk = topk_count(topk_ratio, N // block_size)
-    idx = select(q, k, block_size, topk, causal=causal, pooling=pooling, group=group)
-    out = forward(q, k, v, idx, 1.0 / math.sqrt(D), descales, causal=causal)
+    ks = block_size - int(round(overlap_ratio * block_size))
+    topk = topk_count(topk_ratio, key_blocks(N, block_size, ks) if N else 0)
+    idx = select(q, k, block_size, topk, causal=causal, pooling=pooling, group=group,
+                 key_stride=ks)
+    out = forward(q, k, v, idx, 1.0 / math.sqrt(D), descales, causal=causal, key_stride=ks)
     return (out, idx) if return_idx else out
 
 

@@ -36,8 +36,18 @@ bool validate_enabled() {
   return v && v[0] == '1' && v[1] == 0;
 }
 
-// Shape checks common to both entry points. Returns BSATTN_OK or an error with detail.
-int check_shape(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk) {
+// Key blocks of a sequence of N tokens (N % block == 0) at the key stride ks (block: the nb
+// blocks of the partition; below: overlapping blocks, the last one ending at token N).
+int64_t key_count(int64_t N, int block, int ks) {
+  if (N == 0) return 0;
+  if (ks == block) return N / block;
+  return (N - block + ks - 1) / ks + 1;
+}
+
+// Shape checks common to the entry points. key_stride 0 means block. Returns BSATTN_OK or an
+// error with detail.
+int check_shape(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
+                int key_stride) {
   if (dtype != BSATTN_F32 && dtype != BSATTN_BF16 && dtype != BSATTN_FP8_E4M3)
     return fail(BSATTN_E_INVALID, "unknown dtype %d", dtype);
   if (B < 0 || N < 0) return fail(BSATTN_E_INVALID, "negative B or N");
@@ -47,11 +57,16 @@ int check_shape(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int blo
   if (N % block) return fail(BSATTN_E_INVALID, "N (%lld) must be a multiple of block (%d)",
                              (long long)N, block);
   const int64_t nb = N / block;
+  const int ks = key_stride == 0 ? block : key_stride;
+  if (ks > block || 2 * (int64_t)ks < block)
+    return fail(BSATTN_E_INVALID, "key_stride %d outside [block/2, block] (block=%d)", key_stride,
+                block);
+  const int64_t nkb = key_count(N, block, ks);
   if (B == 0 || N == 0) {
-    if (topk < 0 || topk > nb)
-      return fail(BSATTN_E_INVALID, "topk %d outside [0, nb=%lld]", topk, (long long)nb);
-  } else if (topk < 1 || topk > nb) {
-    return fail(BSATTN_E_INVALID, "topk %d outside [1, nb=%lld]", topk, (long long)nb);
+    if (topk < 0 || topk > nkb)
+      return fail(BSATTN_E_INVALID, "topk %d outside [0, key blocks=%lld]", topk, (long long)nkb);
+  } else if (topk < 1 || topk > nkb) {
+    return fail(BSATTN_E_INVALID, "topk %d outside [1, key blocks=%lld]", topk, (long long)nkb);
   }
   if (D != 64 && D != 128) return fail(BSATTN_E_UNSUPPORTED, "D=%d (supported: 64, 128)", D);
   if (block != 64 && block != 128)
@@ -66,8 +81,8 @@ int check_shape(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int blo
 size_t pooled_q_bytes(int64_t B, int64_t N, int Hq, int D, int block) {
   return align256((size_t)B * Hq * (size_t)(N / block) * D * sizeof(float));
 }
-size_t pooled_k_bytes(int64_t B, int64_t N, int Hkv, int D, int block) {
-  return align256((size_t)B * Hkv * (size_t)(N / block) * D * sizeof(float));
+size_t pooled_k_bytes(int64_t B, int64_t nkb, int Hkv, int D) {
+  return align256((size_t)B * Hkv * (size_t)nkb * D * sizeof(float));
 }
 // score matrix, only for the many-block path
 size_t scores_bytes(int64_t B, int64_t N, int Hq, int block) {
@@ -96,37 +111,66 @@ const char* bsattn_status_str(int status) {
 
 const char* bsattn_last_error(void) { return g_err; }
 
-size_t bsattn_select_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int D, int block) {
+int64_t bsattn_key_blocks(int64_t N, int block, int key_stride) {
+  if (N < 0 || block < 1 || N % block) {
+    fail(BSATTN_E_INVALID, "N (%lld) must be >= 0 and a multiple of block (%d)", (long long)N,
+         block);
+    return -1;
+  }
+  const int ks = key_stride == 0 ? block : key_stride;
+  if (ks > block || 2 * (int64_t)ks < block) {
+    fail(BSATTN_E_INVALID, "key_stride %d outside [block/2, block] (block=%d)", key_stride, block);
+    return -1;
+  }
+  return key_count(N, block, ks);
+}
+
+size_t bsattn_select_workspace_bytes_ex(int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
+                                        int key_stride) {
   if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || D < 1 || block < 1 || N % block) {
     fail(BSATTN_E_INVALID, "invalid sizes for the workspace query");
     return 0;
   }
+  const int64_t nkb = bsattn_key_blocks(N, block, key_stride);
+  if (nkb < 0) return 0;
   if (B == 0 || N == 0) return 0;
-  return pooled_q_bytes(B, N, Hq, D, block) + pooled_k_bytes(B, N, Hkv, D, block) +
+  return pooled_q_bytes(B, N, Hq, D, block) + pooled_k_bytes(B, nkb, Hkv, D) +
          scores_bytes(B, N, Hq, block);
+}
+
+size_t bsattn_select_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int D, int block) {
+  return bsattn_select_workspace_bytes_ex(B, N, Hq, Hkv, D, block, 0);
 }
 
 int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                   const void* q, const void* k, int32_t* idx, void* workspace,
                   size_t workspace_bytes, void* stream) {
-  return bsattn_select_ex(dtype, B, N, Hq, Hkv, D, block, topk, 0u, 0, 0ull, q, k, idx,
+  return bsattn_select_ex(dtype, B, N, Hq, Hkv, D, block, topk, 0u, 0, 0ull, 0, q, k, idx,
                           workspace, workspace_bytes, stream);
 }
 
 int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
-                     int topk, unsigned flags, int nrand, uint64_t seed, const void* q,
-                     const void* k, int32_t* idx, void* workspace, size_t workspace_bytes,
-                     void* stream) {
-  int st = check_shape(dtype, B, N, Hq, Hkv, D, block, topk);
+                     int topk, unsigned flags, int nrand, uint64_t seed, int key_stride,
+                     const void* q, const void* k, int32_t* idx, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_shape(dtype, B, N, Hq, Hkv, D, block, topk, key_stride);
   if (st != BSATTN_OK) return st;
+  const int ks = key_stride == 0 ? block : key_stride;
+  const bool overlap = ks != block;
   if (flags & ~(unsigned)(BSATTN_CAUSAL | BSATTN_POOL_MAX | BSATTN_GROUP_SELECT))
     return fail(BSATTN_E_INVALID, "unknown flags 0x%x", flags);
   if (nrand < 0 || nrand > topk)
     return fail(BSATTN_E_INVALID, "nrand %d outside [0, topk=%d]", nrand, topk);
   if (nrand > 0 && (flags & BSATTN_CAUSAL))
     return fail(BSATTN_E_UNSUPPORTED, "random places with the causal selection");
+  if (overlap && (flags & BSATTN_CAUSAL))
+    return fail(BSATTN_E_UNSUPPORTED, "overlapping key blocks with the causal selection");
   if (B == 0 || N == 0) return BSATTN_OK;
   const int64_t nb = N / block;
+  const int64_t nkb = key_count(N, block, ks);
+  if (overlap && nkb > bsattn::kMaxFusedBlocks)
+    return fail(BSATTN_E_UNSUPPORTED, "selection over %lld overlapping key blocks (supported: <= %d)",
+                (long long)nkb, bsattn::kMaxFusedBlocks);
   const bool large = bsattn::materialized_scores(nb, flags & BSATTN_GROUP_SELECT);
   if (large && (nb > bsattn::kMaxLargeBlocks || nb % 64))
     return fail(BSATTN_E_UNSUPPORTED,
@@ -141,7 +185,7 @@ int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, in
   if (!q || !k || !idx) return fail(BSATTN_E_INVALID, "null q, k or idx");
   if (!aligned16(q) || !aligned16(k) || ((uintptr_t)idx & 3u))
     return fail(BSATTN_E_INVALID, "q and k must be 16-byte aligned, idx 4-byte aligned");
-  const size_t need = bsattn_select_workspace_bytes(B, N, Hq, Hkv, D, block);
+  const size_t need = bsattn_select_workspace_bytes_ex(B, N, Hq, Hkv, D, block, key_stride);
   if (!workspace || workspace_bytes < need)
     return fail(BSATTN_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   if ((uintptr_t)workspace & 255u) return fail(BSATTN_E_WORKSPACE, "workspace not 256-byte aligned");
@@ -152,10 +196,10 @@ int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, in
   const int kind = dtype == BSATTN_F32 ? 0 : dtype == BSATTN_BF16 ? 1 : 2;
   const bool pmax = flags & BSATTN_POOL_MAX, causal = flags & BSATTN_CAUSAL;
   if (large) {
-    float* S = (float*)((char*)kbar + pooled_k_bytes(B, N, Hkv, D, block));
-    st = hip_status(
-        bsattn::launch_pool(kind, 3, B, N, Hq, Hkv, D, block, q, k, qbar, kbar, pmax, s),
-        "pool launch");
+    float* S = (float*)((char*)kbar + pooled_k_bytes(B, nkb, Hkv, D));
+    st = hip_status(bsattn::launch_pool(kind, 3, B, N, Hq, Hkv, D, block, ks, nkb, q, k, qbar,
+                                        kbar, pmax, s),
+                    "pool launch");
     if (st != BSATTN_OK) return st;
     st = hip_status(bsattn::launch_scores_large(B, Hq, Hkv, (int)nb, D, qbar, kbar, S, s),
                     "score launch");
@@ -163,31 +207,38 @@ int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, in
     return hip_status(bsattn::launch_topk_rows(B * Hq * nb, (int)nb, topk, S, idx, causal, s),
                       "top-k launch");
   }
-  st = hip_status(
-      bsattn::launch_pool(kind, 2, B, N, Hq, Hkv, D, block, q, k, qbar, kbar, pmax, s),
-      "key pool launch");
+  st = hip_status(bsattn::launch_pool(kind, 2, B, N, Hq, Hkv, D, block, ks, nkb, q, k, qbar,
+                                      kbar, pmax, s),
+                  "key pool launch");
   if (st != BSATTN_OK) return st;
-  return hip_status(bsattn::launch_pool_score_select(kind, B, N, Hq, Hkv, D, block, topk, q,
-                                                     qbar, kbar, idx, flags, nrand, seed, s),
+  return hip_status(bsattn::launch_pool_score_select(kind, B, N, Hq, Hkv, D, block, topk, nkb,
+                                                     q, qbar, kbar, idx, flags, nrand, seed, s),
                     "query pool/score/select launch");
 }
 
 int bsattn_forward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                    const void* q, const void* k, const void* v, const int32_t* idx, float scale,
                    const float* descale_qkv, void* out, void* stream) {
-  return bsattn_forward_ex(dtype, B, N, Hq, Hkv, D, block, topk, 0u, q, k, v, idx, scale,
+  return bsattn_forward_ex(dtype, B, N, Hq, Hkv, D, block, topk, 0u, 0, q, k, v, idx, scale,
                            descale_qkv, out, nullptr, stream);
 }
 
 int bsattn_forward_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
-                      int topk, unsigned flags, const void* q, const void* k, const void* v,
-                      const int32_t* idx, float scale, const float* descale_qkv, void* out,
-                      float* lse, void* stream) {
-  int st = check_shape(dtype, B, N, Hq, Hkv, D, block, topk);
+                      int topk, unsigned flags, int key_stride, const void* q, const void* k,
+                      const void* v, const int32_t* idx, float scale, const float* descale_qkv,
+                      void* out, float* lse, void* stream) {
+  int st = check_shape(dtype, B, N, Hq, Hkv, D, block, topk, key_stride);
   if (st != BSATTN_OK) return st;
   if (flags & ~(unsigned)(BSATTN_CAUSAL | BSATTN_POOL_MAX | BSATTN_GROUP_SELECT))
     return fail(BSATTN_E_INVALID, "unknown flags 0x%x", flags);
   const bool causal = flags & BSATTN_CAUSAL;
+  const int ks = key_stride == 0 ? block : key_stride;
+  const int64_t nkb = key_count(N, block, ks);
+  if (ks != block && causal)
+    return fail(BSATTN_E_UNSUPPORTED, "overlapping key blocks with the causal variant");
+  if (ks != block && nkb > bsattn::kMaxKeyBlocks)
+    return fail(BSATTN_E_UNSUPPORTED, "attention over %lld overlapping key blocks (supported: <= %d)",
+                (long long)nkb, bsattn::kMaxKeyBlocks);
   if (!isfinite(scale) || !(scale > 0.f))
     return fail(BSATTN_E_INVALID, "scale must be finite and > 0");
   if (dtype == BSATTN_FP8_E4M3) {
@@ -206,35 +257,36 @@ int bsattn_forward_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, i
   if (validate_enabled()) {
     unsigned int bad = 0;
     const int64_t nb = N / block;
-    st = hip_status(bsattn::validate_idx(B * Hq * nb, topk, (int)nb, idx, causal, s, &bad),
-                    "idx validation");
+    st = hip_status(
+        bsattn::validate_idx(B * Hq * nb, topk, (int)nb, (int)nkb, idx, causal, s, &bad),
+        "idx validation");
     if (st != BSATTN_OK) return st;
     if (bad)
       return fail(BSATTN_E_INVALID,
                   causal ? "idx: %u rows are not causal rows (strictly ascending in [0, i], "
                            "then -1; nb=%lld)"
-                         : "idx: %u rows are not strictly ascending in [0, nb=%lld)",
-                  bad, (long long)nb);
+                         : "idx: %u rows are not strictly ascending in [0, key blocks=%lld)",
+                  bad, (long long)(causal ? nb : nkb));
   }
   if (dtype == BSATTN_BF16) {
     if (!bsattn::attn_bf16_supported(D, block))
       return fail(BSATTN_E_UNSUPPORTED, "bf16 attention for D=%d block=%d", D, block);
     return hip_status(bsattn::launch_attn_bf16(B, N, Hq, Hkv, D, block, topk, q, k, v, idx,
-                                               scale, out, lse, causal, s),
+                                               scale, out, lse, causal, ks, nkb, s),
                       "bf16 attention launch");
   }
   if (dtype == BSATTN_F32) {
     if (!bsattn::attn_f32_supported(D, block))
       return fail(BSATTN_E_UNSUPPORTED, "fp32 attention for D=%d block=%d", D, block);
     return hip_status(bsattn::launch_attn_f32(B, N, Hq, Hkv, D, block, topk, q, k, v, idx,
-                                              scale, out, lse, causal, s),
+                                              scale, out, lse, causal, ks, nkb, s),
                       "fp32 attention launch");
   }
   if (!bsattn::attn_fp8_supported(D, block))
     return fail(BSATTN_E_UNSUPPORTED, "fp8 attention for D=%d block=%d (supported: D=128)", D,
                 block);
   return hip_status(bsattn::launch_attn_fp8(B, N, Hq, Hkv, D, block, topk, q, k, v, idx, scale,
-                                            descale_qkv, out, lse, causal, s),
+                                            descale_qkv, out, lse, causal, ks, nkb, s),
                     "fp8 attention launch");
 }
 
@@ -254,7 +306,7 @@ int bsattn_backward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int
                     const int32_t* idx, const void* out, const void* dout, const float* lse,
                     float scale, float* dq, float* dk, float* dv, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  int st = check_shape(dtype, B, N, Hq, Hkv, D, block, topk);
+  int st = check_shape(dtype, B, N, Hq, Hkv, D, block, topk, 0);
   if (st != BSATTN_OK) return st;
   if (flags & ~(unsigned)(BSATTN_CAUSAL | BSATTN_POOL_MAX | BSATTN_GROUP_SELECT))
     return fail(BSATTN_E_INVALID, "unknown flags 0x%x", flags);

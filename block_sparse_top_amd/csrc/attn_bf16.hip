@@ -97,18 +97,21 @@ __device__ __forceinline__ s16x4 ds_read_tr16(const char* lds_bytes) {
 template <int SB, bool HALF>
 constexpr int tile_rows() { return HALF ? 64 : SB; }
 
-template <int D, int SB, bool CAUSAL, bool HALF>
+// OVL: overlapping key blocks (key block j starts at token j*kstride; nkb of them): the tile of
+// block j starts at key_tile_start and its first key_tile_skip keys score -inf.
+template <int D, int SB, bool CAUSAL, bool HALF, bool OVL>
 __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
     float* __restrict__ lse, int64_t N, int Hq, int Hkv, int nb, int topk, float c,
-    uint32_t total_tiles) {
+    uint32_t total_tiles, int nkb, int kstride) {
   constexpr int BLK = tile_rows<SB, HALF>();  // rows of one tile and of this work-group
   constexpr int UN = SB / BLK;                // tiles per selected block = work-groups per
                                               // query block
   using C = Cfg<D, BLK>;
   __shared__ __attribute__((aligned(1024))) char Kl[C::TILE];   // [BLK][D] bf16, swizzled
   __shared__ __attribute__((aligned(1024))) char Vl[C::TILE];
+  __shared__ uint32_t chosen[OVL ? kMaxKeyBlocks / 32 : 1];   // OVL: the row's key blocks
 
   // tile order: (b, kv head, head within group, query block, half); blocks reading the same
   // K/V are consecutive and land on one XCD
@@ -142,7 +145,7 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
   const char* kbase0 = (const char*)(k + (int64_t)b * N * krs + (int64_t)g * D);
   const char* vbase0 = (const char*)(v + (int64_t)b * N * krs + (int64_t)g * D);
   const int kcount = CAUSAL && i + 1 < topk ? i + 1 : topk;   // entries of the row used
-  const unsigned klim = CAUSAL ? (unsigned)(i + 1) : (unsigned)nb;   // admissible blocks
+  const unsigned klim = CAUSAL ? (unsigned)(i + 1) : (unsigned)(OVL ? nkb : nb);   // admissible
 
   // DMA source byte offsets of this lane inside a tile (fixed), destination spans uniform
   uint32_t goff[C::DMA];
@@ -155,7 +158,12 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
   bool bad = false;
   auto tile_base = [&](int kb, int u) -> int64_t {   // unit u (BLK rows) of selected block kb
     if ((unsigned)kb >= klim) { bad = true; kb = 0; }
-    return ((int64_t)kb * SB + BLK * u) * krs * 2;
+    const int64_t first = OVL ? key_tile_start(kb, kstride, SB, N) : (int64_t)kb * SB;
+    return (first + BLK * u) * krs * 2;
+  };
+  auto skip_of = [&](int kb) -> int {          // OVL: leading keys of kb's tile left out
+    if (!OVL || (unsigned)kb >= klim) return 0;
+    return key_tile_skip(kb, kstride, SB, N, is_selected(chosen, kb - 1));
   };
   // The transfers are issued from inline asm so that the compiler's wait-count pass, which
   // cannot tell the K and V buffers apart, does not add full vmcnt(0) waits before every LDS
@@ -212,6 +220,7 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
   for (int qc = 0; qc < C::QC; ++qc) { mc[qc] = 0.f; lsum[qc] = 0.f; }
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
+  if (OVL) mark_selected(chosen, myidx, kcount, nkb, tid, C::NT);
   // Q must have landed before the first transfer: the hand-placed vmcnt waits in the loop
   // count transfers only (the empty asm consumes the loaded registers here)
 #pragma unroll
@@ -219,6 +228,7 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) asm volatile("" ::"v"(qf[qc][s]));
   int kb_cur = myidx[0], u_cur = 0;
+  int skip_cur = skip_of(kb_cur);
   {
     const int64_t tb = tile_base(kb_cur, 0);
     dma(kbase0 + tb, Kl);
@@ -230,6 +240,7 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
     const int kb_next = more ? myidx[(t + 1) / UN] : 0;
     const int u_next = (t + 1) % UN;
     const int64_t tb_next = more ? tile_base(kb_next, u_next) : 0;
+    const int skip_next = OVL && more ? skip_of(kb_next) : 0;
 
     // ---- K(t): wait for this wave's share (V(t) may still fly), then the whole work-group
     wait_vmcnt<C::DMA>();
@@ -266,6 +277,17 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
             const int key = BLK * u_cur + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
             const int qry = BLK * hq + C::QW * wave + 32 * qc + l32;
             if (key > qry) sacc[kt][qc][r] = -__builtin_inff();
+          }
+    }
+    if (OVL && skip_cur > BLK * u_cur) {       // keys before the block or held by block kb-1
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+        for (int qc = 0; qc < C::QC; ++qc)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = BLK * u_cur + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (key < skip_cur) sacc[kt][qc][r] = -__builtin_inff();
           }
     }
 
@@ -307,7 +329,7 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
         const float bm = row_max(qc);
         const float l_row = lsum[qc] + __shfl_xor(lsum[qc], 32);   // same on both lanes
         if (l_row == 0.f) {                    // nothing accumulated yet: O and l are zero
-          mc[qc] = bm;
+          if (bm != -__builtin_inff()) mc[qc] = bm;   // (a unit whose keys are all left out)
         } else {
           const float m_new = fmaxf(mc[qc], bm);
           const float alpha = __builtin_amdgcn_exp2f(mc[qc] - m_new);
@@ -353,6 +375,7 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
       }
     kb_cur = kb_next;
     u_cur = u_next;
+    if (OVL) skip_cur = skip_next;
   }
 
   // epilogue: O = O^T / l, bf16, 4 consecutive d per store
@@ -380,18 +403,21 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
 template <int D, int BLK, bool HALF>
 hipError_t launch_tiles(int64_t B, int64_t N, int Hq, int Hkv, int topk, const void* q,
                         const void* k, const void* v, const int32_t* idx, float c, void* out,
-                        float* lse, bool causal, hipStream_t stream) {
+                        float* lse, bool causal, int nkb, int kstride, hipStream_t stream) {
   const int nb = (int)(N / BLK);
   constexpr int TR = tile_rows<BLK, HALF>();
   const uint32_t total = (uint32_t)(B * Hq * nb * (BLK / TR));
+#define BSATTN_BF16_LAUNCH(causal_, ovl_)                                                     \
+  attn_bf16_kernel<D, BLK, causal_, HALF, ovl_><<<total, Cfg<D, TR>::NT, 0, stream>>>(        \
+      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, lse, N, \
+      Hq, Hkv, nb, topk, c, total, nkb, kstride)
   if (causal)
-    attn_bf16_kernel<D, BLK, true, HALF><<<total, Cfg<D, TR>::NT, 0, stream>>>(
-        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, lse, N,
-        Hq, Hkv, nb, topk, c, total);
+    BSATTN_BF16_LAUNCH(true, false);
+  else if (kstride != BLK)
+    BSATTN_BF16_LAUNCH(false, true);
   else
-    attn_bf16_kernel<D, BLK, false, HALF><<<total, Cfg<D, TR>::NT, 0, stream>>>(
-        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, lse, N,
-        Hq, Hkv, nb, topk, c, total);
+    BSATTN_BF16_LAUNCH(false, false);
+#undef BSATTN_BF16_LAUNCH
   return hipGetLastError();
 }
 
@@ -402,12 +428,14 @@ constexpr int64_t kHalfTileMaxBytes = 64ll << 20;
 template <int D, int BLK>
 hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int topk, const void* q, const void* k,
                   const void* v, const int32_t* idx, float c, void* out, float* lse,
-                  bool causal, hipStream_t stream) {
-  if (BLK == 128 && N * D * 2 * 2 <= kHalfTileMaxBytes)
-    return launch_tiles<D, BLK, true>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal,
-                                      stream);
+                  bool causal, int nkb, int kstride, hipStream_t stream) {
+  if constexpr (BLK == 128) {
+    if (N * D * 2 * 2 <= kHalfTileMaxBytes)
+      return launch_tiles<D, BLK, true>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal,
+                                        nkb, kstride, stream);
+  }
   return launch_tiles<D, BLK, false>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal,
-                                     stream);
+                                     nkb, kstride, stream);
 }
 
 }  // namespace
@@ -418,13 +446,17 @@ bool attn_bf16_supported(int D, int block) {
 
 hipError_t launch_attn_bf16(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                             const void* q, const void* k, const void* v, const int32_t* idx,
-                            float scale, void* out, float* lse, bool causal,
-                            hipStream_t stream) {
+                            float scale, void* out, float* lse, bool causal, int key_stride,
+                            int64_t nkb, hipStream_t stream) {
   const float c = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
-  if (D == 64 && block == 64) return launch<64, 64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal, stream);
-  if (D == 64 && block == 128) return launch<64, 128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal, stream);
-  if (D == 128 && block == 64) return launch<128, 64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal, stream);
-  return launch<128, 128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal, stream);
+  const int nk = (int)nkb;
+#define BSATTN_BF16_SHAPE(d_, b_) \
+  launch<d_, b_>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal, nk, key_stride, stream)
+  if (D == 64 && block == 64) return BSATTN_BF16_SHAPE(64, 64);
+  if (D == 64 && block == 128) return BSATTN_BF16_SHAPE(64, 128);
+  if (D == 128 && block == 64) return BSATTN_BF16_SHAPE(128, 64);
+  return BSATTN_BF16_SHAPE(128, 128);
+#undef BSATTN_BF16_SHAPE
 }
 
 }  // namespace bsattn

@@ -28,6 +28,9 @@
 // Causal variant (template flag): query block i reads the first min(topk, i+1) entries of its
 // row, each in [0, i]; in its own block the scores of keys after the query are -inf before
 // the row maximum and the weights.
+// Overlapping key blocks (template flag; the MSA page's §5.3): block j's tile starts at
+// key_tile_start and its first key_tile_skip keys score -inf (at least one key of every tile
+// counts, so the row maximum of a tile is finite).
 #include "common.h"
 #include "launch.h"
 
@@ -78,14 +81,16 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f3
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-template <int BLK, bool CAUSAL>
+template <int BLK, bool CAUSAL, bool OVL>
 __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse,
-    int64_t N, int Hq, int Hkv, int nb, int topk, float c, float dv, uint32_t total_tiles) {
+    int64_t N, int Hq, int Hkv, int nb, int topk, float c, float dv, uint32_t total_tiles,
+    int nkb, int kstride) {
   using C = Cfg8<BLK>;
   __shared__ __attribute__((aligned(1024))) char Kl[C::TILE];
   __shared__ __attribute__((aligned(1024))) char Vl[C::TILE];
+  __shared__ uint32_t chosen[OVL ? kMaxKeyBlocks / 32 : 1];   // OVL: the row's key blocks
 
   const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
   const int G = Hq / Hkv;
@@ -129,10 +134,14 @@ __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
   }
   bool bad = false;
   const int kcount = CAUSAL && i + 1 < topk ? i + 1 : topk;   // entries of the row used
-  const unsigned klim = CAUSAL ? (unsigned)(i + 1) : (unsigned)nb;
+  const unsigned klim = CAUSAL ? (unsigned)(i + 1) : (unsigned)(OVL ? nkb : nb);
   auto tile_base = [&](int kb) -> int64_t {
     if ((unsigned)kb >= klim) { bad = true; kb = 0; }
-    return (int64_t)kb * BLK * krs;
+    return (OVL ? key_tile_start(kb, kstride, BLK, N) : (int64_t)kb * BLK) * krs;
+  };
+  auto skip_of = [&](int kb) -> int {          // OVL: leading keys of kb's tile left out
+    if (!OVL || (unsigned)kb >= klim) return 0;
+    return key_tile_skip(kb, kstride, BLK, N, is_selected(chosen, kb - 1));
   };
   // transfers from inline asm: the compiler's wait-count pass adds no vmcnt(0) before the
   // LDS reads; each wave issues exactly DMA transfers per tile and no other vector-memory
@@ -181,7 +190,9 @@ __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
   float m = -__builtin_inff();                // reference (exp2 domain) of this lane's row
   float lsum = 0.f;
 
+  if (OVL) mark_selected(chosen, myidx, kcount, nkb, tid, C::NT);
   int kb_cur = myidx[0];
+  int skip_cur = skip_of(kb_cur);
   {
     const int64_t tb = tile_base(kb_cur);
     dma(kbase0 + tb, Kl);
@@ -192,6 +203,7 @@ __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
     const bool more = t + 1 < kcount;
     const int kb_next = more ? myidx[t + 1] : 0;
     const int64_t tb_next = more ? tile_base(kb_next) : 0;
+    const int skip_next = OVL && more ? skip_of(kb_next) : 0;
 
     wait_vmcnt<C::DMA>();
     if (C::NW > 1) __syncthreads();
@@ -224,6 +236,15 @@ __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
         for (int r = 0; r < 16; ++r) {
           const int key = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
           if (key > 32 * wave + l32) sacc[kt][r] = -__builtin_inff();
+        }
+    }
+    if (OVL && skip_cur > 0) {                 // keys before the block or held by block kb-1
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key < skip_cur) sacc[kt][r] = -__builtin_inff();
         }
     }
 
@@ -285,6 +306,7 @@ __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
 #pragma unroll
       for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] = mfma8(va[ks][dt], pb[ks], oacc[dt]);
     kb_cur = kb_next;
+    if (OVL) skip_cur = skip_next;
   }
 
   const float l_all = lsum + __shfl_xor(lsum, 32);
@@ -308,17 +330,20 @@ __global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
 template <int BLK>
 hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int topk, const void* q, const void* k,
                   const void* v, const int32_t* idx, float c, float dv, void* out, float* lse,
-                  bool causal, hipStream_t stream) {
+                  bool causal, int nkb, int kstride, hipStream_t stream) {
   const int nb = (int)(N / BLK);
   const uint32_t total = (uint32_t)(B * Hq * nb);
+#define BSATTN_FP8_LAUNCH(causal_, ovl_)                                                      \
+  attn_fp8_kernel<BLK, causal_, ovl_><<<total, Cfg8<BLK>::NT, 0, stream>>>(                    \
+      (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, (uint16_t*)out, lse, N, Hq, \
+      Hkv, nb, topk, c, dv, total, nkb, kstride)
   if (causal)
-    attn_fp8_kernel<BLK, true><<<total, Cfg8<BLK>::NT, 0, stream>>>(
-        (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, (uint16_t*)out, lse, N, Hq,
-        Hkv, nb, topk, c, dv, total);
+    BSATTN_FP8_LAUNCH(true, false);
+  else if (kstride != BLK)
+    BSATTN_FP8_LAUNCH(false, true);
   else
-    attn_fp8_kernel<BLK, false><<<total, Cfg8<BLK>::NT, 0, stream>>>(
-        (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, (uint16_t*)out, lse, N, Hq,
-        Hkv, nb, topk, c, dv, total);
+    BSATTN_FP8_LAUNCH(false, false);
+#undef BSATTN_FP8_LAUNCH
   return hipGetLastError();
 }
 
@@ -329,13 +354,16 @@ bool attn_fp8_supported(int D, int block) { return D == 128 && (block == 64 || b
 hipError_t launch_attn_fp8(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                            const void* q, const void* k, const void* v, const int32_t* idx,
                            float scale, const float* descale_qkv, void* out, float* lse,
-                           bool causal, hipStream_t stream) {
+                           bool causal, int key_stride, int64_t nkb, hipStream_t stream) {
   (void)D;
   const float c = (float)((double)scale * 1.4426950408889634 * (double)descale_qkv[0] *
                           (double)descale_qkv[1]);
   const float dv = descale_qkv[2];
-  if (block == 64) return launch<64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, dv, out, lse, causal, stream);
-  return launch<128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, dv, out, lse, causal, stream);
+  if (block == 64)
+    return launch<64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, dv, out, lse, causal, (int)nkb,
+                      key_stride, stream);
+  return launch<128>(B, N, Hq, Hkv, topk, q, k, v, idx, c, dv, out, lse, causal, (int)nkb,
+                     key_stride, stream);
 }
 
 }  // namespace bsattn

@@ -114,6 +114,39 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t n) {
   return z ^ (z >> 31);
 }
 
+// Overlapping key blocks (the MSA page's §5.3 overlap remedy): key block j holds the tokens
+// [j*stride, min(j*stride + SB, N)) with SB/2 <= stride <= SB, so only neighbouring blocks share
+// tokens. Attention reads the SB-token tile that starts at key_tile_start (the last block's
+// tile moves back to end at token N, so every tile lies inside the sequence) and leaves out
+// its first key_tile_skip keys: tokens before the block's start, and tokens that the selected
+// block j-1 already holds (the union of a row's blocks counts each token once). Each block
+// has at least one token of its own, so the skip is below SB.
+__device__ __forceinline__ int64_t key_tile_start(int j, int stride, int SB, int64_t N) {
+  const int64_t s = (int64_t)j * stride;
+  return s < N - SB ? s : N - SB;
+}
+__device__ __forceinline__ int key_tile_skip(int j, int stride, int SB, int64_t N,
+                                             bool prev_selected) {
+  const int64_t first = prev_selected ? (int64_t)(j - 1) * stride + SB : (int64_t)j * stride;
+  return (int)(first - key_tile_start(j, stride, SB, N));
+}
+
+// Bitmap (LDS, (nkb + 31) / 32 words) of the key blocks named by the first `count` entries
+// of a row; entries outside [0, nkb) are left out. All threads of the work-group take part.
+__device__ __forceinline__ void mark_selected(uint32_t* bits, const int32_t* row, int count,
+                                              int nkb, int tid, int nthreads) {
+  for (int w = tid; w < (nkb + 31) / 32; w += nthreads) bits[w] = 0u;
+  __syncthreads();
+  for (int p = tid; p < count; p += nthreads) {
+    const int j = row[p];
+    if ((unsigned)j < (unsigned)nkb) atomicOr(&bits[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+}
+__device__ __forceinline__ bool is_selected(const uint32_t* bits, int j) {
+  return j >= 0 && ((bits[j >> 5] >> (j & 31)) & 1u);
+}
+
 // Selection options (flags of the extended entry points)
 constexpr unsigned kCausal = 1u;     // key blocks j <= i only, own block forced
 constexpr unsigned kPoolMax = 2u;    // in-block elementwise maximum instead of the mean

@@ -7,17 +7,18 @@
 
 namespace bsattn {
 
-// Step 1: per-block mean (fp32 out, [B, H, nb, D]) of the tensors in `which` (bit 0: q,
-// bit 1: k). kind: 0 fp32, 1 bf16, 2 fp8.
+// Step 1: per-block mean (fp32 out, [B, H, nblk, D]) of the tensors in `which` (bit 0: q,
+// bit 1: k). kind: 0 fp32, 1 bf16, 2 fp8. q has nb = N / block blocks; k has nkb key blocks
+// starting every key_stride tokens (key_stride == block: the same nb blocks).
 hipError_t launch_pool(int kind, int which, int64_t B, int64_t N, int Hq, int Hkv, int D,
-                       int block, const void* q, const void* k, float* qbar, float* kbar,
-                       bool pmax, hipStream_t stream);
+                       int block, int key_stride, int64_t nkb, const void* q, const void* k,
+                       float* qbar, float* kbar, bool pmax, hipStream_t stream);
 
-// Steps 1 (query side), 2 and 3 fused for nb <= kMaxFusedBlocks: query pooling (also stored
-// to qbar), block scores against the pooled keys kbar, top-k per row.
+// Steps 1 (query side), 2 and 3 fused for nkb <= kMaxFusedBlocks key blocks: query pooling
+// (also stored to qbar), block scores against the nkb pooled keys kbar, top-k per row.
 constexpr int kMaxFusedBlocks = 1024;
 hipError_t launch_pool_score_select(int kind, int64_t B, int64_t N, int Hq, int Hkv, int D,
-                                    int block, int topk, const void* q, float* qbar,
+                                    int block, int topk, int64_t nkb, const void* q, float* qbar,
                                     const float* kbar, int32_t* idx, unsigned flags,
                                     int nrand, uint64_t seed, hipStream_t stream);
 
@@ -37,19 +38,24 @@ hipError_t launch_scores_large(int64_t B, int Hq, int Hkv, int nb, int D, const 
 hipError_t launch_topk_rows(int64_t rows, int nb, int topk, const float* S, int32_t* idx,
                             bool causal, hipStream_t stream);
 
+// Overlapping key blocks: at most this many per sequence in attention (an LDS bitmap of a
+// row's chosen blocks); the selection takes up to kMaxFusedBlocks of them.
+constexpr int kMaxKeyBlocks = 8192;
+
 // Step 4, bf16 inputs on bf16 MFMA. Supported (D, block): D, block in {64, 128}.
+// key_stride == block: plain key blocks; otherwise nkb overlapping key blocks (not causal).
 bool attn_bf16_supported(int D, int block);
 hipError_t launch_attn_bf16(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                             const void* q, const void* k, const void* v, const int32_t* idx,
-                            float scale, void* out, float* lse, bool causal,
-                            hipStream_t stream);
+                            float scale, void* out, float* lse, bool causal, int key_stride,
+                            int64_t nkb, hipStream_t stream);
 
-// Step 4, fp32 inputs on the fp32 vector ALUs.
+// Step 4, fp32 inputs on the fp32 vector ALUs (key blocks as for bf16).
 bool attn_f32_supported(int D, int block);
 hipError_t launch_attn_f32(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                            const void* q, const void* k, const void* v, const int32_t* idx,
-                           float scale, void* out, float* lse, bool causal,
-                           hipStream_t stream);
+                           float scale, void* out, float* lse, bool causal, int key_stride,
+                           int64_t nkb, hipStream_t stream);
 
 // Step 4, OCP fp8 e4m3 inputs on the fp8 MFMA, bf16 output. Supported: D = 128,
 // block in {64, 128}. descale_qkv: host array of the three per-tensor descales.
@@ -57,7 +63,7 @@ bool attn_fp8_supported(int D, int block);
 hipError_t launch_attn_fp8(int64_t B, int64_t N, int Hq, int Hkv, int D, int block, int topk,
                            const void* q, const void* k, const void* v, const int32_t* idx,
                            float scale, const float* descale_qkv, void* out, float* lse,
-                           bool causal, hipStream_t stream);
+                           bool causal, int key_stride, int64_t nkb, hipStream_t stream);
 
 // Backward (bf16 inputs, fp32 gradients): supported for block 64, D in {64, 128}.
 // dtype_kind: 0 fp32, 1 bf16, 2 fp8. Workspace: Dvec [B,Hq,N] fp32, key-block offsets
@@ -84,11 +90,11 @@ hipError_t launch_decode(int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int bl
                          const float* kbar, const int32_t* lens, float scale, void* out,
                          int32_t* idx, void* workspace, hipStream_t stream);
 
-// Checks every idx row (topk values, strictly ascending, in [0, nb); causal: the first
-// min(topk, i+1) values strictly ascending in [0, i] for query block i, the rest -1); waits
-// for the stream and returns the number of failing rows in *bad_rows. Uses one device-global
-// counter per device: concurrent validations on one device race.
-hipError_t validate_idx(int64_t rows, int topk, int nb, const int32_t* idx, bool causal,
-                        hipStream_t stream, unsigned int* bad_rows);
+// Checks every idx row (topk values, strictly ascending, in [0, nkb); causal: the first
+// min(topk, i+1) values strictly ascending in [0, i] for query block i = row mod nb, the rest
+// -1); waits for the stream and returns the number of failing rows in *bad_rows. Uses one
+// device-global counter per device: concurrent validations on one device race.
+hipError_t validate_idx(int64_t rows, int topk, int nb, int nkb, const int32_t* idx,
+                        bool causal, hipStream_t stream, unsigned int* bad_rows);
 
 }  // namespace bsattn

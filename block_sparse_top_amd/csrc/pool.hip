@@ -8,10 +8,14 @@
 // are stored [B, H, nb, D] in fp32 so that each (batch, head) row set is contiguous for the
 // score step.
 //
-// The kernel is HBM-bound: every input byte is read once with 16-byte loads. One work-group
-// reduces one (batch, block) of one tensor: the block is `block` consecutive token rows of
-// H*D elements each, i.e. one contiguous span of block*H*D elements. Threads own 16-byte
-// columns of a row and walk the tokens; partial sums of token groups meet in LDS.
+// Overlapping key blocks (the MSA page's §5.3 overlap remedy): key block j pools the tokens
+// [j*stride, min(j*stride + block, N)); a shorter last block is averaged over its own tokens.
+//
+// The kernel is HBM-bound: every input byte is read once with 16-byte loads (overlapping key
+// blocks read their shared tokens twice). One work-group reduces one (batch, block) of one
+// tensor: the block is up to `block` consecutive token rows of H*D elements each, i.e. one
+// contiguous span. Threads own 16-byte columns of a row and walk the tokens; partial sums of
+// token groups meet in LDS.
 #include "common.h"
 #include "launch.h"
 
@@ -28,8 +32,10 @@ __device__ __forceinline__ u32x4 load16(const uint8_t* p) {
 
 struct PoolArgs {
   const uint8_t* x;   // [B, N, H, D] storage
-  float* out;         // [B, H, nb, D]
+  float* out;         // [B, H, nblk, D]
   int H;
+  int64_t nblk;       // blocks of this tensor
+  int stride;         // tokens between block starts (block, or the key stride)
 };
 
 // fold one 16-byte vector into the accumulators: sum, or elementwise max when pmax
@@ -39,19 +45,24 @@ __device__ __forceinline__ void fold(bool pmax, const u32x4& w, float* acc) {
 }
 
 template <int KIND>
-__global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka, int64_t nb,
-                                                        int D, int block, float inv_block,
-                                                        bool pmax) {
+__global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka, int64_t nmax,
+                                                        int64_t N, int D, int block,
+                                                        float inv_block, bool pmax) {
   constexpr int E = Vec<KIND>::E;
   const float init = pmax ? -__builtin_inff() : 0.f;
   extern __shared__ float red[];                       // [T][V*E] partial sums
   const PoolArgs a = blockIdx.y == 0 ? qa : ka;
-  const int64_t bi = blockIdx.x;                       // b * nb + i
-  const int64_t b = bi / nb, i = bi - b * nb;
+  const int64_t bi = blockIdx.x;                       // b * nmax + i
+  const int64_t b = bi / nmax, i = bi - b * nmax;
+  if (i >= a.nblk) return;                             // the other tensor has more blocks
+  const int64_t first = i * a.stride;                  // first token of block (b, i)
+  const int cnt = N - first < block ? (int)(N - first) : block;   // its tokens
   const int V = a.H * D / E;                           // 16-byte vectors per token row
   const int64_t row_bytes = (int64_t)V * 16;
-  const uint8_t* base = a.x + bi * block * row_bytes;  // first token of block (b, i)
+  const uint8_t* base = a.x + (b * N + first) * row_bytes;
+  const float scale = pmax ? 1.0f : cnt == block ? inv_block : 1.0f / (float)cnt;
   const int tid = threadIdx.x;
+  const int nblk = (int)a.nblk;
 
   if (V <= kThreads) {
     const int T = kThreads / V;                        // token groups
@@ -62,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
     if (grp < T) {
       const uint8_t* p = base + (int64_t)c * 16;
       int t = grp;
-      for (; t + (kUnroll - 1) * T < block; t += kUnroll * T) {   // kUnroll loads in flight
+      for (; t + (kUnroll - 1) * T < cnt; t += kUnroll * T) {     // kUnroll loads in flight
         u32x4 w[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) w[u] = load16(p + (int64_t)(t + u * T) * row_bytes);
@@ -74,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
           for (int u = 0; u < kUnroll; ++u) Vec<KIND>::add(w[u], acc);
         }
       }
-      for (; t < block; t += T) fold<KIND>(pmax, load16(p + (int64_t)t * row_bytes), acc);
+      for (; t < cnt; t += T) fold<KIND>(pmax, load16(p + (int64_t)t * row_bytes), acc);
 #pragma unroll
       for (int e = 0; e < E; ++e) red[grp * V * E + c * E + e] = acc[e];
     }
@@ -84,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
       for (int g2 = 0; g2 < T; ++g2)
         s = pmax ? fmaxf(s, red[g2 * V * E + o]) : s + red[g2 * V * E + o];
       const int h = o / D, d = o - h * D;
-      a.out[(((int64_t)b * a.H + h) * nb + i) * D + d] = s * inv_block;
+      a.out[(((int64_t)b * a.H + h) * nblk + i) * D + d] = s * scale;
     }
   } else {
     for (int c = tid; c < V; c += kThreads) {
@@ -93,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
       for (int e = 0; e < E; ++e) acc[e] = init;
       const uint8_t* p = base + (int64_t)c * 16;
       int t = 0;
-      for (; t + kUnroll - 1 < block; t += kUnroll) {
+      for (; t + kUnroll - 1 < cnt; t += kUnroll) {
         u32x4 w[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) w[u] = load16(p + (int64_t)(t + u) * row_bytes);
@@ -105,12 +116,12 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
           for (int u = 0; u < kUnroll; ++u) Vec<KIND>::add(w[u], acc);
         }
       }
-      for (; t < block; ++t) fold<KIND>(pmax, load16(p + (int64_t)t * row_bytes), acc);
+      for (; t < cnt; ++t) fold<KIND>(pmax, load16(p + (int64_t)t * row_bytes), acc);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int o = c * E + e;
         const int h = o / D, d = o - h * D;
-        a.out[(((int64_t)b * a.H + h) * nb + i) * D + d] = acc[e] * inv_block;
+        a.out[(((int64_t)b * a.H + h) * nblk + i) * D + d] = acc[e] * scale;
       }
     }
   }
@@ -119,8 +130,8 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
 }  // namespace
 
 hipError_t launch_pool(int kind, int which, int64_t B, int64_t N, int Hq, int Hkv, int D,
-                       int block, const void* q, const void* k, float* qbar, float* kbar,
-                       bool pmax, hipStream_t stream) {
+                       int block, int key_stride, int64_t nkb, const void* q, const void* k,
+                       float* qbar, float* kbar, bool pmax, hipStream_t stream) {
   const int64_t nb = N / block;
   const int ebytes = kind == 0 ? 4 : kind == 1 ? 2 : 1;
   const int E = 16 / ebytes;
@@ -133,15 +144,16 @@ hipError_t launch_pool(int kind, int which, int64_t B, int64_t N, int Hq, int Hk
       lds = s > lds ? s : lds;
     }
   }
-  PoolArgs qa{(const uint8_t*)q, qbar, Hq};
-  PoolArgs ka{(const uint8_t*)k, kbar, Hkv};
+  PoolArgs qa{(const uint8_t*)q, qbar, Hq, nb, block};
+  PoolArgs ka{(const uint8_t*)k, kbar, Hkv, nkb, key_stride};
   if (which == 2) qa = ka;                             // k only: grid.y == 1 reads qa
-  dim3 grid((unsigned)(B * nb), which == 3 ? 2 : 1);
-  const float inv = pmax ? 1.0f : 1.0f / (float)block;  // exact for power-of-two blocks
+  const int64_t nmax = which == 1 ? nb : which == 2 ? nkb : (nb > nkb ? nb : nkb);
+  dim3 grid((unsigned)(B * nmax), which == 3 ? 2 : 1);
+  const float inv = 1.0f / (float)block;               // exact for power-of-two blocks
   switch (kind) {
-    case 0: pool_kernel<0><<<grid, kThreads, lds, stream>>>(qa, ka, nb, D, block, inv, pmax); break;
-    case 1: pool_kernel<1><<<grid, kThreads, lds, stream>>>(qa, ka, nb, D, block, inv, pmax); break;
-    default: pool_kernel<2><<<grid, kThreads, lds, stream>>>(qa, ka, nb, D, block, inv, pmax); break;
+    case 0: pool_kernel<0><<<grid, kThreads, lds, stream>>>(qa, ka, nmax, N, D, block, inv, pmax); break;
+    case 1: pool_kernel<1><<<grid, kThreads, lds, stream>>>(qa, ka, nmax, N, D, block, inv, pmax); break;
+    default: pool_kernel<2><<<grid, kThreads, lds, stream>>>(qa, ka, nmax, N, D, block, inv, pmax); break;
   }
   return hipGetLastError();
 }

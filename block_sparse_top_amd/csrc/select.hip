@@ -35,9 +35,11 @@
 // the sum are the sum of the heads' scores), and the chosen blocks are written for each of
 // the G heads; the pooled-query workspace rows of the group's first head hold the sums.
 // nrand > 0 (random places): the row keeps its top topk - nrand blocks, then draw p takes the
-// (x mod m_p)-th of the m_p = nb - (topk - nrand) - p blocks not yet chosen, in ascending
+// (x mod m_p)-th of the m_p = nk - (topk - nrand) - p blocks not yet chosen, in ascending
 // order, x = element row * 2^16 + p of the SplitMix64 sequence (Steele, Lea, Flood, 2014)
 // seeded with `seed`, row = (batch, selection head, query block) in C order.
+// Rows are the nb query blocks, columns the nk key blocks: nk = nb, or more with overlapping
+// key blocks (the MSA page's §5.3), whose pooled rows the key pool wrote (not with kCausal).
 #include "common.h"
 #include "launch.h"
 
@@ -55,11 +57,11 @@ struct SelCfg {
   static constexpr int RG = kWaves * RW;                       // rows per work-group
 };
 
-template <int KIND, int CPL>  // storage kind; score columns per lane: nb <= 64 * CPL
+template <int KIND, int CPL>  // storage kind; score columns per lane: nk <= 64 * CPL
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const uint8_t* __restrict__ q, float* __restrict__ qbar, const float* __restrict__ kbar,
-    int32_t* __restrict__ idx, int64_t N, int Hq, int Hkv, int nb, int D, int block, int topk,
-    int row_tiles, float inv_block, unsigned flags, int nrand, uint64_t seed) {
+    int32_t* __restrict__ idx, int64_t N, int Hq, int Hkv, int nb, int nk, int D, int block,
+    int topk, int row_tiles, float inv_block, unsigned flags, int nrand, uint64_t seed) {
   constexpr int RW = SelCfg<CPL>::RW, RG = SelCfg<CPL>::RG;
   constexpr int E = Vec<KIND>::E;
   constexpr int EB = 16 / E;                // bytes per stored element
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   const int h0 = group ? g * G : sh % HS;   // first query head pooled here
   const int nh = group ? G : 1;             // query heads pooled and summed
   const int bh = b * Hq + h0;               // workspace row set of the pooled queries
-  const float* K = kbar + ((int64_t)b * Hkv + g) * nb * D;
+  const float* K = kbar + ((int64_t)b * Hkv + g) * nk * D;
   const int row0 = rt * RG;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int D4 = D / 4;
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
       const int col = e / D4, d4 = e - col * D4;
       const int j = c * 64 + col;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (j < nb) v = *(const f32x4*)(K + (int64_t)j * D + 4 * d4);
+      if (j < nk) v = *(const f32x4*)(K + (int64_t)j * D + 4 * d4);
       float* dst = ks + col * KS + 4 * d4;
       dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
     }
@@ -193,10 +195,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   for (int r = 0; r < RW; ++r) {
     const int row = row0 + wave * RW + r;
     if (row >= nb) break;                   // wave-uniform
-    // columns past nb (and, causal, past the row) hold key 0, which no candidate (always
+    // columns past nk (and, causal, past the row) hold key 0, which no candidate (always
     // >= 1) and no T reached by the search (>= 1 once any bit is set) can count; causal rows
     // give their own block the largest key
-    const int lim = causal ? row + 1 : nb;  // admissible columns j < lim
+    const int lim = causal ? row + 1 : nk;  // admissible columns j < lim
     const int kt = causal && row + 1 < topk ? row + 1 : topk;   // places of the row
     const int kr = kt - nrand;              // places taken by score (nrand = 0 if causal)
     uint32_t key[CPL];
@@ -237,12 +239,12 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     if (nrand > 0) {
       const uint64_t srow = (uint64_t)((int64_t)sh * nb + row);
       for (int p = 0; p < nrand; ++p) {
-        const uint32_t m = (uint32_t)(nb - kr - p);              // blocks not yet chosen
+        const uint32_t m = (uint32_t)(nk - kr - p);              // blocks not yet chosen
         const uint32_t x = (uint32_t)(splitmix64(seed, srow * 65536u + (uint64_t)p) % m);
         uint32_t before = 0;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-          const uint64_t mrem = __builtin_amdgcn_ballot_w64((c * 64 + lane) < nb && !chosen[c]);
+          const uint64_t mrem = __builtin_amdgcn_ballot_w64((c * 64 + lane) < nk && !chosen[c]);
           const uint32_t cnt = (uint32_t)__builtin_popcountll(mrem);
           if (x >= before && x < before + cnt && ((mrem >> lane) & 1ull) &&
               (uint32_t)lanes_below(mrem) == x - before)
@@ -266,41 +268,44 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 }
 
 template <int KIND, int CPL>
-hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int nb, int D, int block, int topk,
-                  const void* q, float* qbar, const float* kbar, int32_t* idx, unsigned flags,
-                  int nrand, uint64_t seed, hipStream_t stream) {
+hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int nb, int nk, int D, int block,
+                  int topk, const void* q, float* qbar, const float* kbar, int32_t* idx,
+                  unsigned flags, int nrand, uint64_t seed, hipStream_t stream) {
   constexpr int RG = SelCfg<CPL>::RG;
   const int row_tiles = (nb + RG - 1) / RG;
   const int HS = (flags & kGroup) ? Hkv : Hq;
   const dim3 grid((unsigned)(B * HS * row_tiles));
   const size_t lds = (size_t)(64 * (D + 1) + RG * D) * sizeof(float);
   select_kernel<KIND, CPL><<<grid, kThreads, lds, stream>>>(
-      (const uint8_t*)q, qbar, kbar, idx, N, Hq, Hkv, nb, D, block, topk, row_tiles,
+      (const uint8_t*)q, qbar, kbar, idx, N, Hq, Hkv, nb, nk, D, block, topk, row_tiles,
       1.0f / (float)block, flags, nrand, seed);
   return hipGetLastError();
 }
 
 template <int KIND>
-hipError_t launch_kind(int64_t B, int64_t N, int Hq, int Hkv, int nb, int D, int block, int topk,
-                       const void* q, float* qbar, const float* kbar, int32_t* idx,
+hipError_t launch_kind(int64_t B, int64_t N, int Hq, int Hkv, int nb, int nk, int D, int block,
+                       int topk, const void* q, float* qbar, const float* kbar, int32_t* idx,
                        unsigned flags, int nrand, uint64_t seed, hipStream_t stream) {
-  if (nb <= 64) return launch<KIND, 1>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
-  if (nb <= 128) return launch<KIND, 2>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
-  if (nb <= 256) return launch<KIND, 4>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
-  if (nb <= 512) return launch<KIND, 8>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
-  return launch<KIND, 16>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
+#define BSATTN_SELECT_CPL(cpl) \
+  launch<KIND, cpl>(B, N, Hq, Hkv, nb, nk, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream)
+  if (nk <= 64) return BSATTN_SELECT_CPL(1);
+  if (nk <= 128) return BSATTN_SELECT_CPL(2);
+  if (nk <= 256) return BSATTN_SELECT_CPL(4);
+  if (nk <= 512) return BSATTN_SELECT_CPL(8);
+  return BSATTN_SELECT_CPL(16);
+#undef BSATTN_SELECT_CPL
 }
 
 }  // namespace
 
 hipError_t launch_pool_score_select(int kind, int64_t B, int64_t N, int Hq, int Hkv, int D,
-                                    int block, int topk, const void* q, float* qbar,
+                                    int block, int topk, int64_t nkb, const void* q, float* qbar,
                                     const float* kbar, int32_t* idx, unsigned flags,
                                     int nrand, uint64_t seed, hipStream_t stream) {
-  const int nb = (int)(N / block);
-  if (kind == 0) return launch_kind<0>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
-  if (kind == 1) return launch_kind<1>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
-  return launch_kind<2>(B, N, Hq, Hkv, nb, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
+  const int nb = (int)(N / block), nk = (int)nkb;
+  if (kind == 0) return launch_kind<0>(B, N, Hq, Hkv, nb, nk, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
+  if (kind == 1) return launch_kind<1>(B, N, Hq, Hkv, nb, nk, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
+  return launch_kind<2>(B, N, Hq, Hkv, nb, nk, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream);
 }
 
 }  // namespace bsattn

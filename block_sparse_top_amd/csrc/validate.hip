@@ -1,6 +1,6 @@
 // Optional check of the selected-block indices handed to bsattn_forward (enabled by the
-// environment variable BSATTN_VALIDATE=1): every row must hold topk values in [0, nb), strictly
-// ascending. The attention kernels themselves only guard against out-of-range values (such a
+// environment variable BSATTN_VALIDATE=1): every row must hold topk values in [0, nkb) (the key
+// blocks: nb, or more when key blocks overlap), strictly ascending. The attention kernels themselves only guard against out-of-range values (such a
 // row's output becomes NaN); duplicates or a wrong order would silently change the result.
 #include "common.h"
 #include "launch.h"
@@ -17,12 +17,12 @@ __global__ void reset_kernel() { g_bad_rows = 0u; }
 // places with values in [0, i] and hold -1 in the others
 __global__ __launch_bounds__(256) void validate_kernel(const int32_t* __restrict__ idx,
                                                        int64_t rows, int topk, int nb,
-                                                       bool causal) {
+                                                       int nkb, bool causal) {
   const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= rows) return;
   const int i = (int)(r % nb);
   const int used = causal && i + 1 < topk ? i + 1 : topk;
-  const int lim = causal ? i + 1 : nb;
+  const int lim = causal ? i + 1 : nkb;
   const int32_t* row = idx + r * topk;
   bool ok = true;
   int prev = -1;
@@ -37,15 +37,15 @@ __global__ __launch_bounds__(256) void validate_kernel(const int32_t* __restrict
 
 }  // namespace
 
-hipError_t validate_idx(int64_t rows, int topk, int nb, const int32_t* idx, bool causal,
-                        hipStream_t stream, unsigned int* bad_rows) {
+hipError_t validate_idx(int64_t rows, int topk, int nb, int nkb, const int32_t* idx,
+                        bool causal, hipStream_t stream, unsigned int* bad_rows) {
   *bad_rows = 0;
   if (rows == 0) return hipSuccess;
   reset_kernel<<<1, 1, 0, stream>>>();
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   validate_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(idx, rows, topk, nb,
-                                                                      causal);
+                                                                      nkb, causal);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = hipMemcpyFromSymbolAsync(bad_rows, HIP_SYMBOL(g_bad_rows), sizeof(unsigned int), 0,

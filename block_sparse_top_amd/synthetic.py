@@ -192,3 +192,24 @@ def sample_rows(count: int, population: int, index: int, salt: int = 0):
     g = _gen(seeds(index)["sample"] + salt, "cpu")
     count = min(count, population)
     return torch.randperm(population, generator=g)[:count].sort().values.tolist()
+
+
+def random_block_sets(B: int, H: int, nq: int, nkb: int, topk: int, index: int,
+                      device="cpu") -> torch.Tensor:
+    """int32 [B, H, nq, topk]: per row, topk distinct key blocks out of [0, nkb), seeded.
+
+    Rows 3m are runs of consecutive blocks (neighbours share tokens when key blocks overlap),
+    rows 3m+1 the run that ends at the last key block, rows 3m+2 random sets; rows are
+    ascending except every fifth row, which is descending (attention takes a row's entries
+    in any order).
+    """
+    g = _gen(seeds(index)["sample"] + 101, "cpu")
+    rows = B * H * nq
+    sets = torch.rand((rows, nkb), generator=g).argsort(dim=1)[:, :topk].sort(dim=1).values
+    r = torch.arange(rows)[:, None]
+    start = torch.randint(0, nkb - topk + 1, (rows, 1), generator=g)
+    step = torch.arange(topk)[None, :]
+    sets = torch.where(r % 3 == 0, start + step, sets)
+    sets = torch.where(r % 3 == 1, nkb - topk + step, sets)
+    sets = torch.where(r % 5 == 0, sets.flip(1), sets)
+    return sets.to(torch.int32).reshape(B, H, nq, topk).to(device)

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define BSATTN_ABI_VERSION 2
+#define BSATTN_ABI_VERSION 3
 
 typedef enum {
   BSATTN_OK = 0,
@@ -76,7 +76,9 @@ typedef enum {
 
 /* Version of this ABI (BSATTN_ABI_VERSION of the built library). Version 2 added the
  * BSATTN_* option flags, the two _ex entry points (with the optional log-sum-exp output) and
- * the backward; version-1 calls are unchanged. */
+ * the backward; version 3 added the key_stride argument of the _ex entry points (overlapping
+ * key blocks), bsattn_key_blocks and bsattn_select_workspace_bytes_ex. Version-1 calls are
+ * unchanged. */
 int bsattn_abi_version(void);
 
 /* Static English text of a status code; never NULL. */
@@ -93,6 +95,22 @@ const char* bsattn_last_error(void);
  * values without the per-tensor descale (a positive factor that does not change the
  * selection). Returns 0 and records an error for invalid sizes. */
 size_t bsattn_select_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int D, int block);
+
+/* Overlapping key blocks (the MSA page's §5.3 remedy for block-boundary effects: overlapping
+ * blocks with overlap ratio 0.25). With key_stride s (block/2 <= s <= block; 0 means block),
+ * key block j holds the tokens [j*s, min(j*s + block, N)): key blocks follow until one ends at
+ * token N, so there are ceil((N - block) / s) + 1 of them (N / block when s == block). Query
+ * blocks stay the N / block blocks of `block` tokens. The selection pools, scores and picks
+ * key blocks (a shorter last block is pooled over its own tokens); attention of a query block
+ * runs over the union of the tokens of its key blocks, each token once. Returns the number of
+ * key blocks, or -1 (error recorded) for N < 0, N % block != 0 or a stride outside
+ * [block/2, block]. */
+int64_t bsattn_key_blocks(int64_t N, int block, int key_stride);
+
+/* bsattn_select_workspace_bytes for key blocks at key_stride (0: block): the pooled-k part is
+ * fp32 [B, Hkv, bsattn_key_blocks(N, block, key_stride), D]. */
+size_t bsattn_select_workspace_bytes_ex(int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
+                                        int key_stride);
 
 /*
  * Block selection (steps 1-2 of "SparseFormer 注意力实现" on the SparseFormer page).
@@ -119,8 +137,8 @@ int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int b
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* bsattn_select with options: flags is a combination of BSATTN_CAUSAL, BSATTN_POOL_MAX and
- * BSATTN_GROUP_SELECT (0 gives bsattn_select). Other bits: BSATTN_E_INVALID. Same workspace
- * size.
+ * BSATTN_GROUP_SELECT (0 gives bsattn_select). Other bits: BSATTN_E_INVALID. Workspace:
+ * bsattn_select_workspace_bytes_ex with the same key_stride.
  *   nrand  random places (the MSA page's §5.1 remedy "5% random blocks"; 0: none): each row
  *          keeps its topk - nrand best blocks, then draw p = 0 .. nrand-1 takes the
  *          (x mod m_p)-th of the m_p = nb - (topk - nrand) - p blocks not yet chosen, in
@@ -128,13 +146,18 @@ int bsattn_select(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int b
  *          (Steele, Lea, Flood, OOPSLA 2014) seeded with `seed`; row = (b * S + s) * nb + i
  *          for selection head s of S (S = Hq, or Hkv with BSATTN_GROUP_SELECT). The row stays
  *          ascending. 0 <= nrand <= topk (else BSATTN_E_INVALID); not with BSATTN_CAUSAL and
- *          only for nb <= 1024 (else BSATTN_E_UNSUPPORTED).
+ *          only for nb <= 1024 (else BSATTN_E_UNSUPPORTED). With overlapping key blocks the
+ *          draws run over the key blocks (nb above reads bsattn_key_blocks).
  *   seed   the generator's seed.
+ *   key_stride  0 or block: the plain blocks. Otherwise overlapping key blocks (see
+ *          bsattn_key_blocks; stride outside [block/2, block]: BSATTN_E_INVALID): idx rows name
+ *          key blocks, 1 <= topk <= bsattn_key_blocks(...); not with BSATTN_CAUSAL and for at
+ *          most 1024 key blocks (else BSATTN_E_UNSUPPORTED).
  * Arguments, layouts and errors otherwise as bsattn_select. */
 int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
-                     int topk, unsigned flags, int nrand, uint64_t seed, const void* q,
-                     const void* k, int32_t* idx, void* workspace, size_t workspace_bytes,
-                     void* stream);
+                     int topk, unsigned flags, int nrand, uint64_t seed, int key_stride,
+                     const void* q, const void* k, int32_t* idx, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /*
  * Gathered-block attention (step 3 of "SparseFormer 注意力实现"; MSA page §2.1 with a
@@ -172,15 +195,19 @@ int bsattn_forward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int 
  * BSATTN_POOL_MAX and BSATTN_GROUP_SELECT are accepted and have no effect here; other bits:
  * BSATTN_E_INVALID. Under BSATTN_VALIDATE=1 causal rows are checked in that form (unused
  * places must hold -1).
+ *   key_stride  0 or block: the plain blocks. Otherwise idx rows name overlapping key blocks
+ *        (bsattn_key_blocks) in [0, key blocks) and each query block attends to the union of
+ *        their tokens, every token once (rows should name distinct blocks); not with
+ *        BSATTN_CAUSAL and for at most 8192 key blocks (else BSATTN_E_UNSUPPORTED).
  *   lse  optional device pointer (NULL: not written), fp32 [B, Hq, N], 4-byte aligned: the
  *        natural log-sum-exp of every query row's scaled scores over its keys,
  *        log sum_u exp(scale * q_t . k_u) (for fp8, of the descaled values); NaN for a row
  *        whose idx entry was out of range. bsattn_backward takes it.
  * Arguments, layouts and errors otherwise as bsattn_forward. */
 int bsattn_forward_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
-                      int topk, unsigned flags, const void* q, const void* k, const void* v,
-                      const int32_t* idx, float scale, const float* descale_qkv, void* out,
-                      float* lse, void* stream);
+                      int topk, unsigned flags, int key_stride, const void* q, const void* k,
+                      const void* v, const int32_t* idx, float scale, const float* descale_qkv,
+                      void* out, float* lse, void* stream);
 
 /* Bytes of device workspace bsattn_backward needs (0 for an empty call): Dvec fp32
  * [B, Hq, N], key-block offsets int32 [B, Hkv, nb + 1], pair lists int32 [B, Hq, nb, topk],
@@ -197,8 +224,8 @@ size_t bsattn_backward_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, in
  *   dV_U += P^T dO_i, dP = dO_i V_U^T, dS = P * (dP - rowsum(dO_i * O_i)),
  *   dQ_i = scale * dS K_U, dK_U += scale * dS^T Q_i
  * (GQA: a KV head collects the contributions of all its query heads).
- * Supported: dtype BSATTN_BF16, D in {64, 128}, block 64, nb <= 4096; other combinations give
- * BSATTN_E_UNSUPPORTED. Products on bf16 MFMA with fp32 accumulation (P and dS rounded to bf16
+ * Supported: dtype BSATTN_BF16, D in {64, 128}, block 64, nb <= 4096, the plain key blocks
+ * (a forward with key_stride 0 or block); other combinations give BSATTN_E_UNSUPPORTED. Products on bf16 MFMA with fp32 accumulation (P and dS rounded to bf16
  * as MFMA operands); the key-side sums run in a fixed order, so results are reproducible.
  * Arguments
  *   dtype .. topk, flags  as for bsattn_forward_ex (BSATTN_CAUSAL selects the causal variant;

@@ -27,14 +27,15 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"bsattn_select", "bsattn_forward", "bsattn_select_workspace_bytes",
             "bsattn_abi_version", "bsattn_status_str", "bsattn_last_error",
-            "bsattn_select_ex", "bsattn_forward_ex"} <= set(names)
+            "bsattn_select_ex", "bsattn_forward_ex", "bsattn_key_blocks",
+            "bsattn_select_workspace_bytes_ex"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings():
     L = bst.lib()
-    assert L.bsattn_abi_version() == 2
+    assert L.bsattn_abi_version() == 3
     for s in range(5):
         assert L.bsattn_status_str(s).decode() == bsattn.STATUS[s]
     assert L.bsattn_status_str(99).decode() == "unknown status"
@@ -101,7 +102,8 @@ def sel_ex(flags, **kw):
     a.update(kw)
     return bst.lib().bsattn_select_ex(a["dtype"], a["B"], a["N"], a["Hq"], a["Hkv"], a["D"],
                                       a["block"], a["topk"], flags, a.get("nrand", 0), 0,
-                                      a["q"], a["k"], a["idx"], a["ws"], a["wsb"], None)
+                                      a.get("ks", 0), a["q"], a["k"], a["idx"], a["ws"], a["wsb"],
+                                      None)
 
 
 def test_extended_entry_points_reject():
@@ -112,15 +114,52 @@ def test_extended_entry_points_reject():
     assert sel_ex(1, nrand=1) == 2 and "causal" in last()
     assert sel_ex(0, nrand=1, N=64 * 2048, topk=3) == 2 and "random" in last()
     L = bst.lib()
-    st = L.bsattn_forward_ex(1, 1, 512, 2, 2, 64, 64, 2, 16, FAKE, FAKE, FAKE, FAKE, 0.125, None,
-                             FAKE, None, None)
+    st = L.bsattn_forward_ex(1, 1, 512, 2, 2, 64, 64, 2, 16, 0, FAKE, FAKE, FAKE, FAKE, 0.125,
+                             None, FAKE, None, None)
     assert st == 1 and "flags" in last()
-    st = L.bsattn_forward_ex(1, 1, 512, 2, 2, 64, 64, 2, 1, FAKE, FAKE, FAKE, FAKE,
+    st = L.bsattn_forward_ex(1, 1, 512, 2, 2, 64, 64, 2, 1, 0, FAKE, FAKE, FAKE, FAKE,
                              float("inf"), None, FAKE, None, None)
     assert st == 1 and "scale" in last()
-    st = L.bsattn_forward_ex(1, 1, 512, 2, 2, 64, 64, 2, 0, FAKE, FAKE, FAKE, FAKE, 0.125, None,
-                             FAKE, ctypes.c_void_p(0x10002), None)
+    st = L.bsattn_forward_ex(1, 1, 512, 2, 2, 64, 64, 2, 0, 0, FAKE, FAKE, FAKE, FAKE, 0.125,
+                             None, FAKE, ctypes.c_void_p(0x10002), None)
     assert st == 1 and "lse" in last()
+
+
+def test_key_blocks():
+    L = bst.lib()
+    # ceil((N - block) / stride) + 1 key blocks, the last one ending at token N
+    for N, blk, ks, n in ((512, 64, 0, 8), (512, 64, 64, 8), (512, 64, 48, 11), (8192, 64, 48, 171),
+                          (8192, 128, 96, 85), (256, 64, 32, 7), (0, 64, 48, 0), (64, 64, 48, 1)):
+        assert L.bsattn_key_blocks(N, blk, ks) == n, (N, blk, ks)
+        assert bst.key_blocks(N, blk, ks) == n
+    for N, blk, ks in ((500, 64, 48), (512, 64, 31), (512, 64, 65), (-64, 64, 0)):
+        assert L.bsattn_key_blocks(N, blk, ks) == -1 and last()
+    with pytest.raises(bsattn.BsattnError):
+        bst.key_blocks(512, 64, 20)
+    n = L.bsattn_select_workspace_bytes_ex(2, 8192, 16, 4, 64, 64, 48)
+    assert n == 2 * 16 * 128 * 64 * 4 + 2 * 4 * 171 * 64 * 4
+    assert L.bsattn_select_workspace_bytes_ex(2, 8192, 16, 4, 64, 64, 0) == \
+        L.bsattn_select_workspace_bytes(2, 8192, 16, 4, 64, 64)
+
+
+def test_overlap_rejects():
+    L = bst.lib()
+    assert sel_ex(0, ks=31) == 1 and "key_stride" in last()
+    assert sel_ex(0, ks=65) == 1 and "key_stride" in last()
+    assert sel_ex(0, ks=48, topk=12) == 1 and "topk" in last()          # 11 key blocks
+    assert sel_ex(1, ks=48) == 2 and "causal" in last()
+    assert sel_ex(0, ks=48, N=64 * 800, topk=3) == 2 and "overlapping" in last()   # 1066 > 1024
+    assert sel_ex(0, ks=48, topk=11, q=None) == 1 and "null" in last()  # topk 11 passes the checks
+    assert sel_ex(0, ks=48, topk=11, wsb=16) == 3 and "workspace" in last()
+    st = L.bsattn_forward_ex(1, 1, 512, 2, 2, 64, 64, 2, 1, 48, FAKE, FAKE, FAKE, FAKE, 0.125,
+                             None, FAKE, None, None)
+    assert st == 2 and "causal" in last()
+    st = L.bsattn_forward_ex(1, 1, 64 * 11000, 2, 2, 64, 64, 2, 0, 48, FAKE, FAKE, FAKE, FAKE,
+                             0.125, None, FAKE, None, None)
+    assert st == 2 and "overlapping" in last()
+    st = L.bsattn_forward_ex(1, 1, 512, 2, 2, 64, 64, 11, 0, 48, FAKE, FAKE, FAKE, None, 0.125,
+                             None, FAKE, None, None)
+    assert st == 1 and "null" in last()
 
 
 def bwd(**kw):
