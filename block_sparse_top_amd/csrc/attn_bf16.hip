@@ -8,7 +8,8 @@
 // blocks with a reference maximum and a normaliser in fp32.
 //
 // Work split: one work-group owns 64 query rows of one (batch, query head) — a whole 64-token
-// query block, or half of a 128-token one; each of its waves owns QW query rows (QW = 64 for
+// query block, or half of a 128-token one (whole 128-row tiles when one head's K and V exceed
+// the last-level cache, see launch); each of its waves owns QW query rows (QW = 64 for
 // D = 64, 32 for D = 128), i.e. QW/32 column tiles of the 32x32 MFMA. Per selected key block each wave computes
 //   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q^T in registers)
 //   P^T = exp2(c*S^T - m)   (c = scale*log2(e), m = row reference, usually 0)
@@ -39,6 +40,11 @@
 // Causal variant (template flag): query block i reads the first min(topk, i+1) entries of its
 // row, each of which must lie in [0, i]; in its own block i the scores of keys after the
 // query are set to -inf before the weights (weight 0).
+//
+// Overlapping key blocks (template flag; the MSA page's §5.3 overlap remedy): the row's key
+// blocks are marked in an LDS bitmap, block j is read from its tile at key_tile_start and
+// the tile's first key_tile_skip keys score -inf, so the union of the row's blocks counts
+// each token once.
 #include "common.h"
 #include "launch.h"
 
