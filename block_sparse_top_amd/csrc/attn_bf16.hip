@@ -7,10 +7,11 @@
 // blocks, §3.1: GQA. The softmax is exact: it is evaluated online over the k selected key
 // blocks with a reference maximum and a normaliser in fp32.
 //
-// Work split: one work-group owns 64 query rows of one (batch, query head) — a whole 64-token
-// query block, or half of a 128-token one (whole 128-row tiles when one head's K and V exceed
-// the last-level cache, see launch); each of its waves owns QW query rows (QW = 64 for
-// D = 64, 32 for D = 128), i.e. QW/32 column tiles of the 32x32 MFMA. Per selected key block each wave computes
+// Work split: one work-group owns the query rows of one query block of one (batch, query
+// head); each of its waves owns QW query rows (QW = 64 for D = 64, 32 for D = 128), i.e. QW/32
+// column tiles of the 32x32 MFMA. A 128-token selected block is walked in two 64-key steps,
+// so that one step's operands fit in registers with two waves per SIMD while every gathered
+// tile is still fetched once per query block. Per step each wave computes
 //   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q^T in registers)
 //   P^T = exp2(c*S^T - m)   (c = scale*log2(e), m = row reference, usually 0)
 //   O^T += V^T P^T (A = V^T via ds_read_b64_tr_b16 transpose reads of the row-major V tile,
@@ -59,19 +60,21 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void global_cvoid;
 
-template <int D, int BLK>
+// R query rows per work-group, KU keys per step (one K and one V tile in LDS)
+template <int D, int R, int KU>
 struct Cfg {
   static constexpr int QW = D == 64 ? 64 : 32;  // query rows per wave
   static constexpr int QC = QW / 32;           // 32-query column tiles per wave
-  static constexpr int NW = BLK / QW;          // waves
+  static constexpr int NW = R / QW;            // waves
   static constexpr int NT = NW * kWave;        // threads
-  static constexpr int TILE = BLK * D * 2;     // bytes of one K or V tile
+  static constexpr int TILE = KU * D * 2;      // bytes of one K or V tile
   static constexpr int DMA = TILE / 1024 / NW; // 1 KiB transfers per tile per wave
-  static constexpr int NKT = BLK / 32;         // 32-key sub-tiles per block
+  static constexpr int NKT = KU / 32;          // 32-key sub-tiles per step
   static constexpr int NS = D / 16;            // k-steps of Q K^T
   static constexpr int NDT = D / 32;           // 32-row d tiles of O^T
-  static constexpr int NPS = BLK / 16;         // k-steps of V^T P^T
+  static constexpr int NPS = KU / 16;          // k-steps of V^T P^T
   static_assert(DMA * NW * 1024 == TILE, "tile must split into whole 1 KiB transfers");
+  static_assert(DMA == 4 || DMA == 8, "the transfer sequences issue 4 or 8 spans of 1 KiB");
 };
 
 // vmcnt-only waits (expcnt and lgkmcnt left free), gfx9 s_waitcnt encoding
@@ -95,37 +98,34 @@ __device__ __forceinline__ s16x4 ds_read_tr16(const char* lds_bytes) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_void*)(lds_bytes));
 }
 
-// Rows per tile and per work-group (HALF): a 128-token selection block can run as 64-row
-// halves — a work-group takes half of a query block and each selected block as two 64-key
-// units. Whole 128-row tiles need every operand of a block in registers at once (one wave per
-// SIMD), halves fetch every gathered tile twice; the launch takes halves when one (batch, KV
-// head)'s K and V stay in the last-level cache.
-template <int SB, bool HALF>
-constexpr int tile_rows() { return HALF ? 64 : SB; }
-
+// A work-group takes R rows of a query block of SB tokens (R = SB, or R = 64: SB / R
+// work-groups per query block) and walks each selected block in steps of KU keys (SB / KU
+// steps). KU = 64 keeps one step's operands in registers with two waves per SIMD; a whole
+// 128-key step needs them all at once (one wave per SIMD). R = SB reads each gathered tile
+// once per query block, R = 64 once per row part.
+//
 // OVL: overlapping key blocks (key block j starts at token j*kstride; nkb of them): the tile of
 // block j starts at key_tile_start and its first key_tile_skip keys score -inf.
-template <int D, int SB, bool CAUSAL, bool HALF, bool OVL>
-__global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel(
+template <int D, int SB, int R, int KU, bool CAUSAL, bool OVL>
+__global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
     float* __restrict__ lse, int64_t N, int Hq, int Hkv, int nb, int topk, float c,
     uint32_t total_tiles, int nkb, int kstride) {
-  constexpr int BLK = tile_rows<SB, HALF>();  // rows of one tile and of this work-group
-  constexpr int UN = SB / BLK;                // tiles per selected block = work-groups per
-                                              // query block
-  using C = Cfg<D, BLK>;
-  __shared__ __attribute__((aligned(1024))) char Kl[C::TILE];   // [BLK][D] bf16, swizzled
+  constexpr int RP = SB / R;                  // work-groups (row parts) per query block
+  constexpr int UN = SB / KU;                 // steps per selected block
+  using C = Cfg<D, R, KU>;
+  __shared__ __attribute__((aligned(1024))) char Kl[C::TILE];   // [KU][D] bf16, swizzled
   __shared__ __attribute__((aligned(1024))) char Vl[C::TILE];
   __shared__ uint32_t chosen[OVL ? kMaxKeyBlocks / 32 : 1];   // OVL: the row's key blocks
 
-  // tile order: (b, kv head, head within group, query block, half); blocks reading the same
-  // K/V are consecutive and land on one XCD
+  // tile order: (b, kv head, head within group, query block, row part); blocks reading the
+  // same K/V are consecutive and land on one XCD
   const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
   const int G = Hq / Hkv;
-  const int i = (int)((tile / UN) % nb);
-  const int hq = (int)(tile % UN);            // which BLK rows of the query block
-  uint32_t rest = tile / UN / nb;
+  const int i = (int)((tile / RP) % nb);
+  const int hq = (int)(tile % RP);            // which R rows of the query block
+  uint32_t rest = tile / RP / nb;
   const int hh = (int)(rest % G);
   rest /= G;
   const int g = (int)(rest % Hkv);
@@ -138,7 +138,7 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
   const int64_t krs = (int64_t)Hkv * D;        // token stride of k/v
 
   // Q^T as B operands: lane holds q[row = QW*wave + 32*qc + l32][d = 16s + 8*half .. +7]
-  const int64_t qrow0 = (int64_t)b * N + (int64_t)i * SB + BLK * hq + C::QW * wave + l32;
+  const int64_t qrow0 = (int64_t)b * N + (int64_t)i * SB + R * hq + C::QW * wave + l32;
   bf16x8 qf[C::QC][C::NS];
 #pragma unroll
   for (int qc = 0; qc < C::QC; ++qc)
@@ -162,10 +162,10 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
     goff[x] = (uint32_t)((r * krs + swz(r, p) * 8) * 2);
   }
   bool bad = false;
-  auto tile_base = [&](int kb, int u) -> int64_t {   // unit u (BLK rows) of selected block kb
+  auto tile_base = [&](int kb, int u) -> int64_t {   // step u (KU keys) of selected block kb
     if ((unsigned)kb >= klim) { bad = true; kb = 0; }
     const int64_t first = OVL ? key_tile_start(kb, kstride, SB, N) : (int64_t)kb * SB;
-    return (first + BLK * u) * krs * 2;
+    return (first + KU * u) * krs * 2;
   };
   auto skip_of = [&](int kb) -> int {          // OVL: leading keys of kb's tile left out
     if (!OVL || (unsigned)kb >= klim) return 0;
@@ -176,11 +176,23 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
   // read; the waits below are placed by hand (each wave issues exactly DMA transfers per tile
   // and no other vector-memory instruction inside the loop). M0 (the LDS destination) is
   // saved and restored around them.
-  static_assert(C::DMA == 8, "the transfer sequence below issues 8 spans of 1 KiB");
   auto dma = [&](const char* src_base, char* dst) {
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(lds_void*)dst + wave * C::DMA * 1024);
     uint32_t m0_saved;
+    if constexpr (C::DMA == 4) {
+      asm volatile(
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %6\n\t"
+          "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %6\n\t"
+          "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %6\n\t"
+          "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %6\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(m0_saved)
+          : "s"(lds0), "v"(goff[0]), "v"(goff[1]), "v"(goff[2]), "v"(goff[3]), "s"(src_base)
+          : "memory", "scc");
+      return;
+    } else {
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %10\n\t"
@@ -196,6 +208,7 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
         : "s"(lds0), "v"(goff[0]), "v"(goff[1]), "v"(goff[2]), "v"(goff[3]), "v"(goff[4]),
           "v"(goff[5]), "v"(goff[6]), "v"(goff[7]), "s"(src_base)
         : "memory", "scc");
+    }
   };
 
   // LDS read offsets of this lane
@@ -241,7 +254,7 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
     dma(vbase0 + tb, Vl);
   }
 
-  for (int t = 0; t < kcount * UN; ++t) {     // units: UN per selected block
+  for (int t = 0; t < kcount * UN; ++t) {     // steps: UN per selected block
     const bool more = t + 1 < kcount * UN;
     const int kb_next = more ? myidx[(t + 1) / UN] : 0;
     const int u_next = (t + 1) % UN;
@@ -280,19 +293,19 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
         for (int qc = 0; qc < C::QC; ++qc)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = BLK * u_cur + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-            const int qry = BLK * hq + C::QW * wave + 32 * qc + l32;
+            const int key = KU * u_cur + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+            const int qry = R * hq + C::QW * wave + 32 * qc + l32;
             if (key > qry) sacc[kt][qc][r] = -__builtin_inff();
           }
     }
-    if (OVL && skip_cur > BLK * u_cur) {       // keys before the block or held by block kb-1
+    if (OVL && skip_cur > KU * u_cur) {        // keys before the block or held by block kb-1
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
         for (int qc = 0; qc < C::QC; ++qc)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = BLK * u_cur + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+            const int key = KU * u_cur + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
             if (key < skip_cur) sacc[kt][qc][r] = -__builtin_inff();
           }
     }
@@ -335,7 +348,7 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
         const float bm = row_max(qc);
         const float l_row = lsum[qc] + __shfl_xor(lsum[qc], 32);   // same on both lanes
         if (l_row == 0.f) {                    // nothing accumulated yet: O and l are zero
-          if (bm != -__builtin_inff()) mc[qc] = bm;   // (a unit whose keys are all left out)
+          if (bm != -__builtin_inff()) mc[qc] = bm;   // (a step whose keys are all left out)
         } else {
           const float m_new = fmaxf(mc[qc], bm);
           const float alpha = __builtin_amdgcn_exp2f(mc[qc] - m_new);
@@ -406,20 +419,19 @@ __global__ __launch_bounds__((HALF ? 64 : SB) / (D == 64 ? 64 : 32) * 64) void a
   }
 }
 
-template <int D, int BLK, bool HALF>
+template <int D, int SB, int R, int KU>
 hipError_t launch_tiles(int64_t B, int64_t N, int Hq, int Hkv, int topk, const void* q,
                         const void* k, const void* v, const int32_t* idx, float c, void* out,
                         float* lse, bool causal, int nkb, int kstride, hipStream_t stream) {
-  const int nb = (int)(N / BLK);
-  constexpr int TR = tile_rows<BLK, HALF>();
-  const uint32_t total = (uint32_t)(B * Hq * nb * (BLK / TR));
+  const int nb = (int)(N / SB);
+  const uint32_t total = (uint32_t)(B * Hq * nb * (SB / R));
 #define BSATTN_BF16_LAUNCH(causal_, ovl_)                                                     \
-  attn_bf16_kernel<D, BLK, causal_, HALF, ovl_><<<total, Cfg<D, TR>::NT, 0, stream>>>(        \
+  attn_bf16_kernel<D, SB, R, KU, causal_, ovl_><<<total, Cfg<D, R, KU>::NT, 0, stream>>>(     \
       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, (uint16_t*)out, lse, N, \
       Hq, Hkv, nb, topk, c, total, nkb, kstride)
   if (causal)
     BSATTN_BF16_LAUNCH(true, false);
-  else if (kstride != BLK)
+  else if (kstride != SB)
     BSATTN_BF16_LAUNCH(false, true);
   else
     BSATTN_BF16_LAUNCH(false, false);
@@ -427,21 +439,16 @@ hipError_t launch_tiles(int64_t B, int64_t N, int Hq, int Hkv, int topk, const v
   return hipGetLastError();
 }
 
-// K and V of one (batch, KV head) up to this size: 128-token blocks run as 64-row halves (the
-// gathered tiles, fetched twice, come from the 256 MB last-level cache); beyond, whole tiles.
-constexpr int64_t kHalfTileMaxBytes = 64ll << 20;
-
-template <int D, int BLK>
+template <int D, int SB>
 hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int topk, const void* q, const void* k,
                   const void* v, const int32_t* idx, float c, void* out, float* lse,
                   bool causal, int nkb, int kstride, hipStream_t stream) {
-  if constexpr (BLK == 128) {
-    if (N * D * 2 * 2 <= kHalfTileMaxBytes)
-      return launch_tiles<D, BLK, true>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal,
+  if constexpr (SB == 128)
+    return launch_tiles<D, SB, 128, 64>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal,
                                         nkb, kstride, stream);
-  }
-  return launch_tiles<D, BLK, false>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal,
-                                     nkb, kstride, stream);
+  else
+    return launch_tiles<D, SB, SB, SB>(B, N, Hq, Hkv, topk, q, k, v, idx, c, out, lse, causal,
+                                       nkb, kstride, stream);
 }
 
 }  // namespace

@@ -91,8 +91,8 @@ FWD_SHAPES = [
     # B, N, Hq, Hkv, D, block, key_stride, topk
     (2, 64 * 38, 4, 2, 64, 64, 48, 7),
     (1, 64 * 30, 2, 1, 128, 64, 48, 12),
-    (1, 128 * 21, 6, 3, 128, 128, 96, 5),   # 64-row halves: the skip falls in the first half
-    (1, 128 * 12, 2, 1, 64, 128, 64, 6),    # stride block/2: a skipped first half is all -inf
+    (1, 128 * 21, 6, 3, 128, 128, 96, 5),   # 64-key steps: the skip falls in the first step
+    (1, 128 * 12, 2, 1, 64, 128, 64, 6),    # stride block/2: a skipped first step is all -inf
     (1, 128 * 12, 2, 2, 128, 128, 64, 6),
     (2, 64 * 16, 2, 2, 64, 64, 32, 5),
 ]
@@ -176,14 +176,14 @@ def test_forward_overlap_every_block_is_dense(dtype):
 
 
 @pytest.mark.parametrize("shape", [
-    # K and V of one (batch, KV head) above 64 MiB: whole 128-row tiles
+    # 1536 key blocks of 128 tokens, K and V of the head above 64 MiB
     (1, 128 * 1152, 2, 1, 128, 128, 96, 9),
 ], ids=str)
-def test_forward_overlap_whole_tiles(shape):
+def test_forward_overlap_large_head(shape):
     B, N, Hq, Hkv, D, blk, ks, topk = shape
     assert N * D * 2 * 2 > 64 << 20
     nkb = bst.key_blocks(N, blk, ks)
-    say(f"[forward overlap, whole tiles] shape={shape} key blocks={nkb}")
+    say(f"[forward overlap, large head] shape={shape} key blocks={nkb}")
     q, k, v, ds = syn.iid_inputs(B, N, Hq, Hkv, D, "bf16", index=31, device=DEV)
     idx = syn.random_block_sets(B, Hq, N // blk, nkb, topk, index=31, device=DEV)
     out = bst.forward(q, k, v, idx, key_stride=ks)

@@ -97,15 +97,15 @@ def test_forward_causal(shape, dtype):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [
-    # K and V of one (batch, KV head) above 64 MiB: 128-token blocks run as whole 128-row
-    # tiles, not as 64-row halves (the launch picks by that footprint)
+    # K and V of one (batch, KV head) above the 4 MB L2 and 64 MiB: 128-token blocks in
+    # 64-key steps with gathered tiles from the last-level cache or HBM, >1024 key blocks
     (1, 128 * 1152, 2, 1, 128, 128, 9),
     (1, 128 * 2112, 1, 1, 64, 128, 6),
 ], ids=str)
-def test_forward_block128_whole_tiles(shape, causal):
+def test_forward_block128_large_heads(shape, causal):
     B, N, Hq, Hkv, D, blk, topk = shape
     assert N * D * 2 * 2 > 64 << 20
-    say(f"[block 128 whole tiles] shape={shape} causal={causal}")
+    say(f"[block 128, large heads] shape={shape} causal={causal}")
     q, k, v, ds = syn.iid_inputs(B, N, Hq, Hkv, D, "bf16", index=23, device=DEV)
     ws = torch.empty(bst.select_workspace_bytes(B, N, Hq, Hkv, D, blk), dtype=torch.uint8,
                      device=DEV)
