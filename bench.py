@@ -72,6 +72,44 @@ def traffic_per_launch():
         return None
 
 
+def achievable_peaks(L, device, stream, reps=3):
+    """What the chip sustains (include/bsattn_probe.h): dense bf16 MFMA TFLOP/s, HBM read GB/s,
+    HBM copy GB/s (read + written bytes), each the best of `reps` HIP-event-timed launches."""
+    import ctypes
+    import torch
+    groups = 2048                                   # 8 work-groups of 4 waves per CU
+    sink = torch.empty(L.bsattn_probe_sink_floats(groups), dtype=torch.float32, device=device)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    nbytes = 1 << 30
+    src = torch.empty(2 * nbytes, dtype=torch.uint8, device=device)
+    src[:nbytes].fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    flops = ctypes.c_double(0.0)
+
+    def best(call, work):
+        call()                                      # warm-up
+        out = 0.0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            e1.synchronize()
+            out = max(out, work / (e0.elapsed_time(e1) / 1e3))
+        return out
+
+    def mfma():
+        assert L.bsattn_probe_mfma_bf16(20000, groups, P(sink), ctypes.byref(flops), sp) == 0
+    mfma()
+    tf = best(mfma, flops.value) / 1e12
+    rd = best(lambda: L.bsattn_probe_read(P(src), 2 * nbytes, groups, P(sink), sp), 2 * nbytes) / 1e9
+    cp = best(lambda: L.bsattn_probe_copy(P(src), P(dst), nbytes, groups, sp), 2 * nbytes) / 1e9
+    del src, dst
+    return {"mfma_bf16_tflops": round(tf, 1), "hbm_read_gbs": round(rd, 1),
+            "hbm_copy_gbs": round(cp, 1)}
+
+
 def cpu_baseline(w, q, k, v, ds, max_batches, budget_s=10.0, causal=False, pooling="mean",
                  group=False, key_stride=0):
     """The fp64 oracle, as it stands, on batch elements 0, 1, ... of the workload until
@@ -335,6 +373,13 @@ def main():
         "select_hbm_frac": round(sel_bytes / (sel_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "select_algorithmic_bytes": sel_bytes,
     }
+    if w.dtype == "bf16":
+        ach = achievable_peaks(L, dev, stream)
+        rec["achievable"] = ach
+        rec["roofline"]["achievable_peak"] = ach["mfma_bf16_tflops"]
+        rec["roofline"]["achievable_frac"] = round(achieved / ach["mfma_bf16_tflops"], 4)
+        rec["select_achievable_hbm_frac"] = round(
+            sel_bytes / (sel_ms / 1e3) / 1e9 / ach["hbm_read_gbs"], 4)
     if args.backward:
         rec["backward"] = time_backward(args, w, q, k, v, idx, out, topk, scale, flags, L, P, sp,
                                         stream, flops)

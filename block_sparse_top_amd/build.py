@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbsattn.so")
 SOURCES = ["api.hip", "pool.hip", "select.hip", "select_large.hip", "attn_bf16.hip", "attn_f32.hip", "attn_fp8.hip",
-           "validate.hip", "attn_bwd.hip", "decode.hip"]
+           "validate.hip", "attn_bwd.hip", "decode.hip", "probe.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include "../../include/bsattn.h"
+#include "../../include/bsattn_probe.h"
 #include "launch.h"
 
 namespace {
@@ -408,6 +409,39 @@ int bsattn_decode(int dtype, int64_t B, int64_t Lmax, int Hq, int Hkv, int D, in
                                           kbar, lens, scale, out, idx, workspace,
                                           (hipStream_t)stream),
                     "decode launch");
+}
+
+// ---- achievable-peak probes (include/bsattn_probe.h)
+
+size_t bsattn_probe_sink_floats(int groups) { return groups > 0 ? (size_t)groups * 256 : 0; }
+
+int bsattn_probe_mfma_bf16(int64_t iters, int groups, float* sink, double* flops, void* stream) {
+  if (iters < 1 || iters > ((int64_t)1 << 30) || groups < 1 || groups > 65535)
+    return fail(BSATTN_E_INVALID, "iters in [1, 2^30] and groups in [1, 65535] required");
+  if (!sink || ((uintptr_t)sink & 3u)) return fail(BSATTN_E_INVALID, "sink null or unaligned");
+  if (flops) *flops = 2.0 * 32 * 32 * 16 * 8 * 4 * (double)groups * (double)iters;
+  return hip_status(bsattn::launch_probe_mfma_bf16(iters, groups, sink, (hipStream_t)stream),
+                    "mfma probe launch");
+}
+
+int bsattn_probe_read(const void* src, size_t bytes, int groups, float* sink, void* stream) {
+  if (!src || !sink || !aligned16(src) || ((uintptr_t)sink & 3u) || bytes == 0 || bytes % 16 ||
+      groups < 1 || groups > 65535)
+    return fail(BSATTN_E_INVALID, "read probe: bad pointer, size or group count");
+  return hip_status(bsattn::launch_probe_read(src, (int64_t)(bytes / 16), groups, sink,
+                                              (hipStream_t)stream),
+                    "read probe launch");
+}
+
+int bsattn_probe_copy(const void* src, void* dst, size_t bytes, int groups, void* stream) {
+  if (!src || !dst || !aligned16(src) || !aligned16(dst) || bytes == 0 || bytes % 16 ||
+      groups < 1 || groups > 65535)
+    return fail(BSATTN_E_INVALID, "copy probe: bad pointer, size or group count");
+  const char *s0 = (const char*)src, *d0 = (const char*)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(BSATTN_E_INVALID, "copy probe: overlap");
+  return hip_status(bsattn::launch_probe_copy(src, dst, (int64_t)(bytes / 16), groups,
+                                              (hipStream_t)stream),
+                    "copy probe launch");
 }
 
 }  // extern "C"

@@ -1,0 +1,107 @@
+// Achievable-peak probes (measurement support, declared in include/bsattn_probe.h): what this
+// chip sustains for the two resources the path is bound by, to set next to the vendor peaks.
+//
+// mfma_bf16_kernel: every wave issues chains of independent v_mfma_f32_32x32x16_bf16 (eight
+// accumulators, so that each MFMA waits on nothing) for `iters` rounds; the operands stay in
+// registers, so nothing but the matrix cores is exercised. Each chain has its own operands,
+// pseudo-random values of unit scale (as attention's bf16 operands are), so consecutive MFMAs
+// switch data as real work does: constant or tiny operands draw less power and let the chip
+// hold a clock that real data does not. The accumulators are summed into one float per lane
+// at the end so that the work is not optimised away.
+// read_kernel: a grid-stride sum of a large buffer with 16-byte nontemporal loads, 8 in flight
+// per thread (HBM read rate). copy_kernel: 16-byte loads and stores (read + write rate).
+#include "common.h"
+#include "launch.h"
+
+namespace bsattn {
+namespace {
+
+constexpr int kChains = 8;
+
+// pseudo-random value in [-2, 2) from an integer (a 32-bit integer hash)
+__device__ __forceinline__ float unit_value(uint32_t x) {
+  x ^= x >> 16; x *= 0x7feb352dU; x ^= x >> 15; x *= 0x846ca68bU; x ^= x >> 16;
+  return (float)(x >> 8) * (4.0f / 16777216.0f) - 2.0f;
+}
+
+__global__ __launch_bounds__(256) void mfma_bf16_kernel(int64_t iters, float* __restrict__ sink) {
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  bf16x8 a[kChains], b[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[c][e] = (__bf16)unit_value(t * 131u + c * 17u + e);
+      b[c][e] = (__bf16)unit_value(t * 131u + c * 17u + e + 0x9e3779b9u);
+    }
+  f32x16 acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], b[c], acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                   float* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t x = 0;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4 w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= w[u].x ^ w[u].y ^ w[u].z ^ w[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 w = __builtin_nontemporal_load(src + i);
+    x ^= w.x ^ w.y ^ w.z ^ w.w;
+  }
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = (float)(x & 0xffff);
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
+                                                   u32x4* __restrict__ dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    u32x4 w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(w[u], dst + i + u * stride);
+  }
+  for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+}  // namespace
+
+hipError_t launch_probe_mfma_bf16(int64_t iters, int groups, float* sink, hipStream_t stream) {
+  mfma_bf16_kernel<<<groups, 256, 0, stream>>>(iters, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const void* src, int64_t n16, int groups, float* sink,
+                             hipStream_t stream) {
+  read_kernel<<<groups, 256, 0, stream>>>((const u32x4*)src, n16, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_copy(const void* src, void* dst, int64_t n16, int groups,
+                             hipStream_t stream) {
+  copy_kernel<<<groups, 256, 0, stream>>>((const u32x4*)src, (u32x4*)dst, n16);
+  return hipGetLastError();
+}
+
+}  // namespace bsattn

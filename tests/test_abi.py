@@ -11,15 +11,19 @@ import block_sparse_top_amd as bst
 from block_sparse_top_amd import bsattn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "bsattn.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call below fails first
 
 
 def declared_functions():
-    text = open(HEADER, encoding="utf-8").read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(bsattn_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = open(h, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(bsattn_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -28,7 +32,8 @@ def test_library_exports_every_declared_function():
     assert {"bsattn_select", "bsattn_forward", "bsattn_select_workspace_bytes",
             "bsattn_abi_version", "bsattn_status_str", "bsattn_last_error",
             "bsattn_select_ex", "bsattn_forward_ex", "bsattn_key_blocks",
-            "bsattn_select_workspace_bytes_ex"} <= set(names)
+            "bsattn_select_workspace_bytes_ex", "bsattn_probe_mfma_bf16", "bsattn_probe_read",
+            "bsattn_probe_copy", "bsattn_probe_sink_floats"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -217,3 +222,16 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 128, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         bst.select(x, x, 64, 1)
+
+
+def test_probe_rejects():
+    L = bst.lib()
+    fl = ctypes.c_double(0.0)
+    assert L.bsattn_probe_sink_floats(4) == 1024 and L.bsattn_probe_sink_floats(0) == 0
+    assert L.bsattn_probe_mfma_bf16(0, 4, FAKE, ctypes.byref(fl), None) == 1
+    assert L.bsattn_probe_mfma_bf16(10, 70000, FAKE, ctypes.byref(fl), None) == 1
+    assert L.bsattn_probe_mfma_bf16(10, 4, None, ctypes.byref(fl), None) == 1 and "sink" in last()
+    assert L.bsattn_probe_read(FAKE, 24, 4, FAKE, None) == 1
+    assert L.bsattn_probe_read(None, 32, 4, FAKE, None) == 1
+    assert L.bsattn_probe_copy(FAKE, ctypes.c_void_p(0x10010), 64, 4, None) == 1 and "overlap" in last()
+    assert L.bsattn_probe_copy(FAKE, ctypes.c_void_p(0x20000), 0, 4, None) == 1
