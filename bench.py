@@ -256,6 +256,10 @@ def bench_decode(args):
                      "algorithmic_bytes_per_step": total},
         "decode_ms": round(ms, 4),
     }
+    ach = achievable_peaks(L, q.device, stream)
+    rec["achievable"] = ach
+    rec["roofline"]["achievable_peak"] = ach["hbm_read_gbs"]
+    rec["roofline"]["achievable_frac"] = round(rec["roofline"]["achieved"] / ach["hbm_read_gbs"], 4)
     print(json.dumps(rec), flush=True)
 
 
