@@ -316,10 +316,10 @@ int bsattn_backward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int
   const int kind = dtype == BSATTN_F32 ? 0 : dtype == BSATTN_BF16 ? 1 : 2;
   if (!bsattn::attn_bwd_supported(kind, D, block))
     return fail(BSATTN_E_UNSUPPORTED, "backward for dtype %d D=%d block=%d (supported: bf16, "
-                                      "D 64 or 128, block 64)", dtype, D, block);
-  if (N / block > bsattn::kMaxBwdBlocks)
-    return fail(BSATTN_E_UNSUPPORTED, "backward over nb=%lld > %d blocks",
-                (long long)(N / block), bsattn::kMaxBwdBlocks);
+                                      "D 64 or 128, block 64 or 128)", dtype, D, block);
+  if (N / 64 > bsattn::kMaxBwdBlocks)
+    return fail(BSATTN_E_UNSUPPORTED, "backward over %lld 64-token blocks > %d",
+                (long long)(N / 64), bsattn::kMaxBwdBlocks);
   if (B == 0 || N == 0) return BSATTN_OK;
   if (!q || !k || !v || !idx || !out || !dout || !lse || !dq || !dk || !dv)
     return fail(BSATTN_E_INVALID, "null pointer argument");
@@ -331,9 +331,21 @@ int bsattn_backward(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int
   if (!workspace || workspace_bytes < need)
     return fail(BSATTN_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   if ((uintptr_t)workspace & 255u) return fail(BSATTN_E_WORKSPACE, "workspace not 256-byte aligned");
-  return hip_status(bsattn::launch_attn_bwd(B, N, Hq, Hkv, D, topk, flags & BSATTN_CAUSAL, q, k, v,
-                                            idx, out, dout, lse, scale, dq, dk, dv, workspace,
-                                            (hipStream_t)stream),
+  const bool causal = flags & BSATTN_CAUSAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (block == 128) {                         // as 64-token blocks with expanded index rows
+    int32_t* idx64 = (int32_t*)((char*)workspace +
+                                bsattn::attn_bwd_workspace_bytes(B, N, Hq, Hkv, 64, 2 * topk));
+    st = hip_status(bsattn::launch_expand_idx128(B * Hq * (N / 128), (int)(N / 128), topk,
+                                                 causal, idx, idx64, s),
+                    "index expansion launch");
+    if (st != BSATTN_OK) return st;
+    return hip_status(bsattn::launch_attn_bwd(B, N, Hq, Hkv, D, 2 * topk, causal, q, k, v, idx64,
+                                              out, dout, lse, scale, dq, dk, dv, workspace, s),
+                      "backward launch");
+  }
+  return hip_status(bsattn::launch_attn_bwd(B, N, Hq, Hkv, D, topk, causal, q, k, v, idx, out,
+                                            dout, lse, scale, dq, dk, dv, workspace, s),
                     "backward launch");
 }
 

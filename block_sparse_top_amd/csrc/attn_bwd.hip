@@ -481,16 +481,61 @@ hipError_t launch_bwd(int64_t B, int64_t N, int Hq, int Hkv, int topk, const voi
 
 }  // namespace
 
+namespace {
+
+// 128-token blocks as 64-token blocks: query block i (128 tokens) becomes the 64-token blocks
+// 2i and 2i+1, each selected block j the 64-token blocks 2j and 2j+1 (the key set of every
+// query is unchanged, so the gradients are those of the 128-token selection). Causal rows of
+// the first half leave out 2i+1, the second half of their own block, which lies after each of
+// their queries. An entry out of range becomes two out-of-range entries (skipped like it).
+// One thread per 64-token row.
+__global__ __launch_bounds__(256) void expand_idx128_kernel(const int32_t* __restrict__ idx,
+                                                            int32_t* __restrict__ idx64,
+                                                            int64_t rows, int nb, int topk,
+                                                            bool causal) {
+  const int64_t r64 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r64 >= 2 * rows) return;
+  const int64_t r = r64 >> 1;
+  const int part = (int)(r64 & 1), i = (int)(r % nb);
+  const int32_t* src = idx + r * topk;
+  int32_t* dst = idx64 + r64 * 2 * topk;
+  const int used = causal && i + 1 < topk ? i + 1 : topk;
+  int p = 0;
+  for (int t = 0; t < used; ++t) {
+    const int j = src[t];
+    if ((unsigned)j >= (unsigned)nb) {
+      dst[p++] = -1;
+      dst[p++] = -1;
+    } else {
+      dst[p++] = 2 * j;
+      if (!(causal && part == 0 && j == i)) dst[p++] = 2 * j + 1;
+    }
+  }
+  for (; p < 2 * topk; ++p) dst[p] = -1;
+}
+
+}  // namespace
+
 bool attn_bwd_supported(int dtype_kind, int D, int block) {
-  return dtype_kind == 1 && (D == 64 || D == 128) && block == kBlk;
+  return dtype_kind == 1 && (D == 64 || D == 128) && (block == kBlk || block == 2 * kBlk);
 }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int block, int topk) {
-  const int64_t nb = N / block;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  if (block == 2 * kBlk)                     // the 64-token form, then its index rows
+    return attn_bwd_workspace_bytes(B, N, Hq, Hkv, kBlk, 2 * topk) +
+           al((size_t)B * Hq * (N / kBlk) * 2 * topk * sizeof(int32_t));
+  const int64_t nb = N / block;
   return al((size_t)B * Hq * N * sizeof(float)) +                  // Dvec
          al((size_t)B * Hkv * (nb + 1) * sizeof(int32_t)) +        // offsets
          al((size_t)B * Hq * nb * topk * sizeof(int32_t));         // pairs
+}
+
+hipError_t launch_expand_idx128(int64_t rows, int nb, int topk, bool causal, const int32_t* idx,
+                                int32_t* idx64, hipStream_t stream) {
+  expand_idx128_kernel<<<(unsigned)((2 * rows + 255) / 256), 256, 0, stream>>>(idx, idx64, rows,
+                                                                            nb, topk, causal);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd(int64_t B, int64_t N, int Hq, int Hkv, int D, int topk, bool causal,

@@ -65,12 +65,16 @@ hipError_t launch_attn_fp8(int64_t B, int64_t N, int Hq, int Hkv, int D, int blo
                            float scale, const float* descale_qkv, void* out, float* lse,
                            bool causal, int key_stride, int64_t nkb, hipStream_t stream);
 
-// Backward (bf16 inputs, fp32 gradients): supported for block 64, D in {64, 128}.
+// Backward (bf16 inputs, fp32 gradients): supported for block 64 and 128, D in {64, 128}.
 // dtype_kind: 0 fp32, 1 bf16, 2 fp8. Workspace: Dvec [B,Hq,N] fp32, key-block offsets
-// [B,Hkv,nb+1], pair lists [B,Hq,nb,topk] int32.
+// [B,Hkv,nb+1], pair lists [B,Hq,nb,topk] int32 (block 128: those of the 64-token form with
+// 2*topk places, then its index rows [B,Hq,N/64,2*topk] written by launch_expand_idx128).
+// launch_attn_bwd works on 64-token blocks.
 constexpr int kMaxBwdBlocks = 4096;
 bool attn_bwd_supported(int dtype_kind, int D, int block);
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int block, int topk);
+hipError_t launch_expand_idx128(int64_t rows, int nb, int topk, bool causal, const int32_t* idx,
+                                int32_t* idx64, hipStream_t stream);
 hipError_t launch_attn_bwd(int64_t B, int64_t N, int Hq, int Hkv, int D, int topk, bool causal,
                            const void* q, const void* k, const void* v, const int32_t* idx,
                            const void* out, const void* dout, const float* lse, float scale,

@@ -211,7 +211,9 @@ int bsattn_forward_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, i
 
 /* Bytes of device workspace bsattn_backward needs (0 for an empty call): Dvec fp32
  * [B, Hq, N], key-block offsets int32 [B, Hkv, nb + 1], pair lists int32 [B, Hq, nb, topk],
- * each part 256-byte aligned. Returns 0 and records an error for invalid sizes. */
+ * each part 256-byte aligned; for block 128 those of the 64-token form (nb = N / 64, 2 * topk
+ * places) followed by its index rows, int32 [B, Hq, N / 64, 2 * topk]. Returns 0 and records
+ * an error for invalid sizes. */
 size_t bsattn_backward_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
                                        int topk);
 
@@ -224,8 +226,11 @@ size_t bsattn_backward_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, in
  *   dV_U += P^T dO_i, dP = dO_i V_U^T, dS = P * (dP - rowsum(dO_i * O_i)),
  *   dQ_i = scale * dS K_U, dK_U += scale * dS^T Q_i
  * (GQA: a KV head collects the contributions of all its query heads).
- * Supported: dtype BSATTN_BF16, D in {64, 128}, block 64, nb <= 4096, the plain key blocks
- * (a forward with key_stride 0 or block); other combinations give BSATTN_E_UNSUPPORTED. Products on bf16 MFMA with fp32 accumulation (P and dS rounded to bf16
+ * Supported: dtype BSATTN_BF16, D in {64, 128}, block 64 or 128, N / 64 <= 4096, the plain
+ * key blocks (a forward with key_stride 0 or block); other combinations give
+ * BSATTN_E_UNSUPPORTED. Block 128 runs as 64-token blocks: each 128-token query block as two
+ * 64-row halves over both halves of every selected block (the same key set per query), the
+ * index rows of that form written to the workspace first. Products on bf16 MFMA with fp32 accumulation (P and dS rounded to bf16
  * as MFMA operands); the key-side sums run in a fixed order, so results are reproducible.
  * Arguments
  *   dtype .. topk, flags  as for bsattn_forward_ex (BSATTN_CAUSAL selects the causal variant;

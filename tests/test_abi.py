@@ -180,8 +180,9 @@ def bwd(**kw):
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(dtype=0), 2, "backward"),
     (dict(dtype=2, D=128), 2, "backward"),
-    (dict(block=128, N=1024), 2, "block=128"),
-    (dict(N=64 * 5000, topk=3), 2, "nb=5000"),
+    (dict(block=32, N=1024), 2, "block=32"),
+    (dict(N=64 * 5000, topk=3), 2, "64-token blocks"),
+    (dict(block=128, N=128 * 2100, topk=3), 2, "64-token blocks"),
     (dict(flags=8), 1, "flags"),
     (dict(scale=0.0), 1, "scale"),
     (dict(t=None), 1, "null"),
@@ -198,6 +199,10 @@ def test_backward_workspace_bytes():
     n = L.bsattn_backward_workspace_bytes(2, 8192, 16, 4, 64, 64, 38)
     al = lambda x: (x + 255) // 256 * 256
     assert n == al(2 * 16 * 8192 * 4) + al(2 * 4 * 129 * 4) + al(2 * 16 * 128 * 38 * 4)
+    # block 128: the 64-token form with 2 * topk places, then its index rows
+    n = L.bsattn_backward_workspace_bytes(2, 8192, 16, 4, 64, 128, 19)
+    assert n == (al(2 * 16 * 8192 * 4) + al(2 * 4 * 129 * 4) + al(2 * 16 * 128 * 38 * 4)
+                 + al(2 * 16 * 128 * 38 * 4))
 
 
 def test_empty_calls_launch_nothing():

@@ -36,6 +36,11 @@ SHAPES = [
     (1, 64 * 20, 2, 2, 128, 64, 7),     # D 128
     (1, 64 * 8, 2, 1, 64, 64, 8),       # topk = nb (dense), GQA 2
     (2, 64 * 9, 2, 2, 64, 64, 1),       # topk = 1
+    # block 128 (run as 64-token halves over expanded index rows)
+    (1, 128 * 10, 4, 2, 128, 128, 4),   # GQA 2, D 128
+    (2, 128 * 6, 2, 2, 64, 128, 3),     # D 64
+    (1, 128 * 5, 2, 1, 64, 128, 5),     # topk = nb (dense), GQA 2
+    (1, 128 * 7, 2, 2, 128, 128, 1),    # topk = 1: causal rows hold only the own block
 ]
 
 
