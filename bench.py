@@ -103,11 +103,17 @@ def achievable_peaks(L, device, stream, reps=3):
         assert L.bsattn_probe_mfma_bf16(20000, groups, P(sink), ctypes.byref(flops), sp) == 0
     mfma()
     tf = best(mfma, flops.value) / 1e12
+    flops8 = ctypes.c_double(0.0)
+
+    def mfma8():
+        assert L.bsattn_probe_mfma_fp8(10000, groups, P(sink), ctypes.byref(flops8), sp) == 0
+    mfma8()
+    tf8 = best(mfma8, flops8.value) / 1e12
     rd = best(lambda: L.bsattn_probe_read(P(src), 2 * nbytes, groups, P(sink), sp), 2 * nbytes) / 1e9
     cp = best(lambda: L.bsattn_probe_copy(P(src), P(dst), nbytes, groups, sp), 2 * nbytes) / 1e9
     del src, dst
-    return {"mfma_bf16_tflops": round(tf, 1), "hbm_read_gbs": round(rd, 1),
-            "hbm_copy_gbs": round(cp, 1)}
+    return {"mfma_bf16_tflops": round(tf, 1), "mfma_fp8_tflops": round(tf8, 1),
+            "hbm_read_gbs": round(rd, 1), "hbm_copy_gbs": round(cp, 1)}
 
 
 def cpu_baseline(w, q, k, v, ds, max_batches, budget_s=10.0, causal=False, pooling="mean",
@@ -377,11 +383,12 @@ def main():
         "select_hbm_frac": round(sel_bytes / (sel_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "select_algorithmic_bytes": sel_bytes,
     }
-    if w.dtype == "bf16":
+    if w.dtype in ("bf16", "fp8"):
         ach = achievable_peaks(L, dev, stream)
         rec["achievable"] = ach
-        rec["roofline"]["achievable_peak"] = ach["mfma_bf16_tflops"]
-        rec["roofline"]["achievable_frac"] = round(achieved / ach["mfma_bf16_tflops"], 4)
+        apeak = ach["mfma_bf16_tflops" if w.dtype == "bf16" else "mfma_fp8_tflops"]
+        rec["roofline"]["achievable_peak"] = apeak
+        rec["roofline"]["achievable_frac"] = round(achieved / apeak, 4)
         rec["select_achievable_hbm_frac"] = round(
             sel_bytes / (sel_ms / 1e3) / 1e9 / ach["hbm_read_gbs"], 4)
     if args.backward:

@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
     L.bsattn_probe_sink_floats.argtypes = [i32]
     L.bsattn_probe_mfma_bf16.restype = i32
     L.bsattn_probe_mfma_bf16.argtypes = [i64, i32, vp, ctypes.POINTER(ctypes.c_double), vp]
+    L.bsattn_probe_mfma_fp8.restype = i32
+    L.bsattn_probe_mfma_fp8.argtypes = [i64, i32, vp, ctypes.POINTER(ctypes.c_double), vp]
     L.bsattn_probe_read.restype = i32
     L.bsattn_probe_read.argtypes = [vp, sz, i32, vp, vp]
     L.bsattn_probe_copy.restype = i32

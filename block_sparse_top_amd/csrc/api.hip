@@ -436,6 +436,15 @@ int bsattn_probe_mfma_bf16(int64_t iters, int groups, float* sink, double* flops
                     "mfma probe launch");
 }
 
+int bsattn_probe_mfma_fp8(int64_t iters, int groups, float* sink, double* flops, void* stream) {
+  if (iters < 1 || iters > ((int64_t)1 << 30) || groups < 1 || groups > 65535)
+    return fail(BSATTN_E_INVALID, "iters in [1, 2^30] and groups in [1, 65535] required");
+  if (!sink || ((uintptr_t)sink & 3u)) return fail(BSATTN_E_INVALID, "sink null or unaligned");
+  if (flops) *flops = 2.0 * 32 * 32 * 64 * 8 * 4 * (double)groups * (double)iters;
+  return hip_status(bsattn::launch_probe_mfma_fp8(iters, groups, sink, (hipStream_t)stream),
+                    "mfma fp8 probe launch");
+}
+
 int bsattn_probe_read(const void* src, size_t bytes, int groups, float* sink, void* stream) {
   if (!src || !sink || !aligned16(src) || ((uintptr_t)sink & 3u) || bytes == 0 || bytes % 16 ||
       groups < 1 || groups > 65535)

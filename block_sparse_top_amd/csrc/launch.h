@@ -103,6 +103,7 @@ hipError_t validate_idx(int64_t rows, int topk, int nb, int nkb, const int32_t* 
 
 // Achievable-peak probes (measurement support; no part of the method).
 hipError_t launch_probe_mfma_bf16(int64_t iters, int groups, float* sink, hipStream_t stream);
+hipError_t launch_probe_mfma_fp8(int64_t iters, int groups, float* sink, hipStream_t stream);
 hipError_t launch_probe_read(const void* src, int64_t n16, int groups, float* sink,
                              hipStream_t stream);
 hipError_t launch_probe_copy(const void* src, void* dst, int64_t n16, int groups,

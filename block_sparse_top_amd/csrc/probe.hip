@@ -7,7 +7,7 @@
 // pseudo-random values of unit scale (as attention's bf16 operands are), so consecutive MFMAs
 // switch data as real work does: constant or tiny operands draw less power and let the chip
 // hold a clock that real data does not. The accumulators are summed into one float per lane
-// at the end so that the work is not optimised away.
+// at the end so that the work is not optimised away. mfma_fp8_kernel: the same on the fp8 MFMA.
 // read_kernel: a grid-stride sum of a large buffer with 16-byte nontemporal loads, 8 in flight
 // per thread (HBM read rate). copy_kernel: 16-byte loads and stores (read + write rate).
 #include "common.h"
@@ -43,6 +43,42 @@ __global__ __launch_bounds__(256) void mfma_bf16_kernel(int64_t iters, float* __
 #pragma unroll
     for (int c = 0; c < kChains; ++c)
       acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], b[c], acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// the same stream on the fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, e4m3 operands, unit
+// scales); operand bytes are pseudo-random e4m3 codes of unit scale (exponent field 5..8)
+__global__ __launch_bounds__(256) void mfma_fp8_kernel(int64_t iters, float* __restrict__ sink) {
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  i32x8 a[kChains], b[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t ra = __float_as_uint(unit_value(t * 131u + c * 17u + e));
+      const uint32_t rb = __float_as_uint(unit_value(t * 131u + c * 17u + e + 0x9e3779b9u));
+      // four codes per word: sign and mantissa from the hash, exponent field 5 + (bits & 3)
+      a[c][e] = (int)((ra & 0x87878787u) | (((ra >> 3) & 0x03030303u) + 0x05050505u) << 3);
+      b[c][e] = (int)((rb & 0x87878787u) | (((rb >> 3) & 0x03030303u) + 0x05050505u) << 3);
+    }
+  f32x16 acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[c], b[c], acc[c], 0, 0, 0, 127,
+                                                               0, 127);
   }
   float s = 0.f;
 #pragma unroll
@@ -89,6 +125,11 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
 
 hipError_t launch_probe_mfma_bf16(int64_t iters, int groups, float* sink, hipStream_t stream) {
   mfma_bf16_kernel<<<groups, 256, 0, stream>>>(iters, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_mfma_fp8(int64_t iters, int groups, float* sink, hipStream_t stream) {
+  mfma_fp8_kernel<<<groups, 256, 0, stream>>>(iters, sink);
   return hipGetLastError();
 }
 

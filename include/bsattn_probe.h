@@ -28,6 +28,10 @@ size_t bsattn_probe_sink_floats(int groups);
  * 1 <= iters <= 2^30; else BSATTN_E_INVALID. */
 int bsattn_probe_mfma_bf16(int64_t iters, int groups, float* sink, double* flops, void* stream);
 
+/* The same on the fp8 MFMA: iters x 8 independent v_mfma_scale_f32_32x32x64_f8f6f4 per wave
+ * (e4m3 operands of unit scale, unit block scales; 32x32x64 multiply-adds each). */
+int bsattn_probe_mfma_fp8(int64_t iters, int groups, float* sink, double* flops, void* stream);
+
 /* HBM read stream: reads `bytes` (a multiple of 16, > 0) from src (device, 16-byte aligned)
  * once with 16-byte loads in `groups` work-groups of 256 threads; sink as above. */
 int bsattn_probe_read(const void* src, size_t bytes, int groups, float* sink, void* stream);

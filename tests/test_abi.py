@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
             "bsattn_abi_version", "bsattn_status_str", "bsattn_last_error",
             "bsattn_select_ex", "bsattn_forward_ex", "bsattn_key_blocks",
             "bsattn_select_workspace_bytes_ex", "bsattn_probe_mfma_bf16", "bsattn_probe_read",
-            "bsattn_probe_copy", "bsattn_probe_sink_floats"} <= set(names)
+            "bsattn_probe_copy", "bsattn_probe_sink_floats", "bsattn_probe_mfma_fp8"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 

@@ -24,6 +24,10 @@ def test_probes_run_and_copy_is_exact():
     torch.cuda.synchronize()
     assert fl.value == 2.0 * 32 * 32 * 16 * 8 * 4 * groups * 100
     assert torch.isfinite(sink).all()
+    assert L.bsattn_probe_mfma_fp8(100, groups, P(sink), ctypes.byref(fl), sp) == 0
+    torch.cuda.synchronize()
+    assert fl.value == 2.0 * 32 * 32 * 64 * 8 * 4 * groups * 100
+    assert torch.isfinite(sink).all()
     g = torch.Generator(device=DEV).manual_seed(5)
     src = torch.randint(0, 256, (3 << 20,), dtype=torch.uint8, device=DEV, generator=g)
     dst = torch.zeros_like(src)
