@@ -177,9 +177,6 @@ int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, in
     return fail(BSATTN_E_UNSUPPORTED,
                 "selection over nb=%lld blocks (supported: nb <= %d, or a multiple of 64 up to %d)",
                 (long long)nb, bsattn::kMaxFusedBlocks, bsattn::kMaxLargeBlocks);
-  if (large && (flags & BSATTN_GROUP_SELECT))
-    return fail(BSATTN_E_UNSUPPORTED, "group selection over nb=%lld > %d blocks",
-                (long long)nb, bsattn::kMaxFusedBlocks);
   if (large && nrand > 0)
     return fail(BSATTN_E_UNSUPPORTED, "random places over nb=%lld > %d blocks", (long long)nb,
                 bsattn::kMaxFusedBlocks);
@@ -202,10 +199,12 @@ int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, in
                                         kbar, pmax, s),
                     "pool launch");
     if (st != BSATTN_OK) return st;
-    st = hip_status(bsattn::launch_scores_large(B, Hq, Hkv, (int)nb, D, qbar, kbar, S, s),
+    const bool group = flags & BSATTN_GROUP_SELECT;
+    st = hip_status(bsattn::launch_scores_large(B, Hq, Hkv, (int)nb, D, qbar, kbar, S, group, s),
                     "score launch");
     if (st != BSATTN_OK) return st;
-    return hip_status(bsattn::launch_topk_rows(B * Hq * nb, (int)nb, topk, S, idx, causal, s),
+    return hip_status(bsattn::launch_topk_rows(B * (group ? Hkv : Hq) * nb, (int)nb, topk, S, idx,
+                                               causal, group ? Hq / Hkv : 1, s),
                       "top-k launch");
   }
   st = hip_status(bsattn::launch_pool(kind, 2, B, N, Hq, Hkv, D, block, ks, nkb, q, k, qbar,

@@ -119,15 +119,17 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
   __shared__ __attribute__((aligned(1024))) char Vl[C::TILE];
   __shared__ uint32_t chosen[OVL ? kMaxKeyBlocks / 32 : 1];   // OVL: the row's key blocks
 
-  // tile order: (b, kv head, head within group, query block, row part); blocks reading the
-  // same K/V are consecutive and land on one XCD
+  // tile order: (b, kv head, query block, head within group, row part); blocks reading the
+  // same K/V are consecutive and land on one XCD, and the G heads of a query block (which
+  // read the same tiles under a group-shared selection) run side by side
   const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
   const int G = Hq / Hkv;
-  const int i = (int)((tile / RP) % nb);
   const int hq = (int)(tile % RP);            // which R rows of the query block
-  uint32_t rest = tile / RP / nb;
+  uint32_t rest = tile / RP;
   const int hh = (int)(rest % G);
   rest /= G;
+  const int i = (int)(rest % nb);
+  rest /= nb;
   const int g = (int)(rest % Hkv);
   const int b = (int)(rest / Hkv);
   const int h = g * G + hh;

@@ -23,7 +23,8 @@ hipError_t launch_pool_score_select(int kind, int64_t B, int64_t N, int Hq, int 
                                     int nrand, uint64_t seed, hipStream_t stream);
 
 // Steps 2-3 for nb > kMaxFusedBlocks (nb % 64 == 0, nb <= kMaxLargeBlocks): S = scores
-// [B, Hq, nb, nb] fp32 in the workspace, then the top-k of each of its rows.
+// [B, Hq, nb, nb] fp32 in the workspace ([B, Hkv, nb, nb] with group), then the top-k of each
+// of its rows.
 constexpr int kMaxLargeBlocks = 8192;
 
 // Whether a selection over nb key blocks writes the score matrix to the workspace (measured:
@@ -33,10 +34,13 @@ inline bool materialized_scores(int64_t nb, bool group) {
   (void)group;
   return nb > kMaxFusedBlocks;
 }
-hipError_t launch_scores_large(int64_t B, int Hq, int Hkv, int nb, int D, const float* qbar,
-                               const float* kbar, float* S, hipStream_t stream);
+// group: the pooled queries of each KV group are summed in place into the rows of its first
+// head and S holds one [nb, nb] matrix per (batch, KV head); topk_rows then writes each row to
+// the idx rows of the G heads of its group (G = 1: one row each).
+hipError_t launch_scores_large(int64_t B, int Hq, int Hkv, int nb, int D, float* qbar,
+                               const float* kbar, float* S, bool group, hipStream_t stream);
 hipError_t launch_topk_rows(int64_t rows, int nb, int topk, const float* S, int32_t* idx,
-                            bool causal, hipStream_t stream);
+                            bool causal, int G, hipStream_t stream);
 
 // Overlapping key blocks: at most this many per sequence in attention (an LDS bitmap of a
 // row's chosen blocks); the selection takes up to kMaxFusedBlocks of them.

@@ -20,6 +20,11 @@
 // Output positions come from block-wide exclusive scans, so the row is written in ascending j.
 // Causal option: as in the fused kernel, columns j > i get key 0, column i the largest key,
 // the row keeps min(topk, i+1) blocks and its remaining places are set to -1.
+//
+// Group-shared selection (GQA, MSA §3.1): group_sum_kernel adds the pooled queries of each
+// group's G heads into the rows of its first head (the scores of the sum are the sum of the
+// heads' scores), the product runs once per (batch, KV head) on those rows, and each row's
+// top-k is written to the idx rows of all G heads.
 #include "common.h"
 #include "launch.h"
 
@@ -32,15 +37,18 @@ typedef float f32x16v __attribute__((ext_vector_type(16)));
 __global__ __launch_bounds__(64) void score_gemm_kernel(const float* __restrict__ qbar,
                                                         const float* __restrict__ kbar,
                                                         float* __restrict__ S, int Hq, int Hkv,
-                                                        int nb, int D, int tiles) {
-  // tile index: (b*Hq + h) * tiles^2 + ti * tiles + tj, 64x64 each
-  // tiles of one (batch, head) share their pooled rows: keep them on one XCD's L2
+                                                        int nb, int D, int tiles, bool group) {
+  // tile index: (b*HS + s) * tiles^2 + ti * tiles + tj, 64x64 each, s a selection head (a
+  // query head, or a KV head whose group's summed queries sit in the rows of its first head);
+  // tiles of one (batch, selection head) share their pooled rows: keep them on one XCD's L2
+  const int G = Hq / Hkv, HS = group ? Hkv : Hq;
   const int64_t t = xcd_remap(blockIdx.x, gridDim.x);
   const int tj = (int)(t % tiles), ti = (int)((t / tiles) % tiles);
-  const int64_t bh = t / ((int64_t)tiles * tiles);
-  const int h = (int)(bh % Hq), b = (int)(bh / Hq);
-  const int g = h / (Hq / Hkv);
-  const float* Q = qbar + bh * nb * D;
+  const int64_t bh = t / ((int64_t)tiles * tiles);   // b * HS + s
+  const int sh = (int)(bh % HS), b = (int)(bh / HS);
+  const int hq = group ? sh * G : sh;                 // query head of the pooled rows
+  const int g = group ? sh : sh / G;
+  const float* Q = qbar + ((int64_t)b * Hq + hq) * nb * D;
   const float* K = kbar + ((int64_t)b * Hkv + g) * nb * D;
   const int lane = threadIdx.x, l32 = lane & 31, half = lane >> 5;
   const int half_d = D / 2;
@@ -126,9 +134,12 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total)
   return before + incl - v;
 }
 
+// rows of S: (b * HS + s) * nb + i; the top-k of a row goes to the idx rows of the G query
+// heads s*G .. s*G+G-1 of a group (group), or of query head s
 __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __restrict__ S,
                                                                  int32_t* __restrict__ idx,
-                                                                 int nb, int topk, bool causal) {
+                                                                 int nb, int topk, bool causal,
+                                                                 int G) {
   __shared__ int red[4];
   const int64_t row = blockIdx.x;
   const int i = (int)(row % nb);           // query block of this row
@@ -178,31 +189,57 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
     eq_seen += is_eq;
   }
   int tot_sel;
-  int pos = block_exclusive_scan(sel, red, &tot_sel);
-  int32_t* out = idx + row * topk;
-  eq_seen = eq_before;
+  const int pos0 = block_exclusive_scan(sel, red, &tot_sel);
+  const int64_t bs = row / nb;             // b * HS + s
+  for (int hh = 0; hh < G; ++hh) {
+    int32_t* out = idx + ((bs * G + hh) * nb + i) * topk;
+    int pos = pos0;
+    eq_seen = eq_before;
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    const bool is_eq = (j0 + e < lim) && key[e] == T;
-    if (key[e] > T || (is_eq && eq_seen < need)) out[pos++] = j0 + e;
-    eq_seen += is_eq;
+    for (int e = 0; e < kPerThread; ++e) {
+      const bool is_eq = (j0 + e < lim) && key[e] == T;
+      if (key[e] > T || (is_eq && eq_seen < need)) out[pos++] = j0 + e;
+      eq_seen += is_eq;
+    }
+    for (int p = kr + t; p < topk; p += kTopkThreads) out[p] = -1;   // unused causal places
   }
-  for (int p = kr + t; p < topk; p += kTopkThreads) out[p] = -1;   // unused causal places
+}
+
+// in place: rows of head g*G of each group += rows of heads g*G+1 .. g*G+G-1, in head order
+__global__ __launch_bounds__(256) void group_sum_kernel(float* __restrict__ qbar, int64_t B,
+                                                        int Hq, int Hkv, int64_t per_head) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, g, element)
+  if (e >= B * Hkv * per_head) return;
+  const int G = Hq / Hkv;
+  const int64_t bg = e / per_head, x = e % per_head;
+  float* first = qbar + bg * G * per_head + x;       // head g*G of batch b
+  float s = first[0];
+  for (int hh = 1; hh < G; ++hh) s += first[hh * per_head];
+  first[0] = s;
 }
 
 }  // namespace
 
-hipError_t launch_scores_large(int64_t B, int Hq, int Hkv, int nb, int D, const float* qbar,
-                               const float* kbar, float* S, hipStream_t stream) {
+hipError_t launch_scores_large(int64_t B, int Hq, int Hkv, int nb, int D, float* qbar,
+                               const float* kbar, float* S, bool group, hipStream_t stream) {
+  if (group && Hq > Hkv) {
+    const int64_t n = B * Hkv * (int64_t)nb * D;
+    group_sum_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, stream>>>(
+        qbar, B, Hq, Hkv, (int64_t)nb * D);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int tiles = nb / 64;
-  const int64_t n = B * Hq * (int64_t)tiles * tiles;
-  score_gemm_kernel<<<dim3((unsigned)n), 64, 0, stream>>>(qbar, kbar, S, Hq, Hkv, nb, D, tiles);
+  const int64_t n = B * (group ? Hkv : Hq) * (int64_t)tiles * tiles;
+  score_gemm_kernel<<<dim3((unsigned)n), 64, 0, stream>>>(qbar, kbar, S, Hq, Hkv, nb, D, tiles,
+                                                          group);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_rows(int64_t rows, int nb, int topk, const float* S, int32_t* idx,
-                            bool causal, hipStream_t stream) {
-  topk_rows_kernel<<<dim3((unsigned)rows), kTopkThreads, 0, stream>>>(S, idx, nb, topk, causal);
+                            bool causal, int G, hipStream_t stream) {
+  topk_rows_kernel<<<dim3((unsigned)rows), kTopkThreads, 0, stream>>>(S, idx, nb, topk, causal,
+                                                                      G);
   return hipGetLastError();
 }
 

@@ -71,7 +71,8 @@ typedef enum {
 /* Selection only (GQA, MSA page §3.1): one selection per KV head, from the sum over its
  * Hq/Hkv query heads of their block scores; it is written to the idx rows of each of those
  * heads. The workspace's pooled-query rows of the group's first head then hold the summed
- * pooled queries. Supported for nb <= 1024. */
+ * pooled queries. For nb > 1024 the score matrix part of the workspace holds one
+ * [nb, nb] matrix per (batch, KV head). */
 #define BSATTN_GROUP_SELECT 4u
 
 /* Version of this ABI (BSATTN_ABI_VERSION of the built library). Version 2 added the

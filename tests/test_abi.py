@@ -113,7 +113,7 @@ def sel_ex(flags, **kw):
 
 def test_extended_entry_points_reject():
     assert sel_ex(8) == 1 and "flags" in last()                   # unknown bit
-    assert sel_ex(4, N=64 * 2048, topk=3) == 2 and "group" in last()   # group: fused path only
+    assert sel_ex(4, nrand=1, N=64 * 2048, topk=3) == 2 and "random" in last()  # fused only
     assert sel_ex(1, q=None) == 1 and "null" in last()           # checks as bsattn_select
     assert sel_ex(0, nrand=3) == 1 and "nrand" in last()         # nrand > topk
     assert sel_ex(1, nrand=1) == 2 and "causal" in last()

@@ -172,6 +172,31 @@ def test_select_many_blocks_causal():
     say("  ", check_idx(idx, O.block_scores(O.pool_max(qo, blk), O.pool_max(ko, blk)), topk))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 64 * 1152, 4, 2, 64, 64, 40), (2, 128 * 1088, 8, 2, 128, 128, 9)],
+                         ids=str)
+def test_select_many_blocks_group(shape, dtype, causal):
+    """Group-shared selection over more than 1024 key blocks (score matrix per KV head in the
+    workspace): the heads of a group share their rows, which follow the index rule under the
+    summed scores of the group."""
+    B, N, Hq, Hkv, D, blk, topk = shape
+    say(f"[select many blocks group] dtype={dtype} shape={shape} causal={causal}")
+    q, k, _, _ = syn.iid_inputs(B, N, Hq, Hkv, D, dtype, index=34, device=DEV)
+    ws = torch.empty(bst.select_workspace_bytes(B, N, Hq, Hkv, D, blk), dtype=torch.uint8,
+                     device=DEV)
+    idx = bst.select(q, k, blk, topk, group=True, causal=causal, workspace=ws).cpu().numpy()
+    G = Hq // Hkv
+    for j in range(1, G):
+        assert np.array_equal(idx[:, j::G], idx[:, ::G])
+    S = O.group_scores(O.block_scores(O.pool(stored_values(q), blk), O.pool(stored_values(k), blk)),
+                       Hkv)
+    if causal:
+        check_idx_causal(idx[:, ::G], S, topk)
+    else:
+        say("  ", check_idx(idx[:, ::G], S, topk))
+
+
 @pytest.mark.parametrize("opts", [{}, dict(causal=True), dict(group=True)],
                          ids=lambda o: "-".join(o) or "plain")
 def test_select_mid_range_blocks(opts):
