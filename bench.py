@@ -272,8 +272,9 @@ def bench_decode(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
-              "multi-GPU variant in this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library is a "
+              "single-GPU path; it shards over (batch, KV-head group) with no communication, so "
+              "N GPUs run N independent copies of this measurement.", file=sys.stderr)
         sys.exit(2)
     if args.decode:
         bench_decode(args)
