@@ -96,13 +96,28 @@ __global__ __launch_bounds__(256) void dselect_kernel(
     // scores: lane owns blocks lane + 64c (c < CPL); this wave's d range in order
     const float* K = kbar + ((int64_t)b * Hkv + g) * D * nbmax;
     constexpr int DR = D / SPLIT;
-    for (int d = part * DR; d < (part + 1) * DR; ++d) {
-      const float qd = qs[slot][d];
-      const float* row = K + (int64_t)d * nbmax;
+    // d rows loaded before their products: 64 values per lane in flight (RB * CPL <= 64)
+    constexpr int RB0 = CPL >= 64 ? 1 : 64 / CPL;
+    constexpr int RB = RB0 < DR ? RB0 : DR;
+    static_assert(DR % RB == 0, "d range in whole row batches");
+    // the loads of RB rows are all issued before the first product, so their latencies
+    // overlap (a dependent load-then-use per row leaves the wave waiting on every row);
+    // the products keep ascending d, so the sums are unchanged
+    for (int d0 = part * DR; d0 < (part + 1) * DR; d0 += RB) {
+      float kv[RB][CPL];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int j = lane + 64 * c;
-        if (j < own) acc[c] = __builtin_fmaf(qd, row[j], acc[c]);
+      for (int u = 0; u < RB; ++u)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int j = lane + 64 * c;
+          kv[u][c] = j < own ? K[(int64_t)(d0 + u) * nbmax + j] : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const float qd = qs[slot][d0 + u];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          if (lane + 64 * c < own) acc[c] = __builtin_fmaf(qd, kv[u][c], acc[c]);
       }
     }
   }
@@ -309,7 +324,7 @@ template <int D, int CPL>
 hipError_t launch_dsel(const void* q, const float* kbar, const int32_t* lens, int32_t* idx,
                        int64_t Lmax, int Hq, int Hkv, int block, int nbmax, int topk,
                        unsigned heads, hipStream_t stream) {
-  if (CPL <= 32)                              // nb <= 2048: 4 waves per (sequence, head)
+  if constexpr (CPL <= 32)                    // nb <= 2048: 4 waves per (sequence, head)
     dselect_kernel<D, CPL, 4><<<heads, 256, 0, stream>>>(
         (const uint16_t*)q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, (int)heads);
   else

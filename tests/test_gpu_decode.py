@@ -49,6 +49,13 @@ CASES = [
     (3, 128 * 12, 8, 2, 128, 128, 3, [1536, 1000, 129]),
     (2, 64 * 40, 4, 4, 128, 64, 1, [2560, 65]),
     (2, 64 * 16, 2, 1, 64, 64, 16, [1024, 700]),          # topk covers every block
+    # more key blocks: 4, 16 and 32 columns per lane (4 waves per head), then 64 and 128
+    # (one wave per head)
+    (2, 64 * 200, 4, 2, 64, 64, 20, [12800, 5000]),
+    (2, 64 * 1000, 8, 2, 128, 64, 76, [64000, 33333]),
+    (1, 64 * 2000, 4, 2, 64, 64, 50, [128000]),
+    (1, 64 * 3000, 2, 1, 64, 64, 30, [192000]),
+    (1, 64 * 8192, 2, 1, 64, 64, 40, [524288]),
 ]
 
 
