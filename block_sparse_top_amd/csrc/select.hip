@@ -166,13 +166,29 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     __syncthreads();                        // previous chunk consumed (and qs written)
-    for (int e = tid; e < 64 * D4; e += kThreads) {
-      const int col = e / D4, d4 = e - col * D4;
-      const int j = c * 64 + col;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (j < nk) v = *(const f32x4*)(K + (int64_t)j * D + 4 * d4);
-      float* dst = ks + col * KS + 4 * d4;
-      dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
+    {
+      // all loads of the chunk first (up to 8 per thread: D <= 128), then the LDS stores
+      constexpr int kMaxPer = 8;
+      f32x4 vv[kMaxPer];
+#pragma unroll
+      for (int u = 0; u < kMaxPer; ++u) {
+        const int e = tid + u * kThreads;
+        vv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (e < 64 * D4) {
+          const int col = e / D4, d4 = e - col * D4;
+          const int j = c * 64 + col;
+          if (j < nk) vv[u] = *(const f32x4*)(K + (int64_t)j * D + 4 * d4);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kMaxPer; ++u) {
+        const int e = tid + u * kThreads;
+        if (e < 64 * D4) {
+          const int col = e / D4, d4 = e - col * D4;
+          float* dst = ks + col * KS + 4 * d4;
+          dst[0] = vv[u][0]; dst[1] = vv[u][1]; dst[2] = vv[u][2]; dst[3] = vv[u][3];
+        }
+      }
     }
     __syncthreads();
     const float* qw = qs + wave * RW * D;
