@@ -68,12 +68,20 @@ __global__ __launch_bounds__(64) void score_gemm_kernel(const float* __restrict_
     qrow[a] = Q + (int64_t)(ti * 64 + 32 * a + l32) * D + half * half_d;
     krow[a] = K + (int64_t)(tj * 64 + 32 * a + l32) * D + half * half_d;
   }
+  // the operands of step s0 + 4 are loaded while step s0 multiplies
+  f32x4 qa[2], kb[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    qa[a] = *(const f32x4*)(qrow[a]);
+    kb[a] = *(const f32x4*)(krow[a]);
+  }
   for (int s0 = 0; s0 < half_d; s0 += 4) {
-    f32x4 qa[2], kb[2];
+    f32x4 qn[2], kn[2];
+    const int sn = s0 + 4 < half_d ? s0 + 4 : s0;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      qa[a] = *(const f32x4*)(qrow[a] + s0);
-      kb[a] = *(const f32x4*)(krow[a] + s0);
+      qn[a] = *(const f32x4*)(qrow[a] + sn);
+      kn[a] = *(const f32x4*)(krow[a] + sn);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -82,6 +90,11 @@ __global__ __launch_bounds__(64) void score_gemm_kernel(const float* __restrict_
 #pragma unroll
         for (int c = 0; c < 2; ++c)
           acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[a][e], kb[c][e], acc[a][c], 0, 0, 0);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      qa[a] = qn[a];
+      kb[a] = kn[a];
+    }
   }
   // acc[a][c][r]: row ti*64 + 32a + 8(r/4) + 4*half + r%4, column tj*64 + 32c + l32
   float* Sbh = S + bh * nb * nb;
