@@ -8,8 +8,8 @@
 // switch data as real work does: constant or tiny operands draw less power and let the chip
 // hold a clock that real data does not. The accumulators are summed into one float per lane
 // at the end so that the work is not optimised away. mfma_fp8_kernel: the same on the fp8 MFMA.
-// read_kernel: a grid-stride sum of a large buffer with 16-byte nontemporal loads, 8 in flight
-// per thread (HBM read rate). copy_kernel: 16-byte loads and stores (read + write rate).
+// read_kernel: a sum of a large buffer with 16-byte nontemporal loads (HBM read rate);
+// copy_kernel: 16-byte loads and stores (read + write rate).
 #include "common.h"
 #include "launch.h"
 
@@ -88,19 +88,25 @@ __global__ __launch_bounds__(256) void mfma_fp8_kernel(int64_t iters, float* __r
   sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Each work-group streams one contiguous range (as the path's pooling and attention read
+// whole blocks); 16 loads of 16 bytes in flight per thread.
+constexpr int kStreamUnroll = 16;
+
 __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n16,
                                                    float* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t begin = (int64_t)blockIdx.x * per;
+  const int64_t end = begin + per < n16 ? begin + per : n16;
+  int64_t i = begin + threadIdx.x;
   uint32_t x = 0;
-  for (; i + 7 * stride < n16; i += 8 * stride) {
-    u32x4 w[8];
+  for (; i + (kStreamUnroll - 1) * 256 < end; i += kStreamUnroll * 256) {
+    u32x4 w[kStreamUnroll];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) w[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < kStreamUnroll; ++u) w[u] = __builtin_nontemporal_load(src + i + u * 256);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x ^= w[u].x ^ w[u].y ^ w[u].z ^ w[u].w;
+    for (int u = 0; u < kStreamUnroll; ++u) x ^= w[u].x ^ w[u].y ^ w[u].z ^ w[u].w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < end; i += 256) {
     const u32x4 w = __builtin_nontemporal_load(src + i);
     x ^= w.x ^ w.y ^ w.z ^ w.w;
   }
@@ -109,16 +115,19 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
 
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
                                                    u32x4* __restrict__ dst, int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    u32x4 w[4];
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t begin = (int64_t)blockIdx.x * per;
+  const int64_t end = begin + per < n16 ? begin + per : n16;
+  int64_t i = begin + threadIdx.x;
+  constexpr int kU = kStreamUnroll / 2;
+  for (; i + (kU - 1) * 256 < end; i += kU * 256) {
+    u32x4 w[kU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) w[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < kU; ++u) w[u] = __builtin_nontemporal_load(src + i + u * 256);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(w[u], dst + i + u * stride);
+    for (int u = 0; u < kU; ++u) __builtin_nontemporal_store(w[u], dst + i + u * 256);
   }
-  for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  for (; i < end; i += 256) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 }  // namespace
