@@ -24,7 +24,7 @@
 // Data movement: K and V tiles go from HBM/L2 straight into LDS with global_load_lds_dwordx4
 // (lane l of one instruction fills bytes [16l, 16l+16) of a 1 KiB LDS span; the lane fetches
 // whichever 16-byte chunk belongs there). One LDS buffer per tensor: the wave reads all K
-// operands of block t into registers, then starts the K transfer of block t+1 and computes
+// operands of step t into registers, then starts the K transfer of step t+1 and computes
 // S^T and the softmax while it flies; V likewise before the PV product. The 16-byte chunk c
 // of tile row r sits at chunk position c ^ f(r), f(r) = 2(r&3) + ((r>>2)&1), which makes both
 // the row reads of K (8 rows, one chunk) and the transpose reads of V (4 rows, 2 chunks) hit
