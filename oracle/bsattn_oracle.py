@@ -502,10 +502,12 @@ def attend_backward(q, k, v, idx, block, scale, dout, causal: bool = False):
     return dq, dk, dv
 
 
-def decode_select(q_tok, kbar, lens, block: int, topk: int) -> np.ndarray:
+def decode_select(q_tok, kbar, lens, block: int, topk: int, group: bool = False) -> np.ndarray:
     """Blocks for one decode step [R26]. q_tok [B, Hq, D]; kbar [B, Hkv, nb, D] (rows of
     complete blocks are read); lens [B] (1 <= lens[b]). Returns int64 [B, Hq, topk]:
-    ascending, own block last, -1 in unused places."""
+    ascending, own block last, -1 in unused places. group: one choice per KV head from the
+    sum of its query heads' scores, used by each of them [R22 applied to R26].
+    """
     B, Hq, D = q_tok.shape
     Hkv = kbar.shape[1]
     out = np.full((B, Hq, topk), -1, dtype=np.int64)
@@ -513,8 +515,13 @@ def decode_select(q_tok, kbar, lens, block: int, topk: int) -> np.ndarray:
         own = (int(lens[b]) - 1) // block
         kb = min(topk, own + 1)
         for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
             if kb > 1:
-                s = kbar[b, kv_head(h, Hq, Hkv), :own] @ q_tok[b, h]       # [own]
+                if group:
+                    heads = [x for x in range(Hq) if kv_head(x, Hq, Hkv) == g]
+                    s = sum(kbar[b, g, :own] @ q_tok[b, x] for x in heads)        # [own]
+                else:
+                    s = kbar[b, g, :own] @ q_tok[b, h]                            # [own]
                 out[b, h, :kb - 1] = select_topk(s[None], kb - 1)[0]
             out[b, h, kb - 1] = own
     return out

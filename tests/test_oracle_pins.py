@@ -434,6 +434,21 @@ def check_decode(o=O):
             assert np.allclose(got[b, h], ref[0, 0, 0].numpy(), rtol=0, atol=1e-12)
     z = o.decode_select(np.zeros_like(qt), kbar, lens, blk, 3)
     assert z[0, 0].tolist() == [0, 1, 7] and z[2, 0].tolist() == [0, 1, -1]
+    # group choice: a full sort of the summed scores of the KV head's query heads (heads 2g,
+    # 2g+1 here), shared by both; with one query head per KV head it is the per-head choice
+    for topk in (1, 3, 8):
+        idx = o.decode_select(qt, kbar, lens, blk, topk, group=True)
+        for b in range(B):
+            own = (lens[b] - 1) // blk
+            kb = min(topk, own + 1)
+            for g in range(2):
+                s = kbar[b, g, :own] @ (qt[b, 2 * g] + qt[b, 2 * g + 1])
+                past = np.lexsort((np.arange(own), -s))[:kb - 1]
+                want = sorted(past.tolist() + [own]) + [-1] * (topk - kb)
+                assert idx[b, 2 * g].tolist() == want and idx[b, 2 * g + 1].tolist() == want
+    kb1 = o.pool(kc[:, :, :1].repeat(4, axis=2), blk)              # Hkv = Hq = 4
+    assert np.array_equal(o.decode_select(qt, kb1, lens, blk, 5, group=True),
+                          o.decode_select(qt, kb1, lens, blk, 5))
 
 
 def check_random_fill(o=O):
@@ -712,8 +727,12 @@ MUTANTS = {
     "backward_dk_unscaled": dict(
         attend_backward=lambda q, k, v, idx, blk, scale, dout, causal=False:
         (lambda g: (g[0], g[1] / scale, g[2]))(O.attend_backward(q, k, v, idx, blk, scale, dout, causal))),
+    "decode_group_first_head_only": dict(
+        decode_select=lambda q, kb, lens, blk, topk, group=False: O.decode_select(
+            np.repeat(q[:, ::q.shape[1] // kb.shape[1]], q.shape[1] // kb.shape[1], axis=1)
+            if group else q, kb, lens, blk, topk, group=False)),
     "decode_own_block_not_forced": dict(
-        decode_select=lambda q, kb, lens, blk, topk: _decode_unforced(q, kb, lens, blk, topk)),
+        decode_select=lambda q, kb, lens, blk, topk, group=False: _decode_unforced(q, kb, lens, blk, topk)),
     "random_fill_with_replacement": dict(
         select_topk_random=lambda S, k, r, seed: _random_with_replacement(S, k, r, seed)),
     "lse_log2": dict(attend_lse=lambda q, k, idx, blk, scale, causal=False:
