@@ -225,9 +225,12 @@ def bench_decode(args):
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
     scale = 1.0 / math.sqrt(w.D)
 
+    flags = bst.GROUP_SELECT if args.group else 0
+
     def step():
-        st = L.bsattn_decode(1, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, P(q), P(kc), P(vc),
-                             P(kbar), P(lens), scale, P(out), P(idx), P(ws), ws.numel(), sp)
+        st = L.bsattn_decode_ex(1, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, P(q), P(kc),
+                                P(vc), P(kbar), P(lens), scale, P(out), P(idx), P(ws), ws.numel(),
+                                sp)
         assert st == 0, L.bsattn_last_error()
 
     for _ in range(args.warmup):
@@ -242,10 +245,12 @@ def bench_decode(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
-    # bytes each query head's kernels read: keys and values of its chosen blocks, the pooled
-    # keys of its KV head, the query, the output and idx
-    kv_bytes = w.B * w.Hq * topk * w.block * w.D * 2 * 2
-    kbar_bytes = w.B * w.Hq * w.nb * w.D * 4
+    # bytes the step must read: keys and values of the chosen blocks (per query head; with a
+    # group-shared selection once per KV head, whose query heads read the same blocks), the
+    # pooled keys (per selection), the query, the output and idx
+    sel_heads = w.Hkv if args.group else w.Hq
+    kv_bytes = w.B * sel_heads * topk * w.block * w.D * 2 * 2
+    kbar_bytes = w.B * sel_heads * w.nb * w.D * 4
     total = kv_bytes + kbar_bytes + w.B * w.Hq * (w.D * 4 + topk * 4)
     rec = {
         "metric": "decode tokens/s (one new token per sequence, block-sparse attention step)",
@@ -254,7 +259,8 @@ def bench_decode(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) caches, resident in HBM)",
         "config": {"workload": w.name, "B": w.B, "cache_len": w.N, "Hq": w.Hq, "Hkv": w.Hkv,
-                   "D": w.D, "block": w.block, "topk": topk, "parallelism": "single GPU"},
+                   "D": w.D, "block": w.block, "topk": topk, "parallelism": "single GPU",
+                   **({"group_select": True} if args.group else {})},
         "roofline": {"bound": "hbm", "achieved": round(total / (ms / 1e3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(total / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,

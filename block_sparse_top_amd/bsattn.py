@@ -93,6 +93,9 @@ def lib() -> ctypes.CDLL:
     L.bsattn_decode.restype = i32
     L.bsattn_decode.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                 ctypes.c_float, vp, vp, vp, sz, vp]
+    L.bsattn_decode_ex.restype = i32
+    L.bsattn_decode_ex.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, ctypes.c_uint, vp, vp,
+                                   vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     _lib = L
     return L
 
@@ -290,9 +293,10 @@ def decode_pool(k_cache, lens_new, kbar, block: int, lens_old=None):
 
 
 def decode(q, k_cache, v_cache, kbar, lens, block: int, topk: int, scale: float | None = None,
-           workspace=None):
+           workspace=None, *, group: bool = False):
     """One decode step: q bf16 [B, Hq, D] (the newest token of each sequence), caches bf16
-    [B, Lmax, Hkv, D], kbar from `decode_pool`, lens int32 [B] on the device.
+    [B, Lmax, Hkv, D], kbar from `decode_pool`, lens int32 [B] on the device. group: one
+    choice of blocks per KV head from its query heads' summed scores, shared by them.
     Returns (out bf16 [B, Hq, D], idx int32 [B, Hq, topk])."""
     B, Hq, D = q.shape
     Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
@@ -304,8 +308,9 @@ def decode(q, k_cache, v_cache, kbar, lens, block: int, topk: int, scale: float 
         n = int(L.bsattn_decode_workspace_bytes(B, Hq, D, max(topk, 1))) if B else 0
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
     with torch.cuda.device(q.device):
-        _check(L.bsattn_decode(_DTYPES[q.dtype], B, Lmax, Hq, Hkv, D, block, topk, _ptr(q),
-                               _ptr(k_cache), _ptr(v_cache), _ptr(kbar), _ptr(lens), scale,
-                               _ptr(out), _ptr(idx), _ptr(workspace), workspace.numel(),
-                               _stream(q.device)))
+        _check(L.bsattn_decode_ex(_DTYPES[q.dtype], B, Lmax, Hq, Hkv, D, block, topk,
+                                  GROUP_SELECT if group else 0, _ptr(q), _ptr(k_cache),
+                                  _ptr(v_cache), _ptr(kbar), _ptr(lens), scale, _ptr(out),
+                                  _ptr(idx), _ptr(workspace), workspace.numel(),
+                                  _stream(q.device)))
     return out, idx

@@ -401,8 +401,19 @@ int bsattn_decode(int dtype, int64_t B, int64_t Lmax, int Hq, int Hkv, int D, in
                   const void* q, const void* k_cache, const void* v_cache, const float* kbar,
                   const int32_t* lens, float scale, void* out, int32_t* idx, void* workspace,
                   size_t workspace_bytes, void* stream) {
+  return bsattn_decode_ex(dtype, B, Lmax, Hq, Hkv, D, block, topk, 0u, q, k_cache, v_cache, kbar,
+                          lens, scale, out, idx, workspace, workspace_bytes, stream);
+}
+
+int bsattn_decode_ex(int dtype, int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int block,
+                     int topk, unsigned flags, const void* q, const void* k_cache,
+                     const void* v_cache, const float* kbar, const int32_t* lens, float scale,
+                     void* out, int32_t* idx, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   int st = check_decode(dtype, B, Lmax, Hq, Hkv, D, block);
   if (st != BSATTN_OK) return st;
+  if (flags & ~(unsigned)BSATTN_GROUP_SELECT)
+    return fail(BSATTN_E_INVALID, "decode flags 0x%x (only BSATTN_GROUP_SELECT)", flags);
   if (topk < 1) return fail(BSATTN_E_INVALID, "topk %d must be >= 1", topk);
   if (!isfinite(scale) || !(scale > 0.f))
     return fail(BSATTN_E_INVALID, "scale must be finite and > 0");
@@ -416,7 +427,8 @@ int bsattn_decode(int dtype, int64_t B, int64_t Lmax, int Hq, int Hkv, int D, in
   if (!workspace || workspace_bytes < need)
     return fail(BSATTN_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   if ((uintptr_t)workspace & 255u) return fail(BSATTN_E_WORKSPACE, "workspace not 256-byte aligned");
-  return hip_status(bsattn::launch_decode(B, Lmax, Hq, Hkv, D, block, topk, q, k_cache, v_cache,
+  return hip_status(bsattn::launch_decode(B, Lmax, Hq, Hkv, D, block, topk,
+                                          flags & BSATTN_GROUP_SELECT, q, k_cache, v_cache,
                                           kbar, lens, scale, out, idx, workspace,
                                           (hipStream_t)stream),
                     "decode launch");

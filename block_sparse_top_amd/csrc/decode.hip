@@ -15,13 +15,16 @@
 //                      between the old and the new length (all complete blocks without old
 //                      lengths).
 //   dselect_kernel     one work-group of 4 waves per (sequence, query head) for up to 2048
-//                      blocks (one wave beyond): lane l owns blocks l + 64c; each wave sums a
+//                      blocks (one wave beyond; with a group-shared selection per (sequence,
+//                      KV head), on the sum of the group's queries, writing the same row for
+//                      each of its query heads): lane l owns blocks l + 64c; each wave sums a
 //                      quarter of d in order (coalesced loads of the transposed cache), the
 //                      quarters meet in LDS in a fixed order (fp32 scores), then one wave runs
 //                      the prefill selection's bitwise threshold search with ballots and
 //                      compacts the chosen blocks in ascending order.
 //   dattn_kernel       split-K over the chosen blocks (flash-decoding): one wave per
-//                      (sequence, query head, split); per block, lanes own keys for the scores
+//                      (sequence, query head, split), the G heads of a KV head side by side;
+//                      per block, lanes own keys for the scores
 //                      (16-byte row loads), the weights go through LDS, then groups of lanes
 //                      own 8 consecutive d of one key (16-byte loads, several keys in
 //                      flight) for the weighted value sum. Writes the split's (max, sum,
@@ -70,7 +73,7 @@ template <int D, int CPL, int SPLIT>
 __global__ __launch_bounds__(256) void dselect_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ kbar,
     const int32_t* __restrict__ lens, int32_t* __restrict__ idx, int64_t Lmax, int Hq, int Hkv,
-    int block, int nbmax, int topk, int heads) {
+    int block, int nbmax, int topk, int heads, bool group) {
   constexpr int HPW = SPLIT == 1 ? kSelWaves : 1;       // (sequence, head) pairs per group
   __shared__ float qs[HPW][D];
   __shared__ float partial[SPLIT == 1 ? 1 : SPLIT - 1][SPLIT == 1 ? 1 : 64 * CPL];
@@ -80,15 +83,24 @@ __global__ __launch_bounds__(256) void dselect_kernel(
   const int bh = blockIdx.x * HPW + slot;
   if (bh >= heads) return;                    // SPLIT == 1 only (grid covers heads exactly
                                               // for SPLIT == 4): no barrier follows
-  const int b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
-  int32_t* out = idx + (int64_t)bh * topk;
+  // selection row bh = b * HS + s: query head s, or (group) KV head s, whose G query heads'
+  // queries are summed (in head order) and which writes the same row for each of them
+  const int G = Hq / Hkv, HS = group ? Hkv : Hq;
+  const int b = bh / HS, s = bh % HS;
+  const int g = group ? s : s / G;
+  const int h0 = group ? s * G : s, nh = group ? G : 1;
+  int32_t* out = idx + ((int64_t)b * Hq + h0) * topk;     // rows out + j * topk, j < nh
   const int64_t L = lens[b];
   const bool len_ok = L >= 1 && L <= Lmax;
   const int own = len_ok ? (int)((L - 1) / block) : 0;
   const int kb = own + 1 < topk ? own + 1 : topk;
   const int need = len_ok ? kb - 1 : 0;       // places for complete earlier blocks
-  for (int d = lane; d < D; d += kWave)
-    qs[slot][d] = __uint_as_float((uint32_t)q[(int64_t)bh * D + d] << 16);
+  for (int d = lane; d < D; d += kWave) {
+    const uint16_t* qh = q + ((int64_t)b * Hq + h0) * D + d;
+    float x = __uint_as_float((uint32_t)qh[0] << 16);
+    for (int j = 1; j < nh; ++j) x += __uint_as_float((uint32_t)qh[(int64_t)j * D] << 16);
+    qs[slot][d] = x;
+  }
   float acc[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
@@ -133,7 +145,8 @@ __global__ __launch_bounds__(256) void dselect_kernel(
       for (int c = 0; c < CPL; ++c) acc[c] += partial[w][lane + 64 * c];
   }
   if (!len_ok) {                              // invalid length: no block
-    for (int p = lane; p < topk; p += kWave) out[p] = -1;
+    for (int j = 0; j < nh; ++j)
+      for (int p = lane; p < topk; p += kWave) out[(int64_t)j * topk + p] = -1;
     return;
   }
   if (need > 0) {
@@ -161,13 +174,16 @@ __global__ __launch_bounds__(256) void dselect_kernel(
       const uint64_t meq = __builtin_amdgcn_ballot_w64(is_eq);
       const bool sel = valid && (key[c] > T || (is_eq && eq_before + lanes_below(meq) < eq_need));
       const uint64_t msel = __builtin_amdgcn_ballot_w64(sel);
-      if (sel) out[sel_before + lanes_below(msel)] = lane + 64 * c;
+      if (sel)
+        for (int j = 0; j < nh; ++j) out[(int64_t)j * topk + sel_before + lanes_below(msel)] = lane + 64 * c;
       eq_before += __builtin_popcountll(meq);
       sel_before += __builtin_popcountll(msel);
     }
   }
-  if (lane == 0) out[kb - 1] = own;
-  for (int p = kb + lane; p < topk; p += kWave) out[p] = -1;
+  for (int j = 0; j < nh; ++j) {
+    if (lane == 0) out[(int64_t)j * topk + kb - 1] = own;
+    for (int p = kb + lane; p < topk; p += kWave) out[(int64_t)j * topk + p] = -1;
+  }
 }
 
 // ---------------------------------------------------------------- split-K attention
@@ -179,8 +195,18 @@ __global__ __launch_bounds__(64) void dattn_kernel(
     int block, int topk, int splits, float c) {
   __shared__ float qs[D];
   __shared__ float ps[128];                   // weights of one block (block <= 128)
-  const int bh = blockIdx.x / splits, sp = blockIdx.x % splits;
-  const int b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
+  // work order (b, KV head, split, head within group): the G query heads of a KV head that
+  // read the same split of their blocks run side by side on one XCD (under a group-shared
+  // selection they read the same keys and values, which then come from its L2)
+  const int G = Hq / Hkv;
+  uint32_t w = xcd_remap(blockIdx.x, gridDim.x);
+  const int hh = (int)(w % G);
+  w /= G;
+  const int sp = (int)(w % splits);
+  w /= splits;
+  const int g = (int)(w % Hkv), b = (int)(w / Hkv);
+  const int h = g * G + hh;
+  const int bh = b * Hq + h;
   const int lane = threadIdx.x;
   const int64_t L = lens[b];
   const int64_t rs = (int64_t)Hkv * D;
@@ -323,26 +349,26 @@ __global__ __launch_bounds__(64) void dcombine_kernel(const float* __restrict__ 
 template <int D, int CPL>
 hipError_t launch_dsel(const void* q, const float* kbar, const int32_t* lens, int32_t* idx,
                        int64_t Lmax, int Hq, int Hkv, int block, int nbmax, int topk,
-                       unsigned heads, hipStream_t stream) {
+                       unsigned heads, bool group, hipStream_t stream) {
   if constexpr (CPL <= 32)                    // nb <= 2048: 4 waves per (sequence, head)
     dselect_kernel<D, CPL, 4><<<heads, 256, 0, stream>>>(
-        (const uint16_t*)q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, (int)heads);
+        (const uint16_t*)q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, (int)heads, group);
   else
     dselect_kernel<D, CPL, 1><<<(heads + kSelWaves - 1) / kSelWaves, kSelWaves * 64, 0, stream>>>(
-        (const uint16_t*)q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, (int)heads);
+        (const uint16_t*)q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, (int)heads, group);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_dselect(const void* q, const float* kbar, const int32_t* lens, int32_t* idx,
                           int64_t Lmax, int Hq, int Hkv, int block, int nbmax, int topk,
-                          unsigned heads, hipStream_t stream) {
-  if (nbmax <= 64) return launch_dsel<D, 1>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, stream);
-  if (nbmax <= 256) return launch_dsel<D, 4>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, stream);
-  if (nbmax <= 1024) return launch_dsel<D, 16>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, stream);
-  if (nbmax <= 2048) return launch_dsel<D, 32>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, stream);
-  if (nbmax <= 4096) return launch_dsel<D, 64>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, stream);
-  return launch_dsel<D, kSelCols>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, stream);
+                          unsigned heads, bool group, hipStream_t stream) {
+  if (nbmax <= 64) return launch_dsel<D, 1>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, group, stream);
+  if (nbmax <= 256) return launch_dsel<D, 4>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, group, stream);
+  if (nbmax <= 1024) return launch_dsel<D, 16>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, group, stream);
+  if (nbmax <= 2048) return launch_dsel<D, 32>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, group, stream);
+  if (nbmax <= 4096) return launch_dsel<D, 64>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, group, stream);
+  return launch_dsel<D, kSelCols>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax, topk, heads, group, stream);
 }
 
 }  // namespace
@@ -375,7 +401,7 @@ hipError_t launch_decode_pool(int64_t B, int64_t Lmax, int Hkv, int D, int block
 }
 
 hipError_t launch_decode(int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int block, int topk,
-                         const void* q, const void* k_cache, const void* v_cache,
+                         bool group, const void* q, const void* k_cache, const void* v_cache,
                          const float* kbar, const int32_t* lens, float scale, void* out,
                          int32_t* idx, void* workspace, hipStream_t stream) {
   const int nbmax = (int)(Lmax / block);
@@ -383,10 +409,11 @@ hipError_t launch_decode(int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int bl
   const float c = (float)((double)scale * 1.4426950408889634);
   float* part = (float*)workspace;
   const unsigned heads = (unsigned)(B * Hq);
+  const unsigned sel_rows = (unsigned)(B * (group ? Hkv : Hq));   // selection rows
   hipError_t e = D == 64 ? launch_dselect<64>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax,
-                                              topk, heads, stream)
+                                              topk, sel_rows, group, stream)
                          : launch_dselect<128>(q, kbar, lens, idx, Lmax, Hq, Hkv, block, nbmax,
-                                               topk, heads, stream);
+                                               topk, sel_rows, group, stream);
   if (e != hipSuccess) return e;
   e = hipGetLastError();
   if (e != hipSuccess) return e;

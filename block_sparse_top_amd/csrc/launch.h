@@ -94,7 +94,7 @@ hipError_t launch_decode_pool(int64_t B, int64_t Lmax, int Hkv, int D, int block
                               const void* k_cache, const int32_t* lens_old,
                               const int32_t* lens_new, float* kbar, hipStream_t stream);
 hipError_t launch_decode(int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int block, int topk,
-                         const void* q, const void* k_cache, const void* v_cache,
+                         bool group, const void* q, const void* k_cache, const void* v_cache,
                          const float* kbar, const int32_t* lens, float scale, void* out,
                          int32_t* idx, void* workspace, hipStream_t stream);
 

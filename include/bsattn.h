@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define BSATTN_ABI_VERSION 3
+#define BSATTN_ABI_VERSION 4
 
 typedef enum {
   BSATTN_OK = 0,
@@ -78,8 +78,8 @@ typedef enum {
 /* Version of this ABI (BSATTN_ABI_VERSION of the built library). Version 2 added the
  * BSATTN_* option flags, the two _ex entry points (with the optional log-sum-exp output) and
  * the backward; version 3 added the key_stride argument of the _ex entry points (overlapping
- * key blocks), bsattn_key_blocks and bsattn_select_workspace_bytes_ex. Version-1 calls are
- * unchanged. */
+ * key blocks), bsattn_key_blocks and bsattn_select_workspace_bytes_ex; version 4 added
+ * bsattn_decode_ex (group-shared decode selection). Version-1 calls are unchanged. */
 int bsattn_abi_version(void);
 
 /* Static English text of a status code; never NULL. */
@@ -291,6 +291,18 @@ int bsattn_decode(int dtype, int64_t B, int64_t Lmax, int Hq, int Hkv, int D, in
                   const void* q, const void* k_cache, const void* v_cache, const float* kbar,
                   const int32_t* lens, float scale, void* out, int32_t* idx, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/* bsattn_decode with options: flags 0 gives bsattn_decode; BSATTN_GROUP_SELECT makes one
+ * choice per (sequence, KV head) from the sum over its Hq/Hkv query heads of their scores
+ * (sum_d (sum_h q[b,h,d]) * kbar[b,g,d,j]; the MSA page's §3.1 GQA, as for bsattn_select_ex),
+ * written to the idx rows of each of those heads, which then read the same blocks (the
+ * attention runs them side by side, so their keys and values are fetched once). Other bits:
+ * BSATTN_E_INVALID. Arguments, layouts and errors otherwise as bsattn_decode. */
+int bsattn_decode_ex(int dtype, int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int block,
+                     int topk, unsigned flags, const void* q, const void* k_cache,
+                     const void* v_cache, const float* kbar, const int32_t* lens, float scale,
+                     void* out, int32_t* idx, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 #ifdef __cplusplus
 }

@@ -49,6 +49,9 @@ the design notes of the repository):
       the complete blocks j < own with the largest q . kbar_j (kbar: mean of the block's keys,
       kept up to date as blocks complete; ties to the lower j); attention over those blocks
       and the own block's cached tokens (all at positions <= L-1).
+  R29 group-shared decode selection: with the option, one choice per (sequence, KV head) by
+      the sum over its query heads of q_h . kbar_j (R22 for a single query token), used by
+      each of those heads.
   R27 random blocks (NEXT N3; the MSA page's §5.1 remedy "5% random blocks"): of a row's k
       places, k - r keep the best scores and r go to blocks drawn uniformly without
       replacement from the others: draw p (p < r) takes the (x mod m_p)-th remaining block in
@@ -506,7 +509,7 @@ def decode_select(q_tok, kbar, lens, block: int, topk: int, group: bool = False)
     """Blocks for one decode step [R26]. q_tok [B, Hq, D]; kbar [B, Hkv, nb, D] (rows of
     complete blocks are read); lens [B] (1 <= lens[b]). Returns int64 [B, Hq, topk]:
     ascending, own block last, -1 in unused places. group: one choice per KV head from the
-    sum of its query heads' scores, used by each of them [R22 applied to R26].
+    sum of its query heads' scores, used by each of them [R29].
     """
     B, Hq, D = q_tok.shape
     Hkv = kbar.shape[1]

@@ -33,14 +33,15 @@ def test_library_exports_every_declared_function():
             "bsattn_abi_version", "bsattn_status_str", "bsattn_last_error",
             "bsattn_select_ex", "bsattn_forward_ex", "bsattn_key_blocks",
             "bsattn_select_workspace_bytes_ex", "bsattn_probe_mfma_bf16", "bsattn_probe_read",
-            "bsattn_probe_copy", "bsattn_probe_sink_floats", "bsattn_probe_mfma_fp8"} <= set(names)
+            "bsattn_probe_copy", "bsattn_probe_sink_floats", "bsattn_probe_mfma_fp8",
+            "bsattn_decode_ex"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings():
     L = bst.lib()
-    assert L.bsattn_abi_version() == 3
+    assert L.bsattn_abi_version() == 4
     for s in range(5):
         assert L.bsattn_status_str(s).decode() == bsattn.STATUS[s]
     assert L.bsattn_status_str(99).decode() == "unknown status"
@@ -240,3 +241,13 @@ def test_probe_rejects():
     assert L.bsattn_probe_read(None, 32, 4, FAKE, None) == 1
     assert L.bsattn_probe_copy(FAKE, ctypes.c_void_p(0x10010), 64, 4, None) == 1 and "overlap" in last()
     assert L.bsattn_probe_copy(FAKE, ctypes.c_void_p(0x20000), 0, 4, None) == 1
+
+
+def test_decode_ex_rejects():
+    L = bst.lib()
+    st = L.bsattn_decode_ex(1, 1, 1024, 4, 2, 64, 64, 4, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125,
+                            FAKE, FAKE, FAKE, 1 << 20, None)
+    assert st == 1 and "flags" in last()
+    st = L.bsattn_decode_ex(0, 1, 1024, 4, 2, 64, 64, 4, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125,
+                            FAKE, FAKE, FAKE, 1 << 20, None)
+    assert st == 2 and "bf16" in last()

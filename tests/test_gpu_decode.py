@@ -85,6 +85,44 @@ def test_decode(case):
         check_out(out.float().cpu().numpy(), dense, "bf16")
 
 
+GROUP_CASES = [
+    # B, Lmax, Hq, Hkv, D, block, topk, lens (GQA 2 to 8, every selection-kernel form)
+    (4, 64 * 20, 4, 2, 64, 64, 5, [1280, 97, 1, 64 * 7]),
+    (3, 128 * 12, 8, 2, 128, 128, 3, [1536, 1000, 129]),
+    (2, 64 * 1000, 8, 2, 128, 64, 76, [64000, 33333]),
+    (1, 64 * 3000, 8, 1, 64, 64, 30, [192000]),
+]
+
+
+@pytest.mark.parametrize("case", GROUP_CASES, ids=lambda c: str(c[:7]))
+def test_decode_group(case):
+    """Group-shared decode selection: the query heads of a KV head share one row, which
+    follows the index rule under the sum of their scores; outputs against the oracle."""
+    B, Lmax, Hq, Hkv, D, blk, topk, lens_l = case
+    say(f"[decode group] {case}")
+    q, kc, vc = caches(B, Lmax, Hq, Hkv, D, index=42)
+    lens = torch.tensor(lens_l, dtype=torch.int32, device=DEV)
+    kbar = torch.empty((B, Hkv, D, Lmax // blk), dtype=torch.float32, device=DEV)
+    bst.decode_pool(kc, lens, kbar, blk)
+    out, idx = bst.decode(q, kc, vc, kbar, lens, blk, topk, group=True)
+    torch.cuda.synchronize()
+    qo, ko, vo = to_f64(q), to_f64(kc), to_f64(vc)
+    kbar_o = O.pool(ko, blk)
+    gidx = idx.cpu().numpy()
+    G = Hq // Hkv
+    for j in range(1, G):
+        assert np.array_equal(gidx[:, j::G], gidx[:, ::G])
+    qsum = qo.reshape(B, Hkv, G, D).sum(axis=2)              # [B, Hkv, D]
+    check_decode_idx(gidx[:, ::G], qsum, kbar_o, lens_l, blk, topk)
+    ref = O.decode_attend(qo, ko, vo, gidx, lens_l, blk, 1 / math.sqrt(D))
+    check_out(out.float().cpu().numpy(), ref, "bf16")
+    # the oracle's own group choice agrees on the rows where the order is clear
+    want = O.decode_select(qo, kbar_o, lens_l, blk, topk, group=True)
+    agree = float(np.mean(np.all(want == gidx, axis=-1)))
+    say(f"   rows equal to the oracle's group choice: {agree:.3f}")
+    assert agree > 0.9
+
+
 def test_decode_incremental_pool_and_invalid_length():
     """Appending tokens block by block keeps kbar equal to a full pooling; a sequence with an
     invalid length gets idx -1 and NaN output, the others are unaffected."""
