@@ -24,8 +24,9 @@
 //                      compacts the chosen blocks in ascending order.
 //   dattn_kernel       split-K over the chosen blocks (flash-decoding): one wave per
 //                      (sequence, query head, split), the G heads of a KV head side by side;
-//                      per block, lanes own keys for the scores
-//                      (16-byte row loads), the weights go through LDS, then groups of lanes
+//                      per block, groups of D/8 lanes read key rows together for the scores
+//                      (16-byte loads, partial dots summed across the group), the weights go
+//                      through LDS, then groups of lanes
 //                      own 8 consecutive d of one key (16-byte loads, several keys in
 //                      flight) for the weighted value sum. Writes the split's (max, sum,
 //                      unnormalised output).
@@ -230,31 +231,46 @@ __global__ __launch_bounds__(64) void dattn_kernel(
   const uint16_t* kb0 = kc + (int64_t)b * Lmax * rs + (int64_t)g * D;
   const uint16_t* vb0 = vc + (int64_t)b * Lmax * rs + (int64_t)g * D;
   const bool len_ok = L >= 1 && L <= Lmax;
+  float qv[8];                                // q[8*dg .. 8*dg+7] for the score pass
+#pragma unroll
+  for (int x = 0; x < 8; ++x) qv[x] = qs[8 * dg + x];
   for (int e = e0; e < e1 && len_ok; ++e) {
     const int j = row[e];
     if (j < 0 || (int64_t)j * block >= L) continue;   // unused place or beyond the cache
     const int64_t t0 = (int64_t)j * block;
     const int nk = (int)(L - t0 < block ? L - t0 : block);   // own block: tokens < L
-    // scores: lane owns keys lane and lane + 64
+    // scores: the LG lanes of key group kq read one key row together (16 bytes each, so one
+    // load instruction covers KG whole rows), multiply by their 8 query values and add the
+    // partial sums across the group; four rounds of keys are in flight
+    __syncthreads();                          // previous block done with ps
+    for (int t = kq; t < nk; t += 4 * KG) {
+      u32x4 w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int tt = t + u * KG;
+        w[u] = u32x4{0u, 0u, 0u, 0u};
+        if (tt < nk) w[u] = *(const u32x4*)(kb0 + (t0 + tt) * rs + 8 * dg);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float a = 0.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          a = __builtin_fmaf(qv[2 * x], bf16lo(w[u][x]), a);
+          a = __builtin_fmaf(qv[2 * x + 1], bf16hi(w[u][x]), a);
+        }
+#pragma unroll
+        for (int off = 1; off < LG; off <<= 1) a += __shfl_xor(a, off);
+        const int tt = t + u * KG;
+        if (dg == 0 && tt < nk) ps[tt] = a * c;   // exp2 domain
+      }
+    }
+    __syncthreads();
     float s[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int t = lane + 64 * u;
-      s[u] = -__builtin_inff();
-      if (t < nk) {
-        const uint16_t* kr = kb0 + (t0 + t) * rs;
-        float a = 0.f;
-#pragma unroll
-        for (int d = 0; d < D; d += 8) {
-          const u32x4 w = *(const u32x4*)(kr + d);
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            a = __builtin_fmaf(qs[d + 2 * x], bf16lo(w[x]), a);
-            a = __builtin_fmaf(qs[d + 2 * x + 1], bf16hi(w[x]), a);
-          }
-        }
-        s[u] = a * c;                         // exp2 domain
-      }
+      s[u] = t < nk ? ps[t] : -__builtin_inff();
     }
     float mb = fmaxf(s[0], s[1]);
 #pragma unroll
@@ -263,7 +279,7 @@ __global__ __launch_bounds__(64) void dattn_kernel(
     const float alpha = __builtin_amdgcn_exp2f(m - mn);    // 0 on the first block
     m = mn;
     float lp = 0.f;
-    __syncthreads();                          // previous block done with ps
+    __syncthreads();                          // scores read before the weights replace them
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int t = lane + 64 * u;
