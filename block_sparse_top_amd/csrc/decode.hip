@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256) void pool_new_kernel(const uint16_t* __restric
 
 // ---------------------------------------------------------------- selection
 constexpr int kSelWaves = 4;                  // (sequence, head) pairs per work-group
+constexpr int kMaxDecodeGroup = 16;           // query heads per KV head in one work-group
 constexpr int kSelCols = kMaxDecodeBlocks / kWave;   // blocks per lane: nb <= 8192
 
 // SPLIT waves per (sequence, head) share the d range (SPLIT = 4, nb <= 2048) or one wave does
@@ -334,6 +335,131 @@ __global__ __launch_bounds__(64) void dattn_kernel(
   }
 }
 
+// Group-shared selection: one work-group of G waves per (sequence, KV head, split), wave w
+// computing query head g*G + w over the group's common blocks. Each block's keys and values
+// go into LDS once for all G waves (the per-head kernel would read them G times); the score
+// pass (groups of D/8 lanes per key row, partial dots summed across the group), the weights
+// and the value pass then run per wave from LDS, writing the same partial results as
+// dattn_kernel for dcombine_kernel.
+template <int D>
+__global__ __launch_bounds__(1024) void dattn_group_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ lens, float* __restrict__ part, int64_t Lmax, int Hq, int Hkv,
+    int block, int topk, int splits, float c) {
+  constexpr int CH = D / 8;                   // 16-byte chunks per key row
+  // LDS (sized at launch): K and V rows of one block [block][D] bf16, the G queries [G][D] and
+  // weights [G][block] fp32
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  const int G = Hq / Hkv;
+  uint16_t* Ks = (uint16_t*)dsm;
+  uint16_t* Vs = Ks + block * D;
+  float* qsm = (float*)(Vs + block * D);
+  float* psm = qsm + G * D;
+  uint32_t w = xcd_remap(blockIdx.x, gridDim.x);   // (b, KV head, split)
+  const int sp = (int)(w % splits);
+  w /= splits;
+  const int g = (int)(w % Hkv), b = (int)(w / Hkv);
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, NT = G * kWave;
+  const int h = g * G + wave, bh = b * Hq + h;
+  const int64_t L = lens[b];
+  const int64_t rs = (int64_t)Hkv * D;
+  float* my = part + ((int64_t)bh * splits + sp) * (D + 2);
+  for (int d = lane; d < D; d += kWave)
+    qsm[wave * D + d] = __uint_as_float((uint32_t)q[(int64_t)bh * D + d] << 16);
+  const int32_t* row = idx + ((int64_t)b * Hq + g * G) * topk;   // the group's common row
+  const int per = (topk + splits - 1) / splits;
+  const int e0 = sp * per, e1 = e0 + per < topk ? e0 + per : topk;
+  float m = -__builtin_inff(), l = 0.f;
+  constexpr int LG = D / 8, KG = 64 / LG;
+  const int dg = lane % LG, kq = lane / LG;
+  float o[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) o[x] = 0.f;
+  const uint16_t* kb0 = kc + (int64_t)b * Lmax * rs + (int64_t)g * D;
+  const uint16_t* vb0 = vc + (int64_t)b * Lmax * rs + (int64_t)g * D;
+  const bool len_ok = L >= 1 && L <= Lmax;
+  __syncthreads();
+  float qv[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) qv[x] = qsm[wave * D + 8 * dg + x];
+  for (int e = e0; e < e1 && len_ok; ++e) {
+    const int j = row[e];
+    if (j < 0 || (int64_t)j * block >= L) continue;   // unused place or beyond the cache
+    const int64_t t0 = (int64_t)j * block;
+    const int nk = (int)(L - t0 < block ? L - t0 : block);   // own block: tokens < L
+    __syncthreads();                          // the previous block is done with Ks, Vs, ps
+    for (int ci = tid; ci < nk * CH; ci += NT) {
+      const int r = ci / CH, cc = ci % CH;
+      *(u32x4*)(Ks + r * D + 8 * cc) = *(const u32x4*)(kb0 + (t0 + r) * rs + 8 * cc);
+      *(u32x4*)(Vs + r * D + 8 * cc) = *(const u32x4*)(vb0 + (t0 + r) * rs + 8 * cc);
+    }
+    __syncthreads();
+    for (int t = kq; t < nk; t += KG) {
+      const u32x4 kw = *(const u32x4*)(Ks + t * D + 8 * dg);
+      float a = 0.f;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        a = __builtin_fmaf(qv[2 * x], bf16lo(kw[x]), a);
+        a = __builtin_fmaf(qv[2 * x + 1], bf16hi(kw[x]), a);
+      }
+#pragma unroll
+      for (int off = 1; off < LG; off <<= 1) a += __shfl_xor(a, off);
+      if (dg == 0) psm[wave * block + t] = a * c;       // exp2 domain
+    }
+    __syncthreads();
+    float s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = lane + 64 * u;
+      s[u] = t < nk ? psm[wave * block + t] : -__builtin_inff();
+    }
+    float mb = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off));
+    const float mn = fmaxf(m, mb);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);    // 0 on the first block
+    m = mn;
+    float lp = 0.f;
+    __syncthreads();                          // scores read before the weights replace them
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = lane + 64 * u;
+      const float p = t < nk ? __builtin_amdgcn_exp2f(s[u] - m) : 0.f;
+      if (t < block) psm[wave * block + t] = p;
+      lp += p;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lp += __shfl_xor(lp, off);
+    l = l * alpha + lp;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) o[x] *= alpha;
+    __syncthreads();
+    for (int t = kq; t < nk; t += KG) {
+      const u32x4 vw = *(const u32x4*)(Vs + t * D + 8 * dg);
+      const float p = psm[wave * block + t];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        o[2 * x] = __builtin_fmaf(p, bf16lo(vw[x]), o[2 * x]);
+        o[2 * x + 1] = __builtin_fmaf(p, bf16hi(vw[x]), o[2 * x + 1]);
+      }
+    }
+  }
+  // sum the key groups (lanes dg, dg + LG, ...)
+#pragma unroll
+  for (int off = LG; off < 64; off <<= 1)
+#pragma unroll
+    for (int x = 0; x < 8; ++x) o[x] += __shfl_xor(o[x], off);
+  if (kq == 0) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) my[2 + 8 * dg + x] = o[x];
+  }
+  if (lane == 0) {
+    my[0] = m;
+    my[1] = l;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void dcombine_kernel(const float* __restrict__ part,
                                                       const int32_t* __restrict__ lens,
@@ -433,14 +559,34 @@ hipError_t launch_decode(int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int bl
   if (e != hipSuccess) return e;
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (D == 64)
+  const int G = Hq / Hkv;
+  if (group && G > 1 && G <= kMaxDecodeGroup) {   // one work-group per (b, KV head, split)
+    const unsigned groups = (unsigned)(B * Hkv * splits);
+    const size_t lds = (size_t)2 * block * D * 2 + (size_t)G * (D + block) * sizeof(float);
+    if (lds > 65536) {                        // beyond the default dynamic LDS of a launch
+      const void* fn = D == 64 ? reinterpret_cast<const void*>(&dattn_group_kernel<64>)
+                               : reinterpret_cast<const void*>(&dattn_group_kernel<128>);
+      const hipError_t ea =
+          hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (ea != hipSuccess) return ea;
+    }
+    if (D == 64)
+      dattn_group_kernel<64><<<groups, G * 64, lds, stream>>>(
+          (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, idx, lens,
+          part, Lmax, Hq, Hkv, block, topk, splits, c);
+    else
+      dattn_group_kernel<128><<<groups, G * 64, lds, stream>>>(
+          (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, idx, lens,
+          part, Lmax, Hq, Hkv, block, topk, splits, c);
+  } else if (D == 64) {
     dattn_kernel<64><<<heads * splits, 64, 0, stream>>>(
         (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, idx, lens, part,
         Lmax, Hq, Hkv, block, topk, splits, c);
-  else
+  } else {
     dattn_kernel<128><<<heads * splits, 64, 0, stream>>>(
         (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, idx, lens, part,
         Lmax, Hq, Hkv, block, topk, splits, c);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (D == 64)
