@@ -31,12 +31,14 @@
 // all 32 banks once.
 //
 // Softmax reference: softmax does not depend on the reference value m subtracted from a row
-// (p = exp2(c*s - m), c = scale*log2(e)), so m stays 0 while every per-lane block sum of
+// (p = exp2(c*s - m), c = scale*log2(e)), so m stays 0 while every per-lane step sum of
 // weights lies in [2^-64, 2^64], which holds for inputs of moderate range: no row max and no
-// rescale are needed. A block outside that range (huge or tiny scores) moves the row's
-// reference to its running max, rescaling O and l by exp2(m_old - m_new). O and l always
-// share one reference, so O/l is the exact softmax average. The normaliser is summed from the
-// bf16-rounded weights (v_dot2c_f32_bf16), i.e. from exactly the weights the PV product uses.
+// rescale are needed. The row is first done with m = 0 throughout, only noting whether a step
+// left that range; a flagged row (huge or tiny scores) is done again from the start, and that
+// pass moves the reference to the running max whenever a step leaves the range, rescaling O
+// and l by exp2(m_old - m_new). O and l always share one reference. The normaliser sums the
+// fp32 weights with plain adds (the bf16 dot instruction shares the matrix unit and would
+// wait for the MFMAs); the PV product takes the same weights rounded to bf16.
 //
 // Causal variant (template flag): query block i reads the first min(topk, i+1) entries of its
 // row, each of which must lie in [0, i]; in its own block i the scores of keys after the
@@ -46,6 +48,8 @@
 // blocks are marked in an LDS bitmap, block j is read from its tile at key_tile_start and
 // the tile's first key_tile_skip keys score -inf, so the union of the row's blocks counts
 // each token once.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -230,16 +234,7 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
   }
 
   f32x16 oacc[C::NDT][C::QC];
-#pragma unroll
-  for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-    for (int qc = 0; qc < C::QC; ++qc)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][qc][r] = 0.f;
   float mc[C::QC], lsum[C::QC];               // reference (exp2 domain); lane's normaliser share
-#pragma unroll
-  for (int qc = 0; qc < C::QC; ++qc) { mc[qc] = 0.f; lsum[qc] = 0.f; }
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   if (OVL) mark_selected(chosen, myidx, kcount, nkb, tid, C::NT);
   // Q must have landed before the first transfer: the hand-placed vmcnt waits in the loop
@@ -248,156 +243,186 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
   for (int qc = 0; qc < C::QC; ++qc)
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) asm volatile("" ::"v"(qf[qc][s]));
-  int kb_cur = myidx[0], u_cur = 0;
-  int skip_cur = skip_of(kb_cur);
-  {
-    const int64_t tb = tile_base(kb_cur, 0);
-    dma(kbase0 + tb, Kl);
-    dma(vbase0 + tb, Vl);
-  }
 
-  for (int t = 0; t < kcount * UN; ++t) {     // steps: UN per selected block
-    const bool more = t + 1 < kcount * UN;
-    const int kb_next = more ? myidx[(t + 1) / UN] : 0;
-    const int u_next = (t + 1) % UN;
-    const int64_t tb_next = more ? tile_base(kb_next, u_next) : 0;
-    const int skip_next = OVL && more ? skip_of(kb_next) : 0;
+  // One pass over the row's steps. The first pass (CHECKED = false) keeps the reference at 0
+  // and only records whether some step's weight sum left [2^-64, 2^64]; rows it flags are
+  // done again from the start with CHECKED = true, which moves the reference to the row max
+  // whenever that happens. Taking the check out of the common pass lets the weights, the
+  // normaliser and the products of consecutive steps overlap.
+  auto pass = [&](auto checked_tag) -> bool {
+    constexpr bool CHECKED = decltype(checked_tag)::value;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+      for (int qc = 0; qc < C::QC; ++qc)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][qc][r] = 0.f;
+#pragma unroll
+    for (int qc = 0; qc < C::QC; ++qc) { mc[qc] = 0.f; lsum[qc] = 0.f; }
+    bool flagged = false;
+    int kb_cur = myidx[0], u_cur = 0;
+    int skip_cur = skip_of(kb_cur);
+    {
+      const int64_t tb = tile_base(kb_cur, 0);
+      dma(kbase0 + tb, Kl);
+      dma(vbase0 + tb, Vl);
+    }
 
-    // ---- K(t): wait for this wave's share (V(t) may still fly), then the whole work-group
-    wait_vmcnt<C::DMA>();
-    if (C::NW > 1) __syncthreads();
-    bf16x8 ka[C::NKT][C::NS];
-#pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-      for (int s = 0; s < C::NS; ++s)
-        ka[kt][s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kl + kt * 32 * D * 2 + koff[s]));
-    wait_lgkmcnt0();
-    if (C::NW > 1) __syncthreads();
-    if (more) dma(kbase0 + tb_next, Kl);
+    for (int t = 0; t < kcount * UN; ++t) {     // steps: UN per selected block
+      const bool more = t + 1 < kcount * UN;
+      const int kb_next = more ? myidx[(t + 1) / UN] : 0;
+      const int u_next = (t + 1) % UN;
+      const int64_t tb_next = more ? tile_base(kb_next, u_next) : 0;
+      const int skip_next = OVL && more ? skip_of(kb_next) : 0;
 
-    // ---- S^T = K Q^T
-    f32x16 sacc[C::NKT][C::QC];
+      // ---- K(t): wait for this wave's share (V(t) may still fly), then the whole work-group
+      wait_vmcnt<C::DMA>();
+      if (C::NW > 1) __syncthreads();
+      bf16x8 ka[C::NKT][C::NS];
 #pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-      for (int qc = 0; qc < C::QC; ++qc) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kt][qc][r] = 0.f;
+      for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
         for (int s = 0; s < C::NS; ++s)
-          sacc[kt][qc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kt][s], qf[qc][s], sacc[kt][qc], 0, 0, 0);
-      }
-    if (CAUSAL && kb_cur == i) {               // own block: keys after the query get -inf
-#pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-        for (int qc = 0; qc < C::QC; ++qc)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = KU * u_cur + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-            const int qry = R * hq + C::QW * wave + 32 * qc + l32;
-            if (key > qry) sacc[kt][qc][r] = -__builtin_inff();
-          }
-    }
-    if (OVL && skip_cur > KU * u_cur) {        // keys before the block or held by block kb-1
-#pragma unroll
-      for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-        for (int qc = 0; qc < C::QC; ++qc)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = KU * u_cur + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key < skip_cur) sacc[kt][qc][r] = -__builtin_inff();
-          }
-    }
+          ka[kt][s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kl + kt * 32 * D * 2 + koff[s]));
+      wait_lgkmcnt0();
+      if (C::NW > 1) __syncthreads();
+      if (more) dma(kbase0 + tb_next, Kl);
 
-    // ---- softmax weights (lane pair l, l^32 shares one query row): p = exp2(c*s - m), m the
-    // row reference in the exp2 domain (0 until a block sum leaves [2^-64, 2^64])
-    auto row_max = [&](int qc) {
-      float mt = sacc[0][qc][0];
+      // ---- S^T = K Q^T
+      f32x16 sacc[C::NKT][C::QC];
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kt][qc][r]);
-      return fmaxf(mt, __shfl_xor(mt, 32)) * c;
-    };
-    uint32_t pw[C::QC][C::NPS][4];
-    float bsum[C::QC];
-    auto weights = [&](int qc) {
-      bsum[qc] = 0.f;
+        for (int qc = 0; qc < C::QC; ++qc) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kt][qc][r] = 0.f;
+#pragma unroll
+          for (int s = 0; s < C::NS; ++s)
+            sacc[kt][qc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kt][s], qf[qc][s], sacc[kt][qc], 0, 0, 0);
+        }
+      if (CAUSAL && kb_cur == i) {               // own block: keys after the query get -inf
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+          for (int qc = 0; qc < C::QC; ++qc)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = KU * u_cur + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+              const int qry = R * hq + C::QW * wave + 32 * qc + l32;
+              if (key > qry) sacc[kt][qc][r] = -__builtin_inff();
+            }
+      }
+      if (OVL && skip_cur > KU * u_cur) {        // keys before the block or held by block kb-1
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+          for (int qc = 0; qc < C::QC; ++qc)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = KU * u_cur + 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+              if (key < skip_cur) sacc[kt][qc][r] = -__builtin_inff();
+            }
+      }
+
+      // ---- softmax weights (lane pair l, l^32 shares one query row): p = exp2(c*s - m), m the
+      // row reference in the exp2 domain (0 until a block sum leaves [2^-64, 2^64])
+      auto row_max = [&](int qc) {
+        float mt = sacc[0][qc][0];
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kt][qc][r]);
+        return fmaxf(mt, __shfl_xor(mt, 32)) * c;
+      };
+      uint32_t pw[C::QC][C::NPS][4];
+      float bsum[C::QC];
+      auto weights = [&](int qc) {
+        float sa = 0.f, sb = 0.f;                // two add chains
+#pragma unroll
+        for (int s = 0; s < C::NPS; ++s)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(sacc[s >> 1][qc][8 * (s & 1) + 2 * e], c, -mc[qc]));
+            const float p1 = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(sacc[s >> 1][qc][8 * (s & 1) + 2 * e + 1], c, -mc[qc]));
+            const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+            pw[qc][s][e] = __builtin_bit_cast(uint32_t, pp);
+            sa += p0;
+            sb += p1;
+          }
+        bsum[qc] = sa + sb;
+      };
+#pragma unroll
+      for (int qc = 0; qc < C::QC; ++qc) weights(qc);
+      bool off_range = false;
+#pragma unroll
+      for (int qc = 0; qc < C::QC; ++qc)
+        off_range |= (bsum[qc] > kSumHi) || (lsum[qc] + bsum[qc] < kSumLo);
+      if (!CHECKED) flagged |= off_range;
+      if (CHECKED && __ballot(off_range)) {      // move the reference to the row max
+#pragma unroll
+        for (int qc = 0; qc < C::QC; ++qc) {
+          const float bm = row_max(qc);
+          const float l_row = lsum[qc] + __shfl_xor(lsum[qc], 32);   // same on both lanes
+          if (l_row == 0.f) {                    // nothing accumulated yet: O and l are zero
+            if (bm != -__builtin_inff()) mc[qc] = bm;   // (a step whose keys are all left out)
+          } else {
+            const float m_new = fmaxf(mc[qc], bm);
+            const float alpha = __builtin_amdgcn_exp2f(mc[qc] - m_new);
+            lsum[qc] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) oacc[dt][qc][r] *= alpha;
+            mc[qc] = m_new;
+          }
+          weights(qc);
+        }
+      }
+#pragma unroll
+      for (int qc = 0; qc < C::QC; ++qc) lsum[qc] += bsum[qc];
+
+      // ---- V(t): wait (K(t+1) may still fly), read all V^T operands, then start V(t+1)
+      if (more) wait_vmcnt<C::DMA>(); else wait_vmcnt<0>();
+      if (C::NW > 1) __syncthreads();
+      bf16x8 va[C::NPS][C::NDT];
 #pragma unroll
       for (int s = 0; s < C::NPS; ++s)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float s0 = sacc[s >> 1][qc][8 * (s & 1) + 2 * e];
-          const float s1 = sacc[s >> 1][qc][8 * (s & 1) + 2 * e + 1];
-          const bf16x2 pp = {(__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0, c, -mc[qc])),
-                             (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s1, c, -mc[qc]))};
-          pw[qc][s][e] = __builtin_bit_cast(uint32_t, pp);
-          bsum[qc] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, bsum[qc], false);
+        for (int dt = 0; dt < C::NDT; ++dt) {
+          const char* p = Vl + (16 * s) * D * 2 + voff[dt];
+          const s16x4 a8[2] = {ds_read_tr16(p), ds_read_tr16(p + 8 * D * 2)};
+          va[s][dt] = __builtin_bit_cast(bf16x8, a8);
         }
-    };
+      wait_lgkmcnt0();
+      if (C::NW > 1) __syncthreads();
+      if (more) dma(vbase0 + tb_next, Vl);
+
+      // ---- O^T += V^T P^T
 #pragma unroll
-    for (int qc = 0; qc < C::QC; ++qc) weights(qc);
-    bool off_range = false;
+      for (int s = 0; s < C::NPS; ++s)
 #pragma unroll
-    for (int qc = 0; qc < C::QC; ++qc)
-      off_range |= (bsum[qc] > kSumHi) || (lsum[qc] + bsum[qc] < kSumLo);
-    if (__ballot(off_range)) {                 // rare: move the reference to the row max
-#pragma unroll
-      for (int qc = 0; qc < C::QC; ++qc) {
-        const float bm = row_max(qc);
-        const float l_row = lsum[qc] + __shfl_xor(lsum[qc], 32);   // same on both lanes
-        if (l_row == 0.f) {                    // nothing accumulated yet: O and l are zero
-          if (bm != -__builtin_inff()) mc[qc] = bm;   // (a step whose keys are all left out)
-        } else {
-          const float m_new = fmaxf(mc[qc], bm);
-          const float alpha = __builtin_amdgcn_exp2f(mc[qc] - m_new);
-          lsum[qc] *= alpha;
+        for (int qc = 0; qc < C::QC; ++qc) {
+          const u32x4 pv = {pw[qc][s][0], pw[qc][s][1], pw[qc][s][2], pw[qc][s][3]};
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
 #pragma unroll
           for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[dt][qc][r] *= alpha;
-          mc[qc] = m_new;
+            oacc[dt][qc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s][dt], pb, oacc[dt][qc], 0, 0, 0);
         }
-        weights(qc);
-      }
+      kb_cur = kb_next;
+      u_cur = u_next;
+      if (OVL) skip_cur = skip_next;
     }
-#pragma unroll
-    for (int qc = 0; qc < C::QC; ++qc) lsum[qc] += bsum[qc];
-
-    // ---- V(t): wait (K(t+1) may still fly), read all V^T operands, then start V(t+1)
-    if (more) wait_vmcnt<C::DMA>(); else wait_vmcnt<0>();
-    if (C::NW > 1) __syncthreads();
-    bf16x8 va[C::NPS][C::NDT];
-#pragma unroll
-    for (int s = 0; s < C::NPS; ++s)
-#pragma unroll
-      for (int dt = 0; dt < C::NDT; ++dt) {
-        const char* p = Vl + (16 * s) * D * 2 + voff[dt];
-        const s16x4 a8[2] = {ds_read_tr16(p), ds_read_tr16(p + 8 * D * 2)};
-        va[s][dt] = __builtin_bit_cast(bf16x8, a8);
-      }
-    wait_lgkmcnt0();
-    if (C::NW > 1) __syncthreads();
-    if (more) dma(vbase0 + tb_next, Vl);
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int s = 0; s < C::NPS; ++s)
-#pragma unroll
-      for (int qc = 0; qc < C::QC; ++qc) {
-        const u32x4 pv = {pw[qc][s][0], pw[qc][s][1], pw[qc][s][2], pw[qc][s][3]};
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
-#pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt)
-          oacc[dt][qc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s][dt], pb, oacc[dt][qc], 0, 0, 0);
-      }
-    kb_cur = kb_next;
-    u_cur = u_next;
-    if (OVL) skip_cur = skip_next;
-  }
+    return flagged;
+  };
+  // the decision is work-group-wide: the waves of a work-group share the tiles and barriers.
+  // The causal and overlapping-block variants keep a single checked pass (their extra masking
+  // leaves no registers for a second copy of the loop with two waves per SIMD).
+  if constexpr (CAUSAL || OVL)
+    pass(std::true_type{});
+  else if (__syncthreads_or(pass(std::false_type{})))
+    pass(std::true_type{});
 
   // epilogue: O = O^T / l, bf16, 4 consecutive d per store
 #pragma unroll

@@ -88,11 +88,14 @@ def test_forward(dtype, shape):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("case", ["huge_first", "tiny_all", "huge_later"])
-def test_extreme_score_ranges(dtype, case):
+@pytest.mark.parametrize("D,blk", [(64, 64), (128, 64), (64, 128)])
+def test_extreme_score_ranges(dtype, case, D, blk):
     """Scores far outside exp2's range: the softmax must still be the exact average
-    (covers the kernels' reference-maximum paths)."""
-    say(f"[extreme] {case} {dtype}")
-    B, N, H, D, blk, topk = 1, 64 * 16, 2, 64, 64, 6
+    (covers the kernels' reference-maximum paths; the bf16 kernel does such rows a second
+    time, with one wave per work-group for (64, 64) and several for the other shapes)."""
+    say(f"[extreme] {case} {dtype} D={D} block={blk}")
+    B, N, H, topk = 1, 1024, 2, 6
+    nb = N // blk
     g = torch.Generator().manual_seed(31)
     q = torch.randn(B, N, H, D, generator=g)
     k = torch.randn(B, N, H, D, generator=g)
@@ -103,13 +106,13 @@ def test_extreme_score_ranges(dtype, case):
         k += 10.0                                  # every key shares a large component ...
         q = -3.0 + 0.1 * q                         # ... and every query points against it
     else:
-        k[:, 9 * blk:10 * blk] *= 40.0             # one key block with huge scores
+        k[:, (nb - 1) * blk:] *= 40.0              # one key block with huge scores
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     q, k, v = (x.to(tdt).to(DEV) for x in (q, k, v))
     idx = bst.select(q, k, blk, topk)
-    if case == "huge_later":                       # make block 9 a late member of every row
-        idx = torch.tensor([[0, 1, 2, 3, 4, 9]] * (H * (N // blk)), dtype=torch.int32,
-                           device=DEV).view(B, H, N // blk, topk)
+    if case == "huge_later":                       # make the last block a late member of every row
+        idx = torch.tensor([[0, 1, 2, 3, 4, nb - 1]] * (H * nb), dtype=torch.int32,
+                           device=DEV).view(B, H, nb, topk)
     out = bst.forward(q, k, v, idx)
     torch.cuda.synchronize()
     qo, ko, vo = to_f64(q), to_f64(k), to_f64(v)
