@@ -86,11 +86,12 @@ def test_decode(case):
 
 
 GROUP_CASES = [
-    # B, Lmax, Hq, Hkv, D, block, topk, lens (GQA 2 to 8, every selection-kernel form)
+    # B, Lmax, Hq, Hkv, D, block, topk, lens (GQA 2 to 16, every selection-kernel form)
     (4, 64 * 20, 4, 2, 64, 64, 5, [1280, 97, 1, 64 * 7]),
     (3, 128 * 12, 8, 2, 128, 128, 3, [1536, 1000, 129]),
     (2, 64 * 1000, 8, 2, 128, 64, 76, [64000, 33333]),
     (1, 64 * 3000, 8, 1, 64, 64, 30, [192000]),
+    (2, 64 * 40, 16, 1, 64, 64, 9, [2560, 700]),     # G = 16: the largest group of one work-group
 ]
 
 
