@@ -37,8 +37,8 @@
 // left that range; a flagged row (huge or tiny scores) is done again from the start, and that
 // pass moves the reference to the running max whenever a step leaves the range, rescaling O
 // and l by exp2(m_old - m_new). O and l always share one reference. The normaliser sums the
-// fp32 weights with plain adds (the bf16 dot instruction shares the matrix unit and would
-// wait for the MFMAs); the PV product takes the same weights rounded to bf16.
+// fp32 weights with plain adds (measured: the bf16 dot instruction waits for MFMAs in flight,
+// so it cannot hide under them); the PV product takes the same weights rounded to bf16.
 //
 // Causal variant (template flag): query block i reads the first min(topk, i+1) entries of its
 // row, each of which must lie in [0, i]; in its own block i the scores of keys after the
