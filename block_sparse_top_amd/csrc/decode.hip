@@ -64,6 +64,43 @@ __global__ __launch_bounds__(256) void pool_new_kernel(const uint16_t* __restric
   }
 }
 
+// ---------------------------------------------------------------- lane reductions
+// Reductions within aligned groups of lanes through DPP moves (VALU): xor 1 and xor 2 inside a
+// quad, then the mirrored quad of the 8-lane half row, then the mirrored half of the 16-lane
+// row. Every lane of the group ends with the group's value; all lanes of a group must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;                // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;                // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;         // lane i <-> 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;             // lane i <-> 15 - i within each 16 lanes
+
+template <int LG>                             // LG = 8 or 16
+__device__ __forceinline__ float group_sum(float a) {
+  static_assert(LG == 8 || LG == 16, "DPP groups of 8 or 16 lanes");
+  a += dpp_mov<kDppXor1>(a);
+  a += dpp_mov<kDppXor2>(a);
+  a += dpp_mov<kDppHalfMirror>(a);
+  if constexpr (LG == 16) a += dpp_mov<kDppMirror>(a);
+  return a;
+}
+__device__ __forceinline__ float wave_sum(float a) {
+  a = group_sum<16>(a);
+  a += __shfl_xor(a, 16);
+  return a + __shfl_xor(a, 32);
+}
+__device__ __forceinline__ float wave_max(float a) {
+  a = fmaxf(a, dpp_mov<kDppXor1>(a));
+  a = fmaxf(a, dpp_mov<kDppXor2>(a));
+  a = fmaxf(a, dpp_mov<kDppHalfMirror>(a));
+  a = fmaxf(a, dpp_mov<kDppMirror>(a));
+  a = fmaxf(a, __shfl_xor(a, 16));
+  return fmaxf(a, __shfl_xor(a, 32));
+}
+
 // ---------------------------------------------------------------- selection
 constexpr int kSelWaves = 4;                  // (sequence, head) pairs per work-group
 constexpr int kMaxDecodeGroup = 16;           // query heads per KV head in one work-group
@@ -260,8 +297,7 @@ __global__ __launch_bounds__(64) void dattn_kernel(
           a = __builtin_fmaf(qv[2 * x], bf16lo(w[u][x]), a);
           a = __builtin_fmaf(qv[2 * x + 1], bf16hi(w[u][x]), a);
         }
-#pragma unroll
-        for (int off = 1; off < LG; off <<= 1) a += __shfl_xor(a, off);
+        a = group_sum<LG>(a);
         const int tt = t + u * KG;
         if (dg == 0 && tt < nk) ps[tt] = a * c;   // exp2 domain
       }
@@ -274,8 +310,7 @@ __global__ __launch_bounds__(64) void dattn_kernel(
       s[u] = t < nk ? ps[t] : -__builtin_inff();
     }
     float mb = fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mb = fmaxf(mb, __shfl_xor(mb, o));
+    mb = wave_max(mb);
     const float mn = fmaxf(m, mb);
     const float alpha = __builtin_amdgcn_exp2f(m - mn);    // 0 on the first block
     m = mn;
@@ -288,8 +323,7 @@ __global__ __launch_bounds__(64) void dattn_kernel(
       if (t < block) ps[t] = p;
       lp += p;
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) lp += __shfl_xor(lp, o);
+    lp = wave_sum(lp);
     l = l * alpha + lp;
 #pragma unroll
     for (int x = 0; x < 8; ++x) o[x] *= alpha;
@@ -403,8 +437,7 @@ __global__ __launch_bounds__(1024) void dattn_group_kernel(
         a = __builtin_fmaf(qv[2 * x], bf16lo(kw[x]), a);
         a = __builtin_fmaf(qv[2 * x + 1], bf16hi(kw[x]), a);
       }
-#pragma unroll
-      for (int off = 1; off < LG; off <<= 1) a += __shfl_xor(a, off);
+      a = group_sum<LG>(a);
       if (dg == 0) psm[wave * block + t] = a * c;       // exp2 domain
     }
     __syncthreads();
@@ -415,8 +448,7 @@ __global__ __launch_bounds__(1024) void dattn_group_kernel(
       s[u] = t < nk ? psm[wave * block + t] : -__builtin_inff();
     }
     float mb = fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off));
+    mb = wave_max(mb);
     const float mn = fmaxf(m, mb);
     const float alpha = __builtin_amdgcn_exp2f(m - mn);    // 0 on the first block
     m = mn;
@@ -429,8 +461,7 @@ __global__ __launch_bounds__(1024) void dattn_group_kernel(
       if (t < block) psm[wave * block + t] = p;
       lp += p;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) lp += __shfl_xor(lp, off);
+    lp = wave_sum(lp);
     l = l * alpha + lp;
 #pragma unroll
     for (int x = 0; x < 8; ++x) o[x] *= alpha;
