@@ -19,6 +19,31 @@ constexpr int kWave = 64;
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Reductions within aligned groups of lanes through DPP moves (VALU, no LDS): xor 1 and xor 2
+// inside a quad, then the mirrored quad of the 8-lane half row, then the mirrored half of the
+// 16-lane row. Every lane of a group ends with the group's value; all lanes of a group must be
+// active.
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_mov(T v) {
+  static_assert(sizeof(T) == 4, "32-bit lanes");
+  return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                           0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;                // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;                // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;         // lane i <-> 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;             // lane i <-> 15 - i within each 16 lanes
+
+template <int LG, typename T>                 // LG = 8 or 16
+__device__ __forceinline__ T group_sum(T a) {
+  static_assert(LG == 8 || LG == 16, "DPP groups of 8 or 16 lanes");
+  a += dpp_mov<kDppXor1>(a);
+  a += dpp_mov<kDppXor2>(a);
+  a += dpp_mov<kDppHalfMirror>(a);
+  if constexpr (LG == 16) a += dpp_mov<kDppMirror>(a);
+  return a;
+}
+
 // Two floats -> packed bfloat16 pair (round to nearest even), lo in bits 0..15.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -64,29 +64,7 @@ __global__ __launch_bounds__(256) void pool_new_kernel(const uint16_t* __restric
   }
 }
 
-// ---------------------------------------------------------------- lane reductions
-// Reductions within aligned groups of lanes through DPP moves (VALU): xor 1 and xor 2 inside a
-// quad, then the mirrored quad of the 8-lane half row, then the mirrored half of the 16-lane
-// row. Every lane of the group ends with the group's value; all lanes of a group must be active.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                               0xF, 0xF, false));
-}
-constexpr int kDppXor1 = 0xB1;                // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;                // quad_perm [2, 3, 0, 1]
-constexpr int kDppHalfMirror = 0x141;         // lane i <-> 7 - i within each 8 lanes
-constexpr int kDppMirror = 0x140;             // lane i <-> 15 - i within each 16 lanes
-
-template <int LG>                             // LG = 8 or 16
-__device__ __forceinline__ float group_sum(float a) {
-  static_assert(LG == 8 || LG == 16, "DPP groups of 8 or 16 lanes");
-  a += dpp_mov<kDppXor1>(a);
-  a += dpp_mov<kDppXor2>(a);
-  a += dpp_mov<kDppHalfMirror>(a);
-  if constexpr (LG == 16) a += dpp_mov<kDppMirror>(a);
-  return a;
-}
+// whole-wave reductions: the DPP steps within each 16 lanes, then across 16 and 32 lanes
 __device__ __forceinline__ float wave_sum(float a) {
   a = group_sum<16>(a);
   a += __shfl_xor(a, 16);

@@ -114,9 +114,11 @@ constexpr int kTopkThreads = 256;
 constexpr int kPerThread = 32;             // columns per thread: nb <= 8192
 
 __device__ __forceinline__ int block_sum(int v, int* red) {
-  // wave sum by butterfly, then the 4 wave sums through LDS (caller syncs around reuse)
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  // wave sum (DPP within 16 lanes, then across 16 and 32 lanes), then the 4 wave sums
+  // through LDS (caller syncs around reuse)
+  v = group_sum<16>(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
   const int w = threadIdx.x / kWave;
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
