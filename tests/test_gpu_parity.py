@@ -123,6 +123,39 @@ def test_extreme_score_ranges(dtype, case, D, blk):
     say("   max_abs, rel_l2 =", err)
 
 
+@pytest.mark.parametrize("D,blk", [(64, 64), (128, 128)])
+def test_flagged_and_plain_rows_in_one_launch(D, blk):
+    """Rows whose weights leave the plain pass's range sit next to rows that do not, in one
+    launch: the bf16 kernel redoes only the flagged work-groups, and every row still matches
+    the oracle (half of the rows read a key block with huge scores, the others do not)."""
+    say(f"[mixed rows] D={D} block={blk}")
+    B, N, H, topk = 1, 2048, 2, 5
+    nb = N // blk
+    g = torch.Generator().manual_seed(43)
+    q = torch.randn(B, N, H, D, generator=g)
+    k = torch.randn(B, N, H, D, generator=g)
+    v = torch.randn(B, N, H, D, generator=g)
+    k[:, (nb - 1) * blk:] *= 40.0                  # the last key block: huge scores
+    q, k, v = (x.to(torch.bfloat16).to(DEV) for x in (q, k, v))
+    rows = []
+    for r in range(H * nb):                        # even rows hold the huge block, odd ones not
+        base = [(r + 3 * e) % (nb - 1) for e in range(topk)]
+        base = sorted(set(base))[:topk - 1] if r % 2 == 0 else sorted(set(base))
+        if r % 2 == 0:
+            base = base + [nb - 1]
+        while len(base) < topk:                    # fill to topk distinct blocks below nb - 1
+            base = sorted(set(base) | {min(set(range(nb - 1)) - set(base))})
+        rows.append(sorted(base))
+    idx = torch.tensor(rows, dtype=torch.int32, device=DEV).view(B, H, nb, topk)
+    out = bst.forward(q, k, v, idx)
+    torch.cuda.synchronize()
+    qo, ko, vo = to_f64(q), to_f64(k), to_f64(v)
+    ref = O.attend(qo, ko, vo, idx.cpu().numpy(), blk, 1 / math.sqrt(D))
+    got = out.float().cpu().numpy()
+    err = check_out(got, ref, "bf16", abs_scale=max(1.0, float(np.abs(ref).max())))
+    say("   max_abs, rel_l2 =", err)
+
+
 def test_tiny_workload_end_to_end():
     w = syn.WORKLOADS["tiny_f32"]
     say("[tiny] block_sparse_attention on", w)
