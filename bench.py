@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--key-stride", type=int, default=0,
                    help="overlapping key blocks starting every KEY_STRIDE tokens (0: block; "
                         "the overlap ratio 0.25 is 3/4 of the block)")
+    p.add_argument("--random-places", type=int, default=0,
+                   help="places of each row filled by seeded random blocks (-1: int(0.05 k), the "
+                        "MSA page's 5 %% random blocks)")
     p.add_argument("--backward", action="store_true",
                    help="also time bsattn_backward (bf16, block 64) on the same selection")
     p.add_argument("--decode", action="store_true",
@@ -317,9 +320,11 @@ def main():
     flags = (bst.CAUSAL if args.causal else 0) | (bst.POOL_MAX if args.pooling == "max" else 0) \
         | (bst.GROUP_SELECT if args.group else 0)
 
+    nrand = int(0.05 * topk) if args.random_places < 0 else args.random_places
+
     def do_select():
-        st = L.bsattn_select_ex(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, 0, 0,
-                                ks, P(q), P(k), P(idx), P(ws), ws.numel(), sp)
+        st = L.bsattn_select_ex(dcode, w.B, w.N, w.Hq, w.Hkv, w.D, w.block, topk, flags, nrand,
+                                12345, ks, P(q), P(k), P(idx), P(ws), ws.numel(), sp)
         assert st == 0, L.bsattn_last_error()
 
     def do_forward():
@@ -381,6 +386,7 @@ def main():
                    **({"causal": True} if args.causal else {}),
                    **({"pooling": "max"} if args.pooling == "max" else {}),
                    **({"group_select": True} if args.group else {}),
+                   **({"random_places": nrand} if nrand else {}),
                    **({"key_stride": ks, "key_blocks": nkb} if ks != w.block else {})},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
