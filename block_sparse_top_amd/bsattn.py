@@ -113,21 +113,41 @@ def _stream(dev) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+def _device_tensor(t, name: str, device, dtype=None, shape=None, min_bytes: int | None = None):
+    """Refuses anything the library must not receive as a device pointer: a tensor on the
+    host or on another device than `device`, a non-contiguous one, a wrong dtype or shape, or
+    one smaller than `min_bytes`. Every tensor argument of every entry point passes here."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (got one on {t.device})")
+    if device is not None and t.device != torch.device(device):
+        raise ValueError(f"{name} is on {t.device}, the other arguments on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, {min_bytes} needed")
+    return t
+
+
 def _shapes(q, k, v=None):
+    if not isinstance(q, torch.Tensor) or not isinstance(k, torch.Tensor):
+        raise TypeError("q and k must be torch tensors")
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be [B, N, H, D]")
     B, N, Hq, D = q.shape
     if k.shape[0] != B or k.shape[1] != N or k.shape[3] != D:
         raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
-    if v is not None and v.shape != k.shape:
-        raise ValueError("v must have the shape of k")
-    for t in (q, k) + ((v,) if v is not None else ()):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q/k/v must be contiguous device tensors")
-        if t.dtype != q.dtype:
-            raise ValueError("q, k, v must share one dtype")
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
+    _device_tensor(q, "q", None)
+    _device_tensor(k, "k", q.device, q.dtype)
+    if v is not None:
+        _device_tensor(v, "v", q.device, q.dtype, k.shape)
     return B, N, Hq, k.shape[2], D
 
 
@@ -181,6 +201,7 @@ def select(q, k, block: int, topk: int, *, causal: bool = False, pooling: str = 
     nbytes = select_workspace_bytes(B, N, Hq, Hkv, D, block, key_stride) if valid else 0
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _device_tensor(workspace, "workspace", q.device, min_bytes=nbytes)
     with torch.cuda.device(q.device):
         _check(lib().bsattn_select_ex(_DTYPES[q.dtype], B, N, Hq, Hkv, D, block, topk, flags,
                                       int(nrand), int(seed) & ((1 << 64) - 1), int(key_stride),
@@ -207,7 +228,8 @@ def forward(q, k, v, idx, scale: float | None = None, descales=(1.0, 1.0, 1.0), 
     log-sum-exp, fp32 [B, Hq, N] (the input `backward` needs).
     """
     B, N, Hq, Hkv, D = _shapes(q, k, v)
-    if idx.dim() != 4 or idx.dtype != torch.int32 or not idx.is_contiguous() or not idx.is_cuda:
+    _device_tensor(idx, "idx", q.device, torch.int32)
+    if idx.dim() != 4:
         raise ValueError("idx must be a contiguous int32 device tensor [B, Hq, nb, topk]")
     nb, topk = idx.shape[2], idx.shape[3]
     if idx.shape[0] != B or idx.shape[1] != Hq or (nb and N % nb):
@@ -219,8 +241,8 @@ def forward(q, k, v, idx, scale: float | None = None, descales=(1.0, 1.0, 1.0), 
     odt = torch.float32 if q.dtype == torch.float32 else torch.bfloat16
     if out is None:
         out = torch.empty((B, N, Hq, D), dtype=odt, device=q.device)
-    elif out.shape != (B, N, Hq, D) or out.dtype != odt or not out.is_contiguous():
-        raise ValueError("out has the wrong shape, dtype or layout")
+    else:
+        _device_tensor(out, "out", q.device, odt, (B, N, Hq, D))
     ds = (ctypes.c_float * 3)(*[float(x) for x in descales])
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if return_lse else None
     with torch.cuda.device(q.device):
@@ -239,13 +261,14 @@ def backward(q, k, v, idx, out, dout, lse, scale: float | None = None, *, causal
     out and lse come from `forward(..., return_lse=True)`; dout is bf16 like out.
     """
     B, N, Hq, Hkv, D = _shapes(q, k, v)
+    _device_tensor(idx, "idx", q.device, torch.int32)
+    if idx.dim() != 4 or idx.shape[0] != B or idx.shape[1] != Hq:
+        raise ValueError("idx must be int32 [B, Hq, nb, topk]")
     nb, topk = idx.shape[2], idx.shape[3]
     block = N // nb if nb else 0
-    for t in (out, dout):
-        if t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise ValueError("out and dout must be contiguous bf16 [B, N, Hq, D]")
-    if lse.shape != (B, Hq, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous fp32 [B, Hq, N]")
+    _device_tensor(out, "out", q.device, torch.bfloat16, q.shape)
+    _device_tensor(dout, "dout", q.device, torch.bfloat16, q.shape)
+    _device_tensor(lse, "lse", q.device, torch.float32, (B, Hq, N))
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
@@ -254,6 +277,7 @@ def backward(q, k, v, idx, out, dout, lse, scale: float | None = None, *, causal
     nbytes = int(L.bsattn_backward_workspace_bytes(B, N, Hq, Hkv, D, block, topk)) if block else 0
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _device_tensor(workspace, "workspace", q.device, min_bytes=nbytes)
     with torch.cuda.device(q.device):
         _check(L.bsattn_backward(_DTYPES[q.dtype], B, N, Hq, Hkv, D, block, topk,
                                  CAUSAL if causal else 0, _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
@@ -284,7 +308,18 @@ def block_sparse_attention(q, k, v, block_size: int = 64, topk_ratio: float = 0.
 def decode_pool(k_cache, lens_new, kbar, block: int, lens_old=None):
     """Pools the key blocks completed between lens_old and lens_new (all complete blocks if
     lens_old is None) into kbar, fp32 [B, Hkv, D, Lmax // block] (transposed), in place."""
+    if not isinstance(k_cache, torch.Tensor) or k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B, Lmax, Hkv, D]")
     B, Lmax, Hkv, D = k_cache.shape
+    if k_cache.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {k_cache.dtype}")
+    dev = k_cache.device
+    _device_tensor(k_cache, "k_cache", None)
+    _device_tensor(lens_new, "lens_new", dev, torch.int32, (B,))
+    if lens_old is not None:
+        _device_tensor(lens_old, "lens_old", dev, torch.int32, (B,))
+    _device_tensor(kbar, "kbar", dev, torch.float32,
+                   (B, Hkv, D, Lmax // block if block > 0 else 0))
     with torch.cuda.device(k_cache.device):
         _check(lib().bsattn_decode_pool(_DTYPES[k_cache.dtype], B, Lmax, Hkv, D, block,
                                         _ptr(k_cache), _ptr(lens_old), _ptr(lens_new),
@@ -298,15 +333,28 @@ def decode(q, k_cache, v_cache, kbar, lens, block: int, topk: int, scale: float 
     [B, Lmax, Hkv, D], kbar from `decode_pool`, lens int32 [B] on the device. group: one
     choice of blocks per KV head from its query heads' summed scores, shared by them.
     Returns (out bf16 [B, Hq, D], idx int32 [B, Hq, topk])."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be [B, Hq, D]")
+    if not isinstance(k_cache, torch.Tensor) or k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B, Lmax, Hkv, D]")
     B, Hq, D = q.shape
     Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    _device_tensor(q, "q", None)
+    _device_tensor(k_cache, "k_cache", q.device, q.dtype, (B, Lmax, Hkv, D))
+    _device_tensor(v_cache, "v_cache", q.device, q.dtype, (B, Lmax, Hkv, D))
+    _device_tensor(kbar, "kbar", q.device, torch.float32,
+                   (B, Hkv, D, Lmax // block if block > 0 else 0))
+    _device_tensor(lens, "lens", q.device, torch.int32, (B,))
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
     idx = torch.empty((B, Hq, topk), dtype=torch.int32, device=q.device)
     L = lib()
+    n = int(L.bsattn_decode_workspace_bytes(B, Hq, D, max(topk, 1))) if B else 0
     if workspace is None:
-        n = int(L.bsattn_decode_workspace_bytes(B, Hq, D, max(topk, 1))) if B else 0
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _device_tensor(workspace, "workspace", q.device, min_bytes=n)
     with torch.cuda.device(q.device):
         _check(L.bsattn_decode_ex(_DTYPES[q.dtype], B, Lmax, Hq, Hkv, D, block, topk,
                                   GROUP_SELECT if group else 0, _ptr(q), _ptr(k_cache),

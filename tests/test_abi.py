@@ -224,10 +224,82 @@ def test_workspace_bytes():
 
 
 def test_python_binding_refuses_cpu_tensors():
+    """Every entry point refuses host tensors before any call into the library (a host
+    pointer handed to a kernel would fault the GPU)."""
     import torch
     x = torch.zeros(1, 128, 2, 64, dtype=torch.bfloat16)
-    with pytest.raises(ValueError):
+    idx = torch.zeros(1, 2, 2, 1, dtype=torch.int32)
+    lse = torch.zeros(1, 2, 128)
+    with pytest.raises(ValueError, match="device"):
         bst.select(x, x, 64, 1)
+    with pytest.raises(ValueError, match="device"):
+        bst.forward(x, x, x, idx)
+    with pytest.raises(ValueError, match="device"):
+        bst.backward(x, x, x, idx, x, x, lse)
+    with pytest.raises(ValueError, match="device"):
+        bst.block_sparse_attention(x, x, x, 64, 0.5)
+    kc = torch.zeros(2, 256, 1, 64, dtype=torch.bfloat16)
+    lens = torch.tensor([200, 256], dtype=torch.int32)
+    kbar = torch.zeros(2, 1, 64, 4)
+    with pytest.raises(ValueError, match="device"):
+        bst.decode_pool(kc, lens, kbar, 64)
+    with pytest.raises(ValueError, match="device"):
+        bst.decode(torch.zeros(2, 2, 64, dtype=torch.bfloat16), kc, kc, kbar, lens, 64, 2)
+
+
+def test_device_tensor_checks():
+    """The binding's argument check: device, contiguity, dtype, shape and size, each refused
+    with a message naming the argument (host tensors stand in; the device test comes first)."""
+    import torch
+    chk = bst.bsattn._device_tensor
+    with pytest.raises(TypeError, match="lens"):
+        chk([1, 2], "lens", None)
+    with pytest.raises(ValueError, match="out must be a device tensor"):
+        chk(torch.zeros(4), "out", None)
+
+
+class _FakeDeviceTensor:
+    """Duck-typed stand-in for a device tensor, to reach the checks after the device test on a
+    machine without a GPU (the binding never hands it to the library in these tests)."""
+
+    def __init__(self, shape, dtype, contiguous=True, device="cuda:0", nbytes=None):
+        import torch
+        self.shape, self.dtype, self._c = tuple(shape), dtype, contiguous
+        self.device = torch.device(device)
+        self.is_cuda = True
+        self._n = 1
+        for d in shape:
+            self._n *= d
+        self._nbytes = nbytes
+
+    def is_contiguous(self):
+        return self._c
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        import torch
+        return torch.empty((), dtype=self.dtype).element_size() if self._nbytes is None else 1
+
+
+def test_device_tensor_checks_after_device(monkeypatch):
+    import torch
+    monkeypatch.setattr(bst.bsattn.torch, "Tensor", _FakeDeviceTensor)
+    chk = bst.bsattn._device_tensor
+    ok = _FakeDeviceTensor((2,), torch.int32)
+    assert chk(ok, "lens", "cuda:0", torch.int32, (2,)) is ok
+    with pytest.raises(ValueError, match="lens is on cuda:1"):
+        chk(_FakeDeviceTensor((2,), torch.int32, device="cuda:1"), "lens", "cuda:0")
+    with pytest.raises(ValueError, match="contiguous"):
+        chk(_FakeDeviceTensor((2,), torch.int32, contiguous=False), "lens", "cuda:0")
+    with pytest.raises(ValueError, match="lens must be torch.int32"):
+        chk(_FakeDeviceTensor((2,), torch.int64), "lens", "cuda:0", torch.int32)
+    with pytest.raises(ValueError, match="shape"):
+        chk(_FakeDeviceTensor((3,), torch.int32), "lens", "cuda:0", torch.int32, (2,))
+    with pytest.raises(ValueError, match="bytes"):
+        chk(_FakeDeviceTensor((100,), torch.uint8, nbytes=100), "workspace", "cuda:0",
+            min_bytes=101)
 
 
 def test_probe_rejects():

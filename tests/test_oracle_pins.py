@@ -62,6 +62,33 @@ def check_e4m3(o=O):
     assert int(nan.sum()) == 2
 
 
+def check_widen(o=O):
+    """widen() per dtype: fp32 and bf16 exactly; fp8 codes times a non-unit descale, against
+    torch's e4m3 decoding (a library routine) and a quantise/widen round trip that must land
+    within e4m3 rounding of the value it started from [R15]."""
+    x32 = rng(11).standard_normal(64).astype(np.float32)
+    assert np.array_equal(o.widen(x32, "f32"), x32.astype(np.float64))
+    bits = rng(12).integers(0, 1 << 15, 64).astype(np.uint16)
+    assert np.array_equal(o.widen(bits, "bf16"),
+                          torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+                          .to(torch.float64).numpy())
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    lib = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for d in (0.37, 1.0 / 448.0, 3.0):
+        assert np.array_equal(o.widen(codes, "fp8", d), lib * d)
+    # round trip: per-tensor amax scaling to 448, e4m3 rounding (torch, nearest even), widen
+    x = torch.from_numpy(rng(13).standard_normal(4096) * 2.5)
+    amax = float(x.abs().max())
+    q8 = (x * (448.0 / amax)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    back = o.widen(q8, "fp8", amax / 448.0)
+    xs = x.numpy()
+    # normal e4m3 values (|x| >= 2^-6 before descaling) carry relative error <= 2^-4; the
+    # subnormal spacing is 2^-9, so the absolute error there is <= 2^-10 (times the descale)
+    tol = np.maximum(2.0 ** -4 * np.abs(xs), 2.0 ** -10 * amax / 448.0) * (1 + 1e-12)
+    assert np.all(np.abs(back - xs) <= tol)
+    assert np.sqrt(np.mean((back - xs) ** 2)) < 0.05 * np.sqrt(np.mean(xs ** 2))
+
+
 def check_pool(o=O):
     B, N, H, D, blk = 2, 24, 3, 5, 4
     x = rng(1).standard_normal((B, N, H, D))
@@ -540,7 +567,7 @@ def check_overlap(o=O):
     assert np.all(top2 == [4, 5]) or np.all(top2 == [5, 6]), top2[0, 0, 0]
 
 
-ALL_CHECKS = [check_bf16_widen, check_e4m3, check_pool, check_scores, check_select_vs_sort,
+ALL_CHECKS = [check_bf16_widen, check_e4m3, check_widen, check_pool, check_scores, check_select_vs_sort,
               check_select_special, check_dense_limit, check_bruteforce, check_ties_and_zero,
               check_invariants, check_gqa, check_batched, check_causal_select,
               check_causal_dense_limit, check_causal_bruteforce, check_pool_max,
@@ -740,6 +767,11 @@ MUTANTS = {
     "group_first_head_only": dict(
         group_scores=lambda S, Hkv: S.reshape(S.shape[0], Hkv, -1, *S.shape[2:])[:, :, 0]),
     "e4m3_bias_8": dict(decode_e4m3=lambda c: O.decode_e4m3(c) / 2),
+    "widen_divides_by_descale": dict(
+        widen=lambda x, dt, d=1.0: O.decode_e4m3(x) / np.float64(d) if dt == "fp8"
+        else O.widen(x, dt, d)),
+    "widen_ignores_descale": dict(
+        widen=lambda x, dt, d=1.0: O.decode_e4m3(x) if dt == "fp8" else O.widen(x, dt, d)),
     "bf16_low_bits": dict(widen_bf16_bits=lambda b: np.asarray(b, dtype=np.uint16).astype(np.float64)),
     "topk_round_not_truncate": dict(topk_count=lambda r, nb: int(round(r * nb))),
     "overlap_short_block_dropped": dict(
