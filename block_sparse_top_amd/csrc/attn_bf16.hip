@@ -36,7 +36,10 @@
 // rescale are needed. The row is first done with m = 0 throughout, only noting whether a step
 // left that range; a flagged row (huge or tiny scores) is done again from the start, and that
 // pass moves the reference to the running max whenever a step leaves the range, rescaling O
-// and l by exp2(m_old - m_new). O and l always share one reference. The normaliser sums the
+// and l by exp2(m_old - m_new). O and l always share one reference. A row whose output sums
+// are not finite after that (values near the top of the bf16 range times weights up to 2^64)
+// is done once more with the upper bound of the range lowered to 1: the reference then
+// follows the running maximum and every weight is at most 1, as in a max-referenced softmax. The normaliser sums the
 // fp32 weights with plain adds (measured: the bf16 dot instruction waits for MFMAs in flight,
 // so it cannot hide under them); the PV product takes the same weights rounded to bf16.
 //
@@ -182,9 +185,15 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
   // read; the waits below are placed by hand (each wave issues exactly DMA transfers per tile
   // and no other vector-memory instruction inside the loop). M0 (the LDS destination) is
   // saved and restored around them.
-  auto dma = [&](const char* src_base, char* dst) {
+  auto dma = [&](const char* src_base_any, char* dst) {
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(lds_void*)dst + wave * C::DMA * 1024);
+    // the source base is the same in every lane; readfirstlane keeps it in scalar registers
+    // where the compiler cannot prove that (the asm operand below must be an SGPR pair)
+    const uint64_t sb = (uint64_t)(uintptr_t)src_base_any;
+    const char* src_base = (const char*)(uintptr_t)(
+        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb) |
+        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32)) << 32));
     uint32_t m0_saved;
     if constexpr (C::DMA == 4) {
       asm volatile(
@@ -249,7 +258,7 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
   // done again from the start with CHECKED = true, which moves the reference to the row max
   // whenever that happens. Taking the check out of the common pass lets the weights, the
   // normaliser and the products of consecutive steps overlap.
-  auto pass = [&](auto checked_tag) -> bool {
+  auto pass = [&](auto checked_tag, float sum_hi) -> bool {
     constexpr bool CHECKED = decltype(checked_tag)::value;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
@@ -362,7 +371,7 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
       bool off_range = false;
 #pragma unroll
       for (int qc = 0; qc < C::QC; ++qc)
-        off_range |= (bsum[qc] > kSumHi) || (lsum[qc] + bsum[qc] < kSumLo);
+        off_range |= (bsum[qc] > sum_hi) || (lsum[qc] + bsum[qc] < kSumLo);
       if (!CHECKED) flagged |= off_range;
       if (CHECKED && __ballot(off_range)) {      // move the reference to the row max
 #pragma unroll
@@ -421,13 +430,42 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
     }
     return flagged;
   };
+  // whether this lane's output sums are all finite (the reference 0 lets weights reach 2^64
+  // per step, so values near the top of the bf16 range can overflow where a max-referenced
+  // softmax would not)
+  auto finite = [&]() -> bool {
+    bool fin = true;
+#pragma unroll
+    for (int qc = 0; qc < C::QC; ++qc) {
+      fin &= __builtin_isfinite(lsum[qc]);
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) fin &= __builtin_isfinite(oacc[dt][qc][r]);
+    }
+    return fin;
+  };
   // the decision is work-group-wide: the waves of a work-group share the tiles and barriers.
   // The causal and overlapping-block variants keep a single checked pass (their extra masking
   // leaves no registers for a second copy of the loop with two waves per SIMD).
-  if constexpr (CAUSAL || OVL)
-    pass(std::true_type{});
-  else if (__syncthreads_or(pass(std::false_type{})))
-    pass(std::true_type{});
+  // A row whose sums are not finite after that is done once more with the upper bound 1:
+  // its reference then follows the running row maximum and no weight exceeds 1.
+  // (one inlined copy of each pass: the checked pass runs in a loop; the decisions are
+  // work-group-wide, made wave-uniform for the compiler with readfirstlane)
+  auto all_or = [](bool x) -> bool {
+    return __builtin_amdgcn_readfirstlane(__syncthreads_or(x) ? 1 : 0) != 0;
+  };
+  float hi = kSumHi;
+  bool again = true;
+  if constexpr (!(CAUSAL || OVL)) {
+    again = all_or(pass(std::false_type{}, kSumHi));
+    if (!again && all_or(!finite())) { again = true; hi = 1.0f; }
+  }
+  while (again) {
+    pass(std::true_type{}, hi);
+    again = hi != 1.0f && all_or(!finite());
+    hi = 1.0f;
+  }
 
   // epilogue: O = O^T / l, bf16, 4 consecutive d per store
 #pragma unroll

@@ -123,6 +123,38 @@ def test_extreme_score_ranges(dtype, case, D, blk):
     say("   max_abs, rel_l2 =", err)
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["plain", "causal"])
+@pytest.mark.parametrize("D,blk", [(64, 64), (128, 128), (64, 128)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_huge_values_do_not_overflow(dtype, D, blk, causal):
+    """Values near the top of the float range with scores whose weights stay inside the
+    plain pass's range (|scale*q.k| ~ 46, weights ~ 2^46): sum(p * v) overflows fp32 unless the
+    weights are referenced to the row maximum. The output must be finite and match the oracle
+    (the bf16 kernel redoes such rows with weights <= 1)."""
+    say(f"[huge values] {dtype} D={D} block={blk} causal={causal}")
+    B, N, H, topk = 1, 1024, 2, 6
+    g = torch.Generator().manual_seed(47)
+    u = torch.randn(B, 1, H, D, generator=g)
+    a = 46.0 * math.sqrt(D) / (1.4426950408889634 * float((u * u).sum(-1).mean()))
+    q = a * u + 0.3 * torch.randn(B, N, H, D, generator=g)
+    k = u + 0.3 * torch.randn(B, N, H, D, generator=g)
+    v = 1e30 * torch.randn(B, N, H, D, generator=g)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q, k, v = (x.to(tdt).to(DEV) for x in (q, k, v))
+    idx = bst.select(q, k, blk, topk, causal=causal)
+    out = bst.forward(q, k, v, idx, causal=causal)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all(), "output overflowed"
+    qo, ko, vo = to_f64(q), to_f64(k), to_f64(v)
+    ref = O.attend(qo, ko, vo, idx.cpu().numpy(), blk, 1 / math.sqrt(D), causal=causal)
+    # the scores themselves are O(300): fp32 dot products carry ~1e-5 relative error there,
+    # which moves the near one-hot weights; bounds scaled by the output magnitude
+    err = check_out(got, ref, dtype, abs_scale=float(np.abs(ref).max()),
+                    rel_scale=10.0 if dtype == "f32" else 1.0)
+    say("   max_abs/max|ref|, rel_l2 =", err[0] / float(np.abs(ref).max()), err[1])
+
+
 @pytest.mark.parametrize("D,blk", [(64, 64), (128, 128)])
 def test_flagged_and_plain_rows_in_one_launch(D, blk):
     """Rows whose weights leave the plain pass's range sit next to rows that do not, in one
