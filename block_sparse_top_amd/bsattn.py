@@ -66,6 +66,11 @@ def lib() -> ctypes.CDLL:
     L.bsattn_forward_ex.restype = i32
     L.bsattn_forward_ex.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, u32, i32, vp, vp, vp,
                                     vp, ctypes.c_float, ctypes.POINTER(ctypes.c_float), vp, vp, vp]
+    L.bsattn_select_noalloc_max_bytes.restype = sz
+    L.bsattn_select_noalloc_max_bytes.argtypes = []
+    L.bsattn_select_noalloc.restype = i32
+    L.bsattn_select_noalloc.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32, u32, i32,
+                                        ctypes.c_uint64, i32, vp, vp, vp, vp]
     L.bsattn_key_blocks.restype = i64
     L.bsattn_key_blocks.argtypes = [i64, i32, i32]
     # achievable-peak probes (include/bsattn_probe.h)

@@ -6,6 +6,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/bsattn.h"
 #include "../../include/bsattn_probe.h"
 #include "launch.h"
@@ -95,9 +97,68 @@ size_t scores_bytes(int64_t B, int64_t N, int Hq, int block) {
 
 }  // namespace
 
+// ---- device scratch of bsattn_select_noalloc: a file-scope array of fixed size on every GPU
+// the library runs on, held until the process ends. Host code never passes `scratch` itself
+// (its host-side name is no device address): the address comes from hipGetSymbolAddress,
+// once per device, and is kept in g_scratch_ptr.
+namespace bsattn {
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+}  // namespace bsattn
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the scratch array on the current device (looked up on first use there).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BSATTN_E_UNSUPPORTED, "device %d (the static scratch serves devices 0..%d)", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(bsattn::scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p || ((uintptr_t)p & 255u))
+      return fail(BSATTN_E_HIP, "scratch address %p is not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BSATTN_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int bsattn_abi_version(void) { return BSATTN_ABI_VERSION; }
+
+size_t bsattn_select_noalloc_max_bytes(void) { return bsattn::kNoAllocScratchBytes; }
+
+int bsattn_select_noalloc(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
+                          int topk, unsigned flags, int nrand, uint64_t seed, int key_stride,
+                          const void* q, const void* k, int32_t* idx, void* stream) {
+  int st = check_shape(dtype, B, N, Hq, Hkv, D, block, topk, key_stride);
+  if (st != BSATTN_OK) return st;
+  const size_t need = bsattn_select_workspace_bytes_ex(B, N, Hq, Hkv, D, block, key_stride);
+  if (need > bsattn::kNoAllocScratchBytes)
+    return fail(BSATTN_E_WORKSPACE,
+                "selection needs %zu bytes of scratch, the static scratch holds %zu "
+                "(use bsattn_select_ex with a workspace)",
+                need, bsattn::kNoAllocScratchBytes);
+  if (B == 0 || N == 0)
+    return bsattn_select_ex(dtype, B, N, Hq, Hkv, D, block, topk, flags, nrand, seed, key_stride,
+                            q, k, idx, nullptr, 0, stream);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != BSATTN_OK) return st;
+  return bsattn_select_ex(dtype, B, N, Hq, Hkv, D, block, topk, flags, nrand, seed, key_stride,
+                          q, k, idx, ws, bsattn::kNoAllocScratchBytes, stream);
+}
 
 const char* bsattn_status_str(int status) {
   switch (status) {

@@ -161,6 +161,23 @@ int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, in
                      size_t workspace_bytes, void* stream);
 
 /*
+ * bsattn_select_ex without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The pooled blocks (and, for nb > 1024, the score matrix) go to a static
+ * device array of bsattn_select_noalloc_max_bytes() bytes (64 MiB) that the library holds on
+ * every GPU it runs on until the process ends; its address is looked up once per device.
+ * The call allocates nothing. Arguments, layouts and errors as bsattn_select_ex; a selection
+ * whose workspace (bsattn_select_workspace_bytes_ex) exceeds the static size returns
+ * BSATTN_E_WORKSPACE before any HIP call. Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (other streams, other threads) race; calls in one
+ * stream are ordered. Nothing in the array needs to start at zero.
+ */
+size_t bsattn_select_noalloc_max_bytes(void);
+int bsattn_select_noalloc(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, int block,
+                          int topk, unsigned flags, int nrand, uint64_t seed, int key_stride,
+                          const void* q, const void* k, int32_t* idx, void* stream);
+
+/*
  * Gathered-block attention (step 3 of "SparseFormer 注意力实现"; MSA page §2.1 with a
  * block mask, §2.2 second stage).
  *   For query token t of block i and query head h, with g = h / (Hq / Hkv):
