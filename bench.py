@@ -75,11 +75,36 @@ def traffic_per_launch():
         return None
 
 
-def achievable_peaks(L, device, stream, reps=3):
+def probe_lib():
+    """libbsattn_probe.so (include/bsattn_probe.h), the achievable-peak probes: a library of
+    their own, separate from the method's libbsattn.so."""
+    import ctypes
+    path = os.path.join(ROOT, "block_sparse_top_amd", "libbsattn_probe.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with block_sparse_top_amd.build.build()")
+    L = ctypes.CDLL(path)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    L.bsattn_probe_last_error.restype = ctypes.c_char_p
+    L.bsattn_probe_last_error.argtypes = []
+    L.bsattn_probe_sink_floats.restype = sz
+    L.bsattn_probe_sink_floats.argtypes = [i32]
+    L.bsattn_probe_mfma_bf16.restype = i32
+    L.bsattn_probe_mfma_bf16.argtypes = [i64, i32, vp, ctypes.POINTER(ctypes.c_double), vp]
+    L.bsattn_probe_mfma_fp8.restype = i32
+    L.bsattn_probe_mfma_fp8.argtypes = [i64, i32, vp, ctypes.POINTER(ctypes.c_double), vp]
+    L.bsattn_probe_read.restype = i32
+    L.bsattn_probe_read.argtypes = [vp, sz, i32, vp, vp]
+    L.bsattn_probe_copy.restype = i32
+    L.bsattn_probe_copy.argtypes = [vp, vp, sz, i32, vp]
+    return L
+
+
+def achievable_peaks(device, stream, reps=3):
     """What the chip sustains (include/bsattn_probe.h): dense bf16 MFMA TFLOP/s, HBM read GB/s,
     HBM copy GB/s (read + written bytes), each the best of `reps` HIP-event-timed launches."""
     import ctypes
     import torch
+    L = probe_lib()
     groups = 2048                                   # 8 work-groups of 4 waves per CU
     sink = torch.empty(L.bsattn_probe_sink_floats(groups), dtype=torch.float32, device=device)
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -119,18 +144,31 @@ def achievable_peaks(L, device, stream, reps=3):
             "hbm_read_gbs": round(rd, 1), "hbm_copy_gbs": round(cp, 1)}
 
 
-def cpu_baseline(w, q, k, v, ds, max_batches, budget_s=10.0, causal=False, pooling="mean",
+def host_cores():
+    """Host cores the CPU leg may use: the process's affinity mask, capped by OMP_NUM_THREADS
+    where the environment sets one (the box's share of a shared host)."""
+    n = len(os.sched_getaffinity(0))
+    how = f"len(os.sched_getaffinity(0)) = {n}"
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and 0 < int(env) < n:
+        how += f", capped by OMP_NUM_THREADS = {env}"
+        n = int(env)
+    return n, how
+
+
+def cpu_baseline(w, q, k, v, ds, max_batches, budget_s=15.0, causal=False, pooling="mean",
                  group=False, key_stride=0):
     """The fp64 oracle, as it stands, on batch elements 0, 1, ... of the workload until
     `budget_s` seconds of CPU work are done (at least one, at most `max_batches`)."""
     import numpy as np
     import torch
     import oracle.bsattn_oracle as O
+    threads, how = host_cores()
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=threads)
     except Exception:  # pragma: no cover
-        threads = 1
+        limiter = None
 
     def host(t):
         c = t.detach().cpu()
@@ -157,8 +195,10 @@ def cpu_baseline(w, q, k, v, ds, max_batches, budget_s=10.0, causal=False, pooli
             O.attend_batched(qo, ko, vo, idx, w.block, 1.0 / math.sqrt(w.D), causal=causal)
         dt_s += time.perf_counter() - t0
         batches += 1
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {"value": batches * w.N / dt_s, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "cores_from": how, "kind": "oracle",
             "sample": f"{batches} of {w.B} batch elements (all heads, all query blocks), "
                       f"whole path in fp64 numpy, {dt_s:.1f} s"}
 
@@ -271,7 +311,7 @@ def bench_decode(args):
                      "algorithmic_bytes_per_step": total},
         "decode_ms": round(ms, 4),
     }
-    ach = achievable_peaks(L, q.device, stream)
+    ach = achievable_peaks(q.device, stream)
     rec["achievable"] = ach
     rec["roofline"]["achievable_peak"] = ach["hbm_read_gbs"]
     rec["roofline"]["achievable_frac"] = round(rec["roofline"]["achieved"] / ach["hbm_read_gbs"], 4)
@@ -337,6 +377,8 @@ def main():
         do_forward()
     torch.cuda.synchronize()
 
+    # the timed region: exactly `steps` steps back to back; HIP events on the library's
+    # stream around each call give the per-launch durations the roofline uses
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -348,11 +390,48 @@ def main():
         e[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sel_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
-    fwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
+    sel_all = [e[0].elapsed_time(e[1]) for e in evs]
+    fwd_all = [e[1].elapsed_time(e[2]) for e in evs]
+    sel_ms = sum(sel_all) / len(evs)
+    fwd_ms = sum(fwd_all) / len(evs)
     ms_per_step = wall * 1e3 / args.steps
     tokens = w.B * w.N
     value = tokens / (ms_per_step / 1e3)
+
+    # The survey's timing protocol, after the timed region (reported beside it): per call,
+    # repeats of up to 50 launches, the median over 5 repeats; each selection launch follows a
+    # 512 MB write that evicts the 256 MB MALL (the write is outside the events).
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def protocol(call, est_ms, flush_first):
+        n = max(1, min(50, int(round(500.0 / max(est_ms, 1e-3)))))
+        reps = []
+        for r in range(5):
+            if flush_first:
+                tot = 0.0
+                for _ in range(n):
+                    flush.fill_(r & 0xFF)
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    call()
+                    b.record(stream)
+                    b.synchronize()
+                    tot += a.elapsed_time(b)
+                reps.append(tot / n)
+            else:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(n):
+                    call()
+                b.record(stream)
+                b.synchronize()
+                reps.append(a.elapsed_time(b) / n)
+        reps.sort()
+        return {"median_ms": round(reps[2], 4), "repeats_ms": [round(x, 4) for x in reps],
+                "launches_per_repeat": n}
+    proto = {"select_after_mall_flush": protocol(do_select, sel_ms, True),
+             "forward": protocol(do_forward, fwd_ms, False)}
+    del flush
 
     # QK^T + PV over every computed key block (causal: query block i computes min(topk, i+1)
     # blocks, its own one in full although half of it is masked)
@@ -369,11 +448,21 @@ def main():
     achieved = flops / (fwd_ms / 1e3) / 1e12
     peak = PEAK[w.dtype]
     ebytes = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
-    sel_bytes = (w.B * w.N * (w.Hq + w.Hkv) * w.D * ebytes            # read q, k
-                 + 2 * 4 * w.B * (w.nb * w.Hq + nkb * w.Hkv) * w.D    # pooled write + read
-                 + 4 * w.B * w.Hq * w.nb * topk)                      # idx write
-    if w.nb > 1024:                                                   # score matrix write + read
-        sel_bytes += 2 * 4 * w.B * w.Hq * w.nb * w.nb
+    # The selection's algorithmic bytes as the survey counts them: q and k read once, the
+    # pooled blocks written once, idx written; where the score matrix goes through HBM
+    # (more than 1024 blocks) also its write and read and the pooled blocks' read by the
+    # score product. ("moved": what the kernels move on top of that, e.g. the fused kernel
+    # re-reading the pooled keys.)
+    sel_heads = w.Hkv if args.group else w.Hq
+    sel_bytes = (w.B * w.N * (w.Hq + w.Hkv) * w.D * ebytes             # read q, k
+                 + 4 * w.B * (w.nb * w.Hq + nkb * w.Hkv) * w.D         # pooled writes
+                 + 4 * w.B * w.Hq * w.nb * topk)                       # idx write
+    moved = sel_bytes + 4 * w.B * nkb * w.Hkv * w.D                    # pooled keys read back
+    if w.nb > 1024:
+        extra = (2 * 4 * w.B * sel_heads * w.nb * w.nb                 # score matrix write + read
+                 + 4 * w.B * (w.nb * w.Hq + w.nb * w.Hkv) * w.D)       # pooled rows read
+        sel_bytes += extra
+        moved = sel_bytes + (4 * w.B * w.nb * w.Hq * w.D if args.group else 0)
     plain = not (args.causal or args.group or args.pooling == "max" or ks != w.block)
     tr = traffic_per_launch() if plain and w.name == "sparseformer_n8192_bf16" else None
     rec = {
@@ -393,11 +482,18 @@ def main():
                      "traffic": tr, "kernel": f"attn_{w.dtype}_kernel",
                      "algorithmic_flop_per_launch": flops},
         "select_ms": round(sel_ms, 4), "forward_ms": round(fwd_ms, 4),
+        "timed_region": {"select_ms_avg": round(sel_ms, 4), "forward_ms_avg": round(fwd_ms, 4),
+                         "forward_ms_min": round(min(fwd_all), 4),
+                         "forward_ms_max": round(max(fwd_all), 4)},
         "select_hbm_frac": round(sel_bytes / (sel_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-        "select_algorithmic_bytes": sel_bytes,
+        "select_algorithmic_bytes": sel_bytes, "select_moved_bytes": moved,
+        "protocol": proto,
+        "select_hbm_frac_after_flush": round(
+            sel_bytes / (proto["select_after_mall_flush"]["median_ms"] / 1e3) / 1e9
+            / HBM_PEAK_GBS, 4),
     }
     if w.dtype in ("bf16", "fp8"):
-        ach = achievable_peaks(L, dev, stream)
+        ach = achievable_peaks(dev, stream)
         rec["achievable"] = ach
         apeak = ach["mfma_bf16_tflops" if w.dtype == "bf16" else "mfma_fp8_tflops"]
         rec["roofline"]["achievable_peak"] = apeak

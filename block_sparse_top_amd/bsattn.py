@@ -73,17 +73,6 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_uint64, i32, vp, vp, vp, vp]
     L.bsattn_key_blocks.restype = i64
     L.bsattn_key_blocks.argtypes = [i64, i32, i32]
-    # achievable-peak probes (include/bsattn_probe.h)
-    L.bsattn_probe_sink_floats.restype = sz
-    L.bsattn_probe_sink_floats.argtypes = [i32]
-    L.bsattn_probe_mfma_bf16.restype = i32
-    L.bsattn_probe_mfma_bf16.argtypes = [i64, i32, vp, ctypes.POINTER(ctypes.c_double), vp]
-    L.bsattn_probe_mfma_fp8.restype = i32
-    L.bsattn_probe_mfma_fp8.argtypes = [i64, i32, vp, ctypes.POINTER(ctypes.c_double), vp]
-    L.bsattn_probe_read.restype = i32
-    L.bsattn_probe_read.argtypes = [vp, sz, i32, vp, vp]
-    L.bsattn_probe_copy.restype = i32
-    L.bsattn_probe_copy.argtypes = [vp, vp, sz, i32, vp]
     L.bsattn_select_workspace_bytes_ex.restype = sz
     L.bsattn_select_workspace_bytes_ex.argtypes = [i64, i64, i32, i32, i32, i32, i32]
     L.bsattn_backward_workspace_bytes.restype = sz

@@ -19,7 +19,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbsattn.so")
 SOURCES = ["api.hip", "pool.hip", "select.hip", "select_large.hip", "attn_bf16.hip", "attn_f32.hip", "attn_fp8.hip",
-           "validate.hip", "attn_bwd.hip", "decode.hip", "probe.hip"]
+           "validate.hip", "attn_bwd.hip", "decode.hip"]
+# achievable-peak probes (measurement support, include/bsattn_probe.h): a library of their own
+PROBE_LIB = os.path.join(PKG, "libbsattn_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [
@@ -49,18 +52,24 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, list(extra_flags)), srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

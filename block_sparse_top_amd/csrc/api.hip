@@ -9,7 +9,6 @@
 #include <mutex>
 
 #include "../../include/bsattn.h"
-#include "../../include/bsattn_probe.h"
 #include "launch.h"
 
 namespace {
@@ -319,7 +318,9 @@ int bsattn_forward_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, i
     unsigned int bad = 0;
     const int64_t nb = N / block;
     st = hip_status(
-        bsattn::validate_idx(B * Hq * nb, topk, (int)nb, (int)nkb, idx, causal, s, &bad),
+        // the counter goes to the first 4 bytes of out, which the attention overwrites
+        bsattn::validate_idx(B * Hq * nb, topk, (int)nb, (int)nkb, idx, causal,
+                             (unsigned int*)out, s, &bad),
         "idx validation");
     if (st != BSATTN_OK) return st;
     if (bad)
@@ -493,48 +494,6 @@ int bsattn_decode_ex(int dtype, int64_t B, int64_t Lmax, int Hq, int Hkv, int D,
                                           kbar, lens, scale, out, idx, workspace,
                                           (hipStream_t)stream),
                     "decode launch");
-}
-
-// ---- achievable-peak probes (include/bsattn_probe.h)
-
-size_t bsattn_probe_sink_floats(int groups) { return groups > 0 ? (size_t)groups * 256 : 0; }
-
-int bsattn_probe_mfma_bf16(int64_t iters, int groups, float* sink, double* flops, void* stream) {
-  if (iters < 1 || iters > ((int64_t)1 << 30) || groups < 1 || groups > 65535)
-    return fail(BSATTN_E_INVALID, "iters in [1, 2^30] and groups in [1, 65535] required");
-  if (!sink || ((uintptr_t)sink & 3u)) return fail(BSATTN_E_INVALID, "sink null or unaligned");
-  if (flops) *flops = 2.0 * 32 * 32 * 16 * 8 * 4 * (double)groups * (double)iters;
-  return hip_status(bsattn::launch_probe_mfma_bf16(iters, groups, sink, (hipStream_t)stream),
-                    "mfma probe launch");
-}
-
-int bsattn_probe_mfma_fp8(int64_t iters, int groups, float* sink, double* flops, void* stream) {
-  if (iters < 1 || iters > ((int64_t)1 << 30) || groups < 1 || groups > 65535)
-    return fail(BSATTN_E_INVALID, "iters in [1, 2^30] and groups in [1, 65535] required");
-  if (!sink || ((uintptr_t)sink & 3u)) return fail(BSATTN_E_INVALID, "sink null or unaligned");
-  if (flops) *flops = 2.0 * 32 * 32 * 64 * 8 * 4 * (double)groups * (double)iters;
-  return hip_status(bsattn::launch_probe_mfma_fp8(iters, groups, sink, (hipStream_t)stream),
-                    "mfma fp8 probe launch");
-}
-
-int bsattn_probe_read(const void* src, size_t bytes, int groups, float* sink, void* stream) {
-  if (!src || !sink || !aligned16(src) || ((uintptr_t)sink & 3u) || bytes == 0 || bytes % 16 ||
-      groups < 1 || groups > 65535)
-    return fail(BSATTN_E_INVALID, "read probe: bad pointer, size or group count");
-  return hip_status(bsattn::launch_probe_read(src, (int64_t)(bytes / 16), groups, sink,
-                                              (hipStream_t)stream),
-                    "read probe launch");
-}
-
-int bsattn_probe_copy(const void* src, void* dst, size_t bytes, int groups, void* stream) {
-  if (!src || !dst || !aligned16(src) || !aligned16(dst) || bytes == 0 || bytes % 16 ||
-      groups < 1 || groups > 65535)
-    return fail(BSATTN_E_INVALID, "copy probe: bad pointer, size or group count");
-  const char *s0 = (const char*)src, *d0 = (const char*)dst;
-  if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(BSATTN_E_INVALID, "copy probe: overlap");
-  return hip_status(bsattn::launch_probe_copy(src, dst, (int64_t)(bytes / 16), groups,
-                                              (hipStream_t)stream),
-                    "copy probe launch");
 }
 
 }  // extern "C"

@@ -100,17 +100,10 @@ hipError_t launch_decode(int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int bl
 
 // Checks every idx row (topk values, strictly ascending, in [0, nkb); causal: the first
 // min(topk, i+1) values strictly ascending in [0, i] for query block i = row mod nb, the rest
-// -1); waits for the stream and returns the number of failing rows in *bad_rows. Uses one
-// device-global counter per device: concurrent validations on one device race.
+// -1); waits for the stream and returns the number of failing rows in *bad_rows. counter:
+// 4 bytes of device memory the call may overwrite (zeroed first, then counted into).
 hipError_t validate_idx(int64_t rows, int topk, int nb, int nkb, const int32_t* idx,
-                        bool causal, hipStream_t stream, unsigned int* bad_rows);
-
-// Achievable-peak probes (measurement support; no part of the method).
-hipError_t launch_probe_mfma_bf16(int64_t iters, int groups, float* sink, hipStream_t stream);
-hipError_t launch_probe_mfma_fp8(int64_t iters, int groups, float* sink, hipStream_t stream);
-hipError_t launch_probe_read(const void* src, int64_t n16, int groups, float* sink,
-                             hipStream_t stream);
-hipError_t launch_probe_copy(const void* src, void* dst, int64_t n16, int groups,
-                             hipStream_t stream);
+                        bool causal, unsigned int* counter, hipStream_t stream,
+                        unsigned int* bad_rows);
 
 }  // namespace bsattn

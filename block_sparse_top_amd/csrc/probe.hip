@@ -1,5 +1,7 @@
 // Achievable-peak probes (measurement support, declared in include/bsattn_probe.h): what this
 // chip sustains for the two resources the path is bound by, to set next to the vendor peaks.
+// Built into its own library, libbsattn_probe.so, which only the benchmark loads; the
+// method's library (libbsattn.so) does not contain it.
 //
 // mfma_bf16_kernel: every wave issues chains of independent v_mfma_f32_32x32x16_bf16 (eight
 // accumulators, so that each MFMA waits on nothing) for `iters` rounds; the operands stay in
@@ -10,8 +12,11 @@
 // at the end so that the work is not optimised away. mfma_fp8_kernel: the same on the fp8 MFMA.
 // read_kernel: a sum of a large buffer with 16-byte nontemporal loads (HBM read rate);
 // copy_kernel: 16-byte loads and stores (read + write rate).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/bsattn_probe.h"
 #include "common.h"
-#include "launch.h"
 
 namespace bsattn {
 namespace {
@@ -132,26 +137,94 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
 
 }  // namespace
 
-hipError_t launch_probe_mfma_bf16(int64_t iters, int groups, float* sink, hipStream_t stream) {
+static hipError_t launch_probe_mfma_bf16(int64_t iters, int groups, float* sink, hipStream_t stream) {
   mfma_bf16_kernel<<<groups, 256, 0, stream>>>(iters, sink);
   return hipGetLastError();
 }
 
-hipError_t launch_probe_mfma_fp8(int64_t iters, int groups, float* sink, hipStream_t stream) {
+static hipError_t launch_probe_mfma_fp8(int64_t iters, int groups, float* sink, hipStream_t stream) {
   mfma_fp8_kernel<<<groups, 256, 0, stream>>>(iters, sink);
   return hipGetLastError();
 }
 
-hipError_t launch_probe_read(const void* src, int64_t n16, int groups, float* sink,
+static hipError_t launch_probe_read(const void* src, int64_t n16, int groups, float* sink,
                              hipStream_t stream) {
   read_kernel<<<groups, 256, 0, stream>>>((const u32x4*)src, n16, sink);
   return hipGetLastError();
 }
 
-hipError_t launch_probe_copy(const void* src, void* dst, int64_t n16, int groups,
+static hipError_t launch_probe_copy(const void* src, void* dst, int64_t n16, int groups,
                              hipStream_t stream) {
   copy_kernel<<<groups, 256, 0, stream>>>((const u32x4*)src, (u32x4*)dst, n16);
   return hipGetLastError();
 }
 
 }  // namespace bsattn
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+int fail(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return 1;   // BSATTN_E_INVALID
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return 0;
+  snprintf(g_err, sizeof(g_err), "%s: %s", what, hipGetErrorString(e));
+  return 4;   // BSATTN_E_HIP
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* bsattn_probe_last_error(void) { return g_err; }
+
+size_t bsattn_probe_sink_floats(int groups) { return groups > 0 ? (size_t)groups * 256 : 0; }
+
+int bsattn_probe_mfma_bf16(int64_t iters, int groups, float* sink, double* flops, void* stream) {
+  if (iters < 1 || iters > ((int64_t)1 << 30) || groups < 1 || groups > 65535)
+    return fail("iters in [1, 2^30] and groups in [1, 65535] required");
+  if (!sink || ((uintptr_t)sink & 3u)) return fail("sink null or unaligned");
+  if (flops) *flops = 2.0 * 32 * 32 * 16 * 8 * 4 * (double)groups * (double)iters;
+  return hip_status(bsattn::launch_probe_mfma_bf16(iters, groups, sink, (hipStream_t)stream),
+                    "mfma probe launch");
+}
+
+int bsattn_probe_mfma_fp8(int64_t iters, int groups, float* sink, double* flops, void* stream) {
+  if (iters < 1 || iters > ((int64_t)1 << 30) || groups < 1 || groups > 65535)
+    return fail("iters in [1, 2^30] and groups in [1, 65535] required");
+  if (!sink || ((uintptr_t)sink & 3u)) return fail("sink null or unaligned");
+  if (flops) *flops = 2.0 * 32 * 32 * 64 * 8 * 4 * (double)groups * (double)iters;
+  return hip_status(bsattn::launch_probe_mfma_fp8(iters, groups, sink, (hipStream_t)stream),
+                    "mfma fp8 probe launch");
+}
+
+int bsattn_probe_read(const void* src, size_t bytes, int groups, float* sink, void* stream) {
+  if (!src || !sink || !aligned16(src) || ((uintptr_t)sink & 3u) || bytes == 0 || bytes % 16 ||
+      groups < 1 || groups > 65535)
+    return fail("read probe: bad pointer, size or group count");
+  return hip_status(bsattn::launch_probe_read(src, (int64_t)(bytes / 16), groups, sink,
+                                              (hipStream_t)stream),
+                    "read probe launch");
+}
+
+int bsattn_probe_copy(const void* src, void* dst, size_t bytes, int groups, void* stream) {
+  if (!src || !dst || !aligned16(src) || !aligned16(dst) || bytes == 0 || bytes % 16 ||
+      groups < 1 || groups > 65535)
+    return fail("copy probe: bad pointer, size or group count");
+  const char *s0 = (const char*)src, *d0 = (const char*)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return fail("copy probe: overlap");
+  return hip_status(bsattn::launch_probe_copy(src, dst, (int64_t)(bytes / 16), groups,
+                                              (hipStream_t)stream),
+                    "copy probe launch");
+}
+
+}  // extern "C"

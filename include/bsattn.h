@@ -18,7 +18,8 @@
  *   - GQA: query head h reads KV head h / (Hq / Hkv); selection is per query head.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null stream),
  *     never synchronises (except the optional idx validation of bsattn_forward), never
- *     allocates or frees device memory, and keeps no state between calls. Argument checks
+ *     allocates or frees device memory, and keeps no state between calls (the static
+ *     scratch of bsattn_select_noalloc aside). Argument checks
  *     run on the host before any launch.
  *   - Errors are returned, never thrown or printed: the return value is a bsattn_status;
  *     bsattn_last_error() gives a text detail of the last failure on the calling thread.
@@ -41,7 +42,7 @@
 extern "C" {
 #endif
 
-#define BSATTN_ABI_VERSION 4
+#define BSATTN_ABI_VERSION 5
 
 typedef enum {
   BSATTN_OK = 0,
@@ -79,7 +80,9 @@ typedef enum {
  * BSATTN_* option flags, the two _ex entry points (with the optional log-sum-exp output) and
  * the backward; version 3 added the key_stride argument of the _ex entry points (overlapping
  * key blocks), bsattn_key_blocks and bsattn_select_workspace_bytes_ex; version 4 added
- * bsattn_decode_ex (group-shared decode selection). Version-1 calls are unchanged. */
+ * bsattn_decode_ex (group-shared decode selection); version 5 added bsattn_select_noalloc and
+ * moved the measurement probes to their own library (include/bsattn_probe.h). Version-1
+ * calls are unchanged. */
 int bsattn_abi_version(void);
 
 /* Static English text of a status code; never NULL. */
@@ -194,8 +197,9 @@ int bsattn_select_noalloc(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int 
  *                bounds: its output rows are set to NaN. Duplicate entries count twice.
  *                With BSATTN_VALIDATE=1 in the environment every row is first checked on
  *                the GPU (strictly ascending, in [0, nb)); a failing row makes the call
- *                return BSATTN_E_INVALID before the attention launch. This mode waits for
- *                the stream, and concurrent validating calls on one device race.
+ *                return BSATTN_E_INVALID before the attention launch (the first 4 bytes of
+ *                out then hold the check's row count, the rest of out is untouched). This
+ *                mode waits for the stream.
  *   scale        finite softmax scale (the page uses 1/sqrt(D)).
  *   descale_qkv  host pointer to 3 floats (q, k, v per-tensor descales) for fp8; ignored
  *                (may be NULL) for other dtypes. Must be finite and > 0.

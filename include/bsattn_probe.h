@@ -1,12 +1,14 @@
 /*
- * bsattn_probe.h — achievable-peak probes of libbsattn.so (measurement support).
+ * bsattn_probe.h — achievable-peak probes (measurement support), exported by their own
+ * library libbsattn_probe.so, which the benchmark loads; libbsattn.so does not contain them.
  *
  * The roofline of the path compares each kernel with the vendor peaks of the chip (dense bf16
  * MFMA, HBM bandwidth). These probes measure what the chip sustains for the same resources
  * under load (clock throttling under sustained matrix work, memory-system efficiency), so
  * that a kernel can also be set against an achievable ceiling. They compute nothing of the
  * method. The caller times the launches (HIP events on `stream`) and owns every buffer.
- * Status codes and bsattn_last_error as in bsattn.h.
+ * Status codes as in bsattn.h (0 ok, 1 invalid argument, 4 HIP error); the text of the last
+ * failure on the calling thread comes from bsattn_probe_last_error().
  */
 #ifndef BSATTN_PROBE_H
 #define BSATTN_PROBE_H
@@ -17,6 +19,9 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Text detail of the last failing probe call on this thread ("" if none). */
+const char* bsattn_probe_last_error(void);
 
 /* Sink size (floats) the probes write: one float per launched thread. */
 size_t bsattn_probe_sink_floats(int groups);

@@ -74,6 +74,51 @@ def check_idx(gpu_idx: np.ndarray, S: np.ndarray, k: int):
             "ambiguous_differing": int((~exact_ok[amb]).sum()) if amb.size else 0}
 
 
+def check_random_rows(rows_g: np.ndarray, rows_s: np.ndarray, topk: int, nrand: int, seed: int,
+                      rows=None, max_sets: int = 512):
+    """Random places [R27] on rows whose top topk - nrand part is not clear under the oracle's
+    scores: some split of the GPU row into a top part T and drawn blocks must be right, i.e.
+    T (topk - nrand blocks) is a valid top under the index rule's tolerance, and the drawn
+    blocks are exactly the oracle's draws given T (the draws depend only on the seed, the row
+    number and the blocks outside T). rows_g [R, topk] GPU rows, rows_s [R, nb] oracle scores,
+    rows: the row numbers (positions in C order of the whole selection) to check. Returns the
+    number of rows checked."""
+    import itertools
+    nb = rows_s.shape[1]
+    kt = topk - nrand
+    rows = range(rows_g.shape[0]) if rows is None else rows
+    n = 0
+    for r in rows:
+        g, sc = rows_g[r].astype(np.int64), rows_s[r]
+        srt = -np.sort(-sc)
+        s_k = srt[kt - 1] if kt > 0 else np.inf
+        s_k1 = srt[kt] if kt < nb else -np.inf
+        mag = float(np.abs(sc).max())
+        tol = GAP_REL * max(abs(s_k) if np.isfinite(s_k) else 0.0,
+                            abs(s_k1) if np.isfinite(s_k1) else 0.0, mag)
+        sure = [j for j in g if sc[j] > s_k + tol]
+        band = [j for j in g if abs(sc[j] - s_k) <= tol]
+        need = kt - len(sure)
+        assert 0 <= need <= len(band), f"row {r}: no top part of {kt} blocks in the GPU row"
+        ok = False
+        for m, extra in enumerate(itertools.combinations(band, need)):
+            assert m < max_sets, f"row {r}: too many candidate top parts"
+            top = np.array(sure + list(extra), dtype=np.int64)
+            inside = np.zeros(nb, dtype=bool)
+            inside[top] = True
+            if kt and (~inside).any() and sc[inside].min() < sc[~inside].max() - tol:
+                continue
+            tweak = sc.copy()
+            tweak[inside] = np.inf                    # the oracle's top part is then exactly T
+            want = O.select_topk_random(np.tile(tweak, (r + 1, 1)), topk, nrand, seed)[r]
+            if np.array_equal(np.sort(want), np.sort(g)):
+                ok = True
+                break
+        assert ok, f"row {r}: the drawn blocks are not the draws of any valid top part"
+        n += 1
+    return n
+
+
 def check_idx_causal(gpu_idx: np.ndarray, S: np.ndarray, k: int):
     """Causal rows [R20]: row i holds min(k, i+1) ascending blocks, the last being i itself,
     then -1; its first min(k, i+1) - 1 entries must pass the index rule above against the
@@ -121,6 +166,24 @@ def fp8_abs_bound(vmax: float, n_keys: int, ref: np.ndarray) -> float:
     """Worst-case max-abs error of the fp8 path (weights rounded to e4m3, see above)."""
     rmax = float(np.max(np.abs(ref))) if ref.size else 0.0
     return (2.0 ** -4 + n_keys * 2.0 ** -16) * vmax + 2.0 ** -8 * rmax
+
+
+def fp8_figures(gpu_out: np.ndarray, ref: np.ndarray, vmax: float, n_keys: int) -> dict:
+    """What an fp8 comparison achieved next to the rule's bounds: max-abs and its bound,
+    relative L2 over the tensor and its bound, the worst query row's relative L2 and its
+    bound (printed by the fp8 tests, so that the margin of the rule is on record)."""
+    max_abs, rel_l2 = out_errors(gpu_out, ref)
+    d = (gpu_out.astype(np.float64) - ref).reshape(-1, ref.shape[-1])
+    r = ref.reshape(-1, ref.shape[-1])
+    floor = 1e-3 * float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    row_rel = np.linalg.norm(d, axis=1) / np.maximum(np.linalg.norm(r, axis=1), floor) \
+        if r.size else np.zeros(1)
+    return {"max_abs": float(f"{max_abs:.3e}"),
+            "max_abs_bound": float(f"{fp8_abs_bound(vmax, n_keys, ref):.3e}"),
+            "max_abs_over_ref_rms": float(f"{max_abs / max(float(np.sqrt(np.mean(r * r))), 1e-300):.3e}"),
+            "rel_l2": float(f"{rel_l2:.3e}"), "rel_l2_bound": TOL["fp8"][1],
+            "worst_row_rel_l2": float(f"{float(np.max(row_rel)):.3e}"),
+            "worst_row_bound": FP8_ROW_REL}
 
 
 def check_out(gpu_out: np.ndarray, ref: np.ndarray, dt: str, abs_scale: float = 1.0,

@@ -17,9 +17,11 @@ HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.j
 FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call below fails first
 
 
-def declared_functions():
+def declared_functions(header=None):
     names = set()
     for h in HEADERS:
+        if header and os.path.basename(h) != header:
+            continue
         text = open(h, encoding="utf-8").read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         names |= set(re.findall(r"\b(bsattn_\w+)\s*\(", text))
@@ -27,21 +29,32 @@ def declared_functions():
 
 
 def test_library_exports_every_declared_function():
+    """libbsattn.so exports every function of bsattn.h, libbsattn_probe.so those of
+    bsattn_probe.h; the method's library holds no probe."""
+    from bench import probe_lib
     L = bst.lib()
-    names = declared_functions()
+    names = declared_functions("bsattn.h")
     assert {"bsattn_select", "bsattn_forward", "bsattn_select_workspace_bytes",
             "bsattn_abi_version", "bsattn_status_str", "bsattn_last_error",
             "bsattn_select_ex", "bsattn_forward_ex", "bsattn_key_blocks",
-            "bsattn_select_workspace_bytes_ex", "bsattn_probe_mfma_bf16", "bsattn_probe_read",
-            "bsattn_probe_copy", "bsattn_probe_sink_floats", "bsattn_probe_mfma_fp8",
-            "bsattn_decode_ex"} <= set(names)
+            "bsattn_select_workspace_bytes_ex", "bsattn_decode_ex",
+            "bsattn_select_noalloc", "bsattn_select_noalloc_max_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
+    pnames = declared_functions("bsattn_probe.h")
+    assert {"bsattn_probe_mfma_bf16", "bsattn_probe_read", "bsattn_probe_copy",
+            "bsattn_probe_sink_floats", "bsattn_probe_mfma_fp8",
+            "bsattn_probe_last_error"} <= set(pnames)
+    P = probe_lib()
+    for n in pnames:
+        assert hasattr(P, n), n
+        assert not hasattr(L, n), f"{n} is exported by the method's library"
+    assert set(names).isdisjoint(pnames)
 
 
 def test_version_and_status_strings():
     L = bst.lib()
-    assert L.bsattn_abi_version() == 4
+    assert L.bsattn_abi_version() == 5
     for s in range(5):
         assert L.bsattn_status_str(s).decode() == bsattn.STATUS[s]
     assert L.bsattn_status_str(99).decode() == "unknown status"
@@ -303,7 +316,11 @@ def test_device_tensor_checks_after_device(monkeypatch):
 
 
 def test_probe_rejects():
-    L = bst.lib()
+    from bench import probe_lib
+    L = probe_lib()
+
+    def last():
+        return L.bsattn_probe_last_error().decode()
     fl = ctypes.c_double(0.0)
     assert L.bsattn_probe_sink_floats(4) == 1024 and L.bsattn_probe_sink_floats(0) == 0
     assert L.bsattn_probe_mfma_bf16(0, 4, FAKE, ctypes.byref(fl), None) == 1

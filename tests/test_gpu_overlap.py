@@ -15,7 +15,7 @@ import torch
 import block_sparse_top_amd as bst
 from block_sparse_top_amd import synthetic as syn
 import oracle.bsattn_oracle as O
-from tests.parity import check_idx, check_out, to_f64
+from tests.parity import check_idx, check_out, check_random_rows, fp8_figures, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -83,6 +83,9 @@ def test_select_overlap(shape, dtype, opts):
         assert clear.mean() > 0.8
         bad = np.nonzero(clear & ~np.all(rows_g == rows_r, axis=1))[0]
         assert bad.size == 0, f"{bad.size} clear rows differ, first {bad[:5]}"
+        amb = np.nonzero(~clear)[0]
+        checked = check_random_rows(rows_g, rows_s, topk, nrand, seed, rows=amb)
+        say(f"   clear rows {int(clear.sum())}, ambiguous rows checked {checked}")
     else:
         say("  ", check_idx(gidx, S, topk))
 
@@ -122,6 +125,8 @@ def test_forward_overlap_given_rows(shape, dtype):
     idx = syn.random_block_sets(B, Hq, N // blk, nkb, topk, index=28, device=DEV)
     got, ref, fp8v, (qo, ko, vo) = _fwd_case(shape, dtype, idx, 28)
     say("   max_abs, rel_l2 =", check_out(got, ref, dtype, fp8_v=fp8v))
+    if dtype == "fp8":
+        say("   fp8 figures:", fp8_figures(got, ref, *fp8v))
     if dtype != "fp8":
         # negative control: the shared tokens of neighbouring blocks counted twice differ
         twice = np.full_like(ref, np.nan)

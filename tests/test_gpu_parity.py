@@ -12,7 +12,8 @@ import torch
 import block_sparse_top_amd as bst
 from block_sparse_top_amd import synthetic as syn
 import oracle.bsattn_oracle as O
-from tests.parity import check_idx, check_out, dtype_name, out_errors, to_f64, TOL
+from tests.parity import (check_idx, check_out, dtype_name, fp8_figures, out_errors, to_f64,
+                          TOL)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -423,8 +424,9 @@ def test_long_context_gqa_sampled():
     torch.cuda.synchronize()
     say("  gpu done")
     G = w.Hq // w.Hkv
-    rows = syn.sample_rows(16, w.Hq * w.nb, w.index)
+    rows = syn.sample_rows(64, w.Hq * w.nb, w.index)      # 64 seeded (head, query block) rows
     picks = [(0, r // w.nb, r % w.nb) for r in rows]
+    tally = {"clear": 0, "ambiguous": 0}
     gidx = idx.cpu().numpy()
     qfull = np.zeros((1, w.N, 1, w.D))
     for g in sorted({h // G for _, h, _ in picks}):
@@ -435,13 +437,17 @@ def test_long_context_gqa_sampled():
             blk = slice(i * w.block, (i + 1) * w.block)
             qb = to_f64(q[:, blk, h:h + 1])                            # [1, block, 1, D]
             s = O.pool(qb, w.block)[0, 0, 0] @ kbar.T                  # [nb]
-            check_idx(gidx[0, h, i][None], s[None], topk)
+            st = check_idx(gidx[0, h, i][None], s[None], topk)
+            tally["clear"] += st["clear"]
+            tally["ambiguous"] += st["ambiguous"]
             qfull[:, blk] = qb
             ref = O.attend(qfull, kg, vg, gidx[:, h:h + 1], w.block, 1 / math.sqrt(w.D),
                            rows=[(0, 0, i)])
             qfull[:, blk] = 0.0
             check_out(out[0, blk, h].float().cpu().numpy(), ref[0, blk, 0], "bf16")
         say(f"  kv head {g} ok")
+    say("  64 sampled rows:", tally)
+    assert tally["clear"] + tally["ambiguous"] == 64
 
 
 FP8_SHAPES = [
@@ -467,8 +473,9 @@ def test_forward_fp8(shape):
     check_idx(gidx, O.block_scores(O.pool(qo, blk), O.pool(ko, blk)), topk)
     ref = O.attend_batched(qo, ko, vo, gidx, blk, 1.0 / math.sqrt(D))
     vmax = float(np.abs(vo).max())
-    err = check_out(out.float().cpu().numpy(), ref, "fp8", fp8_v=(vmax, topk * blk))
-    say("   max_abs, rel_l2 =", err)
+    got = out.float().cpu().numpy()
+    err = check_out(got, ref, "fp8", fp8_v=(vmax, topk * blk))
+    say("   fp8 figures:", fp8_figures(got, ref, vmax, topk * blk))
     if topk == 1 or topk == N // blk:
         return
     # negative control at this bound: one dropped block of a few is caught
@@ -508,4 +515,5 @@ def test_fp8_workload_sampled():
         for (_, h, i) in mine:
             sl = (0, slice(i * w.block, (i + 1) * w.block), h)
             check_out(got[sl], ref[sl], "fp8", fp8_v=(vmax, topk * w.block))
+            say("   fp8 figures", (b, h, i), fp8_figures(got[sl], ref[sl], vmax, topk * w.block))
     say("  sampled outputs ok")

@@ -5,7 +5,6 @@ import sys
 import pytest
 import torch
 
-import block_sparse_top_amd as bst
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -14,7 +13,8 @@ DEV = "cuda:0"
 def test_probes_run_and_copy_is_exact():
     print("[probes]", flush=True)
     sys.stdout.flush()
-    L = bst.lib()
+    from bench import probe_lib
+    L = probe_lib()
     sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
     groups = 64

@@ -13,7 +13,8 @@ import torch
 import block_sparse_top_amd as bst
 from block_sparse_top_amd import synthetic as syn
 import oracle.bsattn_oracle as O
-from tests.parity import check_idx, check_idx_causal, check_out, to_f64
+from tests.parity import (check_idx, check_idx_causal, check_out, check_random_rows,
+                          fp8_figures, to_f64)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -85,6 +86,8 @@ def test_forward_causal(shape, dtype):
     got = out.float().cpu().numpy()
     fp8v = (float(np.abs(vo).max()), topk * blk) if dtype == "fp8" else None
     say("   max_abs, rel_l2 =", check_out(got, ref, dtype, fp8_v=fp8v))
+    if dtype == "fp8":
+        say("   fp8 figures:", fp8_figures(got, ref, *fp8v))
     if topk == N // blk:
         dense = O.dense_attention(qo, ko, vo, 1 / math.sqrt(D), causal=True)
         check_out(got, dense, dtype, fp8_v=fp8v)
@@ -243,6 +246,10 @@ def test_select_random_places(dtype, nrand, group):
     assert clear.mean() > 0.9
     bad = np.nonzero(clear & ~np.all(rows_g == rows_r, axis=1))[0]
     assert bad.size == 0, f"{bad.size} clear rows differ, first {bad[:5]}"
+    # the other rows: a valid top part plus exactly the oracle's draws given that part
+    amb = np.nonzero(~clear)[0]
+    checked = check_random_rows(rows_g, rows_s, topk, nrand, seed, rows=amb)
+    say(f"   clear rows {int(clear.sum())}, ambiguous rows checked {checked}")
     # a different seed changes some rows
     other = bst.select(q, k, blk, topk, group=group, nrand=nrand, seed=seed + 1).cpu().numpy()
     assert not np.array_equal(other, bst.select(q, k, blk, topk, group=group, nrand=nrand,

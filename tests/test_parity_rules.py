@@ -117,3 +117,41 @@ def test_fp8_rule_accepts_e4m3_weights_and_rejects_one_bad_row():
         check_out(one_row, out, "fp8", fp8_v=(vmax, k * blk))
     with pytest.raises(AssertionError):
         check_out(fp8, out, "fp8")                    # fp8 needs its bound's inputs
+
+
+def test_random_rows_rule():
+    """check_random_rows: accepts the oracle's own rows; on a row whose top part is tied at the
+    boundary, accepts the other valid split with the draws that split implies and rejects it
+    with the draws of the first split; rejects a drawn block that is no draw, and a top part
+    without a clearly better block."""
+    from tests.parity import check_random_rows
+    nb, topk, nrand, seed = 10, 4, 2, 1
+    S = np.array([[9.0, 1.0, 8.0, 2.0, 3.0, 0.5, 4.0, 0.1, 0.2, 0.3],
+                  [9.0, 7.0, 1.0, 2.0, 3.0, 0.5, 0.1, 0.2, 7.0, 0.3]])   # row 1: tie at top-2
+    ref = O.select_topk_random(S, topk, nrand, seed)
+    assert check_random_rows(ref, S, topk, nrand, seed) == 2
+    assert {0, 1} <= set(ref[1])                 # ties go to the lower index
+    tweak = S.copy()
+    tweak[1, [0, 8]] = np.inf                    # the other valid top part {0, 8}
+    alt = O.select_topk_random(tweak, topk, nrand, seed)[1]
+    rows = ref.copy()
+    rows[1] = alt
+    assert check_random_rows(rows, S, topk, nrand, seed, rows=[1]) == 1
+    # top part {0, 8} with the draws of the split {0, 1}
+    mixed = np.sort(np.array([0, 8] + [j for j in ref[1] if j not in (0, 1)]))
+    assert len(set(mixed)) == topk and not np.array_equal(mixed, np.sort(alt))
+    rows[1] = mixed
+    with pytest.raises(AssertionError):
+        check_random_rows(rows, S, topk, nrand, seed, rows=[1])
+    # a drawn block that is not the draw
+    drawn = [j for j in ref[0] if j not in (0, 2)]
+    spare = next(j for j in range(nb) if j not in ref[0])
+    bad = ref.copy()
+    bad[0] = np.sort([0, 2, drawn[0], spare])
+    with pytest.raises(AssertionError):
+        check_random_rows(bad, S, topk, nrand, seed, rows=[0])
+    # a top part without the best block (9.0 at block 0)
+    worse = ref.copy()
+    worse[0] = np.sort([2, 6, 4, 3])
+    with pytest.raises(AssertionError):
+        check_random_rows(worse, S, topk, nrand, seed, rows=[0])
