@@ -9,15 +9,15 @@
 // 设计与实现全解析", §3.3 计算优化) suggests computing the block scores as a matrix product and
 // fusing kernels; here the score rows never leave the chip.
 //
-// Layout: one work-group = 4 waves = 4*RW consecutive query-block rows of one (batch, query
+// Layout: one work-group = 4 waves = 16 consecutive query-block rows of one (batch, query
 // head). It first averages its rows' query tokens (16-byte loads, streamed past the caches:
 // this phase is HBM-bound and overlaps the arithmetic of the other work-groups on the CU),
-// keeps the pooled rows in LDS and also stores them to the workspace. Then each wave holds
-// RW rows x CPL columns of scores in registers, lane l owning columns
-// j = l + 64*c. Key-block columns are staged through LDS 64 at a time with coalesced row
-// loads, kept row-major with a one-float pad (lane j reads row j: banks j + d, no conflict).
-// Scores are fp32, summed over d in order with fused multiply-adds, identically for every
-// column (equal pooled key blocks give equal scores).
+// keeps the pooled rows in LDS and also stores them to the workspace. Key-block columns are
+// staged through LDS 64 at a time with coalesced row loads; the block scores of a chunk are
+// a 16 x 64 product on the fp32 MFMA (the MSA page's scores as a matrix product), fp32
+// operands and sums, the same arithmetic for every column (equal pooled key blocks give equal
+// scores). Each wave then holds 4 rows x CPL columns of scores in registers, lane l owning
+// columns j = l + 64*c.
 //
 // Selection of one row is done by its wave with no sorting: scores map to order-preserving
 // 32-bit keys, and a threshold T is built bit by bit from the top (a candidate bit stays when
@@ -46,31 +46,34 @@
 namespace bsattn {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-
-// Small work-groups (8 rows) give ~5 rounds of work-groups per CU, so that the pooling loads
-// of some overlap the score/select arithmetic of others. From 512 key blocks on, each
-// work-group streams so many pooled keys through LDS that 16 rows share them (fp8 workload,
-// 1024 key blocks: 1.88 -> 1.66 ms).
+// A work-group takes RG = 16 query-block rows (one 16-row tile of the fp32 MFMA; 4 waves) or,
+// from 512 key blocks on, 32 rows (8 waves): every work-group streams all pooled keys through
+// LDS, and 32 rows halve that traffic. 4 rows per wave for the selection.
 template <int CPL>
 struct SelCfg {
-  static constexpr int RW = CPL >= 8 ? 4 : 2;                   // rows per wave
-  static constexpr int RG = kWaves * RW;                       // rows per work-group
+  static constexpr int NWV = CPL >= 8 ? 8 : 4;                 // waves
+  static constexpr int NT = NWV * kWave;                       // threads
+  static constexpr int RW = 4;                                 // rows per wave
+  static constexpr int RG = NWV * RW;                          // rows per work-group
 };
 
-template <int KIND, int CPL>  // storage kind; score columns per lane: nk <= 64 * CPL
-__global__ __launch_bounds__(kThreads) void select_kernel(
+// storage kind; score columns per lane: nk <= 64 * CPL; head dimension
+template <int KIND, int CPL, int D>
+__global__ __launch_bounds__(SelCfg<CPL>::NT) void select_kernel(
     const uint8_t* __restrict__ q, float* __restrict__ qbar, const float* __restrict__ kbar,
-    int32_t* __restrict__ idx, int64_t N, int Hq, int Hkv, int nb, int nk, int D, int block,
-    int topk, int row_tiles, float inv_block, unsigned flags, int nrand, uint64_t seed) {
-  constexpr int RW = SelCfg<CPL>::RW, RG = SelCfg<CPL>::RG;
+    int32_t* __restrict__ idx, int64_t N, int Hq, int Hkv, int nb, int nk, int block,
+    int topk, int row_tiles, float inv_block, unsigned flags, int nrand, uint64_t seed,
+    int D_rt) {
+  constexpr int RW = SelCfg<CPL>::RW, RG = SelCfg<CPL>::RG, kThreads = SelCfg<CPL>::NT;
   constexpr int E = Vec<KIND>::E;
   constexpr int EB = 16 / E;                // bytes per stored element
   extern __shared__ float smem[];
-  const int KS = D + 1;                     // padded row stride of the key chunk
-  float* ks = smem;                         // [64][D+1] current key-block chunk
-  float* qs = smem + 64 * KS;               // [RG][D] pooled query rows of this work-group
+  constexpr int KS = D + 4;                 // padded row stride of the key chunk (16-byte rows)
+  constexpr int SS = 64 + 4;                // row stride of the score chunk
+  float* ks = smem;                         // [64][D+4] current key-block chunk
+  constexpr int kRed = RG * (D / E) < kThreads ? kThreads * E : 0;   // pooling partial sums
+  float* qs = smem + (64 * KS > kRed ? 64 * KS : kRed);   // [RG][D] pooled query rows
+  float* sc = qs + RG * D;                  // [RG][64+4] score chunk (MFMA tiles -> rows)
 
   // work-groups of one (batch, head) read the same pooled keys: keep them on one XCD's L2
   const int tile = (int)xcd_remap(blockIdx.x, gridDim.x);
@@ -87,19 +90,22 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   const float* K = kbar + ((int64_t)b * Hkv + g) * nk * D;
   const int row0 = rt * RG;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int D4 = D / 4;
+  constexpr int D4 = D / 4;
 
-  // ---- pool the RG query rows: pair (row r, 16-byte column c); TG token groups per pair
+  // ---- pool the RG query rows: pair (row r, 16-byte column c); TG token groups per pair.
+  // (This phase takes the head dimension as a run-time value: with the constant the compiler
+  // unrolls it into many more live registers, fewer work-groups per CU and a slower stream.)
+  const int Dr = D_rt;
   const float init = pmax ? -__builtin_inff() : 0.f;
   const float scl = pmax ? 1.f : inv_block;
   for (int j = 0; j < nh; ++j) {
     const int h = h0 + j;
     const bool last = j == nh - 1;
-    const int C16 = D / E;                  // 16-byte columns per token of one head
+    const int C16 = Dr / E;                  // 16-byte columns per token of one head
     const int pairs = RG * C16;
     const int per_pass = pairs < kThreads ? pairs : kThreads;
     const int TG = kThreads / per_pass;     // token groups (>= 1)
-    const int64_t tok_bytes = (int64_t)Hq * D * EB;
+    const int64_t tok_bytes = (int64_t)Hq * Dr * EB;
     float* red = ks;                        // [TG][per_pass][E] partial sums (fits: D >= 64)
     for (int p0 = 0; p0 < pairs; p0 += per_pass) {
       const int pr = p0 + tid % per_pass, tg = tid / per_pass;
@@ -109,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] = init;
       if (tg < TG && row < nb) {
-        const uint8_t* src = q + (((int64_t)b * N + (int64_t)row * block) * Hq + h) * D * EB + c * 16;
+        const uint8_t* src = q + (((int64_t)b * N + (int64_t)row * block) * Hq + h) * Dr * EB + c * 16;
         int t = tg;
         for (; t + 7 * TG < block; t += 8 * TG) {
           u32x4 w[8];
@@ -141,71 +147,88 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
             sum = pmax ? fmaxf(sum, red[t2 * per_pass * E + o]) : sum + red[t2 * per_pass * E + o];
           const int pr2 = p0 + o / E, r2 = pr2 / C16, d = (pr2 % C16) * E + o % E;
           float m = sum * scl;
-          if (j > 0) m += qs[r2 * D + d];   // the same thread wrote it for the previous head
-          qs[r2 * D + d] = m;
-          if (last && row0 + r2 < nb) qbar[((int64_t)bh * nb + row0 + r2) * D + d] = m;
+          if (j > 0) m += qs[r2 * Dr + d];   // the same thread wrote it for the previous head
+          qs[r2 * Dr + d] = m;
+          if (last && row0 + r2 < nb) qbar[((int64_t)bh * nb + row0 + r2) * Dr + d] = m;
         }
       } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           float m = acc[e] * scl;
-          if (j > 0) m += qs[r * D + c * E + e];
-          qs[r * D + c * E + e] = m;
-          if (last && row < nb) qbar[((int64_t)bh * nb + row) * D + c * E + e] = m;
+          if (j > 0) m += qs[r * Dr + c * E + e];
+          qs[r * Dr + c * E + e] = m;
+          if (last && row < nb) qbar[((int64_t)bh * nb + row) * Dr + c * E + e] = m;
         }
       }
     }
   }
 
+  // ---- scores on the fp32 MFMA (v_mfma_f32_16x16x4_f32): per 64-column chunk each wave forms
+  // the 16 x 16 tile S[rows][16*wave .. +16) = qs K^T. The k-slot q4 = lane / 16 of a lane
+  // carries d = (D/4)*q4 + s at k-step s (any split of d gives the same sum in exact
+  // arithmetic; this one gives each lane contiguous operands). Every score goes through the
+  // same products and sums in the same order, so equal pooled key blocks give equal scores.
+  // The tile goes through LDS (sc) to the selection layout, lane = column, 4 rows per wave.
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  const int m16 = lane & 15, q4 = lane >> 4;
+  constexpr int DQ = D / 4;                 // k-steps per tile (16 or 32)
+  float qa[DQ];                             // A operands: qs[m16][DQ*q4 + s], s < DQ
+  __syncthreads();                          // qs complete
+#pragma unroll
+  for (int s4 = 0; s4 < DQ / 4; ++s4) {
+    const f32x4v v = *(const f32x4v*)(qs + (16 * (wave >> 2) + m16) * D + DQ * q4 + 4 * s4);
+    qa[4 * s4] = v[0]; qa[4 * s4 + 1] = v[1]; qa[4 * s4 + 2] = v[2]; qa[4 * s4 + 3] = v[3];
+  }
   float acc[RW][CPL];
 #pragma unroll
-  for (int r = 0; r < RW; ++r)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[r][c] = 0.f;
-
-#pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    __syncthreads();                        // previous chunk consumed (and qs written)
+    __syncthreads();                        // previous chunk's ks and sc consumed
     {
       // all loads of the chunk first (up to 8 per thread: D <= 128), then the LDS stores
-      constexpr int kMaxPer = 8;
-      f32x4 vv[kMaxPer];
+      // (columns past nk load the last key block and are zeroed after the load)
+      constexpr int kPer = 64 * D4 / kThreads;   // 4 (D = 64) or 8 (D = 128)
+      f32x4 vv[kPer];
 #pragma unroll
-      for (int u = 0; u < kMaxPer; ++u) {
+      for (int u = 0; u < kPer; ++u) {
         const int e = tid + u * kThreads;
-        vv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (e < 64 * D4) {
-          const int col = e / D4, d4 = e - col * D4;
-          const int j = c * 64 + col;
-          if (j < nk) vv[u] = *(const f32x4*)(K + (int64_t)j * D + 4 * d4);
-        }
+        const int col = e / D4, d4 = e - col * D4;
+        const int j = c * 64 + col;
+        vv[u] = *(const f32x4*)(K + (int64_t)(j < nk ? j : nk - 1) * D + 4 * d4);
       }
 #pragma unroll
-      for (int u = 0; u < kMaxPer; ++u) {
+      for (int u = 0; u < kPer; ++u) {
         const int e = tid + u * kThreads;
-        if (e < 64 * D4) {
-          const int col = e / D4, d4 = e - col * D4;
-          float* dst = ks + col * KS + 4 * d4;
-          dst[0] = vv[u][0]; dst[1] = vv[u][1]; dst[2] = vv[u][2]; dst[3] = vv[u][3];
-        }
+        const int col = e / D4, d4 = e - col * D4;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        *(f32x4*)(ks + col * KS + 4 * d4) = c * 64 + col < nk ? vv[u] : z;
       }
     }
     __syncthreads();
-    const float* qw = qs + wave * RW * D;
-    const float* kr = ks + lane * KS;
-    for (int d = 0; d < D; d += 4) {
-      const float k0 = kr[d], k1 = kr[d + 1], k2 = kr[d + 2], k3 = kr[d + 3];
+    {
+      // two independent accumulation chains (even and odd groups of four k-steps), added at
+      // the end: the same order for every column
+      const int ct = wave & 3;              // column tile of this wave (16 columns)
+      const float* kb = ks + (16 * ct + m16) * KS + DQ * q4;
+      f32x4v t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < RW; ++r) {
-        const f32x4 qv = *(const f32x4*)(qw + r * D + d);
-        float s = acc[r][c];
-        s = __builtin_fmaf(qv[0], k0, s);
-        s = __builtin_fmaf(qv[1], k1, s);
-        s = __builtin_fmaf(qv[2], k2, s);
-        s = __builtin_fmaf(qv[3], k3, s);
-        acc[r][c] = s;
+      for (int s4 = 0; s4 < DQ / 4; ++s4) {
+        const f32x4v bv = *(const f32x4v*)(kb + 4 * s4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (s4 & 1)
+            t1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * s4 + e], bv[e], t1, 0, 0, 0);
+          else
+            t0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * s4 + e], bv[e], t0, 0, 0, 0);
+        }
       }
+      const f32x4v t = t0 + t1;
+      // lane holds S[row 16*(wave/4) + 4*q4 + e][column 16*(wave%4) + m16]
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[(16 * (wave >> 2) + 4 * q4 + e) * SS + 16 * ct + m16] = t[e];
     }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RW; ++r) acc[r][c] = sc[(wave * RW + r) * SS + lane];
   }
 
   // ---- per-row top-k, one wave per row
@@ -285,18 +308,24 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   }
 }
 
-template <int KIND, int CPL>
-hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int nb, int nk, int D, int block,
+template <int KIND, int CPL, int D>
+hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int nb, int nk, int block,
                   int topk, const void* q, float* qbar, const float* kbar, int32_t* idx,
                   unsigned flags, int nrand, uint64_t seed, hipStream_t stream) {
-  constexpr int RG = SelCfg<CPL>::RG;
+  constexpr int RG = SelCfg<CPL>::RG, NT = SelCfg<CPL>::NT;
   const int row_tiles = (nb + RG - 1) / RG;
   const int HS = (flags & kGroup) ? Hkv : Hq;
   const dim3 grid((unsigned)(B * HS * row_tiles));
-  const size_t lds = (size_t)(64 * (D + 1) + RG * D) * sizeof(float);
-  select_kernel<KIND, CPL><<<grid, kThreads, lds, stream>>>(
-      (const uint8_t*)q, qbar, kbar, idx, N, Hq, Hkv, nb, nk, D, block, topk, row_tiles,
-      1.0f / (float)block, flags, nrand, seed);
+  // the key chunk's LDS also holds the pooling phase's partial sums (TG x pairs x E floats)
+  constexpr int E = Vec<KIND>::E;
+  constexpr int pairs = RG * (D / E);
+  constexpr int per_pass = pairs < NT ? pairs : NT;
+  constexpr int red = pairs < NT ? NT * E : 0;    // as the kernel reserves it
+  constexpr int kchunk = 64 * (D + 4) > red ? 64 * (D + 4) : red;
+  const size_t lds = (size_t)(kchunk + RG * D + RG * (64 + 4)) * sizeof(float);
+  select_kernel<KIND, CPL, D><<<grid, NT, lds, stream>>>(
+      (const uint8_t*)q, qbar, kbar, idx, N, Hq, Hkv, nb, nk, block, topk, row_tiles,
+      1.0f / (float)block, flags, nrand, seed, D);
   return hipGetLastError();
 }
 
@@ -304,8 +333,11 @@ template <int KIND>
 hipError_t launch_kind(int64_t B, int64_t N, int Hq, int Hkv, int nb, int nk, int D, int block,
                        int topk, const void* q, float* qbar, const float* kbar, int32_t* idx,
                        unsigned flags, int nrand, uint64_t seed, hipStream_t stream) {
-#define BSATTN_SELECT_CPL(cpl) \
-  launch<KIND, cpl>(B, N, Hq, Hkv, nb, nk, D, block, topk, q, qbar, kbar, idx, flags, nrand, seed, stream)
+#define BSATTN_SELECT_CPL(cpl)                                                                  \
+  (D == 64 ? launch<KIND, cpl, 64>(B, N, Hq, Hkv, nb, nk, block, topk, q, qbar, kbar, idx, flags, \
+                                   nrand, seed, stream)                                          \
+           : launch<KIND, cpl, 128>(B, N, Hq, Hkv, nb, nk, block, topk, q, qbar, kbar, idx,      \
+                                    flags, nrand, seed, stream))
   if (nk <= 64) return BSATTN_SELECT_CPL(1);
   if (nk <= 128) return BSATTN_SELECT_CPL(2);
   if (nk <= 256) return BSATTN_SELECT_CPL(4);
