@@ -23,9 +23,13 @@
 //
 // Data movement: K and V tiles go from HBM/L2 straight into LDS with global_load_lds_dwordx4
 // (lane l of one instruction fills bytes [16l, 16l+16) of a 1 KiB LDS span; the lane fetches
-// whichever 16-byte chunk belongs there). One LDS buffer per tensor: the wave reads all K
-// operands of step t into registers, then starts the K transfer of step t+1 and computes
-// S^T and the softmax while it flies; V likewise before the PV product. The 16-byte chunk c
+// whichever 16-byte chunk belongs there). One wave per work-group (D = 64, 64-token blocks):
+// one LDS buffer per tensor; the wave reads all K operands of step t into registers, then
+// starts the K transfer of step t+1 and computes S^T and the softmax while it flies; V likewise
+// before the PV product (with several waves and 16 KiB tiles the same, with barriers around the
+// reads). Otherwise, several waves per work-group: two buffers per tensor; after one barrier at
+// the start of step t (every wave's share of step t landed, every wave done with step t-1) the
+// K and V tiles of step t+1 start into the other buffers. The 16-byte chunk c
 // of tile row r sits at chunk position c ^ f(r), f(r) = 2(r&3) + ((r>>2)&1), which makes both
 // the row reads of K (8 rows, one chunk) and the transpose reads of V (4 rows, 2 chunks) hit
 // all 32 banks once.
@@ -122,8 +126,15 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
   constexpr int RP = SB / R;                  // work-groups (row parts) per query block
   constexpr int UN = SB / KU;                 // steps per selected block
   using C = Cfg<D, R, KU>;
-  __shared__ __attribute__((aligned(1024))) char Kl[C::TILE];   // [KU][D] bf16, swizzled
-  __shared__ __attribute__((aligned(1024))) char Vl[C::TILE];
+  // With one wave per work-group each tensor has one LDS buffer (its transfers are waited for
+  // by that wave alone). With several waves sharing the tiles, two buffers per tensor: the
+  // tiles of step t+1 go into the other buffer at the start of step t, after one barrier that
+  // also ends every wave's reads of step t-1 (one barrier per step, not four).
+  // (Two waves with 16 KiB tiles keep one buffer: 64 KiB per work-group would leave one wave
+  // per SIMD.)
+  constexpr int NBUF = (C::NW >= 4 || (C::NW == 2 && C::TILE <= 8192)) ? 2 : 1;
+  __shared__ __attribute__((aligned(1024))) char Kl[NBUF][C::TILE];   // [KU][D] bf16, swizzled
+  __shared__ __attribute__((aligned(1024))) char Vl[NBUF][C::TILE];
   __shared__ uint32_t chosen[OVL ? kMaxKeyBlocks / 32 : 1];   // OVL: the row's key blocks
 
   // tile order: (b, kv head, query block, head within group, row part); blocks reading the
@@ -273,8 +284,8 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
     int skip_cur = skip_of(kb_cur);
     {
       const int64_t tb = tile_base(kb_cur, 0);
-      dma(kbase0 + tb, Kl);
-      dma(vbase0 + tb, Vl);
+      dma(kbase0 + tb, Kl[0]);
+      dma(vbase0 + tb, Vl[0]);
     }
 
     for (int t = 0; t < kcount * UN; ++t) {     // steps: UN per selected block
@@ -285,17 +296,31 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
       const int skip_next = OVL && more ? skip_of(kb_next) : 0;
 
       // ---- K(t): wait for this wave's share (V(t) may still fly), then the whole work-group
-      wait_vmcnt<C::DMA>();
-      if (C::NW > 1) __syncthreads();
+      const int cur = NBUF > 1 ? (t & 1) : 0;
+      const char* Kc = Kl[cur];
+      const char* Vc = Vl[cur];
+      if constexpr (NBUF > 1) {
+        wait_vmcnt<0>();                       // this wave's share of step t's tiles
+        __syncthreads();                       // every share landed; step t-1 read everywhere
+        if (more) {
+          dma(kbase0 + tb_next, Kl[cur ^ 1]);
+          dma(vbase0 + tb_next, Vl[cur ^ 1]);
+        }
+      } else {
+        wait_vmcnt<C::DMA>();                  // K(t) (V(t) may still fly)
+        if (C::NW > 1) __syncthreads();
+      }
       bf16x8 ka[C::NKT][C::NS];
 #pragma unroll
       for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
         for (int s = 0; s < C::NS; ++s)
-          ka[kt][s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kl + kt * 32 * D * 2 + koff[s]));
-      wait_lgkmcnt0();
-      if (C::NW > 1) __syncthreads();
-      if (more) dma(kbase0 + tb_next, Kl);
+          ka[kt][s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Kc + kt * 32 * D * 2 + koff[s]));
+      if constexpr (NBUF == 1) {
+        wait_lgkmcnt0();
+        if (C::NW > 1) __syncthreads();        // every wave's K(t) reads done
+        if (more) dma(kbase0 + tb_next, Kl[0]);
+      }
 
       // ---- S^T = K Q^T
       f32x16 sacc[C::NKT][C::QC];
@@ -396,21 +421,26 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
 #pragma unroll
       for (int qc = 0; qc < C::QC; ++qc) lsum[qc] += bsum[qc];
 
-      // ---- V(t): wait (K(t+1) may still fly), read all V^T operands, then start V(t+1)
-      if (more) wait_vmcnt<C::DMA>(); else wait_vmcnt<0>();
-      if (C::NW > 1) __syncthreads();
+      // ---- V(t): (one buffer: wait, K(t+1) may still fly) read all V^T operands, then start
+      // V(t+1)
+      if constexpr (NBUF == 1) {
+        if (more) wait_vmcnt<C::DMA>(); else wait_vmcnt<0>();
+        if (C::NW > 1) __syncthreads();
+      }
       bf16x8 va[C::NPS][C::NDT];
 #pragma unroll
       for (int s = 0; s < C::NPS; ++s)
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) {
-          const char* p = Vl + (16 * s) * D * 2 + voff[dt];
+          const char* p = Vc + (16 * s) * D * 2 + voff[dt];
           const s16x4 a8[2] = {ds_read_tr16(p), ds_read_tr16(p + 8 * D * 2)};
           va[s][dt] = __builtin_bit_cast(bf16x8, a8);
         }
-      wait_lgkmcnt0();
-      if (C::NW > 1) __syncthreads();
-      if (more) dma(vbase0 + tb_next, Vl);
+      if constexpr (NBUF == 1) {
+        wait_lgkmcnt0();                       // V(t) read before V(t+1) overwrites it
+        if (C::NW > 1) __syncthreads();
+        if (more) dma(vbase0 + tb_next, Vl[0]);
+      }
 
       // ---- O^T += V^T P^T
       if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
