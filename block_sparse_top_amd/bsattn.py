@@ -20,7 +20,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libbsattn.so")
+# BSATTN_LIB names another build of the same library (the tests' host-sanitizer build)
+LIB_PATH = os.environ.get("BSATTN_LIB") or os.path.join(_PKG, "libbsattn.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}

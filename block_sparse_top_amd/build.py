@@ -43,8 +43,14 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+# host AddressSanitizer for a test build of the C-ABI layer (device code is built as usual;
+# every -fsanitize= sits after -Xarch_host so that it applies to the host pass only)
+ASAN_CFLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_LDFLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-shared-libasan"]
+
+
+def _compile(src: str, extra, build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -52,25 +58,30 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def _link(objs, lib):
+def _link(objs, lib, extra=()):
     tmp = lib + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, lib)
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = SOURCES + PROBE_SOURCES
+def build(verbose: bool = False, extra_flags=(), build_dir: str = BUILD, lib: str = LIB,
+          probes: bool = True, asan: bool = False) -> str:
+    """Compiles and links libbsattn.so (and libbsattn_probe.so). build_dir/lib/probes/asan give
+    a separate test build: host AddressSanitizer, no probe library, elsewhere than the product."""
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = SOURCES + (PROBE_SOURCES if probes else [])
+    flags = list(extra_flags) + (ASAN_CFLAGS if asan else [])
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, list(extra_flags)), srcs)))
-    _link([objs[s] for s in SOURCES], LIB)
-    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, flags, build_dir), srcs)))
+    _link([objs[s] for s in SOURCES], lib, ASAN_LDFLAGS if asan else ())
+    if probes:
+        _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB} and {PROBE_LIB}")
-    return LIB
+        print(f"built {lib}" + (f" and {PROBE_LIB}" if probes else ""))
+    return lib
 
 
 if __name__ == "__main__":
