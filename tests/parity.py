@@ -13,9 +13,14 @@ softmax weights enter the fp8 PV product as e4m3 values. Weights are <= 2^8 and 
 normaliser is >= 2^7 (the weight of the element that set the row's reference); a normal
 e4m3 weight carries relative error <= 2^-4, a subnormal one (< 2^-6) absolute error
 <= 2^-10, so |out - ref| <= (2^-4 + n_keys * 2^-17) * max|v| + 2^-8 |ref| (bf16 output
-rounding). The max-abs bound doubles the n_keys term for the fp32 sums. Statistically the errors are far smaller (rms 2^-4/sqrt(3) ~ 3.6% per weight,
-averaging over keys): relative L2 <= 1e-1 over the tensor and <= 2e-1 on every query row, the
-row check catching a single wrong row that the tensor-wide figures would dilute.
+rounding). The max-abs bound doubles the n_keys term for the fp32 sums. Statistically the
+errors are far smaller: a weight rounded to e4m3 carries a relative error of rms
+2^-4/sqrt(3) ~ 3.6 %, and for outputs that average many keys the relative error of a row is
+about that rms whatever the number of keys (the sqrt(sum w^2)/sum w factor of the weights and
+the |v|/|out| factor of the average cancel). Rule: relative L2 <= 5e-2 over the tensor and
+<= 1e-1 on every query row (the row check catching a single wrong row that the tensor-wide
+figures would dilute). Recorded on the GPU (27 fp8 comparisons): 1.6-2.7 % over the tensor,
+3.0-4.2 % on the worst row; the CPU simulation of e4m3 weights: 2.2-2.3 %, worst row <= 5.1 %.
 """
 from __future__ import annotations
 
@@ -25,7 +30,7 @@ import torch
 import oracle.bsattn_oracle as O
 
 GAP_REL = 1e-5
-TOL = {"f32": (1e-4, 1e-5), "bf16": (2e-2, 1e-2), "fp8": (None, 1e-1)}
+TOL = {"f32": (1e-4, 1e-5), "bf16": (2e-2, 1e-2), "fp8": (None, 5e-2)}
 
 
 def dtype_name(t: torch.Tensor) -> str:
@@ -159,7 +164,7 @@ def out_errors(gpu_out: np.ndarray, ref: np.ndarray):
     return max_abs, rel_l2
 
 
-FP8_ROW_REL = 2e-1
+FP8_ROW_REL = 1e-1
 
 
 def fp8_abs_bound(vmax: float, n_keys: int, ref: np.ndarray) -> float:
