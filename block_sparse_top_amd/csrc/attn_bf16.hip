@@ -29,10 +29,16 @@
 // before the PV product (with several waves and 16 KiB tiles the same, with barriers around the
 // reads). Otherwise, several waves per work-group: two buffers per tensor; after one barrier at
 // the start of step t (every wave's share of step t landed, every wave done with step t-1) the
-// K and V tiles of step t+1 start into the other buffers. The 16-byte chunk c
-// of tile row r sits at chunk position c ^ f(r), f(r) = 2(r&3) + ((r>>2)&1), which makes both
-// the row reads of K (8 rows, one chunk) and the transpose reads of V (4 rows, 2 chunks) hit
-// all 32 banks once.
+// K and V tiles of step t+1 start into the other buffers.
+// LDS bank layout: gfx950's LDS has 64 banks of 4 bytes (256 bytes per clock); a 16-byte row
+// read serves 16 lanes per clock and an 8-byte transpose read 32 lanes. The 16-byte chunk c of
+// tile row r sits at chunk position c ^ f(r), with f chosen so that every such group of lanes
+// covers the 64 banks once: at D = 64 (128-byte rows, two per bank line) f(r) = 4((r>>1)&1) +
+// ((r>>2)&3), which gives the 8 even and the 8 odd rows of a 16-row K read 8 distinct chunk
+// positions each and puts rows r and r+2 of a V transpose read on opposite halves of the row;
+// at D = 128 (256-byte rows, one per bank line) f(r) = 4(r&3) + ((r>>2)&3) over 16 chunks,
+// which gives 16 consecutive rows 16 distinct positions and each 4-row group of a V transpose
+// read its own quarter of the row.
 //
 // Softmax reference: softmax does not depend on the reference value m subtracted from a row
 // (p = exp2(c*s - m), c = scale*log2(e)), so m stays 0 while every per-lane step sum of
@@ -98,10 +104,11 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
-// chunk position of logical 16-byte chunk c in tile row r
+// chunk position of logical 16-byte chunk c in tile row r (an involution in c)
+template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
-  const int f = 2 * (r & 3) + ((r >> 2) & 1);
-  return (c & ~7) | ((c & 7) ^ f);
+  if constexpr (D == 64) return c ^ (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
+  else return c ^ (4 * (r & 3) + ((r >> 2) & 3));
 }
 
 __device__ __forceinline__ s16x4 ds_read_tr16(const char* lds_bytes) {
@@ -179,7 +186,7 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
   for (int x = 0; x < C::DMA; ++x) {
     const int pos = (wave * C::DMA + x) * 64 + lane;         // chunk position in the tile
     const int r = pos / (D / 8), p = pos % (D / 8);
-    goff[x] = (uint32_t)((r * krs + swz(r, p) * 8) * 2);
+    goff[x] = (uint32_t)((r * krs + swz<D>(r, p) * 8) * 2);
   }
   bool bad = false;
   auto tile_base = [&](int kb, int u) -> int64_t {   // step u (KU keys) of selected block kb
@@ -240,16 +247,18 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
   // LDS read offsets of this lane
   int koff[C::NS];                             // K row l32, chunk 2s+half (+ 32*kt rows)
 #pragma unroll
-  for (int s = 0; s < C::NS; ++s) koff[s] = l32 * D * 2 + 16 * swz(l32, 2 * s + half);
+  for (int s = 0; s < C::NS; ++s) koff[s] = l32 * D * 2 + 16 * swz<D>(l32, 2 * s + half);
   // V transpose reads: in each 16-lane group lane 4e+t names row 4*half+e (+16s, +8) and
   // columns 32dt + 16*((lane>>4)&1) + 4t, i.e. chunk 4dt + 2*((lane>>4)&1) + t/2, half t&1
-  int voff[C::NDT];
+  // (rows r and r + 8 have their own chunk positions: f depends on bit 3 of the row)
+  int voff[C::NDT], voff8[C::NDT];
   {
     const int e = (lane & 15) >> 2, r = 4 * half + e;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) {
       const int ch = 4 * dt + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-      voff[dt] = r * D * 2 + 16 * swz(r, ch) + 8 * (lane & 1);
+      voff[dt] = r * D * 2 + 16 * swz<D>(r, ch) + 8 * (lane & 1);
+      voff8[dt] = (r + 8) * D * 2 + 16 * swz<D>(r + 8, ch) + 8 * (lane & 1);
     }
   }
 
@@ -432,8 +441,8 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
       for (int s = 0; s < C::NPS; ++s)
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) {
-          const char* p = Vc + (16 * s) * D * 2 + voff[dt];
-          const s16x4 a8[2] = {ds_read_tr16(p), ds_read_tr16(p + 8 * D * 2)};
+          const char* p = Vc + (16 * s) * D * 2;
+          const s16x4 a8[2] = {ds_read_tr16(p + voff[dt]), ds_read_tr16(p + voff8[dt])};
           va[s][dt] = __builtin_bit_cast(bf16x8, a8);
         }
       if constexpr (NBUF == 1) {

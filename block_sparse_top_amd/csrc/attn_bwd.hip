@@ -27,7 +27,9 @@
 // Layout conventions follow the forward kernel: 32x32 MFMA accumulators (register r, lane l:
 // row 8(r/4) + 4(l/32) + r%4, column l%32), 16-key (or 16-query) k-steps whose 16 slots are
 // matched to {4h..4h+3, 8+4h..8+4h+3} on both operands, tiles [64][D] bf16 in LDS with the
-// 16-byte chunk c of row r at chunk c ^ f(r), f(r) = 2(r&3) + ((r>>2)&1).
+// 16-byte chunk c of row r at chunk c ^ f(r): f(r) = 4((r>>1)&1) + ((r>>2)&3) at D = 64 and
+// 4(r&3) + ((r>>2)&3) at D = 128, which keeps row reads (16 rows per clock), transpose reads
+// (4 rows x 64 bytes per clock) and row-major stores on distinct banks of gfx950's 64-bank LDS.
 // Causal option: query block i reads its first min(topk, i+1) entries (each in [0, i]) and in
 // its own block keys after the query get weight 0; the dS of masked pairs is 0.
 #include "common.h"
@@ -43,9 +45,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kBlk = 64;                      // block size of this backward
 constexpr float kLog2e = 1.4426950408889634f;
 
+template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
-  const int f = 2 * (r & 3) + ((r >> 2) & 1);
-  return (c & ~7) | ((c & 7) ^ f);
+  if constexpr (D == 64) return c ^ (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
+  else return c ^ (4 * (r & 3) + ((r >> 2) & 3));
 }
 
 __device__ __forceinline__ s16x4 ds_read_tr16(const char* lds_bytes) {
@@ -76,7 +79,7 @@ struct TileRegs {
     for (int x = 0; x < X; ++x) {
       const int pos = x * NT + tid;
       const int r = pos / CH, c = pos % CH;
-      *(u32x4*)(tile + r * D * 2 + 16 * swz(r, c)) = w[x];
+      *(u32x4*)(tile + r * D * 2 + 16 * swz<D>(r, c)) = w[x];
     }
   }
 };
@@ -85,7 +88,7 @@ struct TileRegs {
 template <int D>
 __device__ __forceinline__ bf16x8 rows_operand(const char* tile, int t, int s, int l32, int half) {
   const int r = 32 * t + l32;
-  return __builtin_bit_cast(bf16x8, *(const u32x4*)(tile + r * D * 2 + 16 * swz(r, 2 * s + half)));
+  return __builtin_bit_cast(bf16x8, *(const u32x4*)(tile + r * D * 2 + 16 * swz<D>(r, 2 * s + half)));
 }
 
 // A operand (32 d x 16 rows) of a row-major tile read transposed: d rows 32*dt + l32, rows
@@ -95,8 +98,9 @@ __device__ __forceinline__ bf16x8 trans_operand(const char* tile, int dt, int ps
   const int half = lane >> 5;
   const int e = (lane & 15) >> 2, r = 4 * half + e;
   const int ch = 4 * dt + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const char* p = tile + (16 * ps + r) * D * 2 + 16 * swz(r, ch) + 8 * (lane & 1);
-  const s16x4 a8[2] = {ds_read_tr16(p), ds_read_tr16(p + 8 * D * 2)};
+  const char* t = tile + 16 * ps * D * 2 + 8 * (lane & 1);
+  const s16x4 a8[2] = {ds_read_tr16(t + r * D * 2 + 16 * swz<D>(r, ch)),
+                       ds_read_tr16(t + (r + 8) * D * 2 + 16 * swz<D>(r + 8, ch))};
   return __builtin_bit_cast(bf16x8, a8);
 }
 

@@ -21,9 +21,11 @@
 // group, output lane i takes byte i%8 of the 8 bytes named by lane 2e + i/8, e = 0..7). The
 // 32 k-slots of lane half h are keys 32kt + 8j + 4h + t (kt<2, j<4, t<4) on both operands of
 // the PV product: exactly the keys the S^T accumulators give that lane. 16-byte chunk c of
-// tile row r sits at chunk c ^ f(r), f(r) = (r&3) | (((r>>2) ^ (r>>3)) & 1) << 2, which keeps
-// both the K row reads (8 rows) and the V transpose reads (8 rows x 2 half-chunks) on 32
-// distinct banks.
+// tile row r sits at chunk c ^ f(r), f(r) = 2((r>>1)&1) + 4((r>>3)&1) + ((r>>2)&1). gfx950's
+// LDS has 64 banks of 4 bytes and a 128-byte row fills half a bank line: the K row reads
+// (16 lanes per clock, rows 0..15) see f take all 8 values on the even and on the odd rows,
+// and the V transpose reads (32 lanes per clock: rows {0,2,8,10} or {4,6,12,14} and the odd
+// ones, 2 chunks each) see f>>1 take 4 distinct values, so both cover the 64 banks once.
 //
 // Causal variant (template flag): query block i reads the first min(topk, i+1) entries of its
 // row, each in [0, i]; in its own block the scores of keys after the query are -inf before
@@ -68,7 +70,7 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
 }
 
 __device__ __forceinline__ int swz8(int r) {
-  return (r & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
+  return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2) | ((r >> 2) & 1);
 }
 
 __device__ __forceinline__ i32x2 ds_read_tr8(const char* lds_bytes) {
@@ -82,7 +84,7 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f3
 }
 
 template <int BLK, bool CAUSAL, bool OVL>
-__global__ __launch_bounds__(BLK * 2) void attn_fp8_kernel(
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(BLK == 64 ? 3 : 2))) void attn_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse,
     int64_t N, int Hq, int Hkv, int nb, int topk, float c, float dv, uint32_t total_tiles,
