@@ -39,6 +39,8 @@
 namespace bsattn {
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 // ---------------------------------------------------------------- pooling of new blocks
 __global__ __launch_bounds__(256) void pool_new_kernel(const uint16_t* __restrict__ kc,
                                                        const int32_t* __restrict__ lens_old,
@@ -353,6 +355,35 @@ __global__ __launch_bounds__(64) void dattn_kernel(
 // pass (groups of D/8 lanes per key row, partial dots summed across the group), the weights
 // and the value pass then run per wave from LDS, writing the same partial results as
 // dattn_kernel for dcombine_kernel.
+// The tiles move with global_load_lds_dwordx4 (1 KiB of consecutive rows per wave
+// instruction, the instructions of a tile dealt round-robin over the waves) and overlap the
+// arithmetic: the next block's keys start as soon as every wave has scored the current keys,
+// its values as soon as every wave has summed the current values. Every wave issues the same
+// number of transfers per tile (a wave short of a distinct one repeats the tile's last: the
+// same bytes to the same place), so the waits count a fixed number per tile.
+
+// vmcnt-only waits (expcnt and lgkmcnt left free), gfx9 s_waitcnt encoding
+template <int N>
+__device__ __forceinline__ void dwait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// wait until at most n of this wave's vector-memory operations are in flight (n uniform)
+__device__ __forceinline__ void dwait_vmcnt_le(int n) {
+  switch (n) {
+    case 0: dwait_vmcnt<0>(); break;
+    case 1: dwait_vmcnt<1>(); break;
+    case 2: dwait_vmcnt<2>(); break;
+    case 3: dwait_vmcnt<3>(); break;
+    case 4: dwait_vmcnt<4>(); break;
+    case 5: dwait_vmcnt<5>(); break;
+    case 6: dwait_vmcnt<6>(); break;
+    case 7: dwait_vmcnt<7>(); break;
+    case 8: dwait_vmcnt<8>(); break;
+    default: dwait_vmcnt<0>(); break;         // (more per tile: wait for all, still correct)
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(1024) void dattn_group_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -362,7 +393,7 @@ __global__ __launch_bounds__(1024) void dattn_group_kernel(
   constexpr int CH = D / 8;                   // 16-byte chunks per key row
   // LDS (sized at launch): K and V rows of one block [block][D] bf16, the G queries [G][D] and
   // weights [G][block] fp32
-  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  extern __shared__ __attribute__((aligned(1024))) char dsm[];
   const int G = Hq / Hkv;
   uint16_t* Ks = (uint16_t*)dsm;
   uint16_t* Vs = Ks + block * D;
@@ -372,7 +403,7 @@ __global__ __launch_bounds__(1024) void dattn_group_kernel(
   const int sp = (int)(w % splits);
   w /= splits;
   const int g = (int)(w % Hkv), b = (int)(w / Hkv);
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, NT = G * kWave;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int h = g * G + wave, bh = b * Hq + h;
   const int64_t L = lens[b];
   const int64_t rs = (int64_t)Hkv * D;
@@ -391,22 +422,56 @@ __global__ __launch_bounds__(1024) void dattn_group_kernel(
   const uint16_t* kb0 = kc + (int64_t)b * Lmax * rs + (int64_t)g * D;
   const uint16_t* vb0 = vc + (int64_t)b * Lmax * rs + (int64_t)g * D;
   const bool len_ok = L >= 1 && L <= Lmax;
+  // transfers: a tile is block*CH/64 wave instructions of 1 KiB; wave w issues ni of them
+  // (instructions w, w+G, ...; the last one repeated where a wave runs out)
+  const int nins = block * CH / kWave;
+  const int ni = (nins + G - 1) / G;
+  auto dma = [&](const uint16_t* src_rows, uint16_t* dst) {   // rows t0.. of a tile
+    const uint64_t src = (uint64_t)(uintptr_t)src_rows;
+    const uint32_t slo = __builtin_amdgcn_readfirstlane((uint32_t)src);
+    const uint32_t shi = __builtin_amdgcn_readfirstlane((uint32_t)(src >> 32));
+    const uint64_t sbase = ((uint64_t)shi << 32) | slo;
+    for (int x = 0; x < ni; ++x) {
+      int ins = wave + G * x;
+      ins = ins < nins ? ins : nins - 1;
+      const int chunk = ins * kWave + lane, r = chunk / CH, cc = chunk % CH;
+      const uint32_t voff = (uint32_t)((r * rs + 8 * cc) * 2);
+      const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(lds_void*)((char*)dst + ins * 1024));
+      uint32_t m0_saved;
+      asm volatile(
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(m0_saved)
+          : "s"(lds0), "v"(voff), "s"(sbase)
+          : "memory", "scc");
+    }
+  };
+  // the split's entries that name a block of the cache, in order
+  auto next_valid = [&](int e) -> int {       // (scalar loads: a vector load here would wait
+    for (; e < e1; ++e) {                     // for the transfers in flight)
+      const int j = row[__builtin_amdgcn_readfirstlane(e)];
+      if (j >= 0 && (int64_t)j * block < L) break;   // else an unused place or beyond the cache
+    }
+    return e;
+  };
   __syncthreads();
   float qv[8];
 #pragma unroll
   for (int x = 0; x < 8; ++x) qv[x] = qsm[wave * D + 8 * dg + x];
-  for (int e = e0; e < e1 && len_ok; ++e) {
-    const int j = row[e];
-    if (j < 0 || (int64_t)j * block >= L) continue;   // unused place or beyond the cache
-    const int64_t t0 = (int64_t)j * block;
+  int e = len_ok ? next_valid(e0) : e1;
+  if (e < e1) {
+    const int64_t t0 = (int64_t)row[e] * block;
+    dma(kb0 + t0 * rs, Ks);
+    dma(vb0 + t0 * rs, Vs);
+  }
+  while (e < e1) {
+    const int en = next_valid(e + 1);
+    const int64_t t0 = (int64_t)row[e] * block;
     const int nk = (int)(L - t0 < block ? L - t0 : block);   // own block: tokens < L
-    __syncthreads();                          // the previous block is done with Ks, Vs, ps
-    for (int ci = tid; ci < nk * CH; ci += NT) {
-      const int r = ci / CH, cc = ci % CH;
-      *(u32x4*)(Ks + r * D + 8 * cc) = *(const u32x4*)(kb0 + (t0 + r) * rs + 8 * cc);
-      *(u32x4*)(Vs + r * D + 8 * cc) = *(const u32x4*)(vb0 + (t0 + r) * rs + 8 * cc);
-    }
-    __syncthreads();
+    dwait_vmcnt_le(ni);                       // this wave's keys of block e (values may fly)
+    __syncthreads();                          // every wave's keys landed
     for (int t = kq; t < nk; t += KG) {
       const u32x4 kw = *(const u32x4*)(Ks + t * D + 8 * dg);
       float a = 0.f;
@@ -418,7 +483,8 @@ __global__ __launch_bounds__(1024) void dattn_group_kernel(
       a = group_sum<LG>(a);
       if (dg == 0) psm[wave * block + t] = a * c;       // exp2 domain
     }
-    __syncthreads();
+    __syncthreads();                          // scores written; every wave done with Ks
+    if (en < e1) dma(kb0 + (int64_t)row[en] * block * rs, Ks);
     float s[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -431,9 +497,8 @@ __global__ __launch_bounds__(1024) void dattn_group_kernel(
     const float alpha = __builtin_amdgcn_exp2f(m - mn);    // 0 on the first block
     m = mn;
     float lp = 0.f;
-    __syncthreads();                          // scores read before the weights replace them
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u) {             // (each wave reads and writes its own row)
       const int t = lane + 64 * u;
       const float p = t < nk ? __builtin_amdgcn_exp2f(s[u] - m) : 0.f;
       if (t < block) psm[wave * block + t] = p;
@@ -443,7 +508,8 @@ __global__ __launch_bounds__(1024) void dattn_group_kernel(
     l = l * alpha + lp;
 #pragma unroll
     for (int x = 0; x < 8; ++x) o[x] *= alpha;
-    __syncthreads();
+    if (en < e1) dwait_vmcnt_le(ni); else dwait_vmcnt<0>();   // values of block e
+    __syncthreads();                          // every wave's values landed, weights written
     for (int t = kq; t < nk; t += KG) {
       const u32x4 vw = *(const u32x4*)(Vs + t * D + 8 * dg);
       const float p = psm[wave * block + t];
@@ -453,6 +519,9 @@ __global__ __launch_bounds__(1024) void dattn_group_kernel(
         o[2 * x + 1] = __builtin_fmaf(p, bf16hi(vw[x]), o[2 * x + 1]);
       }
     }
+    __syncthreads();                          // every wave done with Vs and its weights
+    if (en < e1) dma(vb0 + (int64_t)row[en] * block * rs, Vs);
+    e = en;
   }
   // sum the key groups (lanes dg, dg + LG, ...)
 #pragma unroll
