@@ -49,6 +49,10 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
                                                         int64_t N, int D, int block,
                                                         float inv_block, bool pmax) {
   constexpr int E = Vec<KIND>::E;
+  // loads in flight per thread: an fp8 vector widens to 16 floats and the compiler converts
+  // all loads of a batch before adding them, so fp8 takes 4 at a time (121 registers, four
+  // waves per SIMD; 16 at a time cost 272 registers, one wave per SIMD)
+  constexpr int U = KIND == 2 ? 4 : kUnroll;
   const float init = pmax ? -__builtin_inff() : 0.f;
   extern __shared__ float red[];                       // [T][V*E] partial sums
   const PoolArgs a = blockIdx.y == 0 ? qa : ka;
@@ -73,16 +77,16 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
     if (grp < T) {
       const uint8_t* p = base + (int64_t)c * 16;
       int t = grp;
-      for (; t + (kUnroll - 1) * T < cnt; t += kUnroll * T) {     // kUnroll loads in flight
-        u32x4 w[kUnroll];
+      for (; t + (U - 1) * T < cnt; t += U * T) {     // U loads in flight
+        u32x4 w[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) w[u] = load16(p + (int64_t)(t + u * T) * row_bytes);
+        for (int u = 0; u < U; ++u) w[u] = load16(p + (int64_t)(t + u * T) * row_bytes);
         if (pmax) {
 #pragma unroll
-          for (int u = 0; u < kUnroll; ++u) Vec<KIND>::vmax(w[u], acc);
+          for (int u = 0; u < U; ++u) Vec<KIND>::vmax(w[u], acc);
         } else {
 #pragma unroll
-          for (int u = 0; u < kUnroll; ++u) Vec<KIND>::add(w[u], acc);
+          for (int u = 0; u < U; ++u) Vec<KIND>::add(w[u], acc);
         }
       }
       for (; t < cnt; t += T) fold<KIND>(pmax, load16(p + (int64_t)t * row_bytes), acc);
@@ -104,16 +108,16 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs qa, PoolArgs ka
       for (int e = 0; e < E; ++e) acc[e] = init;
       const uint8_t* p = base + (int64_t)c * 16;
       int t = 0;
-      for (; t + kUnroll - 1 < cnt; t += kUnroll) {
-        u32x4 w[kUnroll];
+      for (; t + U - 1 < cnt; t += U) {
+        u32x4 w[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) w[u] = load16(p + (int64_t)(t + u) * row_bytes);
+        for (int u = 0; u < U; ++u) w[u] = load16(p + (int64_t)(t + u) * row_bytes);
         if (pmax) {
 #pragma unroll
-          for (int u = 0; u < kUnroll; ++u) Vec<KIND>::vmax(w[u], acc);
+          for (int u = 0; u < U; ++u) Vec<KIND>::vmax(w[u], acc);
         } else {
 #pragma unroll
-          for (int u = 0; u < kUnroll; ++u) Vec<KIND>::add(w[u], acc);
+          for (int u = 0; u < U; ++u) Vec<KIND>::add(w[u], acc);
         }
       }
       for (; t < cnt; ++t) fold<KIND>(pmax, load16(p + (int64_t)t * row_bytes), acc);
