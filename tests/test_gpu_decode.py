@@ -92,6 +92,11 @@ GROUP_CASES = [
     (2, 64 * 1000, 8, 2, 128, 64, 76, [64000, 33333]),
     (1, 64 * 3000, 8, 1, 64, 64, 30, [192000]),
     (2, 64 * 40, 16, 1, 64, 64, 9, [2560, 700]),     # G = 16: the largest group of one work-group
+    # the tile transfers of the group kernel: 16 per wave per tile (more than its fixed waits
+    # name: the wait-for-all form), and G = 3 (the tile's 8 transfers do not split evenly, the
+    # last wave repeats one)
+    (2, 128 * 10, 4, 2, 128, 128, 4, [1280, 300]),
+    (2, 64 * 30, 6, 2, 64, 64, 6, [1920, 555]),
 ]
 
 
