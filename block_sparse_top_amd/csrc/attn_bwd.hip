@@ -56,30 +56,69 @@ __device__ __forceinline__ s16x4 ds_read_tr16(const char* lds_bytes) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_void*)(lds_bytes));
 }
 
-// Rows [row0, row0 + 64) of a [*, H, D] bf16 tensor (head offset folded into `base`) as an
-// LDS tile [64][D], swizzled; all NT threads of the work-group take part. The copy is split
-// into a load into registers (issued one step ahead, in flight during the products) and a
-// store into LDS.
+// vmcnt(0) only (expcnt and lgkmcnt left free), gfx9 s_waitcnt encoding
+__device__ __forceinline__ void wait_vmcnt0() {
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+}
+
+// One [64][D] bf16 tile moved from memory straight into LDS with global_load_lds_dwordx4
+// (lane l of an instruction fills bytes [16l, 16l+16) of a 1 KiB span): the chunk at
+// position p of tile row r is fetched from the row's chunk swz(r, p), which gives the
+// swizzled layout above. The waves of the work-group split the spans; the transfers come
+// from inline asm, so the waits before the tile is read are placed by hand.
 template <int D, int NT>
-struct TileRegs {
-  static constexpr int CH = D / 8;            // 16-byte chunks per row
-  static constexpr int X = kBlk * CH / NT;    // chunks per thread
-  u32x4 w[X];
-  __device__ __forceinline__ void load(const uint16_t* base, int64_t row0, int64_t rstride,
-                                       int tid) {
+struct TileDma {
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int SPW = kBlk * CH / 64 / (NT / kWave);   // spans per wave
+  static_assert(SPW == 4 || SPW == 8, "the transfer sequences issue 4 or 8 spans");
+  uint32_t goff[SPW];                                // source byte offsets in the tile
+  __device__ __forceinline__ void init(int64_t rstride, int tid) {
+    const int wave = tid / kWave, lane = tid % kWave;
 #pragma unroll
-    for (int x = 0; x < X; ++x) {
-      const int pos = x * NT + tid;
+    for (int x = 0; x < SPW; ++x) {
+      const int pos = (wave * SPW + x) * kWave + lane;
       const int r = pos / CH, c = pos % CH;
-      w[x] = *(const u32x4*)(base + (row0 + r) * rstride + 8 * c);
+      goff[x] = (uint32_t)((r * rstride + 8 * swz<D>(r, c)) * 2);
     }
   }
-  __device__ __forceinline__ void store(char* tile, int tid) const {
-#pragma unroll
-    for (int x = 0; x < X; ++x) {
-      const int pos = x * NT + tid;
-      const int r = pos / CH, c = pos % CH;
-      *(u32x4*)(tile + r * D * 2 + 16 * swz<D>(r, c)) = w[x];
+  // rows row0.. of a [*, H, D] tensor (head offset folded into base) into dst
+  __device__ __forceinline__ void issue(const uint16_t* base, int64_t row0, int64_t rstride,
+                                        char* dst, int tid) const {
+    const int wave = tid / kWave;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_void*)dst + wave * SPW * 1024);
+    const uint64_t sb = (uint64_t)(uintptr_t)(base + row0 * rstride);
+    const char* src = (const char*)(uintptr_t)(
+        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb) |
+        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32)) << 32));
+    uint32_t m0_saved;
+    if constexpr (SPW == 4) {
+      asm volatile(
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %6\n\t"
+          "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %6\n\t"
+          "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %6\n\t"
+          "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %6\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(m0_saved)
+          : "s"(lds0), "v"(goff[0]), "v"(goff[1]), "v"(goff[2]), "v"(goff[3]), "s"(src)
+          : "memory", "scc");
+    } else {
+      asm volatile(
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %10\n\t"
+          "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %10\n\t"
+          "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %10\n\t"
+          "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %10\n\t"
+          "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %10\n\t"
+          "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, %10\n\t"
+          "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %8, %10\n\t"
+          "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %9, %10\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(m0_saved)
+          : "s"(lds0), "v"(goff[0]), "v"(goff[1]), "v"(goff[2]), "v"(goff[3]), "v"(goff[4]),
+            "v"(goff[5]), "v"(goff[6]), "v"(goff[7]), "s"(src)
+          : "memory", "scc");
     }
   }
 };
@@ -226,8 +265,8 @@ __global__ __launch_bounds__(128) void dq_kernel(
     const float* __restrict__ dvec, float* __restrict__ dq, int64_t N, int Hq, int Hkv, int nb,
     int topk, float c, float scale, uint32_t total_tiles) {
   constexpr int NS = D / 16, NDT = D / 32;
-  __shared__ __attribute__((aligned(16))) char Kt[kBlk * D * 2];
-  __shared__ __attribute__((aligned(16))) char Vt[kBlk * D * 2];
+  __shared__ __attribute__((aligned(1024))) char Kt[2][kBlk * D * 2];   // two buffers each
+  __shared__ __attribute__((aligned(1024))) char Vt[2][kBlk * D * 2];
   const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
   const int G = Hq / Hkv;
   const int i = (int)(tile % nb);
@@ -264,27 +303,25 @@ __global__ __launch_bounds__(128) void dq_kernel(
   const uint16_t* vb0 = v + (int64_t)b * N * krs + (int64_t)g * D;
 
   // an out-of-range entry is never read (the forward gave its rows NaN): block 0 stands in
-  // and the step is skipped
-  TileRegs<D, 128> kr, vr;
-  int jn = myidx[0];
-  {
-    const int64_t r0 = (unsigned)jn < klim ? (int64_t)jn * kBlk : 0;
-    kr.load(kb0, r0, krs, tid);
-    vr.load(vb0, r0, krs, tid);
-  }
+  // and the step is skipped. The tiles of step t + 1 move into the other LDS buffers while
+  // step t is multiplied (one barrier per step).
+  TileDma<D, 128> tk;
+  tk.init(krs, tid);
+  auto fetch = [&](int jj, int buf) {
+    const int64_t r0 = (unsigned)jj < klim ? (int64_t)jj * kBlk : 0;
+    tk.issue(kb0, r0, krs, Kt[buf], tid);
+    tk.issue(vb0, r0, krs, Vt[buf], tid);
+  };
+  if (kcount > 0) fetch(myidx[0], 0);
   for (int t = 0; t < kcount; ++t) {
-    const int j = jn;
-    __syncthreads();                          // the previous step is done with the tiles
-    kr.store(Kt, tid);
-    vr.store(Vt, tid);
-    __syncthreads();
-    if (t + 1 < kcount) {                     // next tiles fly during this step's products
-      jn = myidx[t + 1];
-      const int64_t r0 = (unsigned)jn < klim ? (int64_t)jn * kBlk : 0;
-      kr.load(kb0, r0, krs, tid);
-      vr.load(vb0, r0, krs, tid);
-    }
+    const int j = myidx[t];
+    const int cur = t & 1;
+    wait_vmcnt0();                            // this wave's transfers of step t
+    __syncthreads();                          // every wave's landed; step t-1 done everywhere
+    if (t + 1 < kcount) fetch(myidx[t + 1], cur ^ 1);
     if ((unsigned)j >= klim) continue;        // uniform
+    const char* Kc = Kt[cur];
+    const char* Vc = Vt[cur];
     f32x16 st[2], dpt[2];                     // S^T and dP^T: rows = 64 keys, cols = queries
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -292,8 +329,8 @@ __global__ __launch_bounds__(128) void dq_kernel(
       for (int r = 0; r < 16; ++r) { st[kt][r] = 0.f; dpt[kt][r] = 0.f; }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        st[kt] = mfma(rows_operand<D>(Kt, kt, s, l32, half), qf[s], st[kt]);
-        dpt[kt] = mfma(rows_operand<D>(Vt, kt, s, l32, half), gf[s], dpt[kt]);
+        st[kt] = mfma(rows_operand<D>(Kc, kt, s, l32, half), qf[s], st[kt]);
+        dpt[kt] = mfma(rows_operand<D>(Vc, kt, s, l32, half), gf[s], dpt[kt]);
       }
     }
     // dS^T = P^T (dP^T - Dvec), P^T = exp2(c s - lse2); masked keys give 0
@@ -312,7 +349,7 @@ __global__ __launch_bounds__(128) void dq_kernel(
     for (int ps = 0; ps < 4; ++ps) {
       const bf16x8 bds = pack_step(dpt, ps);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma(trans_operand<D>(Kt, dt, ps, lane), bds, acc[dt]);
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma(trans_operand<D>(Kc, dt, ps, lane), bds, acc[dt]);
     }
   }
   // dQ = scale * (dQ^T)^T: lane holds d = 32dt + 8(r/4) + 4*half + r%4 of query qloc
@@ -339,10 +376,10 @@ __global__ __launch_bounds__(128) void dkv_kernel(
     float* __restrict__ dk, float* __restrict__ dv, int64_t N, int Hq, int Hkv, int nb,
     int topk, float c, float scale, uint32_t total_tiles) {
   constexpr int NS = D / 16, NDT = D / 32;
-  __shared__ __attribute__((aligned(16))) char Qt[kBlk * D * 2];
-  __shared__ __attribute__((aligned(16))) char Gt[kBlk * D * 2];   // dO tile
-  __shared__ __attribute__((aligned(16))) float l2s[kBlk];
-  __shared__ __attribute__((aligned(16))) float dds[kBlk];
+  __shared__ __attribute__((aligned(1024))) char Qt[2][kBlk * D * 2];   // two buffers each
+  __shared__ __attribute__((aligned(1024))) char Gt[2][kBlk * D * 2];   // dO tiles
+  __shared__ __attribute__((aligned(16))) float l2s[2][kBlk];
+  __shared__ __attribute__((aligned(16))) float dds[2][kBlk];
   const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
   const int j = (int)(tile % nb);
   const int bg = (int)(tile / nb);
@@ -368,34 +405,39 @@ __global__ __launch_bounds__(128) void dkv_kernel(
   const int32_t* off = offsets + (int64_t)bg * (nb + 1);
   const int32_t* seg = pairs + (int64_t)bg * G * nb * topk;
   const int p0 = off[j], p1 = off[j + 1];
-  // tiles of pair p + 1 are loaded into registers while pair p is multiplied; a pair value out
-  // of range (only possible for idx rows with repeated blocks) is skipped, pair 0 standing in
-  TileRegs<D, 128> qr, gr;
+  // the tiles of pair p + 1 move into the other LDS buffers while pair p is multiplied (one
+  // barrier per pair); a pair value out of range (only possible for idx rows with repeated
+  // blocks) is skipped, pair 0 standing in
+  TileDma<D, 128> tq;
+  tq.init(qrs, tid);
   float l2n = 0.f, ddn = 0.f;
-  auto fetch = [&](int p) {
+  auto fetch = [&](int p, int buf) {
     int row = seg[p];
     if ((unsigned)row >= (unsigned)(G * nb)) row = 0;
     const int h = g * G + row / nb, i = row % nb;
     const int64_t r0 = (int64_t)b * N + (int64_t)i * kBlk;
-    qr.load(q + (int64_t)h * D, r0, qrs, tid);
-    gr.load(dout + (int64_t)h * D, r0, qrs, tid);
+    tq.issue(q + (int64_t)h * D, r0, qrs, Qt[buf], tid);
+    tq.issue(dout + (int64_t)h * D, r0, qrs, Gt[buf], tid);
     if (tid < kBlk) {
       const int64_t rid = ((int64_t)b * Hq + h) * N + (int64_t)i * kBlk + tid;
       l2n = lse[rid] * kLog2e;
       ddn = dvec[rid];
     }
   };
-  if (p0 < p1) fetch(p0);
+  if (p0 < p1) fetch(p0, 0);
   for (int p = p0; p < p1; ++p) {
     const int row = seg[p];                   // hh * nb + i
-    __syncthreads();                          // the previous pair is done with the tiles
-    qr.store(Qt, tid);
-    gr.store(Gt, tid);
-    if (tid < kBlk) { l2s[tid] = l2n; dds[tid] = ddn; }
-    __syncthreads();
-    if (p + 1 < p1) fetch(p + 1);
+    const int cur = (p - p0) & 1;
+    wait_vmcnt0();                            // this wave's transfers and loads for pair p
+    if (tid < kBlk) { l2s[cur][tid] = l2n; dds[cur][tid] = ddn; }
+    __syncthreads();                          // every wave's landed; pair p-1 done everywhere
+    if (p + 1 < p1) fetch(p + 1, cur ^ 1);
     if ((unsigned)row >= (unsigned)(G * nb)) continue;   // uniform
     const int i = row % nb;
+    const char* Qc = Qt[cur];
+    const char* Gc = Gt[cur];
+    const float* l2c = l2s[cur];
+    const float* ddc = dds[cur];
     f32x16 sa[2], dpa[2];                     // S and dP: rows = 64 queries, cols = keys
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
@@ -403,8 +445,8 @@ __global__ __launch_bounds__(128) void dkv_kernel(
       for (int r = 0; r < 16; ++r) { sa[qt][r] = 0.f; dpa[qt][r] = 0.f; }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        sa[qt] = mfma(rows_operand<D>(Qt, qt, s, l32, half), kf[s], sa[qt]);
-        dpa[qt] = mfma(rows_operand<D>(Gt, qt, s, l32, half), vf[s], dpa[qt]);
+        sa[qt] = mfma(rows_operand<D>(Qc, qt, s, l32, half), kf[s], sa[qt]);
+        dpa[qt] = mfma(rows_operand<D>(Gc, qt, s, l32, half), vf[s], dpa[qt]);
       }
     }
     const bool own = CAUSAL && i == j;
@@ -414,7 +456,7 @@ __global__ __launch_bounds__(128) void dkv_kernel(
       for (int r4 = 0; r4 < 4; ++r4) {
         // registers 4*r4 .. 4*r4+3 hold rows q0 .. q0+3: one 16-byte read of each statistic
         const int q0 = 32 * qt + 8 * r4 + 4 * half;
-        const f32x4 l4 = *(const f32x4*)(l2s + q0), d4 = *(const f32x4*)(dds + q0);
+        const f32x4 l4 = *(const f32x4*)(l2c + q0), d4 = *(const f32x4*)(ddc + q0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = 4 * r4 + u;
@@ -430,8 +472,8 @@ __global__ __launch_bounds__(128) void dkv_kernel(
       const bf16x8 bp = pack_step(sa, ps), bs = pack_step(dpa, ps);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        dva[dt] = mfma(trans_operand<D>(Gt, dt, ps, lane), bp, dva[dt]);
-        dka[dt] = mfma(trans_operand<D>(Qt, dt, ps, lane), bs, dka[dt]);
+        dva[dt] = mfma(trans_operand<D>(Gc, dt, ps, lane), bp, dva[dt]);
+        dka[dt] = mfma(trans_operand<D>(Qc, dt, ps, lane), bs, dka[dt]);
       }
     }
   }
