@@ -265,8 +265,11 @@ __global__ __launch_bounds__(128) void dq_kernel(
     const float* __restrict__ dvec, float* __restrict__ dq, int64_t N, int Hq, int Hkv, int nb,
     int topk, float c, float scale, uint32_t total_tiles) {
   constexpr int NS = D / 16, NDT = D / 32;
-  __shared__ __attribute__((aligned(1024))) char Kt[2][kBlk * D * 2];   // two buffers each
-  __shared__ __attribute__((aligned(1024))) char Vt[2][kBlk * D * 2];
+  // D = 64: one V buffer (24 KiB of LDS per work-group: three waves per SIMD); D = 128: two
+  // (the single-buffer schedule needs more registers than two waves per SIMD allow there)
+  constexpr bool kOneV = D == 64;
+  __shared__ __attribute__((aligned(1024))) char Kt[2][kBlk * D * 2];
+  __shared__ __attribute__((aligned(1024))) char Vt[kOneV ? 1 : 2][kBlk * D * 2];
   const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
   const int G = Hq / Hkv;
   const int i = (int)(tile % nb);
@@ -303,25 +306,35 @@ __global__ __launch_bounds__(128) void dq_kernel(
   const uint16_t* vb0 = v + (int64_t)b * N * krs + (int64_t)g * D;
 
   // an out-of-range entry is never read (the forward gave its rows NaN): block 0 stands in
-  // and the step is skipped. The tiles of step t + 1 move into the other LDS buffers while
-  // step t is multiplied (one barrier per step).
+  // and the step is skipped. The K tile of step t + 1 moves into the other K buffer during
+  // the whole of step t; V, read only by the dP product, goes into the other V buffer too
+  // (D = 128) or into its single buffer once every wave has formed dP (D = 64).
   TileDma<D, 128> tk;
   tk.init(krs, tid);
-  auto fetch = [&](int jj, int buf) {
-    const int64_t r0 = (unsigned)jj < klim ? (int64_t)jj * kBlk : 0;
-    tk.issue(kb0, r0, krs, Kt[buf], tid);
-    tk.issue(vb0, r0, krs, Vt[buf], tid);
-  };
-  if (kcount > 0) fetch(myidx[0], 0);
+  auto row0 = [&](int jj) -> int64_t { return (unsigned)jj < klim ? (int64_t)jj * kBlk : 0; };
+  if (kcount > 0) {
+    tk.issue(kb0, row0(myidx[0]), krs, Kt[0], tid);
+    tk.issue(vb0, row0(myidx[0]), krs, Vt[0], tid);
+  }
   for (int t = 0; t < kcount; ++t) {
     const int j = myidx[t];
     const int cur = t & 1;
+    const bool more = t + 1 < kcount;
     wait_vmcnt0();                            // this wave's transfers of step t
     __syncthreads();                          // every wave's landed; step t-1 done everywhere
-    if (t + 1 < kcount) fetch(myidx[t + 1], cur ^ 1);
-    if ((unsigned)j >= klim) continue;        // uniform
+    if (more) {
+      tk.issue(kb0, row0(myidx[t + 1]), krs, Kt[cur ^ 1], tid);
+      if (!kOneV) tk.issue(vb0, row0(myidx[t + 1]), krs, Vt[kOneV ? 0 : cur ^ 1], tid);
+    }
     const char* Kc = Kt[cur];
-    const char* Vc = Vt[cur];
+    const char* Vc = Vt[kOneV ? 0 : cur];
+    if ((unsigned)j >= klim) {                // uniform: the next V tile still moves
+      if (kOneV) {
+        __syncthreads();
+        if (more) tk.issue(vb0, row0(myidx[t + 1]), krs, Vt[0], tid);
+      }
+      continue;
+    }
     f32x16 st[2], dpt[2];                     // S^T and dP^T: rows = 64 keys, cols = queries
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -332,6 +345,10 @@ __global__ __launch_bounds__(128) void dq_kernel(
         st[kt] = mfma(rows_operand<D>(Kc, kt, s, l32, half), qf[s], st[kt]);
         dpt[kt] = mfma(rows_operand<D>(Vc, kt, s, l32, half), gf[s], dpt[kt]);
       }
+    }
+    if (kOneV) {
+      __syncthreads();                        // every wave has read V(t)
+      if (more) tk.issue(vb0, row0(myidx[t + 1]), krs, Vt[0], tid);
     }
     // dS^T = P^T (dP^T - Dvec), P^T = exp2(c s - lse2); masked keys give 0
     const bool own = CAUSAL && j == i;
