@@ -10,7 +10,6 @@
 //   dQ_i = scale * dS K_U,  dK_U += scale * dS^T Q_i.
 //
 // Kernels:
-//   rowdot_kernel   Dvec[b,h,t] = sum_d dO * O (fp32), one thread per row.
 //   index_kernel    per (batch, KV head): for every key block j the list of (query head of
 //                   the group, query block) pairs that selected it, in ascending pair order
 //                   (LDS counts, a scan, then the rows in order), so the key-side sums run in
@@ -19,6 +18,8 @@
 //                   dP^T = V dO^T on bf16 MFMA (A = K or V rows from LDS, B = Q^T or dO^T in
 //                   registers), P^T and dS^T in fp32, dQ^T += K^T dS^T (A = K^T by LDS
 //                   transpose reads, B = dS^T rounded to bf16 straight from the accumulators).
+//                   It also forms Dvec[b,h,t] = sum_d dO * O (fp32) of its rows and stores it
+//                   for dkv_kernel.
 //   dkv_kernel      key-major: one work-group per (batch, KV head, key block) keeps K and V rows
 //                   of its keys in registers (B operands) and walks its pair list: S = Q K^T,
 //                   dP = dO V^T (A = Q or dO rows from LDS), P and dS in fp32, then
@@ -162,28 +163,6 @@ __device__ __forceinline__ bf16x8 pack_step(const f32x16 (&acc)[2], int ps) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// ---------------------------------------------------------------- Dvec
-template <int D>
-__global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict__ out,
-                                                     const uint16_t* __restrict__ dout,
-                                                     float* __restrict__ dvec, int64_t rows,
-                                                     int64_t N, int Hq) {
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (b, t, h) row
-  if (r >= rows) return;
-  const uint16_t* o = out + r * D;
-  const uint16_t* g = dout + r * D;
-  float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const u32x4 a = *(const u32x4*)(o + 8 * c), x = *(const u32x4*)(g + 8 * c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc += bf16lo(a[e]) * bf16lo(x[e]) + bf16hi(a[e]) * bf16hi(x[e]);
-  }
-  const int h = (int)(r % Hq);
-  const int64_t bt = r / Hq, b = bt / N, t = bt % N;
-  dvec[(b * Hq + h) * N + t] = acc;
-}
 
 // ---------------------------------------------------------------- inverted index
 constexpr int kIdxThreads = 256;
@@ -261,9 +240,9 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(128) void dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const int32_t* __restrict__ idx, const float* __restrict__ lse,
-    const float* __restrict__ dvec, float* __restrict__ dq, int64_t N, int Hq, int Hkv, int nb,
-    int topk, float c, float scale, uint32_t total_tiles) {
+    const uint16_t* __restrict__ out, const int32_t* __restrict__ idx,
+    const float* __restrict__ lse, float* __restrict__ dvec, float* __restrict__ dq, int64_t N,
+    int Hq, int Hkv, int nb, int topk, float c, float scale, uint32_t total_tiles) {
   constexpr int NS = D / 16, NDT = D / 32;
   // D = 64: one V buffer (24 KiB of LDS per work-group: three waves per SIMD); D = 128: two
   // (the single-buffer schedule needs more registers than two waves per SIMD allow there)
@@ -293,7 +272,17 @@ __global__ __launch_bounds__(128) void dq_kernel(
   }
   const int64_t rowid = ((int64_t)b * Hq + h) * N + (int64_t)i * kBlk + qloc;
   const float l2 = lse[rowid] * kLog2e;       // log2-sum-exp of the row
-  const float dd = dvec[rowid];
+  // Dvec of the row, rowsum(dO * O) in fp32: the two lanes of the row take the same 8-element
+  // chunks as their dO operands; stored for dkv_kernel, which runs after this kernel
+  float ddp = 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const bf16x8 o8 = row_chunk(out + qrow * qrs + (int64_t)h * D, s, half);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ddp = __builtin_fmaf((float)gf[s][e], (float)o8[e], ddp);
+  }
+  const float dd = ddp + __shfl_xor(ddp, 32);
+  if (half == 0) dvec[rowid] = dd;
   f32x16 acc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
@@ -519,20 +508,15 @@ hipError_t launch_bwd(int64_t B, int64_t N, int Hq, int Hkv, int topk, const voi
                       hipStream_t stream) {
   const int nb = (int)(N / kBlk);
   const float c = (float)((double)scale * 1.4426950408889634);
-  const int64_t rows = B * N * Hq;
-  rowdot_kernel<D><<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
-      (const uint16_t*)out, (const uint16_t*)dout, dvec, rows, N, Hq);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const size_t lds = (size_t)(2 * nb + 1) * sizeof(int);
   index_kernel<<<(unsigned)(B * Hkv), kIdxThreads, lds, stream>>>(idx, offsets, pairs, Hq, Hkv,
                                                                   nb, topk, CAUSAL);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t tq = (uint32_t)(B * Hq * nb);
   dq_kernel<D, CAUSAL><<<tq, 128, 0, stream>>>(
-      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, idx,
-      lse, dvec, dq, N, Hq, Hkv, nb, topk, c, scale, tq);
+      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
+      (const uint16_t*)out, idx, lse, dvec, dq, N, Hq, Hkv, nb, topk, c, scale, tq);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t tk = (uint32_t)(B * Hkv * nb);
