@@ -398,7 +398,7 @@ def main():
     tokens = w.B * w.N
     value = tokens / (ms_per_step / 1e3)
 
-    # The survey's timing protocol, after the timed region (reported beside it): per call,
+    # A second timing protocol, after the timed region (reported beside it): per call,
     # repeats of up to 50 launches, the median over 5 repeats; each selection launch follows a
     # 512 MB write that evicts the 256 MB MALL (the write is outside the events).
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -448,7 +448,7 @@ def main():
     achieved = flops / (fwd_ms / 1e3) / 1e12
     peak = PEAK[w.dtype]
     ebytes = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
-    # The selection's algorithmic bytes as the survey counts them: q and k read once, the
+    # The selection's algorithmic bytes: q and k read once, the
     # pooled blocks written once, idx written; where the score matrix goes through HBM
     # (more than 1024 blocks) also its write and read and the pooled blocks' read by the
     # score product. ("moved": what the kernels move on top of that, e.g. the fused kernel
