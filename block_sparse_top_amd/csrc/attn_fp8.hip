@@ -191,6 +191,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(BLK == 
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m = -__builtin_inff();                // reference (exp2 domain) of this lane's row
   float lsum = 0.f;
+  const int xaddr = (lane ^ 32) << 2;          // ds_bpermute address of the partner lane
 
   if (OVL) mark_selected(chosen, myidx, kcount, nkb, tid, C::NT);
   int kb_cur = myidx[0];
@@ -256,7 +257,8 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(BLK == 
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kt][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
+    mt = fmaxf(mt, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                       xaddr, __builtin_bit_cast(int, mt)))) * c;
     if (__ballot(mt > m + kGrow)) {
       const float m_new = fmaxf(m, mt);
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // 0 on the first block
@@ -269,6 +271,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(BLK == 
     }
     const float mb = m - kBias;
     i32x8 pb[C::NKS];
+    float sa0 = -0.f, sa1 = -0.f;               // two add chains for the step's weights
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks)
 #pragma unroll
@@ -276,14 +279,17 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(BLK == 
         const f32x16& sa = sacc[2 * ks + (w >> 2)];
         float p[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 4; ++u)
           p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[4 * (w & 3) + u], c, -mb));
-          lsum += p[u];
-        }
-        int dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        sa0 += p[0] + p[2];
+        sa1 += p[1] + p[3];
+        // the first conversion writes the low half and the second the high half, so the
+        // register's earlier contents (here p[0]'s bits, which saves a move) do not matter
+        int dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __builtin_bit_cast(int, p[0]), false);
         dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], dw, true);
         pb[ks][w] = dw;
       }
+    lsum += sa0 + sa1;
 
     if (more) wait_vmcnt<C::DMA>(); else wait_vmcnt<0>();
     if (C::NW > 1) __syncthreads();
