@@ -305,9 +305,11 @@ __global__ __launch_bounds__(128) void dq_kernel(
     tk.issue(kb0, row0(myidx[0]), krs, Kt[0], tid);
     tk.issue(vb0, row0(myidx[0]), krs, Vt[0], tid);
   }
-  for (int t = 0; t < kcount; ++t) {
+  // one step; the buffer index is a compile-time constant (the loop below takes steps two at
+  // a time), so the LDS read addresses stay fixed and the buffer goes into the offset field
+  auto kv_step = [&](int t, auto buf) {
+    constexpr int cur = decltype(buf)::value;
     const int j = myidx[t];
-    const int cur = t & 1;
     const bool more = t + 1 < kcount;
     wait_vmcnt0();                            // this wave's transfers of step t
     __syncthreads();                          // every wave's landed; step t-1 done everywhere
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(128) void dq_kernel(
         __syncthreads();
         if (more) tk.issue(vb0, row0(myidx[t + 1]), krs, Vt[0], tid);
       }
-      continue;
+      return;
     }
     f32x16 st[2], dpt[2];                     // S^T and dP^T: rows = 64 keys, cols = queries
 #pragma unroll
@@ -357,6 +359,10 @@ __global__ __launch_bounds__(128) void dq_kernel(
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) acc[dt] = mfma(trans_operand<D>(Kc, dt, ps, lane), bds, acc[dt]);
     }
+  };
+  for (int t = 0; t < kcount; t += 2) {
+    kv_step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < kcount) kv_step(t + 1, std::integral_constant<int, 1>{});
   }
   // dQ = scale * (dQ^T)^T: lane holds d = 32dt + 8(r/4) + 4*half + r%4 of query qloc
   float* drow = dq + qrow * qrs + (int64_t)h * D;
@@ -431,14 +437,16 @@ __global__ __launch_bounds__(128) void dkv_kernel(
     }
   };
   if (p0 < p1) fetch(p0, 0);
-  for (int p = p0; p < p1; ++p) {
+  // one pair; the buffer index is a compile-time constant (the loop below takes pairs two at a
+  // time), so the LDS read addresses stay fixed and the buffer goes into the offset field
+  auto pair_step = [&](int p, auto buf) {
+    constexpr int cur = decltype(buf)::value;
     const int row = seg[p];                   // hh * nb + i
-    const int cur = (p - p0) & 1;
     wait_vmcnt0();                            // this wave's transfers and loads for pair p
     if (tid < kBlk) { l2s[cur][tid] = l2n; dds[cur][tid] = ddn; }
     __syncthreads();                          // every wave's landed; pair p-1 done everywhere
     if (p + 1 < p1) fetch(p + 1, cur ^ 1);
-    if ((unsigned)row >= (unsigned)(G * nb)) continue;   // uniform
+    if ((unsigned)row >= (unsigned)(G * nb)) return;     // uniform
     const int i = row % nb;
     const char* Qc = Qt[cur];
     const char* Gc = Gt[cur];
@@ -482,6 +490,10 @@ __global__ __launch_bounds__(128) void dkv_kernel(
         dka[dt] = mfma(trans_operand<D>(Qc, dt, ps, lane), bs, dka[dt]);
       }
     }
+  };
+  for (int p = p0; p < p1; p += 2) {
+    pair_step(p, std::integral_constant<int, 0>{});
+    if (p + 1 < p1) pair_step(p + 1, std::integral_constant<int, 1>{});
   }
   float* krow_dk = dk + krow * krs + (int64_t)g * D;
   float* krow_dv = dv + krow * krs + (int64_t)g * D;
