@@ -75,6 +75,7 @@ constexpr float kSumLo = 1.0f / 18446744073709551616.0f;   // 2^-64
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const char lds_char;
 typedef __attribute__((address_space(1))) const void global_cvoid;
 
 // R query rows per work-group, KU keys per step (one K and one V tile in LDS)
@@ -111,9 +112,9 @@ __device__ __forceinline__ int swz(int r, int c) {
   else return c ^ (4 * (r & 3) + ((r >> 2) & 3));
 }
 
-__device__ __forceinline__ s16x4 ds_read_tr16(const char* lds_bytes) {
+__device__ __forceinline__ s16x4 ds_read_tr16(const lds_char* lds_bytes) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_void*)(lds_bytes));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_bytes));
 }
 
 // A work-group takes R rows of a query block of SB tokens (R = SB, or R = 64: SB / R
@@ -203,9 +204,12 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
   // read; the waits below are placed by hand (each wave issues exactly DMA transfers per tile
   // and no other vector-memory instruction inside the loop). M0 (the LDS destination) is
   // saved and restored around them.
-  auto dma = [&](const char* src_base_any, char* dst) {
-    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(lds_void*)dst + wave * C::DMA * 1024);
+  // LDS byte addresses of the tile buffers, taken once from the arrays themselves (the loop
+  // works with these and with LDS-typed pointers only, no generic-pointer casts)
+  const uint32_t kl_addr = (uint32_t)(uintptr_t)(lds_void*)&Kl[0][0];
+  const uint32_t vl_addr = (uint32_t)(uintptr_t)(lds_void*)&Vl[0][0];
+  auto dma = [&](const char* src_base_any, uint32_t dst_lds) {
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(dst_lds + wave * C::DMA * 1024);
     // the source base is the same in every lane; readfirstlane keeps it in scalar registers
     // where the compiler cannot prove that (the asm operand below must be an SGPR pair)
     const uint64_t sb = (uint64_t)(uintptr_t)src_base_any;
@@ -293,11 +297,14 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
     int skip_cur = skip_of(kb_cur);
     {
       const int64_t tb = tile_base(kb_cur, 0);
-      dma(kbase0 + tb, Kl[0]);
-      dma(vbase0 + tb, Vl[0]);
+      dma(kbase0 + tb, kl_addr);
+      dma(vbase0 + tb, vl_addr);
     }
 
-    for (int t = 0; t < kcount * UN; ++t) {     // steps: UN per selected block
+    // one step; with two buffers their index is a compile-time constant (the loop below takes
+    // steps two at a time), so the LDS read addresses stay fixed and the buffer goes into the
+    // offset field
+    auto step = [&](int t, auto buf) {
       const bool more = t + 1 < kcount * UN;
       const int kb_next = more ? myidx[(t + 1) / UN] : 0;
       const int u_next = (t + 1) % UN;
@@ -305,15 +312,17 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
       const int skip_next = OVL && more ? skip_of(kb_next) : 0;
 
       // ---- K(t): wait for this wave's share (V(t) may still fly), then the whole work-group
-      const int cur = NBUF > 1 ? (t & 1) : 0;
+      int cur = 0;                              // run-time index: D = 64 with two buffers
+      if constexpr (std::is_same_v<decltype(buf), int>) cur = NBUF > 1 ? (t & 1) : 0;
+      else cur = decltype(buf)::value;
       const char* Kc = Kl[cur];
-      const char* Vc = Vl[cur];
+      lds_char* Vc = (lds_char*)(uintptr_t)(vl_addr + cur * C::TILE);
       if constexpr (NBUF > 1) {
         wait_vmcnt<0>();                       // this wave's share of step t's tiles
         __syncthreads();                       // every share landed; step t-1 read everywhere
         if (more) {
-          dma(kbase0 + tb_next, Kl[cur ^ 1]);
-          dma(vbase0 + tb_next, Vl[cur ^ 1]);
+          dma(kbase0 + tb_next, kl_addr + (cur ^ 1) * C::TILE);
+          dma(vbase0 + tb_next, vl_addr + (cur ^ 1) * C::TILE);
         }
       } else {
         wait_vmcnt<C::DMA>();                  // K(t) (V(t) may still fly)
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
       if constexpr (NBUF == 1) {
         wait_lgkmcnt0();
         if (C::NW > 1) __syncthreads();        // every wave's K(t) reads done
-        if (more) dma(kbase0 + tb_next, Kl[0]);
+        if (more) dma(kbase0 + tb_next, kl_addr);
       }
 
       // ---- S^T = K Q^T
@@ -384,7 +393,7 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
       uint32_t pw[C::QC][C::NPS][4];
       float bsum[C::QC];
       auto weights = [&](int qc) {
-        float sa = 0.f, sb = 0.f;                // two add chains
+        float sa = -0.f, sb = -0.f;              // two add chains (x + -0 folds to x)
 #pragma unroll
         for (int s = 0; s < C::NPS; ++s)
 #pragma unroll
@@ -441,14 +450,14 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
       for (int s = 0; s < C::NPS; ++s)
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) {
-          const char* p = Vc + (16 * s) * D * 2;
+          lds_char* p = Vc + (16 * s) * D * 2;
           const s16x4 a8[2] = {ds_read_tr16(p + voff[dt]), ds_read_tr16(p + voff8[dt])};
           va[s][dt] = __builtin_bit_cast(bf16x8, a8);
         }
       if constexpr (NBUF == 1) {
         wait_lgkmcnt0();                       // V(t) read before V(t+1) overwrites it
         if (C::NW > 1) __syncthreads();
-        if (more) dma(vbase0 + tb_next, Vl[0]);
+        if (more) dma(vbase0 + tb_next, vl_addr);
       }
 
       // ---- O^T += V^T P^T
@@ -466,6 +475,14 @@ __global__ __launch_bounds__(R / (D == 64 ? 64 : 32) * 64) void attn_bf16_kernel
       kb_cur = kb_next;
       u_cur = u_next;
       if (OVL) skip_cur = skip_next;
+    };
+    if constexpr (NBUF > 1 && D == 128 && !OVL) {   // (with OVL it would need > 256 registers)
+      for (int t = 0; t < kcount * UN; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < kcount * UN) step(t + 1, std::integral_constant<int, 1>{});
+      }
+    } else {
+      for (int t = 0; t < kcount * UN; ++t) step(t, -1);
     }
     return flagged;
   };
