@@ -391,7 +391,7 @@ __global__ __launch_bounds__(128) void dkv_kernel(
   __shared__ __attribute__((aligned(1024))) char Qt[2][kBlk * D * 2];   // two buffers each
   __shared__ __attribute__((aligned(1024))) char Gt[2][kBlk * D * 2];   // dO tiles
   __shared__ __attribute__((aligned(16))) float l2s[2][kBlk];
-  __shared__ __attribute__((aligned(16))) float dds[2][kBlk];
+  __shared__ __attribute__((aligned(16))) float dds[2][kBlk];      // -Dvec of the rows
   const uint32_t tile = xcd_remap(blockIdx.x, total_tiles);
   const int j = (int)(tile % nb);
   const int bg = (int)(tile / nb);
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(128) void dkv_kernel(
     constexpr int cur = decltype(buf)::value;
     const int row = seg[p];                   // hh * nb + i
     wait_vmcnt0();                            // this wave's transfers and loads for pair p
-    if (tid < kBlk) { l2s[cur][tid] = l2n; dds[cur][tid] = ddn; }
+    if (tid < kBlk) { l2s[cur][tid] = l2n; dds[cur][tid] = -ddn; }
     __syncthreads();                          // every wave's landed; pair p-1 done everywhere
     if (p + 1 < p1) fetch(p + 1, cur ^ 1);
     if ((unsigned)row >= (unsigned)(G * nb)) return;     // uniform
@@ -452,11 +452,18 @@ __global__ __launch_bounds__(128) void dkv_kernel(
     const char* Gc = Gt[cur];
     const float* l2c = l2s[cur];
     const float* ddc = dds[cur];
-    f32x16 sa[2], dpa[2];                     // S and dP: rows = 64 queries, cols = keys
+    // S and dP: rows = 64 queries, cols = keys. The dP accumulators start at -Dvec of their
+    // rows (registers 4*r4 .. 4*r4+3 hold rows q0 .. q0+3: one 16-byte read per 4 rows), so the
+    // products leave dP - Dvec in them
+    f32x16 sa[2], dpa[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { sa[qt][r] = 0.f; dpa[qt][r] = 0.f; }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 d4 = *(const f32x4*)(ddc + 32 * qt + 8 * r4 + 4 * half);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { sa[qt][4 * r4 + u] = 0.f; dpa[qt][4 * r4 + u] = d4[u]; }
+      }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         sa[qt] = mfma(rows_operand<D>(Qc, qt, s, l32, half), kf[s], sa[qt]);
@@ -468,16 +475,15 @@ __global__ __launch_bounds__(128) void dkv_kernel(
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        // registers 4*r4 .. 4*r4+3 hold rows q0 .. q0+3: one 16-byte read of each statistic
         const int q0 = 32 * qt + 8 * r4 + 4 * half;
-        const f32x4 l4 = *(const f32x4*)(l2c + q0), d4 = *(const f32x4*)(ddc + q0);
+        const f32x4 l4 = *(const f32x4*)(l2c + q0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = 4 * r4 + u;
           float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[qt][r], c, -l4[u]));
           if (own && kloc > q0 + u) pp = 0.f;
           sa[qt][r] = pp;                                 // P
-          dpa[qt][r] = pp * (dpa[qt][r] - d4[u]);         // dS
+          dpa[qt][r] = pp * dpa[qt][r];                   // dS = P (dP - Dvec)
         }
       }
     // dV^T += dO^T P, dK^T += Q^T dS (k-steps over the 64 queries)
