@@ -190,9 +190,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(BLK == 
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
   float m = -__builtin_inff();                // reference (exp2 domain) of this lane's row
-  float mg = m + kGrow, mb = m - kBias;        // the reference moves above mg; weights exp2(z - mb)
   float lsum = 0.f;
-  const int xaddr = (lane ^ 32) << 2;          // ds_bpermute address of the partner lane
 
   if (OVL) mark_selected(chosen, myidx, kcount, nkb, tid, C::NT);
   int kb_cur = myidx[0];
@@ -252,21 +250,14 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(BLK == 
         }
     }
 
-    // reference: follow the row max (lane pair l, l^32 shares one row). Two max chains; the
-    // IEEE maximum (three-input v_maximum3_f32) takes the accumulators without the quieting
-    // moves fmaxf needs (a NaN score gives a NaN output either way).
-    float mx0 = sacc[0][0], mx1 = sacc[1][0];
+    // reference: follow the row max (lane pair l, l^32 shares one row)
+    float mt = sacc[0][0];
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (kt & 1) mx1 = __builtin_elementwise_maximum(mx1, sacc[kt][r]);
-        else mx0 = __builtin_elementwise_maximum(mx0, sacc[kt][r]);
-      }
-    float mt = __builtin_elementwise_maximum(mx0, mx1);
-    mt = __builtin_elementwise_maximum(mt, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                               xaddr, __builtin_bit_cast(int, mt)))) * c;
-    if (__ballot(mt > mg)) {
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kt][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
+    if (__ballot(mt > m + kGrow)) {
       const float m_new = fmaxf(m, mt);
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // 0 on the first block
       lsum *= alpha;
@@ -275,11 +266,9 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(BLK == 
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
       m = m_new;
-      mg = m + kGrow;
-      mb = m - kBias;
     }
+    const float mb = m - kBias;
     i32x8 pb[C::NKS];
-    float sa0 = -0.f, sa1 = -0.f;               // two add chains for the step's weights
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks)
 #pragma unroll
@@ -287,17 +276,14 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(BLK == 
         const f32x16& sa = sacc[2 * ks + (w >> 2)];
         float p[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 4; ++u) {
           p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[4 * (w & 3) + u], c, -mb));
-        sa0 += p[0] + p[2];
-        sa1 += p[1] + p[3];
-        // the first conversion writes the low half and the second the high half, so the
-        // register's earlier contents (here p[0]'s bits, which saves a move) do not matter
-        int dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __builtin_bit_cast(int, p[0]), false);
+          lsum += p[u];
+        }
+        int dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
         dw = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], dw, true);
         pb[ks][w] = dw;
       }
-    lsum += sa0 + sa1;
 
     if (more) wait_vmcnt<C::DMA>(); else wait_vmcnt<0>();
     if (C::NW > 1) __syncthreads();
