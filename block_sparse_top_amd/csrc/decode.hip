@@ -593,15 +593,47 @@ hipError_t launch_dselect(const void* q, const float* kbar, const int32_t* lens,
 
 }  // namespace
 
+// The most splits a decode step uses (the workspace is sized for it): up to 8192 waves of the
+// per-head kernel, at most 64, at most topk. The launch picks fewer (launch_splits below).
 int decode_splits(int64_t B, int Hq, int topk) {
   const int64_t heads = B * Hq;
-  int64_t s = (8192 + heads - 1) / heads;     // aim at >= 8192 waves (8 per SIMD): each
-                                              // wave's blocks are a chain of dependent loads
+  int64_t s = (8192 + heads - 1) / heads;
   if (s > topk) s = topk;
   if (s < 1) s = 1;
   if (s > 64) s = 64;
   return (int)s;
 }
+
+namespace {
+
+// Splits of each head's (or KV head's) selected blocks for the attention pass. Every wave's
+// blocks are a chain of dependent tile loads, and the step is bound by HBM: about 16 waves
+// per CU in flight saturate the reads, and a second round of work-groups adds a whole chain
+// of latency, so the launch aims at 16 waves per CU and never at more work-groups than the
+// chip holds at once (occupancy query). Measured on 32 sequences x 32768 cached tokens,
+// 32/8 heads, 76 blocks: per-head kernel 2, 3, 4, 5, 6, 8 splits 0.561, 0.466, 0.444, 0.455,
+// 0.539, 0.476 ms; group kernel (4 waves per work-group, 4 resident per CU) 3, 4, 5, 8 splits
+// 0.188, 0.174, 0.205, 0.182 ms: both best at 16 waves per CU.
+hipError_t launch_splits(int64_t units, int waves_per_unit, const void* fn, int threads,
+                         size_t lds, int max_splits, int* splits) {
+  int dev = 0, ncu = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds);
+  if (e != hipSuccess) return e;
+  if (units < 1) units = 1;
+  int64_t s = (int64_t)16 * ncu / (units * waves_per_unit);          // 16 waves per CU
+  const int64_t fill = (int64_t)ncu * (per_cu > 0 ? per_cu : 1) / units;   // one round
+  if (s > fill) s = fill;
+  if (s > max_splits) s = max_splits;
+  if (s < 1) s = 1;
+  *splits = (int)s;
+  return hipSuccess;
+}
+
+}  // namespace
 
 size_t decode_workspace_bytes(int64_t B, int Hq, int D, int topk) {
   return (size_t)B * Hq * decode_splits(B, Hq, topk) * (D + 2) * sizeof(float);
@@ -647,22 +679,8 @@ hipError_t launch_decode(int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int bl
           hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (ea != hipSuccess) return ea;
     }
-    // Splits: as many work-groups as the chip holds at once, no more. Each work-group's blocks
-    // are a chain of dependent tile transfers, so a second round of work-groups adds a whole
-    // chain of latency (measured on 32 sequences x 8 KV heads, 1024 resident work-groups:
-    // 3, 4, 5 and 8 splits took 0.188, 0.174, 0.205 and 0.182 ms). Never more than the
-    // per-head count, for which the workspace is sized.
-    int dev = 0, ncu = 0, per_cu = 0;
-    e = hipGetDevice(&dev);
+    e = launch_splits(B * Hkv, G, fn, G * 64, lds, splits, &splits);
     if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, G * 64, lds);
-    if (e != hipSuccess) return e;
-    const int64_t resident = (int64_t)ncu * (per_cu > 0 ? per_cu : 1);
-    const int64_t fill = resident / (B * Hkv);
-    if (fill >= 1 && fill < splits) splits = (int)fill;
-    else if (fill < 1) splits = 1;
     const unsigned groups = (unsigned)(B * Hkv * splits);
     if (D == 64)
       dattn_group_kernel<64><<<groups, G * 64, lds, stream>>>(
@@ -672,14 +690,19 @@ hipError_t launch_decode(int64_t B, int64_t Lmax, int Hq, int Hkv, int D, int bl
       dattn_group_kernel<128><<<groups, G * 64, lds, stream>>>(
           (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, idx, lens,
           part, Lmax, Hq, Hkv, block, topk, splits, c);
-  } else if (D == 64) {
-    dattn_kernel<64><<<heads * splits, 64, 0, stream>>>(
-        (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, idx, lens, part,
-        Lmax, Hq, Hkv, block, topk, splits, c);
   } else {
-    dattn_kernel<128><<<heads * splits, 64, 0, stream>>>(
-        (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, idx, lens, part,
-        Lmax, Hq, Hkv, block, topk, splits, c);
+    const void* fn = D == 64 ? reinterpret_cast<const void*>(&dattn_kernel<64>)
+                             : reinterpret_cast<const void*>(&dattn_kernel<128>);
+    e = launch_splits(B * Hq, 1, fn, 64, 0, splits, &splits);
+    if (e != hipSuccess) return e;
+    if (D == 64)
+      dattn_kernel<64><<<heads * splits, 64, 0, stream>>>(
+          (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, idx, lens,
+          part, Lmax, Hq, Hkv, block, topk, splits, c);
+    else
+      dattn_kernel<128><<<heads * splits, 64, 0, stream>>>(
+          (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache, idx, lens,
+          part, Lmax, Hq, Hkv, block, topk, splits, c);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
