@@ -56,6 +56,9 @@ CASES = [
     (1, 64 * 2000, 4, 2, 64, 64, 50, [128000]),
     (1, 64 * 3000, 2, 1, 64, 64, 30, [192000]),
     (1, 64 * 8192, 2, 1, 64, 64, 40, [524288]),
+    # many sequences: 128 x 32 heads = 4096 one-wave heads, where the launch gives each head
+    # one split (the split rule's lower clamp)
+    (128, 64 * 8, 32, 8, 64, 64, 3, [1 + (37 * i) % 512 for i in range(127)] + [512]),
 ]
 
 
@@ -97,6 +100,8 @@ GROUP_CASES = [
     # last wave repeats one)
     (2, 128 * 10, 4, 2, 128, 128, 4, [1280, 300]),
     (2, 64 * 30, 6, 2, 64, 64, 6, [1920, 555]),
+    # 128 sequences x 8 KV heads = 1024 four-wave work-groups, one split each
+    (128, 64 * 8, 32, 8, 64, 64, 3, [1 + (37 * i) % 512 for i in range(127)] + [512]),
 ]
 
 
