@@ -22,7 +22,7 @@ sys.path.insert(0, ROOT)
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}        # dense TFLOP/s, MI355X
 HBM_PEAK_GBS = 8000.0
 METRIC = "tokens/sec + % bf16 MFMA peak, block-sparse attn N=8192 H=16 D=64 top-30%"
-ATTN_SOURCE = os.path.join(ROOT, "block_sparse_top_amd", "csrc", "attn_bf16.hip")
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_top_amd", "csrc", "attn_bf16_kernel.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_sparseformer_n8192_traffic.txt")
 
 

@@ -18,8 +18,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbsattn.so")
-SOURCES = ["api.hip", "pool.hip", "select.hip", "select_large.hip", "attn_bf16.hip", "attn_f32.hip", "attn_fp8.hip",
-           "validate.hip", "attn_bwd.hip", "decode.hip"]
+SOURCES = ["api.hip", "pool.hip", "select.hip", "select_large.hip", "attn_bf16.hip",
+           "attn_bf16_page.hip", "attn_f32.hip", "attn_fp8.hip", "validate.hip", "attn_bwd.hip",
+           "decode.hip"]
+# flags of single sources: the (D = 64, block = 64) attention kernels take the iterative ILP
+# machine scheduler (faster on that shape; the other kernels were slower with it)
+SOURCE_FLAGS = {"attn_bf16_page.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 # achievable-peak probes (measurement support, include/bsattn_probe.h): a library of their own
 PROBE_LIB = os.path.join(PKG, "libbsattn_probe.so")
 PROBE_SOURCES = ["probe.hip"]
@@ -51,7 +55,8 @@ ASAN_LDFLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-shared-lib
 
 def _compile(src: str, extra, build_dir: str = BUILD) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *CFLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

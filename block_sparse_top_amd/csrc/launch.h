@@ -53,6 +53,12 @@ hipError_t launch_attn_bf16(int64_t B, int64_t N, int Hq, int Hkv, int D, int bl
                             const void* q, const void* k, const void* v, const int32_t* idx,
                             float scale, void* out, float* lse, bool causal, int key_stride,
                             int64_t nkb, hipStream_t stream);
+// the (D = 64, block = 64) kernels of launch_attn_bf16, built in their own translation unit
+// (attn_bf16_page.hip); c = scale * log2(e), nk key blocks
+hipError_t launch_attn_bf16_d64b64(int64_t B, int64_t N, int Hq, int Hkv, int topk,
+                                   const void* q, const void* k, const void* v,
+                                   const int32_t* idx, float c, void* out, float* lse,
+                                   bool causal, int nk, int key_stride, hipStream_t stream);
 
 // Step 4, fp32 inputs on the fp32 vector ALUs (key blocks as for bf16).
 bool attn_f32_supported(int D, int block);
