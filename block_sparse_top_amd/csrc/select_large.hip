@@ -1,5 +1,6 @@
 // Steps 2-3 of block selection for many key blocks (nb > 1024): the score matrix is built in
-// the workspace by an fp32 MFMA product, then each row's top-k is found by one work-group.
+// the workspace by a matrix product with fp32 accuracy (three-part bf16 split on the bf16
+// MFMA), then each row's top-k is found by one work-group.
 //
 // SparseFormer page ("2026 新一代卷积与Transformer网络架构技术演进与性能对比"), section
 // "SparseFormer 注意力实现": block_scores = einsum over d of the pooled query and key blocks
@@ -7,11 +8,8 @@
 // ("从M2.7到M3：多模态模型稀疏注意力架构设计与实现全解析") §3.2: 1M-token context at block 128, i.e.
 // 8192 key blocks per row; §3.3: block scores as a matrix product.
 //
-// score_gemm_kernel: S[b,h] = qbar[b,h] (nb x D) * kbar[b,g]^T, fp32, unscaled. One wave
-// computes a 64x64 tile with v_mfma_f32_32x32x2_f32 (four 32x32 sub-tiles); the lane half h of
-// k-step s carries d = s + (D/2)*h on both operands, so every lane reads contiguous halves of
-// its query and key rows. Every score goes through the same instruction sequence, so equal
-// pooled key blocks give bit-equal scores.
+// score_gemm_kernel: S[b,h] = qbar[b,h] (nb x D) * kbar[b,g]^T, fp32, unscaled (details at the
+// kernel).
 //
 // topk_rows_kernel: one work-group (256 threads) per row; thread t holds the 32-column chunk
 // j = 32t .. 32t+31 (nb = 8192) as order-preserving keys. A threshold T is built bit by bit
@@ -31,16 +29,52 @@
 namespace bsattn {
 namespace {
 
-typedef float f32x16v __attribute__((ext_vector_type(16)));
-
 // ---------------------------------------------------------------- score GEMM
-__global__ __launch_bounds__(64) void score_gemm_kernel(const float* __restrict__ qbar,
-                                                        const float* __restrict__ kbar,
-                                                        float* __restrict__ S, int Hq, int Hkv,
-                                                        int nb, int D, int tiles, bool group) {
-  // tile index: (b*HS + s) * tiles^2 + ti * tiles + tj, 64x64 each, s a selection head (a
-  // query head, or a KV head whose group's summed queries sit in the rows of its first head);
-  // tiles of one (batch, selection head) share their pooled rows: keep them on one XCD's L2
+// fp32 products on the bf16 MFMA: every pooled value x is split into three bf16 parts
+// x = x0 + x1 + x2 (x0 = bf16(x), x1 = bf16(x - x0), x2 = x - x0 - x1; exact for normal
+// values, each part carrying the next 8 of x's 24 significant bits), and
+//   q.k = q0.k0 + (q0.k1 + q1.k0 + q0.k2 + q1.k1 + q2.k0) + (q1.k2 + q2.k1 + q2.k2).
+// The first product goes to one accumulator, the next five to a second one (added at the end),
+// the last three are left out: they are below 2^-23 of sum_d |q_d k_d|, fp32 rounding level.
+// A product of two bf16 parts is exact in fp32. The bf16 MFMA does 16 times the fp32 one's
+// work per cycle, so the six products take 3/8 of an fp32 product's matrix time.
+//
+// One work-group (4 waves) computes a 128 x 128 tile of S, each wave a 64 x 64 quarter as
+// 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 (A = query rows, B = key rows; lane l takes row
+// l % 32 and d = 16c + 8(l / 32) .. +7 of k-step c on both operands). The pooled rows go
+// through LDS 16 values of d at a time: every thread loads two 16-byte pieces of query rows and
+// two of key rows, splits them and stores the parts (two buffers, one barrier per step; the
+// next step's loads fly during the current step's products). Part p of an operand is
+// [128 rows][16 bf16]; the 16-byte half h of row r sits at half h ^ ((r >> 3) & 1), so the 16
+// lanes of a row read touch every bank once. Every score goes through the same instruction
+// sequence, so equal pooled key blocks give bit-equal scores.
+constexpr int kGemmTile = 128;
+
+__device__ __forceinline__ void split3(const f32x4& v, u32x2 part[3]) {
+  float r[4];
+  const uint32_t a0 = pack_bf16x2(v[0], v[1]), a1 = pack_bf16x2(v[2], v[3]);
+  r[0] = v[0] - bf16lo(a0); r[1] = v[1] - bf16hi(a0);
+  r[2] = v[2] - bf16lo(a1); r[3] = v[3] - bf16hi(a1);
+  const uint32_t b0 = pack_bf16x2(r[0], r[1]), b1 = pack_bf16x2(r[2], r[3]);
+  r[0] -= bf16lo(b0); r[1] -= bf16hi(b0);
+  r[2] -= bf16lo(b1); r[3] -= bf16hi(b1);
+  part[0] = u32x2{a0, a1};
+  part[1] = u32x2{b0, b1};
+  part[2] = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void score_gemm_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, float* __restrict__ S,
+    int Hq, int Hkv, int nb, int tiles, bool group) {
+  constexpr int NC = D / 16;                  // k-steps
+  constexpr int PART = kGemmTile * 32;        // bytes of one part of one operand
+  constexpr int BUF = 6 * PART;               // q parts 0..2, k parts 0..2
+  __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+
+  // tile index: (b*HS + s) * tiles^2 + ti * tiles + tj, s a selection head (a query head, or
+  // a KV head whose group's summed queries sit in the rows of its first head); tiles of one
+  // (batch, selection head) share their pooled rows: keep them on one XCD's L2
   const int G = Hq / Hkv, HS = group ? Hkv : Hq;
   const int64_t t = xcd_remap(blockIdx.x, gridDim.x);
   const int tj = (int)(t % tiles), ti = (int)((t / tiles) % tiles);
@@ -50,63 +84,102 @@ __global__ __launch_bounds__(64) void score_gemm_kernel(const float* __restrict_
   const int g = group ? sh : sh / G;
   const float* Q = qbar + ((int64_t)b * Hq + hq) * nb * D;
   const float* K = kbar + ((int64_t)b * Hkv + g) * nb * D;
-  const int lane = threadIdx.x, l32 = lane & 31, half = lane >> 5;
-  const int half_d = D / 2;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, half = lane >> 5;
 
-  f32x16v acc[2][2];
+  // loads: rows lr and lr + 64 of the tile (clamped to the last pooled row; the scores of
+  // rows and columns past nb are not stored), d = 16c + 4 * quad .. +3
+  const int lr = tid >> 2, quad = tid & 3;
+  const float* src[2][2];                     // [q or k][row]
+  int soff[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int r = lr + 64 * u;
+    const int qr = ti * kGemmTile + r, kr = tj * kGemmTile + r;
+    src[0][u] = Q + (int64_t)(qr < nb ? qr : nb - 1) * D + 4 * quad;
+    src[1][u] = K + (int64_t)(kr < nb ? kr : nb - 1) * D + 4 * quad;
+    soff[u] = r * 32 + 16 * ((quad >> 1) ^ ((r >> 3) & 1)) + 8 * (quad & 1);
+  }
+  int aoff[2], boff[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int ra = 64 * (wave >> 1) + 32 * a + l32, rb = 64 * (wave & 1) + 32 * a + l32;
+    aoff[a] = ra * 32 + 16 * (half ^ ((ra >> 3) & 1));
+    boff[a] = 3 * PART + rb * 32 + 16 * (half ^ ((rb >> 3) & 1));
+  }
+  f32x4 st[2][2];
+  auto load = [&](int c) {
+#pragma unroll
+    for (int o = 0; o < 2; ++o)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) st[o][u] = *(const f32x4*)(src[o][u] + 16 * c);
+  };
+  auto store = [&](char* buf) {
+#pragma unroll
+    for (int o = 0; o < 2; ++o)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        u32x2 part[3];
+        split3(st[o][u], part);
+#pragma unroll
+        for (int p = 0; p < 3; ++p) *(u32x2*)(buf + (3 * o + p) * PART + soff[u]) = part[p];
+      }
+  };
+
+  f32x16 hi[2][2], lo[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
+      for (int r = 0; r < 16; ++r) { hi[a][c][r] = 0.f; lo[a][c][r] = 0.f; }
 
-  const float* qrow[2];
-  const float* krow[2];
+  load(0);
+  store(lds);
+  __syncthreads();
+  for (int c = 0; c < NC; ++c) {
+    const char* cur = lds + (c & 1) * BUF;
+    if (c + 1 < NC) load(c + 1);
+    bf16x8 qa[3][2], kb[3][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    qrow[a] = Q + (int64_t)(ti * 64 + 32 * a + l32) * D + half * half_d;
-    krow[a] = K + (int64_t)(tj * 64 + 32 * a + l32) * D + half * half_d;
-  }
-  // the operands of step s0 + 4 are loaded while step s0 multiplies
-  f32x4 qa[2], kb[2];
+    for (int p = 0; p < 3; ++p)
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    qa[a] = *(const f32x4*)(qrow[a]);
-    kb[a] = *(const f32x4*)(krow[a]);
-  }
-  for (int s0 = 0; s0 < half_d; s0 += 4) {
-    f32x4 qn[2], kn[2];
-    const int sn = s0 + 4 < half_d ? s0 + 4 : s0;
+      for (int a = 0; a < 2; ++a) {
+        qa[p][a] = *(const bf16x8*)(cur + p * PART + aoff[a]);
+        kb[p][a] = *(const bf16x8*)(cur + p * PART + boff[a]);
+      }
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      qn[a] = *(const f32x4*)(qrow[a] + sn);
-      kn[a] = *(const f32x4*)(krow[a] + sn);
-    }
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+      for (int cc = 0; cc < 2; ++cc)
+        hi[a][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][a], kb[0][cc], hi[a][cc], 0, 0, 0);
+    constexpr int PQ[5] = {0, 1, 0, 1, 2}, PK[5] = {1, 0, 2, 1, 0};
+#pragma unroll
+    for (int x = 0; x < 5; ++x)
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[a][e], kb[c][e], acc[a][c], 0, 0, 0);
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      qa[a] = qn[a];
-      kb[a] = kn[a];
-    }
+        for (int cc = 0; cc < 2; ++cc)
+          lo[a][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[PQ[x]][a], kb[PK[x]][cc], lo[a][cc], 0, 0, 0);
+    if (c + 1 < NC) store(lds + ((c + 1) & 1) * BUF);
+    __syncthreads();
   }
-  // acc[a][c][r]: row ti*64 + 32a + 8(r/4) + 4*half + r%4, column tj*64 + 32c + l32
+
+  // hi/lo[a][c][r]: row 64(wave/2) + 32a + 8(r/4) + 4*half + r%4, column 64(wave%2) + 32c + l32
   float* Sbh = S + bh * nb * nb;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int cc = 0; cc < 2; ++cc) {
+      const int row0 = ti * kGemmTile + 64 * (wave >> 1) + 32 * a;
+      const int col = tj * kGemmTile + 64 * (wave & 1) + 32 * cc + l32;
+      if (row0 >= nb || col - l32 >= nb) continue;   // the half tile past nb (nb % 128 = 64)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = ti * 64 + 32 * a + 8 * (r >> 2) + 4 * half + (r & 3);
-        Sbh[(int64_t)row * nb + tj * 64 + 32 * c + l32] = acc[a][c][r];
+        const int row = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        Sbh[(int64_t)row * nb + col] = hi[a][cc][r] + lo[a][cc][r];
       }
+    }
 }
 
 // ---------------------------------------------------------------- per-row top-k
@@ -244,10 +317,14 @@ hipError_t launch_scores_large(int64_t B, int Hq, int Hkv, int nb, int D, float*
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int tiles = nb / 64;
+  const int tiles = (nb + kGemmTile - 1) / kGemmTile;
   const int64_t n = B * (group ? Hkv : Hq) * (int64_t)tiles * tiles;
-  score_gemm_kernel<<<dim3((unsigned)n), 64, 0, stream>>>(qbar, kbar, S, Hq, Hkv, nb, D, tiles,
-                                                          group);
+  if (D == 64)
+    score_gemm_kernel<64><<<dim3((unsigned)n), 256, 0, stream>>>(qbar, kbar, S, Hq, Hkv, nb,
+                                                                  tiles, group);
+  else
+    score_gemm_kernel<128><<<dim3((unsigned)n), 256, 0, stream>>>(qbar, kbar, S, Hq, Hkv, nb,
+                                                                   tiles, group);
   return hipGetLastError();
 }
 
