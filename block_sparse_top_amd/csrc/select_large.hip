@@ -12,9 +12,9 @@
 // kernel).
 //
 // topk_rows_kernel: one work-group (256 threads) per row; thread t holds the 32-column chunk
-// j = 32t .. 32t+31 (nb = 8192) as order-preserving keys. A threshold T is built bit by bit
-// (block-wide counts of keys >= candidate; early exit once exactly k keys are >= T), keys > T
-// are kept and keys == T fill the remaining places in ascending j (the lower index wins).
+// j = 32t .. 32t+31 (nb = 8192) as order-preserving keys. The k-th largest key T is found from
+// key-bucket counts and the keys of one bucket (details at the kernel); keys > T are kept
+// and keys == T fill the remaining places in ascending j (the lower index wins).
 // Output positions come from block-wide exclusive scans, so the row is written in ascending j.
 // Causal option: as in the fused kernel, columns j > i get key 0, column i the largest key,
 // the row keeps min(topk, i+1) blocks and its remaining places are set to -1.
@@ -222,19 +222,38 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total)
   return before + incl - v;
 }
 
+constexpr int kBinBits = 11;
+constexpr int kBins = 1 << kBinBits;       // key buckets per level
+constexpr int kMaxCand = 4 * kWave;        // bucket size one wave resolves (4 keys per lane)
+
 // rows of S: (b * HS + s) * nb + i; the top-k of a row goes to the idx rows of the G query
 // heads s*G .. s*G+G-1 of a group (group), or of query head s
+//
+// The k-th largest key T is found by counting keys into buckets of equal key width (LDS
+// counts): bucket = (key - base) >> shift, so a bucket is a key range, equal keys share one
+// and every key of a higher bucket is larger than every key of a lower one. A scan from the
+// top finds the bucket holding the k-th largest key. If it holds more than kMaxCand keys, its
+// range is cut into buckets again (11 bits narrower, at most three levels over the 32-bit
+// keys); otherwise its keys go to LDS and one wave finds T among them bit by bit with ballots.
+// A bucket one key wide holds equal keys only, and that key is T. The row's own forced block
+// (causal: all-ones key) falls into the top bucket of every level; columns past the row's
+// admissible range (key 0) are not counted.
 __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __restrict__ S,
                                                                  int32_t* __restrict__ idx,
                                                                  int nb, int topk, bool causal,
                                                                  int G) {
   __shared__ int red[4];
+  __shared__ uint32_t redu[8];
+  __shared__ int hist[kBins];
+  __shared__ uint32_t cand[kMaxCand];
+  __shared__ int found[3];                 // bucket of the k-th key, keys above it, candidates
+  __shared__ uint32_t t_found[2];          // T, candidates above T
   const int64_t row = blockIdx.x;
   const int i = (int)(row % nb);           // query block of this row
   const int lim = causal ? i + 1 : nb;     // admissible columns j < lim
   const int kr = causal && i + 1 < topk ? i + 1 : topk;
   const float* srow = S + row * nb;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int j0 = t * kPerThread;
   uint32_t key[kPerThread];
 #pragma unroll
@@ -247,48 +266,132 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
       key[e + q] = j < lim ? (causal && j == i ? 0xFFFFFFFFu : order_key(v[q])) : 0u;
     }
   }
-  // keys of columns past lim are 0: no candidate (>= 1) and no reached T (>= 1) counts them
-  uint32_t T = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    int c = 0;
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) c += key[e] >= cand;
-    const int cnt = block_sum(c, red);
-    if (cnt >= kr) T = cand;
-    if (cnt == kr) break;
-  }
-  int gt = 0, eq = 0;
+
+  // ---- key range of the scored columns: key - 1 takes the uncounted 0 to all ones and
+  // key + 1 takes the forced all-ones key to 0, so neither bounds the range
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
-    gt += key[e] > T;
-    eq += (j0 + e < lim) && key[e] == T;
+    kmin = min(kmin, key[e] - 1u);
+    kmax = max(kmax, key[e] + 1u);
   }
-  const int tot_gt = block_sum(gt, red);
+  for (int b = t; b < kBins; b += kTopkThreads) hist[b] = 0;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+  }
+  if (lane == 0) { redu[w] = kmin; redu[4 + w] = kmax; }
+  if (t == 0) { found[0] = 0; found[1] = 0; found[2] = 0; }
+  __syncthreads();
+  kmin = min(min(redu[0], redu[1]), min(redu[2], redu[3])) + 1u;
+  kmax = max(max(redu[4], redu[5]), max(redu[6], redu[7])) - 1u;
+
+  // ---- bucket levels
+  uint32_t base = kmin;                    // first key of the current range
+  const uint32_t span = kmax > kmin ? kmax - kmin : 0u;
+  int shift = span ? 32 - __builtin_clz(span) - kBinBits : 0;
+  if (shift < 0) shift = 0;
+  bool open = true;                        // the range has no upper end (top bucket so far)
+  int above = 0;                           // keys above the current range
+  int bT = 0, cb = 0;
+  auto member_bucket = [&](uint32_t kk) -> int {   // bucket of kk in the range, or -1
+    if (kk == 0u || kk < base) return -1;
+    const uint32_t b = (kk - base) >> shift;
+    if (b >= (uint32_t)kBins) return open ? kBins - 1 : -1;
+    return (int)b;
+  };
+  for (;;) {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int b = member_bucket(key[e]);
+      if (b >= 0) atomicAdd(&hist[b], 1);
+    }
+    __syncthreads();
+    // thread t scans the 8 buckets [kBins - 8(t+1), kBins - 8t) from the top
+    const int b_top = kBins - 8 * t - 1;
+    int cnt8[8], local = 0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) { cnt8[m] = hist[b_top - m]; local += cnt8[m]; }
+    int total;
+    int run = above + block_exclusive_scan(local, red, &total);   // keys above my buckets
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (run < kr && run + cnt8[m] >= kr) { found[0] = b_top - m; found[1] = run; }
+      run += cnt8[m];
+    }
+    __syncthreads();
+    bT = found[0];
+    above = found[1];
+    cb = hist[bT];
+    if (cb <= kMaxCand || shift == 0) break;   // (block-uniform)
+    // cut bucket bT into kBins narrower buckets (every thread has read found and hist first)
+    base += (uint32_t)bT << shift;
+    open = open && bT == kBins - 1;
+    shift = shift > kBinBits ? shift - kBinBits : 0;
+    __syncthreads();
+    for (int b = t; b < kBins; b += kTopkThreads) hist[b] = 0;
+    __syncthreads();
+  }
+
+  // ---- T from the keys of bucket bT
+  uint32_t T;
+  int tot_gt;                              // keys > T
+  if (cb <= kMaxCand) {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e)
+      if (member_bucket(key[e]) == bT) cand[atomicAdd(&found[2], 1)] = key[e];
+    __syncthreads();
+    if (w == 0) {
+      const int need = kr - above;          // places left for the bucket's keys (>= 1)
+      uint32_t c4[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) c4[m] = lane + kWave * m < cb ? cand[lane + kWave * m] : 0u;
+      // the need-th largest candidate key itself (no early exit: T must be a key of the bucket,
+      // so that no key of a lower bucket exceeds it)
+      uint32_t Tc = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t probe = Tc | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(c4[m] >= probe));
+        if (cnt >= need) Tc = probe;
+      }
+      int gtc = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) gtc += __builtin_popcountll(__builtin_amdgcn_ballot_w64(c4[m] > Tc));
+      if (lane == 0) { t_found[0] = Tc; t_found[1] = (uint32_t)gtc; }
+    }
+    __syncthreads();
+    T = t_found[0];
+    tot_gt = above + (int)t_found[1];
+  } else {                                  // a one-key-wide bucket: all its keys equal T
+    T = base + (uint32_t)bT;
+    tot_gt = above;
+  }
+
+  // ---- the row: keys > T, then keys == T in ascending j until kr places are filled
+  int eq = 0;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) eq += key[e] == T;
   int tot_eq;
-  const int eq_before = block_exclusive_scan(eq, red, &tot_eq);
+  int eq_seen = block_exclusive_scan(eq, red, &tot_eq);
   const int need = kr - tot_gt;            // places for keys equal to T
-  int sel = 0;
-  int eq_seen = eq_before;
+  uint32_t selm = 0;                       // bit e: column j0 + e chosen
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
-    const bool is_eq = (j0 + e < lim) && key[e] == T;
-    sel += key[e] > T || (is_eq && eq_seen < need);
+    const bool is_eq = key[e] == T;
+    selm |= (uint32_t)(key[e] > T || (is_eq && eq_seen < need)) << e;
     eq_seen += is_eq;
   }
   int tot_sel;
-  const int pos0 = block_exclusive_scan(sel, red, &tot_sel);
+  const int pos0 = block_exclusive_scan(__builtin_popcount(selm), red, &tot_sel);
   const int64_t bs = row / nb;             // b * HS + s
   for (int hh = 0; hh < G; ++hh) {
     int32_t* out = idx + ((bs * G + hh) * nb + i) * topk;
     int pos = pos0;
-    eq_seen = eq_before;
-#pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const bool is_eq = (j0 + e < lim) && key[e] == T;
-      if (key[e] > T || (is_eq && eq_seen < need)) out[pos++] = j0 + e;
-      eq_seen += is_eq;
-    }
+    // (pos < kr holds for consistent counts; it also bounds rows of NaN scores)
+    for (uint32_t m = selm; m && pos < kr; m &= m - 1u) out[pos++] = j0 + __builtin_ctz(m);
     for (int p = kr + t; p < topk; p += kTopkThreads) out[p] = -1;   // unused causal places
   }
 }

@@ -12,8 +12,8 @@ import torch
 import block_sparse_top_amd as bst
 from block_sparse_top_amd import synthetic as syn
 import oracle.bsattn_oracle as O
-from tests.parity import (check_idx, check_out, dtype_name, fp8_figures, out_errors, to_f64,
-                          TOL)
+from tests.parity import (check_idx, check_idx_causal, check_out, dtype_name, fp8_figures,
+                          out_errors, to_f64, TOL)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -377,6 +377,47 @@ def test_select_many_blocks(shape):
     assert np.max(np.abs(kbar.cpu().numpy() - pk)) <= 2e-6 * np.abs(ko).max()
     stats = check_idx(idx.cpu().numpy(), O.block_scores(pq, pk), topk)
     say("  ", stats)
+
+
+def test_select_many_blocks_ties_and_outliers():
+    """The per-row selection over more than 1024 key blocks on rows that stress its threshold
+    search: exact ties (duplicated key blocks: the lower index wins), a zero query (every score
+    equal), one key block far above the rest (the others' scores crowd into one value bucket),
+    k = 1 and k = nb, plain and causal."""
+    B, N, H, D, blk = 1, 64 * 1152, 2, 64, 64
+    nb = N // blk
+    say(f"[select many blocks: ties and outliers] nb={nb}")
+    q, k, v, ds = make(B, N, H, H, D, "bf16", index=19)
+    del v
+    k = k.clone()
+    dups = ((1100, 3), (517, 9), (1151, 0), (600, 599))
+    for dst, src in dups:
+        k[:, dst * blk:(dst + 1) * blk] = k[:, src * blk:(src + 1) * blk]
+    qo, ko = to_f64(q), to_f64(k)
+    S = O.block_scores(O.pool(qo, blk), O.pool(ko, blk))
+    for topk in (1, 173, 576, nb):
+        idx = bst.select(q, k, blk, topk).cpu().numpy()
+        say("   topk", topk, check_idx(idx, S, topk))
+        for row in idx.reshape(-1, topk):
+            chosen = set(row.tolist())
+            for dst, src in dups:
+                assert dst not in chosen or src in chosen
+    idx = bst.select(q, k, blk, 300, causal=True).cpu().numpy()
+    check_idx_causal(idx, S, 300)
+    # zero query: every score is 0, the lowest blocks are chosen
+    idx = bst.select(torch.zeros_like(q), k, blk, 200).cpu().numpy()
+    assert np.all(idx == np.arange(200))
+    idx = bst.select(torch.zeros_like(q), k, blk, 200, causal=True).cpu().numpy()
+    for i in range(nb):
+        n = min(200, i + 1)
+        assert np.all(idx[:, :, i, :n - 1] == np.arange(n - 1)) and np.all(idx[:, :, i, n - 1] == i)
+        assert np.all(idx[:, :, i, n:] == -1)
+    # one key block far above the rest
+    k2 = k.clone()
+    k2[:, 700 * blk:701 * blk] *= 3.0e4
+    S2 = O.block_scores(O.pool(qo, blk), O.pool(to_f64(k2), blk))
+    idx = bst.select(q, k2, blk, 150).cpu().numpy()
+    say("   outlier", check_idx(idx, S2, 150))
 
 
 def test_planted_workload_sampled():
