@@ -14,9 +14,9 @@
 // this phase is HBM-bound and overlaps the arithmetic of the other work-groups on the CU),
 // keeps the pooled rows in LDS and also stores them to the workspace. Key-block columns are
 // staged through LDS 64 at a time with coalesced row loads; the block scores of a chunk are
-// a 16 x 64 product on the fp32 MFMA (the MSA page's scores as a matrix product), fp32
-// operands and sums, the same arithmetic for every column (equal pooled key blocks give equal
-// scores). Each wave then holds 4 rows x CPL columns of scores in registers, lane l owning
+// a 16 x 64 product on the bf16 MFMA with fp32 accuracy (three-part bf16 splits of the fp32
+// operands; the MSA page's scores as a matrix product), the same arithmetic for every column
+// (equal pooled key blocks give equal scores). Each wave then holds 4 rows x CPL columns of scores in registers, lane l owning
 // columns j = l + 64*c.
 //
 // Selection of one row is done by its wave with no sorting: scores map to order-preserving
@@ -49,6 +49,13 @@ namespace {
 // A work-group takes RG = 16 query-block rows (one 16-row tile of the fp32 MFMA; 4 waves) or,
 // from 512 key blocks on, 32 rows (8 waves): every work-group streams all pooled keys through
 // LDS, and 32 rows halve that traffic. 4 rows per wave for the selection.
+// LDS floats of the pooled query rows ([RG][D] fp32); at D = 128 the same space then holds
+// their three bf16 parts ([3][RG] rows of 2D + 16 bytes: 16 rows of a read on distinct banks)
+constexpr int kQPartRow = 2 * 128 + 16;
+constexpr int query_lds_floats(int RG, int D) {
+  return D == 128 ? 3 * RG * kQPartRow / 4 : RG * D;
+}
+
 template <int CPL>
 struct SelCfg {
   static constexpr int NWV = CPL >= 8 ? 8 : 4;                 // waves
@@ -73,7 +80,7 @@ __global__ __launch_bounds__(SelCfg<CPL>::NT) void select_kernel(
   float* ks = smem;                         // [64][D+4] current key-block chunk
   constexpr int kRed = RG * (D / E) < kThreads ? kThreads * E : 0;   // pooling partial sums
   float* qs = smem + (64 * KS > kRed ? 64 * KS : kRed);   // [RG][D] pooled query rows
-  float* sc = qs + RG * D;                  // [RG][64+4] score chunk (MFMA tiles -> rows)
+  float* sc = qs + query_lds_floats(RG, D);  // [RG][64+4] score chunk (MFMA tiles -> rows)
 
   // work-groups of one (batch, head) read the same pooled keys: keep them on one XCD's L2
   const int tile = (int)xcd_remap(blockIdx.x, gridDim.x);
@@ -166,21 +173,63 @@ __global__ __launch_bounds__(SelCfg<CPL>::NT) void select_kernel(
     }
   }
 
-  // ---- scores on the fp32 MFMA (v_mfma_f32_16x16x4_f32): per 64-column chunk each wave forms
-  // the 16 x 16 tile S[rows][16*wave .. +16) = qs K^T. The k-slot q4 = lane / 16 of a lane
-  // carries d = (D/4)*q4 + s at k-step s (any split of d gives the same sum in exact
-  // arithmetic; this one gives each lane contiguous operands). Every score goes through the
-  // same products and sums in the same order, so equal pooled key blocks give equal scores.
-  // The tile goes through LDS (sc) to the selection layout, lane = column, 4 rows per wave.
+  // ---- scores with fp32 accuracy on the bf16 MFMA (v_mfma_f32_16x16x32_bf16): every fp32
+  // operand value x is split into three bf16 parts x = x0 + x1 + x2 (x0 = bf16(x),
+  // x1 = bf16(x - x0), x2 = x - x0 - x1; exact for normal values) and a score is
+  // q0.k0 + (q0.k1 + q1.k0 + q0.k2 + q1.k1 + q2.k0): products of bf16 parts are exact in fp32,
+  // the three products left out are below 2^-23 of sum_d |q_d k_d|, and the six bf16
+  // products take 3/8 of the fp32 MFMA's time (the MSA page's scores as a matrix product).
+  // Per 64-column chunk each wave forms the 16 x 16 tile S[rows][16*(wave%4) .. +16) = qs K^T;
+  // the k-slot group q4 = lane / 16 of a lane carries d = 32s + 8*q4 .. +7 at k-step s on both
+  // operands. The query parts are formed once; the key values are split as they are read
+  // from the fp32 chunk in LDS. Every score goes through the same products and sums in the
+  // same order, so equal pooled key blocks give equal scores. The tile goes through LDS (sc)
+  // to the selection layout, lane = column, 4 rows per wave.
   typedef float f32x4v __attribute__((ext_vector_type(4)));
   const int m16 = lane & 15, q4 = lane >> 4;
-  constexpr int DQ = D / 4;                 // k-steps per tile (16 or 32)
-  float qa[DQ];                             // A operands: qs[m16][DQ*q4 + s], s < DQ
-  __syncthreads();                          // qs complete
+  constexpr int NK = D / 32;                // k-steps per tile (2 or 4)
+  auto split8 = [](const f32x4v& lo4, const f32x4v& hi4, bf16x8 part[3]) {
+    // three bf16 parts of 8 consecutive values (part p: x_p of each value, in order)
+    uint32_t w[3][4];
+    const f32x4v v2[2] = {lo4, hi4};
 #pragma unroll
-  for (int s4 = 0; s4 < DQ / 4; ++s4) {
-    const f32x4v v = *(const f32x4v*)(qs + (16 * (wave >> 2) + m16) * D + DQ * q4 + 4 * s4);
-    qa[4 * s4] = v[0]; qa[4 * s4 + 1] = v[1]; qa[4 * s4 + 2] = v[2]; qa[4 * s4 + 3] = v[3];
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float a = v2[h][2 * e], b = v2[h][2 * e + 1];
+        const uint32_t p0 = pack_bf16x2(a, b);
+        const float ra = a - bf16lo(p0), rb = b - bf16hi(p0);
+        const uint32_t p1 = pack_bf16x2(ra, rb);
+        w[0][2 * h + e] = p0;
+        w[1][2 * h + e] = p1;
+        w[2][2 * h + e] = pack_bf16x2(ra - bf16lo(p1), rb - bf16hi(p1));
+      }
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      part[p] = __builtin_bit_cast(bf16x8, u32x4{w[p][0], w[p][1], w[p][2], w[p][3]});
+  };
+  // A operands (qs[m16][32s + 8*q4 .. +7], split): in registers at D = 64; at D = 128 in LDS
+  // (the parts overwrite qs), read per k-step, which keeps 1024 key blocks at 4 waves per SIMD
+  bf16x8 qa[D == 64 ? NK : 1][3];
+  char* qp = (char*)qs;                     // D = 128: [3][RG][kQPartRow bytes]
+  __syncthreads();                          // qs complete
+  if constexpr (D == 64) {
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      const float* qrow = qs + (16 * (wave >> 2) + m16) * D + 32 * s + 8 * q4;
+      split8(*(const f32x4v*)qrow, *(const f32x4v*)(qrow + 4), qa[s]);
+    }
+  } else {
+    static_assert(RG * D / 8 == kThreads, "one group of 8 pooled values per thread");
+    const int r = tid / (D / 8), c8 = tid % (D / 8);
+    const float* src = qs + r * D + 8 * c8;
+    bf16x8 part[3];
+    split8(*(const f32x4v*)src, *(const f32x4v*)(src + 4), part);
+    __syncthreads();                        // every thread has read its values of qs
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      *(bf16x8*)(qp + (p * RG + r) * kQPartRow + 16 * c8) = part[p];
+    __syncthreads();
   }
   float acc[RW][CPL];
 #pragma unroll
@@ -208,23 +257,32 @@ __global__ __launch_bounds__(SelCfg<CPL>::NT) void select_kernel(
     }
     __syncthreads();
     {
-      // two independent accumulation chains (even and odd groups of four k-steps), added at
-      // the end: the same order for every column
+      // the leading product in hi, the five smaller ones in two chains (lo0, lo1), added at
+      // the end in a fixed order: the same for every column
       const int ct = wave & 3;              // column tile of this wave (16 columns)
-      const float* kb = ks + (16 * ct + m16) * KS + DQ * q4;
-      f32x4v t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+      const float* kb = ks + (16 * ct + m16) * KS + 8 * q4;
+      f32x4v hi = {0.f, 0.f, 0.f, 0.f}, lo0 = hi, lo1 = hi;
 #pragma unroll
-      for (int s4 = 0; s4 < DQ / 4; ++s4) {
-        const f32x4v bv = *(const f32x4v*)(kb + 4 * s4);
+      for (int s = 0; s < NK; ++s) {
+        bf16x8 kp[3], qv[3];
+        split8(*(const f32x4v*)(kb + 32 * s), *(const f32x4v*)(kb + 32 * s + 4), kp);
+        if constexpr (D == 64) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (s4 & 1)
-            t1 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * s4 + e], bv[e], t1, 0, 0, 0);
-          else
-            t0 = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[4 * s4 + e], bv[e], t0, 0, 0, 0);
+          for (int p = 0; p < 3; ++p) qv[p] = qa[s][p];
+        } else {
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+            qv[p] = *(const bf16x8*)(qp + (p * RG + 16 * (wave >> 2) + m16) * kQPartRow +
+                                     2 * (32 * s + 8 * q4));
         }
+        hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qv[0], kp[0], hi, 0, 0, 0);
+        lo0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qv[0], kp[1], lo0, 0, 0, 0);
+        lo1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qv[1], kp[0], lo1, 0, 0, 0);
+        lo0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qv[0], kp[2], lo0, 0, 0, 0);
+        lo1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qv[1], kp[1], lo1, 0, 0, 0);
+        lo0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qv[2], kp[0], lo0, 0, 0, 0);
       }
-      const f32x4v t = t0 + t1;
+      const f32x4v t = hi + (lo0 + lo1);
       // lane holds S[row 16*(wave/4) + 4*q4 + e][column 16*(wave%4) + m16]
 #pragma unroll
       for (int e = 0; e < 4; ++e) sc[(16 * (wave >> 2) + 4 * q4 + e) * SS + 16 * ct + m16] = t[e];
@@ -322,10 +380,9 @@ hipError_t launch(int64_t B, int64_t N, int Hq, int Hkv, int nb, int nk, int blo
   // the key chunk's LDS also holds the pooling phase's partial sums (TG x pairs x E floats)
   constexpr int E = Vec<KIND>::E;
   constexpr int pairs = RG * (D / E);
-  constexpr int per_pass = pairs < NT ? pairs : NT;
   constexpr int red = pairs < NT ? NT * E : 0;    // as the kernel reserves it
   constexpr int kchunk = 64 * (D + 4) > red ? 64 * (D + 4) : red;
-  const size_t lds = (size_t)(kchunk + RG * D + RG * (64 + 4)) * sizeof(float);
+  const size_t lds = (size_t)(kchunk + query_lds_floats(RG, D) + RG * (64 + 4)) * sizeof(float);
   select_kernel<KIND, CPL, D><<<grid, NT, lds, stream>>>(
       (const uint8_t*)q, qbar, kbar, idx, N, Hq, Hkv, nb, nk, block, topk, row_tiles,
       1.0f / (float)block, flags, nrand, seed, D);
