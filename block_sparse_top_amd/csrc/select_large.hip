@@ -34,10 +34,14 @@ namespace {
 // x = x0 + x1 + x2 (x0 = bf16(x), x1 = bf16(x - x0), x2 = x - x0 - x1; exact for normal
 // values, each part carrying the next 8 of x's 24 significant bits), and
 //   q.k = q0.k0 + (q0.k1 + q1.k0 + q0.k2 + q1.k1 + q2.k0) + (q1.k2 + q2.k1 + q2.k2).
-// The first product goes to one accumulator, the next five to a second one (added at the end),
-// the last three are left out: they are below 2^-23 of sum_d |q_d k_d|, fp32 rounding level.
-// A product of two bf16 parts is exact in fp32. The bf16 MFMA does 16 times the fp32 one's
-// work per cycle, so the six products take 3/8 of an fp32 product's matrix time.
+// The six products go to one fp32 accumulator, the smallest first; the last three are left
+// out: they are below 2^-23 of sum_d |q_d k_d|, fp32 rounding level. A product of two bf16
+// parts is exact in fp32, and the accumulator's rounding is that of an fp32 product (a CPU
+// simulation of this order: at most 5e-7 of sum_d |q_d k_d|, an fp32 matrix product 2e-7).
+// (A second accumulator for the five smaller products halves that error but takes 64 more
+// registers: 2 instead of 3 waves per SIMD, 5 % slower at 8192 key blocks.) The bf16 MFMA
+// does 16 times the fp32 one's work per cycle, so the six products take 3/8 of an fp32
+// product's matrix time.
 //
 // One work-group (4 waves) computes a 128 x 128 tile of S, each wave a 64 x 64 quarter as
 // 2 x 2 tiles of v_mfma_f32_32x32x16_bf16 (A = query rows, B = key rows; lane l takes row
@@ -64,7 +68,7 @@ __device__ __forceinline__ void split3(const f32x4& v, u32x2 part[3]) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void score_gemm_kernel(
+__global__ __launch_bounds__(256) void score_gemm_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, float* __restrict__ S,
     int Hq, int Hkv, int nb, int tiles, bool group) {
   constexpr int NC = D / 16;                  // k-steps
@@ -126,13 +130,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       }
   };
 
-  f32x16 hi[2][2], lo[2][2];
+  f32x16 acc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { hi[a][c][r] = 0.f; lo[a][c][r] = 0.f; }
+      for (int r = 0; r < 16; ++r) acc[a][c][r] = 0.f;
 
   load(0);
   store(lds);
@@ -148,19 +152,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
         qa[p][a] = *(const bf16x8*)(cur + p * PART + aoff[a]);
         kb[p][a] = *(const bf16x8*)(cur + p * PART + boff[a]);
       }
+    // smallest products first
+    constexpr int PQ[6] = {2, 1, 0, 1, 0, 0}, PK[6] = {0, 1, 2, 0, 1, 0};
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-        hi[a][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][a], kb[0][cc], hi[a][cc], 0, 0, 0);
-    constexpr int PQ[5] = {0, 1, 0, 1, 2}, PK[5] = {1, 0, 2, 1, 0};
-#pragma unroll
-    for (int x = 0; x < 5; ++x)
+    for (int x = 0; x < 6; ++x)
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
-          lo[a][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[PQ[x]][a], kb[PK[x]][cc], lo[a][cc], 0, 0, 0);
+          acc[a][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[PQ[x]][a], kb[PK[x]][cc], acc[a][cc], 0, 0, 0);
     if (c + 1 < NC) store(lds + ((c + 1) & 1) * BUF);
     __syncthreads();
   }
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
-        Sbh[(int64_t)row * nb + col] = hi[a][cc][r] + lo[a][cc][r];
+        Sbh[(int64_t)row * nb + col] = acc[a][cc][r];
       }
     }
 }
