@@ -226,6 +226,13 @@ constexpr int kBinBits = 11;
 constexpr int kBins = 1 << kBinBits;       // key buckets per level
 constexpr int kMaxCand = 4 * kWave;        // bucket size one wave resolves (4 keys per lane)
 
+// Order-preserving key of a float (as order_key): -0.0 becomes +0.0 by adding +0.0, then the
+// sign bit decides between flipping every bit (negative) and setting the top bit.
+__device__ __forceinline__ uint32_t order_key_fast(float s) {
+  const uint32_t u = __float_as_uint(s + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
 // rows of S: (b * HS + s) * nb + i; the top-k of a row goes to the idx rows of the G query
 // heads s*G .. s*G+G-1 of a group (group), or of query head s
 //
@@ -235,13 +242,14 @@ constexpr int kMaxCand = 4 * kWave;        // bucket size one wave resolves (4 k
 // top finds the bucket holding the k-th largest key. If it holds more than kMaxCand keys, its
 // range is cut into buckets again (11 bits narrower, at most three levels over the 32-bit
 // keys); otherwise its keys go to LDS and one wave finds T among them bit by bit with ballots.
-// A bucket one key wide holds equal keys only, and that key is T. The row's own forced block
-// (causal: all-ones key) falls into the top bucket of every level; columns past the row's
-// admissible range (key 0) are not counted.
+// A bucket one key wide holds equal keys only, and that key is T. CAUSAL: the row's own forced
+// block (all-ones key) falls into the top bucket of every level and columns past the row's
+// admissible range (key 0) are not counted. nb is a multiple of 64, so a thread's 32 columns
+// are all inside the row or all past it.
+template <bool CAUSAL>
 __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __restrict__ S,
                                                                  int32_t* __restrict__ idx,
-                                                                 int nb, int topk, bool causal,
-                                                                 int G) {
+                                                                 int nb, int topk, int G) {
   __shared__ int red[4];
   __shared__ uint32_t redu[8];
   __shared__ int hist[kBins];
@@ -250,30 +258,39 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
   __shared__ uint32_t t_found[2];          // T, candidates above T
   const int64_t row = blockIdx.x;
   const int i = (int)(row % nb);           // query block of this row
-  const int lim = causal ? i + 1 : nb;     // admissible columns j < lim
-  const int kr = causal && i + 1 < topk ? i + 1 : topk;
+  const int kr = CAUSAL && i + 1 < topk ? i + 1 : topk;
   const float* srow = S + row * nb;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int j0 = t * kPerThread;
+  const bool has = j0 < (CAUSAL ? i + 1 : nb);   // some admissible column (all, unless causal)
   uint32_t key[kPerThread];
+  if (has) {
+    f32x4 v[kPerThread / 4];
 #pragma unroll
-  for (int e = 0; e < kPerThread; e += 4) {
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (j0 + e < nb) v = *(const f32x4*)(srow + j0 + e);   // nb is a multiple of 4
+    for (int e = 0; e < kPerThread / 4; ++e) v[e] = *(const f32x4*)(srow + j0 + 4 * e);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j = j0 + e + q;
-      key[e + q] = j < lim ? (causal && j == i ? 0xFFFFFFFFu : order_key(v[q])) : 0u;
+    for (int e = 0; e < kPerThread; ++e) key[e] = order_key_fast(v[e / 4][e % 4]);
+    if constexpr (CAUSAL) {                  // columns past the row: 0; the own block: all ones
+#pragma unroll
+      for (int e = 0; e < kPerThread; ++e) {
+        const int j = j0 + e;
+        key[e] = j > i ? 0u : j == i ? 0xFFFFFFFFu : key[e];
+      }
     }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) key[e] = 0u;
   }
 
-  // ---- key range of the scored columns: key - 1 takes the uncounted 0 to all ones and
-  // key + 1 takes the forced all-ones key to 0, so neither bounds the range
+  // ---- key range of the scored columns (causal: key - 1 takes the uncounted 0 to all ones and
+  // key + 1 takes the forced all-ones key to 0, so neither bounds the range)
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  if (has) {
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    kmin = min(kmin, key[e] - 1u);
-    kmax = max(kmax, key[e] + 1u);
+    for (int e = 0; e < kPerThread; ++e) {
+      kmin = min(kmin, CAUSAL ? key[e] - 1u : key[e]);
+      kmax = max(kmax, CAUSAL ? key[e] + 1u : key[e]);
+    }
   }
   for (int b = t; b < kBins; b += kTopkThreads) hist[b] = 0;
 #pragma unroll
@@ -284,8 +301,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
   if (lane == 0) { redu[w] = kmin; redu[4 + w] = kmax; }
   if (t == 0) { found[0] = 0; found[1] = 0; found[2] = 0; }
   __syncthreads();
-  kmin = min(min(redu[0], redu[1]), min(redu[2], redu[3])) + 1u;
-  kmax = max(max(redu[4], redu[5]), max(redu[6], redu[7])) - 1u;
+  kmin = min(min(redu[0], redu[1]), min(redu[2], redu[3]));
+  kmax = max(max(redu[4], redu[5]), max(redu[6], redu[7]));
+  if (CAUSAL) { kmin += 1u; kmax -= 1u; }
 
   // ---- bucket levels
   uint32_t base = kmin;                    // first key of the current range
@@ -295,17 +313,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
   bool open = true;                        // the range has no upper end (top bucket so far)
   int above = 0;                           // keys above the current range
   int bT = 0, cb = 0;
-  auto member_bucket = [&](uint32_t kk) -> int {   // bucket of kk in the range, or -1
-    if (kk == 0u || kk < base) return -1;
-    const uint32_t b = (kk - base) >> shift;
-    if (b >= (uint32_t)kBins) return open ? kBins - 1 : -1;
-    return (int)b;
-  };
-  for (;;) {
+  for (int level = 0;; ++level) {
+    if (has) {
+      if (level == 0) {                      // every counted key lies in the first range
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const int b = member_bucket(key[e]);
-      if (b >= 0) atomicAdd(&hist[b], 1);
+        for (int e = 0; e < kPerThread; ++e) {
+          const uint32_t b = min((key[e] - base) >> shift, (uint32_t)(kBins - 1));
+          if (!CAUSAL || key[e] != 0u) atomicAdd(&hist[b], 1);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < kPerThread; ++e) {
+          const uint32_t kk = key[e];
+          const uint32_t b = (kk - base) >> shift;
+          if (kk != 0u && kk >= base && (b < (uint32_t)kBins || open))
+            atomicAdd(&hist[min(b, (uint32_t)(kBins - 1))], 1);
+        }
+      }
     }
     __syncthreads();
     // thread t scans the 8 buckets [kBins - 8(t+1), kBins - 8t) from the top
@@ -334,13 +358,26 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
     __syncthreads();
   }
 
-  // ---- T from the keys of bucket bT
+  // ---- T from the keys of bucket bT: the keys in [lo, lo + 2^shift), or every key >= lo for
+  // the open top bucket
   uint32_t T;
   int tot_gt;                              // keys > T
+  const uint32_t lo = base + ((uint32_t)bT << shift);
+  const bool top_open = open && bT == kBins - 1;
   if (cb <= kMaxCand) {
+    uint32_t cm = 0;                       // bit e: key e is in the bucket
+    if (has) {
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e)
-      if (member_bucket(key[e]) == bT) cand[atomicAdd(&found[2], 1)] = key[e];
+      for (int e = 0; e < kPerThread; ++e) {
+        const uint32_t kk = key[e];
+        const bool in = kk != 0u && (top_open ? kk >= lo : ((kk - lo) >> shift) == 0u);
+        cm |= (uint32_t)in << e;
+      }
+    }
+    if (cm) {
+      int p = atomicAdd(&found[2], __builtin_popcount(cm));
+      for (uint32_t m = cm; m; m &= m - 1u) cand[p++] = key[__builtin_ctz(m)];
+    }
     __syncthreads();
     if (w == 0) {
       const int need = kr - above;          // places left for the bucket's keys (>= 1)
@@ -366,24 +403,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
     T = t_found[0];
     tot_gt = above + (int)t_found[1];
   } else {                                  // a one-key-wide bucket: all its keys equal T
-    T = base + (uint32_t)bT;
+    T = lo;
     tot_gt = above;
   }
 
   // ---- the row: keys > T, then keys == T in ascending j until kr places are filled
-  int eq = 0;
+  uint32_t gtm = 0, eqm = 0;               // bit e: key e > T, key e == T
+  if (has) {
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) eq += key[e] == T;
-  int tot_eq;
-  int eq_seen = block_exclusive_scan(eq, red, &tot_eq);
-  const int need = kr - tot_gt;            // places for keys equal to T
-  uint32_t selm = 0;                       // bit e: column j0 + e chosen
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    const bool is_eq = key[e] == T;
-    selm |= (uint32_t)(key[e] > T || (is_eq && eq_seen < need)) << e;
-    eq_seen += is_eq;
+    for (int e = 0; e < kPerThread; ++e) {
+      gtm |= (uint32_t)(key[e] > T) << e;
+      eqm |= (uint32_t)(key[e] == T) << e;
+    }
   }
+  int tot_eq;
+  const int eq_before = block_exclusive_scan(__builtin_popcount(eqm), red, &tot_eq);
+  uint32_t selm = gtm;                     // plus this thread's first (need - eq_before) ties
+  int nn = kr - tot_gt - eq_before;
+  for (uint32_t m = eqm; m && nn > 0; m &= m - 1u, --nn) selm |= m & (0u - m);
   int tot_sel;
   const int pos0 = block_exclusive_scan(__builtin_popcount(selm), red, &tot_sel);
   const int64_t bs = row / nb;             // b * HS + s
@@ -433,8 +470,10 @@ hipError_t launch_scores_large(int64_t B, int Hq, int Hkv, int nb, int D, float*
 
 hipError_t launch_topk_rows(int64_t rows, int nb, int topk, const float* S, int32_t* idx,
                             bool causal, int G, hipStream_t stream) {
-  topk_rows_kernel<<<dim3((unsigned)rows), kTopkThreads, 0, stream>>>(S, idx, nb, topk, causal,
-                                                                      G);
+  if (causal)
+    topk_rows_kernel<true><<<dim3((unsigned)rows), kTopkThreads, 0, stream>>>(S, idx, nb, topk, G);
+  else
+    topk_rows_kernel<false><<<dim3((unsigned)rows), kTopkThreads, 0, stream>>>(S, idx, nb, topk, G);
   return hipGetLastError();
 }
 
