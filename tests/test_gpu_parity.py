@@ -379,6 +379,41 @@ def test_select_many_blocks(shape):
     say("  ", stats)
 
 
+@pytest.mark.parametrize("shape", [
+    # B, N, Hq, Hkv, D, block: more than 1024 key blocks (the score matrix stays in the workspace)
+    (1, 64 * 2048, 2, 1, 64, 64),
+    (1, 128 * 1088, 2, 2, 128, 128),
+])
+def test_score_matrix_fp32_accuracy(shape):
+    """The score matrix of the many-block selection is formed on the bf16 MFMA from three-part
+    bf16 splits of the pooled values (reading R12): checked on the hardware against the fp64
+    product of the same pooled rows (the GPU's own, read from the workspace), relative to
+    sum_d |qbar_d kbar_d|. An fp32 matrix product reaches about 2e-7 on such rows; a two-part
+    split would leave terms near 2^-16 = 1.5e-5."""
+    B, N, Hq, Hkv, D, blk = shape
+    nb = N // blk
+    say(f"[score matrix accuracy] shape={shape}")
+    q, k, _, _ = make(B, N, Hq, Hkv, D, "bf16", index=20)
+    ws = torch.empty(bst.select_workspace_bytes(B, N, Hq, Hkv, D, blk), dtype=torch.uint8, device=DEV)
+    idx, qbar, kbar = bst.select(q, k, blk, 16, return_pooled=True, workspace=ws)
+    torch.cuda.synchronize()
+    kb_bytes = (B * Hkv * nb * D * 4 + 255) // 256 * 256
+    qb_bytes = (B * Hq * nb * D * 4 + 255) // 256 * 256
+    S = ws[qb_bytes + kb_bytes: qb_bytes + kb_bytes + B * Hq * nb * nb * 4].view(torch.float32)
+    S = S.view(B, Hq, nb, nb).cpu().numpy().astype(np.float64)
+    qb = qbar.cpu().numpy().astype(np.float64)
+    kb = kbar.cpu().numpy().astype(np.float64)
+    G = Hq // Hkv
+    worst = 0.0
+    for b in range(B):
+        for h in range(Hq):
+            exact = qb[b, h] @ kb[b, h // G].T
+            mag = np.abs(qb[b, h]) @ np.abs(kb[b, h // G]).T
+            worst = max(worst, float(np.max(np.abs(S[b, h] - exact) / mag)))
+    say("   max |S - exact| / sum|q k| =", worst)
+    assert worst <= 1e-6
+
+
 def test_select_many_blocks_ties_and_outliers():
     """The per-row selection over more than 1024 key blocks on rows that stress its threshold
     search: exact ties (duplicated key blocks: the lower index wins), a zero query (every score
