@@ -165,7 +165,10 @@ __global__ __launch_bounds__(256) void score_gemm_kernel(
     __syncthreads();
   }
 
-  // hi/lo[a][c][r]: row 64(wave/2) + 32a + 8(r/4) + 4*half + r%4, column 64(wave%2) + 32c + l32
+  // acc[a][c][r]: row 64(wave/2) + 32a + 8(r/4) + 4*half + r%4, column 64(wave%2) + 32c + l32.
+  // The scores go out past the caches (nontemporal stores: 2.9 % faster selection at 8192 key
+  // blocks); the top-k kernel reads them back with ordinary loads (nontemporal loads there
+  // were 15 % slower).
   float* Sbh = S + bh * nb * nb;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(256) void score_gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = row0 + 8 * (r >> 2) + 4 * half + (r & 3);
-        Sbh[(int64_t)row * nb + col] = acc[a][cc][r];
+        __builtin_nontemporal_store(acc[a][cc][r], Sbh + (int64_t)row * nb + col);
       }
     }
 }
