@@ -43,7 +43,7 @@ the design notes of the repository):
   R22 group-shared selection (GQA, MSA §3.1): one selection per KV head from the sum of
       the block scores of its query heads (equivalently, from the summed pooled queries);
       every query head of the group uses it.
-  R26 decode (NEXT N4; the pages' KV cache and first-token latency remarks): one new query
+  R26 decode (the pages' KV cache and first-token latency remarks): one new query
       token per sequence against a cache of L tokens, the query at position L-1. Its own block
       (L-1) // b, complete or not, is always used; the other min(k, own+1) - 1 places go to
       the complete blocks j < own with the largest q . kbar_j (kbar: mean of the block's keys,
@@ -52,13 +52,13 @@ the design notes of the repository):
   R29 group-shared decode selection: with the option, one choice per (sequence, KV head) by
       the sum over its query heads of q_h . kbar_j (R22 for a single query token), used by
       each of those heads.
-  R27 random blocks (NEXT N3; the MSA page's §5.1 remedy "5% random blocks"): of a row's k
+  R27 random blocks (the MSA page's §5.1 remedy "5% random blocks"): of a row's k
       places, k - r keep the best scores and r go to blocks drawn uniformly without
       replacement from the others: draw p (p < r) takes the (x mod m_p)-th remaining block in
       ascending order, m_p = nb - (k - r) - p, x = element row * 2^16 + p of the SplitMix64
       sequence (Steele, Lea, Flood, OOPSLA 2014) seeded with the caller's seed, row the
       row's position (batch, head, query block) in C order.
-  R28 overlapping key blocks (NEXT N3; the MSA page's §5.3 remedy for block-boundary effects,
+  R28 overlapping key blocks (the MSA page's §5.3 remedy for block-boundary effects,
       overlap ratio 0.25): key block j holds the b tokens from j*s on, cut at N, with the
       stride s = b - overlap*b (48 for b = 64, 96 for b = 128), and key blocks follow until one
       reaches the last token; query blocks stay the b-token partition. Pooling, scores and
@@ -466,7 +466,7 @@ def attend_lse(q, k, idx, block, scale, causal: bool = False) -> np.ndarray:
 
 
 def attend_backward(q, k, v, idx, block, scale, dout, causal: bool = False):
-    """Gradients of the gathered-block attention with the selection held fixed (NEXT N2):
+    """Gradients of the gathered-block attention with the selection held fixed:
     for query block i with selected keys U, P = softmax(scale * Q_i K_U^T) (masked when
     causal), O_i = P V_U, and for the upstream gradient dO_i:
         dV_U += P^T dO_i,   dP = dO_i V_U^T,   dS = P * (dP - rowsum(dO_i * O_i)),

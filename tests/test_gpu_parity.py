@@ -386,7 +386,7 @@ def test_select_many_blocks(shape):
 ])
 def test_score_matrix_fp32_accuracy(shape):
     """The score matrix of the many-block selection is formed on the bf16 MFMA from three-part
-    bf16 splits of the pooled values (reading R12): checked on the hardware against the fp64
+    bf16 splits of the pooled values (fp32 accuracy): checked on the hardware against the fp64
     product of the same pooled rows (the GPU's own, read from the workspace), relative to
     sum_d |qbar_d kbar_d|. An fp32 matrix product reaches about 2e-7 on such rows; a two-part
     split would leave terms near 2^-16 = 1.5e-5."""

@@ -360,7 +360,7 @@ def _dense_masked_torch(q, k, v, idx, blk, scale, causal):
 
 
 def check_backward_autograd(o=O):
-    """Backward [N2] against torch autograd through the explicitly masked dense attention,
+    """Backward against torch autograd through the explicitly masked dense attention,
     with GQA, plain and causal."""
     B, N, Hq, Hkv, D, blk = 2, 192, 4, 2, 16, 32
     q, k, v = rand_qkv(B, N, Hq, Hkv, D, seed=17)

@@ -1,8 +1,8 @@
-"""The block scores' arithmetic on the bf16 MFMA (reading R12), simulated on the CPU.
+"""The block scores' arithmetic on the bf16 MFMA, simulated on the CPU.
 
 Both score kernels form q.k from three-part bf16 splits of the fp32 pooled values
 (x = x0 + x1 + x2, x0 = bf16(x), x1 = bf16(x - x0), x2 = x - x0 - x1) as six products
-q0.k0, q0.k1, q1.k0, q0.k2, q1.k1, q2.k0. These tests check the facts that reading rests on:
+q0.k0, q0.k1, q1.k0, q0.k2, q1.k1, q2.k0, each exact in fp32. These tests check that:
 the split is exact, the three products left out are below 2^-23 of sum_d |q_d k_d|, the sum
 in one fp32 accumulator stays at the accuracy of an fp32 matrix product, and a two-part split
 would not meet the index rule's 1e-5 (MSA page §3.3: scores as a matrix product; the index
