@@ -379,6 +379,23 @@ def test_select_many_blocks(shape):
     say("  ", stats)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "fp8"])
+def test_select_many_blocks_dtypes(dtype):
+    """More than 1024 key blocks with fp32 and fp8 inputs: both sides pooled by the pool
+    kernel (fp8: codes without the descale), the score matrix and the per-row top-k."""
+    B, N, Hq, Hkv, D, blk, topk = 1, 64 * 1088, 4, 2, 128, 64, 250
+    say(f"[select many blocks] dtype={dtype} shape={(B, N, Hq, Hkv, D, blk, topk)}")
+    q, k, _, _ = make(B, N, Hq, Hkv, D, dtype, index=21)
+    idx, qbar, kbar = bst.select(q, k, blk, topk, return_pooled=True)
+    torch.cuda.synchronize()
+    qo = to_f64(q) if dtype != "fp8" else O.decode_e4m3(q.view(torch.uint8).cpu().numpy())
+    ko = to_f64(k) if dtype != "fp8" else O.decode_e4m3(k.view(torch.uint8).cpu().numpy())
+    pq, pk = O.pool(qo, blk), O.pool(ko, blk)
+    assert np.max(np.abs(qbar.cpu().numpy() - pq)) <= 2e-6 * np.abs(qo).max()
+    assert np.max(np.abs(kbar.cpu().numpy() - pk)) <= 2e-6 * np.abs(ko).max()
+    say("  ", check_idx(idx.cpu().numpy(), O.block_scores(pq, pk), topk))
+
+
 @pytest.mark.parametrize("shape", [
     # B, N, Hq, Hkv, D, block: more than 1024 key blocks (the score matrix stays in the workspace)
     (1, 64 * 2048, 2, 1, 64, 64),
