@@ -229,6 +229,19 @@ constexpr int kBinBits = 11;
 constexpr int kBins = 1 << kBinBits;       // key buckets per level
 constexpr int kMaxCand = 4 * kWave;        // bucket size one wave resolves (4 keys per lane)
 
+// m * 2 + (a < b), unsigned: one compare into VCC and one add with that carry (shifts a
+// comparison bit into a mask from the bottom; the compiler forms this with three instructions)
+__device__ __forceinline__ uint32_t shift_in_lt(uint32_t m, uint32_t a, uint32_t b) {
+  asm("v_cmp_lt_u32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
+      : "+v"(m) : "v"(a), "v"(b) : "vcc");
+  return m;
+}
+__device__ __forceinline__ uint32_t shift_in_eq(uint32_t m, uint32_t a, uint32_t b) {
+  asm("v_cmp_eq_u32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc"
+      : "+v"(m) : "v"(a), "v"(b) : "vcc");
+  return m;
+}
+
 // Order-preserving key of a float (as order_key): -0.0 becomes +0.0 by adding +0.0, then the
 // sign bit decides between flipping every bit (negative) and setting the top bit.
 __device__ __forceinline__ uint32_t order_key_fast(float s) {
@@ -414,9 +427,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
   uint32_t gtm = 0, eqm = 0;               // bit e: key e > T, key e == T
   if (has) {
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      gtm |= (uint32_t)(key[e] > T) << e;
-      eqm |= (uint32_t)(key[e] == T) << e;
+    for (int e = kPerThread - 1; e >= 0; --e) {   // shifted in from the top: bit e = key e
+      gtm = shift_in_lt(gtm, T, key[e]);
+      eqm = shift_in_eq(eqm, T, key[e]);
     }
   }
   int tot_eq;
