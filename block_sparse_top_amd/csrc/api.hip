@@ -260,7 +260,8 @@ int bsattn_select_ex(int dtype, int64_t B, int64_t N, int Hq, int Hkv, int D, in
                     "pool launch");
     if (st != BSATTN_OK) return st;
     const bool group = flags & BSATTN_GROUP_SELECT;
-    st = hip_status(bsattn::launch_scores_large(B, Hq, Hkv, (int)nb, D, qbar, kbar, S, group, s),
+    st = hip_status(bsattn::launch_scores_large(B, Hq, Hkv, (int)nb, D, qbar, kbar, S, group,
+                                                causal, s),
                     "score launch");
     if (st != BSATTN_OK) return st;
     return hip_status(bsattn::launch_topk_rows(B * (group ? Hkv : Hq) * nb, (int)nb, topk, S, idx,

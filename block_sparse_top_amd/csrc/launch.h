@@ -36,9 +36,11 @@ inline bool materialized_scores(int64_t nb, bool group) {
 }
 // group: the pooled queries of each KV group are summed in place into the rows of its first
 // head and S holds one [nb, nb] matrix per (batch, KV head); topk_rows then writes each row to
-// the idx rows of the G heads of its group (G = 1: one row each).
+// the idx rows of the G heads of its group (G = 1: one row each). causal: only the tiles on and
+// below the diagonal of each matrix are formed (the causal top-k reads no others).
 hipError_t launch_scores_large(int64_t B, int Hq, int Hkv, int nb, int D, float* qbar,
-                               const float* kbar, float* S, bool group, hipStream_t stream);
+                               const float* kbar, float* S, bool group, bool causal,
+                               hipStream_t stream);
 hipError_t launch_topk_rows(int64_t rows, int nb, int topk, const float* S, int32_t* idx,
                             bool causal, int G, hipStream_t stream);
 

@@ -70,19 +70,34 @@ __device__ __forceinline__ void split3(const f32x4& v, u32x2 part[3]) {
 template <int D>
 __global__ __launch_bounds__(256) void score_gemm_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, float* __restrict__ S,
-    int Hq, int Hkv, int nb, int tiles, bool group) {
+    int Hq, int Hkv, int nb, int tiles, bool group, bool causal) {
   constexpr int NC = D / 16;                  // k-steps
   constexpr int PART = kGemmTile * 32;        // bytes of one part of one operand
   constexpr int BUF = 6 * PART;               // q parts 0..2, k parts 0..2
   __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
 
-  // tile index: (b*HS + s) * tiles^2 + ti * tiles + tj, s a selection head (a query head, or
-  // a KV head whose group's summed queries sit in the rows of its first head); tiles of one
-  // (batch, selection head) share their pooled rows: keep them on one XCD's L2
+  // tile index: (b*HS + s) * per + u, s a selection head (a query head, or a KV head whose
+  // group's summed queries sit in the rows of its first head), u the tile (ti, tj) of that
+  // head's matrix in row-major order: u = ti * tiles + tj, or, causal, over the lower triangle
+  // only, u = ti (ti + 1) / 2 + tj with tj <= ti. A causal row i reads columns up to the end of
+  // i's 32-column chunk, inside i's own 128-column tile, so the tiles above the diagonal are
+  // never read and not formed. Tiles of one (batch, selection head) share their pooled rows:
+  // keep them on one XCD's L2.
   const int G = Hq / Hkv, HS = group ? Hkv : Hq;
+  const int64_t per = causal ? (int64_t)tiles * (tiles + 1) / 2 : (int64_t)tiles * tiles;
   const int64_t t = xcd_remap(blockIdx.x, gridDim.x);
-  const int tj = (int)(t % tiles), ti = (int)((t / tiles) % tiles);
-  const int64_t bh = t / ((int64_t)tiles * tiles);   // b * HS + s
+  const int64_t bh = t / per;                         // b * HS + s
+  const int u = (int)(t - bh * per);
+  int ti, tj;
+  if (causal) {   // float root, then one step either way puts ti (ti+1)/2 <= u < (ti+1)(ti+2)/2
+    ti = (int)((sqrtf(8.f * (float)u + 1.f) - 1.f) * 0.5f);
+    if (ti * (ti + 1) / 2 > u) --ti;
+    if ((ti + 1) * (ti + 2) / 2 <= u) ++ti;
+    tj = u - ti * (ti + 1) / 2;
+  } else {
+    ti = u / tiles;
+    tj = u - ti * tiles;
+  }
   const int sh = (int)(bh % HS), b = (int)(bh / HS);
   const int hq = group ? sh * G : sh;                 // query head of the pooled rows
   const int g = group ? sh : sh / G;
@@ -188,6 +203,7 @@ __global__ __launch_bounds__(256) void score_gemm_kernel(
 // ---------------------------------------------------------------- per-row top-k
 constexpr int kTopkThreads = 256;
 constexpr int kPerThread = 32;             // columns per thread: nb <= 8192
+static_assert(kGemmTile % kPerThread == 0, "a causal row's chunk must lie in its own tile");
 
 __device__ __forceinline__ int block_sum(int v, int* red) {
   // wave sum (DPP within 16 lanes, then across 16 and 32 lanes), then the 4 wave sums
@@ -465,7 +481,8 @@ __global__ __launch_bounds__(256) void group_sum_kernel(float* __restrict__ qbar
 }  // namespace
 
 hipError_t launch_scores_large(int64_t B, int Hq, int Hkv, int nb, int D, float* qbar,
-                               const float* kbar, float* S, bool group, hipStream_t stream) {
+                               const float* kbar, float* S, bool group, bool causal,
+                               hipStream_t stream) {
   if (group && Hq > Hkv) {
     const int64_t n = B * Hkv * (int64_t)nb * D;
     group_sum_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, stream>>>(
@@ -474,13 +491,14 @@ hipError_t launch_scores_large(int64_t B, int Hq, int Hkv, int nb, int D, float*
     if (e != hipSuccess) return e;
   }
   const int tiles = (nb + kGemmTile - 1) / kGemmTile;
-  const int64_t n = B * (group ? Hkv : Hq) * (int64_t)tiles * tiles;
+  const int64_t per = causal ? (int64_t)tiles * (tiles + 1) / 2 : (int64_t)tiles * tiles;
+  const int64_t n = B * (group ? Hkv : Hq) * per;
   if (D == 64)
     score_gemm_kernel<64><<<dim3((unsigned)n), 256, 0, stream>>>(qbar, kbar, S, Hq, Hkv, nb,
-                                                                  tiles, group);
+                                                                  tiles, group, causal);
   else
     score_gemm_kernel<128><<<dim3((unsigned)n), 256, 0, stream>>>(qbar, kbar, S, Hq, Hkv, nb,
-                                                                   tiles, group);
+                                                                   tiles, group, causal);
   return hipGetLastError();
 }
 
