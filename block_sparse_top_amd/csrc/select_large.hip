@@ -17,7 +17,8 @@
 // and keys == T fill the remaining places in ascending j (the lower index wins).
 // Output positions come from block-wide exclusive scans, so the row is written in ascending j.
 // Causal option: as in the fused kernel, columns j > i get key 0, column i the largest key,
-// the row keeps min(topk, i+1) blocks and its remaining places are set to -1.
+// the row keeps min(topk, i+1) blocks and its remaining places are set to -1; a row with
+// i + 1 <= topk keeps all of 0..i and is written without reading its scores.
 //
 // Group-shared selection (GQA, MSA §3.1): group_sum_kernel adds the pooled queries of each
 // group's G heads into the rows of its first head (the scores of the sum are the sum of the
@@ -293,6 +294,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
   const int kr = CAUSAL && i + 1 < topk ? i + 1 : topk;
   const float* srow = S + row * nb;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  if (CAUSAL && kr == i + 1) {   // (block-uniform) the row keeps all its blocks 0..i, in order
+    const int64_t bs = row / nb;
+    for (int hh = 0; hh < G; ++hh) {
+      int32_t* out = idx + ((bs * G + hh) * nb + i) * topk;
+      for (int p = t; p < topk; p += kTopkThreads) out[p] = p <= i ? p : -1;
+    }
+    return;
+  }
   const int j0 = t * kPerThread;
   const bool has = j0 < (CAUSAL ? i + 1 : nb);   // some admissible column (all, unless causal)
   uint32_t key[kPerThread];
