@@ -95,7 +95,9 @@ const char* bsattn_last_error(void);
 /* Bytes of device workspace bsattn_select needs for these sizes (0 for an empty call).
  * Layout, each part 256-byte aligned: pooled q, fp32 [B, Hq, nb, D]; then pooled k,
  * fp32 [B, Hkv, nb, D]; when nb > 1024 also the score matrix, fp32 [B, Hq, nb, nb]
- * (MSA page §3.2: 1M tokens at block 128 give 8192 key blocks per row). For fp8 inputs the pooled values are means of the e4m3 codes'
+ * (MSA page §3.2: 1M tokens at block 128 give 8192 key blocks per row), of which the causal
+ * selection writes only the 128 x 128 tiles on and below the diagonal (its rows read no
+ * other score). For fp8 inputs the pooled values are means of the e4m3 codes'
  * values without the per-tensor descale (a positive factor that does not change the
  * selection). Returns 0 and records an error for invalid sizes. */
 size_t bsattn_select_workspace_bytes(int64_t B, int64_t N, int Hq, int Hkv, int D, int block);
