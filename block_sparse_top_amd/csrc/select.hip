@@ -234,6 +234,14 @@ __global__ __launch_bounds__(SelCfg<CPL>::NT) void select_kernel(
   float acc[RW][CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
+    // causal: a chunk that starts past the work-group's last row holds no admissible column
+    // of its rows (all keys 0 below), nor does any later one; the test is the same for the
+    // whole work-group, so every barrier is still reached by all its waves or by none
+    if (causal && c * 64 > row0 + RG - 1) {
+#pragma unroll
+      for (int r = 0; r < RW; ++r) acc[r][c] = 0.f;
+      continue;
+    }
     __syncthreads();                        // previous chunk's ks and sc consumed
     {
       // all loads of the chunk first (up to 8 per thread: D <= 128), then the LDS stores
