@@ -543,6 +543,41 @@ def test_long_context_gqa_sampled():
     assert tally["clear"] + tally["ambiguous"] == 64
 
 
+@pytest.mark.slow
+def test_long_context_causal_selection_sampled():
+    """1M tokens, 32 query / 8 KV heads, causal selection over 8192 key blocks (the score
+    product forms only the tiles on and below the diagonal; rows with i + 1 <= k skip the
+    search): 64 seeded sampled rows hold min(k, i+1) blocks, the own block last, then -1, and
+    their other blocks follow the index rule under the oracle's scores of the blocks j < i."""
+    w = syn.WORKLOADS["longctx_gqa_n1m_bf16"]
+    say("[long context causal selection]", w)
+    q, k, _, _, _ = syn.workload_inputs(w, device=DEV)
+    topk = O.topk_count(w.ratio, w.nb)
+    ws = torch.empty(bst.select_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.D, w.block),
+                     dtype=torch.uint8, device=DEV)
+    idx = bst.select(q, k, w.block, topk, causal=True, workspace=ws).cpu().numpy()
+    del ws
+    say("  gpu done")
+    G = w.Hq // w.Hkv
+    rows = syn.sample_rows(64, w.Hq * w.nb, w.index + 1)  # 64 seeded (head, query block) rows
+    picks = [(r // w.nb, r % w.nb) for r in rows]
+    n_short = 0
+    for g in sorted({h // G for h, _ in picks}):
+        kbar = O.pool(to_f64(k[:, :, g:g + 1]), w.block)[0, 0]        # [nb, D]
+        for h, i in [p for p in picks if p[0] // G == g]:
+            qb = to_f64(q[:, i * w.block:(i + 1) * w.block, h:h + 1])  # [1, block, 1, D]
+            s = O.pool(qb, w.block)[0, 0, 0] @ kbar.T                 # [nb]
+            row = idx[0, h, i]
+            ki = min(topk, i + 1)
+            assert np.all(row[ki:] == -1), f"head {h} row {i}: unused places not -1"
+            assert row[ki - 1] == i, f"head {h} row {i}: own block not last"
+            if ki > 1:
+                check_idx(np.ascontiguousarray(row[:ki - 1])[None], s[None, :i], ki - 1)
+            n_short += i + 1 <= topk
+        say(f"  kv head {g} ok")
+    say(f"  64 sampled causal rows, {n_short} of them with i + 1 <= k")
+
+
 FP8_SHAPES = [
     # B, N, Hq, Hkv, D, block, topk (the fp8 kernel is built for D = 128)
     (1, 64 * 8, 2, 2, 128, 64, 8),          # topk = nb: dense limit
